@@ -1,0 +1,316 @@
+"""CPU oracle for one decode step of the parallel-block MoE decoder.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import or run this module.  It shares no
+code with the GPU path; both take their inputs from the ``synth`` generator.
+
+What it computes is the decode forward pass the cited pages describe
+(Cohere megakernel articles: the latestnews.news page, second paragraph, lists
+the per-step weight and KV streaming; the ainews.surl.tw page, second
+paragraph, says attention and MoE run concurrently from the same normalized
+input; the aiweekly.co page, second paragraph, names the fused operation kinds:
+QKV projection, attention, MoE routing, gather, GEMMs and normalization).  The
+pages print no formulas, so each op below is its textbook definition, written
+plainly, in float64, with bfloat16 rounding only at the points where the
+method stores bfloat16 values:
+
+* weights, KV cache entries, the normalized input ``xn``, q/k/v after the
+  rotation, the attention output and the expert hidden vector ``h``;
+* router logits are rounded to float32 before the top-k decision (the
+  precision in which the GPU takes that integer decision); everything else,
+  including the residual stream and the logits, stays float64.
+
+Readings where the pages are silent (each also listed in the design notes):
+parallel block ``x <- (x + attn) + moe`` with one RMSNorm per layer; rotate-half
+RoPE with ``inv_freq_i = theta^(-2i/d)``; scale ``1/sqrt(d)``; q head ``h`` uses
+kv head ``h // (n_q / n_kv)``; top-k by (value desc, index asc) and softmax over
+the selected logits; SwiGLU experts ``Wd (silu(Wg xn) * (Wu xn))``; the new
+token's K/V are written to slot ``seq_len`` before attention runs over
+``0..seq_len`` inclusive; untied LM head after a final RMSNorm; greedy argmax
+with ties to the lowest id.
+
+Parity unpinned: the composed multi-layer logits have no closed form; they
+are pinned only through the pinned ops and the whole-step invariants in
+``tests/test_oracle_pins.py``.  The ulp behaviour of exp/silu is covered only
+by the comparison tolerance.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+import synth
+
+# ----------------------------------------------------------------------------
+# bfloat16 representation
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bfloat16 bit patterns (uint16) as float64."""
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+_BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 (ties to even), returned as float64.
+
+    bfloat16 keeps 8 significant bits: with x = m * 2^e, 0.5 <= |m| < 1, the
+    representable neighbours are multiples of 2^(e-8) (2^-133 below the
+    smallest normal 2^-126).  np.rint rounds half to even.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    e = np.maximum(e, -125)
+    q = np.ldexp(np.rint(np.ldexp(x, 8 - e)), e - 8)
+    return np.where(np.abs(q) > _BF16_MAX, np.copysign(np.inf, x), q)
+
+
+def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns of values that are already bfloat16-representable."""
+    r = round_bf16(x)
+    b = r.astype(np.float32).view(np.uint32)
+    return (b >> np.uint32(16)).astype(np.uint16)
+
+
+# ----------------------------------------------------------------------------
+# ops
+
+
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """x_i / sqrt(mean(x^2) + eps) * g_i."""
+    return x * (1.0 / np.sqrt(np.mean(x * x) + eps)) * g
+
+
+def rope_inv_freq(d: int, theta: float) -> np.ndarray:
+    return theta ** (-(2.0 * np.arange(d // 2, dtype=np.float64)) / d)
+
+
+def rope(v: np.ndarray, pos: int, theta: float) -> np.ndarray:
+    """Rotate-half RoPE of a [heads][d] array at position ``pos``.
+
+    Pair (i, i + d/2) is rotated by the angle pos * theta^(-2i/d).
+    """
+    d = v.shape[-1]
+    ang = pos * rope_inv_freq(d, theta)
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = v[..., : d // 2], v[..., d // 2:]
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+
+
+def softmax(z: np.ndarray) -> np.ndarray:
+    e = np.exp(z - np.max(z))
+    return e / np.sum(e)
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    return z / (1.0 + np.exp(-z))
+
+
+def topk_desc(r: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest values, ordered by (value desc, index asc)."""
+    order = sorted(range(len(r)), key=lambda i: (-float(r[i]), i))
+    return np.array(order[:k], dtype=np.int64)
+
+
+def attention_head(q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
+    """softmax(K q / sqrt(d)) V for one query vector over rows of K, V."""
+    s = (K @ q) / np.sqrt(q.shape[0])
+    p = softmax(s)
+    return p @ V
+
+
+# ----------------------------------------------------------------------------
+# weights and KV cache
+
+
+class Weights:
+    """Model weights as float64, generated from the synth recipe and cached.
+
+    ``budget_bytes`` bounds the cache of float64 matrices; expert slices are
+    regenerated on demand once the budget is used.
+    """
+
+    def __init__(self, shape: synth.ModelShape, budget_bytes: float = 6e9, source=None):
+        self.shape = shape
+        self.budget = budget_bytes
+        self.used = 0
+        self.cache: dict = {}
+        self.source = source or (lambda kind, layer, expert: synth.weight_bits(shape, kind, layer, expert))
+
+    def get(self, kind: int, layer: int = 0, expert: int | None = None) -> np.ndarray:
+        key = (kind, layer, expert)
+        w = self.cache.get(key)
+        if w is None:
+            w = bf16_to_f64(self.source(kind, layer, expert))
+            if self.used + w.nbytes <= self.budget:
+                self.cache[key] = w
+                self.used += w.nbytes
+        return w
+
+
+class PagedKV:
+    """Paged K/V pools: per layer ``[num_pages][n_kv][page_size][d]`` bfloat16 bits."""
+
+    def __init__(self, shape: synth.ModelShape, num_pages: int):
+        s = shape
+        self.shape = s
+        dims = (s.n_layers, num_pages, s.n_kv_heads, s.page_size, s.head_dim)
+        self.k = np.full(dims, 0x7FC0, dtype=np.uint16)   # NaN: unwritten slots poison any stray read
+        self.v = np.full(dims, 0x7FC0, dtype=np.uint16)
+
+    def slots(self, page_table_row: np.ndarray, pos: np.ndarray):
+        """(physical page, offset in page) of logical positions ``pos`` through one page-table row."""
+        ps = self.shape.page_size
+        pos = np.asarray(pos, dtype=np.int64)
+        page = np.asarray(page_table_row, dtype=np.int64)[pos // ps]
+        if np.any(page < 0) or np.any(page >= self.k.shape[1]):
+            raise IndexError("page id out of range in page table")
+        return page, pos % ps
+
+    def write(self, layer: int, page_table_row: np.ndarray, pos: int, k_bits: np.ndarray, v_bits: np.ndarray):
+        page, o = self.slots(page_table_row, [pos])
+        self.k[layer, page[0], :, o[0], :] = k_bits
+        self.v[layer, page[0], :, o[0], :] = v_bits
+
+    def gather(self, layer: int, page_table_row: np.ndarray, n: int, g: int):
+        """K, V rows (float64 [n][d]) of kv head ``g`` for logical positions 0..n-1."""
+        page, o = self.slots(page_table_row, np.arange(n))
+        return bf16_to_f64(self.k[layer, page, g, o]), bf16_to_f64(self.v[layer, page, g, o])
+
+    def fill_synthetic(self, page_table: np.ndarray, context: list):
+        """Fill positions 0..context[b]-1 of every sequence from the synth KV recipe."""
+        s = self.shape
+        ps = s.page_size
+        for b, n in enumerate(context):
+            for layer in range(s.n_layers):
+                K = synth.kv_bits(s, layer, "k", b, 0, n)
+                V = synth.kv_bits(s, layer, "v", b, 0, n)
+                for t0 in range(0, n, ps):
+                    t1 = min(n, t0 + ps)
+                    page = int(page_table[b, t0 // ps])
+                    self.k[layer, page, :, : t1 - t0, :] = K[t0:t1].transpose(1, 0, 2)
+                    self.v[layer, page, :, : t1 - t0, :] = V[t0:t1].transpose(1, 0, 2)
+
+
+# ----------------------------------------------------------------------------
+# one decode step
+
+
+@dataclass
+class StepOut:
+    logits: np.ndarray                      # [B][V] float64
+    router_logits: np.ndarray               # [L][B][E] float32 values
+    sel: np.ndarray                         # [L][B][k] int64
+    margin: np.ndarray                      # [L][B] float: r_(k) - r_(k+1) (inf when k == E)
+    next_token: np.ndarray                  # [B] int64 greedy argmax
+    top2_gap: np.ndarray                    # [B] logit gap between best and second best
+    trace: dict = field(default_factory=dict)
+
+
+def decode_step(W: Weights, kv: PagedKV, tokens, page_table, seq_lens, trace: bool = False) -> StepOut:
+    """One decode step for a ragged batch.
+
+    tokens[b] is the new token of sequence b; seq_lens[b] tokens are already in
+    the cache, so the new token sits at position p = seq_lens[b].  Its K/V are
+    written to the cache, and attention runs over positions 0..p.
+    """
+    s = W.shape
+    L, H, d, E, k = s.n_layers, s.hidden, s.head_dim, s.n_experts, s.top_k
+    nq, nkv = s.n_q_heads, s.n_kv_heads
+    group = nq // nkv
+    B = len(tokens)
+    logits = np.zeros((B, s.vocab))
+    rl = np.zeros((L, B, E), dtype=np.float32)
+    sel_all = np.zeros((L, B, k), dtype=np.int64)
+    margin = np.zeros((L, B))
+    tr: dict = {}
+    for b in range(B):
+        p = int(seq_lens[b])
+        pt = np.asarray(page_table[b])
+        x = W.get(synth.K_EMBED)[int(tokens[b])].copy()
+        for l in range(L):
+            xn = round_bf16(rmsnorm(x, W.get(synth.K_ATTN_NORM, l), s.rms_eps))
+            # attention path
+            qkv = W.get(synth.K_WQKV, l) @ xn
+            q = qkv[: nq * d].reshape(nq, d)
+            kk = qkv[nq * d: (nq + nkv) * d].reshape(nkv, d)
+            vv = qkv[(nq + nkv) * d:].reshape(nkv, d)
+            q16 = round_bf16(rope(q, p, s.rope_theta))
+            k16 = round_bf16(rope(kk, p, s.rope_theta))
+            v16 = round_bf16(vv)
+            kv.write(l, pt, p, f64_to_bf16_bits(k16), f64_to_bf16_bits(v16))
+            o = np.zeros((nq, d))
+            for g in range(nkv):
+                K, V = kv.gather(l, pt, p + 1, g)
+                for h in range(g * group, (g + 1) * group):
+                    o[h] = attention_head(q16[h], K, V)
+            a16 = round_bf16(o.reshape(-1))
+            attn = W.get(synth.K_WO, l) @ a16
+            # MoE path, from the same normalized input
+            r = (W.get(synth.K_ROUTER, l) @ xn).astype(np.float32)
+            sel = topk_desc(r, k)
+            wsel = softmax(r[sel].astype(np.float64))
+            moe = np.zeros(H)
+            hs = []
+            for j in range(k):
+                e = int(sel[j])
+                gate = W.get(synth.K_W_GATE, l, e) @ xn
+                up = W.get(synth.K_W_UP, l, e) @ xn
+                h16 = round_bf16(silu(gate) * up)
+                hs.append(h16)
+                moe = moe + wsel[j] * (W.get(synth.K_W_DOWN, l, e) @ h16)
+            x_in = x
+            x = (x + attn) + moe
+            rl[l, b] = r
+            sel_all[l, b] = sel
+            srt = np.sort(r.astype(np.float64))[::-1]
+            margin[l, b] = srt[k - 1] - srt[k] if k < E else np.inf
+            if trace:
+                tr.setdefault("x_in", {})[(l, b)] = x_in
+                tr.setdefault("xn", {})[(l, b)] = xn
+                tr.setdefault("q16", {})[(l, b)] = q16
+                tr.setdefault("k16", {})[(l, b)] = k16
+                tr.setdefault("v16", {})[(l, b)] = v16
+                tr.setdefault("a16", {})[(l, b)] = a16
+                tr.setdefault("attn", {})[(l, b)] = attn
+                tr.setdefault("moe", {})[(l, b)] = moe
+                tr.setdefault("h16", {})[(l, b)] = np.stack(hs)
+                tr.setdefault("w", {})[(l, b)] = wsel
+        xf = round_bf16(rmsnorm(x, W.get(synth.K_FINAL_NORM), s.rms_eps))
+        logits[b] = W.get(synth.K_LM_HEAD) @ xf
+        if trace:
+            tr.setdefault("x_final", {})[b] = x
+    nxt = np.argmax(logits, axis=1)
+    srt = np.sort(logits, axis=1)
+    gap = srt[:, -1] - srt[:, -2]
+    return StepOut(logits, rl, sel_all, margin, nxt, gap, tr)
+
+
+def prefill_as_decode(W: Weights, kv: PagedKV, prompt, page_table_row) -> StepOut:
+    """Feed prompt tokens one decode step at a time (positions 0..n-1) for one sequence."""
+    out = None
+    pt = np.asarray(page_table_row)[None, :]
+    for t, tok in enumerate(prompt):
+        out = decode_step(W, kv, [int(tok)], pt, [t])
+    return out
+
+
+# ----------------------------------------------------------------------------
+# speed-of-light model
+
+
+def sol_tokens_per_s(bandwidth_bytes_per_s: float, bytes_per_step: float, batch: int = 1) -> float:
+    """Bandwidth bound on decode throughput: batch * bandwidth / bytes streamed per step."""
+    return batch * bandwidth_bytes_per_s / bytes_per_step
+
+
+def step_bytes(shape: synth.ModelShape, seq_lens, distinct_experts_per_layer: float) -> float:
+    """Algorithmic HBM bytes read by one step: active weights, embedding rows and KV for 0..p."""
+    w = shape.active_weight_bytes(distinct_experts_per_layer)
+    w += 2.0 * shape.hidden * len(seq_lens)
+    per_tok_kv = shape.kv_bytes_per_token()
+    kv = sum(per_tok_kv * (int(p) + 1) for p in seq_lens)
+    return w + kv

@@ -1,0 +1,367 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each test ties one part of the oracle to a closed form, an invariant, a
+library routine, a brute-force computation on tiny inputs, or the numbers the
+pages print, chosen so that a plausible slip (a dropped gain, a wrong sign or
+pairing in the rotation, an off-by-one position, a wrong GQA group, a
+transposed operand, a wrong tie rule) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import synth
+from oracle import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# --------------------------------------------------------------------------- bf16
+
+
+def test_round_bf16_matches_torch_on_f32_values():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000),
+                        # exact ties between neighbouring bf16 values
+                        (1.0 + (2 * np.arange(1, 200) + 1) * 2.0 ** -8) * 2.0 ** rng.integers(-20, 20, 199)])
+    x32 = x.astype(np.float32)
+    ref = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.round_bf16(x32.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+def test_round_bf16_rounds_the_exact_value_once():
+    u = 2.0 ** -8
+    cases = {
+        1.0 + u: 1.0,                          # tie -> even
+        1.0 + 3 * u: 1.0 + 4 * u,              # tie -> even (up)
+        1.0 + u + 2.0 ** -40: 1.0 + 2 * u,     # above the tie: rounding via fp32 first would give 1.0
+        -(1.0 + u + 2.0 ** -40): -(1.0 + 2 * u),
+        0.0: 0.0,
+        3.0: 3.0,
+        2.0 ** -130 * 1.3: 2.0 ** -133 * round(1.3 * 8),   # subnormal quantum 2^-133
+        3.5e38: math.inf,
+    }
+    for x, want in cases.items():
+        assert O.round_bf16(np.array([x]))[0] == want, x
+
+
+def test_bf16_bits_roundtrip():
+    bits = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
+    finite = ((bits.astype(np.uint32) >> 7) & 0xFF) != 0xFF
+    v = O.bf16_to_f64(bits[finite])
+    assert np.array_equal(O.f64_to_bf16_bits(v), bits[finite])
+
+
+# --------------------------------------------------------------------------- RMSNorm
+
+
+def test_rmsnorm_closed_form_on_constant_vector():
+    rng = np.random.default_rng(1)
+    g = 1.0 + 0.02 * rng.standard_normal(64)
+    for c, eps in ((3.0, 1e-6), (1e-3, 1e-6), (-2.0, 0.5)):
+        got = O.rmsnorm(np.full(64, c), g, eps)
+        assert np.allclose(got, c / math.sqrt(c * c + eps) * g, rtol=1e-14, atol=0)
+
+
+def test_rmsnorm_scale_invariance_and_unit_rms():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal(256)
+    g = np.ones(256)
+    y = O.rmsnorm(x, g, 0.0)
+    assert abs(np.sqrt(np.mean(y * y)) - 1.0) < 1e-14
+    assert np.allclose(O.rmsnorm(7.5 * x, g, 0.0), y, rtol=1e-14)
+
+
+# --------------------------------------------------------------------------- RoPE
+
+
+def test_rope_position_zero_is_identity():
+    v = np.random.default_rng(3).standard_normal((4, 64))
+    assert np.array_equal(O.rope(v, 0, 1e4), v)
+
+
+def test_rope_hand_computed_d4():
+    # d = 4, theta = 1e4: inv_freq = [1, 1e-2]; pairs are (0, 2) and (1, 3)
+    v = np.array([[1.0, 2.0, 3.0, 4.0]])
+    p = 5
+    a0, a1 = 5.0, 0.05
+    want = [1 * math.cos(a0) - 3 * math.sin(a0), 2 * math.cos(a1) - 4 * math.sin(a1),
+            1 * math.sin(a0) + 3 * math.cos(a0), 2 * math.sin(a1) + 4 * math.cos(a1)]
+    assert np.allclose(O.rope(v, p, 1e4)[0], want, rtol=1e-15, atol=1e-15)
+
+
+def test_rope_equals_complex_rotation_and_is_relative():
+    rng = np.random.default_rng(4)
+    d, theta = 128, 1e4
+    q, k = rng.standard_normal(d), rng.standard_normal(d)
+    m = 1234
+    z = (q[: d // 2] + 1j * q[d // 2:]) * np.exp(1j * m * theta ** (-np.arange(0, d, 2) / d))
+    r = O.rope(q[None], m, theta)[0]
+    assert np.allclose(r[: d // 2], z.real, atol=1e-12) and np.allclose(r[d // 2:], z.imag, atol=1e-12)
+    # norm preserved pair by pair
+    assert np.allclose(r[: d // 2] ** 2 + r[d // 2:] ** 2, q[: d // 2] ** 2 + q[d // 2:] ** 2, rtol=1e-12)
+    # <rope(q, m), rope(k, n)> depends only on m - n
+    d1 = O.rope(q[None], 40, theta)[0] @ O.rope(k[None], 17, theta)[0]
+    d2 = O.rope(q[None], 40 + 999, theta)[0] @ O.rope(k[None], 17 + 999, theta)[0]
+    assert abs(d1 - d2) < 1e-10
+
+
+# --------------------------------------------------------------------------- attention
+
+
+def test_attention_single_position_returns_v():
+    rng = np.random.default_rng(5)
+    q, K, V = rng.standard_normal(64), rng.standard_normal((1, 64)), rng.standard_normal((1, 64))
+    assert np.array_equal(O.attention_head(q, K, V), V[0])
+
+
+def test_attention_equal_keys_give_mean_v():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal(64)
+    K = np.tile(rng.standard_normal(64), (37, 1))
+    V = rng.standard_normal((37, 64))
+    assert np.allclose(O.attention_head(q, K, V), V.mean(axis=0), rtol=1e-13, atol=1e-15)
+
+
+def test_attention_matches_scipy_softmax_brute_force():
+    rng = np.random.default_rng(7)
+    for n in (2, 17, 300):
+        q, K, V = rng.standard_normal(128), rng.standard_normal((n, 128)), rng.standard_normal((n, 128))
+        p = scipy.special.softmax(np.array([q @ K[t] for t in range(n)]) / math.sqrt(128))
+        want = sum(p[t] * V[t] for t in range(n))
+        assert np.allclose(O.attention_head(q, K, V), want, rtol=1e-12, atol=1e-14)
+        assert abs(O.softmax(K @ q).sum() - 1.0) < 1e-14
+
+
+# --------------------------------------------------------------------------- router
+
+
+def test_topk_matches_stable_full_sort_with_ties():
+    rng = np.random.default_rng(8)
+    for _ in range(200):
+        r = rng.integers(0, 6, 32).astype(np.float32)   # many exact ties
+        k = int(rng.integers(1, 9))
+        want = np.argsort(-r.astype(np.float64), kind="stable")[:k]
+        assert np.array_equal(O.topk_desc(r, k), want)
+
+
+def test_softmax_over_selected_equals_renormalised_full_softmax():
+    rng = np.random.default_rng(9)
+    r = rng.standard_normal(128)
+    sel = O.topk_desc(r, 8)
+    full = scipy.special.softmax(r)
+    assert np.allclose(O.softmax(r[sel]), full[sel] / full[sel].sum(), rtol=1e-13)
+    assert abs(O.softmax(r[sel]).sum() - 1.0) < 1e-15
+
+
+def test_silu_closed_forms():
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    assert abs(O.silu(np.array([1.0]))[0] - 1.0 / (1.0 + math.exp(-1.0))) < 1e-16
+    assert abs(O.silu(np.array([40.0]))[0] - 40.0) < 1e-12
+    assert abs(O.silu(np.array([-40.0]))[0]) < 1e-15
+
+
+def test_gemv_matches_exact_sum():
+    rng = np.random.default_rng(10)
+    bits = synth.normal_bf16(0, 77, 0, 16 * 2048, 0.02).reshape(16, 2048)
+    W = O.bf16_to_f64(bits)
+    x = O.round_bf16(rng.standard_normal(2048))
+    y = W @ x
+    for i in range(16):
+        exact = math.fsum(float(W[i, j]) * float(x[j]) for j in range(2048))
+        assert abs(y[i] - exact) <= 1e-13 * max(1.0, abs(exact))
+
+
+# --------------------------------------------------------------------------- whole step on the tiny model
+
+
+def _tiny_setup(pages_shuffled: bool, source=None, n_prompt: int = 6):
+    s = synth.TINY
+    W = O.Weights(s, source=source)
+    num_pages = 4
+    pt = np.arange(num_pages, dtype=np.int32)
+    if pages_shuffled:
+        pt = np.array([2, 0, 3, 1], dtype=np.int32)
+    kv = O.PagedKV(s, num_pages)
+    return s, W, kv, pt
+
+
+def test_paged_shuffled_equals_identity_bit_exact():
+    toks = synth.uniform_u32(synth.SEED_PROMPT, synth.tid(synth.K_PROMPT, 0), 0, 20, synth.TINY.vocab)
+    outs = []
+    for shuffled in (False, True):
+        s, W, kv, pt = _tiny_setup(shuffled)
+        for t, tok in enumerate(toks):
+            out = O.decode_step(W, kv, [int(tok)], pt[None], [t])
+        outs.append(out.logits)
+    assert np.array_equal(outs[0], outs[1])
+
+
+def _full_recompute_logits(W, toks):
+    """Non-cached causal forward over the whole sequence; logits of the last position.
+
+    Each layer handles all positions at once: K/V of every position are
+    computed in the same pass, and position t attends over rows 0..t.
+    """
+    s = W.shape
+    n, d, nq, nkv = len(toks), s.head_dim, s.n_q_heads, s.n_kv_heads
+    X = np.stack([W.get(synth.K_EMBED)[int(t)] for t in toks])
+    for l in range(s.n_layers):
+        XN = np.stack([O.round_bf16(O.rmsnorm(X[t], W.get(synth.K_ATTN_NORM, l), s.rms_eps)) for t in range(n)])
+        QKV = np.stack([W.get(synth.K_WQKV, l) @ XN[t] for t in range(n)])
+        Q = np.stack([O.round_bf16(O.rope(QKV[t, : nq * d].reshape(nq, d), t, s.rope_theta)) for t in range(n)])
+        K = np.stack([O.round_bf16(O.rope(QKV[t, nq * d:(nq + nkv) * d].reshape(nkv, d), t, s.rope_theta)) for t in range(n)])
+        V = np.stack([O.round_bf16(QKV[t, (nq + nkv) * d:].reshape(nkv, d)) for t in range(n)])
+        Xn = np.empty_like(X)
+        for t in range(n):
+            o = np.stack([O.attention_head(Q[t, h], K[: t + 1, h // (nq // nkv)], V[: t + 1, h // (nq // nkv)])
+                          for h in range(nq)])
+            attn = W.get(synth.K_WO, l) @ O.round_bf16(o.reshape(-1))
+            r = (W.get(synth.K_ROUTER, l) @ XN[t]).astype(np.float32)
+            sel = np.argsort(-r.astype(np.float64), kind="stable")[: s.top_k]
+            w = scipy.special.softmax(r[sel].astype(np.float64))
+            moe = np.zeros(s.hidden)
+            for j, e in enumerate(sel):
+                h = O.round_bf16(O.silu(W.get(synth.K_W_GATE, l, int(e)) @ XN[t]) * (W.get(synth.K_W_UP, l, int(e)) @ XN[t]))
+                moe = moe + w[j] * (W.get(synth.K_W_DOWN, l, int(e)) @ h)
+            Xn[t] = (X[t] + attn) + moe
+        X = Xn
+    xf = O.round_bf16(O.rmsnorm(X[-1], W.get(synth.K_FINAL_NORM), s.rms_eps))
+    return W.get(synth.K_LM_HEAD) @ xf
+
+
+def test_cached_decode_equals_full_recompute():
+    toks = synth.uniform_u32(synth.SEED_PROMPT, synth.tid(synth.K_PROMPT, 0), 0, 19, synth.TINY.vocab)
+    s, W, kv, pt = _tiny_setup(True)
+    for t, tok in enumerate(toks):
+        out = O.decode_step(W, kv, [int(tok)], pt[None], [t])
+    ref = _full_recompute_logits(W, toks)
+    assert np.max(np.abs(out.logits[0] - ref)) <= 1e-9 * np.max(np.abs(ref))
+
+
+def _modified_source(s, zero_kinds=(), identical_experts=False, zero_k_rows=False):
+    def src(kind, layer, expert):
+        if identical_experts and kind in (synth.K_W_GATE, synth.K_W_UP, synth.K_W_DOWN):
+            a = synth.weight_bits(s, kind, layer, 0 if expert is not None else None)
+            if expert is None:
+                a = np.broadcast_to(a[0], a.shape).copy()
+        else:
+            a = synth.weight_bits(s, kind, layer, expert)
+        if kind in zero_kinds:
+            a = np.zeros_like(a)
+        if zero_k_rows and kind == synth.K_WQKV:
+            a = a.copy()
+            nq, nkv, d = s.n_q_heads, s.n_kv_heads, s.head_dim
+            a[nq * d:(nq + nkv) * d] = 0
+        return a
+    return src
+
+
+def test_zero_attention_and_expert_outputs_leave_residual_as_embedding():
+    s = synth.TINY
+    W = O.Weights(s, source=_modified_source(s, zero_kinds=(synth.K_WO, synth.K_W_DOWN)))
+    kv = O.PagedKV(s, 2)
+    tok = 77
+    out = O.decode_step(W, kv, [tok], np.arange(2, dtype=np.int32)[None], [0], trace=True)
+    e = W.get(synth.K_EMBED)[tok]
+    assert np.array_equal(out.trace["x_final"][0], e)
+    want = W.get(synth.K_LM_HEAD) @ O.round_bf16(O.rmsnorm(e, W.get(synth.K_FINAL_NORM), s.rms_eps))
+    assert np.array_equal(out.logits[0], want)
+
+
+def test_identical_experts_reduce_to_one_dense_swiglu_ffn():
+    s = synth.TINY
+    W = O.Weights(s, source=_modified_source(s, identical_experts=True))
+    kv = O.PagedKV(s, 2)
+    out = O.decode_step(W, kv, [5], np.arange(2, dtype=np.int32)[None], [0], trace=True)
+    for l in range(s.n_layers):
+        xn = out.trace["xn"][(l, 0)]
+        h = O.round_bf16(O.silu(W.get(synth.K_W_GATE, l, 0) @ xn) * (W.get(synth.K_W_UP, l, 0) @ xn))
+        dense = W.get(synth.K_W_DOWN, l, 0) @ h
+        assert np.allclose(out.trace["moe"][(l, 0)], dense, rtol=1e-13, atol=1e-16)
+
+
+def test_gqa_groups_read_their_own_kv_head():
+    """Zero keys give uniform attention: head h must average the V of kv head h // (nq/nkv)."""
+    s = synth.TINY
+    W = O.Weights(s, source=_modified_source(s, zero_k_rows=True))
+    kv = O.PagedKV(s, 1)
+    p = 5
+    pt = np.zeros((1, 1), dtype=np.int32)
+    consts = [0.5, -2.0]                       # V of kv head g is consts[g] at positions 0..p-1
+    for g in range(s.n_kv_heads):
+        kv.k[:, 0, g, :p, :] = 0
+        kv.v[:, 0, g, :p, :] = O.f64_to_bf16_bits(np.array([consts[g]]))[0]
+    out = O.decode_step(W, kv, [9], pt, [p], trace=True)
+    group = s.n_q_heads // s.n_kv_heads
+    for l in range(s.n_layers):
+        v_new = out.trace["v16"][(l, 0)]
+        a = out.trace["a16"][(l, 0)].reshape(s.n_q_heads, s.head_dim)
+        for h in range(s.n_q_heads):
+            g = h // group
+            want = O.round_bf16((p * consts[g] + v_new[g]) / (p + 1))
+            assert np.array_equal(a[h], want), (l, h)
+
+
+def test_new_kv_written_at_position_slot_and_rotated_at_p():
+    s, W, kv, pt = _tiny_setup(True)
+    toks = [3, 900, 41]
+    for t, tok in enumerate(toks):
+        out = O.decode_step(W, kv, [tok], pt[None], [t], trace=True)
+    p = len(toks) - 1
+    for l in range(s.n_layers):
+        xn = out.trace["xn"][(l, 0)]
+        nq, nkv, d = s.n_q_heads, s.n_kv_heads, s.head_dim
+        kk = (W.get(synth.K_WQKV, l) @ xn)[nq * d:(nq + nkv) * d].reshape(nkv, d)
+        want = O.f64_to_bf16_bits(O.rope(kk, p, s.rope_theta))
+        page, off = int(pt[p // s.page_size]), p % s.page_size
+        assert np.array_equal(kv.k[l, page, :, off, :], want)
+        # slots after p are still poison
+        assert np.all(kv.k[l, page, :, off + 1:, :] == 0x7FC0)
+
+
+def test_greedy_ties_go_to_lowest_id():
+    logits = np.array([[0.0, 3.0, 1.0, 3.0]])
+    assert int(np.argmax(logits, axis=1)[0]) == 1
+
+
+# --------------------------------------------------------------------------- speed-of-light numbers the pages print
+
+
+def test_sol_bound_reproduces_the_pages_numbers():
+    with open(os.path.join(GOLDEN, "sol_bound_h100.json")) as f:
+        g = json.load(f)
+    bound = O.sol_tokens_per_s(g["hbm_bytes_per_s"], g["weight_bytes"] + g["kv_bytes"])
+    assert abs(bound - g["bound_tok_s"]) / g["bound_tok_s"] < 0.01
+    assert round(100 * g["megakernel_tok_s"] / g["bound_tok_s"]) == g["megakernel_pct"]
+    assert round(100 * g["vllm_tok_s"] / g["bound_tok_s"]) == g["vllm_pct"]
+    assert round(g["megakernel_tok_s"] / g["vllm_tok_s"], 2) == g["speedup"]
+
+
+def test_step_bytes_30b_shape_8k():
+    s = synth.MOE30B
+    # 48 layers x 2 (K, V) x 4 kv heads x 128 x 2 bytes per token
+    assert s.kv_bytes_per_token() == 98304
+    b = O.step_bytes(s, [8192], s.top_k)
+    w = s.active_weight_bytes(s.top_k)
+    assert abs(w / 1e9 - 6.0835) < 5e-4
+    assert abs((b - w - 2 * s.hidden) - 98304 * 8193) < 1
+
+
+def test_non_square_shape_catches_transposed_operands():
+    """Every matrix of this shape is non-square, so a transposed operand cannot broadcast."""
+    s = synth.ModelShape(n_layers=2, hidden=96, n_q_heads=4, n_kv_heads=2, head_dim=16,
+                         n_experts=6, top_k=2, inter=40, vocab=200)
+    assert len({s.hidden, s.attn_dim, s.qkv_rows, s.inter, s.n_experts, s.vocab}) == 6
+    W = O.Weights(s)
+    kv = O.PagedKV(s, 2)
+    out = None
+    for t, tok in enumerate((1, 150, 7)):
+        out = O.decode_step(W, kv, [tok], np.array([[1, 0]], dtype=np.int32), [t])
+    assert out.logits.shape == (1, 200) and np.all(np.isfinite(out.logits))
