@@ -1,0 +1,197 @@
+/*
+ * mk.h -- C ABI of the persistent MoE decode megakernel for MI355X (gfx950).
+ *
+ * One call to mk_decode_step runs one BF16 autoregressive decode step of a
+ * parallel-block mixture-of-experts decoder (RMSNorm, QKV projection, rotary
+ * embedding, paged split-KV attention, router top-k, expert gather with
+ * gate/up/down projections, residuals, LM head) as a single persistent kernel:
+ * one workgroup per compute unit works through a task table that the host
+ * built ahead of time, and tasks wait on counters in global memory instead of
+ * on kernel boundaries.
+ *
+ * Where the operations come from (the Cohere megakernel pages):
+ *  - latestnews.news, "Cohere speeds up North Mini Code with new megakernel",
+ *    paragraphs 2-3: the whole decode forward pass in one persistent kernel,
+ *    a host-built static schedule, global-memory counters, paged attention
+ *    and ragged sequence lengths;
+ *  - ainews.surl.tw, paragraph 2: a fine-grained task table of GEMM tiles and
+ *    attention splits assigned to compute units in advance; attention and MoE
+ *    run concurrently from the same normalized input;
+ *  - aiweekly.co, paragraphs 2-4: the fused operation kinds (QKV projection,
+ *    attention, MoE routing, gather, GEMMs, normalization), fixed-size task
+ *    descriptors, a consumer waiting on a single count, and prefetch of
+ *    immutable weights.
+ *
+ * Conventions for every entry point:
+ *  - Return MK_OK (0) or a negative MK_ERR_* code; no exception crosses the ABI.
+ *    mk_last_error_message() returns a thread-local description of the last
+ *    failure on the calling thread.
+ *  - "device pointer" = memory the caller allocated on the GPU (e.g. through
+ *    PyTorch); the library never allocates or frees device memory and owns
+ *    only its host-side state.
+ *  - "stream" = a hipStream_t passed as void*; NULL means the default stream.
+ *    Work is enqueued asynchronously on it.
+ *  - Matrices are row-major [out][in] bfloat16 (raw 16-bit patterns).
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct mk_ctx mk_ctx;
+
+enum {
+  MK_OK = 0,
+  MK_ERR_INVALID_ARG = -1,   /* bad argument detected on the host; nothing enqueued */
+  MK_ERR_UNSUPPORTED = -2,   /* configuration outside what the kernels handle */
+  MK_ERR_STATE = -3,         /* call out of order (no schedule, not bound, reset needed) */
+  MK_ERR_SCHEDULE = -4,      /* schedule failed validation (deadlock or bad fan-in) */
+  MK_ERR_HIP = -5,           /* a HIP runtime call failed; the message names it */
+  MK_ERR_DEVICE_PAGE = -10,  /* kernel met a page id outside [0, num_pages) */
+  MK_ERR_DEVICE_SEQ = -11,   /* kernel met seq_len < 0 or seq_len + 1 > max_pages_per_seq * page_size */
+  MK_ERR_DEVICE_TOKEN = -12, /* kernel met a token id outside [0, vocab) */
+  MK_ERR_DEVICE_TIMEOUT = -13 /* a dependency wait exceeded the spin limit; the grid drained */
+};
+
+/* Model shape and capacity.  Supported: hidden, n_q_heads*head_dim and inter
+ * multiples of 128; head_dim 64 or 128; n_q_heads a multiple of n_kv_heads
+ * with at most 8 q heads per kv head; n_experts <= 128; top_k <= 8;
+ * page_size == 16; 1 <= max_batch <= 8. */
+typedef struct mk_config {
+  int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim;
+  int32_t n_experts, top_k, inter, vocab;
+  int32_t page_size;          /* tokens per KV page (16) */
+  int32_t max_batch;          /* largest batch a step may carry */
+  int32_t max_pages_per_seq;  /* page-table row stride; a sequence holds at most this many pages */
+  int32_t num_pages;          /* pages in each layer's K pool and V pool */
+  float rms_eps;              /* RMSNorm epsilon (1e-6) */
+  double rope_theta;          /* RoPE base (1e4) */
+} mk_config;
+
+/* Creates a context for one model shape.  Host only, no GPU call.
+ * cfg is copied.  *out receives the context (free with mk_destroy). */
+int mk_create(const mk_config* cfg, mk_ctx** out);
+
+/* Builds the static task table (host only, deterministic, integer only) for
+ * num_cus persistent workgroups (0 = query the current device), validates it
+ * by simulating every queue on the host (deadlock freedom, fan-in of each
+ * counter), and reports the size of the device workspace the caller must
+ * provide to mk_bind.  ctx_hint is the expected number of cached tokens per
+ * sequence; it only decides how many compute units take attention tasks
+ * versus expert tasks, never what is computed.  (ainews.surl.tw, paragraph 2:
+ * the table of GEMM tiles and attention splits is assigned in advance.) */
+int mk_build_schedule(mk_ctx* ctx, int32_t num_cus, int64_t ctx_hint, size_t* workspace_bytes);
+
+/* Binds caller-owned device buffers and uploads the task table into the
+ * workspace on `stream` (synchronizes that stream before returning).
+ *  weights: host array of n_weights device pointers, n_weights = 3 + 7*n_layers,
+ *    in this order: embed [vocab][hidden], lm_head [vocab][hidden],
+ *    final_norm [hidden], then per layer: attn_norm [hidden],
+ *    wqkv [(n_q+2*n_kv)*head_dim][hidden] (q rows, then k rows, then v rows),
+ *    wo [hidden][n_q*head_dim], router [n_experts][hidden],
+ *    w_gate [n_experts][inter][hidden], w_up [n_experts][inter][hidden],
+ *    w_down [n_experts][hidden][inter].
+ *  k_pool, v_pool: device, [n_layers][num_pages][n_kv_heads][page_size][head_dim] bf16.
+ *  workspace: device, at least the size mk_build_schedule reported, 256-byte aligned.
+ * The buffers must stay valid until the context is destroyed or bound again. */
+int mk_bind(mk_ctx* ctx, const void* const* weights, int32_t n_weights, void* k_pool, void* v_pool,
+            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Enqueues one decode step for a ragged batch of n sequences (1 <= n <= max_batch).
+ *  d_tokens: device int32[n], the new token of each sequence.
+ *  d_page_table: device int32[n][max_pages_per_seq], physical page of each
+ *    logical page (-1 = none).  Shared by all layers.
+ *  d_seq_lens: device int32[n], tokens already cached; the new token sits at
+ *    position seq_lens[b].  Its K/V are written to slot seq_lens[b] % page_size
+ *    of page page_table[b][seq_lens[b] / page_size]; attention covers
+ *    positions 0..seq_lens[b].  seq_lens is not modified: the caller advances it.
+ *  d_logits: device float[n][vocab], written.
+ *  d_next_tokens: device int32[n] receiving the greedy argmax (lowest id on
+ *    ties), or NULL.
+ * Asynchronous.  One step per context may be in flight at a time; steps on
+ * one stream are ordered.  Device-detected errors are sticky: read them with
+ * mk_get_error. */
+int mk_decode_step(mk_ctx* ctx, int32_t n, const int32_t* d_tokens, const int32_t* d_page_table,
+                   const int32_t* d_seq_lens, float* d_logits, int32_t* d_next_tokens, void* stream);
+
+/* Synchronizes `stream`, reads the sticky device error word and clears it.
+ * *code receives 0 or an MK_ERR_DEVICE_* code; *cu and *task (may be NULL)
+ * the workgroup and task that raised it.  After a device error the context
+ * needs mk_reset before the next step. */
+int mk_get_error(mk_ctx* ctx, int32_t* code, int32_t* cu, int32_t* task, void* stream);
+
+/* Clears counters, tickets and the error word on `stream` with a fill kernel. */
+int mk_reset(mk_ctx* ctx, void* stream);
+
+/* Sets the bound of every dependency wait in microseconds (default 2e6).
+ * Host only; applies from the next step. */
+int mk_set_spin_limit_us(mk_ctx* ctx, int64_t microseconds);
+
+const char* mk_last_error_message(void);
+void mk_destroy(mk_ctx* ctx);
+
+/* ---- host-only introspection (no GPU call; for tests and tooling) ---- */
+
+typedef struct mk_schedule_info {
+  int32_t num_cus;
+  int32_t n_tasks;
+  int32_t n_counters;
+  int32_t n_attn;      /* attention split tasks per layer */
+  int32_t n_gateup;    /* expert gate/up tasks per layer */
+  int32_t n_out;       /* output-row tasks per layer */
+  int32_t n_lmhead;    /* LM head tasks */
+  int32_t task_int32s; /* int32 fields per task descriptor (32) */
+  int64_t lds_bytes;   /* dynamic LDS per workgroup */
+  int64_t workspace_bytes;
+} mk_schedule_info;
+
+int mk_get_schedule_info(const mk_ctx* ctx, mk_schedule_info* out);
+
+/* Copies the task table (n_tasks * 32 int32) and the per-CU queue offsets
+ * (num_cus + 1 int32) into host buffers of the given capacities. */
+int mk_copy_schedule(const mk_ctx* ctx, int32_t* tasks, int64_t tasks_cap, int32_t* queue_off, int64_t off_cap);
+
+/* Re-runs the host simulation of the built table.  Returns MK_OK or
+ * MK_ERR_SCHEDULE; *completed receives the number of tasks that ran. */
+int mk_validate_schedule(const mk_ctx* ctx, int32_t* completed);
+
+/* Simulates an arbitrary task table (n_tasks * 32 int32, queue offsets of
+ * num_cus + 1 int32, n_counters counters) the way mk_validate_schedule does:
+ * every wait must name the full fan-in of its counter, and running each
+ * queue in order, a task at a time whenever its waits are met, must finish
+ * every task.  Returns MK_OK or MK_ERR_SCHEDULE (MK_ERR_INVALID_ARG for a
+ * malformed table); *completed receives the number of tasks that ran. */
+int mk_simulate_table(const int32_t* tasks, int32_t n_tasks, const int32_t* queue_off, int32_t num_cus,
+                      int32_t n_counters, int32_t* completed);
+
+/* Host mirror of the kernel's runtime attention split: for seq_lens[0..n),
+ * n_kv heads and n_tasks split tasks, writes the chunk length in tokens to
+ * *chunk and, per task, (b, kv head, first token, end token) into
+ * plan[n_tasks][4] (b = -1 for an idle task). */
+int mk_attn_plan(const int32_t* seq_lens, int32_t n, int32_t n_kv, int32_t n_tasks, int32_t page_size,
+                 int32_t* chunk, int32_t* plan);
+
+/* Offsets (bytes from the workspace base) of the per-layer activation
+ * buffers, for debugging and layer-by-layer comparison:
+ *  x: float [n_layers+1][max_batch][hidden] residual entering each layer (slot 0 unused)
+ *  qkv: float [n_layers][max_batch][(n_q+2*n_kv)*head_dim] before rotation
+ *  router: float [n_layers][max_batch][n_experts]
+ *  attn_out: bf16 [n_layers][max_batch][n_q*head_dim]
+ *  h: bf16 [n_layers][max_batch*top_k][inter] (row b*top_k+j: j-th expert of token b)
+ *  sel: int32 [n_layers][max_batch][top_k] experts chosen for each token, best first */
+typedef struct mk_ws_offsets {
+  int64_t x, qkv, router, attn_out, h, sel;
+} mk_ws_offsets;
+
+int mk_get_ws_offsets(const mk_ctx* ctx, mk_ws_offsets* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MK_H */

@@ -1,0 +1,598 @@
+// Host half of the C ABI in include/mk.h: argument checks, the static
+// schedule builder and its simulator, the workspace layout, binding of
+// caller-owned buffers and the per-step launch.
+//
+// The schedule follows the pages' description of the table (ainews.surl.tw,
+// paragraph 2: tiles and attention splits assigned to compute units in
+// advance; aiweekly.co, paragraphs 2-3: fixed-size descriptors, a task waits
+// on one count) with its own layout: one queue per compute unit, per layer
+//   PRE (norm + Wqkv / router rows)  ->  ATTN or GATEUP  ->  OUT (Wo + down rows),
+// then LM head rows.  Every counter is signalled once per task and waited on
+// as "value >= epoch * fan-in", so nothing is reset between steps.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/mk.h"
+#include "mk_types.h"
+
+using namespace mk;
+
+extern "C" int mkk_launch_step(const KArgs* a, int grid, size_t lds_bytes, hipStream_t stream);
+extern "C" int mkk_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t stream);
+
+namespace {
+
+thread_local std::string g_msg;
+
+int fail(int code, const std::string& m) {
+  g_msg = m;
+  return code;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct WsLayout {
+  size_t state = 0, n_state_u32 = 0;  // counters, tickets, error word (zeroed by mk_reset)
+  size_t ctr = 0, tickets = 0, err = 0;
+  size_t tasks = 0, queue_off = 0, wtab = 0, inv_freq = 0;
+  size_t x = 0, qkv = 0, rlog = 0, attn_part = 0, attn_out = 0, h = 0, lm_part = 0, sel = 0;
+  size_t total = 0;
+};
+
+}  // namespace
+
+struct mk_ctx {
+  mk_config cfg{};
+  bool built = false, bound = false, need_reset = false;
+  int ncu = 0, n_attn = 0, n_gu = 0, n_out = 0, n_lm = 0, n_ctr = 0, n_tickets = 0;
+  int out_rows_max = 0, gu_rows_max = 0, lm_rows_max = 0;
+  int lds_b = 0, lds_c = 0;
+  size_t lds_bytes = 0;
+  std::vector<Task> tasks;
+  std::vector<int32_t> qoff;
+  WsLayout ws;
+  // bound state
+  uint8_t* wsp = nullptr;
+  uint16_t* kpool = nullptr;
+  uint16_t* vpool = nullptr;
+  uint32_t epoch = 0;
+  int64_t spin_us = 2000000;
+};
+
+static int check_config(const mk_config& c) {
+  auto bad = [](const char* what) { return fail(MK_ERR_UNSUPPORTED, std::string("unsupported config: ") + what); };
+  if (c.n_layers < 1 || c.hidden < 1 || c.n_q_heads < 1 || c.n_kv_heads < 1 || c.n_experts < 1 || c.top_k < 1 ||
+      c.inter < 1 || c.vocab < 2 || c.num_pages < 1 || c.max_pages_per_seq < 1 || c.max_batch < 1)
+    return fail(MK_ERR_INVALID_ARG, "config has a non-positive size");
+  if (c.hidden % 128) return bad("hidden % 128 != 0");
+  if (c.inter % 128) return bad("inter % 128 != 0");
+  if ((c.n_q_heads * c.head_dim) % 128) return bad("n_q_heads*head_dim % 128 != 0");
+  if (c.head_dim != 64 && c.head_dim != 128) return bad("head_dim must be 64 or 128");
+  if (c.n_q_heads % c.n_kv_heads) return bad("n_q_heads % n_kv_heads != 0");
+  if (c.n_q_heads / c.n_kv_heads > kMaxGroup) return bad("more than 8 q heads per kv head");
+  if (c.n_experts > kMaxExperts) return bad("n_experts > 128");
+  if (c.top_k > kMaxTopK || c.top_k > c.n_experts) return bad("top_k > 8 or > n_experts");
+  if (c.page_size != 16) return bad("page_size must be 16");
+  if (c.max_batch > kMaxBatch) return bad("max_batch > 8");
+  if (!(c.rms_eps >= 0.f) || !(c.rope_theta > 0.0)) return fail(MK_ERR_INVALID_ARG, "bad rms_eps or rope_theta");
+  if ((int64_t)c.max_pages_per_seq * c.page_size > (1 << 30)) return bad("context bound too large");
+  return MK_OK;
+}
+
+extern "C" int mk_create(const mk_config* cfg, mk_ctx** out) {
+  if (!cfg || !out) return fail(MK_ERR_INVALID_ARG, "null argument");
+  int r = check_config(*cfg);
+  if (r) return r;
+  mk_ctx* c = new (std::nothrow) mk_ctx();
+  if (!c) return fail(MK_ERR_INVALID_ARG, "out of host memory");
+  c->cfg = *cfg;
+  *out = c;
+  return MK_OK;
+}
+
+extern "C" void mk_destroy(mk_ctx* ctx) { delete ctx; }
+
+extern "C" const char* mk_last_error_message(void) { return g_msg.c_str(); }
+
+// ---------------------------------------------------------------------------
+// schedule
+
+static void split_rows(int rows, int parts, int i, int* r0, int* r1) {
+  *r0 = (int)((int64_t)rows * i / parts);
+  *r1 = (int)((int64_t)rows * (i + 1) / parts);
+}
+
+static Task make_task(int op, int layer) {
+  Task t;
+  std::memset(&t, 0, sizeof t);
+  t.op = op;
+  t.layer = layer;
+  t.wait[0] = t.wait[1] = -1;
+  t.signal = -1;
+  return t;
+}
+
+static int simulate_raw(const Task* tasks, int nt, const int32_t* qoff, int ncu, int n_ctr, int32_t* completed) {
+  if (completed) *completed = 0;
+  if (nt < 0 || ncu < 1 || n_ctr < 0 || qoff[0] != 0 || qoff[ncu] != nt)
+    return fail(MK_ERR_INVALID_ARG, "malformed task table");
+  for (int q = 0; q < ncu; ++q)
+    if (qoff[q + 1] < qoff[q]) return fail(MK_ERR_INVALID_ARG, "queue offsets not ascending");
+  std::vector<int64_t> ctr(n_ctr, 0), signals(n_ctr, 0);
+  for (int i = 0; i < nt; ++i) {
+    const Task& t = tasks[i];
+    if (t.signal >= n_ctr || t.wait[0] >= n_ctr || t.wait[1] >= n_ctr)
+      return fail(MK_ERR_INVALID_ARG, "counter index out of range");
+    if (t.signal >= 0) signals[t.signal]++;
+  }
+  // every wait must name the full fan-in of its counter
+  for (int i = 0; i < nt; ++i)
+    for (int k = 0; k < 2; ++k)
+      if (tasks[i].wait[k] >= 0 && signals[tasks[i].wait[k]] != tasks[i].fanin[k])
+        return fail(MK_ERR_SCHEDULE, "schedule: task " + std::to_string(i) +
+                                         " waits for a fan-in that differs from the signals on its counter");
+  std::vector<int> head(qoff, qoff + ncu);
+  int done = 0;
+  bool progress = true;
+  while (progress) {
+    progress = false;
+    for (int q = 0; q < ncu; ++q) {
+      while (head[q] < qoff[q + 1]) {
+        const Task& t = tasks[head[q]];
+        bool ready = true;
+        for (int k = 0; k < 2; ++k)
+          if (t.wait[k] >= 0 && ctr[t.wait[k]] < t.fanin[k]) ready = false;
+        if (!ready) break;
+        if (t.signal >= 0) ctr[t.signal]++;
+        head[q]++;
+        done++;
+        progress = true;
+      }
+    }
+  }
+  if (completed) *completed = done;
+  if (done != nt) return fail(MK_ERR_SCHEDULE, "schedule: deadlock in host simulation (" + std::to_string(done) +
+                                                   " of " + std::to_string(nt) + " tasks ran)");
+  return MK_OK;
+}
+
+static int simulate(const mk_ctx* c, int32_t* completed) {
+  return simulate_raw(c->tasks.data(), (int)c->tasks.size(), c->qoff.data(), c->ncu, c->n_ctr, completed);
+}
+
+extern "C" int mk_simulate_table(const int32_t* tasks, int32_t n_tasks, const int32_t* queue_off, int32_t num_cus,
+                                 int32_t n_counters, int32_t* completed) {
+  if (!tasks || !queue_off) return fail(MK_ERR_INVALID_ARG, "null table");
+  return simulate_raw((const Task*)tasks, n_tasks, queue_off, num_cus, n_counters, completed);
+}
+
+static WsLayout layout_workspace(const mk_ctx* c) {
+  const mk_config& f = c->cfg;
+  WsLayout w;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  const size_t B = f.max_batch, L = f.n_layers;
+  const size_t qkv_rows = (size_t)(f.n_q_heads + 2 * f.n_kv_heads) * f.head_dim;
+  const size_t group = f.n_q_heads / f.n_kv_heads;
+  w.state = o;
+  w.ctr = 0;
+  w.tickets = c->n_ctr;
+  w.err = c->n_ctr + c->n_tickets;
+  w.n_state_u32 = c->n_ctr + c->n_tickets + E_WORDS;
+  take(4 * w.n_state_u32);
+  w.tasks = take(sizeof(Task) * c->tasks.size());
+  w.queue_off = take(4 * (c->ncu + 1));
+  w.wtab = take(8 * (3 + 7 * L));
+  w.inv_freq = take(8 * (f.head_dim / 2));
+  w.x = take(4 * (L + 1) * B * f.hidden);
+  w.qkv = take(4 * L * B * qkv_rows);
+  w.rlog = take(4 * L * B * f.n_experts);
+  w.attn_part = take(4 * L * c->n_attn * group * (f.head_dim + 2));
+  w.attn_out = take(2 * L * B * f.n_q_heads * f.head_dim);
+  w.h = take(2 * L * B * f.top_k * f.inter);
+  w.lm_part = take(4 * 2 * c->n_lm * B);
+  w.sel = take(4 * L * B * f.top_k);
+  w.total = o;
+  return w;
+}
+
+extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, size_t* workspace_bytes) {
+  if (!c) return fail(MK_ERR_INVALID_ARG, "null context");
+  if (num_cus < 0 || ctx_hint < 0) return fail(MK_ERR_INVALID_ARG, "negative num_cus or ctx_hint");
+  const mk_config& f = c->cfg;
+  size_t lds_cap = 160 * 1024;
+  if (num_cus == 0) {
+    int dev = 0;
+    hipDeviceProp_t p;
+    if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&p, dev) != hipSuccess)
+      return fail(MK_ERR_HIP, "cannot query the current device");
+    num_cus = p.multiProcessorCount;
+    lds_cap = p.sharedMemPerBlock;
+  }
+  const int ncu = num_cus;
+  const int L = f.n_layers, H = f.hidden, E = f.n_experts, B = f.max_batch;
+  const int qkv_rows = (f.n_q_heads + 2 * f.n_kv_heads) * f.head_dim;
+  const int group = f.n_q_heads / f.n_kv_heads;
+  if (ncu < 2) return fail(MK_ERR_UNSUPPORTED, "need at least 2 compute units");
+
+  // Compute units split between attention chunks and expert gate/up rows in
+  // proportion to the bytes each streams per layer (attention weighted 1.5x
+  // for its extra arithmetic).  The split never changes results.
+  const double hint = ctx_hint > 0 ? (double)ctx_hint : 4096.0;
+  const double attn_bytes = 1.5 * hint * B * f.n_kv_heads * f.head_dim * 4.0;
+  const double gu_bytes = (double)std::min(E, B * f.top_k) * 2.0 * f.inter * H * 2.0;
+  int n_attn = (int)std::lround(ncu * attn_bytes / (attn_bytes + gu_bytes));
+  const char* env = std::getenv("MK_ATTN_CUS");
+  if (env) n_attn = std::atoi(env);
+  n_attn = std::max(n_attn, B * f.n_kv_heads);
+  n_attn = std::min(n_attn, ncu - 1);
+  if (n_attn < B * f.n_kv_heads) return fail(MK_ERR_UNSUPPORTED, "too few compute units for the attention split");
+  const int n_gu = ncu - n_attn;
+
+  c->tasks.clear();
+  c->qoff.assign(ncu + 1, 0);
+  c->ncu = ncu;
+  c->n_attn = n_attn;
+  c->n_gu = n_gu;
+  c->n_ctr = (L + 1) * kCtrPerLayer;
+  c->n_tickets = L * B * f.n_kv_heads + 1;
+
+  // fan-ins
+  const int R1 = qkv_rows + E;
+  std::vector<int> n_qkv_tasks(L, 0), n_router_tasks(L, 0), n_out_tasks(L, 0);
+  int n_lm = 0;
+  c->out_rows_max = 0;
+  c->lm_rows_max = 0;
+  for (int q = 0; q < ncu; ++q) {
+    int r0, r1;
+    split_rows(R1, ncu, q, &r0, &r1);
+    if (r0 < std::min(r1, qkv_rows)) n_qkv_tasks[0]++;
+    if (std::max(r0, qkv_rows) < r1) n_router_tasks[0]++;
+    split_rows(H, ncu, q, &r0, &r1);
+    if (r1 > r0) n_out_tasks[0]++;
+    c->out_rows_max = std::max(c->out_rows_max, r1 - r0);
+    split_rows(f.vocab, ncu, q, &r0, &r1);
+    if (r1 > r0) n_lm++;
+    c->lm_rows_max = std::max(c->lm_rows_max, r1 - r0);
+  }
+  for (int l = 1; l < L; ++l) {
+    n_qkv_tasks[l] = n_qkv_tasks[0];
+    n_router_tasks[l] = n_router_tasks[0];
+    n_out_tasks[l] = n_out_tasks[0];
+  }
+  c->n_out = n_out_tasks[0];
+  c->n_lm = n_lm;
+
+  int lm_i = 0;
+  for (int q = 0; q < ncu; ++q) {
+    c->qoff[q] = (int)c->tasks.size();
+    for (int l = 0; l < L; ++l) {
+      int r0, r1;
+      split_rows(R1, ncu, q, &r0, &r1);
+      // PRE: the qkv part and the router part of this range
+      const int cut0[2] = {r0, std::max(r0, qkv_rows)};
+      const int cut1[2] = {std::min(r1, qkv_rows), r1};
+      for (int part = 0; part < 2; ++part) {
+        if (cut0[part] >= cut1[part]) continue;
+        Task t = make_task(OP_PRE, l);
+        if (l > 0) {
+          t.wait[0] = ctr_index(l - 1, C_XNEXT);
+          t.fanin[0] = n_out_tasks[l - 1];
+        }
+        t.r0 = cut0[part];
+        t.r1 = cut1[part];
+        t.signal = ctr_index(l, part == 0 ? C_QKV : C_ROUTER);
+        c->tasks.push_back(t);
+      }
+      // stage 2
+      if (q < n_attn) {
+        Task t = make_task(OP_ATTN, l);
+        t.wait[0] = ctr_index(l, C_QKV);
+        t.fanin[0] = n_qkv_tasks[l];
+        t.idx = q;
+        t.count = n_attn;
+        t.signal = ctr_index(l, C_ATTN);
+        c->tasks.push_back(t);
+      } else {
+        Task t = make_task(OP_GATEUP, l);
+        t.wait[0] = ctr_index(l, C_ROUTER);
+        t.fanin[0] = n_router_tasks[l];
+        t.idx = q - n_attn;
+        t.count = n_gu;
+        t.signal = ctr_index(l, C_GATEUP);
+        c->tasks.push_back(t);
+      }
+      // OUT
+      split_rows(H, ncu, q, &r0, &r1);
+      if (r1 > r0) {
+        Task t = make_task(OP_OUT, l);
+        t.wait[0] = ctr_index(l, C_ATTN);
+        t.fanin[0] = n_attn;
+        t.wait[1] = ctr_index(l, C_GATEUP);
+        t.fanin[1] = n_gu;
+        t.r0 = r0;
+        t.r1 = r1;
+        t.signal = ctr_index(l, C_XNEXT);
+        c->tasks.push_back(t);
+      }
+    }
+    int r0, r1;
+    split_rows(f.vocab, ncu, q, &r0, &r1);
+    if (r1 > r0) {
+      Task t = make_task(OP_LMHEAD, L);
+      t.wait[0] = ctr_index(L - 1, C_XNEXT);
+      t.fanin[0] = n_out_tasks[L - 1];
+      t.r0 = r0;
+      t.r1 = r1;
+      t.idx = lm_i++;
+      t.count = n_lm;
+      t.signal = ctr_index(L, C_DONE);
+      c->tasks.push_back(t);
+    }
+  }
+  c->qoff[ncu] = (int)c->tasks.size();
+
+  // LDS: region A (input vectors), B (top-k state, reductions), C (per-op arrays)
+  const int maxU = std::min(E, B * f.top_k);
+  c->gu_rows_max = (int)(((int64_t)maxU * f.inter + n_gu - 1) / n_gu) + 1;
+  size_t a_bytes = std::max({(size_t)B * H * 2, (size_t)B * f.n_q_heads * f.head_dim * 2,
+                             (size_t)B * f.top_k * f.inter * 2, (size_t)group * f.head_dim * 2});
+  a_bytes = align_up(a_bytes, 256);
+  const size_t b_bytes = 4096;
+  size_t c_gu = (size_t)std::min(c->gu_rows_max, kGuPass) * B * 2 * 4;
+  size_t c_out = (size_t)c->out_rows_max * B * 4 + (size_t)c->out_rows_max * B * f.top_k * 4;
+  size_t c_lm = (size_t)c->lm_rows_max * B * 4;
+  size_t c_attn = (size_t)kWaves * 16 * kMaxGroup * 4 + (size_t)kWaves * group * (f.head_dim + 2) * 4;
+  size_t c_bytes = align_up(std::max({c_gu, c_out, c_lm, c_attn}), 256);
+  c->lds_b = (int)a_bytes;
+  c->lds_c = (int)(a_bytes + b_bytes);
+  c->lds_bytes = a_bytes + b_bytes + c_bytes;
+  if (c->lds_bytes > lds_cap)
+    return fail(MK_ERR_UNSUPPORTED, "LDS need " + std::to_string(c->lds_bytes) + " exceeds " + std::to_string(lds_cap));
+
+  int r = simulate(c, nullptr);
+  if (r) return r;
+  c->ws = layout_workspace(c);
+  c->built = true;
+  c->bound = false;
+  if (workspace_bytes) *workspace_bytes = c->ws.total;
+  return MK_OK;
+}
+
+extern "C" int mk_validate_schedule(const mk_ctx* c, int32_t* completed) {
+  if (!c || !c->built) return fail(MK_ERR_STATE, "no schedule built");
+  return simulate(c, completed);
+}
+
+extern "C" int mk_get_schedule_info(const mk_ctx* c, mk_schedule_info* out) {
+  if (!c || !out) return fail(MK_ERR_INVALID_ARG, "null argument");
+  if (!c->built) return fail(MK_ERR_STATE, "no schedule built");
+  out->num_cus = c->ncu;
+  out->n_tasks = (int32_t)c->tasks.size();
+  out->n_counters = c->n_ctr;
+  out->n_attn = c->n_attn;
+  out->n_gateup = c->n_gu;
+  out->n_out = c->n_out;
+  out->n_lmhead = c->n_lm;
+  out->task_int32s = kTaskInts;
+  out->lds_bytes = (int64_t)c->lds_bytes;
+  out->workspace_bytes = (int64_t)c->ws.total;
+  return MK_OK;
+}
+
+extern "C" int mk_copy_schedule(const mk_ctx* c, int32_t* tasks, int64_t tasks_cap, int32_t* queue_off, int64_t off_cap) {
+  if (!c || !c->built) return fail(MK_ERR_STATE, "no schedule built");
+  const int64_t need = (int64_t)c->tasks.size() * kTaskInts;
+  if (tasks) {
+    if (tasks_cap < need) return fail(MK_ERR_INVALID_ARG, "task buffer too small");
+    std::memcpy(tasks, c->tasks.data(), need * 4);
+  }
+  if (queue_off) {
+    if (off_cap < c->ncu + 1) return fail(MK_ERR_INVALID_ARG, "offset buffer too small");
+    std::memcpy(queue_off, c->qoff.data(), (c->ncu + 1) * 4);
+  }
+  return MK_OK;
+}
+
+extern "C" int mk_attn_plan(const int32_t* seq_lens, int32_t n, int32_t n_kv, int32_t n_tasks, int32_t page_size,
+                            int32_t* chunk, int32_t* plan) {
+  if (!seq_lens || !chunk || !plan || n < 1 || n > kMaxBatch || n_kv < 1 || page_size < 1 || n_tasks < n * n_kv)
+    return fail(MK_ERR_INVALID_ARG, "bad attention plan arguments");
+  int32_t lens1[kMaxBatch];
+  for (int b = 0; b < n; ++b) {
+    if (seq_lens[b] < 0) return fail(MK_ERR_INVALID_ARG, "negative seq_len");
+    lens1[b] = seq_lens[b] + 1;
+  }
+  const int64_t C = attn_chunk_len(lens1, n, n_kv, n_tasks, page_size);
+  *chunk = (int32_t)C;
+  for (int i = 0; i < n_tasks; ++i) {
+    int b, g, t0, t1, first, nch;
+    if (attn_chunk_of(lens1, n, n_kv, C, i, &b, &g, &t0, &t1, &first, &nch)) {
+      plan[4 * i + 0] = b;
+      plan[4 * i + 1] = g;
+      plan[4 * i + 2] = t0;
+      plan[4 * i + 3] = t1;
+    } else {
+      plan[4 * i + 0] = -1;
+      plan[4 * i + 1] = plan[4 * i + 2] = plan[4 * i + 3] = 0;
+    }
+  }
+  return MK_OK;
+}
+
+extern "C" int mk_get_ws_offsets(const mk_ctx* c, mk_ws_offsets* out) {
+  if (!c || !out) return fail(MK_ERR_INVALID_ARG, "null argument");
+  if (!c->built) return fail(MK_ERR_STATE, "no schedule built");
+  out->x = (int64_t)c->ws.x;
+  out->qkv = (int64_t)c->ws.qkv;
+  out->router = (int64_t)c->ws.rlog;
+  out->attn_out = (int64_t)c->ws.attn_out;
+  out->h = (int64_t)c->ws.h;
+  out->sel = (int64_t)c->ws.sel;
+  return MK_OK;
+}
+
+extern "C" int mk_set_spin_limit_us(mk_ctx* c, int64_t us) {
+  if (!c || us < 1) return fail(MK_ERR_INVALID_ARG, "bad spin limit");
+  c->spin_us = us;
+  return MK_OK;
+}
+
+// ---------------------------------------------------------------------------
+// device binding and launch
+
+static int hip_fail(hipError_t e, const char* what) {
+  return fail(MK_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+static int zero_state(mk_ctx* c, hipStream_t s) {
+  int r = mkk_fill_u32((uint32_t*)(c->wsp + c->ws.state), 0u, c->ws.n_state_u32, s);
+  if (r) return fail(MK_ERR_HIP, "state fill kernel launch failed");
+  c->epoch = 0;
+  c->need_reset = false;
+  return MK_OK;
+}
+
+extern "C" int mk_bind(mk_ctx* c, const void* const* weights, int32_t n_weights, void* k_pool, void* v_pool,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (!c) return fail(MK_ERR_INVALID_ARG, "null context");
+  if (!c->built) return fail(MK_ERR_STATE, "mk_build_schedule must run before mk_bind");
+  const mk_config& f = c->cfg;
+  if (!weights || n_weights != 3 + 7 * f.n_layers) return fail(MK_ERR_INVALID_ARG, "weights must hold 3 + 7*n_layers pointers");
+  for (int i = 0; i < n_weights; ++i)
+    if (!weights[i]) return fail(MK_ERR_INVALID_ARG, "null weight pointer " + std::to_string(i));
+  if (!k_pool || !v_pool || !workspace) return fail(MK_ERR_INVALID_ARG, "null pool or workspace");
+  if (workspace_bytes < c->ws.total) return fail(MK_ERR_INVALID_ARG, "workspace smaller than reported");
+  if (((uintptr_t)workspace) % 256) return fail(MK_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  for (int i = 0; i < n_weights; ++i)
+    if (((uintptr_t)weights[i]) % 16) return fail(MK_ERR_INVALID_ARG, "weight pointer not 16-byte aligned");
+  if (((uintptr_t)k_pool) % 16 || ((uintptr_t)v_pool) % 16) return fail(MK_ERR_INVALID_ARG, "pool not 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  c->wsp = (uint8_t*)workspace;
+  c->kpool = (uint16_t*)k_pool;
+  c->vpool = (uint16_t*)v_pool;
+
+  std::vector<uint64_t> wtab(n_weights);
+  for (int i = 0; i < n_weights; ++i) wtab[i] = (uint64_t)(uintptr_t)weights[i];
+  std::vector<double> inv_freq(f.head_dim / 2);
+  for (int i = 0; i < f.head_dim / 2; ++i) inv_freq[i] = std::pow(f.rope_theta, -(2.0 * i) / f.head_dim);
+
+  hipError_t e;
+  if ((e = hipMemcpyAsync(c->wsp + c->ws.tasks, c->tasks.data(), sizeof(Task) * c->tasks.size(), hipMemcpyHostToDevice, s)) ||
+      (e = hipMemcpyAsync(c->wsp + c->ws.queue_off, c->qoff.data(), 4 * c->qoff.size(), hipMemcpyHostToDevice, s)) ||
+      (e = hipMemcpyAsync(c->wsp + c->ws.wtab, wtab.data(), 8 * wtab.size(), hipMemcpyHostToDevice, s)) ||
+      (e = hipMemcpyAsync(c->wsp + c->ws.inv_freq, inv_freq.data(), 8 * inv_freq.size(), hipMemcpyHostToDevice, s)))
+    return hip_fail(e, "hipMemcpyAsync (schedule upload)");
+  int r = zero_state(c, s);
+  if (r) return r;
+  if ((e = hipStreamSynchronize(s))) return hip_fail(e, "hipStreamSynchronize (bind)");
+  c->bound = true;
+  return MK_OK;
+}
+
+extern "C" int mk_decode_step(mk_ctx* c, int32_t n, const int32_t* d_tokens, const int32_t* d_page_table,
+                              const int32_t* d_seq_lens, float* d_logits, int32_t* d_next_tokens, void* stream) {
+  if (!c) return fail(MK_ERR_INVALID_ARG, "null context");
+  if (!c->bound) return fail(MK_ERR_STATE, "context not bound");
+  if (c->need_reset) return fail(MK_ERR_STATE, "a device error was reported; call mk_reset first");
+  const mk_config& f = c->cfg;
+  if (n < 1 || n > f.max_batch) return fail(MK_ERR_INVALID_ARG, "batch outside [1, max_batch]");
+  if (!d_tokens || !d_page_table || !d_seq_lens || !d_logits) return fail(MK_ERR_INVALID_ARG, "null step buffer");
+
+  KArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.L = f.n_layers;
+  a.H = f.hidden;
+  a.nq = f.n_q_heads;
+  a.nkv = f.n_kv_heads;
+  a.d = f.head_dim;
+  a.E = f.n_experts;
+  a.topk = f.top_k;
+  a.I = f.inter;
+  a.V = f.vocab;
+  a.ps = f.page_size;
+  a.max_batch = f.max_batch;
+  a.max_pages = f.max_pages_per_seq;
+  a.num_pages = f.num_pages;
+  a.qkv_rows = (f.n_q_heads + 2 * f.n_kv_heads) * f.head_dim;
+  a.group = f.n_q_heads / f.n_kv_heads;
+  a.eps = f.rms_eps;
+  a.n_attn = c->n_attn;
+  a.n_gu = c->n_gu;
+  a.n_lm = c->n_lm;
+  a.gu_rows_max = c->gu_rows_max;
+  a.out_rows_max = c->out_rows_max;
+  a.lm_rows_max = c->lm_rows_max;
+  a.lds_b = c->lds_b;
+  a.lds_c = c->lds_c;
+  uint8_t* w = c->wsp;
+  a.tasks = (const Task*)(w + c->ws.tasks);
+  a.queue_off = (const int32_t*)(w + c->ws.queue_off);
+  uint32_t* st = (uint32_t*)(w + c->ws.state);
+  a.ctr = st + c->ws.ctr;
+  a.tickets = st + c->ws.tickets;
+  a.err = (int32_t*)(st + c->ws.err);
+  a.wtab = (const uint64_t*)(w + c->ws.wtab);
+  a.inv_freq = (const double*)(w + c->ws.inv_freq);
+  a.x = (float*)(w + c->ws.x);
+  a.qkv = (float*)(w + c->ws.qkv);
+  a.rlog = (float*)(w + c->ws.rlog);
+  a.attn_part = (float*)(w + c->ws.attn_part);
+  a.attn_out = (uint16_t*)(w + c->ws.attn_out);
+  a.h = (uint16_t*)(w + c->ws.h);
+  a.lm_part = (float*)(w + c->ws.lm_part);
+  a.sel_out = (int32_t*)(w + c->ws.sel);
+  a.k_pool = c->kpool;
+  a.v_pool = c->vpool;
+  a.n = n;
+  a.epoch = ++c->epoch;
+  a.tokens = d_tokens;
+  a.page_table = d_page_table;
+  a.seq_lens = d_seq_lens;
+  a.logits = d_logits;
+  a.next_tok = d_next_tokens;
+  a.spin_limit_ticks = (uint64_t)c->spin_us * 100;  // s_memrealtime runs at 100 MHz
+  int r = mkk_launch_step(&a, c->ncu, c->lds_bytes, (hipStream_t)stream);
+  if (r) {
+    c->epoch--;
+    return fail(MK_ERR_HIP, std::string("cooperative launch failed: ") + hipGetErrorString((hipError_t)r));
+  }
+  return MK_OK;
+}
+
+extern "C" int mk_get_error(mk_ctx* c, int32_t* code, int32_t* cu, int32_t* task, void* stream) {
+  if (!c || !code) return fail(MK_ERR_INVALID_ARG, "null argument");
+  if (!c->bound) return fail(MK_ERR_STATE, "context not bound");
+  hipStream_t s = (hipStream_t)stream;
+  int32_t ew[E_WORDS];
+  hipError_t e;
+  uint32_t* st = (uint32_t*)(c->wsp + c->ws.state);
+  if ((e = hipMemcpyAsync(ew, st + c->ws.err, sizeof ew, hipMemcpyDeviceToHost, s))) return hip_fail(e, "hipMemcpyAsync (error word)");
+  if ((e = hipStreamSynchronize(s))) return hip_fail(e, "hipStreamSynchronize (error word)");
+  *code = ew[E_CODE];
+  if (cu) *cu = ew[E_CU];
+  if (task) *task = ew[E_TASK];
+  if (ew[E_CODE] != 0 || ew[E_ABORT] != 0) {
+    c->need_reset = true;
+    int r = mkk_fill_u32(st + c->ws.err, 0u, E_WORDS, s);
+    if (r) return fail(MK_ERR_HIP, "error-word fill kernel launch failed");
+  }
+  return MK_OK;
+}
+
+extern "C" int mk_reset(mk_ctx* c, void* stream) {
+  if (!c) return fail(MK_ERR_INVALID_ARG, "null context");
+  if (!c->bound) return fail(MK_ERR_STATE, "context not bound");
+  return zero_state(c, (hipStream_t)stream);
+}

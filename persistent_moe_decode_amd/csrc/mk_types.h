@@ -1,0 +1,153 @@
+// Internal types shared by the host scheduler (mk_host.cpp) and the
+// megakernel (mk_kernel.hip): the task descriptor, counter numbering, the
+// kernel argument block and the runtime attention-split function.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define MK_HD __host__ __device__ inline
+#else
+#define MK_HD inline
+#endif
+
+namespace mk {
+
+constexpr int kThreads = 512;      // 8 wave64 per workgroup, one workgroup per CU
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxBatch = 8;
+constexpr int kMaxTopK = 8;
+constexpr int kMaxExperts = 128;
+constexpr int kMaxGroup = 8;       // q heads per kv head
+constexpr int kTaskInts = 32;      // 128-byte descriptor
+constexpr int kGuPass = 256;       // gate/up virtual rows per pass of one task
+
+enum Op : int32_t {
+  OP_PRE = 1,     // RMSNorm + rows of [Wq; Wk; Wv] or of the router
+  OP_ATTN = 2,    // paged split-KV attention chunk; last arriver of a (seq, kv head) combines
+  OP_GATEUP = 3,  // top-k + rows of the selected experts' gate/up + SwiGLU
+  OP_OUT = 4,     // rows of Wo and of the selected experts' down projection + residual
+  OP_LMHEAD = 5,  // final RMSNorm + LM head rows; last arriver takes the argmax
+};
+
+// One task: 32 int32 (128 bytes, one cache line).
+struct Task {
+  int32_t op;
+  int32_t layer;
+  int32_t wait[2];    // counter index or -1
+  int32_t fanin[2];   // signals per step on that counter
+  int32_t signal;     // counter to increment once when done, or -1
+  int32_t r0, r1;     // row range (PRE, OUT, LMHEAD)
+  int32_t idx, count; // index of this task among the op's tasks of the layer, and their number
+  int32_t pad[21];
+};
+static_assert(sizeof(Task) == kTaskInts * 4, "task descriptor is 128 bytes");
+
+// Counters: per layer l, kCtrPerLayer slots.
+enum CtrSlot : int32_t { C_QKV = 0, C_ROUTER = 1, C_ATTN = 2, C_GATEUP = 3, C_XNEXT = 4, C_DONE = 5 };
+constexpr int kCtrPerLayer = 8;
+
+MK_HD int ctr_index(int layer, int slot) { return layer * kCtrPerLayer + slot; }
+
+// Error word layout (int32): code, cu, task, aux, abort flag.
+enum ErrSlot : int32_t { E_CODE = 0, E_CU = 1, E_TASK = 2, E_AUX = 3, E_ABORT = 4, E_WORDS = 8 };
+
+struct KArgs {
+  // shape
+  int32_t L, H, nq, nkv, d, E, topk, I, V, ps, max_batch, max_pages, num_pages;
+  int32_t qkv_rows, group;
+  float eps;
+  // schedule
+  int32_t n_attn, n_gu, n_lm;
+  int32_t gu_rows_max, out_rows_max, lm_rows_max;  // largest row range of one task
+  int32_t lds_b, lds_c;                            // LDS region offsets (bytes)
+  const Task* tasks;
+  const int32_t* queue_off;
+  uint32_t* ctr;        // counters [L * kCtrPerLayer + 8]
+  uint32_t* tickets;    // attention tickets [L][max_batch][nkv], then 1 for the LM head
+  int32_t* err;         // E_WORDS
+  const uint64_t* wtab; // device pointers of the weights
+  const double* inv_freq; // [d/2]
+  // activations
+  float* x;             // [L+1][max_batch][H]
+  float* qkv;           // [L][max_batch][qkv_rows]
+  float* rlog;          // [L][max_batch][E]
+  float* attn_part;     // [L][n_attn][group*(d+2)]
+  uint16_t* attn_out;   // [L][max_batch][nq*d]
+  uint16_t* h;          // [L][max_batch*topk][I]
+  float* lm_part;       // [n_lm][max_batch][2] (value, index as float bits)
+  int32_t* sel_out;     // [L][max_batch][topk] experts chosen per token (written by gate/up task 0)
+  // KV pools
+  uint16_t* k_pool;
+  uint16_t* v_pool;
+  // step
+  int32_t n;
+  uint32_t epoch;
+  const int32_t* tokens;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  float* logits;
+  int32_t* next_tok;
+  uint64_t spin_limit_ticks; // s_memrealtime ticks (100 MHz)
+};
+
+// Weight table order.
+enum WIdx : int32_t { W_EMBED = 0, W_LM_HEAD = 1, W_FINAL_NORM = 2, W_LAYER0 = 3 };
+enum WLayer : int32_t { WL_NORM = 0, WL_QKV = 1, WL_O = 2, WL_ROUTER = 3, WL_GATE = 4, WL_UP = 5, WL_DOWN = 6, WL_COUNT = 7 };
+MK_HD int widx(int layer, int which) { return W_LAYER0 + layer * WL_COUNT + which; }
+
+// ---------------------------------------------------------------------------
+// Runtime attention split (identical on host and device).
+//
+// Every (sequence b, kv head g) pair is a segment of n_b = seq_len_b + 1
+// positions.  All segments are cut into chunks of C tokens (C a multiple of
+// the page size, so chunks start on page boundaries; the last chunk of a
+// segment is shorter), C being the smallest multiple of the page size for
+// which the number of chunks fits in n_tasks.  Chunks are numbered segment
+// by segment (b major, g minor); chunk number i goes to split task i.
+
+MK_HD int64_t attn_count_chunks(const int32_t* lens1, int n, int nkv, int64_t C) {
+  int64_t c = 0;
+  for (int b = 0; b < n; ++b) c += (int64_t)nkv * ((lens1[b] + C - 1) / C);
+  return c;
+}
+
+// lens1[b] = positions of sequence b (seq_len + 1, already clamped >= 1).
+// Requires n * nkv <= n_tasks.
+MK_HD int64_t attn_chunk_len(const int32_t* lens1, int n, int nkv, int n_tasks, int ps) {
+  int64_t maxlen = 1;
+  for (int b = 0; b < n; ++b) maxlen = lens1[b] > maxlen ? lens1[b] : maxlen;
+  int64_t hi = (maxlen + ps - 1) / ps;  // chunk = whole segment: n*nkv chunks
+  int64_t lo = 1;
+  while (lo < hi) {                      // smallest page count per chunk that fits
+    int64_t mid = (lo + hi) / 2;
+    if (attn_count_chunks(lens1, n, nkv, mid * ps) <= n_tasks) hi = mid; else lo = mid + 1;
+  }
+  return lo * ps;
+}
+
+// Chunk i -> (b, g, t0, t1); returns false for an idle task.
+MK_HD bool attn_chunk_of(const int32_t* lens1, int n, int nkv, int64_t C, int i, int* b, int* g, int* t0, int* t1,
+                         int* first_chunk, int* nchunks) {
+  int64_t base = 0;
+  for (int bb = 0; bb < n; ++bb) {
+    int64_t per = (lens1[bb] + C - 1) / C;
+    for (int gg = 0; gg < nkv; ++gg) {
+      if (i < base + per) {
+        int64_t j = i - base;
+        *b = bb;
+        *g = gg;
+        *t0 = (int)(j * C);
+        int64_t e = (j + 1) * C;
+        *t1 = (int)(e < lens1[bb] ? e : lens1[bb]);
+        *first_chunk = (int)base;
+        *nchunks = (int)per;
+        return true;
+      }
+      base += per;
+    }
+  }
+  return false;
+}
+
+}  // namespace mk

@@ -1,0 +1,180 @@
+"""Host-only checks of the C ABI library: exports, config checks, schedule, simulator, attention split.
+
+None of these make a GPU call.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import synth
+from persistent_moe_decode_amd import mk
+
+OP_PRE, OP_ATTN, OP_GATEUP, OP_OUT, OP_LMHEAD = 1, 2, 3, 4, 5
+F_OP, F_LAYER, F_WAIT0, F_WAIT1, F_FAN0, F_FAN1, F_SIGNAL, F_R0, F_R1, F_IDX, F_COUNT = range(11)
+
+
+def test_library_exports_every_declared_symbol():
+    L = mk.lib()
+    names = mk.header_symbols()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _ctx(shape, max_batch=1, max_pages=16, num_pages=16):
+    return mk.Context(mk.config_from_shape(shape, max_batch, max_pages, num_pages))
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("hidden", 200, "MK_ERR_UNSUPPORTED"), ("head_dim", 96, "MK_ERR_UNSUPPORTED"),
+    ("page_size", 32, "MK_ERR_UNSUPPORTED"), ("max_batch", 9, "MK_ERR_UNSUPPORTED"),
+    ("n_kv_heads", 3, "MK_ERR_UNSUPPORTED"), ("top_k", 9, "MK_ERR_UNSUPPORTED"),
+    ("n_layers", 0, "MK_ERR_INVALID_ARG"), ("num_pages", 0, "MK_ERR_INVALID_ARG"),
+])
+def test_create_rejects_bad_configs(field, value, code):
+    cfg = mk.config_from_shape(synth.TINY, 1, 8, 8)
+    setattr(cfg, field, value)
+    with pytest.raises(mk.MkError) as e:
+        mk.Context(cfg)
+    assert e.value.code == mk.CODES[code]
+
+
+def test_calls_out_of_order_fail_cleanly():
+    c = _ctx(synth.TINY)
+    with pytest.raises(mk.MkError) as e:
+        c.info()
+    assert e.value.code == mk.CODES["MK_ERR_STATE"]
+    c.build_schedule(64, 100)
+    with pytest.raises(mk.MkError) as e:
+        c.decode_step(1, 0, 0, 0, 0, None, 0)
+    assert e.value.code == mk.CODES["MK_ERR_STATE"]
+
+
+@pytest.mark.parametrize("name", synth.WORKLOADS)
+@pytest.mark.parametrize("ncu", [256, 80, 7])
+def test_schedule_builds_and_simulates(name, ncu):
+    w = synth.workload(name)
+    c = _ctx(w.shape, w.batch, w.max_pages_per_seq, w.num_pages)
+    if ncu < w.batch * w.shape.n_kv_heads + 1:
+        with pytest.raises(mk.MkError):
+            c.build_schedule(ncu, int(np.mean(w.context)))
+        return
+    ws = c.build_schedule(ncu, int(np.mean(w.context)))
+    info = c.info()
+    assert info.num_cus == ncu and info.workspace_bytes == ws and info.lds_bytes <= 160 * 1024
+    assert c.validate() == info.n_tasks
+    tasks, qoff = c.schedule()
+    L = w.shape.n_layers
+    ops = tasks[:, F_OP]
+    assert np.sum(ops == OP_ATTN) == L * info.n_attn
+    assert np.sum(ops == OP_GATEUP) == L * info.n_gateup
+    assert info.n_attn + info.n_gateup == ncu
+    assert info.n_attn >= w.batch * w.shape.n_kv_heads
+    # PRE rows cover [Wqkv; router] exactly once per layer; OUT rows cover hidden; LM rows cover vocab
+    for l in range(L):
+        pre = tasks[(ops == OP_PRE) & (tasks[:, F_LAYER] == l)]
+        cover = np.zeros(w.shape.qkv_rows + w.shape.n_experts, dtype=int)
+        for t in pre:
+            cover[t[F_R0]:t[F_R1]] += 1
+            assert t[F_R1] <= w.shape.qkv_rows or t[F_R0] >= w.shape.qkv_rows
+        assert np.all(cover == 1)
+        out = tasks[(ops == OP_OUT) & (tasks[:, F_LAYER] == l)]
+        cover = np.zeros(w.shape.hidden, dtype=int)
+        for t in out:
+            cover[t[F_R0]:t[F_R1]] += 1
+        assert np.all(cover == 1)
+    lm = tasks[ops == OP_LMHEAD]
+    cover = np.zeros(w.shape.vocab, dtype=int)
+    for t in lm:
+        cover[t[F_R0]:t[F_R1]] += 1
+    assert np.all(cover == 1)
+    # every queue runs layers in order
+    for q in range(ncu):
+        layers = tasks[qoff[q]:qoff[q + 1], F_LAYER]
+        assert np.all(np.diff(layers) >= 0)
+
+
+def test_schedule_is_deterministic():
+    w = synth.workload("moe30b_8k")
+    a = _ctx(w.shape, 1, w.max_pages_per_seq, w.num_pages)
+    b = _ctx(w.shape, 1, w.max_pages_per_seq, w.num_pages)
+    assert a.build_schedule(256, 8192) == b.build_schedule(256, 8192)
+    ta, qa = a.schedule()
+    tb, qb = b.schedule()
+    assert np.array_equal(ta, tb) and np.array_equal(qa, qb)
+
+
+def _tiny_table():
+    w = synth.workload("tiny")
+    c = _ctx(w.shape, 1, w.max_pages_per_seq, w.num_pages)
+    c.build_schedule(16, 128)
+    tasks, qoff = c.schedule()
+    return tasks, qoff, c.info().n_counters
+
+
+def test_simulator_accepts_the_built_table():
+    tasks, qoff, nctr = _tiny_table()
+    code, done = mk.simulate_table(tasks, qoff, nctr)
+    assert code == 0 and done == len(tasks)
+
+
+def test_simulator_catches_a_dropped_signal():
+    tasks, qoff, nctr = _tiny_table()
+    t = tasks.copy()
+    i = int(np.nonzero(t[:, F_OP] == OP_PRE)[0][0])
+    t[i, F_SIGNAL] = -1
+    code, _ = mk.simulate_table(t, qoff, nctr)
+    assert code == mk.CODES["MK_ERR_SCHEDULE"]
+
+
+def test_simulator_catches_consumer_before_producer():
+    tasks, qoff, nctr = _tiny_table()
+    t = tasks.copy()
+    # on queue 0, put the OUT task of layer 0 before its own PRE task
+    q = t[qoff[0]:qoff[1]]
+    i_pre = int(np.nonzero((q[:, F_OP] == OP_PRE) & (q[:, F_LAYER] == 0))[0][0])
+    i_out = int(np.nonzero((q[:, F_OP] == OP_OUT) & (q[:, F_LAYER] == 0))[0][0])
+    q[[i_pre, i_out]] = q[[i_out, i_pre]]
+    t[qoff[0]:qoff[1]] = q
+    code, done = mk.simulate_table(t, qoff, nctr)
+    assert code == mk.CODES["MK_ERR_SCHEDULE"] and done < len(t)
+
+
+def test_simulator_catches_wrong_fanin():
+    tasks, qoff, nctr = _tiny_table()
+    t = tasks.copy()
+    i = int(np.nonzero(t[:, F_OP] == OP_OUT)[0][0])
+    t[i, F_FAN0] -= 1
+    code, _ = mk.simulate_table(t, qoff, nctr)
+    assert code == mk.CODES["MK_ERR_SCHEDULE"]
+
+
+@pytest.mark.parametrize("lens,nkv,ntasks", [
+    ([0], 4, 64), ([8192], 4, 64), ([8192], 4, 85), ([15], 2, 64), ([16], 2, 64), ([17], 2, 3),
+    ([262144], 4, 256), ([1024, 32768, 7, 0, 16, 15, 17, 5000], 4, 40), ([3, 3, 3], 1, 3),
+])
+def test_attention_split_partitions_every_segment(lens, nkv, ntasks):
+    C, plan = mk.attn_plan(lens, nkv, ntasks)
+    assert C % 16 == 0 and C >= 16
+    seen = {}
+    for i, (b, g, t0, t1) in enumerate(plan):
+        if b < 0:
+            continue
+        assert t0 % 16 == 0 and 0 <= t0 < t1 <= lens[b] + 1 and t1 - t0 <= C
+        seen.setdefault((b, g), []).append((t0, t1, i))
+    assert len(seen) == len(lens) * nkv
+    for (b, g), chunks in seen.items():
+        chunks.sort()
+        assert chunks[0][0] == 0 and chunks[-1][1] == lens[b] + 1
+        for (a0, a1, ia), (b0, b1, ib) in zip(chunks, chunks[1:]):
+            assert a1 == b0 and ib == ia + 1          # contiguous, consecutive task numbers
+    # C is the smallest page multiple that fits: one page less would need more than ntasks chunks
+    if C > 16:
+        need = sum(nkv * -(-(l + 1) // (C - 16)) for l in lens)
+        assert need > ntasks
+
+
+def test_attention_split_rejects_too_few_tasks():
+    with pytest.raises(mk.MkError):
+        mk.attn_plan([10, 10], 4, 7)
