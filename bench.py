@@ -1,0 +1,211 @@
+"""Decode throughput of the persistent megakernel on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+Default workload: the 30B-total / 3.3B-active shape (48 layers, hidden 2048,
+32 q / 4 kv heads of 128, 128 experts top-8 with intermediate 768, vocab
+151936), batch 1, 8192 cached tokens of synthetic KV, random-init BF16
+weights from the seeded generator.  A step is one whole decode step: one
+launch of the megakernel, whose device argmax feeds the next step's token;
+sequence lengths for every step are precomputed on the device, so nothing
+but decode launches sits in the timed region.
+
+Prints one JSON line (rank 0): tok/s, the megakernel's achieved HBM
+bandwidth (algorithmic bytes per step / average launch time, timed with
+events on the launch stream) against MI355X's 8 TB/s, and the CPU oracle's
+rate on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "decode tok/s at bs=1 8K ctx; achieved HBM GB/s as % of MI355X peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("mk_kernel.hip", "mk_host.cpp", "mk_types.h"):
+        with open(os.path.join(ROOT, "persistent_moe_decode_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they match this kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def step_bytes_kernel(shape, seq_lens, distinct):
+    """Algorithmic HBM bytes one decode step reads: active weights (one embedding row per token) + KV 0..p."""
+    H = shape.hidden
+    w = shape.active_weight_bytes(distinct) + 2.0 * H * len(seq_lens)
+    kv = sum(shape.kv_bytes_per_token() * (int(p) + 1) for p in seq_lens)
+    return w + kv
+
+
+def cpu_baseline(w, budget_s: float = 25.0):
+    """The CPU oracle, untuned, on a bounded sample: decode steps until ~budget_s of CPU time."""
+    import numpy as np
+
+    import synth
+    from oracle import oracle as O
+
+    W = O.Weights(w.shape, budget_bytes=float(2 ** 36))
+    pt = w.page_table()
+    kv = O.PagedKV(w.shape, w.num_pages)
+    kv.fill_synthetic(pt, w.context)
+    toks = [int(w.prompt(b)[w.context[b]]) for b in range(w.batch)]
+    # one untimed step populates the weight cache with everything but newly routed experts
+    out = O.decode_step(W, kv, toks, pt, list(w.context))
+    toks = [int(t) for t in out.next_token]
+    n, t0 = 0, time.perf_counter()
+    while True:
+        lens = [c + 1 + n for c in w.context]
+        out = O.decode_step(W, kv, toks, pt, lens)
+        toks = [int(t) for t in out.next_token]
+        n += 1
+        if time.perf_counter() - t0 > budget_s or n >= 16:
+            break
+    dt = time.perf_counter() - t0
+    try:
+        import threadpoolctl
+        cores = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        cores = os.cpu_count() or 1
+    return {"value": round(w.batch * n / dt, 4), "unit": "tok/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} decode step(s) of {w.name} (batch {w.batch}, context {w.context[0] if w.batch == 1 else 'ragged'}) "
+                      f"after one warm-up step; float64 numpy, expert weights regenerated when first routed"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="moe30b_8k")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=25.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one MI355X: the decode megakernel runs on a single GPU; "
+              "multi-GPU runs are not part of this build (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from persistent_moe_decode_amd.runtime import DeviceDecoder
+
+    w = synth.workload(args.workload)
+    total = args.warmup + args.steps
+    if total > w.steps:
+        w.steps = total  # page capacity for every position the run writes
+    t0 = time.time()
+    dec = DeviceDecoder(w)
+    dec.fill_synthetic_kv()
+    log(f"[bench] setup {time.time() - t0:.1f}s, {dec.info.num_cus} CUs, n_attn {dec.info.n_attn}, "
+        f"lds {dec.info.lds_bytes} B, workspace {dec.ws_bytes / 2**20:.1f} MiB")
+    dev = dec.dev
+    B = w.batch
+    ctx = torch.tensor(w.context, dtype=torch.int32, device=dev)
+    lens_all = torch.stack([ctx + i for i in range(total)]).contiguous()  # [step][B]
+    toks = [torch.tensor([int(w.prompt(b)[w.context[b]]) for b in range(B)], dtype=torch.int32, device=dev),
+            torch.zeros(B, dtype=torch.int32, device=dev)]
+    stream = torch.cuda.current_stream(dev)
+
+    def run(i):
+        dec.ctx.decode_step(B, toks[i % 2].data_ptr(), dec.page_table.data_ptr(), lens_all[i].data_ptr(),
+                            dec.logits.data_ptr(), toks[(i + 1) % 2].data_ptr(), dec.stream)
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize(dev)
+    dec.check_error()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    e0.record(stream)
+    for i in range(args.warmup, total):
+        run(i)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    dec.check_error()
+    ms = e0.elapsed_time(e1)
+    ms_step = ms / args.steps
+    tok_s = B * args.steps / (ms / 1e3)
+
+    # algorithmic bytes over the timed steps: distinct experts per layer from the routing of each step
+    sel = dec.sel()[:, :B, :]
+    distinct = np.mean([len(set(sel[l].reshape(-1).tolist())) for l in range(w.shape.n_layers)])
+    bytes_tot = sum(step_bytes_kernel(w.shape, [c + i for c in w.context], distinct)
+                    for i in range(args.warmup, total))
+    bytes_step = bytes_tot / args.steps
+    gbs = bytes_step / (ms_step / 1e3) / 1e9
+    traffic = measured_traffic(args.workload)
+    log(f"[bench] {ms_step:.3f} ms/step, {tok_s:.1f} tok/s, {bytes_step / 1e9:.4f} GB/step, {gbs:.0f} GB/s "
+        f"({100 * gbs / PEAK_HBM_GBS:.1f}% of peak)")
+
+    cpu = None
+    if not args.no_cpu:
+        t1 = time.time()
+        cpu = cpu_baseline(w, args.cpu_budget)
+        log(f"[bench] cpu baseline {cpu['value']} tok/s ({time.time() - t1:.0f}s)")
+
+    s = w.shape
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded random-init weights N(0, 0.02), synthetic N(0, 1) KV, shuffled pages",
+        "config": {
+            "workload": f"{w.name}: {s.n_layers} layers, hidden {s.hidden}, {s.n_q_heads}q/{s.n_kv_heads}kv x "
+                        f"{s.head_dim}, {s.n_experts} experts top-{s.top_k} inter {s.inter}, vocab {s.vocab}; "
+                        f"batch {B}, context {w.context if B > 1 else w.context[0]}, page {s.page_size}",
+            "batch": B,
+            "context": w.context[0] if B == 1 else w.context,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": round(bytes_step),
+            "kernel": "mk_megakernel",
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

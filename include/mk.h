@@ -132,6 +132,15 @@ int mk_reset(mk_ctx* ctx, void* stream);
  * Host only; applies from the next step. */
 int mk_set_spin_limit_us(mk_ctx* ctx, int64_t microseconds);
 
+/* Test hook for checking each layer in isolation: when d_x is not NULL,
+ * every layer l >= 1 and the final RMSNorm read their input residual from
+ * the caller's device buffer d_x (float [n_layers+1][max_batch][hidden],
+ * slot 0 unused) instead of the residual the previous layer wrote, so each
+ * layer runs on inputs the caller chose (e.g. a reference implementation's).
+ * Layer outputs are still written to the workspace (mk_get_ws_offsets).
+ * NULL restores normal operation.  Host only; applies from the next step. */
+int mk_set_layer_inputs(mk_ctx* ctx, const float* d_x);
+
 const char* mk_last_error_message(void);
 void mk_destroy(mk_ctx* ctx);
 

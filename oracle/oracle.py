@@ -207,16 +207,28 @@ class StepOut:
     margin: np.ndarray                      # [L][B] float: r_(k) - r_(k+1) (inf when k == E)
     next_token: np.ndarray                  # [B] int64 greedy argmax
     top2_gap: np.ndarray                    # [B] logit gap between best and second best
+    sel_alt: np.ndarray = None              # [L][B][k] the set with the k-th and (k+1)-th exchanged
     trace: dict = field(default_factory=dict)
 
 
-def decode_step(W: Weights, kv: PagedKV, tokens, page_table, seq_lens, trace: bool = False) -> StepOut:
+ROUTE_TIE = 1e-3   # router margin below which either expert set is a correct result
+
+
+def decode_step(W: Weights, kv: PagedKV, tokens, page_table, seq_lens, trace: bool = False,
+                route_alt=None) -> StepOut:
     """One decode step for a ragged batch.
 
     tokens[b] is the new token of sequence b; seq_lens[b] tokens are already in
     the cache, so the new token sits at position p = seq_lens[b].  Its K/V are
     written to the cache, and attention runs over positions 0..p.
+
+    route_alt: (layer, b) pairs at which the step takes the other correct
+    routing: where the k-th and (k+1)-th router logits lie within ROUTE_TIE
+    of each other, a decoder computing in a different precision may pick
+    either, so the set with those two exchanged is also a correct result.
+    Only valid at such near-ties (checked).
     """
+    route_alt = route_alt or set()
     s = W.shape
     L, H, d, E, k = s.n_layers, s.hidden, s.head_dim, s.n_experts, s.top_k
     nq, nkv = s.n_q_heads, s.n_kv_heads
@@ -225,6 +237,7 @@ def decode_step(W: Weights, kv: PagedKV, tokens, page_table, seq_lens, trace: bo
     logits = np.zeros((B, s.vocab))
     rl = np.zeros((L, B, E), dtype=np.float32)
     sel_all = np.zeros((L, B, k), dtype=np.int64)
+    sel_alt = np.full((L, B, k), -1, dtype=np.int64)
     margin = np.zeros((L, B))
     tr: dict = {}
     for b in range(B):
@@ -252,6 +265,14 @@ def decode_step(W: Weights, kv: PagedKV, tokens, page_table, seq_lens, trace: bo
             # MoE path, from the same normalized input
             r = (W.get(synth.K_ROUTER, l) @ xn).astype(np.float32)
             sel = topk_desc(r, k)
+            if k < E:
+                ext = topk_desc(r, k + 1)
+                alt = np.concatenate([ext[: k - 1], ext[k:]])
+                sel_alt[l, b] = alt
+                if (l, b) in route_alt:
+                    if not float(r[ext[k - 1]]) - float(r[ext[k]]) <= ROUTE_TIE:
+                        raise ValueError(f"layer {l} seq {b}: no routing near-tie to take the alternative of")
+                    sel = alt
             wsel = softmax(r[sel].astype(np.float64))
             moe = np.zeros(H)
             hs = []
@@ -286,7 +307,7 @@ def decode_step(W: Weights, kv: PagedKV, tokens, page_table, seq_lens, trace: bo
     nxt = np.argmax(logits, axis=1)
     srt = np.sort(logits, axis=1)
     gap = srt[:, -1] - srt[:, -2]
-    return StepOut(logits, rl, sel_all, margin, nxt, gap, tr)
+    return StepOut(logits, rl, sel_all, margin, nxt, gap, sel_alt, tr)
 
 
 def prefill_as_decode(W: Weights, kv: PagedKV, prompt, page_table_row) -> StepOut:

@@ -64,6 +64,7 @@ struct mk_ctx {
   uint16_t* vpool = nullptr;
   uint32_t epoch = 0;
   int64_t spin_us = 2000000;
+  const float* x_in = nullptr;
 };
 
 static int check_config(const mk_config& c) {
@@ -443,6 +444,13 @@ extern "C" int mk_get_ws_offsets(const mk_ctx* c, mk_ws_offsets* out) {
   return MK_OK;
 }
 
+extern "C" int mk_set_layer_inputs(mk_ctx* c, const float* d_x) {
+  if (!c) return fail(MK_ERR_INVALID_ARG, "null context");
+  if (d_x && ((uintptr_t)d_x) % 4) return fail(MK_ERR_INVALID_ARG, "layer inputs not 4-byte aligned");
+  c->x_in = d_x;
+  return MK_OK;
+}
+
 extern "C" int mk_set_spin_limit_us(mk_ctx* c, int64_t us) {
   if (!c || us < 1) return fail(MK_ERR_INVALID_ARG, "bad spin limit");
   c->spin_us = us;
@@ -553,6 +561,7 @@ extern "C" int mk_decode_step(mk_ctx* c, int32_t n, const int32_t* d_tokens, con
   a.h = (uint16_t*)(w + c->ws.h);
   a.lm_part = (float*)(w + c->ws.lm_part);
   a.sel_out = (int32_t*)(w + c->ws.sel);
+  a.x_in = c->x_in;
   a.k_pool = c->kpool;
   a.v_pool = c->vpool;
   a.n = n;

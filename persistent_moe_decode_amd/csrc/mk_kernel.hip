@@ -210,8 +210,12 @@ DEV const uint16_t* token_row(const KArgs& a, int b, int task) {
 }
 
 // Residual entering `layer` (layer 0: the embedding row).
+// With the layer-input hook set, layers >= 1 (and the final norm) read the
+// residual the caller supplied instead of the one the previous layer wrote.
 DEV float load_x(const KArgs& a, int layer, int b, int i, const uint16_t* emb) {
-  return layer == 0 ? bf2f(emb[i]) : a.x[((size_t)layer * a.max_batch + b) * a.H + i];
+  if (layer == 0) return bf2f(emb[i]);
+  const float* src = a.x_in ? a.x_in : a.x;
+  return src[((size_t)layer * a.max_batch + b) * a.H + i];
 }
 
 // xs[b][H] = bf16(x_b / sqrt(mean(x_b^2) + eps) * g) for b < n.

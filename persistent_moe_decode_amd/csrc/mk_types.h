@@ -77,6 +77,7 @@ struct KArgs {
   uint16_t* h;          // [L][max_batch*topk][I]
   float* lm_part;       // [n_lm][max_batch][2] (value, index as float bits)
   int32_t* sel_out;     // [L][max_batch][topk] experts chosen per token (written by gate/up task 0)
+  const float* x_in;    // test hook: layer inputs [L+1][max_batch][H] read instead of x (NULL = off)
   // KV pools
   uint16_t* k_pool;
   uint16_t* v_pool;

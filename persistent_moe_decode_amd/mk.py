@@ -77,6 +77,7 @@ def lib():
         "mk_get_error": [P, pi32, pi32, pi32, P],
         "mk_reset": [P, P],
         "mk_set_spin_limit_us": [P, I64],
+        "mk_set_layer_inputs": [P, P],
         "mk_get_schedule_info": [P, ctypes.POINTER(ScheduleInfo)],
         "mk_copy_schedule": [P, pi32, I64, pi32, I64],
         "mk_validate_schedule": [P, pi32],
@@ -184,6 +185,9 @@ class Context:
 
     def reset(self, stream: int):
         check(lib().mk_reset(self.h, stream), "mk_reset")
+
+    def set_layer_inputs(self, ptr: int | None):
+        check(lib().mk_set_layer_inputs(self.h, ptr or None), "mk_set_layer_inputs")
 
     def set_spin_limit_us(self, us: int):
         check(lib().mk_set_spin_limit_us(self.h, us), "mk_set_spin_limit_us")

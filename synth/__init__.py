@@ -59,7 +59,7 @@ def build_lib(force: bool = False) -> str:
     src = os.path.join(_HERE, "synth.c")
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src):
         tmp = _LIB_PATH + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c99",
+        subprocess.check_call(["gcc", "-O3", "-fPIC", "-shared", "-fopenmp", "-std=c99",
                                "-o", tmp, src, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH

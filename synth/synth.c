@@ -68,7 +68,7 @@ void synth_normal_bf16(uint64_t seed, uint64_t tid, uint64_t start, uint64_t cou
   const uint64_t key = synth_key(seed, tid);
   const float c = synth_normal_scale(sigma);
   int64_t n = (int64_t)count;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (n > 262144)
   for (int64_t j = 0; j < n; ++j) {
     float s = (float)irwin_hall(word_at(key, start + (uint64_t)j));
     out[j] = f32_to_bf16_rne(s * c);
@@ -81,7 +81,7 @@ void synth_gain_bf16(uint64_t seed, uint64_t tid, uint64_t start, uint64_t count
   const uint64_t key = synth_key(seed, tid);
   const float c = synth_normal_scale(sigma);
   int64_t n = (int64_t)count;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (n > 262144)
   for (int64_t j = 0; j < n; ++j) {
     float s = (float)irwin_hall(word_at(key, start + (uint64_t)j));
     float t = s * c;
@@ -94,7 +94,7 @@ void synth_uniform_u32(uint64_t seed, uint64_t tid, uint64_t start, uint64_t cou
                        uint32_t n, uint32_t* out) {
   const uint64_t key = synth_key(seed, tid);
   int64_t m = (int64_t)count;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (m > 262144)
   for (int64_t j = 0; j < m; ++j) {
     uint64_t w = word_at(key, start + (uint64_t)j);
     out[j] = (uint32_t)(((w >> 32) * (uint64_t)n) >> 32);

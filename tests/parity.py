@@ -1,14 +1,37 @@
 """Step-by-step comparison of the GPU decode (through the C ABI) with the CPU oracle.
 
-Protocol, per step:
-  * logits: per sequence, max_i |gpu_i - oracle_i| / max_i |oracle_i| <= LOGIT_TOL;
-  * expert choice: bit-exact wherever the oracle's k-th / (k+1)-th router margin
-    exceeds MARGIN (1e-3); below it either set is a correct result and the
-    flip is only counted;
-  * greedy token: equal unless the oracle's top-1 / top-2 gap is within
-    GAP_FACTOR times the step's largest absolute logit difference;
-  * both sides are fed the oracle's greedy token (teacher forcing), each side
-    keeps its own KV cache.
+Why two modes.  The decoder rounds to bfloat16 at several points per layer
+(xn, q/k/v, attention output, expert hidden).  Any change of accumulation
+order (fp32 on the GPU, fp64 in the oracle) moves a pre-rounding value across
+a rounding boundary now and then; the one-ulp flip shifts the residual by
+~1e-5, which flips the rounding of ~2% of the next layer's xn, and the
+difference grows ~20x per layer until it settles near 5e-3 relative.  So a
+free-running comparison of many layers cannot keep router decisions
+identical at 1e-3 margins; a layer-by-layer one can.
+
+isolated (the strict check): each step, the oracle runs first and its
+  residual entering every layer is handed to the GPU through the layer-input
+  hook (oracle -> GPU only), so every layer of the GPU runs on the oracle's
+  inputs.  Per layer: expert choice bit-exact wherever the oracle's k-th /
+  (k+1)-th margin exceeds MARGIN (else the GPU's set must be one of the two
+  correct ones); router logits within ROUTER_TOL; the layer's output
+  residual within X_TOL; the new K/V entries within one bfloat16 ulp (plus
+  KV_ABS of the head vector's largest entry, for entries that cancel to
+  almost nothing, where fp32 accumulation error alone exceeds an ulp).
+  Logits within LOGIT_TOL; greedy token equal unless the oracle's top-2 gap
+  is within GAP_FACTOR times the step's largest logit difference.
+
+free (end to end): each side keeps its own state.  Where the expert choice
+  first differs at a margin above MARGIN, the GPU's set must still be a
+  correct top-k for the oracle's logits perturbed by twice the measured
+  router-logit difference at that layer (the drift described above), and
+  the step's logits are not compared; all other steps meet LOGIT_TOL and
+  the greedy rule.  At near-ties the oracle recomputes the step down the
+  branch the GPU took (the oracle's own alternative, never GPU values).
+  Both modes check every layer's GPU expert choice against the exact top-k
+  of the GPU's own router logits (the kernel's integer logic, bit-exact).
+
+Both sides are fed the oracle's greedy token (teacher forcing).
 """
 from __future__ import annotations
 
@@ -24,14 +47,21 @@ from oracle import oracle as O
 LOGIT_TOL = 2e-2
 MARGIN = 1e-3
 GAP_FACTOR = 4.0
+ROUTER_TOL = 5e-4    # isolated mode: |router logit| difference per layer
+X_TOL = 2e-3         # isolated mode: max|dx| / max|x| of each layer's output residual
+KV_ABS = 1e-5        # isolated mode: new K/V slack beyond one ulp, relative to the head vector's max
 
 
 @dataclass
 class Report:
     steps: int = 0
     max_rel: float = 0.0
+    max_router: float = 0.0
+    max_x: float = 0.0
     route_checked: int = 0
     route_ties: int = 0
+    cascade_steps: int = 0
+    kv_checked: int = 0
     greedy_checked: int = 0
     greedy_excused: int = 0
     failures: list = field(default_factory=list)
@@ -39,75 +69,207 @@ class Report:
     def ok(self) -> bool:
         return not self.failures
 
+    def summary(self) -> str:
+        return (f"steps {self.steps} logits max_rel {self.max_rel:.2e} router max {self.max_router:.2e} "
+                f"x max_rel {self.max_x:.2e} routes {self.route_checked} ties {self.route_ties} "
+                f"cascade-steps {self.cascade_steps} kv {self.kv_checked} greedy {self.greedy_checked} "
+                f"excused {self.greedy_excused}")
 
-def compare_step(rep: Report, tag: str, dec, ref, n: int) -> None:
-    torch.cuda.synchronize()
-    dec.check_error()
-    got = dec.logits[:n].cpu().numpy().astype(np.float64)
-    rep.steps += 1
-    for b in range(n):
-        o = ref.logits[b]
-        diff = np.abs(got[b] - o)
-        rel = float(diff.max() / np.abs(o).max())
-        rep.max_rel = max(rep.max_rel, rel)
-        if not rel <= LOGIT_TOL:
-            rep.failures.append(f"{tag} seq {b}: logit rel err {rel:.3e}")
-        gtok = int(np.argmax(got[b]))
-        rep.greedy_checked += 1
-        if gtok != int(ref.next_token[b]):
-            if ref.top2_gap[b] <= GAP_FACTOR * diff.max():
-                rep.greedy_excused += 1
-            else:
-                rep.failures.append(f"{tag} seq {b}: greedy {gtok} vs {int(ref.next_token[b])} "
-                                    f"(gap {ref.top2_gap[b]:.3e}, max diff {diff.max():.3e})")
-    sel = dec.sel()
-    L = ref.sel.shape[0]
-    for l in range(L):
+
+def _topk(r: np.ndarray, k: int) -> list:
+    return sorted(np.argsort(-r.astype(np.float64), kind="stable")[:k].tolist())
+
+
+def _admissible(r_or: np.ndarray, chosen: list, k: int, delta: float) -> bool:
+    """True if `chosen` is a top-k of r_or perturbed by at most delta/2 per entry."""
+    others = [i for i in range(len(r_or)) if i not in chosen]
+    return min(float(r_or[i]) for i in chosen) >= max(float(r_or[j]) for j in others) - delta
+
+
+def _check_logits(rep, tag, got, ref, b):
+    o = ref.logits[b]
+    diff = np.abs(got - o)
+    rel = float(diff.max() / np.abs(o).max())
+    rep.max_rel = max(rep.max_rel, rel)
+    if not rel <= LOGIT_TOL:
+        rep.failures.append(f"{tag} seq {b}: logit rel err {rel:.3e}")
+    rep.greedy_checked += 1
+    gtok = int(np.argmax(got))
+    if gtok != int(ref.next_token[b]):
+        if ref.top2_gap[b] <= GAP_FACTOR * diff.max():
+            rep.greedy_excused += 1
+        else:
+            rep.failures.append(f"{tag} seq {b}: greedy {gtok} vs {int(ref.next_token[b])} "
+                                f"(gap {ref.top2_gap[b]:.3e}, max diff {diff.max():.3e})")
+
+
+def _self_consistent(rep, tag, sel, rl, n, k):
+    for l in range(sel.shape[0]):
         for b in range(n):
-            rep.route_checked += 1
-            a = sorted(sel[l, b].tolist())
-            e = sorted(ref.sel[l, b].tolist())
-            if a != e:
-                if ref.margin[l, b] <= MARGIN:
-                    rep.route_ties += 1
-                else:
-                    rep.failures.append(f"{tag} layer {l} seq {b}: experts {a} vs {e} (margin {ref.margin[l, b]:.2e})")
+            if sorted(sel[l, b].tolist()) != _topk(rl[l, b], k):
+                rep.failures.append(f"{tag} layer {l} seq {b}: GPU experts {sorted(sel[l, b].tolist())} are not "
+                                    f"the top-{k} of its own router logits")
 
 
-def run(w: synth.Workload, steps: int | None = None, dec=None, W=None, log=print) -> Report:
-    """Run `steps` decode steps of workload w on both sides; returns the report."""
-    from persistent_moe_decode_amd.runtime import DeviceDecoder
+def oracle_step(W, kv, toks, pt, lens, gpu_sel, n: int, trace=False):
+    """Oracle step on the correct routing branch the GPU took at each near-tie."""
+    alts = set()
+    L = W.shape.n_layers
+    while True:
+        ref = O.decode_step(W, kv, toks, pt, lens, trace=trace, route_alt=alts)
+        new = None
+        for b in range(n):
+            for l in range(L):
+                if sorted(gpu_sel[l, b].tolist()) != sorted(ref.sel[l, b].tolist()):
+                    if (ref.margin[l, b] <= MARGIN and (l, b) not in alts
+                            and sorted(gpu_sel[l, b].tolist()) == sorted(ref.sel_alt[l, b].tolist())):
+                        new = (l, b)
+                    break  # later layers follow from this one
+            if new:
+                break
+        if new is None or len(alts) >= 8:
+            return ref, alts
+        alts.add(new)
 
-    steps = w.steps if steps is None else steps
-    t0 = time.time()
-    dec = dec or DeviceDecoder(w)
-    W = W or O.Weights(w.shape, budget_bytes=float(2 ** 36))
-    pt = w.page_table()
-    kv = O.PagedKV(w.shape, w.num_pages)
-    rep = Report()
-    n = w.batch
-    if w.kv_mode == "synthetic":
-        dec.fill_synthetic_kv()
-        kv.fill_synthetic(pt, w.context)
-        toks = [int(w.prompt(b)[w.context[b]]) for b in range(n)]
-    else:
-        # prompt fed one decode step at a time on both sides
-        assert n == 1
-        prompt = w.prompt(0)[: w.context[0]]
-        ref = None
-        for t, tok in enumerate(prompt):
-            dec.step([int(tok)], [t])
-            ref = O.decode_step(W, kv, [int(tok)], pt, [t])
-            compare_step(rep, f"prefill {t}", dec, ref, n)
-        toks = [int(ref.next_token[0])]
-    log(f"[parity {w.name}] setup+prefill {time.time() - t0:.1f}s")
-    for step in range(steps):
-        lens = [c + step for c in w.context]
+
+class Runner:
+    """Both sides of one workload, stepped together."""
+
+    def __init__(self, w: synth.Workload, dec=None, log=print):
+        from persistent_moe_decode_amd.runtime import DeviceDecoder
+
+        self.w, self.log = w, log
+        t0 = time.time()
+        self.dec = dec or DeviceDecoder(w)
+        self.W = O.Weights(w.shape, budget_bytes=float(2 ** 36))
+        self.pt = w.page_table()
+        self.kv = O.PagedKV(w.shape, w.num_pages)
+        self.rep = Report()
+        self.n = w.batch
+        s = w.shape
+        self.x_inj = None
+        if w.kv_mode == "synthetic":
+            self.dec.fill_synthetic_kv()
+            self.kv.fill_synthetic(self.pt, w.context)
+        log(f"[parity {w.name}] setup {time.time() - t0:.1f}s")
+        self.t0 = time.time()
+
+    # -------------------------------------------------------------- free running
+
+    def step_free(self, toks, lens, tag):
+        rep, dec, n, k = self.rep, self.dec, self.n, self.w.shape.top_k
         dec.step(toks, lens)
-        ref = O.decode_step(W, kv, toks, pt, lens)
-        compare_step(rep, f"step {step}", dec, ref, n)
-        toks = [int(x) for x in ref.next_token]
-        if step % 8 == 0:
-            log(f"[parity {w.name}] step {step} max_rel {rep.max_rel:.3e} ties {rep.route_ties} "
-                f"{time.time() - t0:.1f}s")
-    return rep
+        torch.cuda.synchronize()
+        dec.check_error()
+        sel, rl = dec.sel()[:, :n], dec.router_logits()[:, :n]
+        ref, alts = oracle_step(self.W, self.kv, toks, self.pt, lens, sel, n)
+        rep.steps += 1
+        rep.route_ties += len(alts)
+        _self_consistent(rep, tag, sel, rl, n, k)
+        got = dec.logits[:n].cpu().numpy().astype(np.float64)
+        for b in range(n):
+            diverged = False
+            for l in range(self.w.shape.n_layers):
+                rep.route_checked += 1
+                a, e = sorted(sel[l, b].tolist()), sorted(ref.sel[l, b].tolist())
+                if a == e:
+                    continue
+                drift = float(np.max(np.abs(rl[l, b] - ref.router_logits[l, b])))
+                if not _admissible(ref.router_logits[l, b], a, k, max(2 * drift, MARGIN)):
+                    rep.failures.append(f"{tag} layer {l} seq {b}: experts {a} vs {e} (margin "
+                                        f"{ref.margin[l, b]:.2e}, router drift {drift:.2e})")
+                diverged = True
+                break
+            if diverged:
+                rep.cascade_steps += 1
+            else:
+                _check_logits(rep, tag, got[b], ref, b)
+        return ref
+
+    # -------------------------------------------------------------- isolated layers
+
+    def step_isolated(self, toks, lens, tag):
+        rep, dec, n, s = self.rep, self.dec, self.n, self.w.shape
+        L, k = s.n_layers, s.top_k
+        ref = O.decode_step(self.W, self.kv, toks, self.pt, lens, trace=True)
+        mb = dec.ctx.cfg.max_batch
+        if self.x_inj is None:
+            self.x_inj = torch.zeros((L + 1, mb, s.hidden), dtype=torch.float32, device=dec.dev)
+            dec.ctx.set_layer_inputs(self.x_inj.data_ptr())
+        host = np.zeros((L + 1, mb, s.hidden), dtype=np.float32)
+        for b in range(n):
+            for l in range(1, L):
+                host[l, b] = ref.trace["x_in"][(l, b)]
+            host[L, b] = ref.trace["x_final"][b]
+        self.x_inj.copy_(torch.from_numpy(host))
+        dec.step(toks, lens)
+        torch.cuda.synchronize()
+        dec.check_error()
+        rep.steps += 1
+        sel, rl, xs = dec.sel()[:, :n], dec.router_logits()[:, :n], dec.residual()[:, :n]
+        _self_consistent(rep, tag, sel, rl, n, k)
+        got = dec.logits[:n].cpu().numpy().astype(np.float64)
+        for b in range(n):
+            p = int(lens[b])
+            for l in range(L):
+                rep.route_checked += 1
+                dr = float(np.max(np.abs(rl[l, b] - ref.router_logits[l, b])))
+                rep.max_router = max(rep.max_router, dr)
+                if not dr <= ROUTER_TOL:
+                    rep.failures.append(f"{tag} layer {l} seq {b}: router logits differ by {dr:.2e}")
+                a, e = sorted(sel[l, b].tolist()), sorted(ref.sel[l, b].tolist())
+                took_alt = False
+                if a != e:
+                    if ref.margin[l, b] <= MARGIN and a == sorted(ref.sel_alt[l, b].tolist()):
+                        rep.route_ties += 1
+                        took_alt = True
+                    else:
+                        rep.failures.append(f"{tag} layer {l} seq {b}: experts {a} vs {e} (margin {ref.margin[l, b]:.2e})")
+                # the layer's output residual
+                xo = ref.trace["x_in"][(l + 1, b)] if l + 1 < L else ref.trace["x_final"][b]
+                if not took_alt:
+                    rx = float(np.max(np.abs(xs[l + 1, b] - xo)) / np.max(np.abs(xo)))
+                    rep.max_x = max(rep.max_x, rx)
+                    if not rx <= X_TOL:
+                        rep.failures.append(f"{tag} layer {l} seq {b}: output residual rel err {rx:.2e}")
+                # the new K/V entries: within one bfloat16 ulp, plus the fp32 accumulation
+                # error of the projection (KV_ABS of the head vector's scale) for entries
+                # that cancel to almost nothing
+                kg, vg = dec.kv_at(l, b, p)
+                for name, g16, o64 in (("k", kg, ref.trace["k16"][(l, b)]), ("v", vg, ref.trace["v16"][(l, b)])):
+                    gv = O.bf16_to_f64(g16)
+                    ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(o64), 1e-30))[1] - 8)
+                    scale = np.max(np.abs(o64), axis=-1, keepdims=True)
+                    bad = np.abs(gv - o64) > ulp * 1.0000001 + KV_ABS * scale
+                    rep.kv_checked += gv.size
+                    if np.any(bad):
+                        rep.failures.append(f"{tag} layer {l} seq {b}: new {name} off by more than one ulp "
+                                            f"at {int(bad.sum())} entries")
+            _check_logits(rep, tag, got[b], ref, b)
+        return ref
+
+    # -------------------------------------------------------------- driver
+
+    def run(self, steps: int, mode: str) -> Report:
+        w, rep, n = self.w, self.rep, self.n
+        step_fn = self.step_isolated if mode == "isolated" else self.step_free
+        if w.kv_mode == "synthetic":
+            toks = [int(w.prompt(b)[w.context[b]]) for b in range(n)]
+        else:
+            assert n == 1
+            ref = None
+            for t, tok in enumerate(w.prompt(0)[: w.context[0]]):
+                ref = step_fn([int(tok)], [t], f"prefill {t}")
+            toks = [int(ref.next_token[0])]
+            self.log(f"[parity {w.name}] prefill done {time.time() - self.t0:.1f}s")
+        for step in range(steps):
+            lens = [c + step for c in w.context]
+            ref = step_fn(toks, lens, f"step {step}")
+            toks = [int(x) for x in ref.next_token]
+            if step % 8 == 0 or step == steps - 1:
+                self.log(f"[parity {w.name} {mode}] step {step}: {rep.summary()} {time.time() - self.t0:.1f}s")
+        return rep
+
+
+def run(w: synth.Workload, steps: int | None = None, mode: str = "isolated", log=print) -> Report:
+    return Runner(w, log=log).run(w.steps if steps is None else steps, mode)

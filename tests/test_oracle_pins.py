@@ -365,3 +365,20 @@ def test_non_square_shape_catches_transposed_operands():
     for t, tok in enumerate((1, 150, 7)):
         out = O.decode_step(W, kv, [tok], np.array([[1, 0]], dtype=np.int32), [t])
     assert out.logits.shape == (1, 200) and np.all(np.isfinite(out.logits))
+
+
+def test_route_alternative_only_at_a_near_tie():
+    """Equal router rows tie every logit: the alternative set swaps the k-th for the (k+1)-th."""
+    s = synth.TINY
+
+    def src(kind, layer, expert):
+        a = synth.weight_bits(s, kind, layer, expert)
+        if kind == synth.K_ROUTER:
+            a = np.broadcast_to(a[0], a.shape).copy()
+        return a
+    W = O.Weights(s, source=src)
+    out = O.decode_step(W, O.PagedKV(s, 1), [3], np.zeros((1, 1), dtype=np.int32), [0], route_alt={(1, 0)})
+    assert list(out.sel[0, 0]) == [0, 1] and list(out.sel[1, 0]) == [0, 2]
+    assert list(out.sel_alt[1, 0]) == [0, 2] and out.margin[1, 0] == 0.0
+    with pytest.raises(ValueError):
+        O.decode_step(O.Weights(s), O.PagedKV(s, 1), [3], np.zeros((1, 1), dtype=np.int32), [0], route_alt={(0, 0)})
