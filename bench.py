@@ -105,6 +105,7 @@ def main():
     ap.add_argument("--workload", default="moe30b_8k")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=25.0)
+    ap.add_argument("--trace", default="", help="write a Perfetto timeline of one extra step to this path")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one MI355X: the decode megakernel runs on a single GPU; "
@@ -164,6 +165,20 @@ def main():
     traffic = measured_traffic(args.workload)
     log(f"[bench] {ms_step:.3f} ms/step, {tok_s:.1f} tok/s, {bytes_step / 1e9:.4f} GB/step, {gbs:.0f} GB/s "
         f"({100 * gbs / PEAK_HBM_GBS:.1f}% of peak)")
+
+    if args.trace:
+        # one more step, traced, outside the timed region
+        from persistent_moe_decode_amd import trace as tr
+        ntask = dec.info.n_tasks
+        buf = torch.zeros(tr.WORDS * ntask, dtype=torch.int64, device=dev)
+        dec.ctx.set_trace(buf.data_ptr(), ntask)
+        run(total - 1)
+        torch.cuda.synchronize(dev)
+        dec.ctx.set_trace(None)
+        tasks, qoff = dec.ctx.schedule()
+        rec = buf.view(ntask, tr.WORDS).cpu().numpy()
+        log("[bench] trace " + json.dumps(tr.summarize(tasks, qoff, rec)))
+        tr.dump(args.trace, tasks, qoff, rec)
 
     cpu = None
     if not args.no_cpu:

@@ -96,7 +96,9 @@ int mk_build_schedule(mk_ctx* ctx, int32_t num_cus, int64_t ctx_hint, size_t* wo
  *    wo [hidden][n_q*head_dim], router [n_experts][hidden],
  *    w_gate [n_experts][inter][hidden], w_up [n_experts][inter][hidden],
  *    w_down [n_experts][hidden][inter].
- *  k_pool, v_pool: device, [n_layers][num_pages][n_kv_heads][page_size][head_dim] bf16.
+ *  k_pool: device, [n_layers][num_pages][n_kv_heads][page_size][head_dim] bf16.
+ *  v_pool: device, [n_layers][num_pages][n_kv_heads][head_dim][page_size] bf16
+ *    (dims-major inside a page, the layout the P*V matrix-core product reads).
  *  workspace: device, at least the size mk_build_schedule reported, 256-byte aligned.
  * The buffers must stay valid until the context is destroyed or bound again. */
 int mk_bind(mk_ctx* ctx, const void* const* weights, int32_t n_weights, void* k_pool, void* v_pool,
@@ -140,6 +142,15 @@ int mk_set_spin_limit_us(mk_ctx* ctx, int64_t microseconds);
  * Layer outputs are still written to the workspace (mk_get_ws_offsets).
  * NULL restores normal operation.  Host only; applies from the next step. */
 int mk_set_layer_inputs(mk_ctx* ctx, const float* d_x);
+
+/* Per-task timeline: when d_records is not NULL, every task q < capacity
+ * writes eight uint64 at d_records[8*q], readings of the constant 100 MHz
+ * clock (s_memrealtime): [0] its workgroup fetched it, [1] its dependencies
+ * were met, [2..5] phase marks inside the task body (0 where the body has
+ * fewer phases), [6] it had signalled, [7] unused.  Tasks are numbered as
+ * in mk_copy_schedule.  NULL turns tracing off.  Host only; applies from
+ * the next step. */
+int mk_set_trace(mk_ctx* ctx, uint64_t* d_records, int64_t capacity);
 
 const char* mk_last_error_message(void);
 void mk_destroy(mk_ctx* ctx);

@@ -42,7 +42,7 @@ struct WsLayout {
   size_t state = 0, n_state_u32 = 0;  // counters, tickets, error word (zeroed by mk_reset)
   size_t ctr = 0, tickets = 0, err = 0;
   size_t tasks = 0, queue_off = 0, wtab = 0, inv_freq = 0;
-  size_t x = 0, qkv = 0, rlog = 0, attn_part = 0, attn_out = 0, h = 0, lm_part = 0, sel = 0;
+  size_t x = 0, qkv = 0, rlog = 0, attn_part = 0, attn_out = 0, h = 0, lm_part = 0, sel = 0, topk = 0;
   size_t total = 0;
 };
 
@@ -53,7 +53,7 @@ struct mk_ctx {
   bool built = false, bound = false, need_reset = false;
   int ncu = 0, n_attn = 0, n_gu = 0, n_out = 0, n_lm = 0, n_ctr = 0, n_tickets = 0;
   int out_rows_max = 0, gu_rows_max = 0, lm_rows_max = 0;
-  int lds_b = 0, lds_c = 0;
+  int lds_b = 0, lds_c = 0, lds_p = 0, pf_bytes = 0;
   size_t lds_bytes = 0;
   std::vector<Task> tasks;
   std::vector<int32_t> qoff;
@@ -65,6 +65,8 @@ struct mk_ctx {
   uint32_t epoch = 0;
   int64_t spin_us = 2000000;
   const float* x_in = nullptr;
+  uint64_t* trace = nullptr;
+  int64_t trace_cap = 0;
 };
 
 static int check_config(const mk_config& c) {
@@ -204,6 +206,7 @@ static WsLayout layout_workspace(const mk_ctx* c) {
   w.h = take(2 * L * B * f.top_k * f.inter);
   w.lm_part = take(4 * 2 * c->n_lm * B);
   w.sel = take(4 * L * B * f.top_k);
+  w.topk = take((size_t)kTopKRecord * L);
   w.total = o;
   return w;
 }
@@ -247,7 +250,7 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
   c->n_attn = n_attn;
   c->n_gu = n_gu;
   c->n_ctr = (L + 1) * kCtrPerLayer;
-  c->n_tickets = L * B * f.n_kv_heads + 1;
+  c->n_tickets = L * B * f.n_kv_heads + 1 + L;  // attention (seq, kv head) merges, LM argmax, router top-k
 
   // fan-ins
   const int R1 = qkv_rows + E;
@@ -294,6 +297,7 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
         t.r0 = cut0[part];
         t.r1 = cut1[part];
         t.signal = ctr_index(l, part == 0 ? C_QKV : C_ROUTER);
+        if (part == 1) t.count = n_router_tasks[l];  // the last of them publishes the layer's routing
         c->tasks.push_back(t);
       }
       // stage 2
@@ -350,17 +354,26 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
   size_t a_bytes = std::max({(size_t)B * H * 2, (size_t)B * f.n_q_heads * f.head_dim * 2,
                              (size_t)B * f.top_k * f.inter * 2, (size_t)group * f.head_dim * 2});
   a_bytes = align_up(a_bytes, 256);
-  const size_t b_bytes = 4096;
+  const size_t b_bytes = kLdsB;
   size_t c_gu = (size_t)std::min(c->gu_rows_max, kGuPass) * B * 2 * 4;
   size_t c_out = (size_t)c->out_rows_max * B * 4 + (size_t)c->out_rows_max * B * f.top_k * 4;
-  size_t c_lm = (size_t)c->lm_rows_max * B * 4;
-  size_t c_attn = (size_t)kWaves * 16 * kMaxGroup * 4 + (size_t)kWaves * group * (f.head_dim + 2) * 4;
+  size_t c_lm = (size_t)std::min(c->lm_rows_max, kLmPass) * B * 4;
+  size_t c_attn = std::max((size_t)kWaves * 16 * kMaxGroup * 4 + (size_t)kWaves * group * (f.head_dim + 2) * 4,
+                           (size_t)n_attn * group * 2 * 4 + (size_t)group * 4);  // merge scales of all chunks
   size_t c_bytes = align_up(std::max({c_gu, c_out, c_lm, c_attn}), 256);
   c->lds_b = (int)a_bytes;
   c->lds_c = (int)(a_bytes + b_bytes);
-  c->lds_bytes = a_bytes + b_bytes + c_bytes;
-  if (c->lds_bytes > lds_cap)
-    return fail(MK_ERR_UNSUPPORTED, "LDS need " + std::to_string(c->lds_bytes) + " exceeds " + std::to_string(lds_cap));
+  c->lds_p = (int)(a_bytes + b_bytes + c_bytes);
+  if ((size_t)c->lds_p > lds_cap)
+    return fail(MK_ERR_UNSUPPORTED, "LDS need " + std::to_string(c->lds_p) + " exceeds " + std::to_string(lds_cap));
+  // region P: the largest first weight tile (PRE rows of Wqkv/router, OUT rows of Wo), as far as LDS allows
+  const size_t pre_tile = (size_t)((R1 + ncu - 1) / ncu + 1) * H * 2;
+  const size_t out_tile = (size_t)c->out_rows_max * f.n_q_heads * f.head_dim * 2;
+  size_t pf = std::min(std::max(pre_tile, out_tile), lds_cap - (size_t)c->lds_p);
+  const char* pf_env = std::getenv("MK_PREFETCH_BYTES");
+  if (pf_env) pf = std::min(pf, (size_t)std::atoll(pf_env));
+  c->pf_bytes = (int)(pf / 1024 * 1024);
+  c->lds_bytes = (size_t)c->lds_p + c->pf_bytes;
 
   int r = simulate(c, nullptr);
   if (r) return r;
@@ -448,6 +461,15 @@ extern "C" int mk_set_layer_inputs(mk_ctx* c, const float* d_x) {
   if (!c) return fail(MK_ERR_INVALID_ARG, "null context");
   if (d_x && ((uintptr_t)d_x) % 4) return fail(MK_ERR_INVALID_ARG, "layer inputs not 4-byte aligned");
   c->x_in = d_x;
+  return MK_OK;
+}
+
+extern "C" int mk_set_trace(mk_ctx* c, uint64_t* d_records, int64_t capacity) {
+  if (!c) return fail(MK_ERR_INVALID_ARG, "null context");
+  if (d_records && capacity < 1) return fail(MK_ERR_INVALID_ARG, "trace capacity must be positive");
+  if (d_records && ((uintptr_t)d_records) % 8) return fail(MK_ERR_INVALID_ARG, "trace buffer not 8-byte aligned");
+  c->trace = d_records;
+  c->trace_cap = d_records ? capacity : 0;
   return MK_OK;
 }
 
@@ -544,6 +566,8 @@ extern "C" int mk_decode_step(mk_ctx* c, int32_t n, const int32_t* d_tokens, con
   a.lm_rows_max = c->lm_rows_max;
   a.lds_b = c->lds_b;
   a.lds_c = c->lds_c;
+  a.lds_p = c->lds_p;
+  a.pf_bytes = c->pf_bytes;
   uint8_t* w = c->wsp;
   a.tasks = (const Task*)(w + c->ws.tasks);
   a.queue_off = (const int32_t*)(w + c->ws.queue_off);
@@ -561,7 +585,10 @@ extern "C" int mk_decode_step(mk_ctx* c, int32_t n, const int32_t* d_tokens, con
   a.h = (uint16_t*)(w + c->ws.h);
   a.lm_part = (float*)(w + c->ws.lm_part);
   a.sel_out = (int32_t*)(w + c->ws.sel);
+  a.topk_g = w + c->ws.topk;
   a.x_in = c->x_in;
+  a.trace = c->trace;
+  a.trace_cap = c->trace_cap;
   a.k_pool = c->kpool;
   a.v_pool = c->vpool;
   a.n = n;

@@ -26,6 +26,7 @@
 using namespace mk;
 
 #define DEV __device__ __forceinline__
+#define TASK __device__ __forceinline__
 
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
 
@@ -82,12 +83,14 @@ DEV float group_sum(float v) {
 struct TopK {
   int32_t sel[kMaxBatch][kMaxTopK];
   float w[kMaxBatch][kMaxTopK];
-  int32_t nU, maxtok;
+  int32_t nU, maxtok, pad_[2];
   int32_t U[kMaxBatch * kMaxTopK];                // distinct experts, ascending
   int32_t ntok[kMaxBatch * kMaxTopK];             // tokens routed to U[u]
   int32_t pair[kMaxBatch * kMaxTopK][kMaxBatch];  // b*topk+j of each of them, ascending b
 };
-static_assert(sizeof(TopK) <= 3584, "top-k state fits region B");
+constexpr int kTopKBytes = 3136;
+static_assert(sizeof(TopK) <= kTopKBytes && sizeof(TopK) % 16 == 0, "top-k state fits region B, 16-byte multiple");
+static_assert(sizeof(TopK) == kTopKRecord, "published routing record size");
 
 struct Lds {
   uint8_t* base;
@@ -95,19 +98,28 @@ struct Lds {
   TopK* tk;
   int32_t* flags;  // [16]
   float* red;      // [16]
+  double* red8;    // [kWaves][kMaxBatch]
+  float* rbuf;     // router logits [max_batch][E]
   uint8_t* C;
+  uint8_t* P;      // prefetched weight tile
 };
 
+// Region B (kLdsB bytes): top-k state | flags | red | red8 | ... | rbuf at +4096.
 DEV Lds carve(uint8_t* lds, const KArgs& a) {
   Lds s;
   s.base = lds;
   s.A = lds;
   s.tk = (TopK*)(lds + a.lds_b);
-  s.flags = (int32_t*)(lds + a.lds_b + 3584);
-  s.red = (float*)(lds + a.lds_b + 3584 + 64);
+  s.flags = (int32_t*)(lds + a.lds_b + kTopKBytes);
+  s.red = (float*)(lds + a.lds_b + kTopKBytes + 64);
+  s.red8 = (double*)(lds + a.lds_b + kTopKBytes + 128);
+  s.rbuf = (float*)(lds + a.lds_b + 4096);
   s.C = lds + a.lds_c;
+  s.P = lds + a.lds_p;
   return s;
 }
+static_assert(kTopKBytes + 128 + 8 * kWaves * kMaxBatch <= 4096, "region B head fits");
+static_assert(4096 + 4 * kMaxBatch * kMaxExperts <= kLdsB, "router logits fit region B");
 
 // All threads get the block-wide sum; the order of the partial sums is fixed.
 DEV float block_sum(float v, float* red) {
@@ -200,6 +212,11 @@ DEV bool arrive_last(uint32_t* ticket, uint32_t count, int32_t* slot) {
 
 DEV const uint16_t* wptr(const KArgs& a, int i) { return (const uint16_t*)(uintptr_t)a.wtab[i]; }
 
+// Trace mark k (0..3) of task qi: the clock when thread 0 passes this point.
+DEV void mark(const KArgs& a, int qi, int k) {
+  if (a.trace && threadIdx.x == 0 && qi < a.trace_cap) a.trace[kTraceWords * (size_t)qi + 2 + k] = wall_clock64();
+}
+
 DEV const uint16_t* token_row(const KArgs& a, int b, int task) {
   int tok = a.tokens[b];
   if (tok < 0 || tok >= a.V) {
@@ -218,20 +235,55 @@ DEV float load_x(const KArgs& a, int layer, int b, int i, const uint16_t* emb) {
   return src[((size_t)layer * a.max_batch + b) * a.H + i];
 }
 
-// xs[b][H] = bf16(x_b / sqrt(mean(x_b^2) + eps) * g) for b < n.
-DEV void norm_inputs(const KArgs& a, int layer, const uint16_t* gain, uint16_t* xs, float* red, int task) {
-  const int H = a.H;
-  for (int b = 0; b < a.n; ++b) {
-    const uint16_t* emb = layer == 0 ? token_row(a, b, task) : nullptr;
-    float ss = 0.f;
-    for (int i = threadIdx.x; i < H; i += kThreads) {
-      const float v = load_x(a, layer, b, i, emb);
-      ss += v * v;
+// double -> bfloat16 bits, round to nearest even: round the 52-bit mantissa to
+// 7 fraction bits, dropping 45 (add half-minus-one plus the kept lsb; carries
+// run into the exponent as they should), then the value is exact in float and
+// its upper half is the bfloat16.
+DEV uint16_t d2bf(double v) {
+  uint64_t u = (uint64_t)__double_as_longlong(v);
+  if ((u & 0x7fffffffffffffffull) > 0x7ff0000000000000ull) return 0x7fc0;
+  u += 0x00000fffffffffffull + ((u >> 45) & 1ull);
+  u &= ~0x00001fffffffffffull;
+  return (uint16_t)(__float_as_uint((float)__longlong_as_double((long long)u)) >> 16);
+}
+
+// xs[b][H] = bf16(x_b / sqrt(mean(x_b^2) + eps) * g) for b < n, evaluated in
+// double so the one rounding to bf16 is the only one (the normalized input
+// feeds every projection of the layer).  The sums of squares of all rows are
+// reduced together: one barrier for the whole batch.
+DEV void norm_inputs(const KArgs& a, int layer, const uint16_t* gain, uint16_t* xs, double* red8, int task) {
+  const int H = a.H, n = a.n;
+  double ss[kMaxBatch];
+#pragma unroll
+  for (int b = 0; b < kMaxBatch; ++b) {
+    ss[b] = 0.0;
+    if (b < n) {
+      const uint16_t* emb = layer == 0 ? token_row(a, b, task) : nullptr;
+      for (int i = threadIdx.x; i < H; i += kThreads) {
+        const double v = load_x(a, layer, b, i, emb);
+        ss[b] += v * v;
+      }
     }
-    const float tot = block_sum(ss, red);
-    const float inv = 1.0f / sqrtf(tot / (float)H + a.eps);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int b = 0; b < kMaxBatch; ++b) {
+    if (b < n) {
+      double w = ss[b];
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) w += __shfl_xor(w, m);
+      if (lane == 0) red8[wave * kMaxBatch + b] = w;
+    }
+  }
+  __syncthreads();
+  for (int b = 0; b < n; ++b) {
+    double tot = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) tot += red8[w * kMaxBatch + b];
+    const double inv = 1.0 / sqrt(tot / (double)H + (double)a.eps);
+    const uint16_t* emb = layer == 0 ? token_row(a, b, task) : nullptr;
     for (int i = threadIdx.x; i < H; i += kThreads)
-      xs[(size_t)b * H + i] = f2bf(load_x(a, layer, b, i, emb) * inv * bf2f(gain[i]));
+      xs[(size_t)b * H + i] = d2bf((double)load_x(a, layer, b, i, emb) * inv * (double)bf2f(gain[i]));
   }
   __syncthreads();
 }
@@ -321,46 +373,59 @@ DEV void run_rowdots(int K, int njobs, int maxnx, const Job& job) {
 // ---------------------------------------------------------------------------
 // Router top-k: per token, the top_k logits ordered by (value desc, index
 // asc), their softmax, the distinct experts in ascending order and, for each
-// of them, the (token, slot) pairs routed to it.  Wave 0 computes, all read.
+// of them, the (token, slot) pairs routed to it.
+//
+// Selection by rank: every (token, expert) counts the experts that beat it
+// under the total order (value desc, index asc), in parallel over all
+// threads; the ones with rank < top_k land in slot `rank`.
 
 DEV bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
 
-DEV void compute_topk(const KArgs& a, int layer, TopK* tk) {
+DEV void compute_topk(const KArgs& a, int layer, TopK* tk, float* rbuf) {
   const int lane = threadIdx.x & 63;
+  const int E = a.E, K = a.topk, n = a.n;
+  const float* rl = a.rlog + (size_t)layer * a.max_batch * E;
+  for (int i = threadIdx.x; i < n * E; i += kThreads) {
+    const float v = rl[i];
+    rbuf[i] = v != v ? kNegInf : v;  // NaN never outranks a number
+  }
+  __syncthreads();
+  // four threads per (token, expert), each counting a quarter of the rivals; a quad sum joins them
+  for (int i4 = threadIdx.x; i4 < 4 * n * E; i4 += kThreads) {
+    const int i = i4 >> 2, part = i4 & 3;
+    const int b = i / E, e = i - b * E;
+    const float v = rbuf[i];
+    const float* rb = rbuf + b * E;
+    int rank = 0;
+#pragma unroll 8
+    for (int j = part; j < E; j += 4) {
+      const float u = rb[j];
+      rank += (u > v) | ((u == v) & (j < e));
+    }
+    float rf = (float)rank;
+    rf += dpp<0xB1>(rf);
+    rf += dpp<0x4E>(rf);
+    rank = (int)rf;
+    if (part == 0 && rank < K) {
+      tk->sel[b][rank] = e;
+      tk->w[b][rank] = v;
+    }
+  }
+  __syncthreads();
   if ((threadIdx.x >> 6) == 0) {
-    const int E = a.E, K = a.topk;
-    for (int b = 0; b < a.n; ++b) {
-      const float* r = a.rlog + ((size_t)layer * a.max_batch + b) * E;
-      float v0 = lane < E ? r[lane] : kNegInf;
-      float v1 = lane + 64 < E ? r[lane + 64] : kNegInf;
-      if (v0 != v0) v0 = kNegInf;  // NaN never outranks a number
-      if (v1 != v1) v1 = kNegInf;
-      bool t0 = lane >= E, t1 = lane + 64 >= E;
-      float selv0 = 0.f;
+    // softmax over each token's selected logits, slot order
+    if (lane < n) {
+      const float v0 = tk->w[lane][0];
+      float ex[kMaxTopK];
       float wsum = 0.f;
-      for (int j = 0; j < K; ++j) {
-        float bv = kNegInf;
-        int bi = 0x7fffffff;
-        if (!t0 && better(v0, lane, bv, bi)) { bv = v0; bi = lane; }
-        if (!t1 && better(v1, lane + 64, bv, bi)) { bv = v1; bi = lane + 64; }
 #pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-          const float ov = __shfl_xor(bv, m);
-          const int oi = __shfl_xor(bi, m);
-          if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-        }
-        if (bi == lane) t0 = true;
-        if (bi == lane + 64) t1 = true;
-        if (j == 0) selv0 = bv;
-        const float e = __expf(bv - selv0);
-        wsum += e;
-        if (lane == 0) {
-          tk->sel[b][j] = bi;
-          tk->w[b][j] = e;
-        }
+      for (int j = 0; j < kMaxTopK; ++j) {
+        ex[j] = j < K ? __expf(tk->w[lane][j] - v0) : 0.f;
+        wsum += ex[j];
       }
-      if (lane == 0)
-        for (int j = 0; j < K; ++j) tk->w[b][j] = tk->w[b][j] / wsum;
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j)
+        if (j < K) tk->w[lane][j] = ex[j] / wsum;
     }
     // distinct experts, ascending
     const int np = a.n * K;
@@ -405,28 +470,100 @@ DEV void compute_topk(const KArgs& a, int layer, TopK* tk) {
   __syncthreads();
 }
 
+// The layer's routing is computed once, by the last router task to finish,
+// and published as a TopK record; gate/up and output tasks copy it into LDS.
+DEV void publish_topk(const KArgs& a, int layer, const TopK* tk) {
+  const uint4* src = (const uint4*)tk;
+  uint4* dst = (uint4*)(a.topk_g + (size_t)layer * sizeof(TopK));
+  for (int i = threadIdx.x; i < (int)(sizeof(TopK) / 16); i += kThreads) dst[i] = src[i];
+  if (threadIdx.x < a.n * a.topk)
+    a.sel_out[(size_t)layer * a.max_batch * a.topk + threadIdx.x] = tk->sel[threadIdx.x / a.topk][threadIdx.x % a.topk];
+}
+
+DEV void load_topk(const KArgs& a, int layer, TopK* tk) {
+  const uint4* src = (const uint4*)(a.topk_g + (size_t)layer * sizeof(TopK));
+  uint4* dst = (uint4*)tk;
+  for (int i = threadIdx.x; i < (int)(sizeof(TopK) / 16); i += kThreads) dst[i] = src[i];
+}
+
 // ---------------------------------------------------------------------------
 // PRE: RMSNorm + rows [r0, r1) of the stacked [Wq; Wk; Wv; Wr] matrix.
 
+// Immutable weight tiles are prefetched into the LDS region P before the
+// task waits for its inputs (the pages' third-ranked gain: weights start
+// streaming before dependencies resolve).  Rows [0, npf) of a job's matrix
+// are then read from P, the rest from HBM.
+DEV void prefetch_to_lds(const uint16_t* src, uint8_t* dst_lds, int nbytes) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint8_t* s8 = (const uint8_t*)src;
+  const int nchunk = (nbytes + 1023) >> 10;
+  for (int c = wave; c < nchunk; c += kWaves) {
+    const int off = (c << 10) + (lane << 4);
+    if (off < nbytes)
+      __builtin_amdgcn_global_load_lds((const void*)(s8 + off),
+                                       (__attribute__((address_space(3))) void*)(dst_lds + (c << 10)), 16, 0, 0);
+  }
+}
+
+DEV void attn_plan(const KArgs& a, const Task& t, const Lds& s, int qi);
+
+// Work a task can do before its inputs are ready: the first weight tile of
+// PRE and OUT tasks (rows [r0, r1) of Wqkv / router / Wo) starts streaming
+// into LDS; attention tasks work out their chunk.  Returns the rows prefetched.
+DEV int task_prefetch(const KArgs& a, const Task& t, const Lds& s, int qi) {
+  const uint16_t* src;
+  int K, nrows;
+  if (t.op == OP_PRE) {
+    K = a.H;
+    nrows = t.r1 - t.r0;
+    src = t.r0 < a.qkv_rows ? wptr(a, widx(t.layer, WL_QKV)) + (size_t)t.r0 * K
+                            : wptr(a, widx(t.layer, WL_ROUTER)) + (size_t)(t.r0 - a.qkv_rows) * K;
+  } else if (t.op == OP_OUT) {
+    K = a.nq * a.d;
+    nrows = t.r1 - t.r0;
+    src = wptr(a, widx(t.layer, WL_O)) + (size_t)t.r0 * K;
+  } else {
+    if (t.op == OP_ATTN) attn_plan(a, t, s, qi);
+    return 0;
+  }
+  const int npf = min(nrows, a.pf_bytes / (K * 2));
+  if (npf > 0) prefetch_to_lds(src, s.P, npf * K * 2);
+  return npf;
+}
+
+// Makes every wave's prefetched tile visible to the whole workgroup.
+DEV void prefetch_wait() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
 struct JobPre {
   const uint16_t* W;
+  const uint16_t* pf;  // prefetched rows (LDS)
+  int npf;
   int r0, K;
   const uint16_t* xs;
   float* out;  // [b][ld] + r0 already applied
   int ld;
-  DEV const uint4* row(int i) const { return (const uint4*)(W + (size_t)(r0 + i) * K); }
+  DEV const uint4* row(int i) const {
+    return i < npf ? (const uint4*)(pf + (size_t)i * K) : (const uint4*)(W + (size_t)(r0 + i) * K);
+  }
   DEV int nx(int) const { return 1 << 30; }
   DEV const uint4* x(int, int t) const { return (const uint4*)(xs + (size_t)t * K); }
   DEV void emit(int i, int t, float v) const { out[(size_t)t * ld + i] = v; }
 };
 
-DEV void task_pre(const KArgs& a, const Task& t, const Lds& s, int qi) {
+TASK void task_pre(const KArgs& a, const Task& t, const Lds& s, int qi, int npf) {
   const int l = t.layer;
   uint16_t* xs = (uint16_t*)s.A;
-  norm_inputs(a, l, wptr(a, widx(l, WL_NORM)), xs, s.red, qi);
+  norm_inputs(a, l, wptr(a, widx(l, WL_NORM)), xs, s.red8, qi);
+  prefetch_wait();
+  mark(a, qi, 0);
   JobPre j;
   j.K = a.H;
   j.xs = xs;
+  j.pf = (const uint16_t*)s.P;
+  j.npf = npf;
   if (t.r0 < a.qkv_rows) {
     j.W = wptr(a, widx(l, WL_QKV));
     j.r0 = t.r0;
@@ -439,35 +576,196 @@ DEV void task_pre(const KArgs& a, const Task& t, const Lds& s, int qi) {
     j.ld = a.E;
   }
   run_rowdots(a.H, t.r1 - t.r0, a.n, j);
+  if (t.r0 >= a.qkv_rows) {
+    // router rows: the last router task of the layer takes the top-k for everyone
+    uint32_t* ticket = a.tickets + (size_t)a.L * a.max_batch * a.nkv + 1 + l;
+    if (arrive_last(ticket, (uint32_t)t.count, s.flags + 12)) {
+      compute_topk(a, l, s.tk, s.rbuf);
+      publish_topk(a, l, s.tk);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
 // ATTN: one chunk [t0, t1) of the positions of (sequence b, kv head g).
+//
+// Per page of 16 positions a wave runs two MFMA contractions:
+//   S^T[16 pos][16 heads] = K[16 pos][d] * Q^T[d][16 heads]   (v_mfma_f32_16x16x32_bf16,
+//     the group's q heads padded to 16 with zero rows), so lane l holds the
+//     scores of positions 4*(l/16)..+3 for head l%16;
+//   O[16 heads][d] += P[16 heads][16 pos] * V[16 pos][d]      (v_mfma_f32_16x16x16_bf16,
+//     d/16 tiles), where the probabilities above are already in the A-operand
+//     layout (row = head l%16, k = positions 4*(l/16)..+3).
+// The B operand of the second product needs 4 consecutive positions of one
+// dim per lane, which is why V pages are stored dims-major.  Softmax is online
+// per page (running max and sum per head, O rows rescaled), in fp32; the
+// probabilities enter the MFMA as a bf16 pair (high part + remainder), so the
+// P*V product is as accurate as the fp32 sum it is divided by.  K/V of the
+// next page are loaded while the current one is processed.
 
-DEV void task_attn(const KArgs& a, const Task& t, const Lds& s, int qi) {
-  const int l = t.layer, G = a.group, d = a.d, ps = a.ps;
-  int32_t* plan = s.flags + 2;  // b, g, t0, t1, first, nch, ok
-  int32_t* lens1 = (int32_t*)s.C;
+typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
+typedef short short4_v __attribute__((ext_vector_type(4)));
+typedef float float4_v __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct AttnPage {
+  uint4 k[D / 32];  // lane l: K[pos l%16][32c + 8*(l/16) .. +7]
+  uint2 v[D / 16];  // lane l: V[pos 4*(l/16) .. +3][dim 16t + l%16]
+  int nvalid;       // positions of the page inside the chunk
+};
+
+template <int D>
+DEV void attn_fetch(const KArgs& a, AttnPage<D>& P, int l, int b, int g, int tb, int t1, int qi) {
+  const int lane = threadIdx.x & 63, r = lane & 15, grp = lane >> 4;
+  const int page = a.page_table[(size_t)b * a.max_pages + tb / a.ps];
+  const bool pg_ok = page >= 0 && page < a.num_pages;
+  if (!pg_ok && lane == 0) raise_error(a, MK_ERR_DEVICE_PAGE, qi, page);
+  P.nvalid = pg_ok ? min(16, t1 - tb) : 0;
+  const size_t boff = (((size_t)l * a.num_pages + (pg_ok ? page : 0)) * a.nkv + g) * (size_t)16 * D;
+  const uint16_t* kb = a.k_pool + boff;
+  const uint16_t* vb = a.v_pool + boff;
+  const bool krow = r < P.nvalid, vcol = 4 * grp < P.nvalid;
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c)
+    P.k[c] = krow ? *(const uint4*)(kb + r * D + 32 * c + 8 * grp) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t)
+    P.v[t] = vcol ? *(const uint2*)(vb + (16 * t + r) * 16 + 4 * grp) : make_uint2(0, 0);
+}
+
+template <int D>
+DEV void attn_page(const AttnPage<D>& P, const bf16x8_v (&qb)[D / 32], float scale, float& m, float& lsum,
+                   float4_v (&o)[D / 16]) {
+  const int lane = threadIdx.x & 63, grp = lane >> 4;
+  float4_v sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c)
+    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, P.k[c]), qb[c], sacc, 0, 0, 0);
+  float sv[4];
+  float bm = kNegInf;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sv[i] = (4 * grp + i < P.nvalid) ? sacc[i] * scale : kNegInf;  // select: poison slots never enter
+    bm = fmaxf(bm, sv[i]);
+  }
+  bm = fmaxf(bm, __shfl_xor(bm, 16));
+  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  const float mn = fmaxf(m, bm);
+  const float alpha = mn == kNegInf ? 1.f : __expf(m - mn);
+  // p = p_hi + p_lo, both bf16: two MFMAs keep the P*V product at ~2^-16 relative
+  short4_v pa, pl;
+  float ps = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float pf = sv[i] == kNegInf ? 0.f : __expf(sv[i] - mn);
+    const uint16_t hi = f2bf(pf);
+    pa[i] = (short)hi;
+    pl[i] = (short)f2bf(pf - bf2f(hi));
+    ps += pf;
+  }
+  lsum = lsum * alpha + ps;
+  m = mn;
+  // O rows are heads 4*(l/16)+i; their rescale factors live in lanes 4*(l/16)+i
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float ai = __shfl(alpha, 4 * grp + i);
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) o[t][i] *= ai;
+  }
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    short4_v vb4;
+    const uint2 vv = P.v[t];
+    vb4[0] = (4 * grp + 0 < P.nvalid) ? (short)(vv.x & 0xffffu) : (short)0;
+    vb4[1] = (4 * grp + 1 < P.nvalid) ? (short)(vv.x >> 16) : (short)0;
+    vb4[2] = (4 * grp + 2 < P.nvalid) ? (short)(vv.y & 0xffffu) : (short)0;
+    vb4[3] = (4 * grp + 3 < P.nvalid) ? (short)(vv.y >> 16) : (short)0;
+    o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb4, o[t], 0, 0, 0);
+    o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vb4, o[t], 0, 0, 0);
+  }
+}
+
+// This wave's pages of the chunk; leaves (o, m, sum) per head in mrg[wave][G][d+2].
+template <int D>
+DEV void attn_wave(const KArgs& a, const Lds& s, int qi, const uint16_t* q_s, int l, int b, int g, int t0, int t1,
+                   float* mrg) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r = lane & 15, grp = lane >> 4;
+  const int G = a.group;
+  bf16x8_v qb[D / 32];
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    const uint4 qv = r < G ? *(const uint4*)(q_s + r * D + 32 * c + 8 * grp) : make_uint4(0, 0, 0, 0);
+    qb[c] = __builtin_bit_cast(bf16x8_v, qv);
+  }
+  const float scale = 1.0f / sqrtf((float)D);
+  float m = kNegInf, lsum = 0.f;
+  float4_v o[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) o[t] = float4_v{0.f, 0.f, 0.f, 0.f};
+  const int nblk = (t1 - t0 + 15) / 16;
+  int blk = wave;
+  if (blk < nblk) {
+    AttnPage<D> cur, nxt;
+    attn_fetch<D>(a, cur, l, b, g, t0 + 16 * blk, t1, qi);
+    while (true) {
+      const int nb = blk + kWaves;
+      const bool more = nb < nblk;
+      if (more) attn_fetch<D>(a, nxt, l, b, g, t0 + 16 * nb, t1, qi);
+      attn_page<D>(cur, qb, scale, m, lsum, o);
+      if (!more) break;
+      cur = nxt;
+      blk = nb;
+    }
+  }
+  // per-head totals over the 4 lane groups, then this wave's row of the merge buffer
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  if (grp == 0 && r < G) {
+    float* row = mrg + ((size_t)wave * G + r) * (D + 2);
+    row[D] = m;
+    row[D + 1] = lsum;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * grp + i;
+    if (h < G) {
+      float* row = mrg + ((size_t)wave * G + h) * (D + 2);
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) row[16 * t + r] = o[t][i];
+    }
+  }
+}
+
+// The chunk of split task t.idx, from the step's sequence lengths only, so it
+// runs before the task's wait; thread 0 writes it to plan = flags[2..9]
+// (the wait's barrier publishes it).
+DEV void attn_plan(const KArgs& a, const Task& t, const Lds& s, int qi) {
+  int32_t* plan = s.flags + 2;  // b, g, t0, t1, first, nch, ok, p
   if (threadIdx.x == 0) {
-    const int cap = a.max_pages * ps;
-    for (int b = 0; b < a.n; ++b) {
-      int p = a.seq_lens[b];
-      if (p < 0 || p + 1 > cap) {
+    int32_t lens1[kMaxBatch];
+    const int cap = a.max_pages * a.ps;
+#pragma unroll
+    for (int b = 0; b < kMaxBatch; ++b) {
+      int p = b < a.n ? a.seq_lens[b] : 0;
+      if (b < a.n && (p < 0 || p + 1 > cap)) {
         raise_error(a, MK_ERR_DEVICE_SEQ, qi, b);
         p = p < 0 ? 0 : cap - 1;
       }
       lens1[b] = p + 1;
     }
-    const int64_t C = attn_chunk_len(lens1, a.n, a.nkv, a.n_attn, ps);
-    int b, g, t0, t1, first, nch;
+    const int64_t C = attn_chunk_len(lens1, a.n, a.nkv, a.n_attn, a.ps);
+    int b = 0, g = 0, t0 = 0, t1 = 0, first = 0, nch = 0;
     const bool ok = attn_chunk_of(lens1, a.n, a.nkv, C, t.idx, &b, &g, &t0, &t1, &first, &nch);
     plan[0] = b; plan[1] = g; plan[2] = t0; plan[3] = t1; plan[4] = first; plan[5] = nch; plan[6] = ok;
     plan[7] = lens1[ok ? b : 0] - 1;
   }
-  __syncthreads();
+}
+
+TASK void task_attn(const KArgs& a, const Task& t, const Lds& s, int qi) {
+  const int l = t.layer, G = a.group, d = a.d, ps = a.ps;
+  const int32_t* plan = s.flags + 2;
   if (!plan[6]) return;
   const int b = plan[0], g = plan[1], t0 = plan[2], t1 = plan[3], first = plan[4], nch = plan[5], p = plan[7];
-  __syncthreads();  // plan and lens1 read before region C is reused below
 
   const int half = d / 2;
   uint16_t* q_s = (uint16_t*)s.A;  // [G][d] rotated q, bf16
@@ -499,119 +797,23 @@ DEV void task_attn(const KArgs& a, const Task& t, const Lds& s, int qi) {
         a.k_pool[off + i] = f2bf(x0 * cf - x1 * sf);
         a.k_pool[off + i + half] = f2bf(x0 * sf + x1 * cf);
       }
-      for (int i = threadIdx.x; i < d; i += kThreads) a.v_pool[off + i] = f2bf(vv[i]);
+      // V pages are stored dims-major: element (dim, slot) of a (page, head) block at dim*page_size + slot
+      const size_t voff = (((size_t)l * a.num_pages + page) * a.nkv + g) * (size_t)ps * d + p % ps;
+      for (int i = threadIdx.x; i < d; i += kThreads) a.v_pool[voff + (size_t)i * ps] = f2bf(vv[i]);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __threadfence_block();
   __syncthreads();
+  mark(a, qi, 0);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const float scale = 1.0f / sqrtf((float)d);
-  float m[kMaxGroup], ls[kMaxGroup], o0[kMaxGroup], o1[kMaxGroup];
-#pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) {
-    m[h] = kNegInf;
-    ls[h] = 0.f;
-    o0[h] = 0.f;
-    o1[h] = 0.f;
-  }
-  float* pbuf = (float*)s.C + wave * 16 * kMaxGroup;  // [h][16] probabilities of this wave's block
-  const int tl = lane >> 2, qd = lane & 3;
-  const int nblk = (t1 - t0 + 15) / 16;
-  for (int blk = wave; blk < nblk; blk += kWaves) {
-    const int tb = t0 + blk * 16;
-    const int page = a.page_table[(size_t)b * a.max_pages + tb / ps];
-    if (page < 0 || page >= a.num_pages) {
-      if (lane == 0) raise_error(a, MK_ERR_DEVICE_PAGE, qi, page);
-      continue;
-    }
-    const size_t boff = (((size_t)l * a.num_pages + page) * a.nkv + g) * (size_t)ps * d;
-    const uint16_t* kb = a.k_pool + boff;
-    const uint16_t* vb = a.v_pool + boff;
-    const bool valid = tb + tl < t1;
-    // scores: 4 lanes per position, d/4 dims each
-    const uint4* kr = (const uint4*)(kb + tl * d + qd * (d / 4));
-    uint4 kv[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) kv[c] = (valid && c < d / 32) ? kr[c] : make_uint4(0, 0, 0, 0);
-    float sc[kMaxGroup];
-#pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) {
-      float acc = 0.f;
-      if (h < G) {
-        const uint4* qr = (const uint4*)(q_s + h * d + qd * (d / 4));
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (c < d / 32) acc = dot8(kv[c], qr[c], acc);
-      }
-      acc += dpp<0xB1>(acc);
-      acc += dpp<0x4E>(acc);
-      sc[h] = valid ? acc * scale : kNegInf;
-    }
-    // V rows of the block (lane owns d/64 consecutive dims)
-    uint32_t vr[16];
-#pragma unroll
-    for (int tt = 0; tt < 16; ++tt) {
-      const bool ok = tb + tt < t1;
-      if (d == 128)
-        vr[tt] = ok ? *(const uint32_t*)(vb + tt * d + 2 * lane) : 0u;
-      else
-        vr[tt] = ok ? (uint32_t)vb[tt * d + lane] : 0u;
-    }
-    // online softmax over the block's 16 positions
-#pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) {
-      if (h >= G) break;
-      float bm = sc[h];
-      bm = fmaxf(bm, __shfl_xor(bm, 4));
-      bm = fmaxf(bm, __shfl_xor(bm, 8));
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
-      const float mn = fmaxf(m[h], bm);
-      const float alpha = __expf(m[h] - mn);
-      const float pr = valid ? __expf(sc[h] - mn) : 0.f;
-      float bs = pr;
-      bs += __shfl_xor(bs, 4);
-      bs += __shfl_xor(bs, 8);
-      bs += __shfl_xor(bs, 16);
-      bs += __shfl_xor(bs, 32);
-      ls[h] = ls[h] * alpha + bs;
-      m[h] = mn;
-      o0[h] *= alpha;
-      o1[h] *= alpha;
-      if (qd == 0) pbuf[h * 16 + tl] = pr;
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int tt = 0; tt < 16; ++tt) {
-      const float v0 = d == 128 ? bf2f(vr[tt] & 0xffffu) : bf2f(vr[tt]);
-      const float v1 = d == 128 ? bf2f(vr[tt] >> 16) : 0.f;
-#pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h) {
-        if (h < G) {
-          const float pp = pbuf[h * 16 + tt];
-          o0[h] += pp * v0;
-          o1[h] += pp * v1;
-        }
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
-
-  // merge the 8 waves' running states into this chunk's partial
+  // positions of the chunk, 16 (one page) at a time, pages dealt to waves round robin
   float* mrg = (float*)s.C + kWaves * 16 * kMaxGroup;  // [wave][G][d+2]
-  const int DPV = d / 64;
-  for (int h = 0; h < G; ++h) {
-    float* row = mrg + ((size_t)wave * G + h) * (d + 2);
-    row[lane * DPV] = o0[h];
-    if (DPV == 2) row[lane * DPV + 1] = o1[h];
-    if (lane == 0) {
-      row[d] = m[h];
-      row[d + 1] = ls[h];
-    }
-  }
+  if (d == 128)
+    attn_wave<128>(a, s, qi, q_s, l, b, g, t0, t1, mrg);
+  else
+    attn_wave<64>(a, s, qi, q_s, l, b, g, t0, t1, mrg);
+  mark(a, qi, 1);
   __syncthreads();
   float* part = a.attn_part + ((size_t)l * a.n_attn + t.idx) * G * (d + 2);
   for (int e = threadIdx.x; e < G * d; e += kThreads) {
@@ -633,21 +835,40 @@ DEV void task_attn(const KArgs& a, const Task& t, const Lds& s, int qi) {
   }
   // last chunk of (b, g) merges all chunks: o = sum_j e^(m_j - M) o_j / sum_j e^(m_j - M) l_j
   uint32_t* ticket = a.tickets + ((size_t)l * a.max_batch + b) * a.nkv + g;
+  mark(a, qi, 2);
   if (arrive_last(ticket, (uint32_t)nch, s.flags + 10)) {
     const float* parts = a.attn_part + ((size_t)l * a.n_attn + first) * G * (d + 2);
     uint16_t* out = a.attn_out + ((size_t)l * a.max_batch + b) * a.nq * d + (size_t)g * G * d;
+    // (m, l) of every chunk and head in one parallel pass, then the per-head
+    // scale factors, then the weighted sums with the partial loads in flight together
+    float* mj = (float*)s.C;             // [nch][G] maxima, then scale factors
+    float* lj = mj + (size_t)nch * G;    // [nch][G] sums
+    float* Lh = lj + (size_t)nch * G;    // [G] merged sums
+    for (int i = threadIdx.x; i < nch * G; i += kThreads) {
+      const float* row = parts + (size_t)i * (d + 2);
+      mj[i] = row[d];
+      lj[i] = row[d + 1];
+    }
+    __syncthreads();
+    if (threadIdx.x < G) {
+      const int hh = threadIdx.x;
+      float M = kNegInf;
+      for (int j = 0; j < nch; ++j) M = fmaxf(M, mj[j * G + hh]);
+      float Ls = 0.f;
+      for (int j = 0; j < nch; ++j) {
+        const float sc = __expf(mj[j * G + hh] - M);
+        mj[j * G + hh] = sc;
+        Ls += lj[j * G + hh] * sc;
+      }
+      Lh[hh] = Ls;
+    }
+    __syncthreads();
     for (int e = threadIdx.x; e < G * d; e += kThreads) {
       const int hh = e / d, dim = e % d;
-      float M = kNegInf;
-      for (int j = 0; j < nch; ++j) M = fmaxf(M, parts[((size_t)j * G + hh) * (d + 2) + d]);
-      float O = 0.f, Ls = 0.f;
-      for (int j = 0; j < nch; ++j) {
-        const float* row = parts + ((size_t)j * G + hh) * (d + 2);
-        const float sc = __expf(row[d] - M);
-        O += row[dim] * sc;
-        Ls += row[d + 1] * sc;
-      }
-      out[hh * d + dim] = f2bf(O / Ls);
+      float O = 0.f;
+#pragma unroll 8
+      for (int j = 0; j < nch; ++j) O += parts[((size_t)j * G + hh) * (d + 2) + dim] * mj[j * G + hh];
+      out[hh * d + dim] = f2bf(O / Lh[hh]);
     }
   }
 }
@@ -684,14 +905,14 @@ struct JobGateUp {
   DEV void emit(int i, int t, float v) const { gs[((size_t)(i >> 1) * maxB + t) * 2 + (i & 1)] = v; }
 };
 
-DEV void task_gateup(const KArgs& a, const Task& t, const Lds& s, int qi) {
+TASK void task_gateup(const KArgs& a, const Task& t, const Lds& s, int qi) {
   const int l = t.layer;
-  compute_topk(a, l, s.tk);
+  load_topk(a, l, s.tk);  // visible to all threads after the norm's barriers
+  mark(a, qi, 0);
   uint16_t* xs = (uint16_t*)s.A;
-  norm_inputs(a, l, wptr(a, widx(l, WL_NORM)), xs, s.red, qi);
+  norm_inputs(a, l, wptr(a, widx(l, WL_NORM)), xs, s.red8, qi);
+  mark(a, qi, 1);
   const TopK* tk = s.tk;
-  if (t.idx == 0 && threadIdx.x < a.n * a.topk)
-    a.sel_out[(size_t)l * a.max_batch * a.topk + threadIdx.x] = tk->sel[threadIdx.x / a.topk][threadIdx.x % a.topk];
   const int64_t R = (int64_t)tk->nU * a.I;
   const int64_t va = R * t.idx / a.n_gu, vb = R * (t.idx + 1) / a.n_gu;
   JobGateUp j;
@@ -732,10 +953,14 @@ DEV void task_gateup(const KArgs& a, const Task& t, const Lds& s, int qi) {
 
 struct JobO {
   const uint16_t* W;
+  const uint16_t* pf;  // prefetched rows (LDS)
+  int npf;
   int r0, K, maxB;
   const uint16_t* xs;
   float* ao;
-  DEV const uint4* row(int i) const { return (const uint4*)(W + (size_t)(r0 + i) * K); }
+  DEV const uint4* row(int i) const {
+    return i < npf ? (const uint4*)(pf + (size_t)i * K) : (const uint4*)(W + (size_t)(r0 + i) * K);
+  }
   DEV int nx(int) const { return 1 << 30; }
   DEV const uint4* x(int, int t) const { return (const uint4*)(xs + (size_t)t * K); }
   DEV void emit(int i, int t, float v) const { ao[(size_t)i * maxB + t] = v; }
@@ -762,7 +987,7 @@ DEV void copy_to_lds(uint16_t* dst, const uint16_t* src, int elems) {
   for (int i = threadIdx.x; i < elems / 8; i += kThreads) d4[i] = s4[i];
 }
 
-DEV void task_out(const KArgs& a, const Task& t, const Lds& s, int qi) {
+TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf) {
   const int l = t.layer, nr = t.r1 - t.r0, n = a.n, AD = a.nq * a.d;
   float* ao = (float*)s.C;                                    // [out_rows_max][maxB]
   float* contrib = ao + (size_t)a.out_rows_max * a.max_batch;  // [out_rows_max][maxB*topk]
@@ -770,8 +995,10 @@ DEV void task_out(const KArgs& a, const Task& t, const Lds& s, int qi) {
   // attention output projection
   uint16_t* xs = (uint16_t*)s.A;
   copy_to_lds(xs, a.attn_out + (size_t)l * a.max_batch * AD, n * AD);
-  __syncthreads();
+  prefetch_wait();
   JobO jo;
+  jo.pf = (const uint16_t*)s.P;
+  jo.npf = npf;
   jo.W = wptr(a, widx(l, WL_O));
   jo.r0 = t.r0;
   jo.K = AD;
@@ -779,11 +1006,14 @@ DEV void task_out(const KArgs& a, const Task& t, const Lds& s, int qi) {
   jo.xs = xs;
   jo.ao = ao;
   run_rowdots(AD, nr, n, jo);
+  mark(a, qi, 0);
   // expert down projections
-  compute_topk(a, l, s.tk);  // begins and ends with barriers, so xs is free afterwards
+  __syncthreads();  // every wave is done with xs
+  load_topk(a, l, s.tk);
   const TopK* tk = s.tk;
   copy_to_lds(xs, a.h + (size_t)l * a.max_batch * a.topk * a.I, n * a.topk * a.I);
   __syncthreads();
+  mark(a, qi, 1);
   JobDown jd;
   jd.tk = tk;
   jd.W = wptr(a, widx(l, WL_DOWN));
@@ -796,6 +1026,7 @@ DEV void task_out(const KArgs& a, const Task& t, const Lds& s, int qi) {
   jd.maxBK = maxBK;
   run_rowdots(a.I, nr * tk->nU, tk->maxtok, jd);
   __syncthreads();
+  mark(a, qi, 2);
   // x_{l+1} = (x_l + attn) + sum_j w_j y_j
   for (int e = threadIdx.x; e < nr * n; e += kThreads) {
     const int rr = e / n, b = e % n;
@@ -846,36 +1077,56 @@ DEV void block_argmax(float& v, int& i, float* red) {
     if (better(red[w], ((int*)red)[8 + w], v, i)) { v = red[w]; i = ((int*)red)[8 + w]; }
 }
 
-DEV void task_lmhead(const KArgs& a, const Task& t, const Lds& s, int qi) {
+TASK void task_lmhead(const KArgs& a, const Task& t, const Lds& s, int qi) {
   const int L = a.L, nr = t.r1 - t.r0;
   uint16_t* xs = (uint16_t*)s.A;
-  norm_inputs(a, L, wptr(a, W_FINAL_NORM), xs, s.red, qi);
+  norm_inputs(a, L, wptr(a, W_FINAL_NORM), xs, s.red8, qi);
+  mark(a, qi, 0);
   JobLM j;
   j.W = wptr(a, W_LM_HEAD);
-  j.r0 = t.r0;
   j.K = a.H;
   j.V = a.V;
   j.maxB = a.max_batch;
   j.xs = xs;
   j.lmv = (float*)s.C;
   j.logits = a.logits;
-  run_rowdots(a.H, nr, a.n, j);
-  __syncthreads();
-  for (int b = 0; b < a.n; ++b) {
-    float v = kNegInf;
-    int i = 0x7fffffff;
-    for (int r = threadIdx.x; r < nr; r += kThreads) {
-      float x = j.lmv[(size_t)r * a.max_batch + b];
-      if (x != x) x = kNegInf;
-      if (better(x, t.r0 + r, v, i)) { v = x; i = t.r0 + r; }
+  // rows in passes of at most kLmPass (bounds the LDS copy of the logits); thread 0
+  // keeps the running best of each sequence
+  float best_v[kMaxBatch];
+  int best_i[kMaxBatch];
+#pragma unroll
+  for (int b = 0; b < kMaxBatch; ++b) {
+    best_v[b] = kNegInf;
+    best_i[b] = 0x7fffffff;
+  }
+  for (int p0 = 0; p0 < nr; p0 += kLmPass) {
+    const int np = min(kLmPass, nr - p0);
+    j.r0 = t.r0 + p0;
+    run_rowdots(a.H, np, a.n, j);
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < kMaxBatch; ++b) {
+      if (b >= a.n) break;
+      float v = kNegInf;
+      int i = 0x7fffffff;
+      for (int r = threadIdx.x; r < np; r += kThreads) {
+        float x = j.lmv[(size_t)r * a.max_batch + b];
+        if (x != x) x = kNegInf;
+        if (better(x, j.r0 + r, v, i)) { v = x; i = j.r0 + r; }
+      }
+      block_argmax(v, i, s.red);
+      if (better(v, i, best_v[b], best_i[b])) { best_v[b] = v; best_i[b] = i; }
     }
-    block_argmax(v, i, s.red);
-    if (threadIdx.x == 0) {
-      a.lm_part[((size_t)t.idx * a.max_batch + b) * 2] = v;
-      ((int*)a.lm_part)[((size_t)t.idx * a.max_batch + b) * 2 + 1] = i;
+  }
+  mark(a, qi, 1);
+  if (threadIdx.x == 0) {
+    for (int b = 0; b < a.n; ++b) {
+      a.lm_part[((size_t)t.idx * a.max_batch + b) * 2] = best_v[b];
+      ((int*)a.lm_part)[((size_t)t.idx * a.max_batch + b) * 2 + 1] = best_i[b];
     }
   }
   uint32_t* ticket = a.tickets + (size_t)a.L * a.max_batch * a.nkv;
+  mark(a, qi, 2);
   if (arrive_last(ticket, (uint32_t)a.n_lm, s.flags + 11)) {
     for (int b = 0; b < a.n; ++b) {
       float v = kNegInf;
@@ -900,19 +1151,30 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a)
   const int q0 = a.queue_off[cu], q1 = a.queue_off[cu + 1];
   for (int q = q0; q < q1; ++q) {
     const Task t = a.tasks[q];
+    uint64_t t_fetch = 0, t_ready = 0;
+    if (a.trace && threadIdx.x == 0) t_fetch = wall_clock64();
+    // immutable weights start streaming into LDS before the inputs are ready
+    const int npf = task_prefetch(a, t, s, q);
     bool ok = wait_counter(a, t.wait[0], t.fanin[0], q, s.flags + 0);
     if (ok && t.wait[1] >= 0) ok = wait_counter(a, t.wait[1], t.fanin[1], q, s.flags + 1);
+    if (a.trace && threadIdx.x == 0) t_ready = wall_clock64();
     if (ok) {
       switch (t.op) {
-        case OP_PRE: task_pre(a, t, s, q); break;
+        case OP_PRE: task_pre(a, t, s, q, npf); break;
         case OP_ATTN: task_attn(a, t, s, q); break;
         case OP_GATEUP: task_gateup(a, t, s, q); break;
-        case OP_OUT: task_out(a, t, s, q); break;
+        case OP_OUT: task_out(a, t, s, q, npf); break;
         case OP_LMHEAD: task_lmhead(a, t, s, q); break;
         default: break;
       }
     }
     signal_counter(a, t.signal);
+    if (a.trace && threadIdx.x == 0 && q < a.trace_cap) {
+      uint64_t* r = a.trace + kTraceWords * (size_t)q;
+      r[0] = t_fetch;
+      r[1] = t_ready;
+      r[6] = wall_clock64();
+    }
   }
 }
 

@@ -21,6 +21,10 @@ constexpr int kMaxExperts = 128;
 constexpr int kMaxGroup = 8;       // q heads per kv head
 constexpr int kTaskInts = 32;      // 128-byte descriptor
 constexpr int kGuPass = 256;       // gate/up virtual rows per pass of one task
+constexpr int kLmPass = 512;       // LM head rows per pass of one task
+constexpr int kTraceWords = 8;     // per task: fetch, ready, 4 phase marks, done, spare
+constexpr int kLdsB = 8192;        // LDS region B: top-k state, flags, reductions, router logits
+constexpr int kTopKRecord = 3088;  // bytes of one layer's published routing (experts, weights, groups)
 
 enum Op : int32_t {
   OP_PRE = 1,     // RMSNorm + rows of [Wq; Wk; Wv] or of the router
@@ -60,11 +64,12 @@ struct KArgs {
   // schedule
   int32_t n_attn, n_gu, n_lm;
   int32_t gu_rows_max, out_rows_max, lm_rows_max;  // largest row range of one task
-  int32_t lds_b, lds_c;                            // LDS region offsets (bytes)
+  int32_t lds_b, lds_c, lds_p;                     // LDS region offsets (bytes)
+  int32_t pf_bytes;                                // size of the weight prefetch region
   const Task* tasks;
   const int32_t* queue_off;
   uint32_t* ctr;        // counters [L * kCtrPerLayer + 8]
-  uint32_t* tickets;    // attention tickets [L][max_batch][nkv], then 1 for the LM head
+  uint32_t* tickets;    // attention tickets [L][max_batch][nkv], 1 for the LM head, then [L] routers
   int32_t* err;         // E_WORDS
   const uint64_t* wtab; // device pointers of the weights
   const double* inv_freq; // [d/2]
@@ -76,8 +81,11 @@ struct KArgs {
   uint16_t* attn_out;   // [L][max_batch][nq*d]
   uint16_t* h;          // [L][max_batch*topk][I]
   float* lm_part;       // [n_lm][max_batch][2] (value, index as float bits)
-  int32_t* sel_out;     // [L][max_batch][topk] experts chosen per token (written by gate/up task 0)
+  int32_t* sel_out;     // [L][max_batch][topk] experts chosen per token
+  uint8_t* topk_g;      // [L] routing records (kTopKRecord bytes each)
   const float* x_in;    // test hook: layer inputs [L+1][max_batch][H] read instead of x (NULL = off)
+  uint64_t* trace;      // per task: s_memrealtime at fetch, dependencies met, done (NULL = off)
+  int64_t trace_cap;    // tasks the trace buffer holds
   // KV pools
   uint16_t* k_pool;
   uint16_t* v_pool;

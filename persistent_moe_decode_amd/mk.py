@@ -78,6 +78,7 @@ def lib():
         "mk_reset": [P, P],
         "mk_set_spin_limit_us": [P, I64],
         "mk_set_layer_inputs": [P, P],
+        "mk_set_trace": [P, P, I64],
         "mk_get_schedule_info": [P, ctypes.POINTER(ScheduleInfo)],
         "mk_copy_schedule": [P, pi32, I64, pi32, I64],
         "mk_validate_schedule": [P, pi32],
@@ -188,6 +189,9 @@ class Context:
 
     def set_layer_inputs(self, ptr: int | None):
         check(lib().mk_set_layer_inputs(self.h, ptr or None), "mk_set_layer_inputs")
+
+    def set_trace(self, ptr: int | None, capacity: int = 0):
+        check(lib().mk_set_trace(self.h, ptr or None, capacity), "mk_set_trace")
 
     def set_spin_limit_us(self, us: int):
         check(lib().mk_set_spin_limit_us(self.h, us), "mk_set_spin_limit_us")

@@ -87,9 +87,11 @@ class DeviceDecoder:
                 self.weights.append(t)
             stager.sync()
             self.stager = stager
-            pool_shape = (s.n_layers, self.num_pages, s.n_kv_heads, s.page_size, s.head_dim)
-            self.k_pool = torch.full(pool_shape, POISON, dtype=torch.int16, device=self.dev)
-            self.v_pool = torch.full(pool_shape, POISON, dtype=torch.int16, device=self.dev)
+            # K pages are [slot][dim] per (layer, page, head); V pages are dims-major [dim][slot]
+            k_shape = (s.n_layers, self.num_pages, s.n_kv_heads, s.page_size, s.head_dim)
+            v_shape = (s.n_layers, self.num_pages, s.n_kv_heads, s.head_dim, s.page_size)
+            self.k_pool = torch.full(k_shape, POISON, dtype=torch.int16, device=self.dev)
+            self.v_pool = torch.full(v_shape, POISON, dtype=torch.int16, device=self.dev)
             self.ws = torch.zeros(self.ws_bytes + 256, dtype=torch.uint8, device=self.dev)
             self.ws_base = (self.ws.data_ptr() + 255) // 256 * 256
             self.page_table = torch.from_numpy(self.page_table_np).to(self.dev)
@@ -117,7 +119,9 @@ class DeviceDecoder:
                     a = synth.kv_bits(s, layer, which, b, 0, n)
                     buf = np.full((npg * ps, s.n_kv_heads, s.head_dim), POISON, dtype=np.uint16)
                     buf[:n] = a
-                    blk = buf.reshape(npg, ps, s.n_kv_heads, s.head_dim).transpose(0, 2, 1, 3)
+                    blk = buf.reshape(npg, ps, s.n_kv_heads, s.head_dim)
+                    # K pages [head][slot][dim]; V pages dims-major [head][dim][slot]
+                    blk = blk.transpose(0, 2, 1, 3) if which == "k" else blk.transpose(0, 2, 3, 1)
                     src = torch.from_numpy(np.ascontiguousarray(blk).view(np.int16)).to(self.dev)
                     pool[layer].index_copy_(0, pages, src)
         torch.cuda.synchronize(self.dev)
@@ -174,5 +178,5 @@ class DeviceDecoder:
         ps = self.shape.page_size
         page = int(self.page_table_np[b, pos // ps])
         k = self.k_pool[layer, page, :, pos % ps, :].cpu().numpy().view(np.uint16)
-        v = self.v_pool[layer, page, :, pos % ps, :].cpu().numpy().view(np.uint16)
+        v = self.v_pool[layer, page, :, :, pos % ps].cpu().numpy().view(np.uint16)
         return k, v

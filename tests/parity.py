@@ -16,8 +16,7 @@ isolated (the strict check): each step, the oracle runs first and its
   (k+1)-th margin exceeds MARGIN (else the GPU's set must be one of the two
   correct ones); router logits within ROUTER_TOL; the layer's output
   residual within X_TOL; the new K/V entries within one bfloat16 ulp (plus
-  KV_ABS of the head vector's largest entry, for entries that cancel to
-  almost nothing, where fp32 accumulation error alone exceeds an ulp).
+  KV_ABS of the head vector's largest entry, see below).
   Logits within LOGIT_TOL; greedy token equal unless the oracle's top-2 gap
   is within GAP_FACTOR times the step's largest logit difference.
 
@@ -49,7 +48,12 @@ MARGIN = 1e-3
 GAP_FACTOR = 4.0
 ROUTER_TOL = 5e-4    # isolated mode: |router logit| difference per layer
 X_TOL = 2e-3         # isolated mode: max|dx| / max|x| of each layer's output residual
-KV_ABS = 1e-5        # isolated mode: new K/V slack beyond one ulp, relative to the head vector's max
+# isolated mode: new K/V slack beyond one ulp, relative to the head vector's max.  The
+# injected residual is the oracle's rounded to fp32, so now and then one element of the
+# normalized input lands on the other side of a bf16 rounding boundary; that moves every
+# k/v entry by |w| * ulp(xn) ~ 1e-4, more than an ulp for entries near zero.  A wrong
+# rotation, position or head gives differences of the order of the entries themselves.
+KV_ABS = 5e-4
 
 
 @dataclass
