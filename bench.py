@@ -106,6 +106,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=25.0)
     ap.add_argument("--trace", default="", help="write a Perfetto timeline of one extra step to this path")
+    ap.add_argument("--copy-calib", type=int, default=0,
+                    help="after the run, one plain device-to-device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one MI355X: the decode megakernel runs on a single GPU; "
@@ -179,6 +181,17 @@ def main():
         rec = buf.view(ntask, tr.WORDS).cpu().numpy()
         log("[bench] trace " + json.dumps(tr.summarize(tasks, qoff, rec)))
         tr.dump(args.trace, tasks, qoff, rec)
+
+    if args.copy_calib:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch calibrate the counters
+        n = args.copy_calib // 2
+        src = torch.ones(n, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize(dev)
+        dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        log(f"[bench] calibration copy of {2 * n} bytes done")
+        del src, dst
 
     cpu = None
     if not args.no_cpu:
