@@ -110,8 +110,8 @@ def main():
                     help="after the run, one plain device-to-device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one MI355X: the decode megakernel runs on a single GPU; "
-              "multi-GPU runs are not part of this build (use --gpus 1)", file=sys.stderr)
+        print("bench.py measures one MI355X: the decode megakernel runs on a single GPU and has no "
+              "multi-GPU path (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -52,7 +52,7 @@ struct mk_ctx {
   mk_config cfg{};
   bool built = false, bound = false, need_reset = false;
   int ncu = 0, n_attn = 0, n_gu = 0, n_out = 0, n_lm = 0, n_ctr = 0, n_tickets = 0;
-  int out_rows_max = 0, gu_rows_max = 0, lm_rows_max = 0;
+  int out_rows_max = 0, gu_rows_max = 0, lm_rows_max = 0, pre_rows_max = 0;
   int lds_b = 0, lds_c = 0, lds_p = 0, pf_bytes = 0;
   size_t lds_bytes = 0;
   std::vector<Task> tasks;
@@ -118,6 +118,7 @@ static Task make_task(int op, int layer) {
   t.op = op;
   t.layer = layer;
   t.wait[0] = t.wait[1] = -1;
+  t.late_wait = -1;
   t.signal = -1;
   return t;
 }
@@ -128,19 +129,28 @@ static int simulate_raw(const Task* tasks, int nt, const int32_t* qoff, int ncu,
     return fail(MK_ERR_INVALID_ARG, "malformed task table");
   for (int q = 0; q < ncu; ++q)
     if (qoff[q + 1] < qoff[q]) return fail(MK_ERR_INVALID_ARG, "queue offsets not ascending");
+  // a task's waits: the two before its body and the one inside it (which, for
+  // progress, counts like the others: the task signals only after all three)
+  auto waits = [](const Task& t, int k, int* ctr_out, int* fan_out) {
+    *ctr_out = k < 2 ? t.wait[k] : t.late_wait;
+    *fan_out = k < 2 ? t.fanin[k] : t.late_fanin;
+  };
   std::vector<int64_t> ctr(n_ctr, 0), signals(n_ctr, 0);
   for (int i = 0; i < nt; ++i) {
     const Task& t = tasks[i];
-    if (t.signal >= n_ctr || t.wait[0] >= n_ctr || t.wait[1] >= n_ctr)
+    if (t.signal >= n_ctr || t.wait[0] >= n_ctr || t.wait[1] >= n_ctr || t.late_wait >= n_ctr)
       return fail(MK_ERR_INVALID_ARG, "counter index out of range");
     if (t.signal >= 0) signals[t.signal]++;
   }
   // every wait must name the full fan-in of its counter
   for (int i = 0; i < nt; ++i)
-    for (int k = 0; k < 2; ++k)
-      if (tasks[i].wait[k] >= 0 && signals[tasks[i].wait[k]] != tasks[i].fanin[k])
+    for (int k = 0; k < 3; ++k) {
+      int w, f;
+      waits(tasks[i], k, &w, &f);
+      if (w >= 0 && signals[w] != f)
         return fail(MK_ERR_SCHEDULE, "schedule: task " + std::to_string(i) +
                                          " waits for a fan-in that differs from the signals on its counter");
+    }
   std::vector<int> head(qoff, qoff + ncu);
   int done = 0;
   bool progress = true;
@@ -150,8 +160,11 @@ static int simulate_raw(const Task* tasks, int nt, const int32_t* qoff, int ncu,
       while (head[q] < qoff[q + 1]) {
         const Task& t = tasks[head[q]];
         bool ready = true;
-        for (int k = 0; k < 2; ++k)
-          if (t.wait[k] >= 0 && ctr[t.wait[k]] < t.fanin[k]) ready = false;
+        for (int k = 0; k < 3; ++k) {
+          int w, f;
+          waits(t, k, &w, &f);
+          if (w >= 0 && ctr[w] < f) ready = false;
+        }
         if (!ready) break;
         if (t.signal >= 0) ctr[t.signal]++;
         head[q]++;
@@ -252,17 +265,31 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
   c->n_ctr = (L + 1) * kCtrPerLayer;
   c->n_tickets = L * B * f.n_kv_heads + 1 + L;  // attention (seq, kv head) merges, LM argmax, router top-k
 
-  // fan-ins
+  // Stage 1 rows: the router's rows go to the last n_rcu compute units (they
+  // also take the top-k), Wqkv rows to the others, so no unit has two stage-1
+  // tasks and the routing is ready as early as the QKV rows.
   const int R1 = qkv_rows + E;
+  const int n_rcu = std::min(ncu - 1, std::max(1, (int)(((int64_t)ncu * E + R1 - 1) / R1)));
+  const int n_qcu = ncu - n_rcu;
+  auto pre_rows = [&](int q, int* r0, int* r1) {
+    if (q < n_qcu) {
+      split_rows(qkv_rows, n_qcu, q, r0, r1);
+    } else {
+      split_rows(E, n_rcu, q - n_qcu, r0, r1);
+      *r0 += qkv_rows;
+      *r1 += qkv_rows;
+    }
+  };
   std::vector<int> n_qkv_tasks(L, 0), n_router_tasks(L, 0), n_out_tasks(L, 0);
   int n_lm = 0;
   c->out_rows_max = 0;
   c->lm_rows_max = 0;
+  c->pre_rows_max = 0;
   for (int q = 0; q < ncu; ++q) {
     int r0, r1;
-    split_rows(R1, ncu, q, &r0, &r1);
-    if (r0 < std::min(r1, qkv_rows)) n_qkv_tasks[0]++;
-    if (std::max(r0, qkv_rows) < r1) n_router_tasks[0]++;
+    pre_rows(q, &r0, &r1);
+    if (r1 > r0) (r0 < qkv_rows ? n_qkv_tasks[0] : n_router_tasks[0])++;
+    c->pre_rows_max = std::max(c->pre_rows_max, r1 - r0);
     split_rows(H, ncu, q, &r0, &r1);
     if (r1 > r0) n_out_tasks[0]++;
     c->out_rows_max = std::max(c->out_rows_max, r1 - r0);
@@ -283,21 +310,18 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
     c->qoff[q] = (int)c->tasks.size();
     for (int l = 0; l < L; ++l) {
       int r0, r1;
-      split_rows(R1, ncu, q, &r0, &r1);
-      // PRE: the qkv part and the router part of this range
-      const int cut0[2] = {r0, std::max(r0, qkv_rows)};
-      const int cut1[2] = {std::min(r1, qkv_rows), r1};
-      for (int part = 0; part < 2; ++part) {
-        if (cut0[part] >= cut1[part]) continue;
+      pre_rows(q, &r0, &r1);
+      if (r1 > r0) {
+        const bool router = r0 >= qkv_rows;
         Task t = make_task(OP_PRE, l);
         if (l > 0) {
           t.wait[0] = ctr_index(l - 1, C_XNEXT);
           t.fanin[0] = n_out_tasks[l - 1];
         }
-        t.r0 = cut0[part];
-        t.r1 = cut1[part];
-        t.signal = ctr_index(l, part == 0 ? C_QKV : C_ROUTER);
-        if (part == 1) t.count = n_router_tasks[l];  // the last of them publishes the layer's routing
+        t.r0 = r0;
+        t.r1 = r1;
+        t.signal = ctr_index(l, router ? C_ROUTER : C_QKV);
+        if (router) t.count = n_router_tasks[l];  // the last of them publishes the layer's routing
         c->tasks.push_back(t);
       }
       // stage 2
@@ -321,11 +345,13 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
       // OUT
       split_rows(H, ncu, q, &r0, &r1);
       if (r1 > r0) {
+        // expert rows first (needs gate/up), then Wo rows (needs attention): the
+        // attention counter is waited inside the task, after the down projection
         Task t = make_task(OP_OUT, l);
-        t.wait[0] = ctr_index(l, C_ATTN);
-        t.fanin[0] = n_attn;
-        t.wait[1] = ctr_index(l, C_GATEUP);
-        t.fanin[1] = n_gu;
+        t.wait[0] = ctr_index(l, C_GATEUP);
+        t.fanin[0] = n_gu;
+        t.late_wait = ctr_index(l, C_ATTN);
+        t.late_fanin = n_attn;
         t.r0 = r0;
         t.r1 = r1;
         t.signal = ctr_index(l, C_XNEXT);
@@ -367,7 +393,7 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
   if ((size_t)c->lds_p > lds_cap)
     return fail(MK_ERR_UNSUPPORTED, "LDS need " + std::to_string(c->lds_p) + " exceeds " + std::to_string(lds_cap));
   // region P: the largest first weight tile (PRE rows of Wqkv/router, OUT rows of Wo), as far as LDS allows
-  const size_t pre_tile = (size_t)((R1 + ncu - 1) / ncu + 1) * H * 2;
+  const size_t pre_tile = (size_t)c->pre_rows_max * H * 2;
   const size_t out_tile = (size_t)c->out_rows_max * f.n_q_heads * f.head_dim * 2;
   size_t pf = std::min(std::max(pre_tile, out_tile), lds_cap - (size_t)c->lds_p);
   const char* pf_env = std::getenv("MK_PREFETCH_BYTES");

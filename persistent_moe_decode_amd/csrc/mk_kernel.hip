@@ -992,8 +992,27 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf)
   float* ao = (float*)s.C;                                    // [out_rows_max][maxB]
   float* contrib = ao + (size_t)a.out_rows_max * a.max_batch;  // [out_rows_max][maxB*topk]
   const int maxBK = a.max_batch * a.topk;
-  // attention output projection
   uint16_t* xs = (uint16_t*)s.A;
+  // expert down projections: their inputs (gate/up) are ready when the task starts
+  load_topk(a, l, s.tk);
+  copy_to_lds(xs, a.h + (size_t)l * a.max_batch * a.topk * a.I, n * a.topk * a.I);
+  __syncthreads();
+  const TopK* tk = s.tk;
+  mark(a, qi, 0);
+  JobDown jd;
+  jd.tk = tk;
+  jd.W = wptr(a, widx(l, WL_DOWN));
+  jd.hs = xs;
+  jd.contrib = contrib;
+  jd.r0 = t.r0;
+  jd.H = a.H;
+  jd.I = a.I;
+  jd.nU = tk->nU;
+  jd.maxBK = maxBK;
+  run_rowdots(a.I, nr * tk->nU, tk->maxtok, jd);
+  mark(a, qi, 1);
+  // attention output projection: wait for attention, Wo rows are already in LDS
+  wait_counter(a, t.late_wait, t.late_fanin, qi, s.flags + 13);  // its barrier also frees xs
   copy_to_lds(xs, a.attn_out + (size_t)l * a.max_batch * AD, n * AD);
   prefetch_wait();
   JobO jo;
@@ -1006,25 +1025,6 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf)
   jo.xs = xs;
   jo.ao = ao;
   run_rowdots(AD, nr, n, jo);
-  mark(a, qi, 0);
-  // expert down projections
-  __syncthreads();  // every wave is done with xs
-  load_topk(a, l, s.tk);
-  const TopK* tk = s.tk;
-  copy_to_lds(xs, a.h + (size_t)l * a.max_batch * a.topk * a.I, n * a.topk * a.I);
-  __syncthreads();
-  mark(a, qi, 1);
-  JobDown jd;
-  jd.tk = tk;
-  jd.W = wptr(a, widx(l, WL_DOWN));
-  jd.hs = xs;
-  jd.contrib = contrib;
-  jd.r0 = t.r0;
-  jd.H = a.H;
-  jd.I = a.I;
-  jd.nU = tk->nU;
-  jd.maxBK = maxBK;
-  run_rowdots(a.I, nr * tk->nU, tk->maxtok, jd);
   __syncthreads();
   mark(a, qi, 2);
   // x_{l+1} = (x_l + attn) + sum_j w_j y_j

@@ -43,7 +43,9 @@ struct Task {
   int32_t signal;     // counter to increment once when done, or -1
   int32_t r0, r1;     // row range (PRE, OUT, LMHEAD)
   int32_t idx, count; // index of this task among the op's tasks of the layer, and their number
-  int32_t pad[21];
+  int32_t late_wait;  // counter waited inside the body, once its first part is done (-1 = none)
+  int32_t late_fanin;
+  int32_t pad[19];
 };
 static_assert(sizeof(Task) == kTaskInts * 4, "task descriptor is 128 bytes");
 

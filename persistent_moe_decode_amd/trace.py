@@ -6,9 +6,9 @@ fetched, when its dependencies were met, up to four phase marks inside the
 body, and when it had signalled.  This module joins them with the task table.
 
 Phase marks per op: PRE [norm done]; ATTN [q rotated and new K/V written,
-positions done, partial stored]; GATEUP [top-k done, norm done]; OUT [Wo rows
-done, top-k and h loaded, down rows done]; LMHEAD [norm done, rows done,
-local argmax done].
+positions done, partial stored]; GATEUP [routing loaded, norm done]; OUT
+[routing and h loaded, down rows done, attention waited and Wo rows done];
+LMHEAD [norm done, rows done, local argmax done].
 """
 from __future__ import annotations
 
@@ -77,7 +77,9 @@ def perfetto(tasks: np.ndarray, qoff: np.ndarray, rec: np.ndarray) -> dict:
             name = f"{op} L{int(tasks[q, 1])}"
             if b > a:
                 ev.append({"name": "wait " + name, "ph": "X", "ts": a, "dur": b - a, "pid": 0, "tid": cu})
-            ev.append({"name": name, "ph": "X", "ts": b, "dur": max(c - b, 0.001), "pid": 0, "tid": cu})
+            marks = [float((m - t0) * TICK_US) for m in rec[q, 2:6] if m > 0]
+            ev.append({"name": name, "ph": "X", "ts": b, "dur": max(c - b, 0.001), "pid": 0, "tid": cu,
+                       "args": {"phase_ends_us": [round(m, 3) for m in marks], "task": int(q)}})
     return {"traceEvents": ev, "displayTimeUnit": "ns"}
 
 

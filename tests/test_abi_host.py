@@ -11,7 +11,7 @@ import synth
 from persistent_moe_decode_amd import mk
 
 OP_PRE, OP_ATTN, OP_GATEUP, OP_OUT, OP_LMHEAD = 1, 2, 3, 4, 5
-F_OP, F_LAYER, F_WAIT0, F_WAIT1, F_FAN0, F_FAN1, F_SIGNAL, F_R0, F_R1, F_IDX, F_COUNT = range(11)
+F_OP, F_LAYER, F_WAIT0, F_WAIT1, F_FAN0, F_FAN1, F_SIGNAL, F_R0, F_R1, F_IDX, F_COUNT, F_LATE, F_LATE_FAN = range(13)
 
 
 def test_library_exports_every_declared_symbol():
@@ -148,6 +148,39 @@ def test_simulator_catches_wrong_fanin():
     t[i, F_FAN0] -= 1
     code, _ = mk.simulate_table(t, qoff, nctr)
     assert code == mk.CODES["MK_ERR_SCHEDULE"]
+
+
+def test_simulator_counts_the_in_body_wait():
+    tasks, qoff, nctr = _tiny_table()
+    outs = np.nonzero(tasks[:, F_OP] == OP_OUT)[0]
+    assert np.all(tasks[outs, F_LATE] >= 0)           # output tasks wait for attention inside the body
+    t = tasks.copy()
+    t[outs[0], F_LATE_FAN] += 1
+    code, _ = mk.simulate_table(t, qoff, nctr)
+    assert code == mk.CODES["MK_ERR_SCHEDULE"]
+    # an in-body wait on a counter that only a later task of the same queue signals deadlocks
+    t = tasks.copy()
+    q0 = t[qoff[0]:qoff[1]]
+    i_out = int(np.nonzero((q0[:, F_OP] == OP_OUT) & (q0[:, F_LAYER] == 0))[0][0])
+    nxt_pre = int(np.nonzero((q0[:, F_OP] == OP_PRE) & (q0[:, F_LAYER] == 1))[0][0])
+    q0[i_out, F_LATE] = q0[nxt_pre, F_SIGNAL]
+    q0[i_out, F_LATE_FAN] = int(np.sum(t[:, F_SIGNAL] == q0[nxt_pre, F_SIGNAL]))
+    t[qoff[0]:qoff[1]] = q0
+    code, done = mk.simulate_table(t, qoff, nctr)
+    assert code == mk.CODES["MK_ERR_SCHEDULE"] and done < len(t)
+
+
+def test_router_rows_have_their_own_units():
+    w = synth.workload("moe30b_8k")
+    c = _ctx(w.shape, 1, w.max_pages_per_seq, w.num_pages)
+    c.build_schedule(256, 8192)
+    tasks, qoff = c.schedule()
+    for q in range(256):
+        pre = tasks[qoff[q]:qoff[q + 1]]
+        pre = pre[(pre[:, F_OP] == OP_PRE) & (pre[:, F_LAYER] == 0)]
+        assert len(pre) == 1
+    routers = tasks[(tasks[:, F_OP] == OP_PRE) & (tasks[:, F_R0] >= w.shape.qkv_rows) & (tasks[:, F_LAYER] == 0)]
+    assert 1 <= len(routers) <= 8 and np.all(routers[:, F_COUNT] == len(routers))
 
 
 @pytest.mark.parametrize("lens,nkv,ntasks", [
