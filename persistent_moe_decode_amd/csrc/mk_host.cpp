@@ -214,7 +214,7 @@ static WsLayout layout_workspace(const mk_ctx* c) {
   w.x = take(4 * (L + 1) * B * f.hidden);
   w.qkv = take(4 * L * B * qkv_rows);
   w.rlog = take(4 * L * B * f.n_experts);
-  w.attn_part = take(4 * L * c->n_attn * group * (f.head_dim + 2));
+  w.attn_part = take((size_t)4 * L * c->n_attn * attn_part_stride(group, f.head_dim));
   w.attn_out = take(2 * L * B * f.n_q_heads * f.head_dim);
   w.h = take(2 * L * B * f.top_k * f.inter);
   w.lm_part = take(4 * 2 * c->n_lm * B);
@@ -384,18 +384,18 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
   size_t c_gu = (size_t)std::min(c->gu_rows_max, kGuPass) * B * 2 * 4;
   size_t c_out = (size_t)c->out_rows_max * B * 4 + (size_t)c->out_rows_max * B * f.top_k * 4;
   size_t c_lm = (size_t)std::min(c->lm_rows_max, kLmPass) * B * 4;
-  size_t c_attn = std::max((size_t)kWaves * 16 * kMaxGroup * 4 + (size_t)kWaves * group * (f.head_dim + 2) * 4,
-                           (size_t)n_attn * group * 2 * 4 + (size_t)group * 4);  // merge scales of all chunks
+  // attention: the waves' partial results, or (last chunk) the (max, sum) of all chunks plus one float4 per thread
+  size_t c_attn = std::max((size_t)kWaves * (group * f.head_dim + 2 * kMaxGroup) * 4,
+                           align_up((size_t)n_attn * group * 2 * 4, 16) + (size_t)kThreads * 16);
   size_t c_bytes = align_up(std::max({c_gu, c_out, c_lm, c_attn}), 256);
   c->lds_b = (int)a_bytes;
   c->lds_c = (int)(a_bytes + b_bytes);
   c->lds_p = (int)(a_bytes + b_bytes + c_bytes);
   if ((size_t)c->lds_p > lds_cap)
     return fail(MK_ERR_UNSUPPORTED, "LDS need " + std::to_string(c->lds_p) + " exceeds " + std::to_string(lds_cap));
-  // region P: the largest first weight tile (PRE rows of Wqkv/router, OUT rows of Wo), as far as LDS allows
-  const size_t pre_tile = (size_t)c->pre_rows_max * H * 2;
-  const size_t out_tile = (size_t)c->out_rows_max * f.n_q_heads * f.head_dim * 2;
-  size_t pf = std::min(std::max(pre_tile, out_tile), lds_cap - (size_t)c->lds_p);
+  // region P: the rest of LDS, for the first weight tile of PRE and OUT tasks
+  // (rows of Wqkv / router / Wo) and the first K/V pages of attention chunks
+  size_t pf = lds_cap - (size_t)c->lds_p;
   const char* pf_env = std::getenv("MK_PREFETCH_BYTES");
   if (pf_env) pf = std::min(pf, (size_t)std::atoll(pf_env));
   c->pf_bytes = (int)(pf / 1024 * 1024);

@@ -30,6 +30,18 @@ using namespace mk;
 
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
 
+// Weights are addressed through global-address-space pointers and LDS tiles
+// through LDS pointers.  A generic pointer (one the compiler cannot place)
+// becomes a FLAT access, which counts against both the memory and the LDS
+// wait counters, so every later LDS read would wait for all weight loads in
+// flight.
+#define AS_GLOBAL __attribute__((address_space(1)))
+#define AS_LDS __attribute__((address_space(3)))
+typedef uint32_t u32x4_v __attribute__((ext_vector_type(4)));
+typedef const AS_GLOBAL uint16_t gu16;
+typedef const AS_GLOBAL u32x4_v gu4;
+typedef const AS_LDS u32x4_v lu4;
+
 static constexpr float kNegInf = -__builtin_huge_valf();
 
 // ---------------------------------------------------------------------------
@@ -55,6 +67,15 @@ DEV float dot8(const uint4& w, const uint4& x, float acc) {
   acc = dot2(w.z, x.z, acc);
   acc = dot2(w.w, x.w, acc);
   return acc;
+}
+
+// The thread's index, read through an empty volatile asm: the compiler then
+// cannot hoist per-lane arithmetic out of the persistent task loop, where it
+// would stay live across every task body and spill.
+DEV int tid() {
+  int t = (int)__builtin_amdgcn_workitem_id_x();
+  asm volatile("" : "+v"(t));
+  return t;
 }
 
 template <int CTRL>
@@ -125,7 +146,7 @@ static_assert(4096 + 4 * kMaxBatch * kMaxExperts <= kLdsB, "router logits fit re
 DEV float block_sum(float v, float* red) {
   v = group_sum<64>(v);
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  if ((tid() & 63) == 0) red[tid() >> 6] = v;
   __syncthreads();
   float t = 0.f;
 #pragma unroll
@@ -155,7 +176,7 @@ DEV bool aborting(const KArgs& a) {
 // the spin limit the task raises MK_ERR_DEVICE_TIMEOUT and the grid drains.
 // Returns false when the grid is aborting.
 DEV bool wait_counter(const KArgs& a, int idx, int fanin, int task, int32_t* slot) {
-  if (threadIdx.x == 0) {
+  if (tid() == 0) {
     int ok = aborting(a) ? 0 : 1;
     if (ok && idx >= 0) {
       const uint32_t want = a.epoch * (uint32_t)fanin;
@@ -189,7 +210,7 @@ DEV bool wait_counter(const KArgs& a, int idx, int fanin, int task, int32_t* slo
 DEV void signal_counter(const KArgs& a, int idx) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0 && idx >= 0) __hip_atomic_fetch_add(a.ctr + idx, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid() == 0 && idx >= 0) __hip_atomic_fetch_add(a.ctr + idx, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Ticket for "last of count arrivals does the merge": returns true in every
@@ -197,7 +218,7 @@ DEV void signal_counter(const KArgs& a, int idx) {
 DEV bool arrive_last(uint32_t* ticket, uint32_t count, int32_t* slot) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid() == 0) {
     const uint32_t old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     const int last = old == count - 1;
     if (last) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -210,14 +231,14 @@ DEV bool arrive_last(uint32_t* ticket, uint32_t count, int32_t* slot) {
 // ---------------------------------------------------------------------------
 // inputs
 
-DEV const uint16_t* wptr(const KArgs& a, int i) { return (const uint16_t*)(uintptr_t)a.wtab[i]; }
+DEV const gu16* wptr(const KArgs& a, int i) { return (const gu16*)(uintptr_t)a.wtab[i]; }
 
 // Trace mark k (0..3) of task qi: the clock when thread 0 passes this point.
 DEV void mark(const KArgs& a, int qi, int k) {
-  if (a.trace && threadIdx.x == 0 && qi < a.trace_cap) a.trace[kTraceWords * (size_t)qi + 2 + k] = wall_clock64();
+  if (a.trace && tid() == 0 && qi < a.trace_cap) a.trace[kTraceWords * (size_t)qi + 2 + k] = wall_clock64();
 }
 
-DEV const uint16_t* token_row(const KArgs& a, int b, int task) {
+DEV const gu16* token_row(const KArgs& a, int b, int task) {
   int tok = a.tokens[b];
   if (tok < 0 || tok >= a.V) {
     raise_error(a, MK_ERR_DEVICE_TOKEN, task, b);
@@ -229,7 +250,7 @@ DEV const uint16_t* token_row(const KArgs& a, int b, int task) {
 // Residual entering `layer` (layer 0: the embedding row).
 // With the layer-input hook set, layers >= 1 (and the final norm) read the
 // residual the caller supplied instead of the one the previous layer wrote.
-DEV float load_x(const KArgs& a, int layer, int b, int i, const uint16_t* emb) {
+DEV float load_x(const KArgs& a, int layer, int b, int i, const gu16* emb) {
   if (layer == 0) return bf2f(emb[i]);
   const float* src = a.x_in ? a.x_in : a.x;
   return src[((size_t)layer * a.max_batch + b) * a.H + i];
@@ -251,21 +272,21 @@ DEV uint16_t d2bf(double v) {
 // double so the one rounding to bf16 is the only one (the normalized input
 // feeds every projection of the layer).  The sums of squares of all rows are
 // reduced together: one barrier for the whole batch.
-DEV void norm_inputs(const KArgs& a, int layer, const uint16_t* gain, uint16_t* xs, double* red8, int task) {
+DEV void norm_inputs(const KArgs& a, int layer, const gu16* gain, uint16_t* xs, double* red8, int task) {
   const int H = a.H, n = a.n;
   double ss[kMaxBatch];
 #pragma unroll
   for (int b = 0; b < kMaxBatch; ++b) {
     ss[b] = 0.0;
     if (b < n) {
-      const uint16_t* emb = layer == 0 ? token_row(a, b, task) : nullptr;
-      for (int i = threadIdx.x; i < H; i += kThreads) {
+      const gu16* emb = layer == 0 ? token_row(a, b, task) : nullptr;
+      for (int i = tid(); i < H; i += kThreads) {
         const double v = load_x(a, layer, b, i, emb);
         ss[b] += v * v;
       }
     }
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = tid() & 63, wave = tid() >> 6;
 #pragma unroll
   for (int b = 0; b < kMaxBatch; ++b) {
     if (b < n) {
@@ -281,8 +302,8 @@ DEV void norm_inputs(const KArgs& a, int layer, const uint16_t* gain, uint16_t* 
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) tot += red8[w * kMaxBatch + b];
     const double inv = 1.0 / sqrt(tot / (double)H + (double)a.eps);
-    const uint16_t* emb = layer == 0 ? token_row(a, b, task) : nullptr;
-    for (int i = threadIdx.x; i < H; i += kThreads)
+    const gu16* emb = layer == 0 ? token_row(a, b, task) : nullptr;
+    for (int i = tid(); i < H; i += kThreads)
       xs[(size_t)b * H + i] = d2bf((double)load_x(a, layer, b, i, emb) * inv * (double)bf2f(gain[i]));
   }
   __syncthreads();
@@ -292,21 +313,34 @@ DEV void norm_inputs(const KArgs& a, int layer, const uint16_t* gain, uint16_t* 
 // Row dot products: each job is one weight row of K bf16 dotted with up to
 // maxnx input vectors held in LDS.  LPR lanes share a row; each lane loads
 // CPL 16-byte chunks (strided by LPR chunks, so a row's loads coalesce) before
-// any arithmetic, so a whole pass of rows is in flight at once.
+// any arithmetic, so a whole pass of rows is in flight at once.  Rows
+// [i0, i1) are done; they come from HBM (job.row, global loads) or, with
+// FromLds, from a weight tile already in LDS (job.lrow).
 
-template <int LPR, int CPL, class Job>
-DEV void rowdots(int njobs, int maxnx, const Job& job) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+template <bool FromLds, int CPL, int STRIDE, class Job>
+DEV void load_row(const Job& job, int i, int li, bool act, uint4 (&wv)[CPL]) {
+  if constexpr (FromLds) {
+    const lu4* wr = job.lrow(i) + li;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) wv[c] = __builtin_bit_cast(uint4, act ? wr[STRIDE * c] : u32x4_v{0, 0, 0, 0});
+  } else {
+    const gu4* wr = job.row(i) + li;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) wv[c] = __builtin_bit_cast(uint4, act ? wr[STRIDE * c] : u32x4_v{0, 0, 0, 0});
+  }
+}
+
+template <int LPR, int CPL, bool FromLds, class Job>
+DEV void rowdots(int i0, int i1, int maxnx, const Job& job) {
+  const int lane = tid() & 63, wave = tid() >> 6;
   constexpr int RPW = 64 / LPR;
   const int sub = lane / LPR, li = lane % LPR;
-  for (int base = 0; base < njobs; base += kWaves * RPW) {
+  for (int base = i0; base < i1; base += kWaves * RPW) {
     const int i = base + wave * RPW + sub;
-    const bool act = i < njobs;
-    const int ic = act ? i : 0;
-    const uint4* wr = job.row(ic) + li;
+    const bool act = i < i1;
+    const int ic = act ? i : i0;
     uint4 wv[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) wv[c] = act ? wr[LPR * c] : make_uint4(0, 0, 0, 0);
+    load_row<FromLds, CPL, LPR>(job, ic, li, act, wv);
     const int nx = act ? job.nx(ic) : 0;
     for (int t = 0; t < maxnx; ++t) {
       const bool on = t < nx;
@@ -320,54 +354,71 @@ DEV void rowdots(int njobs, int maxnx, const Job& job) {
   }
 }
 
-// Any K that is a multiple of 128: 16 lanes per row, runtime chunk count.
-template <class Job>
-DEV void rowdots_generic(int K, int njobs, int maxnx, const Job& job) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Any K that is a multiple of 128: 16 lanes per row, chunks of 8 per load batch.
+template <bool FromLds, class Job>
+DEV void rowdots_generic(int K, int i0, int i1, int maxnx, const Job& job) {
+  const int lane = tid() & 63, wave = tid() >> 6;
   const int sub = lane / 16, li = lane % 16;
   const int cpl = K / 128;
-  for (int base = 0; base < njobs; base += kWaves * 4) {
+  for (int base = i0; base < i1; base += kWaves * 4) {
     const int i = base + wave * 4 + sub;
-    const bool act = i < njobs;
-    const int ic = act ? i : 0;
+    const bool act = i < i1;
+    const int ic = act ? i : i0;
     const int nx = act ? job.nx(ic) : 0;
-    const uint4* wr = job.row(ic) + li;
     for (int t = 0; t < maxnx; ++t) {
       const bool on = t < nx;
       const uint4* xr = job.x(ic, on ? t : 0) + li;
       float acc = 0.f;
-      for (int c = 0; c < cpl; ++c) acc = dot8(act ? wr[16 * c] : make_uint4(0, 0, 0, 0), xr[16 * c], acc);
+      for (int c = 0; c < cpl; ++c) {
+        uint4 w[1];
+        load_row<FromLds, 1, 16>(job, ic, li + 16 * c, act, w);
+        acc = dot8(w[0], xr[16 * c], acc);
+      }
       acc = group_sum<16>(acc);
       if (on && li == 0) job.emit(i, t, acc);
     }
   }
 }
 
-template <class Job>
-DEV void run_rowdots(int K, int njobs, int maxnx, const Job& job) {
-  if (njobs <= 0 || maxnx <= 0) return;
+template <bool FromLds, class Job>
+DEV void rowdots_range(int K, int i0, int i1, int maxnx, const Job& job) {
+  const int nj = i1 - i0;
+  if (nj <= 0 || maxnx <= 0) return;
   const int ch = K / 8;  // 16-byte chunks per row
-  if (njobs <= 8 && ch == 512) return rowdots<64, 8>(njobs, maxnx, job);
-  if (njobs <= 8 && ch == 256) return rowdots<64, 4>(njobs, maxnx, job);
-  if (njobs <= 16 || ch > 256) {
+  if (nj <= 8 && ch == 512) return rowdots<64, 8, FromLds>(i0, i1, maxnx, job);
+  if (nj <= 8 && ch == 256) return rowdots<64, 4, FromLds>(i0, i1, maxnx, job);
+  if (nj <= 16 || ch > 256) {
     switch (ch) {
-      case 64: return rowdots<32, 2>(njobs, maxnx, job);
-      case 96: return rowdots<32, 3>(njobs, maxnx, job);
-      case 128: return rowdots<32, 4>(njobs, maxnx, job);
-      case 256: return rowdots<32, 8>(njobs, maxnx, job);
-      case 512: return rowdots<32, 16>(njobs, maxnx, job);
+      case 64: return rowdots<32, 2, FromLds>(i0, i1, maxnx, job);
+      case 96: return rowdots<32, 3, FromLds>(i0, i1, maxnx, job);
+      case 128: return rowdots<32, 4, FromLds>(i0, i1, maxnx, job);
+      case 256: return rowdots<32, 8, FromLds>(i0, i1, maxnx, job);
+      case 512: return rowdots<32, 16, FromLds>(i0, i1, maxnx, job);
       default: break;
     }
   }
   switch (ch) {
-    case 16: return rowdots<16, 1>(njobs, maxnx, job);
-    case 32: return rowdots<16, 2>(njobs, maxnx, job);
-    case 64: return rowdots<16, 4>(njobs, maxnx, job);
-    case 96: return rowdots<16, 6>(njobs, maxnx, job);
-    case 128: return rowdots<16, 8>(njobs, maxnx, job);
-    case 256: return rowdots<16, 16>(njobs, maxnx, job);
-    default: return rowdots_generic(K, njobs, maxnx, job);
+    case 16: return rowdots<16, 1, FromLds>(i0, i1, maxnx, job);
+    case 32: return rowdots<16, 2, FromLds>(i0, i1, maxnx, job);
+    case 64: return rowdots<16, 4, FromLds>(i0, i1, maxnx, job);
+    case 96: return rowdots<16, 6, FromLds>(i0, i1, maxnx, job);
+    case 128: return rowdots<16, 8, FromLds>(i0, i1, maxnx, job);
+    case 256: return rowdots<16, 16, FromLds>(i0, i1, maxnx, job);
+    default: return rowdots_generic<FromLds>(K, i0, i1, maxnx, job);
   }
+}
+
+// All rows of a job from HBM.
+template <class Job>
+DEV void run_rowdots(int K, int njobs, int maxnx, const Job& job) {
+  rowdots_range<false>(K, 0, njobs, maxnx, job);
+}
+
+// Rows [0, npf) from the LDS tile, the rest from HBM.
+template <class Job>
+DEV void run_rowdots_pf(int K, int njobs, int npf, int maxnx, const Job& job) {
+  rowdots_range<true>(K, 0, npf, maxnx, job);
+  rowdots_range<false>(K, npf, njobs, maxnx, job);
 }
 
 // ---------------------------------------------------------------------------
@@ -382,16 +433,16 @@ DEV void run_rowdots(int K, int njobs, int maxnx, const Job& job) {
 DEV bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
 
 DEV void compute_topk(const KArgs& a, int layer, TopK* tk, float* rbuf) {
-  const int lane = threadIdx.x & 63;
+  const int lane = tid() & 63;
   const int E = a.E, K = a.topk, n = a.n;
   const float* rl = a.rlog + (size_t)layer * a.max_batch * E;
-  for (int i = threadIdx.x; i < n * E; i += kThreads) {
+  for (int i = tid(); i < n * E; i += kThreads) {
     const float v = rl[i];
     rbuf[i] = v != v ? kNegInf : v;  // NaN never outranks a number
   }
   __syncthreads();
   // four threads per (token, expert), each counting a quarter of the rivals; a quad sum joins them
-  for (int i4 = threadIdx.x; i4 < 4 * n * E; i4 += kThreads) {
+  for (int i4 = tid(); i4 < 4 * n * E; i4 += kThreads) {
     const int i = i4 >> 2, part = i4 & 3;
     const int b = i / E, e = i - b * E;
     const float v = rbuf[i];
@@ -412,7 +463,7 @@ DEV void compute_topk(const KArgs& a, int layer, TopK* tk, float* rbuf) {
     }
   }
   __syncthreads();
-  if ((threadIdx.x >> 6) == 0) {
+  if ((tid() >> 6) == 0) {
     // softmax over each token's selected logits, slot order
     if (lane < n) {
       const float v0 = tk->w[lane][0];
@@ -475,15 +526,15 @@ DEV void compute_topk(const KArgs& a, int layer, TopK* tk, float* rbuf) {
 DEV void publish_topk(const KArgs& a, int layer, const TopK* tk) {
   const uint4* src = (const uint4*)tk;
   uint4* dst = (uint4*)(a.topk_g + (size_t)layer * sizeof(TopK));
-  for (int i = threadIdx.x; i < (int)(sizeof(TopK) / 16); i += kThreads) dst[i] = src[i];
-  if (threadIdx.x < a.n * a.topk)
-    a.sel_out[(size_t)layer * a.max_batch * a.topk + threadIdx.x] = tk->sel[threadIdx.x / a.topk][threadIdx.x % a.topk];
+  for (int i = tid(); i < (int)(sizeof(TopK) / 16); i += kThreads) dst[i] = src[i];
+  if (tid() < a.n * a.topk)
+    a.sel_out[(size_t)layer * a.max_batch * a.topk + tid()] = tk->sel[tid() / a.topk][tid() % a.topk];
 }
 
 DEV void load_topk(const KArgs& a, int layer, TopK* tk) {
   const uint4* src = (const uint4*)(a.topk_g + (size_t)layer * sizeof(TopK));
   uint4* dst = (uint4*)tk;
-  for (int i = threadIdx.x; i < (int)(sizeof(TopK) / 16); i += kThreads) dst[i] = src[i];
+  for (int i = tid(); i < (int)(sizeof(TopK) / 16); i += kThreads) dst[i] = src[i];
 }
 
 // ---------------------------------------------------------------------------
@@ -493,25 +544,26 @@ DEV void load_topk(const KArgs& a, int layer, TopK* tk) {
 // task waits for its inputs (the pages' third-ranked gain: weights start
 // streaming before dependencies resolve).  Rows [0, npf) of a job's matrix
 // are then read from P, the rest from HBM.
-DEV void prefetch_to_lds(const uint16_t* src, uint8_t* dst_lds, int nbytes) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint8_t* s8 = (const uint8_t*)src;
+DEV void prefetch_to_lds(const gu16* src, uint8_t* dst_lds, int nbytes) {
+  const int lane = tid() & 63, wave = tid() >> 6;
+  const AS_GLOBAL uint8_t* s8 = (const AS_GLOBAL uint8_t*)src;
   const int nchunk = (nbytes + 1023) >> 10;
   for (int c = wave; c < nchunk; c += kWaves) {
     const int off = (c << 10) + (lane << 4);
     if (off < nbytes)
-      __builtin_amdgcn_global_load_lds((const void*)(s8 + off),
-                                       (__attribute__((address_space(3))) void*)(dst_lds + (c << 10)), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((AS_GLOBAL void*)(s8 + off), (AS_LDS void*)(dst_lds + (c << 10)), 16, 0, 0);
   }
 }
 
 DEV void attn_plan(const KArgs& a, const Task& t, const Lds& s, int qi);
+template <int D>
+DEV void attn_prefetch(const KArgs& a, const Task& t, const Lds& s, int qi);
 
 // Work a task can do before its inputs are ready: the first weight tile of
 // PRE and OUT tasks (rows [r0, r1) of Wqkv / router / Wo) starts streaming
 // into LDS; attention tasks work out their chunk.  Returns the rows prefetched.
 DEV int task_prefetch(const KArgs& a, const Task& t, const Lds& s, int qi) {
-  const uint16_t* src;
+  const gu16* src;
   int K, nrows;
   if (t.op == OP_PRE) {
     K = a.H;
@@ -523,7 +575,12 @@ DEV int task_prefetch(const KArgs& a, const Task& t, const Lds& s, int qi) {
     nrows = t.r1 - t.r0;
     src = wptr(a, widx(t.layer, WL_O)) + (size_t)t.r0 * K;
   } else {
-    if (t.op == OP_ATTN) attn_plan(a, t, s, qi);
+    if (t.op == OP_ATTN) {
+      attn_plan(a, t, s, qi);
+      __syncthreads();
+      if (a.d == 128) attn_prefetch<128>(a, t, s, qi);
+      else attn_prefetch<64>(a, t, s, qi);
+    }
     return 0;
   }
   const int npf = min(nrows, a.pf_bytes / (K * 2));
@@ -538,16 +595,15 @@ DEV void prefetch_wait() {
 }
 
 struct JobPre {
-  const uint16_t* W;
-  const uint16_t* pf;  // prefetched rows (LDS)
+  const gu16* W;
+  const AS_LDS uint16_t* pf;  // prefetched rows [0, npf)
   int npf;
   int r0, K;
   const uint16_t* xs;
   float* out;  // [b][ld] + r0 already applied
   int ld;
-  DEV const uint4* row(int i) const {
-    return i < npf ? (const uint4*)(pf + (size_t)i * K) : (const uint4*)(W + (size_t)(r0 + i) * K);
-  }
+  DEV const gu4* row(int i) const { return (const gu4*)(W + (size_t)(r0 + i) * K); }
+  DEV const lu4* lrow(int i) const { return (const lu4*)(pf + i * K); }
   DEV int nx(int) const { return 1 << 30; }
   DEV const uint4* x(int, int t) const { return (const uint4*)(xs + (size_t)t * K); }
   DEV void emit(int i, int t, float v) const { out[(size_t)t * ld + i] = v; }
@@ -562,7 +618,7 @@ TASK void task_pre(const KArgs& a, const Task& t, const Lds& s, int qi, int npf)
   JobPre j;
   j.K = a.H;
   j.xs = xs;
-  j.pf = (const uint16_t*)s.P;
+  j.pf = (const AS_LDS uint16_t*)s.P;
   j.npf = npf;
   if (t.r0 < a.qkv_rows) {
     j.W = wptr(a, widx(l, WL_QKV));
@@ -575,7 +631,7 @@ TASK void task_pre(const KArgs& a, const Task& t, const Lds& s, int qi, int npf)
     j.out = a.rlog + (size_t)l * a.max_batch * a.E + j.r0;
     j.ld = a.E;
   }
-  run_rowdots(a.H, t.r1 - t.r0, a.n, j);
+  run_rowdots_pf(a.H, t.r1 - t.r0, npf, a.n, j);
   if (t.r0 >= a.qkv_rows) {
     // router rows: the last router task of the layer takes the top-k for everyone
     uint32_t* ticket = a.tickets + (size_t)a.L * a.max_batch * a.nkv + 1 + l;
@@ -614,9 +670,60 @@ struct AttnPage {
   int nvalid;       // positions of the page inside the chunk
 };
 
+// The first pages of a chunk are copied into LDS region P before the task
+// waits for q (K/V of earlier positions never change during a step): K blocks
+// [npp][16][D], then V blocks [npp][D][16].  In a K block the 16-byte pieces
+// of position r are stored XOR-swizzled by r, so the 16 positions a wave
+// reads at one dim offset sit in different banks.
+template <int D>
+DEV int kslot(int r, int cc) {
+  constexpr int NC = D / 8;  // 16-byte pieces per K row
+  return r * NC + (cc ^ (r & (NC - 1)));
+}
+
+template <int D>
+DEV int attn_lds_pages(const KArgs& a, int nblk) {
+  return min(min(nblk, kMaxLdsPages), a.pf_bytes / (2 * 16 * D * 2));
+}
+
+// Issues the copies (all threads; the plan is already in LDS).  Wave 0
+// records which pages are valid and raises the error for the others.
+template <int D>
+DEV void attn_prefetch(const KArgs& a, const Task& t, const Lds& s, int qi) {
+  const int32_t* plan = s.flags + 2;
+  if (!plan[6]) return;
+  const int b = plan[0], g = plan[1], t0 = plan[2], t1 = plan[3];
+  const int npp = attn_lds_pages<D>(a, (t1 - t0 + 15) / 16);
+  constexpr int NI = 16 * D * 2 / 1024;  // 1 KB copies per K (or V) block
+  const int lane = tid() & 63, wave = tid() >> 6;
+  const int32_t* pt = a.page_table + (size_t)b * a.max_pages + t0 / 16;
+  for (int q = wave; q < npp * 2 * NI; q += kWaves) {
+    const int pi = q / (2 * NI), isv = (q / NI) & 1, k = q % NI;
+    const int page = pt[pi];
+    if (page < 0 || page >= a.num_pages) continue;
+    const size_t boff = (((size_t)t.layer * a.num_pages + page) * a.nkv + g) * (size_t)16 * D;
+    const int slot = 64 * k + lane;
+    const int piece = isv ? slot : kslot<D>(slot / (D / 8), slot % (D / 8));  // the swizzle is its own inverse
+    const uint16_t* src = (isv ? a.v_pool : a.k_pool) + boff + (size_t)piece * 8;
+    uint8_t* dst = s.P + (isv ? (size_t)npp * 16 * D * 2 : 0) + (size_t)pi * 16 * D * 2 + k * 1024;
+    __builtin_amdgcn_global_load_lds((AS_GLOBAL void*)src, (AS_LDS void*)dst, 16, 0, 0);
+  }
+  if (wave == 0) {
+    // lane pi checks page pi; one load per lane, one ballot
+    const int page = lane < npp ? pt[lane] : 0;
+    const bool ok = lane < npp && page >= 0 && page < a.num_pages;
+    if (lane < npp && !ok) raise_error(a, MK_ERR_DEVICE_PAGE, qi, page);
+    const uint64_t m = __ballot(ok);
+    if (lane == 0) {
+      s.flags[14] = (int32_t)(uint32_t)m;
+      s.flags[15] = (int32_t)(uint32_t)(m >> 32);
+    }
+  }
+}
+
 template <int D>
 DEV void attn_fetch(const KArgs& a, AttnPage<D>& P, int l, int b, int g, int tb, int t1, int qi) {
-  const int lane = threadIdx.x & 63, r = lane & 15, grp = lane >> 4;
+  const int lane = tid() & 63, r = lane & 15, grp = lane >> 4;
   const int page = a.page_table[(size_t)b * a.max_pages + tb / a.ps];
   const bool pg_ok = page >= 0 && page < a.num_pages;
   if (!pg_ok && lane == 0) raise_error(a, MK_ERR_DEVICE_PAGE, qi, page);
@@ -633,10 +740,30 @@ DEV void attn_fetch(const KArgs& a, AttnPage<D>& P, int l, int b, int g, int tb,
     P.v[t] = vcol ? *(const uint2*)(vb + (16 * t + r) * 16 + 4 * grp) : make_uint2(0, 0);
 }
 
+typedef uint32_t u32x2_v __attribute__((ext_vector_type(2)));
+
+// Page pi of the chunk from its LDS copy.
+template <int D>
+DEV void attn_fetch_lds(const Lds& s, AttnPage<D>& P, int npp, int pi, int tb, int t1) {
+  const int lane = tid() & 63, r = lane & 15, grp = lane >> 4;
+  const uint32_t mask = (uint32_t)s.flags[pi < 32 ? 14 : 15];
+  P.nvalid = ((mask >> (pi & 31)) & 1u) ? min(16, t1 - tb) : 0;
+  const AS_LDS uint8_t* kb = (const AS_LDS uint8_t*)s.P + (size_t)pi * 16 * D * 2;
+  const AS_LDS uint8_t* vb = (const AS_LDS uint8_t*)s.P + (size_t)(npp + pi) * 16 * D * 2;
+  const bool krow = r < P.nvalid, vcol = 4 * grp < P.nvalid;
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c)
+    P.k[c] = __builtin_bit_cast(uint4, krow ? *(const lu4*)(kb + 16 * kslot<D>(r, 4 * c + grp)) : u32x4_v{0, 0, 0, 0});
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t)
+    P.v[t] = __builtin_bit_cast(
+        uint2, vcol ? *(const AS_LDS u32x2_v*)(vb + 2 * ((16 * t + r) * 16 + 4 * grp)) : u32x2_v{0, 0});
+}
+
 template <int D>
 DEV void attn_page(const AttnPage<D>& P, const bf16x8_v (&qb)[D / 32], float scale, float& m, float& lsum,
                    float4_v (&o)[D / 16]) {
-  const int lane = threadIdx.x & 63, grp = lane >> 4;
+  const int lane = tid() & 63, grp = lane >> 4;
   float4_v sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < D / 32; ++c)
@@ -685,11 +812,29 @@ DEV void attn_page(const AttnPage<D>& P, const bf16x8_v (&qb)[D / 32], float sca
   }
 }
 
-// This wave's pages of the chunk; leaves (o, m, sum) per head in mrg[wave][G][d+2].
+// Per-wave results of a chunk in region C: outputs [wave][G][d], maxima and
+// sums [wave][kMaxGroup].
+struct AttnMerge {
+  float* o;
+  float* m;
+  float* l;
+};
+
+DEV AttnMerge attn_merge_area(const Lds& s, int G, int d) {
+  AttnMerge r;
+  r.o = (float*)s.C;
+  r.m = r.o + (size_t)kWaves * G * d;
+  r.l = r.m + kWaves * kMaxGroup;
+  return r;
+}
+
+// This wave's pages of the chunk (blocks wave, wave + 8, ...; the first npp
+// from LDS, the rest from HBM with the next page loaded while the current one
+// is processed); leaves (o, m, sum) per head in the merge area.
 template <int D>
 DEV void attn_wave(const KArgs& a, const Lds& s, int qi, const uint16_t* q_s, int l, int b, int g, int t0, int t1,
-                   float* mrg) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r = lane & 15, grp = lane >> 4;
+                   int npp, const AttnMerge& mrg) {
+  const int lane = tid() & 63, wave = tid() >> 6, r = lane & 15, grp = lane >> 4;
   const int G = a.group;
   bf16x8_v qb[D / 32];
 #pragma unroll
@@ -706,30 +851,33 @@ DEV void attn_wave(const KArgs& a, const Lds& s, int qi, const uint16_t* q_s, in
   int blk = wave;
   if (blk < nblk) {
     AttnPage<D> cur, nxt;
-    attn_fetch<D>(a, cur, l, b, g, t0 + 16 * blk, t1, qi);
+    if (blk < npp) attn_fetch_lds<D>(s, cur, npp, blk, t0 + 16 * blk, t1);
+    else attn_fetch<D>(a, cur, l, b, g, t0 + 16 * blk, t1, qi);
     while (true) {
       const int nb = blk + kWaves;
       const bool more = nb < nblk;
-      if (more) attn_fetch<D>(a, nxt, l, b, g, t0 + 16 * nb, t1, qi);
+      if (more) {
+        if (nb < npp) attn_fetch_lds<D>(s, nxt, npp, nb, t0 + 16 * nb, t1);
+        else attn_fetch<D>(a, nxt, l, b, g, t0 + 16 * nb, t1, qi);
+      }
       attn_page<D>(cur, qb, scale, m, lsum, o);
       if (!more) break;
       cur = nxt;
       blk = nb;
     }
   }
-  // per-head totals over the 4 lane groups, then this wave's row of the merge buffer
+  // per-head totals over the 4 lane groups, then this wave's part of the merge area
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
   if (grp == 0 && r < G) {
-    float* row = mrg + ((size_t)wave * G + r) * (D + 2);
-    row[D] = m;
-    row[D + 1] = lsum;
+    mrg.m[wave * kMaxGroup + r] = m;
+    mrg.l[wave * kMaxGroup + r] = lsum;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int h = 4 * grp + i;
     if (h < G) {
-      float* row = mrg + ((size_t)wave * G + h) * (D + 2);
+      float* row = mrg.o + ((size_t)wave * G + h) * D;
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) row[16 * t + r] = o[t][i];
     }
@@ -737,11 +885,10 @@ DEV void attn_wave(const KArgs& a, const Lds& s, int qi, const uint16_t* q_s, in
 }
 
 // The chunk of split task t.idx, from the step's sequence lengths only, so it
-// runs before the task's wait; thread 0 writes it to plan = flags[2..9]
-// (the wait's barrier publishes it).
+// runs before the task's wait; thread 0 writes it to plan = flags[2..9].
 DEV void attn_plan(const KArgs& a, const Task& t, const Lds& s, int qi) {
   int32_t* plan = s.flags + 2;  // b, g, t0, t1, first, nch, ok, p
-  if (threadIdx.x == 0) {
+  if (tid() == 0) {
     int32_t lens1[kMaxBatch];
     const int cap = a.max_pages * a.ps;
 #pragma unroll
@@ -761,16 +908,114 @@ DEV void attn_plan(const KArgs& a, const Task& t, const Lds& s, int qi) {
   }
 }
 
+// Last chunk of (b, g) merges all chunks j of the segment:
+//   o_h = sum_j e^(m_jh - M_h) o_jh / sum_j e^(m_jh - M_h) l_jh,  M_h = max_j m_jh.
+// Thread (slice sl, float4 f) takes chunks sl, sl + S, ...; slices are summed
+// in a fixed order.  When all partials fit in region P they are copied there
+// with the LDS DMA (one memory round trip, no registers held); otherwise
+// every thread issues its global loads in batches before using them.
+DEV void attn_combine(const KArgs& a, const Lds& s, const float* parts, int nch, uint16_t* out) {
+  const int G = a.group, d = a.d, GD = G * d, CS = attn_part_stride(G, d);
+  const int nf4 = GD / 4, S = kThreads / nf4;
+  const int sl = tid() / nf4, f = tid() - sl * nf4;
+  const bool act = sl < S;
+  const int hh = 4 * f / d;
+  float* mj = (float*)s.C;                                                 // [nch][G]
+  float* lj = mj + (size_t)nch * G;                                        // [nch][G]
+  float4* red = (float4*)(s.C + ((2 * (size_t)nch * G * 4 + 15) & ~(size_t)15));  // [kThreads]
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float Ls = 0.f;
+  if ((size_t)nch * CS * 4 <= (size_t)a.pf_bytes) {
+    const int lane = tid() & 63, wave = tid() >> 6;
+    const int n16 = nch * CS / 4;  // 16-byte pieces
+    const AS_GLOBAL uint8_t* src = (const AS_GLOBAL uint8_t*)parts;
+    for (int q = wave; 64 * q < n16; q += kWaves) {
+      const int piece = 64 * q + lane;
+      if (piece < n16)
+        __builtin_amdgcn_global_load_lds((AS_GLOBAL void*)(src + 16 * (size_t)piece), (AS_LDS void*)(s.P + 1024 * q),
+                                         16, 0, 0);
+    }
+    prefetch_wait();
+    const float* pl = (const float*)s.P;
+    float M = kNegInf;
+    for (int j = 0; j < nch; ++j) M = fmaxf(M, pl[(size_t)j * CS + GD + hh]);
+    for (int j = 0; j < nch; ++j)
+      Ls += pl[(size_t)j * CS + GD + kMaxGroup + hh] * __expf(pl[(size_t)j * CS + GD + hh] - M);
+    if (act) {
+      for (int j = sl; j < nch; j += S) {
+        const float sc = __expf(pl[(size_t)j * CS + GD + hh] - M);
+        const float4 v = *(const float4*)(pl + (size_t)j * CS + 4 * f);
+        acc.x += v.x * sc;
+        acc.y += v.y * sc;
+        acc.z += v.z * sc;
+        acc.w += v.w * sc;
+      }
+    }
+  } else {
+    constexpr int R = 8;
+    float4 v[R];
+    auto load = [&](int k0) {
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const int j = sl + S * (k0 + k);
+        v[k] = (act && j < nch) ? *(const float4*)(parts + (size_t)j * CS + 4 * f) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    };
+    load(0);
+    for (int i = tid(); i < nch * G; i += kThreads) {
+      const int j = i / G, h = i - j * G;
+      mj[i] = parts[(size_t)j * CS + GD + h];
+      lj[i] = parts[(size_t)j * CS + GD + kMaxGroup + h];
+    }
+    __syncthreads();
+    float M = kNegInf;
+    for (int j = 0; j < nch; ++j) M = fmaxf(M, mj[j * G + hh]);
+    for (int j = 0; j < nch; ++j) Ls += lj[j * G + hh] * __expf(mj[j * G + hh] - M);
+    for (int k0 = 0;; k0 += R) {
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const int j = sl + S * (k0 + k);
+        if (act && j < nch) {
+          const float sc = __expf(mj[j * G + hh] - M);
+          acc.x += v[k].x * sc;
+          acc.y += v[k].y * sc;
+          acc.z += v[k].z * sc;
+          acc.w += v[k].w * sc;
+        }
+      }
+      if (sl + S * (k0 + R) >= nch) break;
+      load(k0 + R);
+    }
+  }
+  red[tid()] = acc;
+  __syncthreads();
+  if (tid() < nf4) {
+    float4 o = red[f];
+    for (int k = 1; k < S; ++k) {
+      const float4 w = red[k * nf4 + f];
+      o.x += w.x;
+      o.y += w.y;
+      o.z += w.z;
+      o.w += w.w;
+    }
+    const uint32_t lo = (uint32_t)f2bf(o.x / Ls) | ((uint32_t)f2bf(o.y / Ls) << 16);
+    const uint32_t hi = (uint32_t)f2bf(o.z / Ls) | ((uint32_t)f2bf(o.w / Ls) << 16);
+    *(uint2*)(out + 4 * f) = make_uint2(lo, hi);
+  }
+}
+
 TASK void task_attn(const KArgs& a, const Task& t, const Lds& s, int qi) {
   const int l = t.layer, G = a.group, d = a.d, ps = a.ps;
   const int32_t* plan = s.flags + 2;
   if (!plan[6]) return;
   const int b = plan[0], g = plan[1], t0 = plan[2], t1 = plan[3], first = plan[4], nch = plan[5], p = plan[7];
+  const int nblk = (t1 - t0 + 15) / 16;
+  const int npp = d == 128 ? attn_lds_pages<128>(a, nblk) : attn_lds_pages<64>(a, nblk);
 
   const int half = d / 2;
   uint16_t* q_s = (uint16_t*)s.A;  // [G][d] rotated q, bf16
   const float* qkv = a.qkv + ((size_t)l * a.max_batch + b) * a.qkv_rows;
-  for (int e = threadIdx.x; e < G * half; e += kThreads) {
+  for (int e = tid(); e < G * half; e += kThreads) {
     const int hh = e / half, i = e % half;
     double sd, cd;
     sincos((double)p * a.inv_freq[i], &sd, &cd);
@@ -780,96 +1025,97 @@ TASK void task_attn(const KArgs& a, const Task& t, const Lds& s, int qi) {
     q_s[hh * d + i] = f2bf(x0 * cf - x1 * sf);
     q_s[hh * d + i + half] = f2bf(x0 * sf + x1 * cf);
   }
-  // the chunk holding position p writes the new token's K (rotated) and V
-  if (t1 == p + 1) {
-    const int page = a.page_table[(size_t)b * a.max_pages + p / ps];
-    if (page < 0 || page >= a.num_pages) {
-      if (threadIdx.x == 0) raise_error(a, MK_ERR_DEVICE_PAGE, qi, page);
+  // the chunk holding position p writes the new token's K (rotated) and V, to
+  // HBM and, when its page was copied, to the LDS copy as well
+  const bool mine = t1 == p + 1;
+  const int page = mine ? a.page_table[(size_t)b * a.max_pages + p / ps] : 0;
+  const bool pg_ok = page >= 0 && page < a.num_pages;
+  uint16_t k_lo = 0, k_hi = 0, v_i = 0;  // thread i < d/2: K dims i and i + d/2; thread i < d: V dim i
+  if (mine) {
+    if (!pg_ok) {
+      if (tid() == 0) raise_error(a, MK_ERR_DEVICE_PAGE, qi, page);
     } else {
       const size_t off = ((((size_t)l * a.num_pages + page) * a.nkv + g) * ps + p % ps) * d;
       const float* kk = qkv + (size_t)a.nq * d + (size_t)g * d;
       const float* vv = qkv + (size_t)(a.nq + a.nkv) * d + (size_t)g * d;
-      for (int i = threadIdx.x; i < half; i += kThreads) {
+      const int i = tid();
+      if (i < half) {
         double sd, cd;
         sincos((double)p * a.inv_freq[i], &sd, &cd);
         const float cf = (float)cd, sf = (float)sd;
         const float x0 = kk[i], x1 = kk[i + half];
-        a.k_pool[off + i] = f2bf(x0 * cf - x1 * sf);
-        a.k_pool[off + i + half] = f2bf(x0 * sf + x1 * cf);
+        k_lo = f2bf(x0 * cf - x1 * sf);
+        k_hi = f2bf(x0 * sf + x1 * cf);
+        a.k_pool[off + i] = k_lo;
+        a.k_pool[off + i + half] = k_hi;
       }
       // V pages are stored dims-major: element (dim, slot) of a (page, head) block at dim*page_size + slot
       const size_t voff = (((size_t)l * a.num_pages + page) * a.nkv + g) * (size_t)ps * d + p % ps;
-      for (int i = threadIdx.x; i < d; i += kThreads) a.v_pool[voff + (size_t)i * ps] = f2bf(vv[i]);
+      if (i < d) {
+        v_i = f2bf(vv[i]);
+        a.v_pool[voff + (size_t)i * ps] = v_i;
+      }
     }
   }
+  // copied pages have landed, q is complete, the new K/V are in HBM
   __builtin_amdgcn_s_waitcnt(0);
   __threadfence_block();
+  __syncthreads();
+  const int pp = (p - t0) / 16;
+  if (mine && pg_ok && pp < npp) {
+    const int i = tid(), r = p % 16;
+    uint16_t* kb = (uint16_t*)(s.P + (size_t)pp * 16 * d * 2);
+    uint16_t* vb = (uint16_t*)(s.P + (size_t)(npp + pp) * 16 * d * 2);
+    const int ks = d == 128 ? 0 : 1;
+    if (i < half) {
+      const int c0 = i / 8, c1 = (i + half) / 8;
+      kb[8 * (ks ? kslot<64>(r, c0) : kslot<128>(r, c0)) + i % 8] = k_lo;
+      kb[8 * (ks ? kslot<64>(r, c1) : kslot<128>(r, c1)) + (i + half) % 8] = k_hi;
+    }
+    if (i < d) vb[i * 16 + r] = v_i;
+  }
   __syncthreads();
   mark(a, qi, 0);
 
   // positions of the chunk, 16 (one page) at a time, pages dealt to waves round robin
-  float* mrg = (float*)s.C + kWaves * 16 * kMaxGroup;  // [wave][G][d+2]
+  const AttnMerge mrg = attn_merge_area(s, G, d);
   if (d == 128)
-    attn_wave<128>(a, s, qi, q_s, l, b, g, t0, t1, mrg);
+    attn_wave<128>(a, s, qi, q_s, l, b, g, t0, t1, npp, mrg);
   else
-    attn_wave<64>(a, s, qi, q_s, l, b, g, t0, t1, mrg);
+    attn_wave<64>(a, s, qi, q_s, l, b, g, t0, t1, npp, mrg);
   mark(a, qi, 1);
   __syncthreads();
-  float* part = a.attn_part + ((size_t)l * a.n_attn + t.idx) * G * (d + 2);
-  for (int e = threadIdx.x; e < G * d; e += kThreads) {
-    const int hh = e / d, dim = e % d;
+  // this chunk's partial: the waves' results merged, as [G][d] outputs, G maxima, G sums
+  const int GD = G * d, CS = attn_part_stride(G, d);
+  float* part = a.attn_part + ((size_t)l * a.n_attn + t.idx) * CS;
+  for (int e4 = tid(); e4 < GD / 4; e4 += kThreads) {
+    const int hh = 4 * e4 / d;
     float M = kNegInf;
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mrg[((size_t)w * G + hh) * (d + 2) + d]);
-    float O = 0.f, Ls = 0.f;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mrg.m[w * kMaxGroup + hh]);
+    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+    float Ls = 0.f;
     for (int w = 0; w < kWaves; ++w) {
-      const float* row = mrg + ((size_t)w * G + hh) * (d + 2);
-      const float sc = row[d] == kNegInf ? 0.f : __expf(row[d] - M);
-      O += row[dim] * sc;
-      Ls += row[d + 1] * sc;
+      const float mw = mrg.m[w * kMaxGroup + hh];
+      const float sc = mw == kNegInf ? 0.f : __expf(mw - M);
+      const float4 ow = *(const float4*)(mrg.o + (size_t)w * GD + 4 * e4);
+      O.x += ow.x * sc;
+      O.y += ow.y * sc;
+      O.z += ow.z * sc;
+      O.w += ow.w * sc;
+      Ls += mrg.l[w * kMaxGroup + hh] * sc;
     }
-    part[hh * (d + 2) + dim] = O;
-    if (dim == 0) {
-      part[hh * (d + 2) + d] = M;
-      part[hh * (d + 2) + d + 1] = Ls;
+    *(float4*)(part + 4 * e4) = O;
+    if ((4 * e4) % d == 0) {
+      part[GD + hh] = M;
+      part[GD + kMaxGroup + hh] = Ls;
     }
   }
-  // last chunk of (b, g) merges all chunks: o = sum_j e^(m_j - M) o_j / sum_j e^(m_j - M) l_j
   uint32_t* ticket = a.tickets + ((size_t)l * a.max_batch + b) * a.nkv + g;
   mark(a, qi, 2);
   if (arrive_last(ticket, (uint32_t)nch, s.flags + 10)) {
-    const float* parts = a.attn_part + ((size_t)l * a.n_attn + first) * G * (d + 2);
+    const float* parts = a.attn_part + ((size_t)l * a.n_attn + first) * CS;
     uint16_t* out = a.attn_out + ((size_t)l * a.max_batch + b) * a.nq * d + (size_t)g * G * d;
-    // (m, l) of every chunk and head in one parallel pass, then the per-head
-    // scale factors, then the weighted sums with the partial loads in flight together
-    float* mj = (float*)s.C;             // [nch][G] maxima, then scale factors
-    float* lj = mj + (size_t)nch * G;    // [nch][G] sums
-    float* Lh = lj + (size_t)nch * G;    // [G] merged sums
-    for (int i = threadIdx.x; i < nch * G; i += kThreads) {
-      const float* row = parts + (size_t)i * (d + 2);
-      mj[i] = row[d];
-      lj[i] = row[d + 1];
-    }
-    __syncthreads();
-    if (threadIdx.x < G) {
-      const int hh = threadIdx.x;
-      float M = kNegInf;
-      for (int j = 0; j < nch; ++j) M = fmaxf(M, mj[j * G + hh]);
-      float Ls = 0.f;
-      for (int j = 0; j < nch; ++j) {
-        const float sc = __expf(mj[j * G + hh] - M);
-        mj[j * G + hh] = sc;
-        Ls += lj[j * G + hh] * sc;
-      }
-      Lh[hh] = Ls;
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < G * d; e += kThreads) {
-      const int hh = e / d, dim = e % d;
-      float O = 0.f;
-#pragma unroll 8
-      for (int j = 0; j < nch; ++j) O += parts[((size_t)j * G + hh) * (d + 2) + dim] * mj[j * G + hh];
-      out[hh * d + dim] = f2bf(O / Lh[hh]);
-    }
+    attn_combine(a, s, parts, nch, out);
   }
 }
 
@@ -879,7 +1125,8 @@ TASK void task_attn(const KArgs& a, const Task& t, const Lds& s, int qi) {
 
 struct JobGateUp {
   const TopK* tk;
-  const uint16_t *wg, *wu, *xs;
+  const gu16 *wg, *wu;
+  const uint16_t* xs;
   float* gs;
   int64_t v0;
   int H, I, maxB, topk;
@@ -888,10 +1135,10 @@ struct JobGateUp {
     *r = (int)(vr % I);
     return (int)(vr / I);
   }
-  DEV const uint4* row(int i) const {
+  DEV const gu4* row(int i) const {
     int r;
     const int u = urow(i, &r);
-    return (const uint4*)(((i & 1) ? wu : wg) + ((size_t)tk->U[u] * I + r) * H);
+    return (const gu4*)(((i & 1) ? wu : wg) + ((size_t)tk->U[u] * I + r) * H);
   }
   DEV int nx(int i) const {
     int r;
@@ -933,7 +1180,7 @@ TASK void task_gateup(const KArgs& a, const Task& t, const Lds& s, int qi) {
     j.v0 = v0;
     run_rowdots(a.H, 2 * nvr, mt, j);
     __syncthreads();
-    for (int e = threadIdx.x; e < nvr * mt; e += kThreads) {
+    for (int e = tid(); e < nvr * mt; e += kThreads) {
       const int vi = e / mt, tt = e % mt;
       const int64_t vr = v0 + vi;
       const int u = (int)(vr / a.I), r = (int)(vr % a.I);
@@ -952,15 +1199,14 @@ TASK void task_gateup(const KArgs& a, const Task& t, const Lds& s, int qi) {
 // OUT: rows [r0, r1) of the hidden state.
 
 struct JobO {
-  const uint16_t* W;
-  const uint16_t* pf;  // prefetched rows (LDS)
+  const gu16* W;
+  const AS_LDS uint16_t* pf;  // prefetched rows [0, npf)
   int npf;
   int r0, K, maxB;
   const uint16_t* xs;
   float* ao;
-  DEV const uint4* row(int i) const {
-    return i < npf ? (const uint4*)(pf + (size_t)i * K) : (const uint4*)(W + (size_t)(r0 + i) * K);
-  }
+  DEV const gu4* row(int i) const { return (const gu4*)(W + (size_t)(r0 + i) * K); }
+  DEV const lu4* lrow(int i) const { return (const lu4*)(pf + i * K); }
   DEV int nx(int) const { return 1 << 30; }
   DEV const uint4* x(int, int t) const { return (const uint4*)(xs + (size_t)t * K); }
   DEV void emit(int i, int t, float v) const { ao[(size_t)i * maxB + t] = v; }
@@ -968,13 +1214,13 @@ struct JobO {
 
 struct JobDown {
   const TopK* tk;
-  const uint16_t* W;
+  const gu16* W;
   const uint16_t* hs;
   float* contrib;
   int r0, H, I, nU, maxBK;
-  DEV const uint4* row(int i) const {
+  DEV const gu4* row(int i) const {
     const int rr = i / nU, u = i % nU;
-    return (const uint4*)(W + ((size_t)tk->U[u] * H + r0 + rr) * I);
+    return (const gu4*)(W + ((size_t)tk->U[u] * H + r0 + rr) * I);
   }
   DEV int nx(int i) const { return tk->ntok[i % nU]; }
   DEV const uint4* x(int i, int t) const { return (const uint4*)(hs + (size_t)tk->pair[i % nU][t] * I); }
@@ -984,7 +1230,7 @@ struct JobDown {
 DEV void copy_to_lds(uint16_t* dst, const uint16_t* src, int elems) {
   const uint4* s4 = (const uint4*)src;
   uint4* d4 = (uint4*)dst;
-  for (int i = threadIdx.x; i < elems / 8; i += kThreads) d4[i] = s4[i];
+  for (int i = tid(); i < elems / 8; i += kThreads) d4[i] = s4[i];
 }
 
 TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf) {
@@ -1016,7 +1262,7 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf)
   copy_to_lds(xs, a.attn_out + (size_t)l * a.max_batch * AD, n * AD);
   prefetch_wait();
   JobO jo;
-  jo.pf = (const uint16_t*)s.P;
+  jo.pf = (const AS_LDS uint16_t*)s.P;
   jo.npf = npf;
   jo.W = wptr(a, widx(l, WL_O));
   jo.r0 = t.r0;
@@ -1024,15 +1270,15 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf)
   jo.maxB = a.max_batch;
   jo.xs = xs;
   jo.ao = ao;
-  run_rowdots(AD, nr, n, jo);
+  run_rowdots_pf(AD, nr, npf, n, jo);
   __syncthreads();
   mark(a, qi, 2);
   // x_{l+1} = (x_l + attn) + sum_j w_j y_j
-  for (int e = threadIdx.x; e < nr * n; e += kThreads) {
+  for (int e = tid(); e < nr * n; e += kThreads) {
     const int rr = e / n, b = e % n;
     float moe = 0.f;
     for (int j = 0; j < a.topk; ++j) moe += tk->w[b][j] * contrib[(size_t)rr * maxBK + b * a.topk + j];
-    const uint16_t* emb = l == 0 ? token_row(a, b, qi) : nullptr;
+    const gu16* emb = l == 0 ? token_row(a, b, qi) : nullptr;
     const float xo = load_x(a, l, b, t.r0 + rr, emb);
     a.x[((size_t)(l + 1) * a.max_batch + b) * a.H + t.r0 + rr] = (xo + ao[(size_t)rr * a.max_batch + b]) + moe;
   }
@@ -1042,12 +1288,12 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf)
 // LMHEAD: rows [r0, r1) of the vocabulary, then the greedy argmax.
 
 struct JobLM {
-  const uint16_t* W;
+  const gu16* W;
   int r0, K, V, maxB;
   const uint16_t* xs;
   float* lmv;
   float* logits;
-  DEV const uint4* row(int i) const { return (const uint4*)(W + (size_t)(r0 + i) * K); }
+  DEV const gu4* row(int i) const { return (const gu4*)(W + (size_t)(r0 + i) * K); }
   DEV int nx(int) const { return 1 << 30; }
   DEV const uint4* x(int, int t) const { return (const uint4*)(xs + (size_t)t * K); }
   DEV void emit(int i, int t, float v) const {
@@ -1066,9 +1312,9 @@ DEV void block_argmax(float& v, int& i, float* red) {
     if (better(ov, oi, v, i)) { v = ov; i = oi; }
   }
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) {
-    red[threadIdx.x >> 6] = v;
-    ((int*)red)[8 + (threadIdx.x >> 6)] = i;
+  if ((tid() & 63) == 0) {
+    red[tid() >> 6] = v;
+    ((int*)red)[8 + (tid() >> 6)] = i;
   }
   __syncthreads();
   v = red[0];
@@ -1109,7 +1355,7 @@ TASK void task_lmhead(const KArgs& a, const Task& t, const Lds& s, int qi) {
       if (b >= a.n) break;
       float v = kNegInf;
       int i = 0x7fffffff;
-      for (int r = threadIdx.x; r < np; r += kThreads) {
+      for (int r = tid(); r < np; r += kThreads) {
         float x = j.lmv[(size_t)r * a.max_batch + b];
         if (x != x) x = kNegInf;
         if (better(x, j.r0 + r, v, i)) { v = x; i = j.r0 + r; }
@@ -1119,7 +1365,7 @@ TASK void task_lmhead(const KArgs& a, const Task& t, const Lds& s, int qi) {
     }
   }
   mark(a, qi, 1);
-  if (threadIdx.x == 0) {
+  if (tid() == 0) {
     for (int b = 0; b < a.n; ++b) {
       a.lm_part[((size_t)t.idx * a.max_batch + b) * 2] = best_v[b];
       ((int*)a.lm_part)[((size_t)t.idx * a.max_batch + b) * 2 + 1] = best_i[b];
@@ -1131,13 +1377,13 @@ TASK void task_lmhead(const KArgs& a, const Task& t, const Lds& s, int qi) {
     for (int b = 0; b < a.n; ++b) {
       float v = kNegInf;
       int i = 0x7fffffff;
-      for (int k = threadIdx.x; k < a.n_lm; k += kThreads) {
+      for (int k = tid(); k < a.n_lm; k += kThreads) {
         const float x = a.lm_part[((size_t)k * a.max_batch + b) * 2];
         const int xi = ((const int*)a.lm_part)[((size_t)k * a.max_batch + b) * 2 + 1];
         if (better(x, xi, v, i)) { v = x; i = xi; }
       }
       block_argmax(v, i, s.red);
-      if (threadIdx.x == 0 && a.next_tok) a.next_tok[b] = i;
+      if (tid() == 0 && a.next_tok) a.next_tok[b] = i;
     }
   }
 }
@@ -1152,12 +1398,12 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a)
   for (int q = q0; q < q1; ++q) {
     const Task t = a.tasks[q];
     uint64_t t_fetch = 0, t_ready = 0;
-    if (a.trace && threadIdx.x == 0) t_fetch = wall_clock64();
+    if (a.trace && tid() == 0) t_fetch = wall_clock64();
     // immutable weights start streaming into LDS before the inputs are ready
     const int npf = task_prefetch(a, t, s, q);
     bool ok = wait_counter(a, t.wait[0], t.fanin[0], q, s.flags + 0);
     if (ok && t.wait[1] >= 0) ok = wait_counter(a, t.wait[1], t.fanin[1], q, s.flags + 1);
-    if (a.trace && threadIdx.x == 0) t_ready = wall_clock64();
+    if (a.trace && tid() == 0) t_ready = wall_clock64();
     if (ok) {
       switch (t.op) {
         case OP_PRE: task_pre(a, t, s, q, npf); break;
@@ -1169,7 +1415,7 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a)
       }
     }
     signal_counter(a, t.signal);
-    if (a.trace && threadIdx.x == 0 && q < a.trace_cap) {
+    if (a.trace && tid() == 0 && q < a.trace_cap) {
       uint64_t* r = a.trace + kTraceWords * (size_t)q;
       r[0] = t_fetch;
       r[1] = t_ready;
@@ -1179,7 +1425,7 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a)
 }
 
 __global__ void mk_fill_u32_kernel(uint32_t* p, uint32_t v, size_t n) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + tid(); i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
 extern "C" int mkk_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t stream) {

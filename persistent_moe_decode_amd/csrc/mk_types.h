@@ -107,6 +107,15 @@ enum WIdx : int32_t { W_EMBED = 0, W_LM_HEAD = 1, W_FINAL_NORM = 2, W_LAYER0 = 3
 enum WLayer : int32_t { WL_NORM = 0, WL_QKV = 1, WL_O = 2, WL_ROUTER = 3, WL_GATE = 4, WL_UP = 5, WL_DOWN = 6, WL_COUNT = 7 };
 MK_HD int widx(int layer, int which) { return W_LAYER0 + layer * WL_COUNT + which; }
 
+// Floats per attention partial (one split task): outputs [group][d], then the
+// running maxima [kMaxGroup] and sums [kMaxGroup]; a multiple of 4, so every
+// partial starts 16-byte aligned.
+MK_HD int attn_part_stride(int group, int d) { return group * d + 2 * kMaxGroup; }
+
+// Pages of a split task's chunk copied into LDS before its inputs are ready
+// (flag words hold one valid bit per page).
+constexpr int kMaxLdsPages = 64;
+
 // ---------------------------------------------------------------------------
 // Runtime attention split (identical on host and device).
 //

@@ -83,3 +83,12 @@ def test_repeat_step_is_bit_identical():
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
     assert int(dec.next_tok[0]) == int(torch.argmax(outs[0][0]))
     assert int(dec.next_tok[1]) == int(torch.argmax(outs[0][1]))
+
+
+@pytest.mark.parametrize("pf_bytes", [0, 8192])
+def test_mid_small_prefetch_region(pf_bytes, monkeypatch):
+    """LDS prefetch region capped: weight tiles and K/V pages partly or not at all in LDS, attention merge from registers."""
+    from tests import parity
+    monkeypatch.setenv("MK_PREFETCH_BYTES", str(pf_bytes))
+    w = synth.Workload(f"mid_pf{pf_bytes}", synth.MID, batch=3, steps=3, context=[2048, 40, 1000])
+    _check(parity.run(w, mode="isolated", log=_log))
