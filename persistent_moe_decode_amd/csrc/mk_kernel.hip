@@ -117,7 +117,7 @@ struct Lds {
   uint8_t* base;
   uint8_t* A;
   TopK* tk;
-  int32_t* flags;  // [16]
+  int32_t* flags;  // [32]
   float* red;      // [16]
   double* red8;    // [kWaves][kMaxBatch]
   float* rbuf;     // router logits [max_batch][E]
@@ -132,14 +132,14 @@ DEV Lds carve(uint8_t* lds, const KArgs& a) {
   s.A = lds;
   s.tk = (TopK*)(lds + a.lds_b);
   s.flags = (int32_t*)(lds + a.lds_b + kTopKBytes);
-  s.red = (float*)(lds + a.lds_b + kTopKBytes + 64);
-  s.red8 = (double*)(lds + a.lds_b + kTopKBytes + 128);
+  s.red = (float*)(lds + a.lds_b + kTopKBytes + 128);
+  s.red8 = (double*)(lds + a.lds_b + kTopKBytes + 192);
   s.rbuf = (float*)(lds + a.lds_b + 4096);
   s.C = lds + a.lds_c;
   s.P = lds + a.lds_p;
   return s;
 }
-static_assert(kTopKBytes + 128 + 8 * kWaves * kMaxBatch <= 4096, "region B head fits");
+static_assert(kTopKBytes + 192 + 8 * kWaves * kMaxBatch <= 4096, "region B head fits");
 static_assert(4096 + 4 * kMaxBatch * kMaxExperts <= kLdsB, "router logits fit region B");
 
 // All threads get the block-wide sum; the order of the partial sums is fixed.
@@ -272,15 +272,32 @@ DEV uint16_t d2bf(double v) {
 // double so the one rounding to bf16 is the only one (the normalized input
 // feeds every projection of the layer).  The sums of squares of all rows are
 // reduced together: one barrier for the whole batch.
+// The first kNormRegs values of each row a thread handles stay in registers
+// between the two passes (all of them when H <= 2048); the loads of both
+// passes' inputs are issued together.
+constexpr int kNormRegs = 4;
+
 DEV void norm_inputs(const KArgs& a, int layer, const gu16* gain, uint16_t* xs, double* red8, int task) {
-  const int H = a.H, n = a.n;
+  const int H = a.H, n = a.n, t0 = tid();
+  float xv[kMaxBatch][kNormRegs], gv[kNormRegs];
   double ss[kMaxBatch];
+#pragma unroll
+  for (int k = 0; k < kNormRegs; ++k) {
+    const int i = t0 + k * kThreads;
+    gv[k] = i < H ? bf2f(gain[i]) : 0.f;
+  }
 #pragma unroll
   for (int b = 0; b < kMaxBatch; ++b) {
     ss[b] = 0.0;
     if (b < n) {
       const gu16* emb = layer == 0 ? token_row(a, b, task) : nullptr;
-      for (int i = tid(); i < H; i += kThreads) {
+#pragma unroll
+      for (int k = 0; k < kNormRegs; ++k) {
+        const int i = t0 + k * kThreads;
+        xv[b][k] = i < H ? load_x(a, layer, b, i, emb) : 0.f;
+        ss[b] += (double)xv[b][k] * (double)xv[b][k];
+      }
+      for (int i = t0 + kNormRegs * kThreads; i < H; i += kThreads) {
         const double v = load_x(a, layer, b, i, emb);
         ss[b] += v * v;
       }
@@ -297,14 +314,22 @@ DEV void norm_inputs(const KArgs& a, int layer, const gu16* gain, uint16_t* xs, 
     }
   }
   __syncthreads();
-  for (int b = 0; b < n; ++b) {
-    double tot = 0.0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) tot += red8[w * kMaxBatch + b];
-    const double inv = 1.0 / sqrt(tot / (double)H + (double)a.eps);
-    const gu16* emb = layer == 0 ? token_row(a, b, task) : nullptr;
-    for (int i = tid(); i < H; i += kThreads)
-      xs[(size_t)b * H + i] = d2bf((double)load_x(a, layer, b, i, emb) * inv * (double)bf2f(gain[i]));
+  for (int b = 0; b < kMaxBatch; ++b) {
+    if (b < n) {
+      double tot = 0.0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) tot += red8[w * kMaxBatch + b];
+      const double inv = 1.0 / sqrt(tot / (double)H + (double)a.eps);
+#pragma unroll
+      for (int k = 0; k < kNormRegs; ++k) {
+        const int i = t0 + k * kThreads;
+        if (i < H) xs[(size_t)b * H + i] = d2bf((double)xv[b][k] * inv * (double)gv[k]);
+      }
+      const gu16* emb = layer == 0 ? token_row(a, b, task) : nullptr;
+      for (int i = t0 + kNormRegs * kThreads; i < H; i += kThreads)
+        xs[(size_t)b * H + i] = d2bf((double)load_x(a, layer, b, i, emb) * inv * (double)bf2f(gain[i]));
+    }
   }
   __syncthreads();
 }
@@ -576,8 +601,14 @@ DEV int task_prefetch(const KArgs& a, const Task& t, const Lds& s, int qi) {
     src = wptr(a, widx(t.layer, WL_O)) + (size_t)t.r0 * K;
   } else {
     if (t.op == OP_ATTN) {
-      attn_plan(a, t, s, qi);
-      __syncthreads();
+      // the split depends only on the step's lengths: worked out once per launch.
+      // flags[16] was last written before an earlier barrier, so every thread
+      // takes the same branch; it is updated only after this barrier.
+      if (s.flags[16] != t.idx) {
+        attn_plan(a, t, s, qi);
+        __syncthreads();
+        if (tid() == 0) s.flags[16] = t.idx;
+      }
       if (a.d == 128) attn_prefetch<128>(a, t, s, qi);
       else attn_prefetch<64>(a, t, s, qi);
     }
@@ -1152,12 +1183,15 @@ struct JobGateUp {
   DEV void emit(int i, int t, float v) const { gs[((size_t)(i >> 1) * maxB + t) * 2 + (i & 1)] = v; }
 };
 
-TASK void task_gateup(const KArgs& a, const Task& t, const Lds& s, int qi) {
+// have_xs: region A still holds this layer's normalized input, left there by
+// the PRE task that ran just before on this compute unit.
+TASK void task_gateup(const KArgs& a, const Task& t, const Lds& s, int qi, bool have_xs) {
   const int l = t.layer;
-  load_topk(a, l, s.tk);  // visible to all threads after the norm's barriers
+  load_topk(a, l, s.tk);  // visible to all threads after the next barrier
   mark(a, qi, 0);
   uint16_t* xs = (uint16_t*)s.A;
-  norm_inputs(a, l, wptr(a, widx(l, WL_NORM)), xs, s.red8, qi);
+  if (have_xs) __syncthreads();
+  else norm_inputs(a, l, wptr(a, widx(l, WL_NORM)), xs, s.red8, qi);
   mark(a, qi, 1);
   const TopK* tk = s.tk;
   const int64_t R = (int64_t)tk->nU * a.I;
@@ -1395,6 +1429,9 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a)
   const Lds s = carve(lds_raw, a);
   const int cu = blockIdx.x;
   const int q0 = a.queue_off[cu], q1 = a.queue_off[cu + 1];
+  if (tid() == 0) s.flags[16] = -1;  // no attention plan cached yet
+  __syncthreads();
+  int xs_layer = -1;                 // layer whose normalized input region A holds
   for (int q = q0; q < q1; ++q) {
     const Task t = a.tasks[q];
     uint64_t t_fetch = 0, t_ready = 0;
@@ -1408,12 +1445,13 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a)
       switch (t.op) {
         case OP_PRE: task_pre(a, t, s, q, npf); break;
         case OP_ATTN: task_attn(a, t, s, q); break;
-        case OP_GATEUP: task_gateup(a, t, s, q); break;
+        case OP_GATEUP: task_gateup(a, t, s, q, xs_layer == t.layer); break;
         case OP_OUT: task_out(a, t, s, q, npf); break;
         case OP_LMHEAD: task_lmhead(a, t, s, q); break;
         default: break;
       }
     }
+    xs_layer = ok && t.op == OP_PRE ? t.layer : (ok && t.op == OP_GATEUP ? xs_layer : -1);
     signal_counter(a, t.signal);
     if (a.trace && tid() == 0 && q < a.trace_cap) {
       uint64_t* r = a.trace + kTraceWords * (size_t)q;
