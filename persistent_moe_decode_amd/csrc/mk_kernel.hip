@@ -277,7 +277,8 @@ DEV uint16_t d2bf(double v) {
 // passes' inputs are issued together.
 constexpr int kNormRegs = 4;
 
-DEV void norm_inputs(const KArgs& a, int layer, const gu16* gain, uint16_t* xs, double* red8, int task) {
+// mk >= 0: trace mark mk of the task once thread 0 has its inputs.
+DEV void norm_inputs(const KArgs& a, int layer, const gu16* gain, uint16_t* xs, double* red8, int task, int mk) {
   const int H = a.H, n = a.n, t0 = tid();
   float xv[kMaxBatch][kNormRegs], gv[kNormRegs];
   double ss[kMaxBatch];
@@ -303,6 +304,7 @@ DEV void norm_inputs(const KArgs& a, int layer, const gu16* gain, uint16_t* xs, 
       }
     }
   }
+  if (mk >= 0) mark(a, task, mk);
   const int lane = tid() & 63, wave = tid() >> 6;
 #pragma unroll
   for (int b = 0; b < kMaxBatch; ++b) {
@@ -580,13 +582,10 @@ DEV void prefetch_to_lds(const gu16* src, uint8_t* dst_lds, int nbytes) {
   }
 }
 
-DEV void attn_plan(const KArgs& a, const Task& t, const Lds& s, int qi);
-template <int D>
-DEV void attn_prefetch(const KArgs& a, const Task& t, const Lds& s, int qi);
 
 // Work a task can do before its inputs are ready: the first weight tile of
 // PRE and OUT tasks (rows [r0, r1) of Wqkv / router / Wo) starts streaming
-// into LDS; attention tasks work out their chunk.  Returns the rows prefetched.
+// into LDS.  Returns the rows prefetched.
 DEV int task_prefetch(const KArgs& a, const Task& t, const Lds& s, int qi) {
   const gu16* src;
   int K, nrows;
@@ -600,18 +599,6 @@ DEV int task_prefetch(const KArgs& a, const Task& t, const Lds& s, int qi) {
     nrows = t.r1 - t.r0;
     src = wptr(a, widx(t.layer, WL_O)) + (size_t)t.r0 * K;
   } else {
-    if (t.op == OP_ATTN) {
-      // the split depends only on the step's lengths: worked out once per launch.
-      // flags[16] was last written before an earlier barrier, so every thread
-      // takes the same branch; it is updated only after this barrier.
-      if (s.flags[16] != t.idx) {
-        attn_plan(a, t, s, qi);
-        __syncthreads();
-        if (tid() == 0) s.flags[16] = t.idx;
-      }
-      if (a.d == 128) attn_prefetch<128>(a, t, s, qi);
-      else attn_prefetch<64>(a, t, s, qi);
-    }
     return 0;
   }
   const int npf = min(nrows, a.pf_bytes / (K * 2));
@@ -643,9 +630,9 @@ struct JobPre {
 TASK void task_pre(const KArgs& a, const Task& t, const Lds& s, int qi, int npf) {
   const int l = t.layer;
   uint16_t* xs = (uint16_t*)s.A;
-  norm_inputs(a, l, wptr(a, widx(l, WL_NORM)), xs, s.red8, qi);
+  norm_inputs(a, l, wptr(a, widx(l, WL_NORM)), xs, s.red8, qi, 0);
   prefetch_wait();
-  mark(a, qi, 0);
+  mark(a, qi, 1);
   JobPre j;
   j.K = a.H;
   j.xs = xs;
@@ -663,6 +650,7 @@ TASK void task_pre(const KArgs& a, const Task& t, const Lds& s, int qi, int npf)
     j.ld = a.E;
   }
   run_rowdots_pf(a.H, t.r1 - t.r0, npf, a.n, j);
+  mark(a, qi, 2);
   if (t.r0 >= a.qkv_rows) {
     // router rows: the last router task of the layer takes the top-k for everyone
     uint32_t* ticket = a.tickets + (size_t)a.L * a.max_batch * a.nkv + 1 + l;
@@ -701,11 +689,12 @@ struct AttnPage {
   int nvalid;       // positions of the page inside the chunk
 };
 
-// The first pages of a chunk are copied into LDS region P before the task
-// waits for q (K/V of earlier positions never change during a step): K blocks
-// [npp][16][D], then V blocks [npp][D][16].  In a K block the 16-byte pieces
-// of position r are stored XOR-swizzled by r, so the 16 positions a wave
-// reads at one dim offset sit in different banks.
+// The last nl blocks of a chunk, [bl0, bl0 + nl), are copied into LDS region
+// P before the task waits for q (K/V of earlier positions never change during
+// a step; the block that receives the new token is patched after the wait):
+// K blocks [nl][16][D], then V blocks [nl][D][16].  In a K block the 16-byte
+// pieces of position r are stored XOR-swizzled by r, so the 16 positions a
+// wave reads at one dim offset sit in different banks.
 template <int D>
 DEV int kslot(int r, int cc) {
   constexpr int NC = D / 8;  // 16-byte pieces per K row
@@ -717,33 +706,30 @@ DEV int attn_lds_pages(const KArgs& a, int nblk) {
   return min(min(nblk, kMaxLdsPages), a.pf_bytes / (2 * 16 * D * 2));
 }
 
-// Issues the copies (all threads; the plan is already in LDS).  Wave 0
-// records which pages are valid and raises the error for the others.
+// Waves 1..7 issue the copies (wave 0, whose thread 0 polls the counters,
+// keeps its load queue short); wave 0 records which of the blocks' pages are
+// valid and raises the error for the others.
 template <int D>
-DEV void attn_prefetch(const KArgs& a, const Task& t, const Lds& s, int qi) {
-  const int32_t* plan = s.flags + 2;
-  if (!plan[6]) return;
-  const int b = plan[0], g = plan[1], t0 = plan[2], t1 = plan[3];
-  const int npp = attn_lds_pages<D>(a, (t1 - t0 + 15) / 16);
+DEV void attn_prefetch(const KArgs& a, const Lds& s, int qi, int l, int b, int g, int t0, int bl0, int nl) {
   constexpr int NI = 16 * D * 2 / 1024;  // 1 KB copies per K (or V) block
   const int lane = tid() & 63, wave = tid() >> 6;
-  const int32_t* pt = a.page_table + (size_t)b * a.max_pages + t0 / 16;
-  for (int q = wave; q < npp * 2 * NI; q += kWaves) {
+  const int32_t* pt = a.page_table + (size_t)b * a.max_pages + t0 / 16 + bl0;
+  for (int q = wave - 1; wave > 0 && q < nl * 2 * NI; q += kWaves - 1) {
     const int pi = q / (2 * NI), isv = (q / NI) & 1, k = q % NI;
     const int page = pt[pi];
     if (page < 0 || page >= a.num_pages) continue;
-    const size_t boff = (((size_t)t.layer * a.num_pages + page) * a.nkv + g) * (size_t)16 * D;
+    const size_t boff = (((size_t)l * a.num_pages + page) * a.nkv + g) * (size_t)16 * D;
     const int slot = 64 * k + lane;
     const int piece = isv ? slot : kslot<D>(slot / (D / 8), slot % (D / 8));  // the swizzle is its own inverse
     const uint16_t* src = (isv ? a.v_pool : a.k_pool) + boff + (size_t)piece * 8;
-    uint8_t* dst = s.P + (isv ? (size_t)npp * 16 * D * 2 : 0) + (size_t)pi * 16 * D * 2 + k * 1024;
+    uint8_t* dst = s.P + (isv ? (size_t)nl * 16 * D * 2 : 0) + (size_t)pi * 16 * D * 2 + k * 1024;
     __builtin_amdgcn_global_load_lds((AS_GLOBAL void*)src, (AS_LDS void*)dst, 16, 0, 0);
   }
   if (wave == 0) {
     // lane pi checks page pi; one load per lane, one ballot
-    const int page = lane < npp ? pt[lane] : 0;
-    const bool ok = lane < npp && page >= 0 && page < a.num_pages;
-    if (lane < npp && !ok) raise_error(a, MK_ERR_DEVICE_PAGE, qi, page);
+    const int page = lane < nl ? pt[lane] : 0;
+    const bool ok = lane < nl && page >= 0 && page < a.num_pages;
+    if (lane < nl && !ok) raise_error(a, MK_ERR_DEVICE_PAGE, qi, page);
     const uint64_t m = __ballot(ok);
     if (lane == 0) {
       s.flags[14] = (int32_t)(uint32_t)m;
@@ -859,12 +845,14 @@ DEV AttnMerge attn_merge_area(const Lds& s, int G, int d) {
   return r;
 }
 
-// This wave's pages of the chunk (blocks wave, wave + 8, ...; the first npp
-// from LDS, the rest from HBM with the next page loaded while the current one
-// is processed); leaves (o, m, sum) per head in the merge area.
+// This wave's pages of the chunk, the blocks congruent to the wave mod 8:
+// early blocks [0, ne) already in registers (e0 = block wave, e1 = block
+// wave + 8), then LDS blocks [bl0, nblk), then HBM blocks [ne, bl0) with the
+// next page loaded while the current one is processed.  Leaves (o, m, sum)
+// per head in the merge area.
 template <int D>
 DEV void attn_wave(const KArgs& a, const Lds& s, int qi, const uint16_t* q_s, int l, int b, int g, int t0, int t1,
-                   int npp, const AttnMerge& mrg) {
+                   int ne, int bl0, int nl, const AttnPage<D>& e0, const AttnPage<D>& e1, const AttnMerge& mrg) {
   const int lane = tid() & 63, wave = tid() >> 6, r = lane & 15, grp = lane >> 4;
   const int G = a.group;
   bf16x8_v qb[D / 32];
@@ -879,18 +867,21 @@ DEV void attn_wave(const KArgs& a, const Lds& s, int qi, const uint16_t* q_s, in
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) o[t] = float4_v{0.f, 0.f, 0.f, 0.f};
   const int nblk = (t1 - t0 + 15) / 16;
-  int blk = wave;
-  if (blk < nblk) {
+  if (wave < ne) attn_page<D>(e0, qb, scale, m, lsum, o);
+  if (wave + kWaves < ne) attn_page<D>(e1, qb, scale, m, lsum, o);
+  for (int blk = bl0 + (wave - bl0 % kWaves + kWaves) % kWaves; blk < nblk; blk += kWaves) {
+    AttnPage<D> cur;
+    attn_fetch_lds<D>(s, cur, nl, blk - bl0, t0 + 16 * blk, t1);
+    attn_page<D>(cur, qb, scale, m, lsum, o);
+  }
+  int blk = ne + (wave - ne % kWaves + kWaves) % kWaves;
+  if (blk < bl0) {
     AttnPage<D> cur, nxt;
-    if (blk < npp) attn_fetch_lds<D>(s, cur, npp, blk, t0 + 16 * blk, t1);
-    else attn_fetch<D>(a, cur, l, b, g, t0 + 16 * blk, t1, qi);
+    attn_fetch<D>(a, cur, l, b, g, t0 + 16 * blk, t1, qi);
     while (true) {
       const int nb = blk + kWaves;
-      const bool more = nb < nblk;
-      if (more) {
-        if (nb < npp) attn_fetch_lds<D>(s, nxt, npp, nb, t0 + 16 * nb, t1);
-        else attn_fetch<D>(a, nxt, l, b, g, t0 + 16 * nb, t1, qi);
-      }
+      const bool more = nb < bl0;
+      if (more) attn_fetch<D>(a, nxt, l, b, g, t0 + 16 * nb, t1, qi);
       attn_page<D>(cur, qb, scale, m, lsum, o);
       if (!more) break;
       cur = nxt;
@@ -1035,40 +1026,65 @@ DEV void attn_combine(const KArgs& a, const Lds& s, const float* parts, int nch,
   }
 }
 
-TASK void task_attn(const KArgs& a, const Task& t, const Lds& s, int qi) {
-  const int l = t.layer, G = a.group, d = a.d, ps = a.ps;
+// Attention waits for its inputs itself: before the wait it works out its
+// chunk (once per launch), starts the LDS copies of the chunk's last blocks
+// and loads its first blocks into registers, so little of the chunk's K/V
+// traffic is left once q is ready.
+template <int D>
+DEV void attn_task(const KArgs& a, const Task& t, const Lds& s, int qi) {
+  // flags[16] (the split task whose plan flags[2..9] holds) was last written
+  // before an earlier barrier, so every thread takes the same branch
+  if (s.flags[16] != t.idx) {
+    attn_plan(a, t, s, qi);
+    __syncthreads();
+    if (tid() == 0) s.flags[16] = t.idx;
+  }
   const int32_t* plan = s.flags + 2;
-  if (!plan[6]) return;
+  if (!plan[6]) {  // idle split task: nothing to wait for
+    if (a.trace && tid() == 0 && qi < a.trace_cap) a.trace[kTraceWords * (size_t)qi + 1] = wall_clock64();
+    return;
+  }
+  const int l = t.layer, G = a.group, ps = a.ps;
   const int b = plan[0], g = plan[1], t0 = plan[2], t1 = plan[3], first = plan[4], nch = plan[5], p = plan[7];
   const int nblk = (t1 - t0 + 15) / 16;
-  const int npp = d == 128 ? attn_lds_pages<128>(a, nblk) : attn_lds_pages<64>(a, nblk);
+  const int nl = attn_lds_pages<D>(a, nblk);
+  const int bl0 = nblk - nl;
+  // early blocks never include the last one (it receives the new token)
+  const int ne = max(0, min(bl0 - (nl == 0 ? 1 : 0), 2 * kWaves));
+  attn_prefetch<D>(a, s, qi, l, b, g, t0, bl0, nl);
+  const int wave = tid() >> 6;
+  AttnPage<D> e0, e1;
+  if (wave < ne) attn_fetch<D>(a, e0, l, b, g, t0 + 16 * wave, t1, qi);
+  if (wave + kWaves < ne) attn_fetch<D>(a, e1, l, b, g, t0 + 16 * (wave + kWaves), t1, qi);
+  if (!wait_counter(a, t.wait[0], t.fanin[0], qi, s.flags + 0)) return;
+  if (a.trace && tid() == 0 && qi < a.trace_cap) a.trace[kTraceWords * (size_t)qi + 1] = wall_clock64();
 
-  const int half = d / 2;
-  uint16_t* q_s = (uint16_t*)s.A;  // [G][d] rotated q, bf16
+  constexpr int half = D / 2;
+  uint16_t* q_s = (uint16_t*)s.A;  // [G][D] rotated q, bf16
   const float* qkv = a.qkv + ((size_t)l * a.max_batch + b) * a.qkv_rows;
   for (int e = tid(); e < G * half; e += kThreads) {
     const int hh = e / half, i = e % half;
     double sd, cd;
     sincos((double)p * a.inv_freq[i], &sd, &cd);
     const float cf = (float)cd, sf = (float)sd;
-    const float* q = qkv + (size_t)(g * G + hh) * d;
+    const float* q = qkv + (size_t)(g * G + hh) * D;
     const float x0 = q[i], x1 = q[i + half];
-    q_s[hh * d + i] = f2bf(x0 * cf - x1 * sf);
-    q_s[hh * d + i + half] = f2bf(x0 * sf + x1 * cf);
+    q_s[hh * D + i] = f2bf(x0 * cf - x1 * sf);
+    q_s[hh * D + i + half] = f2bf(x0 * sf + x1 * cf);
   }
   // the chunk holding position p writes the new token's K (rotated) and V, to
-  // HBM and, when its page was copied, to the LDS copy as well
+  // HBM and, when its block was copied, to the LDS copy as well
   const bool mine = t1 == p + 1;
   const int page = mine ? a.page_table[(size_t)b * a.max_pages + p / ps] : 0;
   const bool pg_ok = page >= 0 && page < a.num_pages;
-  uint16_t k_lo = 0, k_hi = 0, v_i = 0;  // thread i < d/2: K dims i and i + d/2; thread i < d: V dim i
+  uint16_t k_lo = 0, k_hi = 0, v_i = 0;  // thread i < D/2: K dims i and i + D/2; thread i < D: V dim i
   if (mine) {
     if (!pg_ok) {
       if (tid() == 0) raise_error(a, MK_ERR_DEVICE_PAGE, qi, page);
     } else {
-      const size_t off = ((((size_t)l * a.num_pages + page) * a.nkv + g) * ps + p % ps) * d;
-      const float* kk = qkv + (size_t)a.nq * d + (size_t)g * d;
-      const float* vv = qkv + (size_t)(a.nq + a.nkv) * d + (size_t)g * d;
+      const size_t off = ((((size_t)l * a.num_pages + page) * a.nkv + g) * ps + p % ps) * D;
+      const float* kk = qkv + (size_t)a.nq * D + (size_t)g * D;
+      const float* vv = qkv + (size_t)(a.nq + a.nkv) * D + (size_t)g * D;
       const int i = tid();
       if (i < half) {
         double sd, cd;
@@ -1081,46 +1097,42 @@ TASK void task_attn(const KArgs& a, const Task& t, const Lds& s, int qi) {
         a.k_pool[off + i + half] = k_hi;
       }
       // V pages are stored dims-major: element (dim, slot) of a (page, head) block at dim*page_size + slot
-      const size_t voff = (((size_t)l * a.num_pages + page) * a.nkv + g) * (size_t)ps * d + p % ps;
-      if (i < d) {
+      const size_t voff = (((size_t)l * a.num_pages + page) * a.nkv + g) * (size_t)ps * D + p % ps;
+      if (i < D) {
         v_i = f2bf(vv[i]);
         a.v_pool[voff + (size_t)i * ps] = v_i;
       }
     }
   }
-  // copied pages have landed, q is complete, the new K/V are in HBM
+  mark(a, qi, 0);
+  // copied blocks have landed, q is complete, the new K/V are in HBM
   __builtin_amdgcn_s_waitcnt(0);
   __threadfence_block();
   __syncthreads();
   const int pp = (p - t0) / 16;
-  if (mine && pg_ok && pp < npp) {
+  if (mine && pg_ok && pp >= bl0) {
     const int i = tid(), r = p % 16;
-    uint16_t* kb = (uint16_t*)(s.P + (size_t)pp * 16 * d * 2);
-    uint16_t* vb = (uint16_t*)(s.P + (size_t)(npp + pp) * 16 * d * 2);
-    const int ks = d == 128 ? 0 : 1;
+    uint16_t* kb = (uint16_t*)(s.P + (size_t)(pp - bl0) * 16 * D * 2);
+    uint16_t* vb = (uint16_t*)(s.P + (size_t)(nl + pp - bl0) * 16 * D * 2);
     if (i < half) {
-      const int c0 = i / 8, c1 = (i + half) / 8;
-      kb[8 * (ks ? kslot<64>(r, c0) : kslot<128>(r, c0)) + i % 8] = k_lo;
-      kb[8 * (ks ? kslot<64>(r, c1) : kslot<128>(r, c1)) + (i + half) % 8] = k_hi;
+      kb[8 * kslot<D>(r, i / 8) + i % 8] = k_lo;
+      kb[8 * kslot<D>(r, (i + half) / 8) + (i + half) % 8] = k_hi;
     }
-    if (i < d) vb[i * 16 + r] = v_i;
+    if (i < D) vb[i * 16 + r] = v_i;
   }
   __syncthreads();
-  mark(a, qi, 0);
+  mark(a, qi, 1);
 
   // positions of the chunk, 16 (one page) at a time, pages dealt to waves round robin
-  const AttnMerge mrg = attn_merge_area(s, G, d);
-  if (d == 128)
-    attn_wave<128>(a, s, qi, q_s, l, b, g, t0, t1, npp, mrg);
-  else
-    attn_wave<64>(a, s, qi, q_s, l, b, g, t0, t1, npp, mrg);
-  mark(a, qi, 1);
+  const AttnMerge mrg = attn_merge_area(s, G, D);
+  attn_wave<D>(a, s, qi, q_s, l, b, g, t0, t1, ne, bl0, nl, e0, e1, mrg);
+  mark(a, qi, 2);
   __syncthreads();
-  // this chunk's partial: the waves' results merged, as [G][d] outputs, G maxima, G sums
-  const int GD = G * d, CS = attn_part_stride(G, d);
+  // this chunk's partial: the waves' results merged, as [G][D] outputs, G maxima, G sums
+  const int GD = G * D, CS = attn_part_stride(G, D);
   float* part = a.attn_part + ((size_t)l * a.n_attn + t.idx) * CS;
   for (int e4 = tid(); e4 < GD / 4; e4 += kThreads) {
-    const int hh = 4 * e4 / d;
+    const int hh = 4 * e4 / D;
     float M = kNegInf;
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mrg.m[w * kMaxGroup + hh]);
     float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1136,18 +1148,23 @@ TASK void task_attn(const KArgs& a, const Task& t, const Lds& s, int qi) {
       Ls += mrg.l[w * kMaxGroup + hh] * sc;
     }
     *(float4*)(part + 4 * e4) = O;
-    if ((4 * e4) % d == 0) {
+    if ((4 * e4) % D == 0) {
       part[GD + hh] = M;
       part[GD + kMaxGroup + hh] = Ls;
     }
   }
   uint32_t* ticket = a.tickets + ((size_t)l * a.max_batch + b) * a.nkv + g;
-  mark(a, qi, 2);
+  mark(a, qi, 3);
   if (arrive_last(ticket, (uint32_t)nch, s.flags + 10)) {
     const float* parts = a.attn_part + ((size_t)l * a.n_attn + first) * CS;
-    uint16_t* out = a.attn_out + ((size_t)l * a.max_batch + b) * a.nq * d + (size_t)g * G * d;
+    uint16_t* out = a.attn_out + ((size_t)l * a.max_batch + b) * a.nq * D + (size_t)g * G * D;
     attn_combine(a, s, parts, nch, out);
   }
+}
+
+TASK void task_attn(const KArgs& a, const Task& t, const Lds& s, int qi) {
+  if (a.d == 128) attn_task<128>(a, t, s, qi);
+  else attn_task<64>(a, t, s, qi);
 }
 
 // ---------------------------------------------------------------------------
@@ -1191,7 +1208,7 @@ TASK void task_gateup(const KArgs& a, const Task& t, const Lds& s, int qi, bool 
   mark(a, qi, 0);
   uint16_t* xs = (uint16_t*)s.A;
   if (have_xs) __syncthreads();
-  else norm_inputs(a, l, wptr(a, widx(l, WL_NORM)), xs, s.red8, qi);
+  else norm_inputs(a, l, wptr(a, widx(l, WL_NORM)), xs, s.red8, qi, -1);
   mark(a, qi, 1);
   const TopK* tk = s.tk;
   const int64_t R = (int64_t)tk->nU * a.I;
@@ -1293,6 +1310,7 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf)
   mark(a, qi, 1);
   // attention output projection: wait for attention, Wo rows are already in LDS
   wait_counter(a, t.late_wait, t.late_fanin, qi, s.flags + 13);  // its barrier also frees xs
+  mark(a, qi, 2);
   copy_to_lds(xs, a.attn_out + (size_t)l * a.max_batch * AD, n * AD);
   prefetch_wait();
   JobO jo;
@@ -1306,7 +1324,7 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf)
   jo.ao = ao;
   run_rowdots_pf(AD, nr, npf, n, jo);
   __syncthreads();
-  mark(a, qi, 2);
+  mark(a, qi, 3);
   // x_{l+1} = (x_l + attn) + sum_j w_j y_j
   for (int e = tid(); e < nr * n; e += kThreads) {
     const int rr = e / n, b = e % n;
@@ -1360,7 +1378,7 @@ DEV void block_argmax(float& v, int& i, float* red) {
 TASK void task_lmhead(const KArgs& a, const Task& t, const Lds& s, int qi) {
   const int L = a.L, nr = t.r1 - t.r0;
   uint16_t* xs = (uint16_t*)s.A;
-  norm_inputs(a, L, wptr(a, W_FINAL_NORM), xs, s.red8, qi);
+  norm_inputs(a, L, wptr(a, W_FINAL_NORM), xs, s.red8, qi, -1);
   mark(a, qi, 0);
   JobLM j;
   j.W = wptr(a, W_LM_HEAD);
@@ -1438,8 +1456,9 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a)
     if (a.trace && tid() == 0) t_fetch = wall_clock64();
     // immutable weights start streaming into LDS before the inputs are ready
     const int npf = task_prefetch(a, t, s, q);
-    bool ok = wait_counter(a, t.wait[0], t.fanin[0], q, s.flags + 0);
-    if (ok && t.wait[1] >= 0) ok = wait_counter(a, t.wait[1], t.fanin[1], q, s.flags + 1);
+    const bool own_wait = t.op == OP_ATTN;  // attention waits inside, once its loads are in flight
+    bool ok = own_wait || wait_counter(a, t.wait[0], t.fanin[0], q, s.flags + 0);
+    if (ok && !own_wait && t.wait[1] >= 0) ok = wait_counter(a, t.wait[1], t.fanin[1], q, s.flags + 1);
     if (a.trace && tid() == 0) t_ready = wall_clock64();
     if (ok) {
       switch (t.op) {
@@ -1456,7 +1475,7 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a)
     if (a.trace && tid() == 0 && q < a.trace_cap) {
       uint64_t* r = a.trace + kTraceWords * (size_t)q;
       r[0] = t_fetch;
-      r[1] = t_ready;
+      if (!own_wait) r[1] = t_ready;
       r[6] = wall_clock64();
     }
   }

@@ -5,10 +5,11 @@ The megakernel writes, per task, eight words when tracing is on
 fetched, when its dependencies were met, up to four phase marks inside the
 body, and when it had signalled.  This module joins them with the task table.
 
-Phase marks per op: PRE [norm done]; ATTN [q rotated and new K/V written,
-positions done, partial stored]; GATEUP [routing loaded, norm done]; OUT
-[routing and h loaded, down rows done, attention waited and Wo rows done];
-LMHEAD [norm done, rows done, local argmax done].
+Phase marks per op: PRE [inputs loaded, norm done, rows done]; ATTN [q
+rotated and new K/V written, copied pages landed, positions done, partial
+stored]; GATEUP [routing loaded, norm done]; OUT [routing and h loaded, down
+rows done, attention waited, Wo rows done]; LMHEAD [norm done, rows done,
+local argmax done].
 """
 from __future__ import annotations
 
