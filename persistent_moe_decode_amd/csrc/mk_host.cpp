@@ -7,8 +7,10 @@
 // advance; aiweekly.co, paragraphs 2-3: fixed-size descriptors, a task waits
 // on one count) with its own layout: one queue per compute unit, per layer
 //   PRE (norm + Wqkv / router rows)  ->  ATTN or GATEUP  ->  OUT (Wo + down rows),
-// then LM head rows.  Every counter is signalled once per task and waited on
-// as "value >= epoch * fan-in", so nothing is reset between steps.
+// then LM head rows.  A counter is an array of flag words, one per task that
+// signals it (the task's slot); signalling stores the step's epoch into the
+// task's word and a wait ends when all words of the counter hold the epoch,
+// so nothing is reset between steps and no two tasks update one word.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -39,7 +41,7 @@ int fail(int code, const std::string& m) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t state = 0, n_state_u32 = 0;  // counters, tickets, error word (zeroed by mk_reset)
+  size_t state = 0, n_state_u32 = 0;  // counter flags, tickets, error word (zeroed by mk_reset)
   size_t ctr = 0, tickets = 0, err = 0;
   size_t tasks = 0, queue_off = 0, wtab = 0, inv_freq = 0;
   size_t x = 0, qkv = 0, rlog = 0, attn_part = 0, attn_out = 0, h = 0, lm_part = 0, sel = 0, topk = 0;
@@ -51,7 +53,7 @@ struct WsLayout {
 struct mk_ctx {
   mk_config cfg{};
   bool built = false, bound = false, need_reset = false;
-  int ncu = 0, n_attn = 0, n_gu = 0, n_out = 0, n_lm = 0, n_ctr = 0, n_tickets = 0;
+  int ncu = 0, n_attn = 0, n_gu = 0, n_out = 0, n_lm = 0, n_ctr = 0, n_tickets = 0, n_slots = 0;
   int out_rows_max = 0, gu_rows_max = 0, lm_rows_max = 0, pre_rows_max = 0;
   int lds_b = 0, lds_c = 0, lds_p = 0, pf_bytes = 0;
   size_t lds_bytes = 0;
@@ -142,6 +144,16 @@ static int simulate_raw(const Task* tasks, int nt, const int32_t* qoff, int ncu,
       return fail(MK_ERR_INVALID_ARG, "counter index out of range");
     if (t.signal >= 0) signals[t.signal]++;
   }
+  // the signalling tasks of a counter own its flag words 0 .. signals - 1, one each
+  std::vector<std::vector<char>> owned(n_ctr);
+  for (int c = 0; c < n_ctr; ++c) owned[c].assign((size_t)signals[c], 0);
+  for (int i = 0; i < nt; ++i) {
+    const Task& t = tasks[i];
+    if (t.signal < 0) continue;
+    if (t.slot < 0 || t.slot >= signals[t.signal] || owned[t.signal][t.slot])
+      return fail(MK_ERR_SCHEDULE, "schedule: task " + std::to_string(i) + " has a flag slot that is out of range or taken");
+    owned[t.signal][t.slot] = 1;
+  }
   // every wait must name the full fan-in of its counter
   for (int i = 0; i < nt; ++i)
     for (int k = 0; k < 3; ++k) {
@@ -203,9 +215,9 @@ static WsLayout layout_workspace(const mk_ctx* c) {
   const size_t group = f.n_q_heads / f.n_kv_heads;
   w.state = o;
   w.ctr = 0;
-  w.tickets = c->n_ctr;
-  w.err = c->n_ctr + c->n_tickets;
-  w.n_state_u32 = c->n_ctr + c->n_tickets + E_WORDS;
+  w.tickets = (size_t)c->n_ctr * c->n_slots;
+  w.err = w.tickets + c->n_tickets;
+  w.n_state_u32 = w.err + E_WORDS;
   take(4 * w.n_state_u32);
   w.tasks = take(sizeof(Task) * c->tasks.size());
   w.queue_off = take(4 * (c->ncu + 1));
@@ -373,6 +385,13 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
     }
   }
   c->qoff[ncu] = (int)c->tasks.size();
+  // flag slots: the k-th task (in table order) that signals a counter owns its word k
+  {
+    std::vector<int> used(c->n_ctr, 0);
+    for (Task& t : c->tasks)
+      if (t.signal >= 0) t.slot = used[t.signal]++;
+    c->n_slots = std::max(1, *std::max_element(used.begin(), used.end()));
+  }
 
   // LDS: region A (input vectors), B (top-k state, reductions), C (per-op arrays)
   const int maxU = std::min(E, B * f.top_k);
@@ -598,7 +617,8 @@ extern "C" int mk_decode_step(mk_ctx* c, int32_t n, const int32_t* d_tokens, con
   a.tasks = (const Task*)(w + c->ws.tasks);
   a.queue_off = (const int32_t*)(w + c->ws.queue_off);
   uint32_t* st = (uint32_t*)(w + c->ws.state);
-  a.ctr = st + c->ws.ctr;
+  a.flags = st + c->ws.ctr;
+  a.n_slots = c->n_slots;
   a.tickets = st + c->ws.tickets;
   a.err = (int32_t*)(st + c->ws.err);
   a.wtab = (const uint64_t*)(w + c->ws.wtab);

@@ -42,6 +42,25 @@ typedef const AS_GLOBAL uint16_t gu16;
 typedef const AS_GLOBAL u32x4_v gu4;
 typedef const AS_LDS u32x4_v lu4;
 
+// Data that one compute unit writes and another reads within a launch goes
+// through device-coherent accesses: relaxed agent-scope atomic stores and
+// loads (the store is written through past the writer's L2, the load never
+// hits a stale line in the reader's L2), and LDS copies with the same cache
+// policy.  Ordering comes from the flags: a task waits for its own stores to
+// complete before it sets its flag, and readers load only after they have
+// seen every flag they need.  No cache-wide write-back or invalidate is
+// needed, which keeps a wait-and-signal hop to about one memory round trip.
+constexpr int kCohPolicy = 16;  // sc1: device-scope coherent (cache policy operand of the LDS copy)
+DEV void st_coh(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DEV void st_coh(uint32_t* p, uint32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DEV void st_coh(uint16_t* p, uint16_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DEV float ld_coh(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DEV uint32_t ld_coh(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 static constexpr float kNegInf = -__builtin_huge_valf();
 
 // ---------------------------------------------------------------------------
@@ -170,56 +189,60 @@ DEV bool aborting(const KArgs& a) {
   return __hip_atomic_load(&a.err[E_ABORT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
 }
 
-// Thread 0 spins (relaxed agent-scope loads, s_sleep between polls) until
-// counter idx reaches epoch * fanin, then takes one agent-scope acquire fence;
-// the barrier hands the result to the other waves.  The wait is bounded: past
-// the spin limit the task raises MK_ERR_DEVICE_TIMEOUT and the grid drains.
-// Returns false when the grid is aborting.
+// Wave 0 polls the counter's flag words (slot j by lane j mod 64, relaxed
+// device-coherent loads, s_sleep between polls) until every one of the fanin
+// words holds this step's epoch; the barrier hands the result to the other
+// waves.  The wait is bounded: past the spin limit the task raises
+// MK_ERR_DEVICE_TIMEOUT and the grid drains.  Returns false when the grid is
+// aborting.
 DEV bool wait_counter(const KArgs& a, int idx, int fanin, int task, int32_t* slot) {
-  if (tid() == 0) {
+  if (tid() < 64) {
+    const int lane = tid();
     int ok = aborting(a) ? 0 : 1;
     if (ok && idx >= 0) {
-      const uint32_t want = a.epoch * (uint32_t)fanin;
-      uint32_t* c = a.ctr + idx;
+      const uint32_t* f = a.flags + (size_t)idx * a.n_slots;
+      const uint32_t want = a.epoch;
       const uint64_t t0 = wall_clock64();
       uint32_t it = 0;
-      while ((int32_t)(__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - want) < 0) {
+      while (true) {
+        bool done = true;
+        for (int j = lane; j < fanin; j += 64) done &= (int32_t)(ld_coh(f + j) - want) >= 0;
+        if (__all(done)) break;
         __builtin_amdgcn_s_sleep(1);
         if ((++it & 31) == 0) {
-          if (aborting(a)) {
-            ok = 0;
-            break;
-          }
-          if (wall_clock64() - t0 > a.spin_limit_ticks) {
-            raise_error(a, MK_ERR_DEVICE_TIMEOUT, task, idx);
+          int stop = 0;
+          if (lane == 0) stop = aborting(a) ? 1 : (wall_clock64() - t0 > a.spin_limit_ticks ? 2 : 0);
+          stop = __shfl(stop, 0);
+          if (stop) {
+            if (lane == 0 && stop == 2) raise_error(a, MK_ERR_DEVICE_TIMEOUT, task, idx);
             ok = 0;
             break;
           }
         }
       }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
-    *slot = ok;
+    if (lane == 0) *slot = ok;
   }
   __syncthreads();
   return *slot != 0;
 }
 
-// Every wave waits for its own stores, the barrier orders them before thread
-// 0's agent-scope release, and the add publishes the task.
-DEV void signal_counter(const KArgs& a, int idx) {
+// Every wave waits for its own stores to complete, the barrier orders them
+// before thread 0's flag store.
+DEV void signal_counter(const KArgs& a, int idx, int slot) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid() == 0 && idx >= 0) __hip_atomic_fetch_add(a.ctr + idx, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid() == 0 && idx >= 0) st_coh(a.flags + (size_t)idx * a.n_slots + slot, a.epoch);
 }
 
 // Ticket for "last of count arrivals does the merge": returns true in every
-// thread of the last arriving workgroup, which also resets the ticket.
+// thread of the last arriving workgroup, which also resets the ticket.  Each
+// arrival's stores are complete before its add.
 DEV bool arrive_last(uint32_t* ticket, uint32_t count, int32_t* slot) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid() == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int last = old == count - 1;
     if (last) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *slot = last;
@@ -252,8 +275,8 @@ DEV const gu16* token_row(const KArgs& a, int b, int task) {
 // residual the caller supplied instead of the one the previous layer wrote.
 DEV float load_x(const KArgs& a, int layer, int b, int i, const gu16* emb) {
   if (layer == 0) return bf2f(emb[i]);
-  const float* src = a.x_in ? a.x_in : a.x;
-  return src[((size_t)layer * a.max_batch + b) * a.H + i];
+  const size_t o = ((size_t)layer * a.max_batch + b) * a.H + i;
+  return a.x_in ? a.x_in[o] : ld_coh(a.x + o);
 }
 
 // double -> bfloat16 bits, round to nearest even: round the 52-bit mantissa to
@@ -464,7 +487,7 @@ DEV void compute_topk(const KArgs& a, int layer, TopK* tk, float* rbuf) {
   const int E = a.E, K = a.topk, n = a.n;
   const float* rl = a.rlog + (size_t)layer * a.max_batch * E;
   for (int i = tid(); i < n * E; i += kThreads) {
-    const float v = rl[i];
+    const float v = ld_coh(rl + i);
     rbuf[i] = v != v ? kNegInf : v;  // NaN never outranks a number
   }
   __syncthreads();
@@ -551,17 +574,31 @@ DEV void compute_topk(const KArgs& a, int layer, TopK* tk, float* rbuf) {
 // The layer's routing is computed once, by the last router task to finish,
 // and published as a TopK record; gate/up and output tasks copy it into LDS.
 DEV void publish_topk(const KArgs& a, int layer, const TopK* tk) {
-  const uint4* src = (const uint4*)tk;
-  uint4* dst = (uint4*)(a.topk_g + (size_t)layer * sizeof(TopK));
-  for (int i = tid(); i < (int)(sizeof(TopK) / 16); i += kThreads) dst[i] = src[i];
+  const uint32_t* src = (const uint32_t*)tk;
+  uint32_t* dst = (uint32_t*)(a.topk_g + (size_t)layer * sizeof(TopK));
+  for (int i = tid(); i < (int)(sizeof(TopK) / 4); i += kThreads) st_coh(dst + i, src[i]);
   if (tid() < a.n * a.topk)
     a.sel_out[(size_t)layer * a.max_batch * a.topk + tid()] = tk->sel[tid() / a.topk][tid() % a.topk];
 }
 
+// Copies nbytes (a multiple of 16) that other compute units wrote into LDS
+// with the LDS DMA path and the device-coherent policy, all in flight at
+// once; the data is there after the next s_waitcnt(0) and barrier.
+DEV void copy_coh_to_lds(void* dst_lds, const void* src, int nbytes) {
+  const int lane = tid() & 63, wave = tid() >> 6;
+  const AS_GLOBAL uint8_t* s8 = (const AS_GLOBAL uint8_t*)src;
+  uint8_t* d8 = (uint8_t*)dst_lds;
+  const int nchunk = (nbytes + 1023) >> 10;
+  for (int c = wave; c < nchunk; c += kWaves) {
+    const int off = (c << 10) + (lane << 4);
+    if (off < nbytes)
+      __builtin_amdgcn_global_load_lds((AS_GLOBAL void*)(s8 + off), (AS_LDS void*)(d8 + (c << 10)), 16, 0, kCohPolicy);
+  }
+}
+
+// The layer's routing record into LDS (complete after s_waitcnt(0) and a barrier).
 DEV void load_topk(const KArgs& a, int layer, TopK* tk) {
-  const uint4* src = (const uint4*)(a.topk_g + (size_t)layer * sizeof(TopK));
-  uint4* dst = (uint4*)tk;
-  for (int i = tid(); i < (int)(sizeof(TopK) / 16); i += kThreads) dst[i] = src[i];
+  copy_coh_to_lds(tk, a.topk_g + (size_t)layer * sizeof(TopK), (int)sizeof(TopK));
 }
 
 // ---------------------------------------------------------------------------
@@ -624,7 +661,7 @@ struct JobPre {
   DEV const lu4* lrow(int i) const { return (const lu4*)(pf + i * K); }
   DEV int nx(int) const { return 1 << 30; }
   DEV const uint4* x(int, int t) const { return (const uint4*)(xs + (size_t)t * K); }
-  DEV void emit(int i, int t, float v) const { out[(size_t)t * ld + i] = v; }
+  DEV void emit(int i, int t, float v) const { st_coh(out + (size_t)t * ld + i, v); }
 };
 
 TASK void task_pre(const KArgs& a, const Task& t, const Lds& s, int qi, int npf) {
@@ -955,7 +992,7 @@ DEV void attn_combine(const KArgs& a, const Lds& s, const float* parts, int nch,
       const int piece = 64 * q + lane;
       if (piece < n16)
         __builtin_amdgcn_global_load_lds((AS_GLOBAL void*)(src + 16 * (size_t)piece), (AS_LDS void*)(s.P + 1024 * q),
-                                         16, 0, 0);
+                                         16, 0, kCohPolicy);
     }
     prefetch_wait();
     const float* pl = (const float*)s.P;
@@ -980,14 +1017,16 @@ DEV void attn_combine(const KArgs& a, const Lds& s, const float* parts, int nch,
 #pragma unroll
       for (int k = 0; k < R; ++k) {
         const int j = sl + S * (k0 + k);
-        v[k] = (act && j < nch) ? *(const float4*)(parts + (size_t)j * CS + 4 * f) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float* pj = parts + (size_t)j * CS + 4 * f;
+        v[k] = (act && j < nch) ? make_float4(ld_coh(pj), ld_coh(pj + 1), ld_coh(pj + 2), ld_coh(pj + 3))
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
       }
     };
     load(0);
     for (int i = tid(); i < nch * G; i += kThreads) {
       const int j = i / G, h = i - j * G;
-      mj[i] = parts[(size_t)j * CS + GD + h];
-      lj[i] = parts[(size_t)j * CS + GD + kMaxGroup + h];
+      mj[i] = ld_coh(parts + (size_t)j * CS + GD + h);
+      lj[i] = ld_coh(parts + (size_t)j * CS + GD + kMaxGroup + h);
     }
     __syncthreads();
     float M = kNegInf;
@@ -1022,7 +1061,8 @@ DEV void attn_combine(const KArgs& a, const Lds& s, const float* parts, int nch,
     }
     const uint32_t lo = (uint32_t)f2bf(o.x / Ls) | ((uint32_t)f2bf(o.y / Ls) << 16);
     const uint32_t hi = (uint32_t)f2bf(o.z / Ls) | ((uint32_t)f2bf(o.w / Ls) << 16);
-    *(uint2*)(out + 4 * f) = make_uint2(lo, hi);
+    st_coh((uint32_t*)(out + 4 * f), lo);
+    st_coh((uint32_t*)(out + 4 * f + 2), hi);
   }
 }
 
@@ -1068,7 +1108,7 @@ DEV void attn_task(const KArgs& a, const Task& t, const Lds& s, int qi) {
     sincos((double)p * a.inv_freq[i], &sd, &cd);
     const float cf = (float)cd, sf = (float)sd;
     const float* q = qkv + (size_t)(g * G + hh) * D;
-    const float x0 = q[i], x1 = q[i + half];
+    const float x0 = ld_coh(q + i), x1 = ld_coh(q + i + half);
     q_s[hh * D + i] = f2bf(x0 * cf - x1 * sf);
     q_s[hh * D + i + half] = f2bf(x0 * sf + x1 * cf);
   }
@@ -1090,7 +1130,7 @@ DEV void attn_task(const KArgs& a, const Task& t, const Lds& s, int qi) {
         double sd, cd;
         sincos((double)p * a.inv_freq[i], &sd, &cd);
         const float cf = (float)cd, sf = (float)sd;
-        const float x0 = kk[i], x1 = kk[i + half];
+        const float x0 = ld_coh(kk + i), x1 = ld_coh(kk + i + half);
         k_lo = f2bf(x0 * cf - x1 * sf);
         k_hi = f2bf(x0 * sf + x1 * cf);
         a.k_pool[off + i] = k_lo;
@@ -1099,7 +1139,7 @@ DEV void attn_task(const KArgs& a, const Task& t, const Lds& s, int qi) {
       // V pages are stored dims-major: element (dim, slot) of a (page, head) block at dim*page_size + slot
       const size_t voff = (((size_t)l * a.num_pages + page) * a.nkv + g) * (size_t)ps * D + p % ps;
       if (i < D) {
-        v_i = f2bf(vv[i]);
+        v_i = f2bf(ld_coh(vv + i));
         a.v_pool[voff + (size_t)i * ps] = v_i;
       }
     }
@@ -1147,10 +1187,13 @@ DEV void attn_task(const KArgs& a, const Task& t, const Lds& s, int qi) {
       O.w += ow.w * sc;
       Ls += mrg.l[w * kMaxGroup + hh] * sc;
     }
-    *(float4*)(part + 4 * e4) = O;
+    st_coh(part + 4 * e4, O.x);
+    st_coh(part + 4 * e4 + 1, O.y);
+    st_coh(part + 4 * e4 + 2, O.z);
+    st_coh(part + 4 * e4 + 3, O.w);
     if ((4 * e4) % D == 0) {
-      part[GD + hh] = M;
-      part[GD + kMaxGroup + hh] = Ls;
+      st_coh(part + GD + hh, M);
+      st_coh(part + GD + kMaxGroup + hh, Ls);
     }
   }
   uint32_t* ticket = a.tickets + ((size_t)l * a.max_batch + b) * a.nkv + g;
@@ -1204,11 +1247,11 @@ struct JobGateUp {
 // the PRE task that ran just before on this compute unit.
 TASK void task_gateup(const KArgs& a, const Task& t, const Lds& s, int qi, bool have_xs) {
   const int l = t.layer;
-  load_topk(a, l, s.tk);  // visible to all threads after the next barrier
-  mark(a, qi, 0);
+  load_topk(a, l, s.tk);
   uint16_t* xs = (uint16_t*)s.A;
-  if (have_xs) __syncthreads();
-  else norm_inputs(a, l, wptr(a, widx(l, WL_NORM)), xs, s.red8, qi, -1);
+  if (!have_xs) norm_inputs(a, l, wptr(a, widx(l, WL_NORM)), xs, s.red8, qi, -1);
+  prefetch_wait();  // the routing record has landed
+  mark(a, qi, 0);
   mark(a, qi, 1);
   const TopK* tk = s.tk;
   const int64_t R = (int64_t)tk->nU * a.I;
@@ -1239,7 +1282,7 @@ TASK void task_gateup(const KArgs& a, const Task& t, const Lds& s, int qi, bool 
         const float gg = j.gs[((size_t)vi * a.max_batch + tt) * 2];
         const float uu = j.gs[((size_t)vi * a.max_batch + tt) * 2 + 1];
         const float hv = gg / (1.0f + __expf(-gg)) * uu;
-        hl[(size_t)tk->pair[u][tt] * a.I + r] = f2bf(hv);
+        st_coh(hl + (size_t)tk->pair[u][tt] * a.I + r, f2bf(hv));
       }
     }
     __syncthreads();
@@ -1278,12 +1321,6 @@ struct JobDown {
   DEV void emit(int i, int t, float v) const { contrib[(size_t)(i / nU) * maxBK + tk->pair[i % nU][t]] = v; }
 };
 
-DEV void copy_to_lds(uint16_t* dst, const uint16_t* src, int elems) {
-  const uint4* s4 = (const uint4*)src;
-  uint4* d4 = (uint4*)dst;
-  for (int i = tid(); i < elems / 8; i += kThreads) d4[i] = s4[i];
-}
-
 TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf) {
   const int l = t.layer, nr = t.r1 - t.r0, n = a.n, AD = a.nq * a.d;
   float* ao = (float*)s.C;                                    // [out_rows_max][maxB]
@@ -1292,8 +1329,8 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf)
   uint16_t* xs = (uint16_t*)s.A;
   // expert down projections: their inputs (gate/up) are ready when the task starts
   load_topk(a, l, s.tk);
-  copy_to_lds(xs, a.h + (size_t)l * a.max_batch * a.topk * a.I, n * a.topk * a.I);
-  __syncthreads();
+  copy_coh_to_lds(xs, a.h + (size_t)l * a.max_batch * a.topk * a.I, n * a.topk * a.I * 2);
+  prefetch_wait();
   const TopK* tk = s.tk;
   mark(a, qi, 0);
   JobDown jd;
@@ -1311,7 +1348,7 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf)
   // attention output projection: wait for attention, Wo rows are already in LDS
   wait_counter(a, t.late_wait, t.late_fanin, qi, s.flags + 13);  // its barrier also frees xs
   mark(a, qi, 2);
-  copy_to_lds(xs, a.attn_out + (size_t)l * a.max_batch * AD, n * AD);
+  copy_coh_to_lds(xs, a.attn_out + (size_t)l * a.max_batch * AD, n * AD * 2);
   prefetch_wait();
   JobO jo;
   jo.pf = (const AS_LDS uint16_t*)s.P;
@@ -1332,7 +1369,7 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf)
     for (int j = 0; j < a.topk; ++j) moe += tk->w[b][j] * contrib[(size_t)rr * maxBK + b * a.topk + j];
     const gu16* emb = l == 0 ? token_row(a, b, qi) : nullptr;
     const float xo = load_x(a, l, b, t.r0 + rr, emb);
-    a.x[((size_t)(l + 1) * a.max_batch + b) * a.H + t.r0 + rr] = (xo + ao[(size_t)rr * a.max_batch + b]) + moe;
+    st_coh(a.x + ((size_t)(l + 1) * a.max_batch + b) * a.H + t.r0 + rr, (xo + ao[(size_t)rr * a.max_batch + b]) + moe);
   }
 }
 
@@ -1419,8 +1456,8 @@ TASK void task_lmhead(const KArgs& a, const Task& t, const Lds& s, int qi) {
   mark(a, qi, 1);
   if (tid() == 0) {
     for (int b = 0; b < a.n; ++b) {
-      a.lm_part[((size_t)t.idx * a.max_batch + b) * 2] = best_v[b];
-      ((int*)a.lm_part)[((size_t)t.idx * a.max_batch + b) * 2 + 1] = best_i[b];
+      st_coh(a.lm_part + ((size_t)t.idx * a.max_batch + b) * 2, best_v[b]);
+      st_coh((uint32_t*)a.lm_part + ((size_t)t.idx * a.max_batch + b) * 2 + 1, (uint32_t)best_i[b]);
     }
   }
   uint32_t* ticket = a.tickets + (size_t)a.L * a.max_batch * a.nkv;
@@ -1430,8 +1467,8 @@ TASK void task_lmhead(const KArgs& a, const Task& t, const Lds& s, int qi) {
       float v = kNegInf;
       int i = 0x7fffffff;
       for (int k = tid(); k < a.n_lm; k += kThreads) {
-        const float x = a.lm_part[((size_t)k * a.max_batch + b) * 2];
-        const int xi = ((const int*)a.lm_part)[((size_t)k * a.max_batch + b) * 2 + 1];
+        const float x = ld_coh(a.lm_part + ((size_t)k * a.max_batch + b) * 2);
+        const int xi = (int)ld_coh((const uint32_t*)a.lm_part + ((size_t)k * a.max_batch + b) * 2 + 1);
         if (better(x, xi, v, i)) { v = x; i = xi; }
       }
       block_argmax(v, i, s.red);
@@ -1471,7 +1508,7 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a)
       }
     }
     xs_layer = ok && t.op == OP_PRE ? t.layer : (ok && t.op == OP_GATEUP ? xs_layer : -1);
-    signal_counter(a, t.signal);
+    signal_counter(a, t.signal, t.slot);
     if (a.trace && tid() == 0 && q < a.trace_cap) {
       uint64_t* r = a.trace + kTraceWords * (size_t)q;
       r[0] = t_fetch;

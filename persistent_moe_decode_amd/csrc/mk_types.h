@@ -40,16 +40,20 @@ struct Task {
   int32_t layer;
   int32_t wait[2];    // counter index or -1
   int32_t fanin[2];   // signals per step on that counter
-  int32_t signal;     // counter to increment once when done, or -1
+  int32_t signal;     // counter whose flag word `slot` is set when done, or -1
   int32_t r0, r1;     // row range (PRE, OUT, LMHEAD)
   int32_t idx, count; // index of this task among the op's tasks of the layer, and their number
   int32_t late_wait;  // counter waited inside the body, once its first part is done (-1 = none)
   int32_t late_fanin;
-  int32_t pad[19];
+  int32_t slot;       // this task's flag word on its signal counter: 0 .. (signals on that counter) - 1
+  int32_t pad[18];
 };
 static_assert(sizeof(Task) == kTaskInts * 4, "task descriptor is 128 bytes");
 
-// Counters: per layer l, kCtrPerLayer slots.
+// Counters: per layer l, kCtrPerLayer of them.  A counter is an array of
+// flag words, one per task that signals it; a task signals by storing the
+// step's epoch into its own word, and a wait is over when every word of the
+// counter holds the epoch.
 enum CtrSlot : int32_t { C_QKV = 0, C_ROUTER = 1, C_ATTN = 2, C_GATEUP = 3, C_XNEXT = 4, C_DONE = 5 };
 constexpr int kCtrPerLayer = 8;
 
@@ -70,7 +74,8 @@ struct KArgs {
   int32_t pf_bytes;                                // size of the weight prefetch region
   const Task* tasks;
   const int32_t* queue_off;
-  uint32_t* ctr;        // counters [L * kCtrPerLayer + 8]
+  uint32_t* flags;      // counters: [(L + 1) * kCtrPerLayer][n_slots] flag words
+  int32_t n_slots;      // flag words per counter
   uint32_t* tickets;    // attention tickets [L][max_batch][nkv], 1 for the LM head, then [L] routers
   int32_t* err;         // E_WORDS
   const uint64_t* wtab; // device pointers of the weights
@@ -79,7 +84,7 @@ struct KArgs {
   float* x;             // [L+1][max_batch][H]
   float* qkv;           // [L][max_batch][qkv_rows]
   float* rlog;          // [L][max_batch][E]
-  float* attn_part;     // [L][n_attn][group*(d+2)]
+  float* attn_part;     // [L][n_attn][attn_part_stride(group, d)]
   uint16_t* attn_out;   // [L][max_batch][nq*d]
   uint16_t* h;          // [L][max_batch*topk][I]
   float* lm_part;       // [n_lm][max_batch][2] (value, index as float bits)

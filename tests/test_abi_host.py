@@ -11,7 +11,7 @@ import synth
 from persistent_moe_decode_amd import mk
 
 OP_PRE, OP_ATTN, OP_GATEUP, OP_OUT, OP_LMHEAD = 1, 2, 3, 4, 5
-F_OP, F_LAYER, F_WAIT0, F_WAIT1, F_FAN0, F_FAN1, F_SIGNAL, F_R0, F_R1, F_IDX, F_COUNT, F_LATE, F_LATE_FAN = range(13)
+F_OP, F_LAYER, F_WAIT0, F_WAIT1, F_FAN0, F_FAN1, F_SIGNAL, F_R0, F_R1, F_IDX, F_COUNT, F_LATE, F_LATE_FAN, F_SLOT = range(14)
 
 
 def test_library_exports_every_declared_symbol():
@@ -146,6 +146,27 @@ def test_simulator_catches_wrong_fanin():
     t = tasks.copy()
     i = int(np.nonzero(t[:, F_OP] == OP_OUT)[0][0])
     t[i, F_FAN0] -= 1
+    code, _ = mk.simulate_table(t, qoff, nctr)
+    assert code == mk.CODES["MK_ERR_SCHEDULE"]
+
+
+def test_every_counter_has_one_flag_word_per_signalling_task():
+    tasks, qoff, nctr = _tiny_table()
+    sig = tasks[:, F_SIGNAL]
+    for c in np.unique(sig[sig >= 0]):
+        slots = np.sort(tasks[sig == c, F_SLOT])
+        assert np.array_equal(slots, np.arange(len(slots)))
+
+
+def test_simulator_catches_a_shared_flag_word():
+    tasks, qoff, nctr = _tiny_table()
+    t = tasks.copy()
+    outs = np.nonzero((t[:, F_OP] == OP_OUT) & (t[:, F_LAYER] == 0))[0]
+    t[outs[1], F_SLOT] = t[outs[0], F_SLOT]      # two tasks would set the same word
+    code, _ = mk.simulate_table(t, qoff, nctr)
+    assert code == mk.CODES["MK_ERR_SCHEDULE"]
+    t = tasks.copy()
+    t[outs[0], F_SLOT] = len(outs)                # a word past the counter's signallers
     code, _ = mk.simulate_table(t, qoff, nctr)
     assert code == mk.CODES["MK_ERR_SCHEDULE"]
 
