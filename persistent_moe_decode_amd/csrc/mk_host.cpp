@@ -44,7 +44,7 @@ struct WsLayout {
   size_t state = 0, n_state_u32 = 0;  // counter flags, tickets, error word (zeroed by mk_reset)
   size_t ctr = 0, tickets = 0, err = 0;
   size_t tasks = 0, queue_off = 0, wtab = 0, inv_freq = 0;
-  size_t x = 0, qkv = 0, rlog = 0, attn_part = 0, attn_out = 0, h = 0, lm_part = 0, sel = 0, topk = 0;
+  size_t x = 0, qkv = 0, rlog = 0, attn_part = 0, attn_out = 0, h = 0, lm_part = 0, sel = 0;
   size_t total = 0;
 };
 
@@ -231,7 +231,6 @@ static WsLayout layout_workspace(const mk_ctx* c) {
   w.h = take(2 * L * B * f.top_k * f.inter);
   w.lm_part = take(4 * 2 * c->n_lm * B);
   w.sel = take(4 * L * B * f.top_k);
-  w.topk = take((size_t)kTopKRecord * L);
   w.total = o;
   return w;
 }
@@ -255,9 +254,13 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
   const int group = f.n_q_heads / f.n_kv_heads;
   if (ncu < 2) return fail(MK_ERR_UNSUPPORTED, "need at least 2 compute units");
 
-  // Compute units split between attention chunks and expert gate/up rows in
-  // proportion to the bytes each streams per layer (attention weighted 1.5x
-  // for its extra arithmetic).  The split never changes results.
+  // Compute units 0 .. n_attn - 1 run the attention split and no stage-1
+  // rows, so their K/V loads are in flight while the other units normalize
+  // and project; units n_attn .. ncu - 1 run the stage-1 rows and then the
+  // selected experts' gate/up rows.  Every unit takes an equal share of the
+  // output rows.  n_attn follows the bytes attention streams per layer
+  // against the expert gate/up bytes (attention weighted 1.5x for its extra
+  // arithmetic); the split never changes results.
   const double hint = ctx_hint > 0 ? (double)ctx_hint : 4096.0;
   const double attn_bytes = 1.5 * hint * B * f.n_kv_heads * f.head_dim * 4.0;
   const double gu_bytes = (double)std::min(E, B * f.top_k) * 2.0 * f.inter * H * 2.0;
@@ -265,7 +268,7 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
   const char* env = std::getenv("MK_ATTN_CUS");
   if (env) n_attn = std::atoi(env);
   n_attn = std::max(n_attn, B * f.n_kv_heads);
-  n_attn = std::min(n_attn, ncu - 1);
+  n_attn = std::min(n_attn, ncu - 2);  // at least one unit each for the QKV and the router rows
   if (n_attn < B * f.n_kv_heads) return fail(MK_ERR_UNSUPPORTED, "too few compute units for the attention split");
   const int n_gu = ncu - n_attn;
 
@@ -275,15 +278,19 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
   c->n_attn = n_attn;
   c->n_gu = n_gu;
   c->n_ctr = (L + 1) * kCtrPerLayer;
-  c->n_tickets = L * B * f.n_kv_heads + 1 + L;  // attention (seq, kv head) merges, LM argmax, router top-k
+  c->n_tickets = L * B * f.n_kv_heads + 1;  // attention (seq, kv head) merges, LM argmax
 
-  // Stage 1 rows: the router's rows go to the last n_rcu compute units (they
-  // also take the top-k), Wqkv rows to the others, so no unit has two stage-1
-  // tasks and the routing is ready as early as the QKV rows.
+  // Stage-1 rows over units n_attn ..: the router's rows go to the last n_rcu
+  // of them, Wqkv rows to the others, so no unit has two stage-1 tasks and the
+  // routing is ready as early as the QKV rows.
   const int R1 = qkv_rows + E;
-  const int n_rcu = std::min(ncu - 1, std::max(1, (int)(((int64_t)ncu * E + R1 - 1) / R1)));
-  const int n_qcu = ncu - n_rcu;
+  const int m1 = ncu - n_attn;
+  const int n_rcu = std::min(m1 - 1, std::max(1, (int)(((int64_t)m1 * E + R1 - 1) / R1)));
+  const int n_qcu = m1 - n_rcu;
   auto pre_rows = [&](int q, int* r0, int* r1) {
+    *r0 = *r1 = 0;
+    if (q < n_attn) return;
+    q -= n_attn;
     if (q < n_qcu) {
       split_rows(qkv_rows, n_qcu, q, r0, r1);
     } else {
@@ -333,10 +340,9 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
         t.r0 = r0;
         t.r1 = r1;
         t.signal = ctr_index(l, router ? C_ROUTER : C_QKV);
-        if (router) t.count = n_router_tasks[l];  // the last of them publishes the layer's routing
         c->tasks.push_back(t);
       }
-      // stage 2
+      // stage 2: attention units run their chunk, the others gate/up rows
       if (q < n_attn) {
         Task t = make_task(OP_ATTN, l);
         t.wait[0] = ctr_index(l, C_QKV);
@@ -631,7 +637,6 @@ extern "C" int mk_decode_step(mk_ctx* c, int32_t n, const int32_t* d_tokens, con
   a.h = (uint16_t*)(w + c->ws.h);
   a.lm_part = (float*)(w + c->ws.lm_part);
   a.sel_out = (int32_t*)(w + c->ws.sel);
-  a.topk_g = w + c->ws.topk;
   a.x_in = c->x_in;
   a.trace = c->trace;
   a.trace_cap = c->trace_cap;

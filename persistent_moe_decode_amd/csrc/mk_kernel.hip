@@ -130,7 +130,6 @@ struct TopK {
 };
 constexpr int kTopKBytes = 3136;
 static_assert(sizeof(TopK) <= kTopKBytes && sizeof(TopK) % 16 == 0, "top-k state fits region B, 16-byte multiple");
-static_assert(sizeof(TopK) == kTopKRecord, "published routing record size");
 
 struct Lds {
   uint8_t* base;
@@ -571,12 +570,8 @@ DEV void compute_topk(const KArgs& a, int layer, TopK* tk, float* rbuf) {
   __syncthreads();
 }
 
-// The layer's routing is computed once, by the last router task to finish,
-// and published as a TopK record; gate/up and output tasks copy it into LDS.
-DEV void publish_topk(const KArgs& a, int layer, const TopK* tk) {
-  const uint32_t* src = (const uint32_t*)tk;
-  uint32_t* dst = (uint32_t*)(a.topk_g + (size_t)layer * sizeof(TopK));
-  for (int i = tid(); i < (int)(sizeof(TopK) / 4); i += kThreads) st_coh(dst + i, src[i]);
+// The experts chosen per token, reported to the caller (written by one task per layer).
+DEV void write_sel(const KArgs& a, int layer, const TopK* tk) {
   if (tid() < a.n * a.topk)
     a.sel_out[(size_t)layer * a.max_batch * a.topk + tid()] = tk->sel[tid() / a.topk][tid() % a.topk];
 }
@@ -596,10 +591,6 @@ DEV void copy_coh_to_lds(void* dst_lds, const void* src, int nbytes) {
   }
 }
 
-// The layer's routing record into LDS (complete after s_waitcnt(0) and a barrier).
-DEV void load_topk(const KArgs& a, int layer, TopK* tk) {
-  copy_coh_to_lds(tk, a.topk_g + (size_t)layer * sizeof(TopK), (int)sizeof(TopK));
-}
 
 // ---------------------------------------------------------------------------
 // PRE: RMSNorm + rows [r0, r1) of the stacked [Wq; Wk; Wv; Wr] matrix.
@@ -608,11 +599,13 @@ DEV void load_topk(const KArgs& a, int layer, TopK* tk) {
 // task waits for its inputs (the pages' third-ranked gain: weights start
 // streaming before dependencies resolve).  Rows [0, npf) of a job's matrix
 // are then read from P, the rest from HBM.
+// Waves 1..7 issue the copies: wave 0, whose thread 0 polls the flags right
+// after, keeps its load queue short (a wave's loads complete in order).
 DEV void prefetch_to_lds(const gu16* src, uint8_t* dst_lds, int nbytes) {
   const int lane = tid() & 63, wave = tid() >> 6;
   const AS_GLOBAL uint8_t* s8 = (const AS_GLOBAL uint8_t*)src;
   const int nchunk = (nbytes + 1023) >> 10;
-  for (int c = wave; c < nchunk; c += kWaves) {
+  for (int c = wave - 1; wave > 0 && c < nchunk; c += kWaves - 1) {
     const int off = (c << 10) + (lane << 4);
     if (off < nbytes)
       __builtin_amdgcn_global_load_lds((AS_GLOBAL void*)(s8 + off), (AS_LDS void*)(dst_lds + (c << 10)), 16, 0, 0);
@@ -688,14 +681,6 @@ TASK void task_pre(const KArgs& a, const Task& t, const Lds& s, int qi, int npf)
   }
   run_rowdots_pf(a.H, t.r1 - t.r0, npf, a.n, j);
   mark(a, qi, 2);
-  if (t.r0 >= a.qkv_rows) {
-    // router rows: the last router task of the layer takes the top-k for everyone
-    uint32_t* ticket = a.tickets + (size_t)a.L * a.max_batch * a.nkv + 1 + l;
-    if (arrive_last(ticket, (uint32_t)t.count, s.flags + 12)) {
-      compute_topk(a, l, s.tk, s.rbuf);
-      publish_topk(a, l, s.tk);
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1243,15 +1228,17 @@ struct JobGateUp {
   DEV void emit(int i, int t, float v) const { gs[((size_t)(i >> 1) * maxB + t) * 2 + (i & 1)] = v; }
 };
 
+// Every gate/up task takes the layer's top-k itself from the router logits
+// (once the router rows are done), which spares the routing a hop of its own.
 // have_xs: region A still holds this layer's normalized input, left there by
 // the PRE task that ran just before on this compute unit.
 TASK void task_gateup(const KArgs& a, const Task& t, const Lds& s, int qi, bool have_xs) {
   const int l = t.layer;
-  load_topk(a, l, s.tk);
+  compute_topk(a, l, s.tk, s.rbuf);
+  if (t.idx == 0) write_sel(a, l, s.tk);
+  mark(a, qi, 0);
   uint16_t* xs = (uint16_t*)s.A;
   if (!have_xs) norm_inputs(a, l, wptr(a, widx(l, WL_NORM)), xs, s.red8, qi, -1);
-  prefetch_wait();  // the routing record has landed
-  mark(a, qi, 0);
   mark(a, qi, 1);
   const TopK* tk = s.tk;
   const int64_t R = (int64_t)tk->nU * a.I;
@@ -1321,14 +1308,16 @@ struct JobDown {
   DEV void emit(int i, int t, float v) const { contrib[(size_t)(i / nU) * maxBK + tk->pair[i % nU][t]] = v; }
 };
 
-TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf) {
+// have_tk: region B still holds this layer's top-k, left there by the gate/up
+// task that ran just before on this compute unit.
+TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf, bool have_tk) {
   const int l = t.layer, nr = t.r1 - t.r0, n = a.n, AD = a.nq * a.d;
   float* ao = (float*)s.C;                                    // [out_rows_max][maxB]
   float* contrib = ao + (size_t)a.out_rows_max * a.max_batch;  // [out_rows_max][maxB*topk]
   const int maxBK = a.max_batch * a.topk;
   uint16_t* xs = (uint16_t*)s.A;
   // expert down projections: their inputs (gate/up) are ready when the task starts
-  load_topk(a, l, s.tk);
+  if (!have_tk) compute_topk(a, l, s.tk, s.rbuf);
   copy_coh_to_lds(xs, a.h + (size_t)l * a.max_batch * a.topk * a.I, n * a.topk * a.I * 2);
   prefetch_wait();
   const TopK* tk = s.tk;
@@ -1487,6 +1476,7 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a)
   if (tid() == 0) s.flags[16] = -1;  // no attention plan cached yet
   __syncthreads();
   int xs_layer = -1;                 // layer whose normalized input region A holds
+  int tk_layer = -1;                 // layer whose top-k region B holds
   for (int q = q0; q < q1; ++q) {
     const Task t = a.tasks[q];
     uint64_t t_fetch = 0, t_ready = 0;
@@ -1502,12 +1492,13 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a)
         case OP_PRE: task_pre(a, t, s, q, npf); break;
         case OP_ATTN: task_attn(a, t, s, q); break;
         case OP_GATEUP: task_gateup(a, t, s, q, xs_layer == t.layer); break;
-        case OP_OUT: task_out(a, t, s, q, npf); break;
+        case OP_OUT: task_out(a, t, s, q, npf, tk_layer == t.layer); break;
         case OP_LMHEAD: task_lmhead(a, t, s, q); break;
         default: break;
       }
     }
     xs_layer = ok && t.op == OP_PRE ? t.layer : (ok && t.op == OP_GATEUP ? xs_layer : -1);
+    tk_layer = ok && (t.op == OP_GATEUP || t.op == OP_OUT) ? t.layer : (t.op == OP_LMHEAD ? -1 : tk_layer);
     signal_counter(a, t.signal, t.slot);
     if (a.trace && tid() == 0 && q < a.trace_cap) {
       uint64_t* r = a.trace + kTraceWords * (size_t)q;

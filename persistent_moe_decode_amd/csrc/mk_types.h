@@ -24,12 +24,11 @@ constexpr int kGuPass = 256;       // gate/up virtual rows per pass of one task
 constexpr int kLmPass = 512;       // LM head rows per pass of one task
 constexpr int kTraceWords = 8;     // per task: fetch, ready, 4 phase marks, done, spare
 constexpr int kLdsB = 8192;        // LDS region B: top-k state, flags, reductions, router logits
-constexpr int kTopKRecord = 3088;  // bytes of one layer's published routing (experts, weights, groups)
 
 enum Op : int32_t {
   OP_PRE = 1,     // RMSNorm + rows of [Wq; Wk; Wv] or of the router
   OP_ATTN = 2,    // paged split-KV attention chunk; last arriver of a (seq, kv head) combines
-  OP_GATEUP = 3,  // top-k + rows of the selected experts' gate/up + SwiGLU
+  OP_GATEUP = 3,  // router top-k + rows of the selected experts' gate/up + SwiGLU
   OP_OUT = 4,     // rows of Wo and of the selected experts' down projection + residual
   OP_LMHEAD = 5,  // final RMSNorm + LM head rows; last arriver takes the argmax
 };
@@ -76,7 +75,7 @@ struct KArgs {
   const int32_t* queue_off;
   uint32_t* flags;      // counters: [(L + 1) * kCtrPerLayer][n_slots] flag words
   int32_t n_slots;      // flag words per counter
-  uint32_t* tickets;    // attention tickets [L][max_batch][nkv], 1 for the LM head, then [L] routers
+  uint32_t* tickets;    // attention tickets [L][max_batch][nkv], then 1 for the LM head
   int32_t* err;         // E_WORDS
   const uint64_t* wtab; // device pointers of the weights
   const double* inv_freq; // [d/2]
@@ -89,7 +88,6 @@ struct KArgs {
   uint16_t* h;          // [L][max_batch*topk][I]
   float* lm_part;       // [n_lm][max_batch][2] (value, index as float bits)
   int32_t* sel_out;     // [L][max_batch][topk] experts chosen per token
-  uint8_t* topk_g;      // [L] routing records (kTopKRecord bytes each)
   const float* x_in;    // test hook: layer inputs [L+1][max_batch][H] read instead of x (NULL = off)
   uint64_t* trace;      // per task: s_memrealtime at fetch, dependencies met, done (NULL = off)
   int64_t trace_cap;    // tasks the trace buffer holds

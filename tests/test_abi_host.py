@@ -56,7 +56,7 @@ def test_calls_out_of_order_fail_cleanly():
 def test_schedule_builds_and_simulates(name, ncu):
     w = synth.workload(name)
     c = _ctx(w.shape, w.batch, w.max_pages_per_seq, w.num_pages)
-    if ncu < w.batch * w.shape.n_kv_heads + 1:
+    if ncu < w.batch * w.shape.n_kv_heads + 2:
         with pytest.raises(mk.MkError):
             c.build_schedule(ncu, int(np.mean(w.context)))
         return
@@ -70,7 +70,13 @@ def test_schedule_builds_and_simulates(name, ncu):
     assert np.sum(ops == OP_ATTN) == L * info.n_attn
     assert np.sum(ops == OP_GATEUP) == L * info.n_gateup
     assert info.n_attn + info.n_gateup == ncu
-    assert info.n_attn >= w.batch * w.shape.n_kv_heads
+    assert w.batch * w.shape.n_kv_heads <= info.n_attn <= ncu - 2
+    # attention units run their chunk and no stage-1 rows; every other unit one stage-1 and one gate/up task
+    for q in range(ncu):
+        mine = tasks[qoff[q]:qoff[q + 1]]
+        l0 = mine[:, F_LAYER] == 0
+        n = tuple(int(np.sum((mine[:, F_OP] == op) & l0)) for op in (OP_PRE, OP_ATTN, OP_GATEUP))
+        assert n == ((0, 1, 0) if q < info.n_attn else (1, 0, 1)), q
     # PRE rows cover [Wqkv; router] exactly once per layer; OUT rows cover hidden; LM rows cover vocab
     for l in range(L):
         pre = tasks[(ops == OP_PRE) & (tasks[:, F_LAYER] == l)]
@@ -131,12 +137,13 @@ def test_simulator_catches_a_dropped_signal():
 def test_simulator_catches_consumer_before_producer():
     tasks, qoff, nctr = _tiny_table()
     t = tasks.copy()
-    # on queue 0, put the OUT task of layer 0 before its own PRE task
-    q = t[qoff[0]:qoff[1]]
+    # on the last queue (a unit with stage-1 rows), put the OUT task of layer 0 before its own PRE task
+    k = len(qoff) - 2
+    q = t[qoff[k]:qoff[k + 1]]
     i_pre = int(np.nonzero((q[:, F_OP] == OP_PRE) & (q[:, F_LAYER] == 0))[0][0])
     i_out = int(np.nonzero((q[:, F_OP] == OP_OUT) & (q[:, F_LAYER] == 0))[0][0])
     q[[i_pre, i_out]] = q[[i_out, i_pre]]
-    t[qoff[0]:qoff[1]] = q
+    t[qoff[k]:qoff[k + 1]] = q
     code, done = mk.simulate_table(t, qoff, nctr)
     assert code == mk.CODES["MK_ERR_SCHEDULE"] and done < len(t)
 
@@ -181,12 +188,13 @@ def test_simulator_counts_the_in_body_wait():
     assert code == mk.CODES["MK_ERR_SCHEDULE"]
     # an in-body wait on a counter that only a later task of the same queue signals deadlocks
     t = tasks.copy()
-    q0 = t[qoff[0]:qoff[1]]
+    k = len(qoff) - 2
+    q0 = t[qoff[k]:qoff[k + 1]]
     i_out = int(np.nonzero((q0[:, F_OP] == OP_OUT) & (q0[:, F_LAYER] == 0))[0][0])
     nxt_pre = int(np.nonzero((q0[:, F_OP] == OP_PRE) & (q0[:, F_LAYER] == 1))[0][0])
     q0[i_out, F_LATE] = q0[nxt_pre, F_SIGNAL]
     q0[i_out, F_LATE_FAN] = int(np.sum(t[:, F_SIGNAL] == q0[nxt_pre, F_SIGNAL]))
-    t[qoff[0]:qoff[1]] = q0
+    t[qoff[k]:qoff[k + 1]] = q0
     code, done = mk.simulate_table(t, qoff, nctr)
     assert code == mk.CODES["MK_ERR_SCHEDULE"] and done < len(t)
 
@@ -196,12 +204,12 @@ def test_router_rows_have_their_own_units():
     c = _ctx(w.shape, 1, w.max_pages_per_seq, w.num_pages)
     c.build_schedule(256, 8192)
     tasks, qoff = c.schedule()
-    for q in range(256):
-        pre = tasks[qoff[q]:qoff[q + 1]]
-        pre = pre[(pre[:, F_OP] == OP_PRE) & (pre[:, F_LAYER] == 0)]
-        assert len(pre) == 1
     routers = tasks[(tasks[:, F_OP] == OP_PRE) & (tasks[:, F_R0] >= w.shape.qkv_rows) & (tasks[:, F_LAYER] == 0)]
-    assert 1 <= len(routers) <= 8 and np.all(routers[:, F_COUNT] == len(routers))
+    assert 1 <= len(routers) <= 8
+    assert np.all((routers[:, F_R1] <= w.shape.qkv_rows) | (routers[:, F_R0] >= w.shape.qkv_rows))
+    # gate/up tasks wait for the router rows only, not for the QKV rows
+    gu = tasks[(tasks[:, F_OP] == OP_GATEUP) & (tasks[:, F_LAYER] == 0)]
+    assert np.all(gu[:, F_WAIT0] == routers[0, F_SIGNAL]) and np.all(gu[:, F_FAN0] == len(routers))
 
 
 @pytest.mark.parametrize("lens,nkv,ntasks", [
