@@ -412,7 +412,7 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
   // attention: the waves' partial results, or (last chunk) the (max, sum) of all chunks plus one float4 per thread
   size_t c_attn = std::max((size_t)kWaves * (group * f.head_dim + 2 * kMaxGroup) * 4,
                            align_up((size_t)n_attn * group * 2 * 4, 16) + (size_t)kThreads * 16);
-  size_t c_bytes = align_up(std::max({c_gu, c_out, c_lm, c_attn}), 256);
+  size_t c_bytes = align_up(std::max({c_gu, c_out, c_lm, c_attn, (size_t)kTopKScratch}), 256);
   c->lds_b = (int)a_bytes;
   c->lds_c = (int)(a_bytes + b_bytes);
   c->lds_p = (int)(a_bytes + b_bytes + c_bytes);

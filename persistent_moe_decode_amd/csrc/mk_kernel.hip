@@ -481,14 +481,19 @@ DEV void run_rowdots_pf(int K, int njobs, int npf, int maxnx, const Job& job) {
 
 DEV bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
 
-DEV void compute_topk(const KArgs& a, int layer, TopK* tk, float* rbuf) {
+// scratch: 4 * kMaxExperts + kMaxBatch * kMaxExperts bytes of LDS for the
+// per-expert token masks and slots.
+DEV void compute_topk(const KArgs& a, int layer, TopK* tk, float* rbuf, uint8_t* scratch) {
   const int lane = tid() & 63;
   const int E = a.E, K = a.topk, n = a.n;
+  int32_t* emask = (int32_t*)scratch;                  // [kMaxExperts]: bit b set when token b chose expert e
+  uint8_t* eslot = scratch + 4 * kMaxExperts;          // [kMaxBatch][kMaxExperts]: slot of e in token b's top-k
   const float* rl = a.rlog + (size_t)layer * a.max_batch * E;
   for (int i = tid(); i < n * E; i += kThreads) {
     const float v = ld_coh(rl + i);
     rbuf[i] = v != v ? kNegInf : v;  // NaN never outranks a number
   }
+  for (int e = tid(); e < kMaxExperts; e += kThreads) emask[e] = 0;
   __syncthreads();
   // four threads per (token, expert), each counting a quarter of the rivals; a quad sum joins them
   for (int i4 = tid(); i4 < 4 * n * E; i4 += kThreads) {
@@ -509,6 +514,8 @@ DEV void compute_topk(const KArgs& a, int layer, TopK* tk, float* rbuf) {
     if (part == 0 && rank < K) {
       tk->sel[b][rank] = e;
       tk->w[b][rank] = v;
+      atomicOr(emask + e, 1 << b);
+      eslot[b * kMaxExperts + e] = (uint8_t)rank;
     }
   }
   __syncthreads();
@@ -527,43 +534,30 @@ DEV void compute_topk(const KArgs& a, int layer, TopK* tk, float* rbuf) {
       for (int j = 0; j < kMaxTopK; ++j)
         if (j < K) tk->w[lane][j] = ex[j] / wsum;
     }
-    // distinct experts, ascending
-    const int np = a.n * K;
-    bool in0 = false, in1 = false;
-    for (int p = 0; p < np; ++p) {
-      const int e = tk->sel[p / K][p % K];
-      in0 |= e == lane;
-      in1 |= e == lane + 64;
-    }
-    const uint64_t m0 = __ballot(in0), m1 = __ballot(in1);
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int c0 = __popcll(m0);
-    if (in0) tk->U[__popcll(m0 & below)] = lane;
-    if (in1) tk->U[c0 + __popcll(m1 & below)] = lane + 64;
-    // pairs of each expert, in ascending pair order
-    int mytok = 0;
-    if (lane < np) {
-      const int e = tk->sel[lane / K][lane % K];
-      const uint64_t bm = e < 64 ? m0 : m1;
-      const int eb = e & 63;
-      const uint64_t lower = eb == 0 ? 0ull : (~0ull >> (64 - eb));
-      const int u = (e < 64 ? 0 : c0) + __popcll(bm & lower);
-      int t = 0, tot = 0;
-      for (int p = 0; p < np; ++p) {
-        const int ep = tk->sel[p / K][p % K];
-        if (ep == e) {
-          t += p < lane;
-          tot++;
-        }
+    // distinct experts in ascending order (lane e and e + 64), each with its
+    // tokens in ascending order as pairs b * top_k + slot
+    const int m_lo = emask[lane], m_hi = emask[lane + 64];
+    const uint64_t b0 = __ballot(m_lo != 0), b1 = __ballot(m_hi != 0);
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    const int c0 = __popcll(b0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int m = h ? m_hi : m_lo, e = lane + 64 * h;
+      if (m) {
+        const int u = h ? c0 + __popcll(b1 & below) : __popcll(b0 & below);
+        tk->U[u] = e;
+        tk->ntok[u] = __popc(m);
+        int t = 0;
+#pragma unroll
+        for (int bb = 0; bb < kMaxBatch; ++bb)
+          if ((m >> bb) & 1) tk->pair[u][t++] = bb * K + eslot[bb * kMaxExperts + e];
       }
-      tk->pair[u][t] = lane;
-      if (t == 0) tk->ntok[u] = tot;
-      mytok = tot;
     }
+    int mytok = max(__popc(m_lo), __popc(m_hi));
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) mytok = max(mytok, __shfl_xor(mytok, m));
     if (lane == 0) {
-      tk->nU = c0 + __popcll(m1);
+      tk->nU = c0 + __popcll(b1);
       tk->maxtok = mytok;
     }
   }
@@ -1234,7 +1228,7 @@ struct JobGateUp {
 // the PRE task that ran just before on this compute unit.
 TASK void task_gateup(const KArgs& a, const Task& t, const Lds& s, int qi, bool have_xs) {
   const int l = t.layer;
-  compute_topk(a, l, s.tk, s.rbuf);
+  compute_topk(a, l, s.tk, s.rbuf, s.C);
   if (t.idx == 0) write_sel(a, l, s.tk);
   mark(a, qi, 0);
   uint16_t* xs = (uint16_t*)s.A;
@@ -1316,8 +1310,14 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf,
   float* contrib = ao + (size_t)a.out_rows_max * a.max_batch;  // [out_rows_max][maxB*topk]
   const int maxBK = a.max_batch * a.topk;
   uint16_t* xs = (uint16_t*)s.A;
+  // the residual rows this task updates are final already: their loads go out first
+  float x_first = 0.f;
+  if (tid() < nr * n) {
+    const int rr = tid() / n, b = tid() % n;
+    x_first = load_x(a, l, b, t.r0 + rr, l == 0 ? token_row(a, b, qi) : nullptr);
+  }
   // expert down projections: their inputs (gate/up) are ready when the task starts
-  if (!have_tk) compute_topk(a, l, s.tk, s.rbuf);
+  if (!have_tk) compute_topk(a, l, s.tk, s.rbuf, s.C);
   copy_coh_to_lds(xs, a.h + (size_t)l * a.max_batch * a.topk * a.I, n * a.topk * a.I * 2);
   prefetch_wait();
   const TopK* tk = s.tk;
@@ -1356,8 +1356,7 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf,
     const int rr = e / n, b = e % n;
     float moe = 0.f;
     for (int j = 0; j < a.topk; ++j) moe += tk->w[b][j] * contrib[(size_t)rr * maxBK + b * a.topk + j];
-    const gu16* emb = l == 0 ? token_row(a, b, qi) : nullptr;
-    const float xo = load_x(a, l, b, t.r0 + rr, emb);
+    const float xo = e == tid() ? x_first : load_x(a, l, b, t.r0 + rr, l == 0 ? token_row(a, b, qi) : nullptr);
     st_coh(a.x + ((size_t)(l + 1) * a.max_batch + b) * a.H + t.r0 + rr, (xo + ao[(size_t)rr * a.max_batch + b]) + moe);
   }
 }

@@ -17,13 +17,14 @@ constexpr int kThreads = 512;      // 8 wave64 per workgroup, one workgroup per 
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxBatch = 8;
 constexpr int kMaxTopK = 8;
-constexpr int kMaxExperts = 128;
+constexpr int kMaxExperts = 128;   // the top-k's expert pass covers lanes e and e + 64 of one wave
 constexpr int kMaxGroup = 8;       // q heads per kv head
 constexpr int kTaskInts = 32;      // 128-byte descriptor
 constexpr int kGuPass = 256;       // gate/up virtual rows per pass of one task
 constexpr int kLmPass = 512;       // LM head rows per pass of one task
 constexpr int kTraceWords = 8;     // per task: fetch, ready, 4 phase marks, done, spare
 constexpr int kLdsB = 8192;        // LDS region B: top-k state, flags, reductions, router logits
+constexpr int kTopKScratch = 4 * kMaxExperts + kMaxBatch * kMaxExperts;  // region C bytes the top-k borrows
 
 enum Op : int32_t {
   OP_PRE = 1,     // RMSNorm + rows of [Wq; Wk; Wv] or of the router
