@@ -368,6 +368,8 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
         Task t = make_task(OP_OUT, l);
         t.wait[0] = ctr_index(l, C_GATEUP);
         t.fanin[0] = n_gu;
+        t.wait[1] = ctr_index(l, C_ROUTER);  // for the top-k, where no gate/up task left it in LDS
+        t.fanin[1] = n_router_tasks[l];
         t.late_wait = ctr_index(l, C_ATTN);
         t.late_fanin = n_attn;
         t.r0 = r0;

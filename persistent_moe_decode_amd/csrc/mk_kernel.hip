@@ -1302,6 +1302,15 @@ struct JobDown {
   DEV void emit(int i, int t, float v) const { contrib[(size_t)(i / nU) * maxBK + tk->pair[i % nU][t]] = v; }
 };
 
+// Down-projection rows held in registers across the gate/up wait: 16 lanes
+// per row, up to kDownC 16-byte chunks per lane (rows up to 128 * kDownC
+// elements), kDownGroups groups of 4 rows per wave.
+constexpr int kDownC = 8;
+constexpr int kDownGroups = 2;
+
+// Output tasks wait for their inputs themselves: the residual rows, the
+// top-k (from LDS, or computed once the router rows are done) and the first
+// down-projection rows are loaded before the gate/up results are waited for.
 // have_tk: region B still holds this layer's top-k, left there by the gate/up
 // task that ran just before on this compute unit.
 TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf, bool have_tk) {
@@ -1316,12 +1325,11 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf,
     const int rr = tid() / n, b = tid() % n;
     x_first = load_x(a, l, b, t.r0 + rr, l == 0 ? token_row(a, b, qi) : nullptr);
   }
-  // expert down projections: their inputs (gate/up) are ready when the task starts
-  if (!have_tk) compute_topk(a, l, s.tk, s.rbuf, s.C);
-  copy_coh_to_lds(xs, a.h + (size_t)l * a.max_batch * a.topk * a.I, n * a.topk * a.I * 2);
-  prefetch_wait();
+  if (!have_tk) {
+    if (!wait_counter(a, t.wait[1], t.fanin[1], qi, s.flags + 1)) return;
+    compute_topk(a, l, s.tk, s.rbuf, s.C);
+  }
   const TopK* tk = s.tk;
-  mark(a, qi, 0);
   JobDown jd;
   jd.tk = tk;
   jd.W = wptr(a, widx(l, WL_DOWN));
@@ -1332,7 +1340,44 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf,
   jd.I = a.I;
   jd.nU = tk->nU;
   jd.maxBK = maxBK;
-  run_rowdots(a.I, nr * tk->nU, tk->maxtok, jd);
+  const int nd = nr * jd.nU, cpl = a.I / 128;
+  const int npre = (a.I % 128 == 0 && cpl <= kDownC) ? min(nd, kDownGroups * kWaves * 4) : 0;
+  const int lane = tid() & 63, wave = tid() >> 6, li = lane & 15;
+  const int ig = wave * 4 + (lane >> 4);  // row within a group
+  uint4 dp[kDownGroups][kDownC];
+#pragma unroll
+  for (int g = 0; g < kDownGroups; ++g) {
+    const int i = g * kWaves * 4 + ig;
+    const bool act = i < npre;
+    const gu4* wr = jd.row(act ? i : 0) + li;
+#pragma unroll
+    for (int c = 0; c < kDownC; ++c)
+      dp[g][c] = __builtin_bit_cast(uint4, act && c < cpl ? wr[16 * c] : u32x4_v{0, 0, 0, 0});
+  }
+  if (!wait_counter(a, t.wait[0], t.fanin[0], qi, s.flags + 0)) return;
+  if (a.trace && tid() == 0 && qi < a.trace_cap) a.trace[kTraceWords * (size_t)qi + 1] = wall_clock64();
+  copy_coh_to_lds(xs, a.h + (size_t)l * a.max_batch * a.topk * a.I, n * a.topk * a.I * 2);
+  prefetch_wait();
+  mark(a, qi, 0);
+  // expert down projections: the register rows, then the rest from HBM
+  const int mt = tk->maxtok;
+#pragma unroll
+  for (int g = 0; g < kDownGroups; ++g) {
+    const int i = g * kWaves * 4 + ig;
+    const bool act = i < npre;
+    const int nx = act ? jd.nx(i) : 0;
+    for (int tt = 0; tt < mt; ++tt) {
+      const bool on = tt < nx;
+      const uint4* xr = jd.x(act ? i : 0, on ? tt : 0) + li;
+      float acc = 0.f;
+#pragma unroll
+      for (int c = 0; c < kDownC; ++c)
+        if (c < cpl) acc = dot8(dp[g][c], xr[16 * c], acc);
+      acc = group_sum<16>(acc);
+      if (on && li == 0) jd.emit(i, tt, acc);
+    }
+  }
+  rowdots_range<false>(a.I, npre, nd, mt, jd);
   mark(a, qi, 1);
   // attention output projection: wait for attention, Wo rows are already in LDS
   wait_counter(a, t.late_wait, t.late_fanin, qi, s.flags + 13);  // its barrier also frees xs
@@ -1482,7 +1527,8 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a)
     if (a.trace && tid() == 0) t_fetch = wall_clock64();
     // immutable weights start streaming into LDS before the inputs are ready
     const int npf = task_prefetch(a, t, s, q);
-    const bool own_wait = t.op == OP_ATTN;  // attention waits inside, once its loads are in flight
+    // attention and output tasks wait inside, once their loads are in flight
+    const bool own_wait = t.op == OP_ATTN || t.op == OP_OUT;
     bool ok = own_wait || wait_counter(a, t.wait[0], t.fanin[0], q, s.flags + 0);
     if (ok && !own_wait && t.wait[1] >= 0) ok = wait_counter(a, t.wait[1], t.fanin[1], q, s.flags + 1);
     if (a.trace && tid() == 0) t_ready = wall_clock64();
