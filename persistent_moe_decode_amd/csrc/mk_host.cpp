@@ -347,6 +347,8 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
         Task t = make_task(OP_ATTN, l);
         t.wait[0] = ctr_index(l, C_QKV);
         t.fanin[0] = n_qkv_tasks[l];
+        t.wait[1] = ctr_index(l, C_ROUTER);  // the top-k for this unit's output task
+        t.fanin[1] = n_router_tasks[l];
         t.idx = q;
         t.count = n_attn;
         t.signal = ctr_index(l, C_ATTN);

@@ -861,11 +861,11 @@ DEV AttnMerge attn_merge_area(const Lds& s, int G, int d) {
   return r;
 }
 
-// This wave's pages of the chunk, the blocks congruent to the wave mod 8:
-// early blocks [0, ne) already in registers (e0 = block wave, e1 = block
-// wave + 8), then LDS blocks [bl0, nblk), then HBM blocks [ne, bl0) with the
-// next page loaded while the current one is processed.  Leaves (o, m, sum)
-// per head in the merge area.
+// This wave's pages of the chunk: its early blocks, already in registers
+// (waves 1..7: e0 = block wave - 1, e1 = block wave + 6, of [0, ne)), then
+// the LDS blocks [bl0, nblk) and HBM blocks [ne, bl0) congruent to the wave
+// mod 8, the HBM ones with the next page loaded while the current one is
+// processed.  Leaves (o, m, sum) per head in the merge area.
 template <int D>
 DEV void attn_wave(const KArgs& a, const Lds& s, int qi, const uint16_t* q_s, int l, int b, int g, int t0, int t1,
                    int ne, int bl0, int nl, const AttnPage<D>& e0, const AttnPage<D>& e1, const AttnMerge& mrg) {
@@ -883,8 +883,8 @@ DEV void attn_wave(const KArgs& a, const Lds& s, int qi, const uint16_t* q_s, in
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) o[t] = float4_v{0.f, 0.f, 0.f, 0.f};
   const int nblk = (t1 - t0 + 15) / 16;
-  if (wave < ne) attn_page<D>(e0, qb, scale, m, lsum, o);
-  if (wave + kWaves < ne) attn_page<D>(e1, qb, scale, m, lsum, o);
+  if (wave >= 1 && wave - 1 < ne) attn_page<D>(e0, qb, scale, m, lsum, o);
+  if (wave >= 1 && wave + kWaves - 2 < ne) attn_page<D>(e1, qb, scale, m, lsum, o);
   for (int blk = bl0 + (wave - bl0 % kWaves + kWaves) % kWaves; blk < nblk; blk += kWaves) {
     AttnPage<D> cur;
     attn_fetch_lds<D>(s, cur, nl, blk - bl0, t0 + 16 * blk, t1);
@@ -1049,8 +1049,9 @@ DEV void attn_combine(const KArgs& a, const Lds& s, const float* parts, int nch,
 // chunk (once per launch), starts the LDS copies of the chunk's last blocks
 // and loads its first blocks into registers, so little of the chunk's K/V
 // traffic is left once q is ready.
+// Returns true when it left this layer's top-k in region B.
 template <int D>
-DEV void attn_task(const KArgs& a, const Task& t, const Lds& s, int qi) {
+DEV bool attn_task(const KArgs& a, const Task& t, const Lds& s, int qi) {
   // flags[16] (the split task whose plan flags[2..9] holds) was last written
   // before an earlier barrier, so every thread takes the same branch
   if (s.flags[16] != t.idx) {
@@ -1059,23 +1060,30 @@ DEV void attn_task(const KArgs& a, const Task& t, const Lds& s, int qi) {
     if (tid() == 0) s.flags[16] = t.idx;
   }
   const int32_t* plan = s.flags + 2;
-  if (!plan[6]) {  // idle split task: nothing to wait for
+  if (!plan[6]) {  // idle split task: only the top-k for this unit's output task
+    if (!wait_counter(a, t.wait[1], t.fanin[1], qi, s.flags + 1)) return false;
+    compute_topk(a, t.layer, s.tk, s.rbuf, s.C);
     if (a.trace && tid() == 0 && qi < a.trace_cap) a.trace[kTraceWords * (size_t)qi + 1] = wall_clock64();
-    return;
+    return true;
   }
   const int l = t.layer, G = a.group, ps = a.ps;
   const int b = plan[0], g = plan[1], t0 = plan[2], t1 = plan[3], first = plan[4], nch = plan[5], p = plan[7];
   const int nblk = (t1 - t0 + 15) / 16;
   const int nl = attn_lds_pages<D>(a, nblk);
   const int bl0 = nblk - nl;
-  // early blocks never include the last one (it receives the new token)
-  const int ne = max(0, min(bl0 - (nl == 0 ? 1 : 0), 2 * kWaves));
+  // early blocks never include the last one (it receives the new token); wave
+  // 0, whose thread 0 polls the flags, loads none
+  const int ne = max(0, min(bl0 - (nl == 0 ? 1 : 0), 2 * (kWaves - 1)));
   attn_prefetch<D>(a, s, qi, l, b, g, t0, bl0, nl);
   const int wave = tid() >> 6;
   AttnPage<D> e0, e1;
-  if (wave < ne) attn_fetch<D>(a, e0, l, b, g, t0 + 16 * wave, t1, qi);
-  if (wave + kWaves < ne) attn_fetch<D>(a, e1, l, b, g, t0 + 16 * (wave + kWaves), t1, qi);
-  if (!wait_counter(a, t.wait[0], t.fanin[0], qi, s.flags + 0)) return;
+  if (wave >= 1 && wave - 1 < ne) attn_fetch<D>(a, e0, l, b, g, t0 + 16 * (wave - 1), t1, qi);
+  if (wave >= 1 && wave + kWaves - 2 < ne) attn_fetch<D>(a, e1, l, b, g, t0 + 16 * (wave + kWaves - 2), t1, qi);
+  // the router rows are done before the QKV rows as a rule: the top-k for
+  // this unit's output task is taken while q is still on its way
+  if (!wait_counter(a, t.wait[1], t.fanin[1], qi, s.flags + 1)) return false;
+  compute_topk(a, l, s.tk, s.rbuf, s.C);
+  if (!wait_counter(a, t.wait[0], t.fanin[0], qi, s.flags + 0)) return true;
   if (a.trace && tid() == 0 && qi < a.trace_cap) a.trace[kTraceWords * (size_t)qi + 1] = wall_clock64();
 
   constexpr int half = D / 2;
@@ -1182,11 +1190,11 @@ DEV void attn_task(const KArgs& a, const Task& t, const Lds& s, int qi) {
     uint16_t* out = a.attn_out + ((size_t)l * a.max_batch + b) * a.nq * D + (size_t)g * G * D;
     attn_combine(a, s, parts, nch, out);
   }
+  return true;
 }
 
-TASK void task_attn(const KArgs& a, const Task& t, const Lds& s, int qi) {
-  if (a.d == 128) attn_task<128>(a, t, s, qi);
-  else attn_task<64>(a, t, s, qi);
+TASK bool task_attn(const KArgs& a, const Task& t, const Lds& s, int qi) {
+  return a.d == 128 ? attn_task<128>(a, t, s, qi) : attn_task<64>(a, t, s, qi);
 }
 
 // ---------------------------------------------------------------------------
@@ -1341,13 +1349,15 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf,
   jd.nU = tk->nU;
   jd.maxBK = maxBK;
   const int nd = nr * jd.nU, cpl = a.I / 128;
-  const int npre = (a.I % 128 == 0 && cpl <= kDownC) ? min(nd, kDownGroups * kWaves * 4) : 0;
+  // waves 1..7 hold them (wave 0, whose thread 0 polls the flags, loads none)
+  constexpr int kGroupRows = (kWaves - 1) * 4;
+  const int npre = (a.I % 128 == 0 && cpl <= kDownC) ? min(nd, kDownGroups * kGroupRows) : 0;
   const int lane = tid() & 63, wave = tid() >> 6, li = lane & 15;
-  const int ig = wave * 4 + (lane >> 4);  // row within a group
+  const int ig = wave >= 1 ? (wave - 1) * 4 + (lane >> 4) : kDownGroups * kGroupRows;  // row within a group
   uint4 dp[kDownGroups][kDownC];
 #pragma unroll
   for (int g = 0; g < kDownGroups; ++g) {
-    const int i = g * kWaves * 4 + ig;
+    const int i = g * kGroupRows + ig;
     const bool act = i < npre;
     const gu4* wr = jd.row(act ? i : 0) + li;
 #pragma unroll
@@ -1363,7 +1373,7 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf,
   const int mt = tk->maxtok;
 #pragma unroll
   for (int g = 0; g < kDownGroups; ++g) {
-    const int i = g * kWaves * 4 + ig;
+    const int i = g * kGroupRows + ig;
     const bool act = i < npre;
     const int nx = act ? jd.nx(i) : 0;
     for (int tt = 0; tt < mt; ++tt) {
@@ -1532,10 +1542,11 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a)
     bool ok = own_wait || wait_counter(a, t.wait[0], t.fanin[0], q, s.flags + 0);
     if (ok && !own_wait && t.wait[1] >= 0) ok = wait_counter(a, t.wait[1], t.fanin[1], q, s.flags + 1);
     if (a.trace && tid() == 0) t_ready = wall_clock64();
+    bool got_tk = false;
     if (ok) {
       switch (t.op) {
         case OP_PRE: task_pre(a, t, s, q, npf); break;
-        case OP_ATTN: task_attn(a, t, s, q); break;
+        case OP_ATTN: got_tk = task_attn(a, t, s, q); break;
         case OP_GATEUP: task_gateup(a, t, s, q, xs_layer == t.layer); break;
         case OP_OUT: task_out(a, t, s, q, npf, tk_layer == t.layer); break;
         case OP_LMHEAD: task_lmhead(a, t, s, q); break;
@@ -1543,7 +1554,7 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a)
       }
     }
     xs_layer = ok && t.op == OP_PRE ? t.layer : (ok && t.op == OP_GATEUP ? xs_layer : -1);
-    tk_layer = ok && (t.op == OP_GATEUP || t.op == OP_OUT) ? t.layer : (t.op == OP_LMHEAD ? -1 : tk_layer);
+    tk_layer = ok && (t.op == OP_GATEUP || t.op == OP_OUT || got_tk) ? t.layer : (t.op == OP_LMHEAD ? -1 : tk_layer);
     signal_counter(a, t.signal, t.slot);
     if (a.trace && tid() == 0 && q < a.trace_cap) {
       uint64_t* r = a.trace + kTraceWords * (size_t)q;
