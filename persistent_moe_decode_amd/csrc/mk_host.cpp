@@ -285,7 +285,9 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
   // routing is ready as early as the QKV rows.
   const int R1 = qkv_rows + E;
   const int m1 = ncu - n_attn;
-  const int n_rcu = std::min(m1 - 1, std::max(1, (int)(((int64_t)m1 * E + R1 - 1) / R1)));
+  int n_rcu = (int)(((int64_t)m1 * E + R1 - 1) / R1);
+  if (const char* renv = std::getenv("MK_ROUTER_CUS")) n_rcu = std::atoi(renv);
+  n_rcu = std::min(m1 - 1, std::max(1, n_rcu));
   const int n_qcu = m1 - n_rcu;
   auto pre_rows = [&](int q, int* r0, int* r1) {
     *r0 = *r1 = 0;

@@ -226,6 +226,22 @@ DEV bool wait_counter(const KArgs& a, int idx, int fanin, int task, int32_t* slo
   return *slot != 0;
 }
 
+// One look at a counter (no waiting): true in every thread when all fanin
+// flag words already hold this step's epoch.
+DEV bool counter_done(const KArgs& a, int idx, int fanin, int32_t* slot) {
+  if (tid() < 64) {
+    bool done = true;
+    if (idx >= 0) {
+      const uint32_t* f = a.flags + (size_t)idx * a.n_slots;
+      for (int j = tid(); j < fanin; j += 64) done &= (int32_t)(ld_coh(f + j) - a.epoch) >= 0;
+    }
+    const bool all = __all(done);
+    if (tid() == 0) *slot = all ? 1 : 0;
+  }
+  __syncthreads();
+  return *slot != 0;
+}
+
 // Every wave waits for its own stores to complete, the barrier orders them
 // before thread 0's flag store.
 DEV void signal_counter(const KArgs& a, int idx, int slot) {
@@ -1314,7 +1330,7 @@ struct JobDown {
 // per row, up to kDownC 16-byte chunks per lane (rows up to 128 * kDownC
 // elements), kDownGroups groups of 4 rows per wave.
 constexpr int kDownC = 8;
-constexpr int kDownGroups = 2;
+constexpr int kDownGroups = 3;
 
 // Output tasks wait for their inputs themselves: the residual rows, the
 // top-k (from LDS, or computed once the router rows are done) and the first
@@ -1367,6 +1383,13 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf,
   if (!wait_counter(a, t.wait[0], t.fanin[0], qi, s.flags + 0)) return;
   if (a.trace && tid() == 0 && qi < a.trace_cap) a.trace[kTraceWords * (size_t)qi + 1] = wall_clock64();
   copy_coh_to_lds(xs, a.h + (size_t)l * a.max_batch * a.topk * a.I, n * a.topk * a.I * 2);
+  // attention has mostly finished by now: when one look at its flags says so,
+  // its output comes in with h, into the part of region C the task leaves free
+  const size_t c_used = ((size_t)a.out_rows_max * a.max_batch * (1 + a.topk) * 4 + 15) & ~(size_t)15;
+  uint16_t* ao_early = (uint16_t*)(s.C + c_used);
+  bool early = c_used + (size_t)n * AD * 2 <= (size_t)(a.lds_p - a.lds_c) &&
+               counter_done(a, t.late_wait, t.late_fanin, s.flags + 13);
+  if (early) copy_coh_to_lds(ao_early, a.attn_out + (size_t)l * a.max_batch * AD, n * AD * 2);
   prefetch_wait();
   mark(a, qi, 0);
   // expert down projections: the register rows, then the rest from HBM
@@ -1389,11 +1412,13 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf,
   }
   rowdots_range<false>(a.I, npre, nd, mt, jd);
   mark(a, qi, 1);
-  // attention output projection: wait for attention, Wo rows are already in LDS
-  wait_counter(a, t.late_wait, t.late_fanin, qi, s.flags + 13);  // its barrier also frees xs
+  // attention output projection (Wo rows are already in LDS)
+  if (!early) {
+    wait_counter(a, t.late_wait, t.late_fanin, qi, s.flags + 13);  // its barrier also frees xs
+    copy_coh_to_lds(xs, a.attn_out + (size_t)l * a.max_batch * AD, n * AD * 2);
+    prefetch_wait();
+  }
   mark(a, qi, 2);
-  copy_coh_to_lds(xs, a.attn_out + (size_t)l * a.max_batch * AD, n * AD * 2);
-  prefetch_wait();
   JobO jo;
   jo.pf = (const AS_LDS uint16_t*)s.P;
   jo.npf = npf;
@@ -1401,7 +1426,7 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf,
   jo.r0 = t.r0;
   jo.K = AD;
   jo.maxB = a.max_batch;
-  jo.xs = xs;
+  jo.xs = early ? ao_early : xs;
   jo.ao = ao;
   run_rowdots_pf(AD, nr, npf, n, jo);
   __syncthreads();

@@ -12,7 +12,8 @@ import os
 import re
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmk.so")
+# MK_LIBRARY names another build of the same library (for side-by-side timing of build variants)
+LIB_PATH = os.environ.get("MK_LIBRARY") or os.path.join(_HERE, "libmk.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "mk.h")
 
 MK_OK = 0
