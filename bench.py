@@ -55,6 +55,51 @@ def measured_traffic(workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def write_traffic(fetch_csv: str, write_csv: str, workload: str, copy_bytes: int) -> dict:
+    """profiles/traffic_<workload>.json from two rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE, csv).
+
+    Each run ends with one plain copy of copy_bytes (read copy_bytes, write
+    copy_bytes): the largest __amd_rocclr_copyBuffer dispatch of a run scales
+    that counter's KiB to bytes; mk_megakernel dispatches give the per-launch values.
+    """
+    import csv
+
+    import numpy as np
+
+    def read(path, counter):
+        kern, copies = [], []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                v = float(r["Counter_Value"])
+                if r["Kernel_Name"].startswith("mk_megakernel"):
+                    kern.append(v)
+                elif r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer"):
+                    copies.append(v)
+        if not kern or not copies:
+            raise SystemExit(f"{path}: no {counter} values for mk_megakernel and the calibration copy")
+        return kern, max(copies)
+
+    fk, fcal = read(fetch_csv, "FETCH_SIZE")
+    wk, wcal = read(write_csv, "WRITE_SIZE")
+    fscale = copy_bytes / (fcal * 1024.0)
+    wscale = copy_bytes / (wcal * 1024.0)
+    fb = float(np.median(fk)) * 1024.0 * fscale
+    wb = float(np.median(wk)) * 1024.0 * wscale
+    rec = {
+        "workload": workload, "kernel": "mk_megakernel", "kernel_source_sha256_16": kernel_source_hash(),
+        "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk, "calib_copy_bytes": copy_bytes,
+        "calib_fetch_kib": fcal, "calib_write_kib": wcal,
+        "fetch_scale": round(fscale, 5), "write_scale": round(wscale, 5),
+        "hbm_fetch_bytes_per_launch": round(fb), "hbm_write_bytes_per_launch": round(wb),
+        "hbm_bytes_per_launch": round(fb + wb),
+    }
+    with open(os.path.join(ROOT, "profiles", f"traffic_{workload}.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
+
+
 def step_bytes_kernel(shape, seq_lens, distinct):
     """Algorithmic HBM bytes one decode step reads: active weights (one embedding row per token) + KV 0..p."""
     H = shape.hidden
@@ -108,7 +153,14 @@ def main():
     ap.add_argument("--trace", default="", help="write a Perfetto timeline of one extra step to this path")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="after the run, one plain device-to-device copy of this many bytes (counter calibration)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.json from two rocprofv3 counter runs made with "
+                         "--copy-calib 1073741824, then exit (no GPU needed)")
     args = ap.parse_args()
+    if args.write_traffic:
+        rec = write_traffic(*args.write_traffic, args.workload, 1 << 30)
+        print(json.dumps({k: rec[k] for k in ("fetch_scale", "write_scale", "hbm_bytes_per_launch")}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one MI355X: the decode megakernel runs on a single GPU and has no "
               "multi-GPU path (use --gpus 1)", file=sys.stderr)

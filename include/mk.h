@@ -112,6 +112,9 @@ int mk_bind(mk_ctx* ctx, const void* const* weights, int32_t n_weights, void* k_
  *    position seq_lens[b].  Its K/V are written to slot seq_lens[b] % page_size
  *    of page page_table[b][seq_lens[b] / page_size]; attention covers
  *    positions 0..seq_lens[b].  seq_lens is not modified: the caller advances it.
+ *    The page that receives a sequence's new token must not appear in another
+ *    sequence's row of the page table in the same step (pages are read before
+ *    the new entries are written; shared prefix pages are fine).
  *  d_logits: device float[n][vocab], written.
  *  d_next_tokens: device int32[n] receiving the greedy argmax (lowest id on
  *    ties), or NULL.
