@@ -152,12 +152,17 @@ class Weights:
 
 
 class PagedKV:
-    """Paged K/V pools: per layer ``[num_pages][n_kv][page_size][d]`` bfloat16 bits."""
+    """Paged K/V pools: per layer ``[num_pages][n_kv][page_size][d]`` bfloat16 bits.
 
-    def __init__(self, shape: synth.ModelShape, num_pages: int):
+    layers: the layers held (default all); the others cannot be written or read.
+    """
+
+    def __init__(self, shape: synth.ModelShape, num_pages: int, layers=None):
         s = shape
         self.shape = s
-        dims = (s.n_layers, num_pages, s.n_kv_heads, s.page_size, s.head_dim)
+        self.layers = list(range(s.n_layers)) if layers is None else sorted(set(int(l) for l in layers))
+        self._at = {l: i for i, l in enumerate(self.layers)}
+        dims = (len(self.layers), num_pages, s.n_kv_heads, s.page_size, s.head_dim)
         self.k = np.full(dims, 0x7FC0, dtype=np.uint16)   # NaN: unwritten slots poison any stray read
         self.v = np.full(dims, 0x7FC0, dtype=np.uint16)
 
@@ -172,27 +177,29 @@ class PagedKV:
 
     def write(self, layer: int, page_table_row: np.ndarray, pos: int, k_bits: np.ndarray, v_bits: np.ndarray):
         page, o = self.slots(page_table_row, [pos])
-        self.k[layer, page[0], :, o[0], :] = k_bits
-        self.v[layer, page[0], :, o[0], :] = v_bits
+        i = self._at[layer]
+        self.k[i, page[0], :, o[0], :] = k_bits
+        self.v[i, page[0], :, o[0], :] = v_bits
 
     def gather(self, layer: int, page_table_row: np.ndarray, n: int, g: int):
         """K, V rows (float64 [n][d]) of kv head ``g`` for logical positions 0..n-1."""
         page, o = self.slots(page_table_row, np.arange(n))
-        return bf16_to_f64(self.k[layer, page, g, o]), bf16_to_f64(self.v[layer, page, g, o])
+        i = self._at[layer]
+        return bf16_to_f64(self.k[i, page, g, o]), bf16_to_f64(self.v[i, page, g, o])
 
     def fill_synthetic(self, page_table: np.ndarray, context: list):
         """Fill positions 0..context[b]-1 of every sequence from the synth KV recipe."""
         s = self.shape
         ps = s.page_size
         for b, n in enumerate(context):
-            for layer in range(s.n_layers):
+            for i, layer in enumerate(self.layers):
                 K = synth.kv_bits(s, layer, "k", b, 0, n)
                 V = synth.kv_bits(s, layer, "v", b, 0, n)
                 for t0 in range(0, n, ps):
                     t1 = min(n, t0 + ps)
                     page = int(page_table[b, t0 // ps])
-                    self.k[layer, page, :, : t1 - t0, :] = K[t0:t1].transpose(1, 0, 2)
-                    self.v[layer, page, :, : t1 - t0, :] = V[t0:t1].transpose(1, 0, 2)
+                    self.k[i, page, :, : t1 - t0, :] = K[t0:t1].transpose(1, 0, 2)
+                    self.v[i, page, :, : t1 - t0, :] = V[t0:t1].transpose(1, 0, 2)
 
 
 # ----------------------------------------------------------------------------
@@ -214,6 +221,81 @@ class StepOut:
 ROUTE_TIE = 1e-3   # router margin below which either expert set is a correct result
 
 
+@dataclass
+class LayerOut:
+    x: np.ndarray          # [H] float64: the residual leaving the layer
+    r: np.ndarray          # [E] float32 values: router logits
+    sel: np.ndarray        # [k] experts in slot order
+    sel_alt: np.ndarray    # [k] the set with the k-th and (k+1)-th exchanged (or None when k == E)
+    margin: float          # r_(k) - r_(k+1)
+    parts: dict            # intermediates: xn, q16, k16, v16, a16, attn, moe, h16, w
+
+
+def layer_forward(W: Weights, kv: PagedKV, l: int, x: np.ndarray, p: int, pt: np.ndarray,
+                  take_alt: bool = False) -> LayerOut:
+    """One decoder layer for one sequence whose new token sits at position p.
+
+    Parallel block from one normalized input: attention (QKV, rotary, the new
+    K/V written at p, attention over 0..p, O projection) and the MoE path
+    (router, top-k, softmax over the selected logits, SwiGLU experts, weighted
+    sum), then x <- (x + attn) + moe.  take_alt: take the other correct
+    routing at a near-tie of the k-th and (k+1)-th router logits (checked).
+    """
+    s = W.shape
+    H, d, E, k = s.hidden, s.head_dim, s.n_experts, s.top_k
+    nq, nkv = s.n_q_heads, s.n_kv_heads
+    group = nq // nkv
+    xn = round_bf16(rmsnorm(x, W.get(synth.K_ATTN_NORM, l), s.rms_eps))
+    # attention path
+    qkv = W.get(synth.K_WQKV, l) @ xn
+    q = qkv[: nq * d].reshape(nq, d)
+    kk = qkv[nq * d: (nq + nkv) * d].reshape(nkv, d)
+    vv = qkv[(nq + nkv) * d:].reshape(nkv, d)
+    q16 = round_bf16(rope(q, p, s.rope_theta))
+    k16 = round_bf16(rope(kk, p, s.rope_theta))
+    v16 = round_bf16(vv)
+    kv.write(l, pt, p, f64_to_bf16_bits(k16), f64_to_bf16_bits(v16))
+    o = np.zeros((nq, d))
+    for g in range(nkv):
+        K, V = kv.gather(l, pt, p + 1, g)
+        for h in range(g * group, (g + 1) * group):
+            o[h] = attention_head(q16[h], K, V)
+    a16 = round_bf16(o.reshape(-1))
+    attn = W.get(synth.K_WO, l) @ a16
+    # MoE path, from the same normalized input
+    r = (W.get(synth.K_ROUTER, l) @ xn).astype(np.float32)
+    sel = topk_desc(r, k)
+    alt = None
+    if k < E:
+        ext = topk_desc(r, k + 1)
+        alt = np.concatenate([ext[: k - 1], ext[k:]])
+        if take_alt:
+            if not float(r[ext[k - 1]]) - float(r[ext[k]]) <= ROUTE_TIE:
+                raise ValueError(f"layer {l}: no routing near-tie to take the alternative of")
+            sel = alt
+    wsel = softmax(r[sel].astype(np.float64))
+    moe = np.zeros(H)
+    hs = []
+    for j in range(k):
+        e = int(sel[j])
+        gate = W.get(synth.K_W_GATE, l, e) @ xn
+        up = W.get(synth.K_W_UP, l, e) @ xn
+        h16 = round_bf16(silu(gate) * up)
+        hs.append(h16)
+        moe = moe + wsel[j] * (W.get(synth.K_W_DOWN, l, e) @ h16)
+    srt = np.sort(r.astype(np.float64))[::-1]
+    margin = srt[k - 1] - srt[k] if k < E else np.inf
+    parts = {"xn": xn, "q16": q16, "k16": k16, "v16": v16, "a16": a16, "attn": attn, "moe": moe,
+             "h16": np.stack(hs), "w": wsel}
+    return LayerOut((x + attn) + moe, r, sel, alt, margin, parts)
+
+
+def lm_logits(W: Weights, x: np.ndarray) -> np.ndarray:
+    """Final RMSNorm, then the LM head."""
+    xf = round_bf16(rmsnorm(x, W.get(synth.K_FINAL_NORM), W.shape.rms_eps))
+    return W.get(synth.K_LM_HEAD) @ xf
+
+
 def decode_step(W: Weights, kv: PagedKV, tokens, page_table, seq_lens, trace: bool = False,
                 route_alt=None) -> StepOut:
     """One decode step for a ragged batch.
@@ -230,9 +312,7 @@ def decode_step(W: Weights, kv: PagedKV, tokens, page_table, seq_lens, trace: bo
     """
     route_alt = route_alt or set()
     s = W.shape
-    L, H, d, E, k = s.n_layers, s.hidden, s.head_dim, s.n_experts, s.top_k
-    nq, nkv = s.n_q_heads, s.n_kv_heads
-    group = nq // nkv
+    L, E, k = s.n_layers, s.n_experts, s.top_k
     B = len(tokens)
     logits = np.zeros((B, s.vocab))
     rl = np.zeros((L, B, E), dtype=np.float32)
@@ -245,63 +325,18 @@ def decode_step(W: Weights, kv: PagedKV, tokens, page_table, seq_lens, trace: bo
         pt = np.asarray(page_table[b])
         x = W.get(synth.K_EMBED)[int(tokens[b])].copy()
         for l in range(L):
-            xn = round_bf16(rmsnorm(x, W.get(synth.K_ATTN_NORM, l), s.rms_eps))
-            # attention path
-            qkv = W.get(synth.K_WQKV, l) @ xn
-            q = qkv[: nq * d].reshape(nq, d)
-            kk = qkv[nq * d: (nq + nkv) * d].reshape(nkv, d)
-            vv = qkv[(nq + nkv) * d:].reshape(nkv, d)
-            q16 = round_bf16(rope(q, p, s.rope_theta))
-            k16 = round_bf16(rope(kk, p, s.rope_theta))
-            v16 = round_bf16(vv)
-            kv.write(l, pt, p, f64_to_bf16_bits(k16), f64_to_bf16_bits(v16))
-            o = np.zeros((nq, d))
-            for g in range(nkv):
-                K, V = kv.gather(l, pt, p + 1, g)
-                for h in range(g * group, (g + 1) * group):
-                    o[h] = attention_head(q16[h], K, V)
-            a16 = round_bf16(o.reshape(-1))
-            attn = W.get(synth.K_WO, l) @ a16
-            # MoE path, from the same normalized input
-            r = (W.get(synth.K_ROUTER, l) @ xn).astype(np.float32)
-            sel = topk_desc(r, k)
-            if k < E:
-                ext = topk_desc(r, k + 1)
-                alt = np.concatenate([ext[: k - 1], ext[k:]])
-                sel_alt[l, b] = alt
-                if (l, b) in route_alt:
-                    if not float(r[ext[k - 1]]) - float(r[ext[k]]) <= ROUTE_TIE:
-                        raise ValueError(f"layer {l} seq {b}: no routing near-tie to take the alternative of")
-                    sel = alt
-            wsel = softmax(r[sel].astype(np.float64))
-            moe = np.zeros(H)
-            hs = []
-            for j in range(k):
-                e = int(sel[j])
-                gate = W.get(synth.K_W_GATE, l, e) @ xn
-                up = W.get(synth.K_W_UP, l, e) @ xn
-                h16 = round_bf16(silu(gate) * up)
-                hs.append(h16)
-                moe = moe + wsel[j] * (W.get(synth.K_W_DOWN, l, e) @ h16)
-            x_in = x
-            x = (x + attn) + moe
-            rl[l, b] = r
-            sel_all[l, b] = sel
-            srt = np.sort(r.astype(np.float64))[::-1]
-            margin[l, b] = srt[k - 1] - srt[k] if k < E else np.inf
+            out = layer_forward(W, kv, l, x, p, pt, take_alt=(l, b) in route_alt)
+            rl[l, b] = out.r
+            sel_all[l, b] = out.sel
+            if out.sel_alt is not None:
+                sel_alt[l, b] = out.sel_alt
+            margin[l, b] = out.margin
             if trace:
-                tr.setdefault("x_in", {})[(l, b)] = x_in
-                tr.setdefault("xn", {})[(l, b)] = xn
-                tr.setdefault("q16", {})[(l, b)] = q16
-                tr.setdefault("k16", {})[(l, b)] = k16
-                tr.setdefault("v16", {})[(l, b)] = v16
-                tr.setdefault("a16", {})[(l, b)] = a16
-                tr.setdefault("attn", {})[(l, b)] = attn
-                tr.setdefault("moe", {})[(l, b)] = moe
-                tr.setdefault("h16", {})[(l, b)] = np.stack(hs)
-                tr.setdefault("w", {})[(l, b)] = wsel
-        xf = round_bf16(rmsnorm(x, W.get(synth.K_FINAL_NORM), s.rms_eps))
-        logits[b] = W.get(synth.K_LM_HEAD) @ xf
+                tr.setdefault("x_in", {})[(l, b)] = x
+                for name, v in out.parts.items():
+                    tr.setdefault(name, {})[(l, b)] = v
+            x = out.x
+        logits[b] = lm_logits(W, x)
         if trace:
             tr.setdefault("x_final", {})[b] = x
     nxt = np.argmax(logits, axis=1)

@@ -277,3 +277,92 @@ class Runner:
 
 def run(w: synth.Workload, steps: int | None = None, mode: str = "isolated", log=print) -> Report:
     return Runner(w, log=log).run(w.steps if steps is None else steps, mode)
+
+
+# ------------------------------------------------------------------ sampled layers at full size
+
+INPUT_SEED = 6       # seeded residuals injected into every layer (the shared input generator, its own seed)
+INPUT_SIGMA = 0.5
+
+
+def injected_inputs(shape: synth.ModelShape, max_batch: int, n: int) -> np.ndarray:
+    """[L+1][max_batch][H] float32: the residual fed to layer l >= 1 and to the final norm (index L)."""
+    L, H = shape.n_layers, shape.hidden
+    x = np.zeros((L + 1, max_batch, H), dtype=np.float32)
+    for l in range(1, L + 1):
+        for b in range(n):
+            bits = synth.normal_bf16(INPUT_SEED, synth.tid(l, b), 0, H, INPUT_SIGMA)
+            x[l, b] = O.bf16_to_f64(bits).astype(np.float32)
+    return x
+
+
+def run_sampled(w: synth.Workload, layers, log=print) -> Report:
+    """One step at full size with every layer fed a seeded residual; the oracle recomputes the
+    sampled layers from the same inputs (layer 0 from the embedding) and the LM head from the
+    final input, and each is compared in full: expert choice, router logits, output residual,
+    new K/V entries, logits and the greedy token."""
+    from persistent_moe_decode_amd.runtime import DeviceDecoder
+
+    t0 = time.time()
+    s = w.shape
+    L, k, n = s.n_layers, s.top_k, w.batch
+    dec = DeviceDecoder(w)
+    dec.fill_synthetic_kv()
+    mb = dec.ctx.cfg.max_batch
+    host = injected_inputs(s, mb, n)
+    x_inj = torch.from_numpy(host).to(dec.dev)
+    dec.ctx.set_layer_inputs(x_inj.data_ptr())
+    toks = [int(w.prompt(b)[w.context[b]]) for b in range(n)]
+    lens = list(w.context)
+    dec.step(toks, lens)
+    torch.cuda.synchronize()
+    dec.check_error()
+    log(f"[sampled {w.name}] GPU step done {time.time() - t0:.1f}s")
+    sel, rl, xs = dec.sel()[:, :n], dec.router_logits()[:, :n], dec.residual()[:, :n]
+    got = dec.logits[:n].cpu().numpy().astype(np.float64)
+    rep = Report(steps=1)
+    _self_consistent(rep, "sampled", sel, rl, n, k)
+    W = O.Weights(s, budget_bytes=float(2 ** 34))
+    pt = w.page_table()
+    kv = O.PagedKV(s, w.num_pages, layers=layers)
+    kv.fill_synthetic(pt, w.context)
+    log(f"[sampled {w.name}] oracle cache for layers {list(layers)} filled {time.time() - t0:.1f}s")
+    emb = W.get(synth.K_EMBED)
+    for b in range(n):
+        p = int(lens[b])
+        for l in layers:
+            tag = f"layer {l} seq {b}"
+            x_in = emb[toks[b]].copy() if l == 0 else host[l, b].astype(np.float64)
+            ref = O.layer_forward(W, kv, l, x_in, p, pt[b])
+            a, e = sorted(sel[l, b].tolist()), sorted(ref.sel.tolist())
+            if a != e:
+                if ref.margin <= MARGIN and ref.sel_alt is not None and a == sorted(ref.sel_alt.tolist()):
+                    rep.route_ties += 1
+                    ref = O.layer_forward(W, kv, l, x_in, p, pt[b], take_alt=True)
+                else:
+                    rep.failures.append(f"{tag}: experts {a} vs {e} (margin {ref.margin:.2e})")
+            rep.route_checked += 1
+            dr = float(np.max(np.abs(rl[l, b] - ref.r)))
+            rep.max_router = max(rep.max_router, dr)
+            if not dr <= ROUTER_TOL:
+                rep.failures.append(f"{tag}: router logits differ by {dr:.2e}")
+            rx = float(np.max(np.abs(xs[l + 1, b] - ref.x)) / np.max(np.abs(ref.x)))
+            rep.max_x = max(rep.max_x, rx)
+            if not rx <= X_TOL:
+                rep.failures.append(f"{tag}: output residual rel err {rx:.2e}")
+            kg, vg = dec.kv_at(l, b, p)
+            for name, g16, o64 in (("k", kg, ref.parts["k16"]), ("v", vg, ref.parts["v16"])):
+                gv = O.bf16_to_f64(g16)
+                ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(o64), 1e-30))[1] - 8)
+                scale = np.max(np.abs(o64), axis=-1, keepdims=True)
+                bad = np.abs(gv - o64) > ulp * 1.0000001 + KV_ABS * scale
+                rep.kv_checked += gv.size
+                if np.any(bad):
+                    rep.failures.append(f"{tag}: new {name} off by more than one ulp at {int(bad.sum())} entries")
+        lg = O.lm_logits(W, host[L, b].astype(np.float64))
+        srt = np.sort(lg)
+        ref_out = O.StepOut(lg[None, :], None, None, None, np.array([int(np.argmax(lg))]),
+                            np.array([srt[-1] - srt[-2]]))
+        _check_logits(rep, f"seq {b}", got[b], ref_out, 0)
+        log(f"[sampled {w.name}] seq {b} checked {time.time() - t0:.1f}s: {rep.summary()}")
+    return rep

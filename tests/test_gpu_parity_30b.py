@@ -20,3 +20,29 @@ def test_30b_bs1_8k_isolated_first_steps():
     rep = parity.run(synth.workload("moe30b_8k"), steps=2, mode="isolated", log=_log)
     _log(rep.summary())
     assert rep.ok(), "\n".join(rep.failures[:20])
+
+
+def _fresh():
+    import gc
+
+    import torch
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_30b_bs8_ragged_sampled_layers():
+    """Batch 8, contexts U[1024, 32768], full size: layers 0, 24, 47 and the LM head from seeded layer inputs."""
+    from tests import parity
+    _fresh()
+    rep = parity.run_sampled(synth.workload("moe30b_bs8_ragged"), layers=(0, 24, 47), log=_log)
+    _log(rep.summary())
+    assert rep.ok(), "\n".join(rep.failures[:20])
+
+
+def test_30b_256k_sampled_layers():
+    """Batch 1, 262144 cached tokens, full size: layers 0, 24, 47 and the LM head from seeded layer inputs."""
+    from tests import parity
+    _fresh()
+    rep = parity.run_sampled(synth.workload("moe30b_256k"), layers=(0, 24, 47), log=_log)
+    _log(rep.summary())
+    assert rep.ok(), "\n".join(rep.failures[:20])

@@ -382,3 +382,22 @@ def test_route_alternative_only_at_a_near_tie():
     assert list(out.sel_alt[1, 0]) == [0, 2] and out.margin[1, 0] == 0.0
     with pytest.raises(ValueError):
         O.decode_step(O.Weights(s), O.PagedKV(s, 1), [3], np.zeros((1, 1), dtype=np.int32), [0], route_alt={(0, 0)})
+
+
+def test_layer_subset_cache_gives_the_same_layer():
+    """A cache holding only some layers serves those layers exactly as the full cache does."""
+    w = synth.workload("tiny")
+    s = w.shape
+    W = O.Weights(s)
+    pt = w.page_table()
+    full = O.PagedKV(s, w.num_pages)
+    part = O.PagedKV(s, w.num_pages, layers=[1])
+    ctx = [40]
+    full.fill_synthetic(pt, ctx)
+    part.fill_synthetic(pt, ctx)
+    x = O.bf16_to_f64(synth.normal_bf16(9, synth.tid(1, 0), 0, s.hidden, 0.5))
+    a = O.layer_forward(W, full, 1, x, 40, pt[0])
+    b = O.layer_forward(W, part, 1, x, 40, pt[0])
+    assert np.array_equal(a.x, b.x) and np.array_equal(a.sel, b.sel) and np.array_equal(a.r, b.r)
+    with pytest.raises(KeyError):
+        part.gather(0, pt[0], 4, 0)
