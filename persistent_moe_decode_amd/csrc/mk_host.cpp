@@ -7,10 +7,10 @@
 // advance; aiweekly.co, paragraphs 2-3: fixed-size descriptors, a task waits
 // on one count) with its own layout: one queue per compute unit, per layer
 //   PRE (norm + Wqkv / router rows)  ->  ATTN or GATEUP  ->  OUT (Wo + down rows),
-// then LM head rows.  A counter is an array of flag words, one per task that
-// signals it (the task's slot); signalling stores the step's epoch into the
-// task's word and a wait ends when all words of the counter hold the epoch,
-// so nothing is reset between steps and no two tasks update one word.
+// then LM head rows.  A counter is a set of sub-counters in separate lines;
+// the task with slot s (its index among the counter's signallers) adds one to
+// sub-counter s mod 16, and a wait ends when they sum to epoch * fan-in, so
+// nothing is reset between steps.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -144,14 +144,14 @@ static int simulate_raw(const Task* tasks, int nt, const int32_t* qoff, int ncu,
       return fail(MK_ERR_INVALID_ARG, "counter index out of range");
     if (t.signal >= 0) signals[t.signal]++;
   }
-  // the signalling tasks of a counter own its flag words 0 .. signals - 1, one each
+  // the signalling tasks of a counter hold slots 0 .. signals - 1, one each (slots spread the adds over sub-counters)
   std::vector<std::vector<char>> owned(n_ctr);
   for (int c = 0; c < n_ctr; ++c) owned[c].assign((size_t)signals[c], 0);
   for (int i = 0; i < nt; ++i) {
     const Task& t = tasks[i];
     if (t.signal < 0) continue;
     if (t.slot < 0 || t.slot >= signals[t.signal] || owned[t.signal][t.slot])
-      return fail(MK_ERR_SCHEDULE, "schedule: task " + std::to_string(i) + " has a flag slot that is out of range or taken");
+      return fail(MK_ERR_SCHEDULE, "schedule: task " + std::to_string(i) + " has a signal slot that is out of range or taken");
     owned[t.signal][t.slot] = 1;
   }
   // every wait must name the full fan-in of its counter
@@ -215,7 +215,7 @@ static WsLayout layout_workspace(const mk_ctx* c) {
   const size_t group = f.n_q_heads / f.n_kv_heads;
   w.state = o;
   w.ctr = 0;
-  w.tickets = (size_t)c->n_ctr * c->n_slots;
+  w.tickets = (size_t)c->n_ctr * kCounterWords;
   w.err = w.tickets + c->n_tickets;
   w.n_state_u32 = w.err + E_WORDS;
   take(4 * w.n_state_u32);
@@ -397,7 +397,7 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
     }
   }
   c->qoff[ncu] = (int)c->tasks.size();
-  // flag slots: the k-th task (in table order) that signals a counter owns its word k
+  // signal slots: the k-th task (in table order) that signals a counter has slot k
   {
     std::vector<int> used(c->n_ctr, 0);
     for (Task& t : c->tasks)
@@ -630,7 +630,6 @@ extern "C" int mk_decode_step(mk_ctx* c, int32_t n, const int32_t* d_tokens, con
   a.queue_off = (const int32_t*)(w + c->ws.queue_off);
   uint32_t* st = (uint32_t*)(w + c->ws.state);
   a.flags = st + c->ws.ctr;
-  a.n_slots = c->n_slots;
   a.tickets = st + c->ws.tickets;
   a.err = (int32_t*)(st + c->ws.err);
   a.wtab = (const uint64_t*)(w + c->ws.wtab);

@@ -188,25 +188,29 @@ DEV bool aborting(const KArgs& a) {
   return __hip_atomic_load(&a.err[E_ABORT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
 }
 
-// Wave 0 polls the counter's flag words (slot j by lane j mod 64, relaxed
-// device-coherent loads, s_sleep between polls) until every one of the fanin
-// words holds this step's epoch; the barrier hands the result to the other
-// waves.  The wait is bounded: past the spin limit the task raises
-// MK_ERR_DEVICE_TIMEOUT and the grid drains.  Returns false when the grid is
-// aborting.
+// Sum of a counter's sub-counters, in every lane of the calling wave.
+DEV uint32_t counter_sum(const KArgs& a, int idx) {
+  const int lane = tid() & 63;
+  uint32_t v = lane < kSubCounters ? ld_coh(a.flags + (size_t)idx * kCounterWords + lane * kSubStride) : 0u;
+#pragma unroll
+  for (int m = kSubCounters / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return __shfl(v, 0);
+}
+
+// Wave 0 polls the counter (relaxed device-coherent loads of its
+// sub-counters, s_sleep between polls) until it reaches epoch * fanin; the
+// barrier hands the result to the other waves.  The wait is bounded: past
+// the spin limit the task raises MK_ERR_DEVICE_TIMEOUT and the grid drains.
+// Returns false when the grid is aborting.
 DEV bool wait_counter(const KArgs& a, int idx, int fanin, int task, int32_t* slot) {
   if (tid() < 64) {
     const int lane = tid();
     int ok = aborting(a) ? 0 : 1;
     if (ok && idx >= 0) {
-      const uint32_t* f = a.flags + (size_t)idx * a.n_slots;
-      const uint32_t want = a.epoch;
+      const uint32_t want = a.epoch * (uint32_t)fanin;
       const uint64_t t0 = wall_clock64();
       uint32_t it = 0;
-      while (true) {
-        bool done = true;
-        for (int j = lane; j < fanin; j += 64) done &= (int32_t)(ld_coh(f + j) - want) >= 0;
-        if (__all(done)) break;
+      while ((int32_t)(counter_sum(a, idx) - want) < 0) {
         __builtin_amdgcn_s_sleep(1);
         if ((++it & 31) == 0) {
           int stop = 0;
@@ -226,28 +230,25 @@ DEV bool wait_counter(const KArgs& a, int idx, int fanin, int task, int32_t* slo
   return *slot != 0;
 }
 
-// One look at a counter (no waiting): true in every thread when all fanin
-// flag words already hold this step's epoch.
+// One look at a counter (no waiting): true in every thread when it has
+// already reached epoch * fanin.
 DEV bool counter_done(const KArgs& a, int idx, int fanin, int32_t* slot) {
   if (tid() < 64) {
-    bool done = true;
-    if (idx >= 0) {
-      const uint32_t* f = a.flags + (size_t)idx * a.n_slots;
-      for (int j = tid(); j < fanin; j += 64) done &= (int32_t)(ld_coh(f + j) - a.epoch) >= 0;
-    }
-    const bool all = __all(done);
-    if (tid() == 0) *slot = all ? 1 : 0;
+    const bool done = idx < 0 || (int32_t)(counter_sum(a, idx) - a.epoch * (uint32_t)fanin) >= 0;
+    if (tid() == 0) *slot = done ? 1 : 0;
   }
   __syncthreads();
   return *slot != 0;
 }
 
 // Every wave waits for its own stores to complete, the barrier orders them
-// before thread 0's flag store.
+// before thread 0's add.
 DEV void signal_counter(const KArgs& a, int idx, int slot) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid() == 0 && idx >= 0) st_coh(a.flags + (size_t)idx * a.n_slots + slot, a.epoch);
+  if (tid() == 0 && idx >= 0)
+    __hip_atomic_fetch_add(a.flags + (size_t)idx * kCounterWords + (slot % kSubCounters) * kSubStride, 1u,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Ticket for "last of count arrivals does the merge": returns true in every

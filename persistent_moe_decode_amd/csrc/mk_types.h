@@ -40,22 +40,26 @@ struct Task {
   int32_t layer;
   int32_t wait[2];    // counter index or -1
   int32_t fanin[2];   // signals per step on that counter
-  int32_t signal;     // counter whose flag word `slot` is set when done, or -1
+  int32_t signal;     // counter this task adds one to when done, or -1
   int32_t r0, r1;     // row range (PRE, OUT, LMHEAD)
   int32_t idx, count; // index of this task among the op's tasks of the layer, and their number
   int32_t late_wait;  // counter waited inside the body, once its first part is done (-1 = none)
   int32_t late_fanin;
-  int32_t slot;       // this task's flag word on its signal counter: 0 .. (signals on that counter) - 1
+  int32_t slot;       // this task's index among the tasks signalling its counter: 0 .. (signals) - 1
   int32_t pad[18];
 };
 static_assert(sizeof(Task) == kTaskInts * 4, "task descriptor is 128 bytes");
 
-// Counters: per layer l, kCtrPerLayer of them.  A counter is an array of
-// flag words, one per task that signals it; a task signals by storing the
-// step's epoch into its own word, and a wait is over when every word of the
-// counter holds the epoch.
+// Counters: per layer l, kCtrPerLayer of them.  A counter is kSubCounters
+// words, each in its own 128-byte line; the task with slot s adds one to word
+// s % kSubCounters, and a wait is over when the words sum to epoch * fan-in
+// (no reset between steps).  Spreading the adds keeps any one line from
+// serializing many of them, and a waiter reads only kSubCounters lines.
 enum CtrSlot : int32_t { C_QKV = 0, C_ROUTER = 1, C_ATTN = 2, C_GATEUP = 3, C_XNEXT = 4, C_DONE = 5 };
 constexpr int kCtrPerLayer = 8;
+constexpr int kSubCounters = 16;
+constexpr int kSubStride = 32;                           // words between sub-counters (128 bytes)
+constexpr int kCounterWords = kSubCounters * kSubStride;
 
 MK_HD int ctr_index(int layer, int slot) { return layer * kCtrPerLayer + slot; }
 
@@ -74,8 +78,7 @@ struct KArgs {
   int32_t pf_bytes;                                // size of the weight prefetch region
   const Task* tasks;
   const int32_t* queue_off;
-  uint32_t* flags;      // counters: [(L + 1) * kCtrPerLayer][n_slots] flag words
-  int32_t n_slots;      // flag words per counter
+  uint32_t* flags;      // counters: [(L + 1) * kCtrPerLayer][kCounterWords]
   uint32_t* tickets;    // attention tickets [L][max_batch][nkv], then 1 for the LM head
   int32_t* err;         // E_WORDS
   const uint64_t* wtab; // device pointers of the weights
