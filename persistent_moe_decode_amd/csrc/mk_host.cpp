@@ -256,9 +256,8 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
 
   // Compute units 0 .. n_attn - 1 run the attention split and no stage-1
   // rows, so their K/V loads are in flight while the other units normalize
-  // and project; units n_attn .. ncu - 1 run the stage-1 rows and then the
-  // selected experts' gate/up rows.  Every unit takes an equal share of the
-  // output rows.  n_attn follows the bytes attention streams per layer
+  // and project; units n_attn .. ncu - 1 run the stage-1 rows, the selected
+  // experts' gate/up rows and the output rows.  n_attn follows the bytes attention streams per layer
   // against the expert gate/up bytes (attention weighted 1.5x for its extra
   // arithmetic); the split never changes results.
   const double hint = ctx_hint > 0 ? (double)ctx_hint : 4096.0;
@@ -301,6 +300,18 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
       *r1 += qkv_rows;
     }
   };
+  // Output rows: an attention unit takes out_w / 16 of a stage-1 unit's share,
+  // none by default.  The unit that merges a chunk group finishes its layer
+  // late; with output rows it would start the next layer's chunk late too,
+  // arrive last again and merge again, every layer.
+  int out_w = 0;
+  if (const char* oenv = std::getenv("MK_OUT_ATTN_W16")) out_w = std::max(0, std::min(16, std::atoi(oenv)));
+  const int64_t out_total = (int64_t)n_attn * out_w + (int64_t)(ncu - n_attn) * 16;
+  auto out_rows = [&](int q, int* r0, int* r1) {
+    auto cum = [&](int k) { return (int64_t)std::min(k, n_attn) * out_w + (int64_t)std::max(0, k - n_attn) * 16; };
+    *r0 = (int)((int64_t)H * cum(q) / out_total);
+    *r1 = (int)((int64_t)H * cum(q + 1) / out_total);
+  };
   std::vector<int> n_qkv_tasks(L, 0), n_router_tasks(L, 0), n_out_tasks(L, 0);
   int n_lm = 0;
   c->out_rows_max = 0;
@@ -311,7 +322,7 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
     pre_rows(q, &r0, &r1);
     if (r1 > r0) (r0 < qkv_rows ? n_qkv_tasks[0] : n_router_tasks[0])++;
     c->pre_rows_max = std::max(c->pre_rows_max, r1 - r0);
-    split_rows(H, ncu, q, &r0, &r1);
+    out_rows(q, &r0, &r1);
     if (r1 > r0) n_out_tasks[0]++;
     c->out_rows_max = std::max(c->out_rows_max, r1 - r0);
     split_rows(f.vocab, ncu, q, &r0, &r1);
@@ -349,8 +360,6 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
         Task t = make_task(OP_ATTN, l);
         t.wait[0] = ctr_index(l, C_QKV);
         t.fanin[0] = n_qkv_tasks[l];
-        t.wait[1] = ctr_index(l, C_ROUTER);  // the top-k for this unit's output task
-        t.fanin[1] = n_router_tasks[l];
         t.idx = q;
         t.count = n_attn;
         t.signal = ctr_index(l, C_ATTN);
@@ -365,7 +374,7 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
         c->tasks.push_back(t);
       }
       // OUT
-      split_rows(H, ncu, q, &r0, &r1);
+      out_rows(q, &r0, &r1);
       if (r1 > r0) {
         // expert rows first (needs gate/up), then Wo rows (needs attention): the
         // attention counter is waited inside the task, after the down projection
@@ -408,8 +417,10 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
   // LDS: region A (input vectors), B (top-k state, reductions), C (per-op arrays)
   const int maxU = std::min(E, B * f.top_k);
   c->gu_rows_max = (int)(((int64_t)maxU * f.inter + n_gu - 1) / n_gu) + 1;
-  size_t a_bytes = std::max({(size_t)B * H * 2, (size_t)B * f.n_q_heads * f.head_dim * 2,
-                             (size_t)B * f.top_k * f.inter * 2, (size_t)group * f.head_dim * 2});
+  // (the normalization stages its input rows and gain behind xs: fp32 [B][H], then [H] bf16)
+  size_t a_bytes = std::max({align_up((size_t)B * H * 2, 256) + (size_t)B * H * 4 + (size_t)H * 2,
+                             (size_t)B * f.n_q_heads * f.head_dim * 2, (size_t)B * f.top_k * f.inter * 2,
+                             (size_t)(group + 1) * f.head_dim * 2});  // attention: rotated q heads + the new k
   a_bytes = align_up(a_bytes, 256);
   const size_t b_bytes = kLdsB;
   size_t c_gu = (size_t)std::min(c->gu_rows_max, kGuPass) * B * 2 * 4;
