@@ -44,7 +44,7 @@ struct WsLayout {
   size_t state = 0, n_state_u32 = 0;  // counter flags, tickets, error word (zeroed by mk_reset)
   size_t ctr = 0, tickets = 0, err = 0;
   size_t tasks = 0, queue_off = 0, wtab = 0, inv_freq = 0;
-  size_t x = 0, qkv = 0, rlog = 0, attn_part = 0, attn_out = 0, h = 0, lm_part = 0, sel = 0;
+  size_t x = 0, qkv = 0, rlog = 0, attn_part = 0, attn_out = 0, wo_out = 0, h = 0, lm_part = 0, sel = 0;
   size_t total = 0;
 };
 
@@ -228,6 +228,7 @@ static WsLayout layout_workspace(const mk_ctx* c) {
   w.rlog = take(4 * L * B * f.n_experts);
   w.attn_part = take((size_t)4 * L * c->n_attn * attn_part_stride(group, f.head_dim));
   w.attn_out = take(2 * L * B * f.n_q_heads * f.head_dim);
+  w.wo_out = take(4 * L * B * f.hidden);
   w.h = take(2 * L * B * f.top_k * f.inter);
   w.lm_part = take(4 * 2 * c->n_lm * B);
   w.sel = take(4 * L * B * f.top_k);
@@ -256,8 +257,8 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
 
   // Compute units 0 .. n_attn - 1 run the attention split and no stage-1
   // rows, so their K/V loads are in flight while the other units normalize
-  // and project; units n_attn .. ncu - 1 run the stage-1 rows, the selected
-  // experts' gate/up rows and the output rows.  n_attn follows the bytes attention streams per layer
+  // and project, and then the Wo rows; units n_attn .. ncu - 1 run the
+  // stage-1 rows, the selected experts' gate/up rows and the output rows.  n_attn follows the bytes attention streams per layer
   // against the expert gate/up bytes (attention weighted 1.5x for its extra
   // arithmetic); the split never changes results.
   const double hint = ctx_hint > 0 ? (double)ctx_hint : 4096.0;
@@ -300,19 +301,18 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
       *r1 += qkv_rows;
     }
   };
-  // Output rows: an attention unit takes out_w / 16 of a stage-1 unit's share,
-  // none by default.  The unit that merges a chunk group finishes its layer
-  // late; with output rows it would start the next layer's chunk late too,
-  // arrive last again and merge again, every layer.
-  int out_w = 0;
-  if (const char* oenv = std::getenv("MK_OUT_ATTN_W16")) out_w = std::max(0, std::min(16, std::atoi(oenv)));
-  const int64_t out_total = (int64_t)n_attn * out_w + (int64_t)(ncu - n_attn) * 16;
+  // Output rows (expert down projections, residual) over the stage-1 units;
+  // the Wo rows over the attention units, which run them once the chunk
+  // groups are merged, while the experts are still in flight.
   auto out_rows = [&](int q, int* r0, int* r1) {
-    auto cum = [&](int k) { return (int64_t)std::min(k, n_attn) * out_w + (int64_t)std::max(0, k - n_attn) * 16; };
-    *r0 = (int)((int64_t)H * cum(q) / out_total);
-    *r1 = (int)((int64_t)H * cum(q + 1) / out_total);
+    *r0 = *r1 = 0;
+    if (q >= n_attn) split_rows(H, ncu - n_attn, q - n_attn, r0, r1);
   };
-  std::vector<int> n_qkv_tasks(L, 0), n_router_tasks(L, 0), n_out_tasks(L, 0);
+  auto wo_rows = [&](int q, int* r0, int* r1) {
+    *r0 = *r1 = 0;
+    if (q < n_attn) split_rows(H, n_attn, q, r0, r1);
+  };
+  std::vector<int> n_qkv_tasks(L, 0), n_router_tasks(L, 0), n_out_tasks(L, 0), n_wo_tasks(L, 0);
   int n_lm = 0;
   c->out_rows_max = 0;
   c->lm_rows_max = 0;
@@ -325,6 +325,8 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
     out_rows(q, &r0, &r1);
     if (r1 > r0) n_out_tasks[0]++;
     c->out_rows_max = std::max(c->out_rows_max, r1 - r0);
+    wo_rows(q, &r0, &r1);
+    if (r1 > r0) n_wo_tasks[0]++;
     split_rows(f.vocab, ncu, q, &r0, &r1);
     if (r1 > r0) n_lm++;
     c->lm_rows_max = std::max(c->lm_rows_max, r1 - r0);
@@ -333,6 +335,7 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
     n_qkv_tasks[l] = n_qkv_tasks[0];
     n_router_tasks[l] = n_router_tasks[0];
     n_out_tasks[l] = n_out_tasks[0];
+    n_wo_tasks[l] = n_wo_tasks[0];
   }
   c->n_out = n_out_tasks[0];
   c->n_lm = n_lm;
@@ -364,6 +367,16 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
         t.count = n_attn;
         t.signal = ctr_index(l, C_ATTN);
         c->tasks.push_back(t);
+        wo_rows(q, &r0, &r1);
+        if (r1 > r0) {
+          Task w = make_task(OP_WO, l);
+          w.wait[0] = ctr_index(l, C_ATTN);
+          w.fanin[0] = n_attn;
+          w.r0 = r0;
+          w.r1 = r1;
+          w.signal = ctr_index(l, C_WO);
+          c->tasks.push_back(w);
+        }
       } else {
         Task t = make_task(OP_GATEUP, l);
         t.wait[0] = ctr_index(l, C_ROUTER);
@@ -376,15 +389,16 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
       // OUT
       out_rows(q, &r0, &r1);
       if (r1 > r0) {
-        // expert rows first (needs gate/up), then Wo rows (needs attention): the
-        // attention counter is waited inside the task, after the down projection
+        // expert rows (needs gate/up), then the residual update, which also
+        // needs the Wo rows: their counter is waited inside the task, after
+        // the down projection
         Task t = make_task(OP_OUT, l);
         t.wait[0] = ctr_index(l, C_GATEUP);
         t.fanin[0] = n_gu;
         t.wait[1] = ctr_index(l, C_ROUTER);  // for the top-k, where no gate/up task left it in LDS
         t.fanin[1] = n_router_tasks[l];
-        t.late_wait = ctr_index(l, C_ATTN);
-        t.late_fanin = n_attn;
+        t.late_wait = ctr_index(l, C_WO);
+        t.late_fanin = n_wo_tasks[l];
         t.r0 = r0;
         t.r1 = r1;
         t.signal = ctr_index(l, C_XNEXT);
@@ -424,7 +438,7 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
   a_bytes = align_up(a_bytes, 256);
   const size_t b_bytes = kLdsB;
   size_t c_gu = (size_t)std::min(c->gu_rows_max, kGuPass) * B * 2 * 4;
-  size_t c_out = (size_t)c->out_rows_max * B * 4 + (size_t)c->out_rows_max * B * f.top_k * 4;
+  size_t c_out = (size_t)c->out_rows_max * B * f.top_k * 4;  // the experts' contributions to the task's rows
   size_t c_lm = (size_t)std::min(c->lm_rows_max, kLmPass) * B * 4;
   // attention: the waves' partial results, or (last chunk) the (max, sum) of all chunks plus one float4 per thread
   size_t c_attn = std::max((size_t)kWaves * (group * f.head_dim + 2 * kMaxGroup) * 4,
@@ -650,6 +664,7 @@ extern "C" int mk_decode_step(mk_ctx* c, int32_t n, const int32_t* d_tokens, con
   a.rlog = (float*)(w + c->ws.rlog);
   a.attn_part = (float*)(w + c->ws.attn_part);
   a.attn_out = (uint16_t*)(w + c->ws.attn_out);
+  a.wo_out = (float*)(w + c->ws.wo_out);
   a.h = (uint16_t*)(w + c->ws.h);
   a.lm_part = (float*)(w + c->ws.lm_part);
   a.sel_out = (int32_t*)(w + c->ws.sel);

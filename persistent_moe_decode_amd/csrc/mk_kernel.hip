@@ -644,7 +644,7 @@ DEV int task_prefetch(const KArgs& a, const Task& t, const Lds& s, int qi) {
     nrows = t.r1 - t.r0;
     src = t.r0 < a.qkv_rows ? wptr(a, widx(t.layer, WL_QKV)) + (size_t)t.r0 * K
                             : wptr(a, widx(t.layer, WL_ROUTER)) + (size_t)(t.r0 - a.qkv_rows) * K;
-  } else if (t.op == OP_OUT) {
+  } else if (t.op == OP_WO) {
     K = a.nq * a.d;
     nrows = t.r1 - t.r0;
     src = wptr(a, widx(t.layer, WL_O)) + (size_t)t.r0 * K;
@@ -1298,20 +1298,6 @@ TASK void task_gateup(const KArgs& a, const Task& t, const Lds& s, int qi, bool 
 // ---------------------------------------------------------------------------
 // OUT: rows [r0, r1) of the hidden state.
 
-struct JobO {
-  const gu16* W;
-  const AS_LDS uint16_t* pf;  // prefetched rows [0, npf)
-  int npf;
-  int r0, K, maxB;
-  const uint16_t* xs;
-  float* ao;
-  DEV const gu4* row(int i) const { return (const gu4*)(W + (size_t)(r0 + i) * K); }
-  DEV const lu4* lrow(int i) const { return (const lu4*)(pf + i * K); }
-  DEV int nx(int) const { return 1 << 30; }
-  DEV const uint4* x(int, int t) const { return (const uint4*)(xs + (size_t)t * K); }
-  DEV void emit(int i, int t, float v) const { ao[(size_t)i * maxB + t] = v; }
-};
-
 struct JobDown {
   const TopK* tk;
   const gu16* W;
@@ -1338,10 +1324,9 @@ constexpr int kDownGroups = 3;
 // down-projection rows are loaded before the gate/up results are waited for.
 // have_tk: region B still holds this layer's top-k, left there by the gate/up
 // task that ran just before on this compute unit.
-TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf, bool have_tk) {
-  const int l = t.layer, nr = t.r1 - t.r0, n = a.n, AD = a.nq * a.d;
-  float* ao = (float*)s.C;                                    // [out_rows_max][maxB]
-  float* contrib = ao + (size_t)a.out_rows_max * a.max_batch;  // [out_rows_max][maxB*topk]
+TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have_tk) {
+  const int l = t.layer, nr = t.r1 - t.r0, n = a.n;
+  float* contrib = (float*)s.C;  // [out_rows_max][maxB*topk]
   const int maxBK = a.max_batch * a.topk;
   uint16_t* xs = (uint16_t*)s.A;
   // the residual rows this task updates are final already: their loads go out first
@@ -1384,13 +1369,6 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf,
   if (!wait_counter(a, t.wait[0], t.fanin[0], qi, s.flags + 0)) return;
   if (a.trace && tid() == 0 && qi < a.trace_cap) a.trace[kTraceWords * (size_t)qi + 1] = wall_clock64();
   copy_coh_to_lds(xs, a.h + (size_t)l * a.max_batch * a.topk * a.I, n * a.topk * a.I * 2);
-  // attention has mostly finished by now: when one look at its flags says so,
-  // its output comes in with h, into the part of region C the task leaves free
-  const size_t c_used = ((size_t)a.out_rows_max * a.max_batch * (1 + a.topk) * 4 + 15) & ~(size_t)15;
-  uint16_t* ao_early = (uint16_t*)(s.C + c_used);
-  bool early = c_used + (size_t)n * AD * 2 <= (size_t)(a.lds_p - a.lds_c) &&
-               counter_done(a, t.late_wait, t.late_fanin, s.flags + 13);
-  if (early) copy_coh_to_lds(ao_early, a.attn_out + (size_t)l * a.max_batch * AD, n * AD * 2);
   prefetch_wait();
   mark(a, qi, 0);
   // expert down projections: the register rows, then the rest from HBM
@@ -1413,33 +1391,67 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, int npf,
   }
   rowdots_range<false>(a.I, npre, nd, mt, jd);
   mark(a, qi, 1);
-  // attention output projection (Wo rows are already in LDS)
-  if (!early) {
-    wait_counter(a, t.late_wait, t.late_fanin, qi, s.flags + 13);  // its barrier also frees xs
-    copy_coh_to_lds(xs, a.attn_out + (size_t)l * a.max_batch * AD, n * AD * 2);
-    prefetch_wait();
-  }
+  // the attention output times Wo, for these rows (attention units)
+  if (!wait_counter(a, t.late_wait, t.late_fanin, qi, s.flags + 13)) return;
   mark(a, qi, 2);
-  JobO jo;
-  jo.pf = (const AS_LDS uint16_t*)s.P;
-  jo.npf = npf;
-  jo.W = wptr(a, widx(l, WL_O));
-  jo.r0 = t.r0;
-  jo.K = AD;
-  jo.maxB = a.max_batch;
-  jo.xs = early ? ao_early : xs;
-  jo.ao = ao;
-  run_rowdots_pf(AD, nr, npf, n, jo);
-  __syncthreads();
-  mark(a, qi, 3);
   // x_{l+1} = (x_l + attn) + sum_j w_j y_j
+  const float* wo = a.wo_out + (size_t)l * a.max_batch * a.H + t.r0;
   for (int e = tid(); e < nr * n; e += kThreads) {
     const int rr = e / n, b = e % n;
     float moe = 0.f;
     for (int j = 0; j < a.topk; ++j) moe += tk->w[b][j] * contrib[(size_t)rr * maxBK + b * a.topk + j];
     const float xo = e == tid() ? x_first : load_x(a, l, b, t.r0 + rr, l == 0 ? token_row(a, b, qi) : nullptr);
-    st_coh(a.x + ((size_t)(l + 1) * a.max_batch + b) * a.H + t.r0 + rr, (xo + ao[(size_t)rr * a.max_batch + b]) + moe);
+    st_coh(a.x + ((size_t)(l + 1) * a.max_batch + b) * a.H + t.r0 + rr, (xo + ld_coh(wo + (size_t)b * a.H + rr)) + moe);
   }
+}
+
+// ---------------------------------------------------------------------------
+// WO: rows [r0, r1) of Wo times the merged attention output, for the output
+// tasks' residual update.  The task waits for the merges itself: before that
+// the first rows of Wo are in LDS already (copied at task start) and the next
+// (kWaves - 1) * 2 are loaded into registers by waves 1..7 (32 lanes per row,
+// kWoC 16-byte chunks per lane), so mostly arithmetic is left once the
+// attention output is in.
+constexpr int kWoC = 16;
+
+TASK void task_wo(const KArgs& a, const Task& t, const Lds& s, int qi, int npf) {
+  const int l = t.layer, AD = a.nq * a.d, nr = t.r1 - t.r0, n = a.n;
+  const int lane = tid() & 63, wave = tid() >> 6, li = lane & 31;
+  const int nreg = AD == 32 * kWoC * 8 ? min(nr - npf, (kWaves - 1) * 2) : 0;
+  const int ir = npf + (wave >= 1 ? (wave - 1) * 2 + (lane >> 5) : nreg);  // this lane's register row
+  const bool act = ir < npf + nreg;
+  const gu16* W = wptr(a, widx(l, WL_O));
+  const gu4* wsrc = (const gu4*)(W + (size_t)(t.r0 + (act ? ir : 0)) * AD) + li;
+  uint4 wr[kWoC];
+#pragma unroll
+  for (int c = 0; c < kWoC; ++c)
+    wr[c] = __builtin_bit_cast(uint4, act ? __builtin_nontemporal_load(wsrc + 32 * c) : u32x4_v{0, 0, 0, 0});
+  if (!wait_counter(a, t.wait[0], t.fanin[0], qi, s.flags + 0)) return;
+  if (a.trace && tid() == 0 && qi < a.trace_cap) a.trace[kTraceWords * (size_t)qi + 1] = wall_clock64();
+  uint16_t* xs = (uint16_t*)s.A;
+  copy_coh_to_lds(xs, a.attn_out + (size_t)l * a.max_batch * AD, n * AD * 2);
+  prefetch_wait();
+  mark(a, qi, 0);
+  JobPre j;
+  j.pf = (const AS_LDS uint16_t*)s.P;
+  j.npf = npf;
+  j.W = W;
+  j.r0 = t.r0;
+  j.K = AD;
+  j.xs = xs;
+  j.out = a.wo_out + (size_t)l * a.max_batch * a.H + t.r0;
+  j.ld = a.H;
+  rowdots_range<true>(AD, 0, npf, n, j);
+  for (int b = 0; b < n; ++b) {
+    const uint4* xr = (const uint4*)(xs + (size_t)b * AD) + li;
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < kWoC; ++c) acc = dot8(wr[c], xr[32 * c], acc);
+    acc = group_sum<32>(acc);
+    if (act && li == 0) j.emit(ir, b, acc);
+  }
+  rowdots_range<false>(AD, npf + nreg, nr, n, j);
+  mark(a, qi, 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -1563,8 +1575,8 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a)
     if (a.trace && tid() == 0) t_fetch = wall_clock64();
     // immutable weights start streaming into LDS before the inputs are ready
     const int npf = task_prefetch(a, t, s, q);
-    // attention and output tasks wait inside, once their loads are in flight
-    const bool own_wait = t.op == OP_ATTN || t.op == OP_OUT;
+    // attention, Wo and output tasks wait inside, once their loads are in flight
+    const bool own_wait = t.op == OP_ATTN || t.op == OP_OUT || t.op == OP_WO;
     bool ok = own_wait || wait_counter(a, t.wait[0], t.fanin[0], q, s.flags + 0);
     if (ok && !own_wait && t.wait[1] >= 0) ok = wait_counter(a, t.wait[1], t.fanin[1], q, s.flags + 1);
     if (a.trace && tid() == 0) t_ready = wall_clock64();
@@ -1573,7 +1585,8 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a)
         case OP_PRE: task_pre(a, t, s, q, npf); break;
         case OP_ATTN: task_attn(a, t, s, q); break;
         case OP_GATEUP: task_gateup(a, t, s, q, xs_layer == t.layer); break;
-        case OP_OUT: task_out(a, t, s, q, npf, tk_layer == t.layer); break;
+        case OP_OUT: task_out(a, t, s, q, tk_layer == t.layer); break;
+        case OP_WO: task_wo(a, t, s, q, npf); break;
         case OP_LMHEAD: task_lmhead(a, t, s, q); break;
         default: break;
       }

@@ -30,8 +30,9 @@ enum Op : int32_t {
   OP_PRE = 1,     // RMSNorm + rows of [Wq; Wk; Wv] or of the router
   OP_ATTN = 2,    // paged split-KV attention chunk; last arriver of a (seq, kv head) combines
   OP_GATEUP = 3,  // router top-k + rows of the selected experts' gate/up + SwiGLU
-  OP_OUT = 4,     // rows of Wo and of the selected experts' down projection + residual
+  OP_OUT = 4,     // rows of the selected experts' down projection + residual update
   OP_LMHEAD = 5,  // final RMSNorm + LM head rows; last arriver takes the argmax
+  OP_WO = 6,      // rows of Wo times the merged attention output (run by the attention units)
 };
 
 // One task: 32 int32 (128 bytes, one cache line).
@@ -55,7 +56,7 @@ static_assert(sizeof(Task) == kTaskInts * 4, "task descriptor is 128 bytes");
 // s % kSubCounters, and a wait is over when the words sum to epoch * fan-in
 // (no reset between steps).  Spreading the adds keeps any one line from
 // serializing many of them, and a waiter reads only kSubCounters lines.
-enum CtrSlot : int32_t { C_QKV = 0, C_ROUTER = 1, C_ATTN = 2, C_GATEUP = 3, C_XNEXT = 4, C_DONE = 5 };
+enum CtrSlot : int32_t { C_QKV = 0, C_ROUTER = 1, C_ATTN = 2, C_GATEUP = 3, C_XNEXT = 4, C_DONE = 5, C_WO = 6 };
 constexpr int kCtrPerLayer = 8;
 constexpr int kSubCounters = 16;
 constexpr int kSubStride = 32;                           // words between sub-counters (128 bytes)
@@ -89,6 +90,7 @@ struct KArgs {
   float* rlog;          // [L][max_batch][E]
   float* attn_part;     // [L][n_attn][attn_part_stride(group, d)]
   uint16_t* attn_out;   // [L][max_batch][nq*d]
+  float* wo_out;        // [L][max_batch][H] attention output times Wo
   uint16_t* h;          // [L][max_batch*topk][I]
   float* lm_part;       // [n_lm][max_batch][2] (value, index as float bits)
   int32_t* sel_out;     // [L][max_batch][topk] experts chosen per token

@@ -24,7 +24,7 @@ ERRORS = {
 }
 CODES = {v: k for k, v in ERRORS.items()}
 TASK_INT32S = 32
-OPS = {1: "PRE", 2: "ATTN", 3: "GATEUP", 4: "OUT", 5: "LMHEAD"}
+OPS = {1: "PRE", 2: "ATTN", 3: "GATEUP", 4: "OUT", 5: "LMHEAD", 6: "WO"}
 
 
 class MkError(RuntimeError):

@@ -7,9 +7,9 @@ body, and when it had signalled.  This module joins them with the task table.
 
 Phase marks per op: PRE [inputs loaded, norm done, rows done]; ATTN [q
 rotated and new K/V written, copied pages landed, positions done, partial
-stored]; GATEUP [routing loaded, norm done]; OUT [routing and h loaded, down
-rows done, attention waited, Wo rows done]; LMHEAD [norm done, rows done,
-local argmax done].
+stored]; GATEUP [routing loaded, norm done]; OUT [h loaded, down rows done,
+Wo rows waited]; WO [attention output loaded, rows done]; LMHEAD [norm done,
+rows done, local argmax done].
 """
 from __future__ import annotations
 

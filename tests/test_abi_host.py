@@ -10,7 +10,7 @@ import pytest
 import synth
 from persistent_moe_decode_amd import mk
 
-OP_PRE, OP_ATTN, OP_GATEUP, OP_OUT, OP_LMHEAD = 1, 2, 3, 4, 5
+OP_PRE, OP_ATTN, OP_GATEUP, OP_OUT, OP_LMHEAD, OP_WO = 1, 2, 3, 4, 5, 6
 F_OP, F_LAYER, F_WAIT0, F_WAIT1, F_FAN0, F_FAN1, F_SIGNAL, F_R0, F_R1, F_IDX, F_COUNT, F_LATE, F_LATE_FAN, F_SLOT = range(14)
 
 
@@ -71,12 +71,16 @@ def test_schedule_builds_and_simulates(name, ncu):
     assert np.sum(ops == OP_GATEUP) == L * info.n_gateup
     assert info.n_attn + info.n_gateup == ncu
     assert w.batch * w.shape.n_kv_heads <= info.n_attn <= ncu - 2
-    # attention units run their chunk and no stage-1 rows; every other unit one stage-1 and one gate/up task
+    # attention units run their chunk and Wo rows, no stage-1 or output rows; every other
+    # unit one stage-1, one gate/up and one output task
     for q in range(ncu):
         mine = tasks[qoff[q]:qoff[q + 1]]
         l0 = mine[:, F_LAYER] == 0
-        n = tuple(int(np.sum((mine[:, F_OP] == op) & l0)) for op in (OP_PRE, OP_ATTN, OP_GATEUP))
-        assert n == ((0, 1, 0) if q < info.n_attn else (1, 0, 1)), q
+        n = tuple(int(np.sum((mine[:, F_OP] == op) & l0)) for op in (OP_PRE, OP_ATTN, OP_GATEUP, OP_OUT, OP_WO))
+        if q < info.n_attn:
+            assert n[:4] == (0, 1, 0, 0) and n[4] <= 1, q
+        else:
+            assert n[:3] == (1, 0, 1) and n[4] == 0, q
     # PRE rows cover [Wqkv; router] exactly once per layer; OUT rows cover hidden; LM rows cover vocab
     for l in range(L):
         pre = tasks[(ops == OP_PRE) & (tasks[:, F_LAYER] == l)]
@@ -85,11 +89,12 @@ def test_schedule_builds_and_simulates(name, ncu):
             cover[t[F_R0]:t[F_R1]] += 1
             assert t[F_R1] <= w.shape.qkv_rows or t[F_R0] >= w.shape.qkv_rows
         assert np.all(cover == 1)
-        out = tasks[(ops == OP_OUT) & (tasks[:, F_LAYER] == l)]
-        cover = np.zeros(w.shape.hidden, dtype=int)
-        for t in out:
-            cover[t[F_R0]:t[F_R1]] += 1
-        assert np.all(cover == 1)
+        for op in (OP_OUT, OP_WO):
+            out = tasks[(ops == op) & (tasks[:, F_LAYER] == l)]
+            cover = np.zeros(w.shape.hidden, dtype=int)
+            for t in out:
+                cover[t[F_R0]:t[F_R1]] += 1
+            assert np.all(cover == 1)
     lm = tasks[ops == OP_LMHEAD]
     cover = np.zeros(w.shape.vocab, dtype=int)
     for t in lm:
@@ -181,7 +186,7 @@ def test_simulator_catches_a_shared_flag_word():
 def test_simulator_counts_the_in_body_wait():
     tasks, qoff, nctr = _tiny_table()
     outs = np.nonzero(tasks[:, F_OP] == OP_OUT)[0]
-    assert np.all(tasks[outs, F_LATE] >= 0)           # output tasks wait for attention inside the body
+    assert np.all(tasks[outs, F_LATE] >= 0)           # output tasks wait for the Wo rows inside the body
     t = tasks.copy()
     t[outs[0], F_LATE_FAN] += 1
     code, _ = mk.simulate_table(t, qoff, nctr)
