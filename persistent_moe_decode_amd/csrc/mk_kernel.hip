@@ -1315,16 +1315,17 @@ struct JobDown {
 
 // Down-projection rows held in registers across the gate/up wait: 16 lanes
 // per row, up to kDownC 16-byte chunks per lane (rows up to 128 * kDownC
-// elements), kDownGroups groups of 4 rows per wave.
-constexpr int kDownC = 8;
-constexpr int kDownGroups = 3;
+// elements), kDownGroups groups of 4 rows per wave (the 96 rows of a 12-row
+// task at 8 experts fit).
+constexpr int kDownC = 6;
+constexpr int kDownGroups = 4;
 
 // Output tasks wait for their inputs themselves: the residual rows, the
 // top-k (from LDS, or computed once the router rows are done) and the first
 // down-projection rows are loaded before the gate/up results are waited for.
 // have_tk: region B still holds this layer's top-k, left there by the gate/up
 // task that ran just before on this compute unit.
-TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have_tk) {
+TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have_tk, bool has_next, int& next_pf) {
   const int l = t.layer, nr = t.r1 - t.r0, n = a.n;
   float* contrib = (float*)s.C;  // [out_rows_max][maxB*topk]
   const int maxBK = a.max_batch * a.topk;
@@ -1371,6 +1372,13 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool hav
   copy_coh_to_lds(xs, a.h + (size_t)l * a.max_batch * a.topk * a.I, n * a.topk * a.I * 2);
   prefetch_wait();
   mark(a, qi, 0);
+  // region P is idle from here on: the next task's weight tile starts
+  // streaming in now, while the down rows are computed (its copy is then not
+  // in the way of that task's own poll and input loads)
+  if (has_next) {
+    const Task tn = a.tasks[qi + 1];
+    if (tn.op == OP_PRE) next_pf = task_prefetch(a, tn, s, qi + 1);
+  }
   // expert down projections: the register rows, then the rest from HBM
   const int mt = tk->maxtok;
 #pragma unroll
@@ -1569,12 +1577,13 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a)
   __syncthreads();
   int xs_layer = -1;                 // layer whose normalized input region A holds
   int tk_layer = -1;                 // layer whose top-k region B holds
+  int pf_q = -1, pf_n = 0;           // a task whose weight tile an earlier task started, and its rows
   for (int q = q0; q < q1; ++q) {
     const Task t = a.tasks[q];
     uint64_t t_fetch = 0, t_ready = 0;
     if (a.trace && tid() == 0) t_fetch = wall_clock64();
     // immutable weights start streaming into LDS before the inputs are ready
-    const int npf = task_prefetch(a, t, s, q);
+    const int npf = pf_q == q ? pf_n : task_prefetch(a, t, s, q);
     // attention, Wo and output tasks wait inside, once their loads are in flight
     const bool own_wait = t.op == OP_ATTN || t.op == OP_OUT || t.op == OP_WO;
     bool ok = own_wait || wait_counter(a, t.wait[0], t.fanin[0], q, s.flags + 0);
@@ -1585,7 +1594,14 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a)
         case OP_PRE: task_pre(a, t, s, q, npf); break;
         case OP_ATTN: task_attn(a, t, s, q); break;
         case OP_GATEUP: task_gateup(a, t, s, q, xs_layer == t.layer); break;
-        case OP_OUT: task_out(a, t, s, q, tk_layer == t.layer); break;
+        case OP_OUT: {
+          int nx = -1;
+          task_out(a, t, s, q, tk_layer == t.layer, q + 1 < q1, nx);
+          if (nx >= 0) {
+            pf_q = q + 1;
+            pf_n = nx;
+          }
+        } break;
         case OP_WO: task_wo(a, t, s, q, npf); break;
         case OP_LMHEAD: task_lmhead(a, t, s, q); break;
         default: break;
