@@ -496,65 +496,98 @@ DEV void run_rowdots_pf(int K, int njobs, int npf, int maxnx, const Job& job) {
 // asc), their softmax, the distinct experts in ascending order and, for each
 // of them, the (token, slot) pairs routed to it.
 //
-// Selection by rank: every (token, expert) counts the experts that beat it
-// under the total order (value desc, index asc), in parallel over all
-// threads; the ones with rank < top_k land in slot `rank`.
+// One wave per token (wave b takes token b), each lane holding experts lane
+// and lane + 64 as order-preserving 32-bit keys (NaN ranks as -inf):
+//   - the top_k-th largest key T, built bit by bit from the top: a bit stays
+//     set when at least top_k keys are >= the prefix with it (two compares
+//     and two ballot counts per bit);
+//   - the selection: every key > T, then keys == T in index order until
+//     top_k are taken (ballot prefix counts);
+//   - the top_k winners, packed into LDS, are ranked among themselves.
+// A vector instruction of a wave takes four cycles here, so the work is kept
+// to a few hundred instructions rather than all expert pairs compared.
 
+// The order of (value, index) pairs used by every selection here: larger
+// value first, then smaller index.
 DEV bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
 
-// scratch: 4 * kMaxExperts + kMaxBatch * kMaxExperts bytes of LDS for the
-// per-expert token masks and slots.
-DEV void compute_topk(const KArgs& a, int layer, TopK* tk, float* rbuf, uint8_t* scratch) {
-  const int lane = tid() & 63;
+DEV uint32_t topk_key(float v) {
+  const uint32_t u = __float_as_uint(v != v ? kNegInf : v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// scratch: kTopKScratch bytes of LDS: per-expert token masks [kMaxExperts],
+// slots [kMaxBatch][kMaxExperts], then per wave the packed winners
+// (key, expert, logit, exp) [kWaves][4][kMaxTopK].
+DEV void compute_topk(const KArgs& a, int layer, TopK* tk, uint8_t* scratch) {
+  const int lane = tid() & 63, wave = tid() >> 6;
   const int E = a.E, K = a.topk, n = a.n;
-  int32_t* emask = (int32_t*)scratch;                  // [kMaxExperts]: bit b set when token b chose expert e
-  uint8_t* eslot = scratch + 4 * kMaxExperts;          // [kMaxBatch][kMaxExperts]: slot of e in token b's top-k
-  const float* rl = a.rlog + (size_t)layer * a.max_batch * E;
-  for (int i = tid(); i < n * E; i += kThreads) {
-    const float v = ld_coh(rl + i);
-    rbuf[i] = v != v ? kNegInf : v;  // NaN never outranks a number
-  }
+  int32_t* emask = (int32_t*)scratch;
+  uint8_t* eslot = scratch + 4 * kMaxExperts;
+  uint32_t* pk = (uint32_t*)(scratch + 4 * kMaxExperts + kMaxBatch * kMaxExperts) + wave * 4 * kMaxTopK;
+  int32_t* pe = (int32_t*)(pk + kMaxTopK);
+  float* pv = (float*)(pk + 2 * kMaxTopK);
+  float* px = (float*)(pk + 3 * kMaxTopK);
   for (int e = tid(); e < kMaxExperts; e += kThreads) emask[e] = 0;
   __syncthreads();
-  // four threads per (token, expert), each counting a quarter of the rivals; a quad sum joins them
-  for (int i4 = tid(); i4 < 4 * n * E; i4 += kThreads) {
-    const int i = i4 >> 2, part = i4 & 3;
-    const int b = i / E, e = i - b * E;
-    const float v = rbuf[i];
-    const float* rb = rbuf + b * E;
-    int rank = 0;
-#pragma unroll 8
-    for (int j = part; j < E; j += 4) {
-      const float u = rb[j];
-      rank += (u > v) | ((u == v) & (j < e));
+  if (wave < n) {
+    const int b = wave;
+    const float* rl = a.rlog + ((size_t)layer * a.max_batch + b) * E;
+    const float v0 = lane < E ? ld_coh(rl + lane) : kNegInf;
+    const float v1 = lane + 64 < E ? ld_coh(rl + lane + 64) : kNegInf;
+    const uint32_t k0 = lane < E ? topk_key(v0) : 0u, k1 = lane + 64 < E ? topk_key(v1) : 0u;
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = T | (1u << bit);
+      if (__popcll(__ballot(k0 >= c)) + __popcll(__ballot(k1 >= c)) >= K) T = c;
     }
-    float rf = (float)rank;
-    rf += dpp<0xB1>(rf);
-    rf += dpp<0x4E>(rf);
-    rank = (int)rf;
-    if (part == 0 && rank < K) {
-      tk->sel[b][rank] = e;
-      tk->w[b][rank] = v;
-      atomicOr(emask + e, 1 << b);
-      eslot[b * kMaxExperts + e] = (uint8_t)rank;
+    const uint64_t q0 = __ballot(k0 == T), q1 = __ballot(k1 == T);
+    const int need = K - (__popcll(__ballot(k0 > T)) + __popcll(__ballot(k1 > T)));
+    const uint64_t below = (1ull << lane) - 1ull;
+    const bool s0 = k0 > T || (k0 == T && __popcll(q0 & below) < need);
+    const bool s1 = k1 > T || (k1 == T && __popcll(q0) + __popcll(q1 & below) < need);
+    const uint64_t m0 = __ballot(s0), m1 = __ballot(s1);
+    if (s0) {
+      const int p = __popcll(m0 & below);
+      pk[p] = k0;
+      pe[p] = lane;
+      pv[p] = v0 != v0 ? kNegInf : v0;
+    }
+    if (s1) {
+      const int p = __popcll(m0) + __popcll(m1 & below);
+      pk[p] = k1;
+      pe[p] = lane + 64;
+      pv[p] = v1 != v1 ? kNegInf : v1;
+    }
+    __builtin_amdgcn_wave_barrier();
+    int rank = 0;
+    uint32_t kj = 0;
+    int ej = 0;
+    float vj = 0.f;
+    if (lane < K) {
+      kj = pk[lane];
+      ej = pe[lane];
+      vj = pv[lane];
+      for (int i = 0; i < K; ++i) rank += (pk[i] > kj) | ((pk[i] == kj) & (pe[i] < ej));
+      tk->sel[b][rank] = ej;
+      eslot[b * kMaxExperts + ej] = (uint8_t)rank;
+      atomicOr(emask + ej, 1 << b);
+    }
+    // softmax in slot order, relative to the largest logit (slot 0's)
+    float vmax = kNegInf;
+    for (int i = 0; i < K; ++i) vmax = fmaxf(vmax, pv[i]);
+    const float ex = __expf(vj - vmax);
+    __builtin_amdgcn_wave_barrier();
+    if (lane < K) px[rank] = ex;
+    __builtin_amdgcn_wave_barrier();
+    if (lane < K) {
+      float wsum = 0.f;
+      for (int j = 0; j < K; ++j) wsum += px[j];
+      tk->w[b][rank] = ex / wsum;
     }
   }
   __syncthreads();
-  if ((tid() >> 6) == 0) {
-    // softmax over each token's selected logits, slot order
-    if (lane < n) {
-      const float v0 = tk->w[lane][0];
-      float ex[kMaxTopK];
-      float wsum = 0.f;
-#pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j) {
-        ex[j] = j < K ? __expf(tk->w[lane][j] - v0) : 0.f;
-        wsum += ex[j];
-      }
-#pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j)
-        if (j < K) tk->w[lane][j] = ex[j] / wsum;
-    }
+  if (wave == 0) {
     // distinct experts in ascending order (lane e and e + 64), each with its
     // tokens in ascending order as pairs b * top_k + slot
     const int m_lo = emask[lane], m_hi = emask[lane + 64];
@@ -569,8 +602,7 @@ DEV void compute_topk(const KArgs& a, int layer, TopK* tk, float* rbuf, uint8_t*
         tk->U[u] = e;
         tk->ntok[u] = __popc(m);
         int t = 0;
-#pragma unroll
-        for (int bb = 0; bb < kMaxBatch; ++bb)
+        for (int bb = 0; bb < n; ++bb)
           if ((m >> bb) & 1) tk->pair[u][t++] = bb * K + eslot[bb * kMaxExperts + e];
       }
     }
@@ -1253,7 +1285,7 @@ struct JobGateUp {
 // the PRE task that ran just before on this compute unit.
 TASK void task_gateup(const KArgs& a, const Task& t, const Lds& s, int qi, bool have_xs) {
   const int l = t.layer;
-  compute_topk(a, l, s.tk, s.rbuf, s.C);
+  compute_topk(a, l, s.tk, s.C);
   if (t.idx == 0) write_sel(a, l, s.tk);
   mark(a, qi, 0);
   uint16_t* xs = (uint16_t*)s.A;
@@ -1338,7 +1370,7 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool hav
   }
   if (!have_tk) {
     if (!wait_counter(a, t.wait[1], t.fanin[1], qi, s.flags + 1)) return;
-    compute_topk(a, l, s.tk, s.rbuf, s.C);
+    compute_topk(a, l, s.tk, s.C);
   }
   const TopK* tk = s.tk;
   JobDown jd;

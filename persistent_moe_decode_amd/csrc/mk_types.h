@@ -24,7 +24,7 @@ constexpr int kGuPass = 256;       // gate/up virtual rows per pass of one task
 constexpr int kLmPass = 512;       // LM head rows per pass of one task
 constexpr int kTraceWords = 8;     // per task: fetch, ready, 4 phase marks, done, spare
 constexpr int kLdsB = 8192;        // LDS region B: top-k state, flags, reductions, router logits
-constexpr int kTopKScratch = 4 * kMaxExperts + kMaxBatch * kMaxExperts;  // region C bytes the top-k borrows
+constexpr int kTopKScratch = 4 * kMaxExperts + kMaxBatch * kMaxExperts + kWaves * 4 * kMaxTopK * 4;  // region C bytes the top-k borrows
 
 enum Op : int32_t {
   OP_PRE = 1,     // RMSNorm + rows of [Wq; Wk; Wv] or of the router
