@@ -193,10 +193,14 @@ int mk_simulate_table(const int32_t* tasks, int32_t n_tasks, const int32_t* queu
                       int32_t n_counters, int32_t* completed);
 
 /* Host mirror of the kernel's runtime attention split: for seq_lens[0..n),
- * n_kv heads and n_tasks split tasks, writes the chunk length in tokens to
- * *chunk and, per task, (b, kv head, first token, end token) into
- * plan[n_tasks][4] (b = -1 for an idle task). */
-int mk_attn_plan(const int32_t* seq_lens, int32_t n, int32_t n_kv, int32_t n_tasks, int32_t page_size,
+ * n_kv heads and n_tasks split tasks of which the first n_lead (>= n * n_kv)
+ * lead one (sequence, kv head) segment each, writes the chunk length in
+ * tokens to *chunk and, per task, (b, kv head, first token, end token) into
+ * plan[n_tasks][4] (b = -1 for an idle task).  Lead task m < n * n_kv takes
+ * the first chunk of segment m (b = m / n_kv, head m % n_kv); tasks n_lead ..
+ * take the other chunks of all segments in order.  The megakernel uses
+ * n_lead = max_batch * n_kv and n_tasks = the schedule's n_attn. */
+int mk_attn_plan(const int32_t* seq_lens, int32_t n, int32_t n_kv, int32_t n_tasks, int32_t n_lead, int32_t page_size,
                  int32_t* chunk, int32_t* plan);
 
 /* Offsets (bytes from the workspace base) of the per-layer activation

@@ -267,9 +267,13 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
   int n_attn = (int)std::lround(ncu * attn_bytes / (attn_bytes + gu_bytes));
   const char* env = std::getenv("MK_ATTN_CUS");
   if (env) n_attn = std::atoi(env);
-  n_attn = std::max(n_attn, B * f.n_kv_heads);
+  // attention units 0 .. n_lead - 1 lead a (sequence, kv head) segment each:
+  // first chunk and merge, no Wo rows; the others take the remaining chunks
+  // and the Wo rows
+  const int n_lead = B * f.n_kv_heads;
+  n_attn = std::max(n_attn, n_lead + 1);
   n_attn = std::min(n_attn, ncu - 2);  // at least one unit each for the QKV and the router rows
-  if (n_attn < B * f.n_kv_heads) return fail(MK_ERR_UNSUPPORTED, "too few compute units for the attention split");
+  if (n_attn < n_lead + 1) return fail(MK_ERR_UNSUPPORTED, "too few compute units for the attention split");
   const int n_gu = ncu - n_attn;
 
   c->tasks.clear();
@@ -310,7 +314,7 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
   };
   auto wo_rows = [&](int q, int* r0, int* r1) {
     *r0 = *r1 = 0;
-    if (q < n_attn) split_rows(H, n_attn, q, r0, r1);
+    if (q >= n_lead && q < n_attn) split_rows(H, n_attn - n_lead, q - n_lead, r0, r1);
   };
   std::vector<int> n_qkv_tasks(L, 0), n_router_tasks(L, 0), n_out_tasks(L, 0), n_wo_tasks(L, 0);
   int n_lm = 0;
@@ -365,13 +369,15 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
         t.fanin[0] = n_qkv_tasks[l];
         t.idx = q;
         t.count = n_attn;
-        t.signal = ctr_index(l, C_ATTN);
+        // leads signal once their segment is merged; the other chunks report
+        // to their segment's ticket instead
+        t.signal = q < n_lead ? ctr_index(l, C_ATTN) : -1;
         c->tasks.push_back(t);
         wo_rows(q, &r0, &r1);
         if (r1 > r0) {
           Task w = make_task(OP_WO, l);
           w.wait[0] = ctr_index(l, C_ATTN);
-          w.fanin[0] = n_attn;
+          w.fanin[0] = n_lead;
           w.r0 = r0;
           w.r1 = r1;
           w.signal = ctr_index(l, C_WO);
@@ -443,7 +449,8 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
   // attention: the waves' partial results, or (last chunk) the (max, sum) of all chunks plus one float4 per thread
   size_t c_attn = std::max((size_t)kWaves * (group * f.head_dim + 2 * kMaxGroup) * 4,
                            align_up((size_t)n_attn * group * 2 * 4, 16) + (size_t)kThreads * 16);
-  size_t c_bytes = align_up(std::max({c_gu, c_out, c_lm, c_attn, (size_t)kTopKScratch}), 256);
+  const size_t c_mfma = B >= 2 ? (size_t)kMfmaRedBytes : 0;  // partial tiles of split dense rows
+  size_t c_bytes = align_up(std::max({c_gu, c_out, c_lm, c_attn, c_mfma, (size_t)kTopKScratch}), 256);
   c->lds_b = (int)a_bytes;
   c->lds_c = (int)(a_bytes + b_bytes);
   c->lds_p = (int)(a_bytes + b_bytes + c_bytes);
@@ -501,20 +508,21 @@ extern "C" int mk_copy_schedule(const mk_ctx* c, int32_t* tasks, int64_t tasks_c
   return MK_OK;
 }
 
-extern "C" int mk_attn_plan(const int32_t* seq_lens, int32_t n, int32_t n_kv, int32_t n_tasks, int32_t page_size,
-                            int32_t* chunk, int32_t* plan) {
-  if (!seq_lens || !chunk || !plan || n < 1 || n > kMaxBatch || n_kv < 1 || page_size < 1 || n_tasks < n * n_kv)
+extern "C" int mk_attn_plan(const int32_t* seq_lens, int32_t n, int32_t n_kv, int32_t n_tasks, int32_t n_lead,
+                            int32_t page_size, int32_t* chunk, int32_t* plan) {
+  if (!seq_lens || !chunk || !plan || n < 1 || n > kMaxBatch || n_kv < 1 || page_size < 1 || n_lead < n * n_kv ||
+      n_tasks < n_lead)
     return fail(MK_ERR_INVALID_ARG, "bad attention plan arguments");
   int32_t lens1[kMaxBatch];
   for (int b = 0; b < n; ++b) {
     if (seq_lens[b] < 0) return fail(MK_ERR_INVALID_ARG, "negative seq_len");
     lens1[b] = seq_lens[b] + 1;
   }
-  const int64_t C = attn_chunk_len(lens1, n, n_kv, n_tasks, page_size);
+  const int64_t C = attn_chunk_len(lens1, n, n_kv, n_tasks - n_lead + n * n_kv, page_size);
   *chunk = (int32_t)C;
   for (int i = 0; i < n_tasks; ++i) {
-    int b, g, t0, t1, first, nch;
-    if (attn_chunk_of(lens1, n, n_kv, C, i, &b, &g, &t0, &t1, &first, &nch)) {
+    int b, g, t0, t1, first, nch, ch;
+    if (attn_task_chunk(lens1, n, n_kv, C, i, n_lead, &b, &g, &t0, &t1, &first, &nch, &ch)) {
       plan[4 * i + 0] = b;
       plan[4 * i + 1] = g;
       plan[4 * i + 2] = t0;

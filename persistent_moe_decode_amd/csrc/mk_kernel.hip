@@ -9,7 +9,8 @@
 // fan-in).  Task bodies:
 //   PRE     RMSNorm of the residual, then rows of [Wq; Wk; Wv] or of the router;
 //   ATTN    one chunk of paged split-KV attention for a (sequence, kv head);
-//           the last chunk to finish merges all chunks (log-sum-exp combine);
+//           the segment's lead (which took its first chunk) merges all
+//           chunks once the others have reported (log-sum-exp combine);
 //   GATEUP  top-k of the router logits, then rows of the selected experts'
 //           gate and up projections and SwiGLU;
 //   OUT     rows of Wo and of the selected experts' down projections, weighted
@@ -270,6 +271,37 @@ DEV bool arrive_last(uint32_t* ticket, uint32_t count, int32_t* slot) {
   return *slot != 0;
 }
 
+// Wave 0 polls a ticket word until it holds `want`, then resets it for the
+// next step; bounded like wait_counter.  Returns false when the grid is
+// aborting or the wait timed out.
+DEV bool wait_ticket(const KArgs& a, uint32_t* ticket, uint32_t want, int task, int32_t* slot) {
+  if (tid() < 64) {
+    const int lane = tid();
+    int ok = aborting(a) ? 0 : 1;
+    if (ok) {
+      const uint64_t t0 = wall_clock64();
+      uint32_t it = 0;
+      while (__shfl(lane == 0 ? ld_coh(ticket) : 0u, 0) != want) {
+        __builtin_amdgcn_s_sleep(1);
+        if ((++it & 31) == 0) {
+          int stop = 0;
+          if (lane == 0) stop = aborting(a) ? 1 : (wall_clock64() - t0 > a.spin_limit_ticks ? 2 : 0);
+          stop = __shfl(stop, 0);
+          if (stop) {
+            if (lane == 0 && stop == 2) raise_error(a, MK_ERR_DEVICE_TIMEOUT, task, -1);
+            ok = 0;
+            break;
+          }
+        }
+      }
+      if (ok && lane == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (lane == 0) *slot = ok;
+  }
+  __syncthreads();
+  return *slot != 0;
+}
+
 // ---------------------------------------------------------------------------
 // inputs
 
@@ -336,6 +368,29 @@ DEV uint8_t* norm_stage(const KArgs& a, uint16_t* xs) {
   return (uint8_t*)xs + (((size_t)a.max_batch * a.H * 2 + 255) & ~(size_t)255);
 }
 
+// Elements 4c .. 4c + 3 of rows 0 .. n - 1 of the staged input (fp32 rows,
+// or bf16 embedding rows at layer 0); rows >= n read as zero.
+DEV void norm_row4(const uint8_t* stage, bool emb, int H, int n, int c, float (&v)[kMaxBatch][4]) {
+#pragma unroll
+  for (int b = 0; b < kMaxBatch; ++b) {
+    if (b < n && emb) {
+      const uint2 u = *(const uint2*)(stage + ((size_t)b * H + 4 * c) * 2);
+      v[b][0] = bf2f(u.x & 0xffffu);
+      v[b][1] = bf2f(u.x >> 16);
+      v[b][2] = bf2f(u.y & 0xffffu);
+      v[b][3] = bf2f(u.y >> 16);
+    } else if (b < n) {
+      const float4 f = *(const float4*)(stage + ((size_t)b * H + 4 * c) * 4);
+      v[b][0] = f.x;
+      v[b][1] = f.y;
+      v[b][2] = f.z;
+      v[b][3] = f.w;
+    } else {
+      v[b][0] = v[b][1] = v[b][2] = v[b][3] = 0.f;
+    }
+  }
+}
+
 // mk >= 0: trace mark mk of the task once the inputs are in LDS.
 DEV void norm_inputs(const KArgs& a, int layer, const gu16* gain, uint16_t* xs, double* red8, int task, int mk) {
   const int H = a.H, n = a.n, lane = tid() & 63, wave = tid() >> 6;
@@ -355,25 +410,80 @@ DEV void norm_inputs(const KArgs& a, int layer, const gu16* gain, uint16_t* xs, 
   }
   __syncthreads();
   if (mk >= 0) mark(a, task, mk);
-  const float* xf = (const float*)stage;
-  const uint16_t* xb = (const uint16_t*)stage;
-  for (int b = 0; b < n; ++b) {
-    double ss = 0.0;
-    for (int i = tid(); i < H; i += kThreads) {
-      const double v = emb ? (double)bf2f(xb[(size_t)b * H + i]) : (double)xf[(size_t)b * H + i];
-      ss += v * v;
+  if (n == 1) {
+    // one row: thread t takes elements t, t + 512, ... (measured faster than
+    // the vector path below at one row)
+    const float* xf = (const float*)stage;
+    const uint16_t* xb = (const uint16_t*)stage;
+    for (int b = 0; b < n; ++b) {
+      double ss = 0.0;
+      for (int i = tid(); i < H; i += kThreads) {
+        const double v = emb ? (double)bf2f(xb[(size_t)b * H + i]) : (double)xf[(size_t)b * H + i];
+        ss += v * v;
+      }
+      for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+      if (lane == 0) red8[wave * kMaxBatch + b] = ss;
     }
-    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
-    if (lane == 0) red8[wave * kMaxBatch + b] = ss;
-  }
-  __syncthreads();
-  for (int b = 0; b < n; ++b) {
-    double tot = 0.0;
-    for (int w = 0; w < kWaves; ++w) tot += red8[w * kMaxBatch + b];
-    const double inv = 1.0 / sqrt(tot / (double)H + (double)a.eps);
-    for (int i = tid(); i < H; i += kThreads) {
-      const double v = emb ? (double)bf2f(xb[(size_t)b * H + i]) : (double)xf[(size_t)b * H + i];
-      xs[(size_t)b * H + i] = d2bf(v * inv * (double)bf2f(gs[i]));
+    __syncthreads();
+    for (int b = 0; b < n; ++b) {
+      double tot = 0.0;
+      for (int w = 0; w < kWaves; ++w) tot += red8[w * kMaxBatch + b];
+      const double inv = 1.0 / sqrt(tot / (double)H + (double)a.eps);
+      for (int i = tid(); i < H; i += kThreads) {
+        const double v = emb ? (double)bf2f(xb[(size_t)b * H + i]) : (double)xf[(size_t)b * H + i];
+        xs[(size_t)b * H + i] = d2bf(v * inv * (double)bf2f(gs[i]));
+      }
+    }
+  } else {
+    // thread t takes elements 4c .. 4c + 3 of every row, c = t, t + 512, ...
+    // (H is a multiple of 128); the loads of all rows are issued before any
+    // arithmetic, so the LDS round trips overlap instead of adding up
+    double ss[kMaxBatch];
+#pragma unroll
+    for (int b = 0; b < kMaxBatch; ++b) ss[b] = 0.0;
+    for (int c = tid(); 4 * c < H; c += kThreads) {
+      float v[kMaxBatch][4];
+      norm_row4(stage, emb, H, n, c, v);
+#pragma unroll
+      for (int b = 0; b < kMaxBatch; ++b)
+        if (b < n)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ss[b] += (double)v[b][e] * (double)v[b][e];
+    }
+#pragma unroll
+    for (int b = 0; b < kMaxBatch; ++b) {
+      if (b >= n) break;
+      double t = ss[b];
+      for (int m = 32; m >= 1; m >>= 1) t += __shfl_xor(t, m);
+      if (lane == 0) red8[wave * kMaxBatch + b] = t;
+    }
+    __syncthreads();
+    // lane b < n of each wave works out row b's scale (one division per wave,
+    // whatever the batch), the others receive it by shuffle
+    double my = 0.0;
+    if (lane < n) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) my += red8[w * kMaxBatch + lane];
+      my = 1.0 / sqrt(my / (double)H + (double)a.eps);
+    }
+    double inv[kMaxBatch];
+#pragma unroll
+    for (int b = 0; b < kMaxBatch; ++b) inv[b] = b < n ? __shfl(my, b) : 0.0;
+    for (int c = tid(); 4 * c < H; c += kThreads) {
+      float v[kMaxBatch][4];
+      norm_row4(stage, emb, H, n, c, v);
+      const uint2 gw = *(const uint2*)(gs + 4 * c);
+      const double g4[4] = {(double)bf2f(gw.x & 0xffffu), (double)bf2f(gw.x >> 16), (double)bf2f(gw.y & 0xffffu),
+                            (double)bf2f(gw.y >> 16)};
+#pragma unroll
+      for (int b = 0; b < kMaxBatch; ++b) {
+        if (b >= n) break;
+        uint16_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = d2bf((double)v[b][e] * inv[b] * g4[e]);
+        *(uint2*)(xs + (size_t)b * H + 4 * c) =
+            make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
+      }
     }
   }
   __syncthreads();
@@ -450,10 +560,77 @@ DEV void rowdots_generic(int K, int i0, int i1, int maxnx, const Job& job) {
   }
 }
 
+// Dense jobs (every row dotted with all n >= 2 token vectors) on the matrix
+// cores: a wave takes a tile of 16 rows and contracts it with the n token
+// vectors, v_mfma_f32_16x16x32_bf16 per 32 columns:
+//   D[16 rows][16 tokens] += W[16 rows][32] * X^T[32][16 tokens]
+// lane l holds row l % 16 of the weights and token l % 16 of the inputs at
+// columns 8 * (l / 16) .. + 7 of each 32-column block (tokens >= n are zero),
+// and receives D[4 * (l / 16) + q][l % 16] in component q.  Weight rows
+// stream from HBM, eight 16-byte loads per lane in flight per batch.  With
+// fewer tiles than waves the columns are split into kp parts whose partial
+// tiles are summed in LDS (red: kMfmaRedBytes of region C) in part order.
+constexpr int kMfmaBatch = 8;                   // 32-column blocks per load batch
+
+template <class Job>
+DEV void rowdots_mfma(int K, int i0, int i1, int n, const Job& job, float* red) {
+  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  const int lane = tid() & 63, wave = tid() >> 6;
+  const int r = lane & 15, grp = lane >> 4;
+  const int ntile = (i1 - i0 + 15) / 16;
+  int kp = 1;
+  while (red && kp < 8 && ntile * kp < kWaves && (K / (2 * kp)) % (32 * kMfmaBatch) == 0) kp *= 2;
+  const int kl = K / kp;                        // columns per part
+  const int nitem = ntile * kp;
+  const uint4* xb = job.x(i0, r < n ? r : 0);   // token r's input vector (LDS)
+  for (int it = wave; it < nitem; it += kWaves) {
+    const int tile = it / kp, part = it - tile * kp;
+    const int row = i0 + tile * 16 + r;
+    const gu4* wr = job.row(row < i1 ? row : i0) + (size_t)part * (kl / 8) + grp;
+    const uint4* xr = xb + (size_t)part * (kl / 8) + grp;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < kl / 32; kb += kMfmaBatch) {
+      uint4 wa[kMfmaBatch];
+#pragma unroll
+      for (int u = 0; u < kMfmaBatch; ++u) wa[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(wr + 4 * (kb + u)));
+#pragma unroll
+      for (int u = 0; u < kMfmaBatch; ++u) {
+        const uint4 xv = r < n ? xr[4 * (kb + u)] : make_uint4(0, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wa[u]),
+                                                      __builtin_bit_cast(bf16x8_t, xv), acc, 0, 0, 0);
+      }
+    }
+    if (kp == 1) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int rq = i0 + tile * 16 + 4 * grp + q;
+        if (rq < i1 && r < n) job.emit(rq, r, acc[q]);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) red[it * 256 + (4 * grp + q) * 16 + r] = acc[q];
+    }
+  }
+  if (kp > 1) {
+    __syncthreads();
+    for (int e = tid(); e < ntile * 256; e += kThreads) {
+      const int tile = e >> 8, rt = (e >> 4) & 15, tok = e & 15;
+      const int rq = i0 + tile * 16 + rt;
+      float v = 0.f;
+      for (int part = 0; part < kp; ++part) v += red[(tile * kp + part) * 256 + rt * 16 + tok];
+      if (rq < i1 && tok < n) job.emit(rq, tok, v);
+    }
+    __syncthreads();
+  }
+}
+
 template <bool FromLds, class Job>
 DEV void rowdots_range(int K, int i0, int i1, int maxnx, const Job& job) {
   const int nj = i1 - i0;
   if (nj <= 0 || maxnx <= 0) return;
+  if constexpr (!FromLds && Job::kDense)
+    if (maxnx >= 2 && K % (32 * kMfmaBatch) == 0) return rowdots_mfma(K, i0, i1, maxnx, job, job.red);
   const int ch = K / 8;  // 16-byte chunks per row
   if (nj <= 8 && ch == 512) return rowdots<64, 8, FromLds>(i0, i1, maxnx, job);
   if (nj <= 8 && ch == 256) return rowdots<64, 4, FromLds>(i0, i1, maxnx, job);
@@ -683,7 +860,8 @@ DEV int task_prefetch(const KArgs& a, const Task& t, const Lds& s, int qi) {
   } else {
     return 0;
   }
-  const int npf = min(nrows, a.pf_bytes / (K * 2));
+  // (with several tokens the rows go to the matrix cores straight from HBM)
+  const int npf = a.n == 1 ? min(nrows, a.pf_bytes / (K * 2)) : 0;
   if (npf > 0) prefetch_to_lds(src, s.P, npf * K * 2);
   return npf;
 }
@@ -695,8 +873,10 @@ DEV void prefetch_wait() {
 }
 
 struct JobPre {
+  static constexpr bool kDense = true;  // every row is dotted with every token
   const gu16* W;
   const AS_LDS uint16_t* pf;  // prefetched rows [0, npf)
+  float* red;                 // LDS for the matrix-core path's partial tiles (region C)
   int npf;
   int r0, K;
   const uint16_t* xs;
@@ -720,6 +900,7 @@ TASK void task_pre(const KArgs& a, const Task& t, const Lds& s, int qi, int npf)
   j.xs = xs;
   j.pf = (const AS_LDS uint16_t*)s.P;
   j.npf = npf;
+  j.red = (float*)s.C;
   if (t.r0 < a.qkv_rows) {
     j.W = wptr(a, widx(l, WL_QKV));
     j.r0 = t.r0;
@@ -990,9 +1171,10 @@ DEV void attn_wave(const KArgs& a, const Lds& s, int qi, const uint16_t* q_s, in
 }
 
 // The chunk of split task t.idx, from the step's sequence lengths only, so it
-// runs before the task's wait; thread 0 writes it to plan = flags[2..9].
+// runs before the task's wait; thread 0 writes it to plan = flags[2..9] and
+// its chunk number to flags[17].
 DEV void attn_plan(const KArgs& a, const Task& t, const Lds& s, int qi) {
-  int32_t* plan = s.flags + 2;  // b, g, t0, t1, first, nch, ok, p
+  int32_t* plan = s.flags + 2;  // b, g, t0, t1, first, nch, ok, p; [15]: chunk number
   if (tid() == 0) {
     int32_t lens1[kMaxBatch];
     const int cap = a.max_pages * a.ps;
@@ -1005,15 +1187,17 @@ DEV void attn_plan(const KArgs& a, const Task& t, const Lds& s, int qi) {
       }
       lens1[b] = p + 1;
     }
-    const int64_t C = attn_chunk_len(lens1, a.n, a.nkv, a.n_attn, a.ps);
-    int b = 0, g = 0, t0 = 0, t1 = 0, first = 0, nch = 0;
-    const bool ok = attn_chunk_of(lens1, a.n, a.nkv, C, t.idx, &b, &g, &t0, &t1, &first, &nch);
+    const int nlead = a.max_batch * a.nkv;
+    const int64_t C = attn_chunk_len(lens1, a.n, a.nkv, a.n_attn - nlead + a.n * a.nkv, a.ps);
+    int b = 0, g = 0, t0 = 0, t1 = 0, first = 0, nch = 0, ch = 0;
+    const bool ok = attn_task_chunk(lens1, a.n, a.nkv, C, t.idx, nlead, &b, &g, &t0, &t1, &first, &nch, &ch);
     plan[0] = b; plan[1] = g; plan[2] = t0; plan[3] = t1; plan[4] = first; plan[5] = nch; plan[6] = ok;
     plan[7] = lens1[ok ? b : 0] - 1;
+    plan[15] = ch;
   }
 }
 
-// Last chunk of (b, g) merges all chunks j of the segment:
+// The lead of segment (b, g) merges all chunks j of the segment:
 //   o_h = sum_j e^(m_jh - M_h) o_jh / sum_j e^(m_jh - M_h) l_jh,  M_h = max_j m_jh.
 // Thread (slice sl, float4 f) takes chunks sl, sl + S, ...; slices are summed
 // in a fixed order.  When all partials fit in region P they are copied there
@@ -1205,7 +1389,8 @@ DEV void attn_task(const KArgs& a, const Task& t, const Lds& s, int qi) {
   __syncthreads();
   // this chunk's partial: the waves' results merged, as [G][D] outputs, G maxima, G sums
   const int GD = G * D, CS = attn_part_stride(G, D);
-  float* part = a.attn_part + ((size_t)l * a.n_attn + t.idx) * CS;
+  const int chunk = plan[15];
+  float* part = a.attn_part + ((size_t)l * a.n_attn + chunk) * CS;
   for (int e4 = tid(); e4 < GD / 4; e4 += kThreads) {
     const int hh = 4 * e4 / D;
     float M = kNegInf;
@@ -1233,11 +1418,22 @@ DEV void attn_task(const KArgs& a, const Task& t, const Lds& s, int qi) {
   }
   uint32_t* ticket = a.tickets + ((size_t)l * a.max_batch + b) * a.nkv + g;
   mark(a, qi, 3);
-  if (arrive_last(ticket, (uint32_t)nch, s.flags + 10)) {
-    const float* parts = a.attn_part + ((size_t)l * a.n_attn + first) * CS;
-    uint16_t* out = a.attn_out + ((size_t)l * a.max_batch + b) * a.nq * D + (size_t)g * G * D;
-    attn_combine(a, s, parts, nch, out);
+  if (t.idx >= a.max_batch * a.nkv) {
+    // one of the other chunks: report to the segment's ticket (the partial's
+    // stores are complete before the add)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid() == 0) __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
   }
+  // the segment's lead: its own partial's stores complete, then it waits for
+  // the other nch - 1 chunks and merges them all
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (nch > 1 && !wait_ticket(a, ticket, (uint32_t)(nch - 1), qi, s.flags + 10)) return;
+  const float* parts = a.attn_part + ((size_t)l * a.n_attn + first) * CS;
+  uint16_t* out = a.attn_out + ((size_t)l * a.max_batch + b) * a.nq * D + (size_t)g * G * D;
+  attn_combine(a, s, parts, nch, out);
   return;
 }
 
@@ -1251,6 +1447,8 @@ TASK void task_attn(const KArgs& a, const Task& t, const Lds& s, int qi) {
 // nU * I virtual rows, are cut evenly over the gate/up tasks.
 
 struct JobGateUp {
+  static constexpr bool kDense = false;  // rows see a varying token subset
+  float* red = nullptr;
   const TopK* tk;
   const gu16 *wg, *wu;
   const uint16_t* xs;
@@ -1331,6 +1529,8 @@ TASK void task_gateup(const KArgs& a, const Task& t, const Lds& s, int qi, bool 
 // OUT: rows [r0, r1) of the hidden state.
 
 struct JobDown {
+  static constexpr bool kDense = false;  // rows see a varying token subset
+  float* red = nullptr;
   const TopK* tk;
   const gu16* W;
   const uint16_t* hs;
@@ -1357,7 +1557,7 @@ constexpr int kDownGroups = 4;
 // down-projection rows are loaded before the gate/up results are waited for.
 // have_tk: region B still holds this layer's top-k, left there by the gate/up
 // task that ran just before on this compute unit.
-TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have_tk, bool has_next, int& next_pf) {
+TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have_tk) {
   const int l = t.layer, nr = t.r1 - t.r0, n = a.n;
   float* contrib = (float*)s.C;  // [out_rows_max][maxB*topk]
   const int maxBK = a.max_batch * a.topk;
@@ -1404,13 +1604,6 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool hav
   copy_coh_to_lds(xs, a.h + (size_t)l * a.max_batch * a.topk * a.I, n * a.topk * a.I * 2);
   prefetch_wait();
   mark(a, qi, 0);
-  // region P is idle from here on: the next task's weight tile starts
-  // streaming in now, while the down rows are computed (its copy is then not
-  // in the way of that task's own poll and input loads)
-  if (has_next) {
-    const Task tn = a.tasks[qi + 1];
-    if (tn.op == OP_PRE) next_pf = task_prefetch(a, tn, s, qi + 1);
-  }
   // expert down projections: the register rows, then the rest from HBM
   const int mt = tk->maxtok;
 #pragma unroll
@@ -1457,7 +1650,7 @@ constexpr int kWoC = 16;
 TASK void task_wo(const KArgs& a, const Task& t, const Lds& s, int qi, int npf) {
   const int l = t.layer, AD = a.nq * a.d, nr = t.r1 - t.r0, n = a.n;
   const int lane = tid() & 63, wave = tid() >> 6, li = lane & 31;
-  const int nreg = AD == 32 * kWoC * 8 ? min(nr - npf, (kWaves - 1) * 2) : 0;
+  const int nreg = AD == 32 * kWoC * 8 && n == 1 ? min(nr - npf, (kWaves - 1) * 2) : 0;
   const int ir = npf + (wave >= 1 ? (wave - 1) * 2 + (lane >> 5) : nreg);  // this lane's register row
   const bool act = ir < npf + nreg;
   const gu16* W = wptr(a, widx(l, WL_O));
@@ -1475,6 +1668,7 @@ TASK void task_wo(const KArgs& a, const Task& t, const Lds& s, int qi, int npf) 
   JobPre j;
   j.pf = (const AS_LDS uint16_t*)s.P;
   j.npf = npf;
+  j.red = (float*)s.C;
   j.W = W;
   j.r0 = t.r0;
   j.K = AD;
@@ -1498,6 +1692,8 @@ TASK void task_wo(const KArgs& a, const Task& t, const Lds& s, int qi, int npf) 
 // LMHEAD: rows [r0, r1) of the vocabulary, then the greedy argmax.
 
 struct JobLM {
+  static constexpr bool kDense = true;
+  float* red = nullptr;  // region C holds the logits for the argmax: no column split
   const gu16* W;
   int r0, K, V, maxB;
   const uint16_t* xs;
@@ -1609,13 +1805,12 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a)
   __syncthreads();
   int xs_layer = -1;                 // layer whose normalized input region A holds
   int tk_layer = -1;                 // layer whose top-k region B holds
-  int pf_q = -1, pf_n = 0;           // a task whose weight tile an earlier task started, and its rows
   for (int q = q0; q < q1; ++q) {
     const Task t = a.tasks[q];
     uint64_t t_fetch = 0, t_ready = 0;
     if (a.trace && tid() == 0) t_fetch = wall_clock64();
     // immutable weights start streaming into LDS before the inputs are ready
-    const int npf = pf_q == q ? pf_n : task_prefetch(a, t, s, q);
+    const int npf = task_prefetch(a, t, s, q);
     // attention, Wo and output tasks wait inside, once their loads are in flight
     const bool own_wait = t.op == OP_ATTN || t.op == OP_OUT || t.op == OP_WO;
     bool ok = own_wait || wait_counter(a, t.wait[0], t.fanin[0], q, s.flags + 0);
@@ -1626,14 +1821,7 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a)
         case OP_PRE: task_pre(a, t, s, q, npf); break;
         case OP_ATTN: task_attn(a, t, s, q); break;
         case OP_GATEUP: task_gateup(a, t, s, q, xs_layer == t.layer); break;
-        case OP_OUT: {
-          int nx = -1;
-          task_out(a, t, s, q, tk_layer == t.layer, q + 1 < q1, nx);
-          if (nx >= 0) {
-            pf_q = q + 1;
-            pf_n = nx;
-          }
-        } break;
+        case OP_OUT: task_out(a, t, s, q, tk_layer == t.layer); break;
         case OP_WO: task_wo(a, t, s, q, npf); break;
         case OP_LMHEAD: task_lmhead(a, t, s, q); break;
         default: break;

@@ -22,13 +22,14 @@ constexpr int kMaxGroup = 8;       // q heads per kv head
 constexpr int kTaskInts = 32;      // 128-byte descriptor
 constexpr int kGuPass = 256;       // gate/up virtual rows per pass of one task
 constexpr int kLmPass = 512;       // LM head rows per pass of one task
+constexpr int kMfmaRedBytes = 16 * 1024; // region C bytes for the matrix-core path's partial tiles (batch >= 2)
 constexpr int kTraceWords = 8;     // per task: fetch, ready, 4 phase marks, done, spare
 constexpr int kLdsB = 8192;        // LDS region B: top-k state, flags, reductions, router logits
 constexpr int kTopKScratch = 4 * kMaxExperts + kMaxBatch * kMaxExperts + kWaves * 4 * kMaxTopK * 4;  // region C bytes the top-k borrows
 
 enum Op : int32_t {
   OP_PRE = 1,     // RMSNorm + rows of [Wq; Wk; Wv] or of the router
-  OP_ATTN = 2,    // paged split-KV attention chunk; last arriver of a (seq, kv head) combines
+  OP_ATTN = 2,    // paged split-KV attention chunk; a (seq, kv head) segment's lead combines
   OP_GATEUP = 3,  // router top-k + rows of the selected experts' gate/up + SwiGLU
   OP_OUT = 4,     // rows of the selected experts' down projection + residual update
   OP_LMHEAD = 5,  // final RMSNorm + LM head rows; last arriver takes the argmax
@@ -142,7 +143,7 @@ MK_HD int64_t attn_count_chunks(const int32_t* lens1, int n, int nkv, int64_t C)
 }
 
 // lens1[b] = positions of sequence b (seq_len + 1, already clamped >= 1).
-// Requires n * nkv <= n_tasks.
+// Requires n * nkv <= n_tasks.  The number of chunks is at most n_tasks.
 MK_HD int64_t attn_chunk_len(const int32_t* lens1, int n, int nkv, int n_tasks, int ps) {
   int64_t maxlen = 1;
   for (int b = 0; b < n; ++b) maxlen = lens1[b] > maxlen ? lens1[b] : maxlen;
@@ -155,24 +156,47 @@ MK_HD int64_t attn_chunk_len(const int32_t* lens1, int n, int nkv, int n_tasks, 
   return lo * ps;
 }
 
-// Chunk i -> (b, g, t0, t1); returns false for an idle task.
-MK_HD bool attn_chunk_of(const int32_t* lens1, int n, int nkv, int64_t C, int i, int* b, int* g, int* t0, int* t1,
-                         int* first_chunk, int* nchunks) {
+// Split task i -> chunk.  Tasks 0 .. nlead - 1 are the segment leads: task
+// m < n * nkv takes the first chunk of segment m (b = m / nkv, g = m % nkv)
+// and later merges the segment; tasks nlead .. take the other chunks of all
+// segments in chunk order.  *chunk is the chunk's number in segment order
+// (segment b major, g minor; the segment's chunks are first .. first + nch - 1).
+// With n_tasks split tasks, chunk lengths come from
+// attn_chunk_len(..., n_tasks - nlead + n * nkv, ...), so the non-first
+// chunks fit in tasks nlead .. n_tasks - 1.  Returns false for an idle task.
+MK_HD bool attn_task_chunk(const int32_t* lens1, int n, int nkv, int64_t C, int i, int nlead, int* b, int* g, int* t0,
+                           int* t1, int* first_chunk, int* nchunks, int* chunk) {
   int64_t base = 0;
+  if (i < nlead) {
+    if (i >= n * nkv) return false;
+    const int bb = i / nkv;
+    for (int s = 0; s < i; ++s) base += (lens1[s / nkv] + C - 1) / C;
+    *b = bb;
+    *g = i % nkv;
+    *t0 = 0;
+    *t1 = (int)(C < lens1[bb] ? C : lens1[bb]);
+    *first_chunk = (int)base;
+    *nchunks = (int)((lens1[bb] + C - 1) / C);
+    *chunk = (int)base;
+    return true;
+  }
+  int64_t k = i - nlead;
   for (int bb = 0; bb < n; ++bb) {
-    int64_t per = (lens1[bb] + C - 1) / C;
+    const int64_t per = (lens1[bb] + C - 1) / C;
     for (int gg = 0; gg < nkv; ++gg) {
-      if (i < base + per) {
-        int64_t j = i - base;
+      if (k < per - 1) {
+        const int64_t j = k + 1;
         *b = bb;
         *g = gg;
         *t0 = (int)(j * C);
-        int64_t e = (j + 1) * C;
+        const int64_t e = (j + 1) * C;
         *t1 = (int)(e < lens1[bb] ? e : lens1[bb]);
         *first_chunk = (int)base;
         *nchunks = (int)per;
+        *chunk = (int)(base + j);
         return true;
       }
+      k -= per - 1;
       base += per;
     }
   }

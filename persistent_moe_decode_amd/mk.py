@@ -84,7 +84,7 @@ def lib():
         "mk_copy_schedule": [P, pi32, I64, pi32, I64],
         "mk_validate_schedule": [P, pi32],
         "mk_simulate_table": [pi32, I32, pi32, I32, I32, pi32],
-        "mk_attn_plan": [pi32, I32, I32, I32, I32, pi32, pi32],
+        "mk_attn_plan": [pi32, I32, I32, I32, I32, I32, pi32, pi32],
         "mk_get_ws_offsets": [P, ctypes.POINTER(WsOffsets)],
     }
     for name, args in sig.items():
@@ -209,12 +209,16 @@ def simulate_table(tasks, qoff, n_counters: int):
     return code, done.value
 
 
-def attn_plan(seq_lens, n_kv: int, n_tasks: int, page_size: int = 16):
-    """Host mirror of the kernel's runtime attention split: (chunk, plan[n_tasks][4])."""
+def attn_plan(seq_lens, n_kv: int, n_tasks: int, n_lead: int = -1, page_size: int = 16):
+    """Host mirror of the kernel's runtime attention split: (chunk, plan[n_tasks][4]).
+
+    n_lead: split tasks that lead a (sequence, kv head) segment (default: one per segment)."""
     import numpy as np
     sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
     plan = np.zeros((n_tasks, 4), dtype=np.int32)
     chunk = ctypes.c_int32()
-    check(lib().mk_attn_plan(_i32p(sl), sl.size, n_kv, n_tasks, page_size, ctypes.byref(chunk), _i32p(plan)),
-          "mk_attn_plan")
+    if n_lead < 0:
+        n_lead = sl.size * n_kv
+    check(lib().mk_attn_plan(_i32p(sl), sl.size, n_kv, n_tasks, n_lead, page_size, ctypes.byref(chunk),
+                             _i32p(plan)), "mk_attn_plan")
     return chunk.value, plan

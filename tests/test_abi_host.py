@@ -56,7 +56,7 @@ def test_calls_out_of_order_fail_cleanly():
 def test_schedule_builds_and_simulates(name, ncu):
     w = synth.workload(name)
     c = _ctx(w.shape, w.batch, w.max_pages_per_seq, w.num_pages)
-    if ncu < w.batch * w.shape.n_kv_heads + 2:
+    if ncu < w.batch * w.shape.n_kv_heads + 3:
         with pytest.raises(mk.MkError):
             c.build_schedule(ncu, int(np.mean(w.context)))
         return
@@ -70,7 +70,7 @@ def test_schedule_builds_and_simulates(name, ncu):
     assert np.sum(ops == OP_ATTN) == L * info.n_attn
     assert np.sum(ops == OP_GATEUP) == L * info.n_gateup
     assert info.n_attn + info.n_gateup == ncu
-    assert w.batch * w.shape.n_kv_heads <= info.n_attn <= ncu - 2
+    assert w.batch * w.shape.n_kv_heads < info.n_attn <= ncu - 2
     # attention units run their chunk and Wo rows, no stage-1 or output rows; every other
     # unit one stage-1, one gate/up and one output task
     for q in range(ncu):
@@ -217,12 +217,12 @@ def test_router_rows_have_their_own_units():
     assert np.all(gu[:, F_WAIT0] == routers[0, F_SIGNAL]) and np.all(gu[:, F_FAN0] == len(routers))
 
 
-@pytest.mark.parametrize("lens,nkv,ntasks", [
-    ([0], 4, 64), ([8192], 4, 64), ([8192], 4, 85), ([15], 2, 64), ([16], 2, 64), ([17], 2, 3),
-    ([262144], 4, 256), ([1024, 32768, 7, 0, 16, 15, 17, 5000], 4, 40), ([3, 3, 3], 1, 3),
+@pytest.mark.parametrize("lens,nkv,ntasks,nlead", [
+    ([0], 4, 64, 4), ([8192], 4, 64, 4), ([8192], 4, 86, 4), ([8192], 4, 86, 32), ([15], 2, 64, 2), ([16], 2, 64, 16),
+    ([17], 2, 3, 2), ([262144], 4, 256, 4), ([1024, 32768, 7, 0, 16, 15, 17, 5000], 4, 40, 32), ([3, 3, 3], 1, 3, 3),
 ])
-def test_attention_split_partitions_every_segment(lens, nkv, ntasks):
-    C, plan = mk.attn_plan(lens, nkv, ntasks)
+def test_attention_split_partitions_every_segment(lens, nkv, ntasks, nlead):
+    C, plan = mk.attn_plan(lens, nkv, ntasks, nlead)
     assert C % 16 == 0 and C >= 16
     seen = {}
     for i, (b, g, t0, t1) in enumerate(plan):
@@ -233,15 +233,24 @@ def test_attention_split_partitions_every_segment(lens, nkv, ntasks):
     assert len(seen) == len(lens) * nkv
     for (b, g), chunks in seen.items():
         chunks.sort()
-        assert chunks[0][0] == 0 and chunks[-1][1] == lens[b] + 1
+        # the lead of segment m = b * nkv + g holds its first chunk; the others follow in
+        # consecutive task numbers past the leads
+        assert chunks[0][0] == 0 and chunks[0][2] == b * nkv + g and chunks[-1][1] == lens[b] + 1
         for (a0, a1, ia), (b0, b1, ib) in zip(chunks, chunks[1:]):
-            assert a1 == b0 and ib == ia + 1          # contiguous, consecutive task numbers
-    # C is the smallest page multiple that fits: one page less would need more than ntasks chunks
+            assert a1 == b0 and ib >= nlead
+        assert [c[2] for c in chunks[1:]] == list(range(chunks[1][2], chunks[1][2] + len(chunks) - 1)) if len(chunks) > 1 else True
+    # lead tasks beyond the segments are idle
+    assert all(plan[i][0] < 0 for i in range(len(lens) * nkv, nlead))
+    # C is the smallest page multiple that fits: one page less would need more than the tasks there are
+    cap = ntasks - nlead + len(lens) * nkv
+    need = lambda c: sum(nkv * -(-(l + 1) // c) for l in lens)
+    assert need(C) <= cap
     if C > 16:
-        need = sum(nkv * -(-(l + 1) // (C - 16)) for l in lens)
-        assert need > ntasks
+        assert need(C - 16) > cap
 
 
 def test_attention_split_rejects_too_few_tasks():
     with pytest.raises(mk.MkError):
         mk.attn_plan([10, 10], 4, 7)
+    with pytest.raises(mk.MkError):
+        mk.attn_plan([10, 10], 4, 9, 7)  # fewer leads than segments
