@@ -13,11 +13,12 @@
 //           chunks once the others have reported (log-sum-exp combine);
 //   GATEUP  top-k of the router logits, then rows of the selected experts'
 //           gate and up projections and SwiGLU;
-//   OUT     rows of Wo and of the selected experts' down projections, weighted
-//           expert sum and residual add (parallel block: x += attn + moe);
+//   OUT     rows of the selected experts' down projections, weighted expert
+//           sum and residual add (parallel block: x += attn + moe);
 //   LMHEAD  final RMSNorm, rows of the LM head, greedy argmax (last arriver).
-// Weight rows stream from HBM with 128-bit loads, lanes accumulate in fp32
-// with v_dot2_f32_bf16, and groups of lanes reduce through DPP.
+// Weight rows stream from HBM with 128-bit loads; at batch 1 lanes accumulate
+// in fp32 with v_dot2_f32_bf16 and groups of lanes reduce through DPP, at
+// batch >= 2 rows that every token uses run as 16-row matrix-core tiles.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
