@@ -1036,6 +1036,29 @@ DEV void attn_fetch_lds(const Lds& s, AttnPage<D>& P, int npp, int pi, int tb, i
         uint2, vcol ? *(const AS_LDS u32x2_v*)(vb + 2 * ((16 * t + r) * 16 + 4 * grp)) : u32x2_v{0, 0});
 }
 
+// Max / sum over the four 16-lane rows of a wave (lanes l, l ^ 16, l ^ 32,
+// l ^ 48), every lane getting the result, through the gfx950 row-swap
+// instructions: with both operands the same register, permlane16_swap returns
+// (even row, odd row) of each row pair in every lane, permlane32_swap (lower
+// half, upper half); no LDS round trip as with a shuffle.
+DEV float rows4_max(float v) {
+  const uint32_t u = __float_as_uint(v);
+  auto t = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float w = fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+  const uint32_t uw = __float_as_uint(w);
+  auto h = __builtin_amdgcn_permlane32_swap(uw, uw, false, false);
+  return fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+}
+
+DEV float rows4_sum(float v) {
+  const uint32_t u = __float_as_uint(v);
+  auto t = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float w = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+  const uint32_t uw = __float_as_uint(w);
+  auto h = __builtin_amdgcn_permlane32_swap(uw, uw, false, false);
+  return __uint_as_float(h[0]) + __uint_as_float(h[1]);
+}
+
 template <int D>
 DEV void attn_page(const AttnPage<D>& P, const bf16x8_v (&qb)[D / 32], float scale, float& m, float& lsum,
                    float4_v (&o)[D / 16]) {
@@ -1051,8 +1074,7 @@ DEV void attn_page(const AttnPage<D>& P, const bf16x8_v (&qb)[D / 32], float sca
     sv[i] = (4 * grp + i < P.nvalid) ? sacc[i] * scale : kNegInf;  // select: poison slots never enter
     bm = fmaxf(bm, sv[i]);
   }
-  bm = fmaxf(bm, __shfl_xor(bm, 16));
-  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  bm = rows4_max(bm);
   const float mn = fmaxf(m, bm);
   const float alpha = mn == kNegInf ? 1.f : __expf(m - mn);
   // p = p_hi + p_lo, both bf16: two MFMAs keep the P*V product at ~2^-16 relative
@@ -1154,8 +1176,7 @@ DEV void attn_wave(const KArgs& a, const Lds& s, int qi, const uint16_t* q_s, in
     cur = nxt;
   }
   // per-head totals over the 4 lane groups, then this wave's part of the merge area
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  lsum = rows4_sum(lsum);
   if (grp == 0 && r < G) {
     mrg.m[wave * kMaxGroup + r] = m;
     mrg.l[wave * kMaxGroup + r] = lsum;
