@@ -254,3 +254,34 @@ def test_attention_split_rejects_too_few_tasks():
         mk.attn_plan([10, 10], 4, 7)
     with pytest.raises(mk.MkError):
         mk.attn_plan([10, 10], 4, 9, 7)  # fewer leads than segments
+
+
+def test_attention_split_random_shapes():
+    """Seeded sweep: every segment's positions covered once, in page-aligned chunks, first chunk on its lead."""
+    rng = np.random.default_rng(7)
+    for _ in range(300):
+        n = int(rng.integers(1, 9))
+        nkv = int(rng.integers(1, 5))
+        nseg = n * nkv
+        nlead = int(rng.integers(nseg, 8 * nkv + 1)) if nseg < 8 * nkv else nseg
+        ntasks = nlead + int(rng.integers(0, 120))
+        lens = [int(x) for x in rng.integers(0, 5000, size=n)]
+        if rng.random() < 0.2:
+            lens[int(rng.integers(0, n))] = 0
+        C, plan = mk.attn_plan(lens, nkv, ntasks, nlead)
+        assert C % 16 == 0 and C >= 16
+        covered = {}
+        for i, (b, g, t0, t1) in enumerate(plan):
+            if b < 0:
+                continue
+            assert 0 <= t0 < t1 <= lens[b] + 1 and t0 % 16 == 0 and t1 - t0 <= C
+            if t0 == 0:
+                assert i == b * nkv + g          # the lead holds the first chunk
+            else:
+                assert i >= nlead
+            covered.setdefault((b, g), []).append((t0, t1))
+        assert len(covered) == nseg
+        for (b, g), ch in covered.items():
+            ch.sort()
+            assert ch[0][0] == 0 and ch[-1][1] == lens[b] + 1
+            assert all(a1 == b0 for (_, a1), (b0, _) in zip(ch, ch[1:]))
