@@ -107,18 +107,65 @@ DEV float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
+template <int CTRL>
+DEV uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+DEV double dpp_d(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint64_t lo = dpp_u<CTRL>((uint32_t)u), hi = dpp_u<CTRL>((uint32_t)(u >> 32));
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
+
+// The gfx950 row swaps: with both operands the same register,
+// permlane16_swap returns (even row, odd row) of each pair of 16-lane rows in
+// every lane, permlane32_swap (lower half, upper half).  Sums of the two, in
+// that order, at VALU speed (no LDS round trip as with a shuffle).
+DEV float xrow16_sum(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto t = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+DEV float xrow32_sum(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto t = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+DEV double xrow_sum_d(double v, bool half) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+  const auto l = half ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false) : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto h = half ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false) : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  const double a = __longlong_as_double((long long)(((uint64_t)h[0] << 32) | l[0]));
+  const double b = __longlong_as_double((long long)(((uint64_t)h[1] << 32) | l[1]));
+  return a + b;
+}
+
 // Sum over aligned groups of N lanes; every lane of a group gets the sum.
 // quad_perm [1,0,3,2] and [2,3,0,1] pair lanes within a quad, row_half_mirror
-// pairs the two quads of 8 lanes, row_mirror the two halves of a 16-lane row.
+// pairs the two quads of 8 lanes, row_mirror the two halves of a 16-lane row;
+// row swaps then pair 16-lane rows and the two halves of the wave.
 template <int N>
 DEV float group_sum(float v) {
   v += dpp<0xB1>(v);
   if (N >= 4) v += dpp<0x4E>(v);
   if (N >= 8) v += dpp<0x141>(v);
   if (N >= 16) v += dpp<0x140>(v);
-  if (N >= 32) v += __shfl_xor(v, 16);
-  if (N >= 64) v += __shfl_xor(v, 32);
+  if (N >= 32) v = xrow16_sum(v);
+  if (N >= 64) v = xrow32_sum(v);
   return v;
+}
+
+// Sum over the whole wave of a double, in every lane.
+DEV double wave_sum_d(double v) {
+  v += dpp_d<0xB1>(v);
+  v += dpp_d<0x4E>(v);
+  v += dpp_d<0x141>(v);
+  v += dpp_d<0x140>(v);
+  v = xrow_sum_d(v, false);
+  return xrow_sum_d(v, true);
 }
 
 // ---------------------------------------------------------------------------
@@ -194,12 +241,17 @@ DEV bool aborting(const KArgs& a) {
 }
 
 // Sum of a counter's sub-counters, in every lane of the calling wave.
+// The sub-counters sit in lanes 0..15 (the wave's first row): DPP sums the
+// row, lane 0 hands the total to the wave.
+static_assert(kSubCounters == 16, "counter_sum sums one 16-lane row");
 DEV uint32_t counter_sum(const KArgs& a, int idx) {
   const int lane = tid() & 63;
   uint32_t v = lane < kSubCounters ? ld_coh(a.flags + (size_t)idx * kCounterWords + lane * kSubStride) : 0u;
-#pragma unroll
-  for (int m = kSubCounters / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return __shfl(v, 0);
+  v += dpp_u<0xB1>(v);
+  v += dpp_u<0x4E>(v);
+  v += dpp_u<0x141>(v);
+  v += dpp_u<0x140>(v);
+  return __builtin_amdgcn_readfirstlane(v);
 }
 
 // Wave 0 polls the counter (relaxed device-coherent loads of its
@@ -422,7 +474,7 @@ DEV void norm_inputs(const KArgs& a, int layer, const gu16* gain, uint16_t* xs, 
         const double v = emb ? (double)bf2f(xb[(size_t)b * H + i]) : (double)xf[(size_t)b * H + i];
         ss += v * v;
       }
-      for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+      ss = wave_sum_d(ss);
       if (lane == 0) red8[wave * kMaxBatch + b] = ss;
     }
     __syncthreads();
@@ -454,8 +506,7 @@ DEV void norm_inputs(const KArgs& a, int layer, const gu16* gain, uint16_t* xs, 
 #pragma unroll
     for (int b = 0; b < kMaxBatch; ++b) {
       if (b >= n) break;
-      double t = ss[b];
-      for (int m = 32; m >= 1; m >>= 1) t += __shfl_xor(t, m);
+      const double t = wave_sum_d(ss[b]);
       if (lane == 0) red8[wave * kMaxBatch + b] = t;
     }
     __syncthreads();
@@ -1050,14 +1101,7 @@ DEV float rows4_max(float v) {
   return fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
 }
 
-DEV float rows4_sum(float v) {
-  const uint32_t u = __float_as_uint(v);
-  auto t = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  const float w = __uint_as_float(t[0]) + __uint_as_float(t[1]);
-  const uint32_t uw = __float_as_uint(w);
-  auto h = __builtin_amdgcn_permlane32_swap(uw, uw, false, false);
-  return __uint_as_float(h[0]) + __uint_as_float(h[1]);
-}
+DEV float rows4_sum(float v) { return xrow32_sum(xrow16_sum(v)); }
 
 template <int D>
 DEV void attn_page(const AttnPage<D>& P, const bf16x8_v (&qb)[D / 32], float scale, float& m, float& lsum,
