@@ -334,7 +334,7 @@ DEV bool wait_ticket(const KArgs& a, uint32_t* ticket, uint32_t want, int task, 
     if (ok) {
       const uint64_t t0 = wall_clock64();
       uint32_t it = 0;
-      while (__shfl(lane == 0 ? ld_coh(ticket) : 0u, 0) != want) {
+      while (__builtin_amdgcn_readfirstlane(ld_coh(ticket)) != want) {
         __builtin_amdgcn_s_sleep(1);
         if ((++it & 31) == 0) {
           int stop = 0;
@@ -520,7 +520,12 @@ DEV void norm_inputs(const KArgs& a, int layer, const gu16* gain, uint16_t* xs, 
     }
     double inv[kMaxBatch];
 #pragma unroll
-    for (int b = 0; b < kMaxBatch; ++b) inv[b] = b < n ? __shfl(my, b) : 0.0;
+    for (int b = 0; b < kMaxBatch; ++b) {
+      const uint64_t u = (uint64_t)__double_as_longlong(my);
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, b);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), b);
+      inv[b] = b < n ? __longlong_as_double((long long)(((uint64_t)hi << 32) | lo)) : 0.0;
+    }
     for (int c = tid(); 4 * c < H; c += kThreads) {
       float v[kMaxBatch][4];
       norm_row4(stage, emb, H, n, c, v);
@@ -835,9 +840,12 @@ DEV void compute_topk(const KArgs& a, int layer, TopK* tk, uint8_t* scratch) {
           if ((m >> bb) & 1) tk->pair[u][t++] = bb * K + eslot[bb * kMaxExperts + e];
       }
     }
-    int mytok = max(__popc(m_lo), __popc(m_hi));
+    // the most tokens any selected expert has (at most kMaxBatch): one ballot per count
+    const int myt = max(__popc(m_lo), __popc(m_hi));
+    int mytok = 0;
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) mytok = max(mytok, __shfl_xor(mytok, m));
+    for (int k = 1; k <= kMaxBatch; ++k)
+      if (__ballot(myt >= k) != 0ull) mytok = k;
     if (lane == 0) {
       tk->nU = c0 + __popcll(b1);
       tk->maxtok = mytok;
