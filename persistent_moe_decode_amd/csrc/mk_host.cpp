@@ -446,7 +446,7 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
   size_t c_gu = (size_t)std::min(c->gu_rows_max, kGuPass) * B * 2 * 4;
   size_t c_out = (size_t)c->out_rows_max * B * f.top_k * 4;  // the experts' contributions to the task's rows
   size_t c_lm = (size_t)std::min(c->lm_rows_max, kLmPass) * B * 4;
-  // attention: the waves' partial results, or (last chunk) the (max, sum) of all chunks plus one float4 per thread
+  // attention: the waves' partial results, or (a segment's lead) the (max, sum) of all chunks plus one float4 per thread
   size_t c_attn = std::max((size_t)kWaves * (group * f.head_dim + 2 * kMaxGroup) * 4,
                            align_up((size_t)n_attn * group * 2 * 4, 16) + (size_t)kThreads * 16);
   const size_t c_mfma = B >= 2 ? (size_t)kMfmaRedBytes : 0;  // partial tiles of split dense rows

@@ -511,7 +511,7 @@ DEV void norm_inputs(const KArgs& a, int layer, const gu16* gain, uint16_t* xs, 
     }
     __syncthreads();
     // lane b < n of each wave works out row b's scale (one division per wave,
-    // whatever the batch), the others receive it by shuffle
+    // whatever the batch), the others read it from that lane
     double my = 0.0;
     if (lane < n) {
 #pragma unroll
