@@ -92,3 +92,13 @@ def test_mid_small_prefetch_region(pf_bytes, monkeypatch):
     monkeypatch.setenv("MK_PREFETCH_BYTES", str(pf_bytes))
     w = synth.Workload(f"mid_pf{pf_bytes}", synth.MID, batch=3, steps=3, context=[2048, 40, 1000])
     _check(parity.run(w, mode="isolated", log=_log))
+
+
+@pytest.mark.parametrize("attn_cus", [13, 40])
+def test_mid_attention_unit_counts(attn_cus, monkeypatch):
+    """Attention units forced to leads + 1 (one unit takes every Wo row and every chunk past a
+    segment's first) and to 40 (larger chunks): same parity bar."""
+    from tests import parity
+    monkeypatch.setenv("MK_ATTN_CUS", str(attn_cus))
+    w = synth.Workload(f"mid_attn{attn_cus}", synth.MID, batch=3, steps=2, context=[1500, 17, 600])
+    _check(parity.run(w, mode="isolated", log=_log))
