@@ -108,38 +108,90 @@ def step_bytes_kernel(shape, seq_lens, distinct):
     return w + kv
 
 
-def cpu_baseline(w, budget_s: float = 25.0):
-    """The CPU oracle, untuned, on a bounded sample: decode steps until ~budget_s of CPU time."""
-    import numpy as np
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_steps(w, W, kv, pt, toks, first_step: int, budget_s: float, max_steps: int, src):
+    """Decode steps of the oracle until budget_s of wall time; returns (steps, wall_s, regen_s, next tokens)."""
+    from oracle import oracle as O
+
+    n, t0 = 0, time.perf_counter()
+    regen0 = src.regen_s
+    while True:
+        lens = [c + first_step + n for c in w.context]
+        out = O.decode_step(W, kv, toks, pt, lens)
+        toks = [int(t) for t in out.next_token]
+        n += 1
+        if time.perf_counter() - t0 > budget_s or n >= max_steps:
+            break
+    return n, time.perf_counter() - t0, src.regen_s - regen0, toks
+
+
+class _TimedSource:
+    """Wraps the oracle's weight source to time regeneration (generator + bf16 -> float64 decode)."""
+
+    def __init__(self, shape):
+        import synth
+        self.shape, self.synth, self.regen_s = shape, synth, 0.0
+
+    def __call__(self, kind, layer, expert):
+        t = time.perf_counter()
+        a = self.synth.weight_bits(self.shape, kind, layer, expert)
+        self.regen_s += time.perf_counter() - t
+        return a
+
+
+def cpu_baseline(w, budget_s: float = 25.0, budget_1t_s: float = 20.0):
+    """The CPU oracle, untuned, on a bounded sample of the same workload.
+
+    One untimed step fills the oracle's weight cache with everything but newly routed experts;
+    then decode steps run until budget_s with every host thread, then until budget_1t_s on one
+    thread (BLAS and OpenMP pools limited to 1).  Weight regeneration (generator plus bf16
+    decode, for experts first routed in a timed step) is timed separately: `value` includes it,
+    `value_excl_regen` does not."""
+    import threadpoolctl
 
     import synth
     from oracle import oracle as O
 
-    W = O.Weights(w.shape, budget_bytes=float(2 ** 36))
+    src = _TimedSource(w.shape)
+    W = O.Weights(w.shape, budget_bytes=float(2 ** 36), source=src)
     pt = w.page_table()
     kv = O.PagedKV(w.shape, w.num_pages)
+    t_kv = time.perf_counter()
     kv.fill_synthetic(pt, w.context)
+    kv_s = time.perf_counter() - t_kv
     toks = [int(w.prompt(b)[w.context[b]]) for b in range(w.batch)]
-    # one untimed step populates the weight cache with everything but newly routed experts
     out = O.decode_step(W, kv, toks, pt, list(w.context))
     toks = [int(t) for t in out.next_token]
-    n, t0 = 0, time.perf_counter()
-    while True:
-        lens = [c + 1 + n for c in w.context]
-        out = O.decode_step(W, kv, toks, pt, lens)
-        toks = [int(t) for t in out.next_token]
-        n += 1
-        if time.perf_counter() - t0 > budget_s or n >= 16:
-            break
-    dt = time.perf_counter() - t0
-    try:
-        import threadpoolctl
-        cores = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
-    except Exception:
-        cores = os.cpu_count() or 1
-    return {"value": round(w.batch * n / dt, 4), "unit": "tok/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{n} decode step(s) of {w.name} (batch {w.batch}, context {w.context[0] if w.batch == 1 else 'ragged'}) "
-                      f"after one warm-up step; float64 numpy, expert weights regenerated when first routed"}
+    pools = threadpoolctl.threadpool_info()
+    threads = max([p.get("num_threads", 1) for p in pools] or [1])
+
+    n, dt, regen, toks = _oracle_steps(w, W, kv, pt, toks, 1, budget_s, 16, src)
+    with threadpoolctl.threadpool_limits(limits=1):
+        n1, dt1, regen1, _ = _oracle_steps(w, W, kv, pt, toks, 1 + n, budget_1t_s, 4, src)
+    B = w.batch
+    return {
+        "value": round(B * n / dt, 4), "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"{n} decode step(s) of {w.name} (batch {B}, context "
+                  f"{w.context[0] if B == 1 else 'ragged'}) after one warm-up step; float64 numpy; "
+                  f"then {n1} step(s) on 1 thread",
+        "value_excl_regen": round(B * n / max(dt - regen, 1e-9), 4),
+        "regen_s": round(regen, 3), "wall_s": round(dt, 3),
+        "value_1thread": round(B * n1 / dt1, 4), "value_1thread_excl_regen": round(B * n1 / max(dt1 - regen1, 1e-9), 4),
+        "regen_1thread_s": round(regen1, 3),
+        "kv_fill_s": round(kv_s, 2),
+        "host_cores": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model(),
+        "thread_pools": {p.get("internal_api", "?"): p.get("num_threads") for p in pools},
+    }
 
 
 def main():
@@ -244,6 +296,14 @@ def main():
         torch.cuda.synchronize(dev)
         log(f"[bench] calibration copy of {2 * n} bytes done")
         del src, dst
+
+    # ordered teardown before anything else runs: the device is idle, the context destroyed and its
+    # buffers released, then libmk.so is unloaded so its HIP code-object unregistration runs now
+    # rather than among the interpreter's exit handlers (after a profiler has finalized)
+    dec.close()
+    del dec, toks, lens_all, ctx
+    from persistent_moe_decode_amd import mk
+    mk.unload()
 
     cpu = None
     if not args.no_cpu:

@@ -74,18 +74,50 @@ typedef struct mk_config {
 } mk_config;
 
 /* Creates a context for one model shape.  Host only, no GPU call.
- * cfg is copied.  *out receives the context (free with mk_destroy). */
+ * cfg is copied.  *out receives the context (free with mk_destroy).
+ * max_batch is part of the shape, not of the schedule: the workspace layout,
+ * the LDS carve-up and the matrix-core tiles are all sized by it, so one
+ * context serves one batch capacity (steps may carry 1..max_batch sequences).
+ * Source: the 30B-total / 3.3B-active MoE decoder served at batch 1 to 8
+ * (latestnews.news, paragraph 1; ainews.surl.tw, paragraph 4). */
 int mk_create(const mk_config* cfg, mk_ctx** out);
 
-/* Builds the static task table (host only, deterministic, integer only) for
- * num_cus persistent workgroups (0 = query the current device), validates it
- * by simulating every queue on the host (deadlock freedom, fan-in of each
- * counter), and reports the size of the device workspace the caller must
- * provide to mk_bind.  ctx_hint is the expected number of cached tokens per
- * sequence; it only decides how many compute units take attention tasks
- * versus expert tasks, never what is computed.  (ainews.surl.tw, paragraph 2:
- * the table of GEMM tiles and attention splits is assigned in advance.) */
-int mk_build_schedule(mk_ctx* ctx, int32_t num_cus, int64_t ctx_hint, size_t* workspace_bytes);
+/* How the static schedule is cut.  All-zero (or a NULL pointer) gives the
+ * defaults; no field changes what a step computes, only which compute unit
+ * computes it and how much is staged in LDS before a wait.
+ *  num_cus: persistent workgroups, one per compute unit (0 = every compute
+ *    unit of the current device, which also sets the LDS capacity from the
+ *    device; otherwise 160 KB is assumed and no GPU call is made).
+ *  attn_units: compute units that run the attention split and the Wo rows
+ *    (0 = from ctx_hint: attention's K/V bytes against the experts' gate/up
+ *    bytes).  Clamped to [max_batch*n_kv_heads + 1, num_cus - 2].
+ *  router_units: stage-1 units that compute the router rows (0 = default).
+ *    Clamped to [1, stage-1 units - 1].
+ *  prefetch_bytes: upper bound on the LDS region that receives weight tiles
+ *    and K/V pages before a task's wait (0 = all LDS left over by the other
+ *    regions; > 0 = at most this many bytes; < 0 = no such region).
+ *  ctx_hint: expected cached tokens per sequence (0 = 4096); used only to
+ *    size attn_units when that is 0. */
+typedef struct mk_schedule_params {
+  int32_t num_cus;
+  int32_t attn_units;
+  int32_t router_units;
+  int32_t prefetch_bytes;
+  int64_t ctx_hint;
+} mk_schedule_params;
+
+/* Fills *p with the defaults (all fields zero). */
+void mk_schedule_params_default(mk_schedule_params* p);
+
+/* Builds the static task table (host only apart from the device query,
+ * deterministic, integer only), validates it by simulating every queue on the
+ * host (deadlock freedom, the fan-in of each counter, signal slots), and
+ * reports the size of the device workspace the caller must provide to
+ * mk_bind.  params may be NULL (defaults).  Source: the host builds a task
+ * table in advance that assigns GEMM tiles and attention splits to the
+ * compute units (ainews.surl.tw, paragraph 2; latestnews.news, paragraph 3);
+ * every descriptor is 32 int32 (aiweekly.co, paragraph 2). */
+int mk_build_schedule(mk_ctx* ctx, const mk_schedule_params* params, size_t* workspace_bytes);
 
 /* Binds caller-owned device buffers and uploads the task table into the
  * workspace on `stream` (synchronizes that stream before returning).

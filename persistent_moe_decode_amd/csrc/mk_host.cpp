@@ -16,7 +16,6 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
-#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -236,9 +235,18 @@ static WsLayout layout_workspace(const mk_ctx* c) {
   return w;
 }
 
-extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, size_t* workspace_bytes) {
+extern "C" void mk_schedule_params_default(mk_schedule_params* p) {
+  if (p) std::memset(p, 0, sizeof *p);
+}
+
+extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, size_t* workspace_bytes) {
   if (!c) return fail(MK_ERR_INVALID_ARG, "null context");
-  if (num_cus < 0 || ctx_hint < 0) return fail(MK_ERR_INVALID_ARG, "negative num_cus or ctx_hint");
+  mk_schedule_params p{};
+  if (params) p = *params;
+  int32_t num_cus = p.num_cus;
+  const int64_t ctx_hint = p.ctx_hint;
+  if (num_cus < 0 || ctx_hint < 0 || p.attn_units < 0 || p.router_units < 0)
+    return fail(MK_ERR_INVALID_ARG, "negative num_cus, ctx_hint, attn_units or router_units");
   const mk_config& f = c->cfg;
   size_t lds_cap = 160 * 1024;
   if (num_cus == 0) {
@@ -265,8 +273,7 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
   const double attn_bytes = 1.5 * hint * B * f.n_kv_heads * f.head_dim * 4.0;
   const double gu_bytes = (double)std::min(E, B * f.top_k) * 2.0 * f.inter * H * 2.0;
   int n_attn = (int)std::lround(ncu * attn_bytes / (attn_bytes + gu_bytes));
-  const char* env = std::getenv("MK_ATTN_CUS");
-  if (env) n_attn = std::atoi(env);
+  if (p.attn_units > 0) n_attn = p.attn_units;
   // attention units 0 .. n_lead - 1 lead a (sequence, kv head) segment each:
   // first chunk and merge, no Wo rows; the others take the remaining chunks
   // and the Wo rows
@@ -290,7 +297,7 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
   const int R1 = qkv_rows + E;
   const int m1 = ncu - n_attn;
   int n_rcu = (int)(((int64_t)m1 * E + R1 - 1) / R1);
-  if (const char* renv = std::getenv("MK_ROUTER_CUS")) n_rcu = std::atoi(renv);
+  if (p.router_units > 0) n_rcu = p.router_units;
   n_rcu = std::min(m1 - 1, std::max(1, n_rcu));
   const int n_qcu = m1 - n_rcu;
   auto pre_rows = [&](int q, int* r0, int* r1) {
@@ -459,8 +466,8 @@ extern "C" int mk_build_schedule(mk_ctx* c, int32_t num_cus, int64_t ctx_hint, s
   // region P: the rest of LDS, for the first weight tile of PRE and OUT tasks
   // (rows of Wqkv / router / Wo) and the first K/V pages of attention chunks
   size_t pf = lds_cap - (size_t)c->lds_p;
-  const char* pf_env = std::getenv("MK_PREFETCH_BYTES");
-  if (pf_env) pf = std::min(pf, (size_t)std::atoll(pf_env));
+  if (p.prefetch_bytes > 0) pf = std::min(pf, (size_t)p.prefetch_bytes);
+  if (p.prefetch_bytes < 0) pf = 0;
   c->pf_bytes = (int)(pf / 1024 * 1024);
   c->lds_bytes = (size_t)c->lds_p + c->pf_bytes;
 

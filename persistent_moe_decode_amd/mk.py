@@ -43,6 +43,12 @@ class MkConfig(ctypes.Structure):
     ]
 
 
+class ScheduleParams(ctypes.Structure):
+    """mk_schedule_params: how the schedule is cut (all zero = defaults)."""
+    _fields_ = [("num_cus", ctypes.c_int32), ("attn_units", ctypes.c_int32), ("router_units", ctypes.c_int32),
+                ("prefetch_bytes", ctypes.c_int32), ("ctx_hint", ctypes.c_int64)]
+
+
 class ScheduleInfo(ctypes.Structure):
     _fields_ = [
         ("num_cus", ctypes.c_int32), ("n_tasks", ctypes.c_int32), ("n_counters", ctypes.c_int32),
@@ -72,7 +78,7 @@ def lib():
     pi32 = ctypes.POINTER(ctypes.c_int32)
     sig = {
         "mk_create": [ctypes.POINTER(MkConfig), ctypes.POINTER(P)],
-        "mk_build_schedule": [P, I32, I64, ctypes.POINTER(SZ)],
+        "mk_build_schedule": [P, ctypes.POINTER(ScheduleParams), ctypes.POINTER(SZ)],
         "mk_bind": [P, ctypes.POINTER(P), I32, P, P, P, SZ, P],
         "mk_decode_step": [P, I32, P, P, P, P, P, P],
         "mk_get_error": [P, pi32, pi32, pi32, P],
@@ -95,8 +101,23 @@ def lib():
     L.mk_last_error_message.restype = ctypes.c_char_p
     L.mk_destroy.argtypes = [P]
     L.mk_destroy.restype = None
+    L.mk_schedule_params_default.argtypes = [ctypes.POINTER(ScheduleParams)]
+    L.mk_schedule_params_default.restype = None
     _lib = L
     return L
+
+
+def unload() -> None:
+    """dlclose libmk.so: its HIP module destructor (code-object unregistration) runs now, while the
+    HIP runtime is fully alive, instead of among the process's exit handlers.  Every context must be
+    destroyed and the device idle first; lib() loads it again if needed."""
+    global _lib
+    if _lib is None:
+        return
+    import _ctypes
+    handle = _lib._handle
+    _lib = None
+    _ctypes.dlclose(handle)
 
 
 def header_symbols() -> list:
@@ -142,9 +163,15 @@ class Context:
         except Exception:
             pass
 
-    def build_schedule(self, num_cus: int = 0, ctx_hint: int = 0) -> int:
+    def build_schedule(self, num_cus: int = 0, ctx_hint: int = 0, attn_units: int = 0, router_units: int = 0,
+                       prefetch_bytes: int = 0) -> int:
+        """mk_build_schedule; returns the workspace size in bytes."""
+        p = ScheduleParams()
+        lib().mk_schedule_params_default(ctypes.byref(p))
+        p.num_cus, p.ctx_hint, p.attn_units, p.router_units, p.prefetch_bytes = (
+            num_cus, ctx_hint, attn_units, router_units, prefetch_bytes)
         ws = ctypes.c_size_t()
-        check(lib().mk_build_schedule(self.h, num_cus, ctx_hint, ctypes.byref(ws)), "mk_build_schedule")
+        check(lib().mk_build_schedule(self.h, ctypes.byref(p), ctypes.byref(ws)), "mk_build_schedule")
         return ws.value
 
     def info(self) -> ScheduleInfo:

@@ -60,7 +60,8 @@ class DeviceDecoder:
     """All device state of one workload, bound to one mk context."""
 
     def __init__(self, w: synth.Workload, device: str = "cuda:0", num_cus: int = 0, ctx_hint: int | None = None,
-                 max_batch: int | None = None):
+                 max_batch: int | None = None, **sched):
+        """sched: further mk_schedule_params fields (attn_units, router_units, prefetch_bytes)."""
         self.w = w
         self.shape = s = w.shape
         self.dev = torch.device(device)
@@ -71,7 +72,7 @@ class DeviceDecoder:
         cfg = mk.config_from_shape(s, max_batch or w.batch, self.max_pages, self.num_pages)
         self.ctx = mk.Context(cfg)
         hint = ctx_hint if ctx_hint is not None else int(np.mean(w.context)) + w.steps // 2
-        self.ws_bytes = self.ctx.build_schedule(num_cus, hint)
+        self.ws_bytes = self.ctx.build_schedule(num_cus, hint, **sched)
         self.info = self.ctx.info()
         self.offsets = self.ctx.ws_offsets()
         stream = torch.cuda.current_stream(self.dev)
@@ -142,6 +143,18 @@ class DeviceDecoder:
         nxt = self.next_tok if next_out is None else next_out
         self.ctx.decode_step(n, tok.data_ptr(), self.page_table.data_ptr(), sl.data_ptr(), self.logits.data_ptr(),
                              nxt.data_ptr(), self.stream)
+
+    def close(self) -> None:
+        """Ordered teardown: wait for the device, destroy the context, release every device buffer."""
+        torch.cuda.synchronize(self.dev)
+        if getattr(self, "ctx", None) is not None:
+            self.ctx.close()
+            self.ctx = None
+        for name in ("weights", "k_pool", "v_pool", "ws", "page_table", "tokens", "seq_lens", "logits", "next_tok",
+                     "stager"):
+            if hasattr(self, name):
+                delattr(self, name)
+        torch.cuda.empty_cache()
 
     def check_error(self):
         code, cu, task = self.ctx.get_error(self.stream)

@@ -30,12 +30,21 @@ free (end to end): each side keeps its own state.  Where the expert choice
   Both modes check every layer's GPU expert choice against the exact top-k
   of the GPU's own router logits (the kernel's integer logic, bit-exact).
 
-Both sides are fed the oracle's greedy token (teacher forcing).
+Teacher forcing: by default both sides are fed the oracle's greedy token.  With
+teacher=False each side feeds its own greedy token (the GPU its device argmax) and
+the run reports the free-running agreement length: the steps until the first token
+disagreement, which must fall where the oracle's top-2 gap is within the step's
+measured logit error (after it the two sequences differ and comparison stops).
+
+Every step also checks the device argmax (next_tok) bit for bit against the argmax of
+the GPU's own logits, lowest id on ties.
 """
 from __future__ import annotations
 
+import json
+import os
 import time
-from dataclasses import dataclass, field
+from dataclasses import asdict, dataclass, field
 
 import numpy as np
 import torch
@@ -68,16 +77,41 @@ class Report:
     kv_checked: int = 0
     greedy_checked: int = 0
     greedy_excused: int = 0
+    next_tok_checked: int = 0
+    kv_max_ulps: float = 0.0
+    kv_over_1ulp: int = 0          # new K/V entries more than one bf16 ulp off (allowed only within KV_ABS of the head's max)
+    agree_steps: int = -1          # free running without teacher forcing: steps before the first token disagreement
+    disagree_cause: str = ""
+    min_top2_gap: float = float("inf")
     failures: list = field(default_factory=list)
 
     def ok(self) -> bool:
         return not self.failures
 
     def summary(self) -> str:
-        return (f"steps {self.steps} logits max_rel {self.max_rel:.2e} router max {self.max_router:.2e} "
-                f"x max_rel {self.max_x:.2e} routes {self.route_checked} ties {self.route_ties} "
-                f"cascade-steps {self.cascade_steps} kv {self.kv_checked} greedy {self.greedy_checked} "
-                f"excused {self.greedy_excused}")
+        s = (f"steps {self.steps} logits max_rel {self.max_rel:.2e} router max {self.max_router:.2e} "
+             f"x max_rel {self.max_x:.2e} routes {self.route_checked} ties {self.route_ties} "
+             f"cascade-steps {self.cascade_steps} kv {self.kv_checked} kv-max-ulps {self.kv_max_ulps:.2f} "
+             f"kv>1ulp {self.kv_over_1ulp} "
+             f"greedy {self.greedy_checked} excused {self.greedy_excused} next-tok {self.next_tok_checked} "
+             f"min-top2-gap {self.min_top2_gap:.2e}")
+        if self.agree_steps >= 0:
+            s += f" free-agree {self.agree_steps}"
+        return s
+
+
+def record(name: str, rep: Report, **extra) -> None:
+    """Append the report's summary as one JSON line to $MK_PARITY_RECORDS/<name>.jsonl, when that is set."""
+    d = os.environ.get("MK_PARITY_RECORDS")
+    if not d:
+        return
+    os.makedirs(d, exist_ok=True)
+    rec = {k: v for k, v in asdict(rep).items() if k != "failures"}
+    rec.update(name=name, ok=rep.ok(), n_failures=len(rep.failures), first_failures=rep.failures[:3],
+               summary=rep.summary(), time=time.strftime("%Y-%m-%d %H:%M:%S"), **extra)
+    rec = {k: (None if isinstance(v, float) and v == float("inf") else v) for k, v in rec.items()}
+    with open(os.path.join(d, f"{name}.jsonl"), "a") as f:
+        f.write(json.dumps(rec) + "\n")
 
 
 def _topk(r: np.ndarray, k: int) -> list:
@@ -98,6 +132,7 @@ def _check_logits(rep, tag, got, ref, b):
     if not rel <= LOGIT_TOL:
         rep.failures.append(f"{tag} seq {b}: logit rel err {rel:.3e}")
     rep.greedy_checked += 1
+    rep.min_top2_gap = min(rep.min_top2_gap, float(ref.top2_gap[b]))
     gtok = int(np.argmax(got))
     if gtok != int(ref.next_token[b]):
         if ref.top2_gap[b] <= GAP_FACTOR * diff.max():
@@ -105,6 +140,25 @@ def _check_logits(rep, tag, got, ref, b):
         else:
             rep.failures.append(f"{tag} seq {b}: greedy {gtok} vs {int(ref.next_token[b])} "
                                 f"(gap {ref.top2_gap[b]:.3e}, max diff {diff.max():.3e})")
+
+
+def _check_next_tok(rep, tag, dec, got, n):
+    """The device argmax must be the argmax of the GPU's own logits, lowest id on ties (integer, exact)."""
+    dev = dec.next_tok[:n].cpu().numpy()
+    for b in range(n):
+        rep.next_tok_checked += 1
+        want = int(np.argmax(got[b]))
+        if int(dev[b]) != want:
+            rep.failures.append(f"{tag} seq {b}: device next_tok {int(dev[b])} vs argmax of its logits {want}")
+    return [int(t) for t in dev]
+
+
+def _kv_ulps(rep, gv, o64):
+    ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(o64), 1e-30))[1] - 8)
+    r = np.abs(gv - o64) / ulp
+    rep.kv_max_ulps = max(rep.kv_max_ulps, float(np.max(r)))
+    rep.kv_over_1ulp += int(np.sum(r > 1.0000001))
+    return ulp
 
 
 def _self_consistent(rep, tag, sel, rl, n, k):
@@ -139,12 +193,12 @@ def oracle_step(W, kv, toks, pt, lens, gpu_sel, n: int, trace=False):
 class Runner:
     """Both sides of one workload, stepped together."""
 
-    def __init__(self, w: synth.Workload, dec=None, log=print):
+    def __init__(self, w: synth.Workload, dec=None, log=print, **sched):
         from persistent_moe_decode_amd.runtime import DeviceDecoder
 
         self.w, self.log = w, log
         t0 = time.time()
-        self.dec = dec or DeviceDecoder(w)
+        self.dec = dec or DeviceDecoder(w, **sched)
         self.W = O.Weights(w.shape, budget_bytes=float(2 ** 36))
         self.pt = w.page_table()
         self.kv = O.PagedKV(w.shape, w.num_pages)
@@ -171,6 +225,9 @@ class Runner:
         rep.route_ties += len(alts)
         _self_consistent(rep, tag, sel, rl, n, k)
         got = dec.logits[:n].cpu().numpy().astype(np.float64)
+        self.dev_tok = _check_next_tok(rep, tag, dec, got, n)
+        self.compared = [False] * n
+        self.max_diff = [0.0] * n
         for b in range(n):
             diverged = False
             for l in range(self.w.shape.n_layers):
@@ -188,6 +245,8 @@ class Runner:
                 rep.cascade_steps += 1
             else:
                 _check_logits(rep, tag, got[b], ref, b)
+                self.compared[b] = True
+                self.max_diff[b] = float(np.max(np.abs(got[b] - ref.logits[b])))
         return ref
 
     # -------------------------------------------------------------- isolated layers
@@ -213,6 +272,9 @@ class Runner:
         sel, rl, xs = dec.sel()[:, :n], dec.router_logits()[:, :n], dec.residual()[:, :n]
         _self_consistent(rep, tag, sel, rl, n, k)
         got = dec.logits[:n].cpu().numpy().astype(np.float64)
+        self.dev_tok = _check_next_tok(rep, tag, dec, got, n)
+        self.compared = [True] * n
+        self.max_diff = [float(np.max(np.abs(got[b] - ref.logits[b]))) for b in range(n)]
         for b in range(n):
             p = int(lens[b])
             for l in range(L):
@@ -242,7 +304,7 @@ class Runner:
                 kg, vg = dec.kv_at(l, b, p)
                 for name, g16, o64 in (("k", kg, ref.trace["k16"][(l, b)]), ("v", vg, ref.trace["v16"][(l, b)])):
                     gv = O.bf16_to_f64(g16)
-                    ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(o64), 1e-30))[1] - 8)
+                    ulp = _kv_ulps(rep, gv, o64)
                     scale = np.max(np.abs(o64), axis=-1, keepdims=True)
                     bad = np.abs(gv - o64) > ulp * 1.0000001 + KV_ABS * scale
                     rep.kv_checked += gv.size
@@ -254,8 +316,15 @@ class Runner:
 
     # -------------------------------------------------------------- driver
 
-    def run(self, steps: int, mode: str) -> Report:
+    def run(self, steps: int, mode: str, teacher: bool = True) -> Report:
+        """Prefill (for prefill-as-decode workloads) then `steps` greedy steps.
+
+        teacher=False: each side feeds its own greedy token; at the first disagreement the
+        oracle's top-2 gap must be within GAP_FACTOR times that step's largest logit difference
+        (a near-tie either token may win), rep.agree_steps records the steps before it, and the
+        run stops there.  With no disagreement agree_steps = steps."""
         w, rep, n = self.w, self.rep, self.n
+        assert teacher or n == 1
         step_fn = self.step_isolated if mode == "isolated" else self.step_free
         if w.kv_mode == "synthetic":
             toks = [int(w.prompt(b)[w.context[b]]) for b in range(n)]
@@ -269,14 +338,38 @@ class Runner:
         for step in range(steps):
             lens = [c + step for c in w.context]
             ref = step_fn(toks, lens, f"step {step}")
-            toks = [int(x) for x in ref.next_token]
+            if not teacher:
+                mine, theirs = self.dev_tok[0], int(ref.next_token[0])
+                if mine != theirs:
+                    rep.agree_steps = step
+                    gap = float(ref.top2_gap[0])
+                    if not self.compared[0]:
+                        # this step's routing already diverged at a margin within the measured
+                        # router drift (step_free checked that): the two logit vectors are results
+                        # of different, both admissible expert sets, and the tokens may differ
+                        rep.disagree_cause = "routing divergence within the measured router drift"
+                    elif gap <= GAP_FACTOR * self.max_diff[0]:
+                        rep.disagree_cause = f"near-tie of the top-2 logits (gap {gap:.3e})"
+                    else:
+                        rep.failures.append(f"step {step}: free-running tokens {mine} vs {theirs} at a top-2 gap "
+                                            f"{gap:.3e} (max logit diff {self.max_diff[0]:.3e})")
+                    self.log(f"[parity {w.name} {mode} no-teacher] first disagreement at step {step}: "
+                             f"{rep.summary()}")
+                    return rep
+                toks = [mine]
+            else:
+                toks = [int(x) for x in ref.next_token]
             if step % 8 == 0 or step == steps - 1:
                 self.log(f"[parity {w.name} {mode}] step {step}: {rep.summary()} {time.time() - self.t0:.1f}s")
+        if not teacher:
+            rep.agree_steps = steps
         return rep
 
 
-def run(w: synth.Workload, steps: int | None = None, mode: str = "isolated", log=print) -> Report:
-    return Runner(w, log=log).run(w.steps if steps is None else steps, mode)
+def run(w: synth.Workload, steps: int | None = None, mode: str = "isolated", log=print, teacher: bool = True,
+        **sched) -> Report:
+    """sched: mk_schedule_params fields passed to the device decoder (attn_units, prefetch_bytes, ...)."""
+    return Runner(w, log=log, **sched).run(w.steps if steps is None else steps, mode, teacher)
 
 
 # ------------------------------------------------------------------ sampled layers at full size
@@ -322,6 +415,7 @@ def run_sampled(w: synth.Workload, layers, log=print) -> Report:
     got = dec.logits[:n].cpu().numpy().astype(np.float64)
     rep = Report(steps=1)
     _self_consistent(rep, "sampled", sel, rl, n, k)
+    _check_next_tok(rep, "sampled", dec, got, n)
     W = O.Weights(s, budget_bytes=float(2 ** 34))
     pt = w.page_table()
     kv = O.PagedKV(s, w.num_pages, layers=layers)
@@ -353,7 +447,7 @@ def run_sampled(w: synth.Workload, layers, log=print) -> Report:
             kg, vg = dec.kv_at(l, b, p)
             for name, g16, o64 in (("k", kg, ref.parts["k16"]), ("v", vg, ref.parts["v16"])):
                 gv = O.bf16_to_f64(g16)
-                ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(o64), 1e-30))[1] - 8)
+                ulp = _kv_ulps(rep, gv, o64)
                 scale = np.max(np.abs(o64), axis=-1, keepdims=True)
                 bad = np.abs(gv - o64) > ulp * 1.0000001 + KV_ABS * scale
                 rep.kv_checked += gv.size

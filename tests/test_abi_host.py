@@ -285,3 +285,70 @@ def test_attention_split_random_shapes():
             ch.sort()
             assert ch[0][0] == 0 and ch[-1][1] == lens[b] + 1
             assert all(a1 == b0 for (_, a1), (b0, _) in zip(ch, ch[1:]))
+
+
+# --------------------------------------------------------------------------- schedule parameters
+
+
+def _mid_ctx(max_batch=3):
+    w = synth.Workload("mid_p", synth.MID, batch=max_batch, steps=3, context=[2048, 40, 1000][:max_batch])
+    return w, _ctx(w.shape, max_batch, w.max_pages_per_seq, w.num_pages)
+
+
+def test_schedule_params_null_means_defaults():
+    """NULL params = all-zero params: both query the current device (no GPU here: MK_ERR_HIP, no crash)."""
+    import torch
+    w, a = _mid_ctx()
+    _, b = _mid_ctx()
+    ws_a, ws_b = ctypes.c_size_t(), ctypes.c_size_t()
+    ra = mk.lib().mk_build_schedule(a.h, None, ctypes.byref(ws_a))
+    zero = mk.ScheduleParams()
+    rb = mk.lib().mk_build_schedule(b.h, ctypes.byref(zero), ctypes.byref(ws_b))
+    assert ra == rb
+    if torch.cuda.is_available():
+        assert ra == 0 and ws_a.value == ws_b.value
+        assert np.array_equal(a.schedule()[0], b.schedule()[0])
+    else:
+        assert ra == mk.CODES["MK_ERR_HIP"]
+    p = mk.ScheduleParams()
+    mk.lib().mk_schedule_params_default(ctypes.byref(p))
+    assert (p.num_cus, p.attn_units, p.router_units, p.prefetch_bytes, p.ctx_hint) == (0, 0, 0, 0, 0)
+
+
+def test_schedule_params_attn_units_and_clamping():
+    w, c = _mid_ctx()
+    n_lead = 3 * w.shape.n_kv_heads
+    for want, got in ((40, 40), (13, 13), (1, n_lead + 1), (10_000, 256 - 2)):
+        c.build_schedule(256, 1000, attn_units=want)
+        assert c.info().n_attn == got, want
+        assert c.validate() == c.info().n_tasks
+
+
+def test_schedule_params_router_units():
+    w, c = _mid_ctx()
+    for nr in (1, 2, 7):
+        c.build_schedule(256, 1000, router_units=nr)
+        tasks, qoff = c.schedule()
+        pre0 = tasks[(tasks[:, F_OP] == OP_PRE) & (tasks[:, F_LAYER] == 0)]
+        router = pre0[pre0[:, F_R0] >= w.shape.qkv_rows]
+        assert len(router) == nr
+        assert c.validate() == c.info().n_tasks
+
+
+def test_schedule_params_prefetch_cap():
+    w, c = _mid_ctx()
+    c.build_schedule(256, 1000)
+    full = c.info().lds_bytes
+    c.build_schedule(256, 1000, prefetch_bytes=8192)
+    capped = c.info().lds_bytes
+    c.build_schedule(256, 1000, prefetch_bytes=-1)
+    none = c.info().lds_bytes
+    assert none + 8192 == capped and capped < full <= 160 * 1024
+
+
+def test_schedule_params_negative_counts_rejected():
+    w, c = _mid_ctx()
+    for kw in ({"attn_units": -1}, {"router_units": -2}, {"ctx_hint": -5}, {"num_cus": -1}):
+        with pytest.raises(mk.MkError) as e:
+            c.build_schedule(**{"num_cus": 256, **kw})
+        assert e.value.code == mk.CODES["MK_ERR_INVALID_ARG"], kw

@@ -16,8 +16,11 @@ def _log(msg):
     print(msg, flush=True)
 
 
-def _check(rep):
+def _check(rep, name=None):
+    from tests import parity
     _log(rep.summary())
+    if name:
+        parity.record(name, rep)
     assert rep.ok(), "\n".join(rep.failures[:20])
 
 
@@ -26,14 +29,14 @@ def test_tiny_prefill_then_greedy_free():
     from tests import parity
     rep = parity.run(synth.workload("tiny"), mode="free", log=_log)
     assert rep.steps == 128 + 16
-    _check(rep)
+    _check(rep, "tiny_free")
 
 
 def test_tiny_prefill_then_greedy_isolated():
     from tests import parity
     rep = parity.run(synth.workload("tiny"), mode="isolated", log=_log)
     assert rep.steps == 128 + 16
-    _check(rep)
+    _check(rep, "tiny_isolated")
 
 
 def test_tiny_ragged_batch_edges():
@@ -41,7 +44,7 @@ def test_tiny_ragged_batch_edges():
     from tests import parity
     w = synth.Workload("tiny_ragged", synth.TINY, batch=8, steps=4, context=[0, 1, 15, 16, 17, 31, 32, 100],
                        spare_pages=3)
-    _check(parity.run(w, mode="isolated", log=_log))
+    _check(parity.run(w, mode="isolated", log=_log), "tiny_ragged_edges")
 
 
 def test_mid_isolated_64_steps():
@@ -49,23 +52,34 @@ def test_mid_isolated_64_steps():
     from tests import parity
     rep = parity.run(synth.workload("mid"), mode="isolated", log=_log)
     assert rep.steps == 64
-    _check(rep)
+    _check(rep, "mid_isolated_64")
 
 
 def test_mid_free_running_64_steps():
     from tests import parity
     rep = parity.run(synth.workload("mid"), mode="free", log=_log)
     assert rep.steps == 64
-    # most steps keep the same routing end to end and are compared in full
-    assert rep.cascade_steps <= 24, rep.summary()
-    _check(rep)
+    _check(rep, "mid_free_64")
+    # most steps keep the same routing end to end and are compared in full: 2 of 64 steps had a
+    # routing divergence (within the measured drift) when this bound was set; 4 more allow for
+    # the run-to-run spread of which steps meet a near-margin router decision
+    assert rep.cascade_steps <= 6, rep.summary()
+
+
+def test_mid_free_running_no_teacher_forcing():
+    """Each side feeds its own greedy token: the agreement length is recorded; a disagreement must fall
+    at a near-tie of the oracle's top-2 logits (either token is then a correct result)."""
+    from tests import parity
+    rep = parity.run(synth.workload("mid"), mode="free", log=_log, teacher=False)
+    _check(rep, "mid_free_no_teacher")
+    _log(f"free-running agreement: {rep.agree_steps} of 64 steps ({rep.disagree_cause or 'no disagreement'})")
 
 
 def test_mid_batch8_ragged():
     from tests import parity
     w = synth.Workload("mid_bs8", synth.MID, batch=8, steps=3,
                        context=[1, 700, 2048, 33, 1500, 16, 4000, 257])
-    _check(parity.run(w, mode="isolated", log=_log))
+    _check(parity.run(w, mode="isolated", log=_log), "mid_bs8_ragged")
 
 
 def test_repeat_step_is_bit_identical():
@@ -85,20 +99,19 @@ def test_repeat_step_is_bit_identical():
     assert int(dec.next_tok[1]) == int(torch.argmax(outs[0][1]))
 
 
-@pytest.mark.parametrize("pf_bytes", [0, 8192])
-def test_mid_small_prefetch_region(pf_bytes, monkeypatch):
-    """LDS prefetch region capped: weight tiles and K/V pages partly or not at all in LDS, attention merge from registers."""
+@pytest.mark.parametrize("pf_bytes", [-1, 8192])
+def test_mid_small_prefetch_region(pf_bytes):
+    """LDS prefetch region capped (none, 8 KB): weight tiles and K/V pages partly or not at all in LDS,
+    attention merge from registers."""
     from tests import parity
-    monkeypatch.setenv("MK_PREFETCH_BYTES", str(pf_bytes))
     w = synth.Workload(f"mid_pf{pf_bytes}", synth.MID, batch=3, steps=3, context=[2048, 40, 1000])
-    _check(parity.run(w, mode="isolated", log=_log))
+    _check(parity.run(w, mode="isolated", log=_log, prefetch_bytes=pf_bytes))
 
 
 @pytest.mark.parametrize("attn_cus", [13, 40])
-def test_mid_attention_unit_counts(attn_cus, monkeypatch):
+def test_mid_attention_unit_counts(attn_cus):
     """Attention units forced to leads + 1 (one unit takes every Wo row and every chunk past a
     segment's first) and to 40 (larger chunks): same parity bar."""
     from tests import parity
-    monkeypatch.setenv("MK_ATTN_CUS", str(attn_cus))
     w = synth.Workload(f"mid_attn{attn_cus}", synth.MID, batch=3, steps=2, context=[1500, 17, 600])
-    _check(parity.run(w, mode="isolated", log=_log))
+    _check(parity.run(w, mode="isolated", log=_log, attn_units=attn_cus))

@@ -401,3 +401,75 @@ def test_layer_subset_cache_gives_the_same_layer():
     assert np.array_equal(a.x, b.x) and np.array_equal(a.sel, b.sel) and np.array_equal(a.r, b.r)
     with pytest.raises(KeyError):
         part.gather(0, pt[0], 4, 0)
+
+
+# --------------------------------------------------------------------------- synthetic KV fill and LM head
+
+
+@pytest.mark.parametrize("name,context", [("tiny", [40, 0, 17, 16]), ("mid", [300, 33, 1])])
+def test_fill_synthetic_places_every_position_at_its_page_slot(name, context):
+    """Every logical position t of sequence b lands at (page_table[b][t // 16], t % 16) of every
+    layer and kv head, K from the K stream and V from the V stream, bit for bit; every other
+    slot, and every page no sequence owns, keeps the NaN poison.
+
+    The expected values come straight from the generator, and the slot from the page-table
+    rule, without going through the cache's own gather or slot lookup, so a swapped K/V, a
+    wrong page index, a transposed [slot][head] block or an off-by-one position fails."""
+    base = synth.workload(name)
+    w = synth.Workload(name + "_pin", base.shape, batch=len(context), steps=2, context=context,
+                       shuffle_pages=True, spare_pages=2)
+    s, ps = w.shape, w.shape.page_size
+    pt = w.page_table()
+    assert not np.array_equal(pt[pt >= 0], np.sort(pt[pt >= 0])), "page order must be shuffled"
+    kv = O.PagedKV(s, w.num_pages)
+    kv.fill_synthetic(pt, context)
+    written = np.zeros((w.num_pages, ps), dtype=bool)
+    for b, n in enumerate(context):
+        for t in range(n):
+            written[pt[b, t // ps], t % ps] = True
+    for l in range(s.n_layers):
+        for b, n in enumerate(context):
+            if n == 0:
+                continue
+            K = synth.kv_bits(s, l, "k", b, 0, n)     # [t][head][d]
+            V = synth.kv_bits(s, l, "v", b, 0, n)
+            pages = pt[b, np.arange(n) // ps]
+            slots = np.arange(n) % ps
+            for g in range(s.n_kv_heads):
+                assert np.array_equal(kv.k[l, pages, g, slots, :], K[:, g, :]), (l, b, g)
+                assert np.array_equal(kv.v[l, pages, g, slots, :], V[:, g, :]), (l, b, g)
+        # everything else is untouched poison
+        for arr in (kv.k[l], kv.v[l]):
+            rest = arr.transpose(0, 2, 1, 3)[~written]   # [(page, slot)][head][d]
+            assert np.all(rest == 0x7FC0)
+    # K and V streams differ (a swap would go unnoticed otherwise)
+    assert not np.array_equal(synth.kv_bits(s, 0, "k", 0, 0, 4), synth.kv_bits(s, 0, "v", 0, 0, 4))
+
+
+def test_lm_logits_closed_form_through_the_final_gain():
+    """x = (2, -2, 2, -2): mean(x^2) = 4, so rmsnorm(x) = (1, -1, 1, -1) * 2/sqrt(4 + eps); with the
+    final gain (1.5, 0.75, 2, 1) the bf16-rounded input of the LM head is exactly
+    (1.5, -0.75, 2, -1).  A 6 x 4 LM head of hand-picked rows then gives the logits by hand.
+    A dropped gain, a skipped normalization, a transposed head or the embedding in place of the
+    (untied) head all change them."""
+    s = synth.ModelShape(n_layers=1, hidden=4, n_q_heads=1, n_kv_heads=1, head_dim=64,
+                         n_experts=2, top_k=1, inter=4, vocab=6)
+    head = np.array([[1, 0, 0, 0], [0, 1, 0, 0], [0, 0, 1, 0], [0, 0, 0, 1], [1, 1, 1, 1], [2, -2, 0, 0]],
+                    dtype=np.float64)
+    gain = np.array([1.5, 0.75, 2.0, 1.0])
+
+    def src(kind, layer, expert):
+        if kind == synth.K_LM_HEAD:
+            return O.f64_to_bf16_bits(head)
+        if kind == synth.K_FINAL_NORM:
+            return O.f64_to_bf16_bits(gain)
+        if kind == synth.K_EMBED:
+            return O.f64_to_bf16_bits(-head)     # untied: must not be read
+        return synth.weight_bits(s, kind, layer, expert)
+
+    W = O.Weights(s, source=src)
+    got = O.lm_logits(W, np.array([2.0, -2.0, 2.0, -2.0]))
+    assert np.array_equal(got, np.array([1.5, -0.75, 2.0, -1.0, 1.75, 4.5]))
+    assert int(np.argmax(got)) == 5
+    # the same input scaled by any positive factor normalizes to the same logits
+    assert np.array_equal(O.lm_logits(W, np.array([0.5, -0.5, 0.5, -0.5])), got)
