@@ -41,7 +41,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
   size_t state = 0, n_state_u32 = 0;  // counter flags, tickets, error word (zeroed by mk_reset)
-  size_t ctr = 0, tickets = 0, err = 0;
+  size_t ctr = 0, tickets = 0, err = 0, rll = 0, wot = 0;  // (u32 offsets in the state region)
   size_t tasks = 0, queue_off = 0, wtab = 0, inv_freq = 0;
   size_t x = 0, qkv = 0, rlog = 0, attn_part = 0, attn_out = 0, wo_out = 0, h = 0, lm_part = 0, sel = 0;
   size_t total = 0;
@@ -54,7 +54,7 @@ struct mk_ctx {
   bool built = false, bound = false, need_reset = false;
   int ncu = 0, n_attn = 0, n_gu = 0, n_out = 0, n_lm = 0, n_ctr = 0, n_tickets = 0, n_slots = 0;
   int out_rows_max = 0, gu_rows_max = 0, lm_rows_max = 0, pre_rows_max = 0;
-  int lds_b = 0, lds_c = 0, lds_p = 0, pf_bytes = 0;
+  int lds_b = 0, lds_c = 0, lds_p = 0, pf_bytes = 0, pf_wide = 0, tile_off = 0;
   size_t lds_bytes = 0;
   std::vector<Task> tasks;
   std::vector<int32_t> qoff;
@@ -216,7 +216,10 @@ static WsLayout layout_workspace(const mk_ctx* c) {
   w.ctr = 0;
   w.tickets = (size_t)c->n_ctr * kCounterWords;
   w.err = w.tickets + c->n_tickets;
-  w.n_state_u32 = w.err + E_WORDS;
+  // epoch-tagged words (8-byte aligned): router logits, the attention output times Wo
+  w.rll = align_up(w.err + E_WORDS, 2);
+  w.wot = w.rll + 2 * L * B * (size_t)f.n_experts;
+  w.n_state_u32 = w.wot + 2 * L * B * (size_t)f.hidden;
   take(4 * w.n_state_u32);
   w.tasks = take(sizeof(Task) * c->tasks.size());
   w.queue_off = take(4 * (c->ncu + 1));
@@ -367,6 +370,7 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
         t.r0 = r0;
         t.r1 = r1;
         t.signal = ctr_index(l, router ? C_ROUTER : C_QKV);
+        t.tagged = router ? 1 : 0;  // gate/up and output tasks poll the tagged router logits
         c->tasks.push_back(t);
       }
       // stage 2: attention units run their chunk, the others gate/up rows
@@ -388,6 +392,7 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
           w.r0 = r0;
           w.r1 = r1;
           w.signal = ctr_index(l, C_WO);
+          w.tagged = 1;  // output tasks poll the tagged rows
           c->tasks.push_back(w);
         }
       } else {
@@ -433,6 +438,18 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
     }
   }
   c->qoff[ncu] = (int)c->tasks.size();
+  // each output task learns the PRE task that follows it on its queue (its weight tile is copied
+  // into LDS while the output task waits for the Wo rows)
+  for (int q = 0; q < ncu; ++q)
+    for (int i = c->qoff[q]; i + 1 < c->qoff[q + 1]; ++i) {
+      Task& t = c->tasks[i];
+      const Task& nx = c->tasks[i + 1];
+      if (t.op == OP_OUT && nx.op == OP_PRE) {
+        t.next_layer = nx.layer;
+        t.next_r0 = nx.r0;
+        t.next_r1 = nx.r1;
+      }
+    }
   // signal slots: the k-th task (in table order) that signals a counter has slot k
   {
     std::vector<int> used(c->n_ctr, 0);
@@ -470,6 +487,13 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
   if (p.prefetch_bytes < 0) pf = 0;
   c->pf_bytes = (int)(pf / 1024 * 1024);
   c->lds_bytes = (size_t)c->lds_p + c->pf_bytes;
+  // PRE and WO weight tiles start in region C past the output task's expert contributions (at batch 1
+  // nothing else in C is live across those tasks' start, or while an output task copies the tile)
+  c->tile_off = (int)align_up(c_out, 256);
+  size_t wide = c->lds_bytes - (size_t)c->lds_c - (size_t)c->tile_off;
+  if (p.prefetch_bytes > 0) wide = std::min(wide, (size_t)p.prefetch_bytes);
+  if (p.prefetch_bytes < 0) wide = 0;
+  c->pf_wide = (int)(wide / 1024 * 1024);
 
   int r = simulate(c, nullptr);
   if (r) return r;
@@ -665,6 +689,8 @@ extern "C" int mk_decode_step(mk_ctx* c, int32_t n, const int32_t* d_tokens, con
   a.lds_c = c->lds_c;
   a.lds_p = c->lds_p;
   a.pf_bytes = c->pf_bytes;
+  a.pf_wide = c->pf_wide;
+  a.tile_off = c->tile_off;
   uint8_t* w = c->wsp;
   a.tasks = (const Task*)(w + c->ws.tasks);
   a.queue_off = (const int32_t*)(w + c->ws.queue_off);
@@ -672,6 +698,8 @@ extern "C" int mk_decode_step(mk_ctx* c, int32_t n, const int32_t* d_tokens, con
   a.flags = st + c->ws.ctr;
   a.tickets = st + c->ws.tickets;
   a.err = (int32_t*)(st + c->ws.err);
+  a.rll = (uint64_t*)(st + c->ws.rll);
+  a.wot = (uint64_t*)(st + c->ws.wot);
   a.wtab = (const uint64_t*)(w + c->ws.wtab);
   a.inv_freq = (const double*)(w + c->ws.inv_freq);
   a.x = (float*)(w + c->ws.x);

@@ -66,6 +66,18 @@ DEV uint32_t ld_coh(const uint32_t* p) {
   return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Epoch-tagged words: a value and the step's epoch stored together by one
+// 64-bit device-coherent store, so a reader that sees the tag sees the value
+// (each aligned 8-byte store is single-copy atomic).  A consumer polls the
+// words themselves: the producer needs no counter and no wait for its stores
+// to complete, and the consumer no second round trip after the flag.
+DEV void st_tag(uint64_t* p, float v, uint32_t epoch) {
+  __hip_atomic_store(p, ((uint64_t)epoch << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DEV uint64_t ld_tag(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 static constexpr float kNegInf = -__builtin_huge_valf();
 
 // ---------------------------------------------------------------------------
@@ -190,12 +202,12 @@ struct Lds {
   int32_t* flags;  // [32]
   float* red;      // [16]
   double* red8;    // [kWaves][kMaxBatch]
-  float* rbuf;     // router logits [max_batch][E]
+  float* rot;      // attention units: cos, sin of the rotation at the chunk's position [2][64] (with the plan)
   uint8_t* C;
   uint8_t* P;      // prefetched weight tile
 };
 
-// Region B (kLdsB bytes): top-k state | flags | red | red8 | ... | rbuf at +4096.
+// Region B (kLdsB bytes): top-k state | flags | red | red8 | ... | rotation table at +4096.
 DEV Lds carve(uint8_t* lds, const KArgs& a) {
   Lds s;
   s.base = lds;
@@ -204,13 +216,13 @@ DEV Lds carve(uint8_t* lds, const KArgs& a) {
   s.flags = (int32_t*)(lds + a.lds_b + kTopKBytes);
   s.red = (float*)(lds + a.lds_b + kTopKBytes + 128);
   s.red8 = (double*)(lds + a.lds_b + kTopKBytes + 192);
-  s.rbuf = (float*)(lds + a.lds_b + 4096);
+  s.rot = (float*)(lds + a.lds_b + 4096);
   s.C = lds + a.lds_c;
   s.P = lds + a.lds_p;
   return s;
 }
 static_assert(kTopKBytes + 192 + 8 * kWaves * kMaxBatch <= 4096, "region B head fits");
-static_assert(4096 + 4 * kMaxBatch * kMaxExperts <= kLdsB, "router logits fit region B");
+static_assert(4096 + 2 * 64 * 4 <= kLdsB, "rotation table fits region B");
 
 // All threads get the block-wide sum; the order of the partial sums is fixed.
 DEV float block_sum(float v, float* red) {
@@ -258,12 +270,14 @@ DEV uint32_t counter_sum(const KArgs& a, int idx) {
 // sub-counters, s_sleep between polls) until it reaches epoch * fanin; the
 // barrier hands the result to the other waves.  The wait is bounded: past
 // the spin limit the task raises MK_ERR_DEVICE_TIMEOUT and the grid drains.
-// Returns false when the grid is aborting.
+// The abort flag is read every 32 polls, not before the first one (that
+// would put a dependent round trip in front of every wait).  Returns false
+// when the grid is aborting or the wait timed out.
 DEV bool wait_counter(const KArgs& a, int idx, int fanin, int task, int32_t* slot) {
   if (tid() < 64) {
     const int lane = tid();
-    int ok = aborting(a) ? 0 : 1;
-    if (ok && idx >= 0) {
+    int ok = 1;
+    if (idx >= 0) {
       const uint32_t want = a.epoch * (uint32_t)fanin;
       const uint64_t t0 = wall_clock64();
       uint32_t it = 0;
@@ -298,10 +312,12 @@ DEV bool counter_done(const KArgs& a, int idx, int fanin, int32_t* slot) {
   return *slot != 0;
 }
 
-// Every wave waits for its own stores to complete, the barrier orders them
-// before thread 0's add.
-DEV void signal_counter(const KArgs& a, int idx, int slot) {
-  __builtin_amdgcn_s_waitcnt(0);
+// Waves 0 .. wait_waves - 1 (those that stored what the consumers read) wait
+// for their stores to complete, the barrier orders them before thread 0's
+// add; the other waves may leave loads in flight (an LDS copy for the next
+// task, waited there).
+DEV void signal_counter(const KArgs& a, int idx, int slot, int wait_waves = kWaves) {
+  if ((tid() >> 6) < wait_waves) __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid() == 0 && idx >= 0)
     __hip_atomic_fetch_add(a.flags + (size_t)idx * kCounterWords + (slot % kSubCounters) * kSubStride, 1u,
@@ -325,13 +341,13 @@ DEV bool arrive_last(uint32_t* ticket, uint32_t count, int32_t* slot) {
 }
 
 // Wave 0 polls a ticket word until it holds `want`, then resets it for the
-// next step; bounded like wait_counter.  Returns false when the grid is
+// next step; bounded like wait_counter (abort flag read every 32 polls).  Returns false when the grid is
 // aborting or the wait timed out.
 DEV bool wait_ticket(const KArgs& a, uint32_t* ticket, uint32_t want, int task, int32_t* slot) {
   if (tid() < 64) {
     const int lane = tid();
-    int ok = aborting(a) ? 0 : 1;
-    if (ok) {
+    int ok = 1;
+    {
       const uint64_t t0 = wall_clock64();
       uint32_t it = 0;
       while (__builtin_amdgcn_readfirstlane(ld_coh(ticket)) != want) {
@@ -354,6 +370,32 @@ DEV bool wait_ticket(const KArgs& a, uint32_t* ticket, uint32_t want, int task, 
   __syncthreads();
   return *slot != 0;
 }
+
+// Every thread polls its own tagged words (load_ready loads them and says
+// whether all carry this step's epoch) until every thread's do; the block
+// votes after each round.  Bounded like wait_counter; slot is an LDS word.
+// Returns false in every thread when the grid is aborting or the wait timed out.
+template <class F>
+DEV bool poll_block(const KArgs& a, int task, int32_t* slot, F&& load_ready) {
+  const uint64_t t0 = wall_clock64();
+  for (uint32_t it = 1;; ++it) {
+    if (__syncthreads_and(load_ready())) return true;
+    if ((it & 31) == 0) {
+      if (tid() == 0) *slot = aborting(a) ? 1 : (wall_clock64() - t0 > a.spin_limit_ticks ? 2 : 0);
+      __syncthreads();
+      const int stop = *slot;
+      __syncthreads();
+      if (stop) {
+        if (tid() == 0 && stop == 2) raise_error(a, MK_ERR_DEVICE_TIMEOUT, task, -1);
+        return false;
+      }
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+DEV bool tag_ok(uint64_t w, uint32_t epoch) { return (uint32_t)(w >> 32) == epoch; }
+DEV float tag_val(uint64_t w) { return __uint_as_float((uint32_t)w); }
 
 // ---------------------------------------------------------------------------
 // inputs
@@ -730,16 +772,12 @@ DEV void run_rowdots_pf(int K, int njobs, int npf, int maxnx, const Job& job) {
 // asc), their softmax, the distinct experts in ascending order and, for each
 // of them, the (token, slot) pairs routed to it.
 //
-// One wave per token (wave b takes token b), each lane holding experts lane
-// and lane + 64 as order-preserving 32-bit keys (NaN ranks as -inf):
-//   - the top_k-th largest key T, built bit by bit from the top: a bit stays
-//     set when at least top_k keys are >= the prefix with it (two compares
-//     and two ballot counts per bit);
-//   - the selection: every key > T, then keys == T in index order until
-//     top_k are taken (ballot prefix counts);
-//   - the top_k winners, packed into LDS, are ranked among themselves.
-// A vector instruction of a wave takes four cycles here, so the work is kept
-// to a few hundred instructions rather than all expert pairs compared.
+// Wave b takes token b: it polls the token's epoch-tagged router logits
+// (lanes hold experts lane and lane + 64) until every tag is this step's,
+// then picks the winners in top_k rounds: the largest remaining key (an
+// order-preserving 32-bit image of the logit, NaN ranking as -inf) by a
+// wave-wide max, the lowest expert holding it by a ballot, which is removed
+// before the next round.  Slot j is round j's winner.
 
 // The order of (value, index) pairs used by every selection here: larger
 // value first, then smaller index.
@@ -750,77 +788,105 @@ DEV uint32_t topk_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// scratch: kTopKScratch bytes of LDS: per-expert token masks [kMaxExperts],
-// slots [kMaxBatch][kMaxExperts], then per wave the packed winners
-// (key, expert, logit, exp) [kWaves][4][kMaxTopK].
-DEV void compute_topk(const KArgs& a, int layer, TopK* tk, uint8_t* scratch) {
+// Unsigned maximum over the wave, in every lane: DPP within 16-lane rows,
+// then the gfx950 row swaps across rows and halves.
+DEV uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u<0xB1>(v));
+  v = max(v, dpp_u<0x4E>(v));
+  v = max(v, dpp_u<0x141>(v));
+  v = max(v, dpp_u<0x140>(v));
+  const auto t = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max(t[0], t[1]);
+  const auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max(h[0], h[1]);
+}
+
+// The calling wave polls token b's tagged router logits of `layer` until all
+// carry this step's epoch (bounded like wait_counter); lanes get experts lane
+// and lane + 64.  False when the grid is aborting or the wait timed out.
+DEV bool poll_router(const KArgs& a, int layer, int b, int task, float& v0, float& v1) {
+  const int lane = tid() & 63;
+  const uint64_t* base = a.rll + ((size_t)layer * a.max_batch + b) * a.E;
+  const bool h0 = lane < a.E, h1 = lane + 64 < a.E;
+  const uint64_t t0 = wall_clock64();
+  uint32_t it = 0;
+  while (true) {
+    const uint64_t w0 = h0 ? ld_tag(base + lane) : 0ull;
+    const uint64_t w1 = h1 ? ld_tag(base + lane + 64) : 0ull;
+    const bool ok = (!h0 || (uint32_t)(w0 >> 32) == a.epoch) && (!h1 || (uint32_t)(w1 >> 32) == a.epoch);
+    if (__ballot(!ok) == 0ull) {
+      v0 = __uint_as_float((uint32_t)w0);
+      v1 = __uint_as_float((uint32_t)w1);
+      return true;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    if ((++it & 31) == 0) {
+      int stop = 0;
+      if (lane == 0) stop = aborting(a) ? 1 : (wall_clock64() - t0 > a.spin_limit_ticks ? 2 : 0);
+      stop = __shfl(stop, 0);
+      if (stop) {
+        if (lane == 0 && stop == 2) raise_error(a, MK_ERR_DEVICE_TIMEOUT, task, -1);
+        return false;
+      }
+    }
+  }
+}
+
+// scratch: region C, per-expert token masks [kMaxExperts], then slots
+// [kMaxBatch][kMaxExperts].  fail: an LDS word.  Returns false in every
+// thread when a token's router logits never arrived (abort or time-out).
+// With a trace, wave 0 records when its logits arrived as the task's ready time.
+DEV bool compute_topk(const KArgs& a, int layer, TopK* tk, uint8_t* scratch, int task, int32_t* fail, int mk) {
   const int lane = tid() & 63, wave = tid() >> 6;
   const int E = a.E, K = a.topk, n = a.n;
   int32_t* emask = (int32_t*)scratch;
   uint8_t* eslot = scratch + 4 * kMaxExperts;
-  uint32_t* pk = (uint32_t*)(scratch + 4 * kMaxExperts + kMaxBatch * kMaxExperts) + wave * 4 * kMaxTopK;
-  int32_t* pe = (int32_t*)(pk + kMaxTopK);
-  float* pv = (float*)(pk + 2 * kMaxTopK);
-  float* px = (float*)(pk + 3 * kMaxTopK);
   for (int e = tid(); e < kMaxExperts; e += kThreads) emask[e] = 0;
+  if (tid() == 0) *fail = 0;
   __syncthreads();
   if (wave < n) {
     const int b = wave;
-    const float* rl = a.rlog + ((size_t)layer * a.max_batch + b) * E;
-    const float v0 = lane < E ? ld_coh(rl + lane) : kNegInf;
-    const float v1 = lane + 64 < E ? ld_coh(rl + lane + 64) : kNegInf;
-    const uint32_t k0 = lane < E ? topk_key(v0) : 0u, k1 = lane + 64 < E ? topk_key(v1) : 0u;
-    uint32_t T = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t c = T | (1u << bit);
-      if (__popcll(__ballot(k0 >= c)) + __popcll(__ballot(k1 >= c)) >= K) T = c;
-    }
-    const uint64_t q0 = __ballot(k0 == T), q1 = __ballot(k1 == T);
-    const int need = K - (__popcll(__ballot(k0 > T)) + __popcll(__ballot(k1 > T)));
-    const uint64_t below = (1ull << lane) - 1ull;
-    const bool s0 = k0 > T || (k0 == T && __popcll(q0 & below) < need);
-    const bool s1 = k1 > T || (k1 == T && __popcll(q0) + __popcll(q1 & below) < need);
-    const uint64_t m0 = __ballot(s0), m1 = __ballot(s1);
-    if (s0) {
-      const int p = __popcll(m0 & below);
-      pk[p] = k0;
-      pe[p] = lane;
-      pv[p] = v0 != v0 ? kNegInf : v0;
-    }
-    if (s1) {
-      const int p = __popcll(m0) + __popcll(m1 & below);
-      pk[p] = k1;
-      pe[p] = lane + 64;
-      pv[p] = v1 != v1 ? kNegInf : v1;
-    }
-    __builtin_amdgcn_wave_barrier();
-    int rank = 0;
-    uint32_t kj = 0;
-    int ej = 0;
-    float vj = 0.f;
-    if (lane < K) {
-      kj = pk[lane];
-      ej = pe[lane];
-      vj = pv[lane];
-      for (int i = 0; i < K; ++i) rank += (pk[i] > kj) | ((pk[i] == kj) & (pe[i] < ej));
-      tk->sel[b][rank] = ej;
-      eslot[b * kMaxExperts + ej] = (uint8_t)rank;
-      atomicOr(emask + ej, 1 << b);
-    }
-    // softmax in slot order, relative to the largest logit (slot 0's)
-    float vmax = kNegInf;
-    for (int i = 0; i < K; ++i) vmax = fmaxf(vmax, pv[i]);
-    const float ex = __expf(vj - vmax);
-    __builtin_amdgcn_wave_barrier();
-    if (lane < K) px[rank] = ex;
-    __builtin_amdgcn_wave_barrier();
-    if (lane < K) {
+    float v0, v1;
+    if (!poll_router(a, layer, b, task, v0, v1)) {
+      if (lane == 0) *fail = 1;
+    } else {
+      if (wave == 0 && lane == 0 && a.trace && task < a.trace_cap) a.trace[kTraceWords * (size_t)task + 1] = wall_clock64();
+      v0 = v0 != v0 ? kNegInf : v0;
+      v1 = v1 != v1 ? kNegInf : v1;
+      uint32_t k0 = lane < E ? topk_key(v0) : 0u, k1 = lane + 64 < E ? topk_key(v1) : 0u;
+      int ej = 0;
+      float vj = 0.f;
+      for (int j = 0; j < K; ++j) {
+        // every valid key exceeds 0 (the image of -inf is 0x007fffff), so a removed or absent expert never wins
+        const uint32_t m = wave_max_u32(max(k0, k1));
+        const uint64_t b0 = __ballot(k0 == m), b1 = __ballot(k1 == m);
+        const int e = b0 ? __ffsll((long long)b0) - 1 : 64 + __ffsll((long long)b1) - 1;
+        const float ve = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e < 64 ? v0 : v1), e & 63));
+        if (lane == j) {
+          ej = e;
+          vj = ve;
+        }
+        if (lane == (e & 63)) {
+          if (e < 64) k0 = 0u;
+          else k1 = 0u;
+        }
+      }
+      // softmax in slot order, relative to the largest logit (slot 0's)
+      const float vmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vj), 0));
+      const float ex = lane < K ? __expf(vj - vmax) : 0.f;
       float wsum = 0.f;
-      for (int j = 0; j < K; ++j) wsum += px[j];
-      tk->w[b][rank] = ex / wsum;
+      for (int j = 0; j < K; ++j) wsum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
+      if (lane < K) {
+        tk->sel[b][lane] = ej;
+        tk->w[b][lane] = ex / wsum;
+        eslot[b * kMaxExperts + ej] = (uint8_t)lane;
+        atomicOr(emask + ej, 1 << b);
+      }
+      if (mk >= 0 && wave == 0) mark(a, task, mk);
     }
   }
   __syncthreads();
+  if (*fail) return false;
   if (wave == 0) {
     // distinct experts in ascending order (lane e and e + 64), each with its
     // tokens in ascending order as pairs b * top_k + slot
@@ -852,6 +918,7 @@ DEV void compute_topk(const KArgs& a, int layer, TopK* tk, uint8_t* scratch) {
     }
   }
   __syncthreads();
+  return true;
 }
 
 // The experts chosen per token, reported to the caller (written by one task per layer).
@@ -903,8 +970,12 @@ DEV void prefetch_to_lds(const gu16* src, uint8_t* dst_lds, int nbytes) {
 
 
 // Work a task can do before its inputs are ready: the first weight tile of
-// PRE and OUT tasks (rows [r0, r1) of Wqkv / router / Wo) starts streaming
-// into LDS.  Returns the rows prefetched.
+// PRE and WO tasks (rows [r0, r1) of Wqkv / router / Wo) starts streaming
+// into LDS, from tile_off bytes into region C to the end (at batch 1
+// nothing below the end of LDS from there is live across this point: an
+// output task keeps only its expert contributions, below tile_off).  A PRE
+// task that follows an output task finds its tile already copied by it.
+// Returns the rows in LDS.
 DEV int task_prefetch(const KArgs& a, const Task& t, const Lds& s, int qi) {
   const gu16* src;
   int K, nrows;
@@ -921,8 +992,9 @@ DEV int task_prefetch(const KArgs& a, const Task& t, const Lds& s, int qi) {
     return 0;
   }
   // (with several tokens the rows go to the matrix cores straight from HBM)
-  const int npf = a.n == 1 ? min(nrows, a.pf_bytes / (K * 2)) : 0;
-  if (npf > 0) prefetch_to_lds(src, s.P, npf * K * 2);
+  const int npf = a.n == 1 ? min(nrows, a.pf_wide / (K * 2)) : 0;
+  // flags[18] = layer + 1 of a PRE tile the preceding output task has already copied
+  if (npf > 0 && !(t.op == OP_PRE && s.flags[18] == t.layer + 1)) prefetch_to_lds(src, s.C + a.tile_off, npf * K * 2);
   return npf;
 }
 
@@ -942,11 +1014,16 @@ struct JobPre {
   const uint16_t* xs;
   float* out;  // [b][ld] + r0 already applied
   int ld;
+  uint64_t* tag_out = nullptr;  // router rows: the same values as epoch-tagged words ([b][ld] + r0 applied)
+  uint32_t epoch = 0;
   DEV const gu4* row(int i) const { return (const gu4*)(W + (size_t)(r0 + i) * K); }
   DEV const lu4* lrow(int i) const { return (const lu4*)(pf + i * K); }
   DEV int nx(int) const { return 1 << 30; }
   DEV const uint4* x(int, int t) const { return (const uint4*)(xs + (size_t)t * K); }
-  DEV void emit(int i, int t, float v) const { st_coh(out + (size_t)t * ld + i, v); }
+  DEV void emit(int i, int t, float v) const {
+    st_coh(out + (size_t)t * ld + i, v);
+    if (tag_out) st_tag(tag_out + (size_t)t * ld + i, v, epoch);
+  }
 };
 
 TASK void task_pre(const KArgs& a, const Task& t, const Lds& s, int qi, int npf) {
@@ -958,7 +1035,7 @@ TASK void task_pre(const KArgs& a, const Task& t, const Lds& s, int qi, int npf)
   JobPre j;
   j.K = a.H;
   j.xs = xs;
-  j.pf = (const AS_LDS uint16_t*)s.P;
+  j.pf = (const AS_LDS uint16_t*)(s.C + a.tile_off);
   j.npf = npf;
   j.red = (float*)s.C;
   if (t.r0 < a.qkv_rows) {
@@ -970,6 +1047,8 @@ TASK void task_pre(const KArgs& a, const Task& t, const Lds& s, int qi, int npf)
     j.W = wptr(a, widx(l, WL_ROUTER));
     j.r0 = t.r0 - a.qkv_rows;
     j.out = a.rlog + (size_t)l * a.max_batch * a.E + j.r0;
+    j.tag_out = a.rll + (size_t)l * a.max_batch * a.E + j.r0;
+    j.epoch = a.epoch;
     j.ld = a.E;
   }
   run_rowdots_pf(a.H, t.r1 - t.r0, npf, a.n, j);
@@ -1381,6 +1460,15 @@ DEV void attn_task(const KArgs& a, const Task& t, const Lds& s, int qi) {
   if (s.flags[16] != t.idx) {
     attn_plan(a, t, s, qi);
     __syncthreads();
+    // the rotation of the chunk's sequence at its position p (fixed for the
+    // launch): angles in double, cos / sin rounded to float
+    if (tid() < D / 2) {
+      double sd, cd;
+      sincos((double)s.flags[2 + 7] * a.inv_freq[tid()], &sd, &cd);
+      s.rot[tid()] = (float)cd;
+      s.rot[64 + tid()] = (float)sd;
+    }
+    __syncthreads();
     if (tid() == 0) s.flags[16] = t.idx;
   }
   const int32_t* plan = s.flags + 2;
@@ -1409,35 +1497,47 @@ DEV void attn_task(const KArgs& a, const Task& t, const Lds& s, int qi) {
   if (mine && !pg_ok && tid() == 0) raise_error(a, MK_ERR_DEVICE_PAGE, qi, page);
   const bool put = mine && pg_ok;
   const size_t koff = ((((size_t)l * a.num_pages + page) * a.nkv + g) * ps + p % ps) * D;
+  constexpr int half = D / 2;
+  const int nrot = (G + (put ? 1 : 0)) * half;  // pairs: q heads, then (put) the new k
   if (!wait_counter(a, t.wait[0], t.fanin[0], qi, s.flags + 0)) return;
   if (a.trace && tid() == 0 && qi < a.trace_cap) a.trace[kTraceWords * (size_t)qi + 1] = wall_clock64();
+  // q of the group's heads, the new k and v (all loads in flight before any use)
+  const float* qkv = a.qkv + ((size_t)l * a.max_batch + b) * a.qkv_rows;
+  float x0[2] = {0.f, 0.f}, x1[2] = {0.f, 0.f}, vval = 0.f;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int e = tid() + k * kThreads;
+    if (e < nrot) {
+      const int hh = e / half, i = e % half;
+      const float* src = qkv + (hh < G ? (size_t)(g * G + hh) * D : (size_t)a.nq * D + (size_t)g * D);
+      x0[k] = ld_coh(src + i);
+      x1[k] = ld_coh(src + i + half);
+    }
+  }
+  if (put && tid() < D) vval = ld_coh(qkv + (size_t)(a.nq + a.nkv) * D + (size_t)g * D + tid());
 
   // rotated q heads, and (put) the new k as head G, bf16 in region A
-  constexpr int half = D / 2;
   uint16_t* q_s = (uint16_t*)s.A;  // [G + 1][D]
-  const float* qkv = a.qkv + ((size_t)l * a.max_batch + b) * a.qkv_rows;
-  const int nrot = (G + (put ? 1 : 0)) * half;
-  for (int e = tid(); e < nrot; e += kThreads) {
-    const int hh = e / half, i = e % half;
-    double sd, cd;
-    sincos((double)p * a.inv_freq[i], &sd, &cd);
-    const float cf = (float)cd, sf = (float)sd;
-    const float* src = qkv + (hh < G ? (size_t)(g * G + hh) * D : (size_t)a.nq * D + (size_t)g * D);
-    const float x0 = ld_coh(src + i), x1 = ld_coh(src + i + half);
-    const uint16_t lo = f2bf(x0 * cf - x1 * sf), hi = f2bf(x0 * sf + x1 * cf);
-    q_s[hh * D + i] = lo;
-    q_s[hh * D + i + half] = hi;
-    if (hh == G) {
-      a.k_pool[koff + i] = lo;
-      a.k_pool[koff + i + half] = hi;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int e = tid() + k * kThreads;
+    if (e < nrot) {
+      const int hh = e / half, i = e % half;
+      const float cf = s.rot[i], sf = s.rot[64 + i];
+      const uint16_t lo = f2bf(x0[k] * cf - x1[k] * sf), hi = f2bf(x0[k] * sf + x1[k] * cf);
+      q_s[hh * D + i] = lo;
+      q_s[hh * D + i + half] = hi;
+      if (hh == G) {
+        a.k_pool[koff + i] = lo;
+        a.k_pool[koff + i + half] = hi;
+      }
     }
   }
   // V pages are stored dims-major: element (dim, slot) of a (page, head) block at dim*page_size + slot
   uint16_t v_i = 0;  // thread i < D: V dim i
   if (put && tid() < D) {
-    const float* vv = qkv + (size_t)(a.nq + a.nkv) * D + (size_t)g * D;
     const size_t voff = (((size_t)l * a.num_pages + page) * a.nkv + g) * (size_t)ps * D + p % ps;
-    v_i = f2bf(ld_coh(vv + tid()));
+    v_i = f2bf(vval);
     a.v_pool[voff + (size_t)tid() * ps] = v_i;
   }
   mark(a, qi, 0);
@@ -1557,12 +1657,12 @@ struct JobGateUp {
 // the PRE task that ran just before on this compute unit.
 TASK void task_gateup(const KArgs& a, const Task& t, const Lds& s, int qi, bool have_xs) {
   const int l = t.layer;
-  compute_topk(a, l, s.tk, s.C);
+  if (!compute_topk(a, l, s.tk, s.C, qi, s.flags + 0, 0)) return;
   if (t.idx == 0) write_sel(a, l, s.tk);
-  mark(a, qi, 0);
+  mark(a, qi, 1);
   uint16_t* xs = (uint16_t*)s.A;
   if (!have_xs) norm_inputs(a, l, wptr(a, widx(l, WL_NORM)), xs, s.red8, qi, -1);
-  mark(a, qi, 1);
+  mark(a, qi, 2);
   const TopK* tk = s.tk;
   const int64_t R = (int64_t)tk->nU * a.I;
   const int64_t va = R * t.idx / a.n_gu, vb = R * (t.idx + 1) / a.n_gu;
@@ -1631,7 +1731,9 @@ constexpr int kDownGroups = 4;
 // down-projection rows are loaded before the gate/up results are waited for.
 // have_tk: region B still holds this layer's top-k, left there by the gate/up
 // task that ran just before on this compute unit.
-TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have_tk) {
+// Returns the number of leading waves that must wait for their stores before
+// the task signals (the others may still be copying the next task's tile).
+TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have_tk) {
   const int l = t.layer, nr = t.r1 - t.r0, n = a.n;
   float* contrib = (float*)s.C;  // [out_rows_max][maxB*topk]
   const int maxBK = a.max_batch * a.topk;
@@ -1642,10 +1744,7 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool hav
     const int rr = tid() / n, b = tid() % n;
     x_first = load_x(a, l, b, t.r0 + rr, l == 0 ? token_row(a, b, qi) : nullptr);
   }
-  if (!have_tk) {
-    if (!wait_counter(a, t.wait[1], t.fanin[1], qi, s.flags + 1)) return;
-    compute_topk(a, l, s.tk, s.C);
-  }
+  if (!have_tk && !compute_topk(a, l, s.tk, s.C, qi, s.flags + 1, -1)) return kWaves;
   const TopK* tk = s.tk;
   JobDown jd;
   jd.tk = tk;
@@ -1673,7 +1772,7 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool hav
     for (int c = 0; c < kDownC; ++c)
       dp[g][c] = __builtin_bit_cast(uint4, act && c < cpl ? __builtin_nontemporal_load(wr + 16 * c) : u32x4_v{0, 0, 0, 0});
   }
-  if (!wait_counter(a, t.wait[0], t.fanin[0], qi, s.flags + 0)) return;
+  if (!wait_counter(a, t.wait[0], t.fanin[0], qi, s.flags + 0)) return kWaves;
   if (a.trace && tid() == 0 && qi < a.trace_cap) a.trace[kTraceWords * (size_t)qi + 1] = wall_clock64();
   copy_coh_to_lds(xs, a.h + (size_t)l * a.max_batch * a.topk * a.I, n * a.topk * a.I * 2);
   prefetch_wait();
@@ -1698,18 +1797,43 @@ TASK void task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool hav
   }
   rowdots_range<false>(a.I, npre, nd, mt, jd);
   mark(a, qi, 1);
-  // the attention output times Wo, for these rows (attention units)
-  if (!wait_counter(a, t.late_wait, t.late_fanin, qi, s.flags + 13)) return;
+  // batch 1, wave 0 alone storing the residual rows: while the Wo rows are
+  // awaited, waves 1..7 copy the weight tile of the PRE task that follows on
+  // this unit into LDS (above tile_off, clear of the contributions); that
+  // task then finds it there instead of issuing it in front of its own wait
+  const bool early = n == 1 && nr <= 64 && t.next_r1 > t.next_r0 && a.pf_wide > 0;
+  if (early) {
+    const int npf = min(t.next_r1 - t.next_r0, a.pf_wide / (a.H * 2));
+    const gu16* src = t.next_r0 < a.qkv_rows ? wptr(a, widx(t.next_layer, WL_QKV)) + (size_t)t.next_r0 * a.H
+                                             : wptr(a, widx(t.next_layer, WL_ROUTER)) + (size_t)(t.next_r0 - a.qkv_rows) * a.H;
+    prefetch_to_lds(src, s.C + a.tile_off, npf * a.H * 2);
+    if (tid() == 0) s.flags[18] = t.next_layer + 1;
+  }
+  // the attention output times Wo for these rows (attention units), polled as tagged words
+  const uint64_t* wot = a.wot + (size_t)l * a.max_batch * a.H + t.r0;
+  float wo_first = 0.f;
+  const bool ok = poll_block(a, qi, s.flags + 19, [&]() -> int {
+    int r = 1;
+    for (int e = tid(); e < nr * n; e += kThreads) {
+      const uint64_t w = ld_tag(wot + (size_t)(e % n) * a.H + e / n);
+      r &= tag_ok(w, a.epoch);
+      if (e == tid()) wo_first = tag_val(w);
+    }
+    return r;
+  });
+  if (!ok) return early ? 1 : kWaves;
   mark(a, qi, 2);
   // x_{l+1} = (x_l + attn) + sum_j w_j y_j
-  const float* wo = a.wo_out + (size_t)l * a.max_batch * a.H + t.r0;
   for (int e = tid(); e < nr * n; e += kThreads) {
     const int rr = e / n, b = e % n;
     float moe = 0.f;
     for (int j = 0; j < a.topk; ++j) moe += tk->w[b][j] * contrib[(size_t)rr * maxBK + b * a.topk + j];
     const float xo = e == tid() ? x_first : load_x(a, l, b, t.r0 + rr, l == 0 ? token_row(a, b, qi) : nullptr);
-    st_coh(a.x + ((size_t)(l + 1) * a.max_batch + b) * a.H + t.r0 + rr, (xo + ld_coh(wo + (size_t)b * a.H + rr)) + moe);
+    const float wo = e == tid() ? wo_first : tag_val(ld_tag(wot + (size_t)b * a.H + rr));
+    st_coh(a.x + ((size_t)(l + 1) * a.max_batch + b) * a.H + t.r0 + rr, (xo + wo) + moe);
   }
+  // waves whose stores the consumers read must see them complete before the signal
+  return early ? 1 : kWaves;
 }
 
 // ---------------------------------------------------------------------------
@@ -1740,7 +1864,7 @@ TASK void task_wo(const KArgs& a, const Task& t, const Lds& s, int qi, int npf) 
   prefetch_wait();
   mark(a, qi, 0);
   JobPre j;
-  j.pf = (const AS_LDS uint16_t*)s.P;
+  j.pf = (const AS_LDS uint16_t*)(s.C + a.tile_off);
   j.npf = npf;
   j.red = (float*)s.C;
   j.W = W;
@@ -1748,6 +1872,8 @@ TASK void task_wo(const KArgs& a, const Task& t, const Lds& s, int qi, int npf) 
   j.K = AD;
   j.xs = xs;
   j.out = a.wo_out + (size_t)l * a.max_batch * a.H + t.r0;
+  j.tag_out = a.wot + (size_t)l * a.max_batch * a.H + t.r0;
+  j.epoch = a.epoch;
   j.ld = a.H;
   rowdots_range<true>(AD, 0, npf, n, j);
   for (int b = 0; b < n; ++b) {
@@ -1875,7 +2001,10 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a)
   const Lds s = carve(lds_raw, a);
   const int cu = blockIdx.x;
   const int q0 = a.queue_off[cu], q1 = a.queue_off[cu + 1];
-  if (tid() == 0) s.flags[16] = -1;  // no attention plan cached yet
+  if (tid() == 0) {
+    s.flags[16] = -1;  // no attention plan cached yet
+    s.flags[18] = 0;   // no PRE tile copied ahead
+  }
   __syncthreads();
   int xs_layer = -1;                 // layer whose normalized input region A holds
   int tk_layer = -1;                 // layer whose top-k region B holds
@@ -1885,17 +2014,19 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a)
     if (a.trace && tid() == 0) t_fetch = wall_clock64();
     // immutable weights start streaming into LDS before the inputs are ready
     const int npf = task_prefetch(a, t, s, q);
-    // attention, Wo and output tasks wait inside, once their loads are in flight
-    const bool own_wait = t.op == OP_ATTN || t.op == OP_OUT || t.op == OP_WO;
+    // attention, Wo and output tasks wait inside, once their loads are in flight; gate/up
+    // tasks poll the tagged router logits inside
+    const bool own_wait = t.op == OP_ATTN || t.op == OP_OUT || t.op == OP_WO || t.op == OP_GATEUP;
     bool ok = own_wait || wait_counter(a, t.wait[0], t.fanin[0], q, s.flags + 0);
     if (ok && !own_wait && t.wait[1] >= 0) ok = wait_counter(a, t.wait[1], t.fanin[1], q, s.flags + 1);
     if (a.trace && tid() == 0) t_ready = wall_clock64();
+    int wait_waves = kWaves;
     if (ok) {
       switch (t.op) {
         case OP_PRE: task_pre(a, t, s, q, npf); break;
         case OP_ATTN: task_attn(a, t, s, q); break;
         case OP_GATEUP: task_gateup(a, t, s, q, xs_layer == t.layer); break;
-        case OP_OUT: task_out(a, t, s, q, tk_layer == t.layer); break;
+        case OP_OUT: wait_waves = task_out(a, t, s, q, tk_layer == t.layer); break;
         case OP_WO: task_wo(a, t, s, q, npf); break;
         case OP_LMHEAD: task_lmhead(a, t, s, q); break;
         default: break;
@@ -1903,7 +2034,8 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a)
     }
     xs_layer = ok && t.op == OP_PRE ? t.layer : (ok && t.op == OP_GATEUP ? xs_layer : -1);
     tk_layer = ok && (t.op == OP_GATEUP || t.op == OP_OUT) ? t.layer : (t.op == OP_LMHEAD ? -1 : tk_layer);
-    signal_counter(a, t.signal, t.slot);
+    if (t.tagged) __syncthreads();  // consumers poll the tagged output itself
+    else signal_counter(a, t.signal, t.slot, wait_waves);
     if (a.trace && tid() == 0 && q < a.trace_cap) {
       uint64_t* r = a.trace + kTraceWords * (size_t)q;
       r[0] = t_fetch;

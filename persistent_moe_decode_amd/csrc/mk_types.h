@@ -48,7 +48,12 @@ struct Task {
   int32_t late_wait;  // counter waited inside the body, once its first part is done (-1 = none)
   int32_t late_fanin;
   int32_t slot;       // this task's index among the tasks signalling its counter: 0 .. (signals) - 1
-  int32_t pad[18];
+  int32_t tagged;     // 1: consumers read this task's output as epoch-tagged words (value | epoch << 32),
+                      // so its signal is an edge for the host simulator only: on the device no counter
+                      // add and no wait for the stores to complete
+  int32_t next_layer, next_r0, next_r1;  // OUT: the PRE task that follows on this queue (rows; r1 = 0: none),
+                                         // whose weight tile the OUT task copies into LDS while it waits
+  int32_t pad[14];
 };
 static_assert(sizeof(Task) == kTaskInts * 4, "task descriptor is 128 bytes");
 
@@ -77,12 +82,17 @@ struct KArgs {
   int32_t n_attn, n_gu, n_lm;
   int32_t gu_rows_max, out_rows_max, lm_rows_max;  // largest row range of one task
   int32_t lds_b, lds_c, lds_p;                     // LDS region offsets (bytes)
-  int32_t pf_bytes;                                // size of the weight prefetch region
+  int32_t pf_bytes;                                // size of the prefetch region P (K/V pages, merge partials)
+  int32_t pf_wide;                                 // bytes of the PRE / WO weight tile region, which starts tile_off
+                                                   // bytes into region C and runs to the end of LDS
+  int32_t tile_off;                                // (region C below it: the output task's expert contributions)
   const Task* tasks;
   const int32_t* queue_off;
   uint32_t* flags;      // counters: [(L + 1) * kCtrPerLayer][kCounterWords]
   uint32_t* tickets;    // attention tickets [L][max_batch][nkv], then 1 for the LM head
   int32_t* err;         // E_WORDS
+  uint64_t* rll;        // router logits as epoch-tagged words [L][max_batch][E] (zeroed with the counters)
+  uint64_t* wot;        // the attention output times Wo as epoch-tagged words [L][max_batch][H]
   const uint64_t* wtab; // device pointers of the weights
   const double* inv_freq; // [d/2]
   // activations

@@ -7,9 +7,11 @@ body, and when it had signalled.  This module joins them with the task table.
 
 Phase marks per op: PRE [inputs loaded, norm done, rows done]; ATTN [q
 rotated and new K/V written, copied pages landed, positions done, partial
-stored]; GATEUP [routing loaded, norm done]; OUT [h loaded, down rows done,
-Wo rows waited]; WO [attention output loaded, rows done]; LMHEAD [norm done,
-rows done, local argmax done].
+stored]; GATEUP [top-k selected (wave 0), routing tables built, norm done];
+OUT [h loaded, down rows done, Wo rows polled]; WO [attention output loaded,
+rows done]; LMHEAD [norm done, rows done, local argmax done].  Tasks that
+poll epoch-tagged inputs (ATTN, GATEUP, the Wo rows in OUT) record as
+"ready" the moment the tags matched.
 """
 from __future__ import annotations
 
