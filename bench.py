@@ -203,6 +203,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=25.0)
     ap.add_argument("--trace", default="", help="write a Perfetto timeline of one extra step to this path")
+    ap.add_argument("--attn-units", type=int, default=0, help="schedule: attention compute units (0 = default)")
+    ap.add_argument("--router-units", type=int, default=0, help="schedule: router compute units (0 = default)")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="after the run, one plain device-to-device copy of this many bytes (counter calibration)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -229,7 +231,7 @@ def main():
     if total > w.steps:
         w.steps = total  # page capacity for every position the run writes
     t0 = time.time()
-    dec = DeviceDecoder(w)
+    dec = DeviceDecoder(w, attn_units=args.attn_units, router_units=args.router_units)
     dec.fill_synthetic_kv()
     log(f"[bench] setup {time.time() - t0:.1f}s, {dec.info.num_cus} CUs, n_attn {dec.info.n_attn}, "
         f"lds {dec.info.lds_bytes} B, workspace {dec.ws_bytes / 2**20:.1f} MiB")

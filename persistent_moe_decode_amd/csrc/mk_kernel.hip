@@ -93,6 +93,14 @@ DEV uint16_t f2bf(float f) {
   return (uint16_t)(u >> 16);
 }
 
+typedef float float2_v __attribute__((ext_vector_type(2)));
+
+// Two floats -> two bfloat16 bit patterns (round to nearest even), low half
+// first: one gfx950 v_cvt_pk_bf16_f32.  Finite values round exactly as f2bf.
+DEV uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_v){a, b}, bf16x2_v));
+}
+
 DEV float dot2(uint32_t w, uint32_t x, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, w), __builtin_bit_cast(bf16x2_v, x), acc, false);
 }
@@ -1062,12 +1070,14 @@ TASK void task_pre(const KArgs& a, const Task& t, const Lds& s, int qi, int npf)
 //   S^T[16 pos][16 heads] = K[16 pos][d] * Q^T[d][16 heads]   (v_mfma_f32_16x16x32_bf16,
 //     the group's q heads padded to 16 with zero rows), so lane l holds the
 //     scores of positions 4*(l/16)..+3 for head l%16;
-//   O[16 heads][d] += P[16 heads][16 pos] * V[16 pos][d]      (v_mfma_f32_16x16x16_bf16,
-//     d/16 tiles), where the probabilities above are already in the A-operand
-//     layout (row = head l%16, k = positions 4*(l/16)..+3).
-// The B operand of the second product needs 4 consecutive positions of one
+//   O^T[d][16 heads] += V^T[d][16 pos] * P^T[16 pos][16 heads] (v_mfma_f32_16x16x16_bf16,
+//     d/16 tiles), where the probabilities above are already in the B-operand
+//     layout (column = head l%16, k = positions 4*(l/16)..+3), and lane l's
+//     output column is head l%16 too, so the online softmax rescales each lane
+//     by its own factor (no cross-lane exchange).
+// The A operand of the second product needs 4 consecutive positions of one
 // dim per lane, which is why V pages are stored dims-major.  Softmax is online
-// per page (running max and sum per head, O rows rescaled), in fp32; the
+// per page (running max and sum per head, O columns rescaled), in fp32; the
 // probabilities enter the MFMA as a bf16 pair (high part + remainder), so the
 // P*V product is as accurate as the fp32 sum it is divided by.  K/V of the
 // next page are loaded while the current one is processed.
@@ -1208,26 +1218,25 @@ DEV void attn_page(const AttnPage<D>& P, const bf16x8_v (&qb)[D / 32], float sca
   bm = rows4_max(bm);
   const float mn = fmaxf(m, bm);
   const float alpha = mn == kNegInf ? 1.f : __expf(m - mn);
-  // p = p_hi + p_lo, both bf16: two MFMAs keep the P*V product at ~2^-16 relative
-  short4_v pa, pl;
+  float pf[4];
   float ps = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float pf = sv[i] == kNegInf ? 0.f : __expf(sv[i] - mn);
-    const uint16_t hi = f2bf(pf);
-    pa[i] = (short)hi;
-    pl[i] = (short)f2bf(pf - bf2f(hi));
-    ps += pf;
+    pf[i] = sv[i] == kNegInf ? 0.f : __expf(sv[i] - mn);
+    ps += pf[i];
   }
+  // p = p_hi + p_lo, both bf16: two matrix-core products keep P*V at ~2^-16 relative
+  const uint32_t h01 = pack_bf16(pf[0], pf[1]), h23 = pack_bf16(pf[2], pf[3]);
+  const uint32_t l01 = pack_bf16(pf[0] - bf2f(h01 & 0xffffu), pf[1] - bf2f(h01 >> 16));
+  const uint32_t l23 = pack_bf16(pf[2] - bf2f(h23 & 0xffffu), pf[3] - bf2f(h23 >> 16));
+  const short4_v pa = __builtin_bit_cast(short4_v, make_uint2(h01, h23));
+  const short4_v pl = __builtin_bit_cast(short4_v, make_uint2(l01, l23));
   lsum = lsum * alpha + ps;
   m = mn;
-  // O rows are heads 4*(l/16)+i; their rescale factors live in lanes 4*(l/16)+i
+  // O^T[dim][head] = V^T P^T: the lane's column is its own head, so its
+  // rescale factor is its own alpha
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float ai = __shfl(alpha, 4 * grp + i);
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) o[t][i] *= ai;
-  }
+  for (int t = 0; t < D / 16; ++t) o[t] *= alpha;
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) {
     short4_v vb4;
@@ -1236,8 +1245,8 @@ DEV void attn_page(const AttnPage<D>& P, const bf16x8_v (&qb)[D / 32], float sca
     vb4[1] = (4 * grp + 1 < P.nvalid) ? (short)(vv.x >> 16) : (short)0;
     vb4[2] = (4 * grp + 2 < P.nvalid) ? (short)(vv.y & 0xffffu) : (short)0;
     vb4[3] = (4 * grp + 3 < P.nvalid) ? (short)(vv.y >> 16) : (short)0;
-    o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb4, o[t], 0, 0, 0);
-    o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vb4, o[t], 0, 0, 0);
+    o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vb4, pa, o[t], 0, 0, 0);
+    o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vb4, pl, o[t], 0, 0, 0);
   }
 }
 
@@ -1312,14 +1321,11 @@ DEV void attn_wave(const KArgs& a, const Lds& s, int qi, const uint16_t* q_s, in
     mrg.m[wave * kMaxGroup + r] = m;
     mrg.l[wave * kMaxGroup + r] = lsum;
   }
+  // lane (r, grp) holds O^T[16 t + 4 grp + i][head r]
+  if (r < G) {
+    float* row = mrg.o + ((size_t)wave * G + r) * D;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = 4 * grp + i;
-    if (h < G) {
-      float* row = mrg.o + ((size_t)wave * G + h) * D;
-#pragma unroll
-      for (int t = 0; t < D / 16; ++t) row[16 * t + r] = o[t][i];
-    }
+    for (int t = 0; t < D / 16; ++t) *(float4_v*)(row + 16 * t + 4 * grp) = o[t];
   }
 }
 
