@@ -472,7 +472,7 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
   size_t c_lm = (size_t)std::min(c->lm_rows_max, kLmPass) * B * 4;
   // attention: the waves' partial results, or (a segment's lead) the (max, sum) of all chunks plus one float4 per thread
   size_t c_attn = std::max((size_t)kWaves * (group * f.head_dim + 2 * kMaxGroup) * 4,
-                           align_up((size_t)n_attn * group * 2 * 4, 16) + (size_t)kThreads * 16);
+                           align_up((size_t)n_attn * kMaxGroup * 2 * 4, 16) + (size_t)kThreads * 16);
   const size_t c_mfma = B >= 2 ? (size_t)kMfmaRedBytes : 0;  // partial tiles of split dense rows
   size_t c_bytes = align_up(std::max({c_gu, c_out, c_lm, c_attn, c_mfma, (size_t)kTopKScratch}), 256);
   c->lds_b = (int)a_bytes;

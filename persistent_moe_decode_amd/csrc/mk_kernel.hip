@@ -78,6 +78,18 @@ DEV uint64_t ld_tag(const uint64_t* p) {
   return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// 16 bytes at byte offset `off` of [base, base + nbytes), read with the same
+// device-coherent cache policy as the atomic loads above (sc1): data another
+// compute unit wrote in this launch, read after its flag was seen.  One
+// 16-byte load per lane (the LDS copy engine moves data at a fraction of this
+// rate per compute unit); offsets past nbytes read as zero.  base and nbytes
+// must be the same in every lane (they form a scalar buffer resource).
+DEV u32x4_v ld_coh16(const void* base, uint32_t nbytes, uint32_t off) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCohPolicy);
+}
+
 static constexpr float kNegInf = -__builtin_huge_valf();
 
 // ---------------------------------------------------------------------------
@@ -448,22 +460,37 @@ DEV uint16_t d2bf(double v) {
 // xs[b][H] = bf16(x_b / sqrt(mean(x_b^2) + eps) * g) for b < n, evaluated in
 // double so the one rounding to bf16 is the only one (the normalized input
 // feeds every projection of the layer).
-// Wave 0 copies the input rows (this layer's x, fp32, or at layer 0 the
-// tokens' embedding rows, bf16) and the gain into LDS behind xs; its load
-// queue holds nothing else at that point, so the copy does not complete
-// behind weight tiles the other waves have in flight.  The sums of squares
+// The input rows (this layer's x, fp32, or at layer 0 the tokens' embedding
+// rows, bf16) and the gain are copied into LDS behind xs with register
+// loads by all threads.  The sums of squares
 // of all rows are reduced together: one barrier for the whole batch.  The
 // loops run over the batch at run time, which keeps the code short: it runs
 // once per layer and is fetched anew each time.
 
-// One wave copies nbytes (a multiple of 16) from global memory to LDS.
-template <int Policy>
-DEV void wave_copy_to_lds(uint8_t* dst, const AS_GLOBAL void* src, int nbytes) {
-  const int lane = tid() & 63;
-  const AS_GLOBAL uint8_t* s8 = (const AS_GLOBAL uint8_t*)src;
-  for (int c = 0; c < nbytes; c += 1024)
-    if (c + lane * 16 < nbytes)
-      __builtin_amdgcn_global_load_lds((AS_GLOBAL void*)(s8 + c + lane * 16), (AS_LDS void*)(dst + c), 16, 0, Policy);
+// All threads copy nbytes (a multiple of 16) from global memory into LDS with
+// 16-byte register loads, up to 8 per thread in flight before the LDS
+// writes (the LDS copy engine moves far fewer bytes per compute unit).  Coh:
+// the data was written by other compute units in this launch (sc1 loads);
+// otherwise plain loads of data written before the launch.  In LDS after the
+// next barrier.
+template <bool Coh>
+DEV void copy_to_lds(void* dst, const void* src, uint32_t nbytes) {
+  const uint32_t n16 = nbytes / 16;
+  u32x4_v* d = (u32x4_v*)dst;
+  for (uint32_t q0 = 0; q0 < n16; q0 += 8 * kThreads) {
+    u32x4_v v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t q = q0 + k * kThreads + tid();
+      if constexpr (Coh) v[k] = ld_coh16(src, nbytes, q * 16);  // past nbytes: zero, not stored
+      else v[k] = q < n16 ? ((const gu4*)src)[q] : u32x4_v{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t q = q0 + k * kThreads + tid();
+      if (q < n16) d[q] = v[k];
+    }
+  }
 }
 
 // The staging area behind xs in region A: [max_batch][H] fp32 rows, then the gain [H].
@@ -500,16 +527,30 @@ DEV void norm_inputs(const KArgs& a, int layer, const gu16* gain, uint16_t* xs, 
   uint8_t* stage = norm_stage(a, xs);
   uint16_t* gs = (uint16_t*)(stage + (size_t)a.max_batch * H * 4);
   const bool emb = layer == 0;
-  if (wave == 0) {
-    wave_copy_to_lds<0>((uint8_t*)gs, gain, H * 2);
-    if (emb) {
-      for (int b = 0; b < n; ++b) wave_copy_to_lds<0>(stage + (size_t)b * H * 2, token_row(a, b, task), H * 2);
-    } else {
-      const size_t o = (size_t)layer * a.max_batch * H;
-      if (a.x_in) wave_copy_to_lds<0>(stage, (const AS_GLOBAL float*)(a.x_in + o), n * H * 4);
-      else wave_copy_to_lds<kCohPolicy>(stage, (const AS_GLOBAL float*)(a.x + o), n * H * 4);
+  {
+    // the input rows (one 16-byte load per thread and row at hidden 2048) and
+    // the gain, all in flight before any is written to LDS
+    const uint32_t nx16 = emb ? 0u : (uint32_t)n * H / 4, ng16 = (uint32_t)H / 8;
+    const size_t o = (size_t)layer * a.max_batch * H;
+    u32x4_v* st = (u32x4_v*)stage;
+    for (uint32_t q0 = 0; q0 < nx16 + ng16; q0 += 4 * kThreads) {
+      u32x4_v v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t q = q0 + k * kThreads + tid();
+        if (q < nx16) v[k] = a.x_in ? ((const gu4*)(a.x_in + o))[q] : ld_coh16(a.x + o, nx16 * 16, q * 16);
+        else if (q < nx16 + ng16) v[k] = ((const gu4*)gain)[q - nx16];
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t q = q0 + k * kThreads + tid();
+        if (q < nx16) st[q] = v[k];
+        else if (q < nx16 + ng16) ((u32x4_v*)gs)[q - nx16] = v[k];
+      }
     }
-    __builtin_amdgcn_s_waitcnt(0);
+    if (emb)
+      for (int b = 0; b < n; ++b)
+        copy_to_lds<false>(stage + (size_t)b * H * 2, (const void*)(uintptr_t)token_row(a, b, task), H * 2);
   }
   __syncthreads();
   if (mk >= 0) mark(a, task, mk);
@@ -935,30 +976,15 @@ DEV void write_sel(const KArgs& a, int layer, const TopK* tk) {
     a.sel_out[(size_t)layer * a.max_batch * a.topk + tid()] = tk->sel[tid() / a.topk][tid() % a.topk];
 }
 
-// Copies nbytes (a multiple of 16) that other compute units wrote into LDS
-// with the LDS DMA path and the device-coherent policy, all in flight at
-// once; the data is there after the next s_waitcnt(0) and barrier.
-DEV void copy_coh_to_lds(void* dst_lds, const void* src, int nbytes) {
-  const int lane = tid() & 63, wave = tid() >> 6;
-  const AS_GLOBAL uint8_t* s8 = (const AS_GLOBAL uint8_t*)src;
-  uint8_t* d8 = (uint8_t*)dst_lds;
-  const int nchunk = (nbytes + 1023) >> 10;
-  for (int c = wave; c < nchunk; c += kWaves) {
-    const int off = (c << 10) + (lane << 4);
-    if (off < nbytes)
-      __builtin_amdgcn_global_load_lds((AS_GLOBAL void*)(s8 + off), (AS_LDS void*)(d8 + (c << 10)), 16, 0, kCohPolicy);
-  }
-}
-
-
 // ---------------------------------------------------------------------------
 // PRE: RMSNorm + rows [r0, r1) of the stacked [Wq; Wk; Wv; Wr] matrix.
 
-// Immutable weight tiles are prefetched into the LDS region P before the
-// task waits for its inputs (the pages' third-ranked gain: weights start
-// streaming before dependencies resolve).  Rows [0, npf) of a job's matrix
-// are then read from P, the rest from HBM.
-// Waves 1..7 issue the copies: wave 0, whose thread 0 polls the flags right
+// Immutable weight tiles are prefetched into LDS before the task waits for
+// its inputs (the pages' third-ranked gain: weights start streaming before
+// dependencies resolve).  Rows [0, npf) of a job's matrix are then read from
+// LDS, the rest from HBM.
+// Waves 1..7 issue the copies with the LDS copy engine (asynchronous: the
+// waves go on at once, the data lands while the task waits): wave 0, whose thread 0 polls the flags right
 // after, keeps its load queue short (a wave's loads complete in order).
 // Each of waves 1..7 copies one contiguous run of 1 KB chunks: measured on
 // this part, that runs at about 2.5x the rate of dealing the chunks to the
@@ -1094,8 +1120,8 @@ struct AttnPage {
 };
 
 // The last nl blocks of a chunk, [bl0, bl0 + nl), are copied into LDS region
-// P before the task waits for q (K/V of earlier positions never change during
-// a step; the block that receives the new token is patched after the wait):
+// P before the task waits for q (K/V of earlier positions never change during a step; the block that
+// receives the new token is patched after the wait):
 // K blocks [nl][16][D], then V blocks [nl][D][16].  In a K block the 16-byte
 // pieces of position r are stored XOR-swizzled by r, so the 16 positions a
 // wave reads at one dim offset sit in different banks.
@@ -1359,83 +1385,54 @@ DEV void attn_plan(const KArgs& a, const Task& t, const Lds& s, int qi) {
 // The lead of segment (b, g) merges all chunks j of the segment:
 //   o_h = sum_j e^(m_jh - M_h) o_jh / sum_j e^(m_jh - M_h) l_jh,  M_h = max_j m_jh.
 // Thread (slice sl, float4 f) takes chunks sl, sl + S, ...; slices are summed
-// in a fixed order.  When all partials fit in region P they are copied there
-// with the LDS DMA (one memory round trip, no registers held); otherwise
-// every thread issues its global loads in batches before using them.
+// in a fixed order.  Every partial is read with 16-byte coherent loads, the
+// chunks' maxima and sums first (through LDS), the outputs in batches of R
+// loads in flight before any is used.
 DEV void attn_combine(const KArgs& a, const Lds& s, const float* parts, int nch, uint16_t* out) {
   const int G = a.group, d = a.d, GD = G * d, CS = attn_part_stride(G, d);
   const int nf4 = GD / 4, S = kThreads / nf4;
   const int sl = tid() / nf4, f = tid() - sl * nf4;
   const bool act = sl < S;
   const int hh = 4 * f / d;
-  float* mj = (float*)s.C;                                                 // [nch][G]
-  float* lj = mj + (size_t)nch * G;                                        // [nch][G]
-  float4* red = (float4*)(s.C + ((2 * (size_t)nch * G * 4 + 15) & ~(size_t)15));  // [kThreads]
+  const uint32_t nbytes = (uint32_t)nch * CS * 4;
+  float* mj = (float*)s.C;                                                 // [nch][kMaxGroup]
+  float* lj = mj + (size_t)nch * kMaxGroup;                                // [nch][kMaxGroup]
+  float4* red = (float4*)(s.C + ((2 * (size_t)nch * kMaxGroup * 4 + 15) & ~(size_t)15));  // [kThreads]
+  // the maxima and sums: 4 float4 per chunk (G <= kMaxGroup = 8 each)
+  for (int q = tid(); q < 4 * nch; q += kThreads) {
+    const int j = q >> 2, k = q & 3;
+    const u32x4_v v = ld_coh16(parts, nbytes, (uint32_t)(j * CS + GD + 4 * k) * 4);
+    *(u32x4_v*)((k < 2 ? mj : lj) + j * kMaxGroup + 4 * (k & 1)) = v;
+  }
+  constexpr int R = 8;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float Ls = 0.f;
-  if ((size_t)nch * CS * 4 <= (size_t)a.pf_bytes) {
-    const int lane = tid() & 63, wave = tid() >> 6;
-    const int n16 = nch * CS / 4;  // 16-byte pieces
-    const AS_GLOBAL uint8_t* src = (const AS_GLOBAL uint8_t*)parts;
-    for (int q = wave; 64 * q < n16; q += kWaves) {
-      const int piece = 64 * q + lane;
-      if (piece < n16)
-        __builtin_amdgcn_global_load_lds((AS_GLOBAL void*)(src + 16 * (size_t)piece), (AS_LDS void*)(s.P + 1024 * q),
-                                         16, 0, kCohPolicy);
-    }
-    prefetch_wait();
-    const float* pl = (const float*)s.P;
-    float M = kNegInf;
-    for (int j = 0; j < nch; ++j) M = fmaxf(M, pl[(size_t)j * CS + GD + hh]);
-    for (int j = 0; j < nch; ++j)
-      Ls += pl[(size_t)j * CS + GD + kMaxGroup + hh] * __expf(pl[(size_t)j * CS + GD + hh] - M);
-    if (act) {
-      for (int j = sl; j < nch; j += S) {
-        const float sc = __expf(pl[(size_t)j * CS + GD + hh] - M);
-        const float4 v = *(const float4*)(pl + (size_t)j * CS + 4 * f);
-        acc.x += v.x * sc;
-        acc.y += v.y * sc;
-        acc.z += v.z * sc;
-        acc.w += v.w * sc;
-      }
-    }
-  } else {
-    constexpr int R = 8;
-    float4 v[R];
-    auto load = [&](int k0) {
+  u32x4_v v[R];
+  auto load = [&](int k0) {
 #pragma unroll
-      for (int k = 0; k < R; ++k) {
-        const int j = sl + S * (k0 + k);
-        const float* pj = parts + (size_t)j * CS + 4 * f;
-        v[k] = (act && j < nch) ? make_float4(ld_coh(pj), ld_coh(pj + 1), ld_coh(pj + 2), ld_coh(pj + 3))
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    };
-    load(0);
-    for (int i = tid(); i < nch * G; i += kThreads) {
-      const int j = i / G, h = i - j * G;
-      mj[i] = ld_coh(parts + (size_t)j * CS + GD + h);
-      lj[i] = ld_coh(parts + (size_t)j * CS + GD + kMaxGroup + h);
+    for (int k = 0; k < R; ++k) {
+      const int j = sl + S * (k0 + k);
+      v[k] = (act && j < nch) ? ld_coh16(parts, nbytes, (uint32_t)(j * CS + 4 * f) * 4) : u32x4_v{0, 0, 0, 0};
     }
-    __syncthreads();
-    float M = kNegInf;
-    for (int j = 0; j < nch; ++j) M = fmaxf(M, mj[j * G + hh]);
-    for (int j = 0; j < nch; ++j) Ls += lj[j * G + hh] * __expf(mj[j * G + hh] - M);
-    for (int k0 = 0;; k0 += R) {
+  };
+  load(0);
+  __syncthreads();
+  float M = kNegInf, Ls = 0.f;
+  for (int j = 0; j < nch; ++j) M = fmaxf(M, mj[j * kMaxGroup + hh]);
+  for (int j = 0; j < nch; ++j) Ls += lj[j * kMaxGroup + hh] * __expf(mj[j * kMaxGroup + hh] - M);
+  for (int k0 = 0;; k0 += R) {
 #pragma unroll
-      for (int k = 0; k < R; ++k) {
-        const int j = sl + S * (k0 + k);
-        if (act && j < nch) {
-          const float sc = __expf(mj[j * G + hh] - M);
-          acc.x += v[k].x * sc;
-          acc.y += v[k].y * sc;
-          acc.z += v[k].z * sc;
-          acc.w += v[k].w * sc;
-        }
+    for (int k = 0; k < R; ++k) {
+      const int j = sl + S * (k0 + k);
+      if (act && j < nch) {
+        const float sc = __expf(mj[j * kMaxGroup + hh] - M);
+        acc.x += __uint_as_float(v[k][0]) * sc;
+        acc.y += __uint_as_float(v[k][1]) * sc;
+        acc.z += __uint_as_float(v[k][2]) * sc;
+        acc.w += __uint_as_float(v[k][3]) * sc;
       }
-      if (sl + S * (k0 + R) >= nch) break;
-      load(k0 + R);
     }
+    if (sl + S * (k0 + R) >= nch) break;
+    load(k0 + R);
   }
   red[tid()] = acc;
   __syncthreads();
@@ -1448,10 +1445,8 @@ DEV void attn_combine(const KArgs& a, const Lds& s, const float* parts, int nch,
       o.z += w.z;
       o.w += w.w;
     }
-    const uint32_t lo = (uint32_t)f2bf(o.x / Ls) | ((uint32_t)f2bf(o.y / Ls) << 16);
-    const uint32_t hi = (uint32_t)f2bf(o.z / Ls) | ((uint32_t)f2bf(o.w / Ls) << 16);
-    st_coh((uint32_t*)(out + 4 * f), lo);
-    st_coh((uint32_t*)(out + 4 * f + 2), hi);
+    st_coh((uint32_t*)(out + 4 * f), pack_bf16(o.x / Ls, o.y / Ls));
+    st_coh((uint32_t*)(out + 4 * f + 2), pack_bf16(o.z / Ls, o.w / Ls));
   }
 }
 
@@ -1780,7 +1775,7 @@ TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have
   }
   if (!wait_counter(a, t.wait[0], t.fanin[0], qi, s.flags + 0)) return kWaves;
   if (a.trace && tid() == 0 && qi < a.trace_cap) a.trace[kTraceWords * (size_t)qi + 1] = wall_clock64();
-  copy_coh_to_lds(xs, a.h + (size_t)l * a.max_batch * a.topk * a.I, n * a.topk * a.I * 2);
+  copy_to_lds<true>(xs, a.h + (size_t)l * a.max_batch * a.topk * a.I, (uint32_t)n * a.topk * a.I * 2);
   prefetch_wait();
   mark(a, qi, 0);
   // expert down projections: the register rows, then the rest from HBM
@@ -1866,7 +1861,7 @@ TASK void task_wo(const KArgs& a, const Task& t, const Lds& s, int qi, int npf) 
   if (!wait_counter(a, t.wait[0], t.fanin[0], qi, s.flags + 0)) return;
   if (a.trace && tid() == 0 && qi < a.trace_cap) a.trace[kTraceWords * (size_t)qi + 1] = wall_clock64();
   uint16_t* xs = (uint16_t*)s.A;
-  copy_coh_to_lds(xs, a.attn_out + (size_t)l * a.max_batch * AD, n * AD * 2);
+  copy_to_lds<true>(xs, a.attn_out + (size_t)l * a.max_batch * AD, (uint32_t)n * AD * 2);
   prefetch_wait();
   mark(a, qi, 0);
   JobPre j;
