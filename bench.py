@@ -203,6 +203,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=25.0)
     ap.add_argument("--trace", default="", help="write a Perfetto timeline of one extra step to this path")
+    ap.add_argument("--steps-per-launch", type=int, default=16,
+                    help="decode steps per launch of the persistent kernel (greedy tokens fed on the device)")
     ap.add_argument("--attn-units", type=int, default=0, help="schedule: attention compute units (0 = default)")
     ap.add_argument("--router-units", type=int, default=0, help="schedule: router compute units (0 = default)")
     ap.add_argument("--copy-calib", type=int, default=0,
@@ -239,23 +241,31 @@ def main():
     B = w.batch
     ctx = torch.tensor(w.context, dtype=torch.int32, device=dev)
     lens_all = torch.stack([ctx + i for i in range(total)]).contiguous()  # [step][B]
-    toks = [torch.tensor([int(w.prompt(b)[w.context[b]]) for b in range(B)], dtype=torch.int32, device=dev),
-            torch.zeros(B, dtype=torch.int32, device=dev)]
+    # toks[i] = the token step i feeds; a launch of k steps from step i writes toks[i + 1 .. i + k]
+    toks = torch.zeros(total + 1, B, dtype=torch.int32, device=dev)
+    toks[0] = torch.tensor([int(w.prompt(b)[w.context[b]]) for b in range(B)], dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    spl = max(1, args.steps_per_launch)
 
-    def run(i):
-        dec.ctx.decode_step(B, toks[i % 2].data_ptr(), dec.page_table.data_ptr(), lens_all[i].data_ptr(),
-                            dec.logits.data_ptr(), toks[(i + 1) % 2].data_ptr(), dec.stream)
+    def run(i, k):
+        """Steps i .. i + k - 1 in one launch."""
+        dec.ctx.decode_steps(B, k, toks[i].data_ptr(), dec.page_table.data_ptr(), lens_all[i].data_ptr(),
+                             dec.logits.data_ptr(), toks[i + 1].data_ptr(), dec.stream)
 
-    for i in range(args.warmup):
-        run(i)
+    def run_range(i0, i1):
+        i = i0
+        while i < i1:
+            k = min(spl, i1 - i)
+            run(i, k)
+            i += k
+
+    run_range(0, args.warmup)
     torch.cuda.synchronize(dev)
     dec.check_error()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize(dev)
     e0.record(stream)
-    for i in range(args.warmup, total):
-        run(i)
+    run_range(args.warmup, total)
     e1.record(stream)
     torch.cuda.synchronize(dev)
     dec.check_error()
@@ -280,7 +290,7 @@ def main():
         ntask = dec.info.n_tasks
         buf = torch.zeros(tr.WORDS * ntask, dtype=torch.int64, device=dev)
         dec.ctx.set_trace(buf.data_ptr(), ntask)
-        run(total - 1)
+        run(total - 1, 1)
         torch.cuda.synchronize(dev)
         dec.ctx.set_trace(None)
         tasks, qoff = dec.ctx.schedule()
@@ -332,6 +342,7 @@ def main():
                         f"{s.head_dim}, {s.n_experts} experts top-{s.top_k} inter {s.inter}, vocab {s.vocab}; "
                         f"batch {B}, context {w.context if B > 1 else w.context[0]}, page {s.page_size}",
             "batch": B,
+            "steps_per_launch": spl,
             "context": w.context[0] if B == 1 else w.context,
         },
         "roofline": {

@@ -156,6 +156,25 @@ int mk_bind(mk_ctx* ctx, const void* const* weights, int32_t n_weights, void* k_
 int mk_decode_step(mk_ctx* ctx, int32_t n, const int32_t* d_tokens, const int32_t* d_page_table,
                    const int32_t* d_seq_lens, float* d_logits, int32_t* d_next_tokens, void* stream);
 
+/* Enqueues `steps` greedy decode steps of the same ragged batch in ONE launch
+ * of the persistent kernel: step s (0-based) feeds each sequence the greedy
+ * token step s - 1 produced (step 0: d_tokens), writes K/V at position
+ * seq_lens[b] + s and attends over 0..seq_lens[b] + s.  No host round trip
+ * and no kernel boundary between steps.
+ *  d_next_tokens: device int32[steps][n], required when steps > 1: the
+ *    greedy token of every step (lowest id on ties).
+ *  d_logits: device float[n][vocab]: the logits of the last step.
+ *  The page table must hold every position up to seq_lens[b] + steps - 1;
+ *  seq_lens is not modified (the caller advances it by `steps`).
+ * The result equals `steps` calls of mk_decode_step that feed back the greedy
+ * token, bit for bit.  Not combinable with mk_set_layer_inputs.
+ * Source: the whole decode loop in one persistent kernel with no launch or
+ * host synchronization between operations (aiweekly.co, paragraph 2;
+ * ainews.surl.tw, paragraph 1); a step-after-step loop is the next step of
+ * that idea. */
+int mk_decode_steps(mk_ctx* ctx, int32_t n, int32_t steps, const int32_t* d_tokens, const int32_t* d_page_table,
+                    const int32_t* d_seq_lens, float* d_logits, int32_t* d_next_tokens, void* stream);
+
 /* Synchronizes `stream`, reads the sticky device error word and clears it.
  * *code receives 0 or an MK_ERR_DEVICE_* code; *cu and *task (may be NULL)
  * the workgroup and task that raised it.  After a device error the context

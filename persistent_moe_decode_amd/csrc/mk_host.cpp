@@ -652,14 +652,18 @@ extern "C" int mk_bind(mk_ctx* c, const void* const* weights, int32_t n_weights,
   return MK_OK;
 }
 
-extern "C" int mk_decode_step(mk_ctx* c, int32_t n, const int32_t* d_tokens, const int32_t* d_page_table,
-                              const int32_t* d_seq_lens, float* d_logits, int32_t* d_next_tokens, void* stream) {
+extern "C" int mk_decode_steps(mk_ctx* c, int32_t n, int32_t steps, const int32_t* d_tokens,
+                               const int32_t* d_page_table, const int32_t* d_seq_lens, float* d_logits,
+                               int32_t* d_next_tokens, void* stream) {
   if (!c) return fail(MK_ERR_INVALID_ARG, "null context");
   if (!c->bound) return fail(MK_ERR_STATE, "context not bound");
   if (c->need_reset) return fail(MK_ERR_STATE, "a device error was reported; call mk_reset first");
   const mk_config& f = c->cfg;
   if (n < 1 || n > f.max_batch) return fail(MK_ERR_INVALID_ARG, "batch outside [1, max_batch]");
   if (!d_tokens || !d_page_table || !d_seq_lens || !d_logits) return fail(MK_ERR_INVALID_ARG, "null step buffer");
+  if (steps < 1 || steps > (1 << 20)) return fail(MK_ERR_INVALID_ARG, "steps outside [1, 2^20]");
+  if (steps > 1 && !d_next_tokens) return fail(MK_ERR_INVALID_ARG, "several steps need the token buffer");
+  if (steps > 1 && c->x_in) return fail(MK_ERR_STATE, "the layer-input hook applies to single steps only");
 
   KArgs a;
   std::memset(&a, 0, sizeof a);
@@ -717,7 +721,9 @@ extern "C" int mk_decode_step(mk_ctx* c, int32_t n, const int32_t* d_tokens, con
   a.k_pool = c->kpool;
   a.v_pool = c->vpool;
   a.n = n;
-  a.epoch = ++c->epoch;
+  a.nsteps = steps;
+  a.step = 0;
+  a.epoch = c->epoch + 1;
   a.tokens = d_tokens;
   a.page_table = d_page_table;
   a.seq_lens = d_seq_lens;
@@ -725,11 +731,14 @@ extern "C" int mk_decode_step(mk_ctx* c, int32_t n, const int32_t* d_tokens, con
   a.next_tok = d_next_tokens;
   a.spin_limit_ticks = (uint64_t)c->spin_us * 100;  // s_memrealtime runs at 100 MHz
   int r = mkk_launch_step(&a, c->ncu, c->lds_bytes, (hipStream_t)stream);
-  if (r) {
-    c->epoch--;
-    return fail(MK_ERR_HIP, std::string("cooperative launch failed: ") + hipGetErrorString((hipError_t)r));
-  }
+  if (r) return fail(MK_ERR_HIP, std::string("cooperative launch failed: ") + hipGetErrorString((hipError_t)r));
+  c->epoch += (uint32_t)steps;
   return MK_OK;
+}
+
+extern "C" int mk_decode_step(mk_ctx* c, int32_t n, const int32_t* d_tokens, const int32_t* d_page_table,
+                              const int32_t* d_seq_lens, float* d_logits, int32_t* d_next_tokens, void* stream) {
+  return mk_decode_steps(c, n, 1, d_tokens, d_page_table, d_seq_lens, d_logits, d_next_tokens, stream);
 }
 
 extern "C" int mk_get_error(mk_ctx* c, int32_t* code, int32_t* cu, int32_t* task, void* stream) {

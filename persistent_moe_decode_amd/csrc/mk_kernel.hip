@@ -293,12 +293,12 @@ DEV uint32_t counter_sum(const KArgs& a, int idx) {
 // The abort flag is read every 32 polls, not before the first one (that
 // would put a dependent round trip in front of every wait).  Returns false
 // when the grid is aborting or the wait timed out.
-DEV bool wait_counter(const KArgs& a, int idx, int fanin, int task, int32_t* slot) {
+DEV bool wait_counter_at(const KArgs& a, int idx, int fanin, int task, int32_t* slot, uint32_t epoch) {
   if (tid() < 64) {
     const int lane = tid();
     int ok = 1;
     if (idx >= 0) {
-      const uint32_t want = a.epoch * (uint32_t)fanin;
+      const uint32_t want = epoch * (uint32_t)fanin;
       const uint64_t t0 = wall_clock64();
       uint32_t it = 0;
       while ((int32_t)(counter_sum(a, idx) - want) < 0) {
@@ -321,15 +321,8 @@ DEV bool wait_counter(const KArgs& a, int idx, int fanin, int task, int32_t* slo
   return *slot != 0;
 }
 
-// One look at a counter (no waiting): true in every thread when it has
-// already reached epoch * fanin.
-DEV bool counter_done(const KArgs& a, int idx, int fanin, int32_t* slot) {
-  if (tid() < 64) {
-    const bool done = idx < 0 || (int32_t)(counter_sum(a, idx) - a.epoch * (uint32_t)fanin) >= 0;
-    if (tid() == 0) *slot = done ? 1 : 0;
-  }
-  __syncthreads();
-  return *slot != 0;
+DEV bool wait_counter(const KArgs& a, int idx, int fanin, int task, int32_t* slot) {
+  return wait_counter_at(a, idx, fanin, task, slot, a.epoch);
 }
 
 // Waves 0 .. wait_waves - 1 (those that stored what the consumers read) wait
@@ -427,8 +420,10 @@ DEV void mark(const KArgs& a, int qi, int k) {
   if (a.trace && tid() == 0 && qi < a.trace_cap) a.trace[kTraceWords * (size_t)qi + 2 + k] = wall_clock64();
 }
 
+// The token of sequence b in this step: the caller's at step 0, the greedy
+// token of the previous step (written in this launch) after that.
 DEV const gu16* token_row(const KArgs& a, int b, int task) {
-  int tok = a.tokens[b];
+  int tok = a.step == 0 ? a.tokens[b] : (int)ld_coh((const uint32_t*)a.next_tok + (size_t)(a.step - 1) * a.n + b);
   if (tok < 0 || tok >= a.V) {
     raise_error(a, MK_ERR_DEVICE_TOKEN, task, b);
     tok = 0;
@@ -1365,7 +1360,7 @@ DEV void attn_plan(const KArgs& a, const Task& t, const Lds& s, int qi) {
     const int cap = a.max_pages * a.ps;
 #pragma unroll
     for (int b = 0; b < kMaxBatch; ++b) {
-      int p = b < a.n ? a.seq_lens[b] : 0;
+      int p = b < a.n ? a.seq_lens[b] + a.step : 0;
       if (b < a.n && (p < 0 || p + 1 > cap)) {
         raise_error(a, MK_ERR_DEVICE_SEQ, qi, b);
         p = p < 0 ? 0 : cap - 1;
@@ -1990,58 +1985,71 @@ TASK void task_lmhead(const KArgs& a, const Task& t, const Lds& s, int qi) {
         if (better(x, xi, v, i)) { v = x; i = xi; }
       }
       block_argmax(v, i, s.red);
-      if (tid() == 0 && a.next_tok) a.next_tok[b] = i;
+      if (tid() == 0 && a.next_tok) st_coh((uint32_t*)a.next_tok + (size_t)a.step * a.n + b, (uint32_t)i);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
 
-extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a) {
+// Runs a.nsteps decode steps: step s uses epoch a.epoch + s (counter targets,
+// tags) and positions seq_lens + s; its layer-0 tasks wait for step s - 1's
+// LM head (the greedy token).  Every queue ends with its LM head task, so a
+// queue starts step s + 1 only after its share of step s.
+extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a0) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
+  KArgs a = a0;
   const Lds s = carve(lds_raw, a);
   const int cu = blockIdx.x;
   const int q0 = a.queue_off[cu], q1 = a.queue_off[cu + 1];
-  if (tid() == 0) {
-    s.flags[16] = -1;  // no attention plan cached yet
-    s.flags[18] = 0;   // no PRE tile copied ahead
-  }
-  __syncthreads();
-  int xs_layer = -1;                 // layer whose normalized input region A holds
-  int tk_layer = -1;                 // layer whose top-k region B holds
-  for (int q = q0; q < q1; ++q) {
-    const Task t = a.tasks[q];
-    uint64_t t_fetch = 0, t_ready = 0;
-    if (a.trace && tid() == 0) t_fetch = wall_clock64();
-    // immutable weights start streaming into LDS before the inputs are ready
-    const int npf = task_prefetch(a, t, s, q);
-    // attention, Wo and output tasks wait inside, once their loads are in flight; gate/up
-    // tasks poll the tagged router logits inside
-    const bool own_wait = t.op == OP_ATTN || t.op == OP_OUT || t.op == OP_WO || t.op == OP_GATEUP;
-    bool ok = own_wait || wait_counter(a, t.wait[0], t.fanin[0], q, s.flags + 0);
-    if (ok && !own_wait && t.wait[1] >= 0) ok = wait_counter(a, t.wait[1], t.fanin[1], q, s.flags + 1);
-    if (a.trace && tid() == 0) t_ready = wall_clock64();
-    int wait_waves = kWaves;
-    if (ok) {
-      switch (t.op) {
-        case OP_PRE: task_pre(a, t, s, q, npf); break;
-        case OP_ATTN: task_attn(a, t, s, q); break;
-        case OP_GATEUP: task_gateup(a, t, s, q, xs_layer == t.layer); break;
-        case OP_OUT: wait_waves = task_out(a, t, s, q, tk_layer == t.layer); break;
-        case OP_WO: task_wo(a, t, s, q, npf); break;
-        case OP_LMHEAD: task_lmhead(a, t, s, q); break;
-        default: break;
-      }
+  for (int step = 0; step < a0.nsteps; ++step) {
+    a.step = step;
+    a.epoch = a0.epoch + (uint32_t)step;
+    if (tid() == 0) {
+      s.flags[16] = -1;  // no attention plan cached yet (positions moved)
+      s.flags[18] = 0;   // no PRE tile copied ahead
     }
-    xs_layer = ok && t.op == OP_PRE ? t.layer : (ok && t.op == OP_GATEUP ? xs_layer : -1);
-    tk_layer = ok && (t.op == OP_GATEUP || t.op == OP_OUT) ? t.layer : (t.op == OP_LMHEAD ? -1 : tk_layer);
-    if (t.tagged) __syncthreads();  // consumers poll the tagged output itself
-    else signal_counter(a, t.signal, t.slot, wait_waves);
-    if (a.trace && tid() == 0 && q < a.trace_cap) {
-      uint64_t* r = a.trace + kTraceWords * (size_t)q;
-      r[0] = t_fetch;
-      if (!own_wait) r[1] = t_ready;
-      r[6] = wall_clock64();
+    __syncthreads();
+    int xs_layer = -1;                 // layer whose normalized input region A holds
+    int tk_layer = -1;                 // layer whose top-k region B holds
+    for (int q = q0; q < q1; ++q) {
+      const Task t = a.tasks[q];
+      uint64_t t_fetch = 0, t_ready = 0;
+      if (a.trace && tid() == 0) t_fetch = wall_clock64();
+      // immutable weights start streaming into LDS before the inputs are ready
+      const int npf = task_prefetch(a, t, s, q);
+      bool ok = true;
+      // after the first step, layer 0 needs the previous step's greedy token
+      if (step > 0 && t.layer == 0 && (t.op == OP_PRE || t.op == OP_OUT))
+        ok = wait_counter_at(a, ctr_index(a.L, C_DONE), a.n_lm, q, s.flags + 1, a.epoch - 1);
+      // attention, Wo and output tasks wait inside, once their loads are in flight; gate/up
+      // tasks poll the tagged router logits inside
+      const bool own_wait = t.op == OP_ATTN || t.op == OP_OUT || t.op == OP_WO || t.op == OP_GATEUP;
+      if (ok && !own_wait) ok = wait_counter(a, t.wait[0], t.fanin[0], q, s.flags + 0);
+      if (ok && !own_wait && t.wait[1] >= 0) ok = wait_counter(a, t.wait[1], t.fanin[1], q, s.flags + 1);
+      if (a.trace && tid() == 0) t_ready = wall_clock64();
+      int wait_waves = kWaves;
+      if (ok) {
+        switch (t.op) {
+          case OP_PRE: task_pre(a, t, s, q, npf); break;
+          case OP_ATTN: task_attn(a, t, s, q); break;
+          case OP_GATEUP: task_gateup(a, t, s, q, xs_layer == t.layer); break;
+          case OP_OUT: wait_waves = task_out(a, t, s, q, tk_layer == t.layer); break;
+          case OP_WO: task_wo(a, t, s, q, npf); break;
+          case OP_LMHEAD: task_lmhead(a, t, s, q); break;
+          default: break;
+        }
+      }
+      xs_layer = ok && t.op == OP_PRE ? t.layer : (ok && t.op == OP_GATEUP ? xs_layer : -1);
+      tk_layer = ok && (t.op == OP_GATEUP || t.op == OP_OUT) ? t.layer : (t.op == OP_LMHEAD ? -1 : tk_layer);
+      if (t.tagged) __syncthreads();  // consumers poll the tagged output itself
+      else signal_counter(a, t.signal, t.slot, wait_waves);
+      if (a.trace && tid() == 0 && q < a.trace_cap) {
+        uint64_t* r = a.trace + kTraceWords * (size_t)q;
+        r[0] = t_fetch;
+        if (!own_wait) r[1] = t_ready;
+        r[6] = wall_clock64();
+      }
     }
   }
 }

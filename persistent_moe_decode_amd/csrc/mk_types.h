@@ -118,8 +118,10 @@ struct KArgs {
   const int32_t* page_table;
   const int32_t* seq_lens;
   float* logits;
-  int32_t* next_tok;
+  int32_t* next_tok;         // [nsteps][n] greedy tokens (step s > 0 reads step s - 1's), or NULL at one step
   uint64_t spin_limit_ticks; // s_memrealtime ticks (100 MHz)
+  int32_t nsteps;            // decode steps in this launch
+  int32_t step;              // the step being run (set by the kernel: epoch + step, positions + step)
 };
 
 // Weight table order.

@@ -81,6 +81,7 @@ def lib():
         "mk_build_schedule": [P, ctypes.POINTER(ScheduleParams), ctypes.POINTER(SZ)],
         "mk_bind": [P, ctypes.POINTER(P), I32, P, P, P, SZ, P],
         "mk_decode_step": [P, I32, P, P, P, P, P, P],
+        "mk_decode_steps": [P, I32, I32, P, P, P, P, P, P],
         "mk_get_error": [P, pi32, pi32, pi32, P],
         "mk_reset": [P, P],
         "mk_set_spin_limit_us": [P, I64],
@@ -205,6 +206,11 @@ class Context:
                     next_ptr: int | None, stream: int):
         check(lib().mk_decode_step(self.h, n, tokens_ptr, page_table_ptr, seq_lens_ptr, logits_ptr,
                                    next_ptr or None, stream), "mk_decode_step")
+
+    def decode_steps(self, n: int, steps: int, tokens_ptr: int, page_table_ptr: int, seq_lens_ptr: int,
+                     logits_ptr: int, next_ptr: int | None, stream: int):
+        check(lib().mk_decode_steps(self.h, n, steps, tokens_ptr, page_table_ptr, seq_lens_ptr, logits_ptr,
+                                    next_ptr or None, stream), "mk_decode_steps")
 
     def get_error(self, stream: int):
         code, cu, task = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
