@@ -386,14 +386,27 @@ DEV bool wait_ticket(const KArgs& a, uint32_t* ticket, uint32_t want, int task, 
 
 // Every thread polls its own tagged words (load_ready loads them and says
 // whether all carry this step's epoch) until every thread's do; the block
-// votes after each round.  Bounded like wait_counter; slot is an LDS word.
-// Returns false in every thread when the grid is aborting or the wait timed out.
+// votes after each round.  The vote lives in three LDS words taken in turn
+// (slot[1..3], so the kernel keeps no static LDS of its own): thread 0 sets
+// the next round's word to 1 before this round's barrier, any thread not
+// ready clears this round's word, and all read it after the barrier.  The word
+// set for the next round was last read two rounds ago, before the previous
+// barrier.  slot[0] carries the abort / time-out decision.  Bounded like
+// wait_counter.  Returns false in every thread when the grid is aborting or
+// the wait timed out.
 template <class F>
 DEV bool poll_block(const KArgs& a, int task, int32_t* slot, F&& load_ready) {
+  int32_t* vote = slot + 1;
   const uint64_t t0 = wall_clock64();
-  for (uint32_t it = 1;; ++it) {
-    if (__syncthreads_and(load_ready())) return true;
-    if ((it & 31) == 0) {
+  if (tid() == 0) vote[0] = 1;
+  __syncthreads();
+  for (uint32_t it = 0;; ++it) {
+    const uint32_t p = it % 3;
+    if (!load_ready()) vote[p] = 0;
+    if (tid() == 0) vote[p == 2 ? 0 : p + 1] = 1;
+    __syncthreads();
+    if (vote[p]) return true;
+    if ((it & 31) == 31) {
       if (tid() == 0) *slot = aborting(a) ? 1 : (wall_clock64() - t0 > a.spin_limit_ticks ? 2 : 0);
       __syncthreads();
       const int stop = *slot;
@@ -1808,7 +1821,7 @@ TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have
   // the attention output times Wo for these rows (attention units), polled as tagged words
   const uint64_t* wot = a.wot + (size_t)l * a.max_batch * a.H + t.r0;
   float wo_first = 0.f;
-  const bool ok = poll_block(a, qi, s.flags + 19, [&]() -> int {
+  const bool ok = poll_block(a, qi, s.flags + 19, /* flags[19..22] */ [&]() -> int {
     int r = 1;
     for (int e = tid(); e < nr * n; e += kThreads) {
       const uint64_t w = ld_tag(wot + (size_t)(e % n) * a.H + e / n);

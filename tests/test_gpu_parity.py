@@ -47,6 +47,18 @@ def test_tiny_ragged_batch_edges():
     _check(parity.run(w, mode="isolated", log=_log), "tiny_ragged_edges")
 
 
+def test_tiny_schedule_takes_all_lds():
+    """Batch 1 at 45 tokens: the schedule's dynamic LDS is the whole 160 KiB of a compute unit, which
+    launches only while the kernel itself reserves no static LDS."""
+    from persistent_moe_decode_amd import mk
+    from tests import parity
+    w = synth.Workload("tiny_lds_full", synth.TINY, batch=1, steps=3, context=[45])
+    c = mk.Context(mk.config_from_shape(w.shape, w.batch, w.max_pages_per_seq, w.num_pages))
+    c.build_schedule(0, 45 + w.steps // 2)
+    assert c.info().lds_bytes == 160 * 1024
+    _check(parity.run(w, mode="isolated", log=_log), "tiny_lds_full")
+
+
 def test_mid_isolated_64_steps():
     """Mid MoE, 2048-token synthetic context, shuffled page order, 64 greedy steps, every layer on oracle inputs."""
     from tests import parity
