@@ -136,6 +136,29 @@ int mk_build_schedule(mk_ctx* ctx, const mk_schedule_params* params, size_t* wor
 int mk_bind(mk_ctx* ctx, const void* const* weights, int32_t n_weights, void* k_pool, void* v_pool,
             void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code that will be captured
+ * into a HIP graph, tight serving loops, harnesses that forbid hipMalloc): the
+ * same as mk_bind, but the workspace is the library's static one, a 256-byte
+ * aligned array of mk_scratch_capacity() bytes (64 MiB) that every GPU the
+ * library runs on holds until the process ends.  Binds on the current device;
+ * makes no device or host allocation (no hipMalloc, hipFree or allocating
+ * library call).  Uploads the task table and clears the counters, tickets,
+ * error word and epoch-tagged words, like mk_bind.
+ * Errors: MK_ERR_INVALID_ARG if the workspace mk_build_schedule reported is
+ * larger than mk_scratch_capacity() (nothing is bound then), or for the
+ * argument errors of mk_bind; MK_ERR_HIP if the array's device address cannot
+ * be found.
+ * One array per GPU: binding another context on the same device overwrites
+ * this one's table and state, after which this context's calls fail with
+ * MK_ERR_STATE until it is bound again.  Calls that overlap on one GPU (two
+ * contexts' steps in flight on different streams, or a bind while a step
+ * runs) race on the array and give wrong results. */
+int mk_bind_scratch(mk_ctx* ctx, const void* const* weights, int32_t n_weights, void* k_pool, void* v_pool,
+                    void* stream);
+
+/* Size in bytes of the static workspace mk_bind_scratch uses (host only). */
+size_t mk_scratch_capacity(void);
+
 /* Enqueues one decode step for a ragged batch of n sequences (1 <= n <= max_batch).
  *  d_tokens: device int32[n], the new token of each sequence.
  *  d_page_table: device int32[n][max_pages_per_seq], physical page of each

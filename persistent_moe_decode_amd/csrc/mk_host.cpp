@@ -17,6 +17,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -27,6 +28,8 @@ using namespace mk;
 
 extern "C" int mkk_launch_step(const KArgs* a, int grid, size_t lds_bytes, hipStream_t stream);
 extern "C" int mkk_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t stream);
+extern "C" size_t mkk_scratch_bytes();
+extern "C" int mkk_scratch(int* device, void** ptr);
 
 namespace {
 
@@ -58,9 +61,11 @@ struct mk_ctx {
   size_t lds_bytes = 0;
   std::vector<Task> tasks;
   std::vector<int32_t> qoff;
+  std::vector<double> inv_freq;  // rotary frequencies theta^(-2i/d), uploaded by bind
   WsLayout ws;
   // bound state
   uint8_t* wsp = nullptr;
+  int scratch_dev = -1;  // device whose static workspace this context is bound to, else -1
   uint16_t* kpool = nullptr;
   uint16_t* vpool = nullptr;
   uint32_t epoch = 0;
@@ -101,7 +106,32 @@ extern "C" int mk_create(const mk_config* cfg, mk_ctx** out) {
   return MK_OK;
 }
 
-extern "C" void mk_destroy(mk_ctx* ctx) { delete ctx; }
+// Which context each device's static workspace is bound to: binding another context there
+// overwrites the table and state of the previous one, whose later calls then fail.
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+mk_ctx* g_scratch_owner[kMaxDevices] = {};
+}  // namespace
+
+static void release_scratch(mk_ctx* c) {
+  if (c->scratch_dev < 0) return;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_owner[c->scratch_dev] == c) g_scratch_owner[c->scratch_dev] = nullptr;
+  c->scratch_dev = -1;
+}
+
+static bool scratch_lost(const mk_ctx* c) {
+  if (c->scratch_dev < 0) return false;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch_owner[c->scratch_dev] != c;
+}
+
+extern "C" void mk_destroy(mk_ctx* ctx) {
+  if (!ctx) return;
+  release_scratch(ctx);
+  delete ctx;
+}
 
 extern "C" const char* mk_last_error_message(void) { return g_msg.c_str(); }
 
@@ -498,6 +528,9 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
   int r = simulate(c, nullptr);
   if (r) return r;
   c->ws = layout_workspace(c);
+  c->inv_freq.resize(f.head_dim / 2);
+  for (int i = 0; i < f.head_dim / 2; ++i) c->inv_freq[i] = std::pow(f.rope_theta, -(2.0 * i) / f.head_dim);
+  release_scratch(c);
   c->built = true;
   c->bound = false;
   if (workspace_bytes) *workspace_bytes = c->ws.total;
@@ -615,35 +648,37 @@ static int zero_state(mk_ctx* c, hipStream_t s) {
   return MK_OK;
 }
 
-extern "C" int mk_bind(mk_ctx* c, const void* const* weights, int32_t n_weights, void* k_pool, void* v_pool,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+// Checks the bound buffers; the workspace is checked by the caller.
+static int check_bind_args(const mk_ctx* c, const void* const* weights, int32_t n_weights, const void* k_pool,
+                           const void* v_pool) {
   if (!c) return fail(MK_ERR_INVALID_ARG, "null context");
-  if (!c->built) return fail(MK_ERR_STATE, "mk_build_schedule must run before mk_bind");
+  if (!c->built) return fail(MK_ERR_STATE, "mk_build_schedule must run before binding");
   const mk_config& f = c->cfg;
   if (!weights || n_weights != 3 + 7 * f.n_layers) return fail(MK_ERR_INVALID_ARG, "weights must hold 3 + 7*n_layers pointers");
   for (int i = 0; i < n_weights; ++i)
     if (!weights[i]) return fail(MK_ERR_INVALID_ARG, "null weight pointer " + std::to_string(i));
-  if (!k_pool || !v_pool || !workspace) return fail(MK_ERR_INVALID_ARG, "null pool or workspace");
-  if (workspace_bytes < c->ws.total) return fail(MK_ERR_INVALID_ARG, "workspace smaller than reported");
-  if (((uintptr_t)workspace) % 256) return fail(MK_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  if (!k_pool || !v_pool) return fail(MK_ERR_INVALID_ARG, "null pool");
   for (int i = 0; i < n_weights; ++i)
     if (((uintptr_t)weights[i]) % 16) return fail(MK_ERR_INVALID_ARG, "weight pointer not 16-byte aligned");
   if (((uintptr_t)k_pool) % 16 || ((uintptr_t)v_pool) % 16) return fail(MK_ERR_INVALID_ARG, "pool not 16-byte aligned");
-  hipStream_t s = (hipStream_t)stream;
-  c->wsp = (uint8_t*)workspace;
+  return MK_OK;
+}
+
+// Uploads the task table, queue offsets, weight table and rotary frequencies into the
+// workspace and clears its state region.  Makes no allocation: the uploads read the
+// context's own tables and the caller's pointer array.
+static int bind_workspace(mk_ctx* c, const void* const* weights, int32_t n_weights, void* k_pool, void* v_pool,
+                          uint8_t* ws, hipStream_t s) {
+  static_assert(sizeof(const void*) == sizeof(uint64_t), "the weight table holds 64-bit device addresses");
+  c->bound = false;
+  c->wsp = ws;
   c->kpool = (uint16_t*)k_pool;
   c->vpool = (uint16_t*)v_pool;
-
-  std::vector<uint64_t> wtab(n_weights);
-  for (int i = 0; i < n_weights; ++i) wtab[i] = (uint64_t)(uintptr_t)weights[i];
-  std::vector<double> inv_freq(f.head_dim / 2);
-  for (int i = 0; i < f.head_dim / 2; ++i) inv_freq[i] = std::pow(f.rope_theta, -(2.0 * i) / f.head_dim);
-
   hipError_t e;
   if ((e = hipMemcpyAsync(c->wsp + c->ws.tasks, c->tasks.data(), sizeof(Task) * c->tasks.size(), hipMemcpyHostToDevice, s)) ||
       (e = hipMemcpyAsync(c->wsp + c->ws.queue_off, c->qoff.data(), 4 * c->qoff.size(), hipMemcpyHostToDevice, s)) ||
-      (e = hipMemcpyAsync(c->wsp + c->ws.wtab, wtab.data(), 8 * wtab.size(), hipMemcpyHostToDevice, s)) ||
-      (e = hipMemcpyAsync(c->wsp + c->ws.inv_freq, inv_freq.data(), 8 * inv_freq.size(), hipMemcpyHostToDevice, s)))
+      (e = hipMemcpyAsync(c->wsp + c->ws.wtab, weights, 8 * (size_t)n_weights, hipMemcpyHostToDevice, s)) ||
+      (e = hipMemcpyAsync(c->wsp + c->ws.inv_freq, c->inv_freq.data(), 8 * c->inv_freq.size(), hipMemcpyHostToDevice, s)))
     return hip_fail(e, "hipMemcpyAsync (schedule upload)");
   int r = zero_state(c, s);
   if (r) return r;
@@ -652,11 +687,47 @@ extern "C" int mk_bind(mk_ctx* c, const void* const* weights, int32_t n_weights,
   return MK_OK;
 }
 
+extern "C" int mk_bind(mk_ctx* c, const void* const* weights, int32_t n_weights, void* k_pool, void* v_pool,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  int r = check_bind_args(c, weights, n_weights, k_pool, v_pool);
+  if (r) return r;
+  if (!workspace) return fail(MK_ERR_INVALID_ARG, "null workspace");
+  if (workspace_bytes < c->ws.total) return fail(MK_ERR_INVALID_ARG, "workspace smaller than reported");
+  if (((uintptr_t)workspace) % 256) return fail(MK_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  release_scratch(c);
+  return bind_workspace(c, weights, n_weights, k_pool, v_pool, (uint8_t*)workspace, (hipStream_t)stream);
+}
+
+extern "C" size_t mk_scratch_capacity(void) { return mkk_scratch_bytes(); }
+
+extern "C" int mk_bind_scratch(mk_ctx* c, const void* const* weights, int32_t n_weights, void* k_pool, void* v_pool,
+                               void* stream) {
+  int r = check_bind_args(c, weights, n_weights, k_pool, v_pool);
+  if (r) return r;
+  const size_t cap = mkk_scratch_bytes();
+  if (c->ws.total > cap)
+    return fail(MK_ERR_INVALID_ARG, "workspace of " + std::to_string(c->ws.total) +
+                                        " bytes exceeds the static workspace of " + std::to_string(cap) + " bytes");
+  int dev = -1;
+  void* p = nullptr;
+  int e = mkk_scratch(&dev, &p);
+  if (e) return hip_fail((hipError_t)e, "static workspace address");
+  if (dev >= kMaxDevices) return fail(MK_ERR_HIP, "device index beyond the static workspace table");
+  release_scratch(c);
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    g_scratch_owner[dev] = c;
+  }
+  c->scratch_dev = dev;
+  return bind_workspace(c, weights, n_weights, k_pool, v_pool, (uint8_t*)p, (hipStream_t)stream);
+}
+
 extern "C" int mk_decode_steps(mk_ctx* c, int32_t n, int32_t steps, const int32_t* d_tokens,
                                const int32_t* d_page_table, const int32_t* d_seq_lens, float* d_logits,
                                int32_t* d_next_tokens, void* stream) {
   if (!c) return fail(MK_ERR_INVALID_ARG, "null context");
   if (!c->bound) return fail(MK_ERR_STATE, "context not bound");
+  if (scratch_lost(c)) return fail(MK_ERR_STATE, "the static workspace was bound to another context since");
   if (c->need_reset) return fail(MK_ERR_STATE, "a device error was reported; call mk_reset first");
   const mk_config& f = c->cfg;
   if (n < 1 || n > f.max_batch) return fail(MK_ERR_INVALID_ARG, "batch outside [1, max_batch]");
@@ -744,6 +815,7 @@ extern "C" int mk_decode_step(mk_ctx* c, int32_t n, const int32_t* d_tokens, con
 extern "C" int mk_get_error(mk_ctx* c, int32_t* code, int32_t* cu, int32_t* task, void* stream) {
   if (!c || !code) return fail(MK_ERR_INVALID_ARG, "null argument");
   if (!c->bound) return fail(MK_ERR_STATE, "context not bound");
+  if (scratch_lost(c)) return fail(MK_ERR_STATE, "the static workspace was bound to another context since");
   hipStream_t s = (hipStream_t)stream;
   int32_t ew[E_WORDS];
   hipError_t e;
@@ -764,5 +836,6 @@ extern "C" int mk_get_error(mk_ctx* c, int32_t* code, int32_t* cu, int32_t* task
 extern "C" int mk_reset(mk_ctx* c, void* stream) {
   if (!c) return fail(MK_ERR_INVALID_ARG, "null context");
   if (!c->bound) return fail(MK_ERR_STATE, "context not bound");
+  if (scratch_lost(c)) return fail(MK_ERR_STATE, "the static workspace was bound to another context since");
   return zero_state(c, (hipStream_t)stream);
 }

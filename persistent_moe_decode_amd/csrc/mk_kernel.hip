@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/mk.h"
 #include "mk_types.h"
 
@@ -2077,6 +2079,38 @@ extern "C" int mkk_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t strea
   if (blocks > 1024) blocks = 1024;
   hipLaunchKernelGGL(mk_fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, v, n);
   return (int)hipGetLastError();
+}
+
+// Workspace for callers that cannot allocate device memory (mk_bind_scratch).
+// Each GPU that loads this library holds one copy until the process ends; host
+// code never passes the name `scratch` to a kernel (on the host it is only a
+// stand-in), it asks mkk_scratch for this device's address instead.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+extern "C" size_t mkk_scratch_bytes() { return kScratchBytes; }
+
+// Device address of the current device's copy of `scratch`, looked up once per
+// device with that device current.
+extern "C" int mkk_scratch(int* device, void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (!p || ((uintptr_t)p) % 256) return (int)hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *device = dev;
+  *ptr = addr[dev];
+  return 0;
 }
 
 extern "C" int mkk_launch_step(const KArgs* a, int grid, size_t lds_bytes, hipStream_t stream) {

@@ -80,6 +80,7 @@ def lib():
         "mk_create": [ctypes.POINTER(MkConfig), ctypes.POINTER(P)],
         "mk_build_schedule": [P, ctypes.POINTER(ScheduleParams), ctypes.POINTER(SZ)],
         "mk_bind": [P, ctypes.POINTER(P), I32, P, P, P, SZ, P],
+        "mk_bind_scratch": [P, ctypes.POINTER(P), I32, P, P, P],
         "mk_decode_step": [P, I32, P, P, P, P, P, P],
         "mk_decode_steps": [P, I32, I32, P, P, P, P, P, P],
         "mk_get_error": [P, pi32, pi32, pi32, P],
@@ -104,6 +105,8 @@ def lib():
     L.mk_destroy.restype = None
     L.mk_schedule_params_default.argtypes = [ctypes.POINTER(ScheduleParams)]
     L.mk_schedule_params_default.restype = None
+    L.mk_scratch_capacity.argtypes = []
+    L.mk_scratch_capacity.restype = SZ
     _lib = L
     return L
 
@@ -202,6 +205,11 @@ class Context:
         arr = (ctypes.c_void_p * len(weight_ptrs))(*weight_ptrs)
         check(lib().mk_bind(self.h, arr, len(weight_ptrs), k_pool_ptr, v_pool_ptr, ws_ptr, ws_bytes, stream), "mk_bind")
 
+    def bind_scratch(self, weight_ptrs, k_pool_ptr: int, v_pool_ptr: int, stream: int):
+        """Bind with the library's static workspace instead of a caller-provided one."""
+        arr = (ctypes.c_void_p * len(weight_ptrs))(*weight_ptrs)
+        check(lib().mk_bind_scratch(self.h, arr, len(weight_ptrs), k_pool_ptr, v_pool_ptr, stream), "mk_bind_scratch")
+
     def decode_step(self, n: int, tokens_ptr: int, page_table_ptr: int, seq_lens_ptr: int, logits_ptr: int,
                     next_ptr: int | None, stream: int):
         check(lib().mk_decode_step(self.h, n, tokens_ptr, page_table_ptr, seq_lens_ptr, logits_ptr,
@@ -229,6 +237,11 @@ class Context:
 
     def set_spin_limit_us(self, us: int):
         check(lib().mk_set_spin_limit_us(self.h, us), "mk_set_spin_limit_us")
+
+
+def scratch_capacity() -> int:
+    """Bytes of the static workspace that Context.bind_scratch uses."""
+    return int(lib().mk_scratch_capacity())
 
 
 def simulate_table(tasks, qoff, n_counters: int):

@@ -60,8 +60,9 @@ class DeviceDecoder:
     """All device state of one workload, bound to one mk context."""
 
     def __init__(self, w: synth.Workload, device: str = "cuda:0", num_cus: int = 0, ctx_hint: int | None = None,
-                 max_batch: int | None = None, **sched):
-        """sched: further mk_schedule_params fields (attn_units, router_units, prefetch_bytes)."""
+                 max_batch: int | None = None, static_workspace: bool = False, **sched):
+        """static_workspace: bind with the library's static workspace (no workspace tensor);
+        sched: further mk_schedule_params fields (attn_units, router_units, prefetch_bytes)."""
         self.w = w
         self.shape = s = w.shape
         self.dev = torch.device(device)
@@ -93,16 +94,21 @@ class DeviceDecoder:
             v_shape = (s.n_layers, self.num_pages, s.n_kv_heads, s.head_dim, s.page_size)
             self.k_pool = torch.full(k_shape, POISON, dtype=torch.int16, device=self.dev)
             self.v_pool = torch.full(v_shape, POISON, dtype=torch.int16, device=self.dev)
-            self.ws = torch.zeros(self.ws_bytes + 256, dtype=torch.uint8, device=self.dev)
-            self.ws_base = (self.ws.data_ptr() + 255) // 256 * 256
+            if not static_workspace:
+                self.ws = torch.zeros(self.ws_bytes + 256, dtype=torch.uint8, device=self.dev)
+                self.ws_base = (self.ws.data_ptr() + 255) // 256 * 256
             self.page_table = torch.from_numpy(self.page_table_np).to(self.dev)
             self.tokens = torch.zeros(self.B, dtype=torch.int32, device=self.dev)
             self.seq_lens = torch.zeros(self.B, dtype=torch.int32, device=self.dev)
             self.logits = torch.zeros(self.B, s.vocab, dtype=torch.float32, device=self.dev)
             self.next_tok = torch.zeros(self.B, dtype=torch.int32, device=self.dev)
             torch.cuda.synchronize(self.dev)
-            self.ctx.bind([t.data_ptr() for t in self.weights], self.k_pool.data_ptr(), self.v_pool.data_ptr(),
-                          self.ws_base, self.ws_bytes, self.stream)
+            ptrs = [t.data_ptr() for t in self.weights]
+            if static_workspace:
+                self.ctx.bind_scratch(ptrs, self.k_pool.data_ptr(), self.v_pool.data_ptr(), self.stream)
+            else:
+                self.ctx.bind(ptrs, self.k_pool.data_ptr(), self.v_pool.data_ptr(), self.ws_base, self.ws_bytes,
+                              self.stream)
 
     # ------------------------------------------------------------------ KV
 
@@ -164,6 +170,8 @@ class DeviceDecoder:
     # ------------------------------------------------------------------ workspace views (debugging, parity)
 
     def _ws_view(self, off: int, count: int, dtype) -> torch.Tensor:
+        if not hasattr(self, "ws"):
+            raise RuntimeError("bound to the static workspace: no workspace tensor to view")
         esz = torch.tensor([], dtype=dtype).element_size()
         start = self.ws_base - self.ws.data_ptr() + off
         return self.ws[start:start + count * esz].view(dtype)

@@ -352,3 +352,21 @@ def test_schedule_params_negative_counts_rejected():
         with pytest.raises(mk.MkError) as e:
             c.build_schedule(**{"num_cus": 256, **kw})
         assert e.value.code == mk.CODES["MK_ERR_INVALID_ARG"], kw
+
+
+def test_bind_scratch_rejects_a_workspace_beyond_the_static_one():
+    """A schedule whose workspace exceeds the static array is refused before any device call."""
+    import dataclasses
+    shape = dataclasses.replace(synth.workload("moe30b_bs8_ragged").shape, n_layers=96)
+    c = _ctx(shape, 8, 64, 512)
+    ws = c.build_schedule(256, 4096)
+    cap = mk.scratch_capacity()
+    assert cap == 64 << 20 and ws > cap
+    fake = [16 * (i + 1) for i in range(3 + 7 * shape.n_layers)]
+    with pytest.raises(mk.MkError) as e:
+        c.bind_scratch(fake, 1 << 20, 2 << 20, 0)
+    assert e.value.code == mk.CODES["MK_ERR_INVALID_ARG"]
+    assert "exceeds the static workspace" in str(e.value)
+    with pytest.raises(mk.MkError) as e:  # nothing was bound
+        c.decode_step(1, 0, 0, 0, 0, None, 0)
+    assert e.value.code == mk.CODES["MK_ERR_STATE"]
