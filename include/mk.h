@@ -279,14 +279,20 @@ int mk_attn_plan(const int32_t* seq_lens, int32_t n, int32_t n_kv, int32_t n_tas
 
 /* Offsets (bytes from the workspace base) of the per-layer activation
  * buffers, for debugging and layer-by-layer comparison:
- *  x: float [n_layers+1][max_batch][hidden] residual entering each layer (slot 0 unused)
+ *  x: float [n_layers+1][max_batch][hidden] residual entering each layer l >= 1 and the
+ *     final norm (slot 0 unused), as the step summed it from layer l-1's outputs, also when
+ *     mk_set_layer_inputs feeds the layers other inputs
  *  qkv: float [n_layers][max_batch][(n_q+2*n_kv)*head_dim] before rotation
  *  router: float [n_layers][max_batch][n_experts]
  *  attn_out: bf16 [n_layers][max_batch][n_q*head_dim]
  *  h: bf16 [n_layers][max_batch*top_k][inter] (row b*top_k+j: j-th expert of token b)
- *  sel: int32 [n_layers][max_batch][top_k] experts chosen for each token, best first */
+ *  sel: int32 [n_layers][max_batch][top_k] experts chosen for each token, best first
+ *  moe_half: float [n_layers+1][max_batch][hidden]: slot l+1 holds x_l + moe_l, layer l's
+ *     residual plus its expert sum (slot 0 unused)
+ *  attn_half: float [n_layers][max_batch][hidden]: layer l's attention output times Wo;
+ *     x_{l+1} is moe_half[l+1] + attn_half[l] */
 typedef struct mk_ws_offsets {
-  int64_t x, qkv, router, attn_out, h, sel;
+  int64_t x, qkv, router, attn_out, h, sel, moe_half, attn_half;
 } mk_ws_offsets;
 
 int mk_get_ws_offsets(const mk_ctx* ctx, mk_ws_offsets* out);

@@ -44,9 +44,9 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
   size_t state = 0, n_state_u32 = 0;  // counter flags, tickets, error word (zeroed by mk_reset)
-  size_t ctr = 0, tickets = 0, err = 0, rll = 0, wot = 0;  // (u32 offsets in the state region)
+  size_t ctr = 0, tickets = 0, err = 0, rll = 0;  // (u32 offsets in the state region)
   size_t tasks = 0, queue_off = 0, wtab = 0, inv_freq = 0;
-  size_t x = 0, qkv = 0, rlog = 0, attn_part = 0, attn_out = 0, wo_out = 0, h = 0, lm_part = 0, sel = 0;
+  size_t x = 0, xr = 0, qkv = 0, rlog = 0, attn_part = 0, attn_out = 0, wo_out = 0, h = 0, lm_part = 0, sel = 0;
   size_t total = 0;
 };
 
@@ -246,16 +246,16 @@ static WsLayout layout_workspace(const mk_ctx* c) {
   w.ctr = 0;
   w.tickets = (size_t)c->n_ctr * kCounterWords;
   w.err = w.tickets + c->n_tickets;
-  // epoch-tagged words (8-byte aligned): router logits, the attention output times Wo
+  // epoch-tagged words (8-byte aligned): router logits
   w.rll = align_up(w.err + E_WORDS, 2);
-  w.wot = w.rll + 2 * L * B * (size_t)f.n_experts;
-  w.n_state_u32 = w.wot + 2 * L * B * (size_t)f.hidden;
+  w.n_state_u32 = w.rll + 2 * L * B * (size_t)f.n_experts;
   take(4 * w.n_state_u32);
   w.tasks = take(sizeof(Task) * c->tasks.size());
   w.queue_off = take(4 * (c->ncu + 1));
   w.wtab = take(8 * (3 + 7 * L));
   w.inv_freq = take(8 * (f.head_dim / 2));
   w.x = take(4 * (L + 1) * B * f.hidden);
+  w.xr = take(4 * (L + 1) * B * f.hidden);
   w.qkv = take(4 * L * B * qkv_rows);
   w.rlog = take(4 * L * B * f.n_experts);
   w.attn_part = take((size_t)4 * L * c->n_attn * attn_part_stride(group, f.head_dim));
@@ -394,8 +394,11 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
         const bool router = r0 >= qkv_rows;
         Task t = make_task(OP_PRE, l);
         if (l > 0) {
+          // x_l is the sum of the expert half (output tasks) and the attention half (Wo tasks)
           t.wait[0] = ctr_index(l - 1, C_XNEXT);
           t.fanin[0] = n_out_tasks[l - 1];
+          t.wait[1] = ctr_index(l - 1, C_WO);
+          t.fanin[1] = n_wo_tasks[l - 1];
         }
         t.r0 = r0;
         t.r1 = r1;
@@ -422,7 +425,6 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
           w.r0 = r0;
           w.r1 = r1;
           w.signal = ctr_index(l, C_WO);
-          w.tagged = 1;  // output tasks poll the tagged rows
           c->tasks.push_back(w);
         }
       } else {
@@ -437,16 +439,13 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
       // OUT
       out_rows(q, &r0, &r1);
       if (r1 > r0) {
-        // expert rows (needs gate/up), then the residual update, which also
-        // needs the Wo rows: their counter is waited inside the task, after
-        // the down projection
+        // expert rows (needs gate/up), then the expert half of the residual
+        // update, x_l + moe_l; the next layer adds the Wo rows' half
         Task t = make_task(OP_OUT, l);
         t.wait[0] = ctr_index(l, C_GATEUP);
         t.fanin[0] = n_gu;
         t.wait[1] = ctr_index(l, C_ROUTER);  // for the top-k, where no gate/up task left it in LDS
         t.fanin[1] = n_router_tasks[l];
-        t.late_wait = ctr_index(l, C_WO);
-        t.late_fanin = n_wo_tasks[l];
         t.r0 = r0;
         t.r1 = r1;
         t.signal = ctr_index(l, C_XNEXT);
@@ -459,6 +458,8 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
       Task t = make_task(OP_LMHEAD, L);
       t.wait[0] = ctr_index(L - 1, C_XNEXT);
       t.fanin[0] = n_out_tasks[L - 1];
+      t.wait[1] = ctr_index(L - 1, C_WO);
+      t.fanin[1] = n_wo_tasks[L - 1];
       t.r0 = r0;
       t.r1 = r1;
       t.idx = lm_i++;
@@ -602,12 +603,14 @@ extern "C" int mk_attn_plan(const int32_t* seq_lens, int32_t n, int32_t n_kv, in
 extern "C" int mk_get_ws_offsets(const mk_ctx* c, mk_ws_offsets* out) {
   if (!c || !out) return fail(MK_ERR_INVALID_ARG, "null argument");
   if (!c->built) return fail(MK_ERR_STATE, "no schedule built");
-  out->x = (int64_t)c->ws.x;
+  out->x = (int64_t)c->ws.xr;
   out->qkv = (int64_t)c->ws.qkv;
   out->router = (int64_t)c->ws.rlog;
   out->attn_out = (int64_t)c->ws.attn_out;
   out->h = (int64_t)c->ws.h;
   out->sel = (int64_t)c->ws.sel;
+  out->moe_half = (int64_t)c->ws.x;
+  out->attn_half = (int64_t)c->ws.wo_out;
   return MK_OK;
 }
 
@@ -774,10 +777,10 @@ extern "C" int mk_decode_steps(mk_ctx* c, int32_t n, int32_t steps, const int32_
   a.tickets = st + c->ws.tickets;
   a.err = (int32_t*)(st + c->ws.err);
   a.rll = (uint64_t*)(st + c->ws.rll);
-  a.wot = (uint64_t*)(st + c->ws.wot);
   a.wtab = (const uint64_t*)(w + c->ws.wtab);
   a.inv_freq = (const double*)(w + c->ws.inv_freq);
   a.x = (float*)(w + c->ws.x);
+  a.xr = (float*)(w + c->ws.xr);
   a.qkv = (float*)(w + c->ws.qkv);
   a.rlog = (float*)(w + c->ws.rlog);
   a.attn_part = (float*)(w + c->ws.attn_part);

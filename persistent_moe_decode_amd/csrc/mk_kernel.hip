@@ -327,13 +327,20 @@ DEV bool wait_counter(const KArgs& a, int idx, int fanin, int task, int32_t* slo
   return wait_counter_at(a, idx, fanin, task, slot, a.epoch);
 }
 
+// A workgroup barrier that orders LDS accesses only: each wave waits for its
+// own LDS reads and writes, not for its vector-memory loads.  __syncthreads()
+// also waits for every LDS copy-engine transfer the wave has in flight (they
+// write LDS), which would hold a wave up for a whole weight tile that nobody
+// reads before a later full barrier.
+DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Waves 0 .. wait_waves - 1 (those that stored what the consumers read) wait
 // for their stores to complete, the barrier orders them before thread 0's
 // add; the other waves may leave loads in flight (an LDS copy for the next
-// task, waited there).
+// task, waited there), which the LDS-only barrier does not wait for.
 DEV void signal_counter(const KArgs& a, int idx, int slot, int wait_waves = kWaves) {
   if ((tid() >> 6) < wait_waves) __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  lds_barrier();
   if (tid() == 0 && idx >= 0)
     __hip_atomic_fetch_add(a.flags + (size_t)idx * kCounterWords + (slot % kSubCounters) * kSubStride, 1u,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -386,44 +393,6 @@ DEV bool wait_ticket(const KArgs& a, uint32_t* ticket, uint32_t want, int task, 
   return *slot != 0;
 }
 
-// Every thread polls its own tagged words (load_ready loads them and says
-// whether all carry this step's epoch) until every thread's do; the block
-// votes after each round.  The vote lives in three LDS words taken in turn
-// (slot[1..3], so the kernel keeps no static LDS of its own): thread 0 sets
-// the next round's word to 1 before this round's barrier, any thread not
-// ready clears this round's word, and all read it after the barrier.  The word
-// set for the next round was last read two rounds ago, before the previous
-// barrier.  slot[0] carries the abort / time-out decision.  Bounded like
-// wait_counter.  Returns false in every thread when the grid is aborting or
-// the wait timed out.
-template <class F>
-DEV bool poll_block(const KArgs& a, int task, int32_t* slot, F&& load_ready) {
-  int32_t* vote = slot + 1;
-  const uint64_t t0 = wall_clock64();
-  if (tid() == 0) vote[0] = 1;
-  __syncthreads();
-  for (uint32_t it = 0;; ++it) {
-    const uint32_t p = it % 3;
-    if (!load_ready()) vote[p] = 0;
-    if (tid() == 0) vote[p == 2 ? 0 : p + 1] = 1;
-    __syncthreads();
-    if (vote[p]) return true;
-    if ((it & 31) == 31) {
-      if (tid() == 0) *slot = aborting(a) ? 1 : (wall_clock64() - t0 > a.spin_limit_ticks ? 2 : 0);
-      __syncthreads();
-      const int stop = *slot;
-      __syncthreads();
-      if (stop) {
-        if (tid() == 0 && stop == 2) raise_error(a, MK_ERR_DEVICE_TIMEOUT, task, -1);
-        return false;
-      }
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
-}
-
-DEV bool tag_ok(uint64_t w, uint32_t epoch) { return (uint32_t)(w >> 32) == epoch; }
-DEV float tag_val(uint64_t w) { return __uint_as_float((uint32_t)w); }
 
 // ---------------------------------------------------------------------------
 // inputs
@@ -446,13 +415,30 @@ DEV const gu16* token_row(const KArgs& a, int b, int task) {
   return wptr(a, W_EMBED) + (size_t)tok * a.H;
 }
 
+// Residual entering `layer` >= 1, from the previous layer's two halves:
+// x_layer = (x_{layer-1} + moe) + attn, the expert half written by the
+// output tasks, the attention half (attention output times Wo) by the Wo
+// tasks.  Neither kind of task waits for the other; whoever reads x adds them.
+DEV float resid(const KArgs& a, int layer, int b, int i) {
+  const size_t o = (size_t)b * a.H + i;
+  return ld_coh(a.x + (size_t)layer * a.max_batch * a.H + o) +
+         ld_coh(a.wo_out + (size_t)(layer - 1) * a.max_batch * a.H + o);
+}
+
 // Residual entering `layer` (layer 0: the embedding row).
 // With the layer-input hook set, layers >= 1 (and the final norm) read the
 // residual the caller supplied instead of the one the previous layer wrote.
 DEV float load_x(const KArgs& a, int layer, int b, int i, const gu16* emb) {
   if (layer == 0) return bf2f(emb[i]);
-  const size_t o = ((size_t)layer * a.max_batch + b) * a.H + i;
-  return a.x_in ? a.x_in[o] : ld_coh(a.x + o);
+  if (a.x_in) return a.x_in[((size_t)layer * a.max_batch + b) * a.H + i];
+  return resid(a, layer, b, i);
+}
+
+DEV u32x4_v add4(u32x4_v u, u32x4_v v) {
+  u32x4_v r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) r[k] = __float_as_uint(__uint_as_float(u[k]) + __uint_as_float(v[k]));
+  return r;
 }
 
 // double -> bfloat16 bits, round to nearest even: round the 52-bit mantissa to
@@ -531,33 +517,53 @@ DEV void norm_row4(const uint8_t* stage, bool emb, int H, int n, int c, float (&
   }
 }
 
-// mk >= 0: trace mark mk of the task once the inputs are in LDS.
-DEV void norm_inputs(const KArgs& a, int layer, const gu16* gain, uint16_t* xs, double* red8, int task, int mk) {
+// mk >= 0: trace mark mk of the task once the inputs are in LDS.  rec (or
+// NULL): where to record the residual entering `layer` (>= 1) as summed here
+// from the previous layer's halves, also when the hook supplies the input.
+DEV void norm_inputs(const KArgs& a, int layer, const gu16* gain, uint16_t* xs, double* red8, int task, int mk,
+                     float* rec = nullptr) {
   const int H = a.H, n = a.n, lane = tid() & 63, wave = tid() >> 6;
   uint8_t* stage = norm_stage(a, xs);
   uint16_t* gs = (uint16_t*)(stage + (size_t)a.max_batch * H * 4);
   const bool emb = layer == 0;
   {
-    // the input rows (one 16-byte load per thread and row at hidden 2048) and
-    // the gain, all in flight before any is written to LDS
+    // the input rows (the two halves of x: one 16-byte load each per thread
+    // and row at hidden 2048) and the gain, all in flight before any is
+    // written to LDS
     const uint32_t nx16 = emb ? 0u : (uint32_t)n * H / 4, ng16 = (uint32_t)H / 8;
     const size_t o = (size_t)layer * a.max_batch * H;
+    const float* xh = a.x + o;                                  // x + moe of the previous layer
+    const float* wh = a.wo_out + o - (size_t)a.max_batch * H;   // its attention output times Wo
     u32x4_v* st = (u32x4_v*)stage;
     for (uint32_t q0 = 0; q0 < nx16 + ng16; q0 += 4 * kThreads) {
-      u32x4_v v[4];
+      u32x4_v v[4], w[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const uint32_t q = q0 + k * kThreads + tid();
-        if (q < nx16) v[k] = a.x_in ? ((const gu4*)(a.x_in + o))[q] : ld_coh16(a.x + o, nx16 * 16, q * 16);
-        else if (q < nx16 + ng16) v[k] = ((const gu4*)gain)[q - nx16];
+        if (q < nx16 && a.x_in) {
+          v[k] = ((const gu4*)(a.x_in + o))[q];
+        } else if (q < nx16) {
+          v[k] = ld_coh16(xh, nx16 * 16, q * 16);
+          w[k] = ld_coh16(wh, nx16 * 16, q * 16);
+        } else if (q < nx16 + ng16) {
+          v[k] = ((const gu4*)gain)[q - nx16];
+        }
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const uint32_t q = q0 + k * kThreads + tid();
-        if (q < nx16) st[q] = v[k];
-        else if (q < nx16 + ng16) ((u32x4_v*)gs)[q - nx16] = v[k];
+        if (q < nx16) {
+          const u32x4_v x = a.x_in ? v[k] : add4(v[k], w[k]);
+          st[q] = x;
+          if (rec && !a.x_in) ((u32x4_v*)(rec + o))[q] = x;
+        } else if (q < nx16 + ng16) {
+          ((u32x4_v*)gs)[q - nx16] = v[k];
+        }
       }
     }
+    if (rec && a.x_in)
+      for (uint32_t q = tid(); q < nx16; q += kThreads)
+        ((u32x4_v*)(rec + o))[q] = add4(ld_coh16(xh, nx16 * 16, q * 16), ld_coh16(wh, nx16 * 16, q * 16));
     if (emb)
       for (int b = 0; b < n; ++b)
         copy_to_lds<false>(stage + (size_t)b * H * 2, (const void*)(uintptr_t)token_row(a, b, task), H * 2);
@@ -1666,9 +1672,11 @@ struct JobGateUp {
 // (once the router rows are done), which spares the routing a hop of its own.
 // have_xs: region A still holds this layer's normalized input, left there by
 // the PRE task that ran just before on this compute unit.
-TASK void task_gateup(const KArgs& a, const Task& t, const Lds& s, int qi, bool have_xs) {
+// Returns whether region B holds this layer's top-k afterwards (false when the
+// router logits never arrived: abort or time-out).
+TASK bool task_gateup(const KArgs& a, const Task& t, const Lds& s, int qi, bool have_xs) {
   const int l = t.layer;
-  if (!compute_topk(a, l, s.tk, s.C, qi, s.flags + 0, 0)) return;
+  if (!compute_topk(a, l, s.tk, s.C, qi, s.flags + 0, 0)) return false;
   if (t.idx == 0) write_sel(a, l, s.tk);
   mark(a, qi, 1);
   uint16_t* xs = (uint16_t*)s.A;
@@ -1708,6 +1716,7 @@ TASK void task_gateup(const KArgs& a, const Task& t, const Lds& s, int qi, bool 
     }
     __syncthreads();
   }
+  return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -1741,10 +1750,11 @@ constexpr int kDownGroups = 4;
 // top-k (from LDS, or computed once the router rows are done) and the first
 // down-projection rows are loaded before the gate/up results are waited for.
 // have_tk: region B still holds this layer's top-k, left there by the gate/up
-// task that ran just before on this compute unit.
+// task that ran just before on this compute unit.  tk_layer: set to the layer
+// whose top-k region B holds when the task ends (-1: none).
 // Returns the number of leading waves that must wait for their stores before
 // the task signals (the others may still be copying the next task's tile).
-TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have_tk) {
+TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have_tk, int& tk_layer) {
   const int l = t.layer, nr = t.r1 - t.r0, n = a.n;
   float* contrib = (float*)s.C;  // [out_rows_max][maxB*topk]
   const int maxBK = a.max_batch * a.topk;
@@ -1755,7 +1765,10 @@ TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have
     const int rr = tid() / n, b = tid() % n;
     x_first = load_x(a, l, b, t.r0 + rr, l == 0 ? token_row(a, b, qi) : nullptr);
   }
-  if (!have_tk && !compute_topk(a, l, s.tk, s.C, qi, s.flags + 1, -1)) return kWaves;
+  if (!have_tk) {
+    tk_layer = compute_topk(a, l, s.tk, s.C, qi, s.flags + 1, -1) ? l : -1;
+    if (tk_layer < 0) return kWaves;
+  }
   const TopK* tk = s.tk;
   JobDown jd;
   jd.tk = tk;
@@ -1808,10 +1821,10 @@ TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have
   }
   rowdots_range<false>(a.I, npre, nd, mt, jd);
   mark(a, qi, 1);
-  // batch 1, wave 0 alone storing the residual rows: while the Wo rows are
-  // awaited, waves 1..7 copy the weight tile of the PRE task that follows on
-  // this unit into LDS (above tile_off, clear of the contributions); that
-  // task then finds it there instead of issuing it in front of its own wait
+  // batch 1, wave 0 alone storing the residual rows: meanwhile waves 1..7
+  // copy the weight tile of the PRE task that follows on this unit into LDS
+  // (above tile_off, clear of the contributions); that task then finds it
+  // there instead of issuing it in front of its own wait
   const bool early = n == 1 && nr <= 64 && t.next_r1 > t.next_r0 && a.pf_wide > 0;
   if (early) {
     const int npf = min(t.next_r1 - t.next_r0, a.pf_wide / (a.H * 2));
@@ -1820,29 +1833,22 @@ TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have
     prefetch_to_lds(src, s.C + a.tile_off, npf * a.H * 2);
     if (tid() == 0) s.flags[18] = t.next_layer + 1;
   }
-  // the attention output times Wo for these rows (attention units), polled as tagged words
-  const uint64_t* wot = a.wot + (size_t)l * a.max_batch * a.H + t.r0;
-  float wo_first = 0.f;
-  const bool ok = poll_block(a, qi, s.flags + 19, /* flags[19..22] */ [&]() -> int {
-    int r = 1;
-    for (int e = tid(); e < nr * n; e += kThreads) {
-      const uint64_t w = ld_tag(wot + (size_t)(e % n) * a.H + e / n);
-      r &= tag_ok(w, a.epoch);
-      if (e == tid()) wo_first = tag_val(w);
-    }
-    return r;
-  });
-  if (!ok) return early ? 1 : kWaves;
+  // the expert half of x_{l+1}: x_l + sum_j w_j y_j (the next layer adds the
+  // Wo rows' half); the record of x_l (layers >= 1) for the caller.  The
+  // contributions in LDS come from every wave: barrier first (LDS only: waves
+  // 1..7 may have the next tile's copy in flight).
+  lds_barrier();
   mark(a, qi, 2);
-  // x_{l+1} = (x_l + attn) + sum_j w_j y_j
   for (int e = tid(); e < nr * n; e += kThreads) {
     const int rr = e / n, b = e % n;
     float moe = 0.f;
     for (int j = 0; j < a.topk; ++j) moe += tk->w[b][j] * contrib[(size_t)rr * maxBK + b * a.topk + j];
     const float xo = e == tid() ? x_first : load_x(a, l, b, t.r0 + rr, l == 0 ? token_row(a, b, qi) : nullptr);
-    const float wo = e == tid() ? wo_first : tag_val(ld_tag(wot + (size_t)b * a.H + rr));
-    st_coh(a.x + ((size_t)(l + 1) * a.max_batch + b) * a.H + t.r0 + rr, (xo + wo) + moe);
+    const size_t o = ((size_t)l * a.max_batch + b) * a.H + t.r0 + rr;
+    st_coh(a.x + o + (size_t)a.max_batch * a.H, xo + moe);
+    if (l > 0) a.xr[o] = a.x_in ? resid(a, l, b, t.r0 + rr) : xo;
   }
+  mark(a, qi, 3);
   // waves whose stores the consumers read must see them complete before the signal
   return early ? 1 : kWaves;
 }
@@ -1883,8 +1889,6 @@ TASK void task_wo(const KArgs& a, const Task& t, const Lds& s, int qi, int npf) 
   j.K = AD;
   j.xs = xs;
   j.out = a.wo_out + (size_t)l * a.max_batch * a.H + t.r0;
-  j.tag_out = a.wot + (size_t)l * a.max_batch * a.H + t.r0;
-  j.epoch = a.epoch;
   j.ld = a.H;
   rowdots_range<true>(AD, 0, npf, n, j);
   for (int b = 0; b < n; ++b) {
@@ -1943,7 +1947,7 @@ DEV void block_argmax(float& v, int& i, float* red) {
 TASK void task_lmhead(const KArgs& a, const Task& t, const Lds& s, int qi) {
   const int L = a.L, nr = t.r1 - t.r0;
   uint16_t* xs = (uint16_t*)s.A;
-  norm_inputs(a, L, wptr(a, W_FINAL_NORM), xs, s.red8, qi, -1);
+  norm_inputs(a, L, wptr(a, W_FINAL_NORM), xs, s.red8, qi, -1, t.idx == 0 ? a.xr : nullptr);
   mark(a, qi, 0);
   JobLM j;
   j.W = wptr(a, W_LM_HEAD);
@@ -2048,15 +2052,17 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a0
         switch (t.op) {
           case OP_PRE: task_pre(a, t, s, q, npf); break;
           case OP_ATTN: task_attn(a, t, s, q); break;
-          case OP_GATEUP: task_gateup(a, t, s, q, xs_layer == t.layer); break;
-          case OP_OUT: wait_waves = task_out(a, t, s, q, tk_layer == t.layer); break;
+          case OP_GATEUP: tk_layer = task_gateup(a, t, s, q, xs_layer == t.layer) ? t.layer : -1; break;
+          case OP_OUT: wait_waves = task_out(a, t, s, q, tk_layer == t.layer, tk_layer); break;
           case OP_WO: task_wo(a, t, s, q, npf); break;
           case OP_LMHEAD: task_lmhead(a, t, s, q); break;
           default: break;
         }
       }
       xs_layer = ok && t.op == OP_PRE ? t.layer : (ok && t.op == OP_GATEUP ? xs_layer : -1);
-      tk_layer = ok && (t.op == OP_GATEUP || t.op == OP_OUT) ? t.layer : (t.op == OP_LMHEAD ? -1 : tk_layer);
+      // region B holds a layer's top-k only after a top-k that succeeded (a failed one, on
+      // abort or time-out, leaves whatever an earlier task or kernel left there)
+      if (t.op == OP_LMHEAD) tk_layer = -1;
       if (t.tagged) __syncthreads();  // consumers poll the tagged output itself
       else signal_counter(a, t.signal, t.slot, wait_waves);
       if (a.trace && tid() == 0 && q < a.trace_cap) {

@@ -92,16 +92,16 @@ struct KArgs {
   uint32_t* tickets;    // attention tickets [L][max_batch][nkv], then 1 for the LM head
   int32_t* err;         // E_WORDS
   uint64_t* rll;        // router logits as epoch-tagged words [L][max_batch][E] (zeroed with the counters)
-  uint64_t* wot;        // the attention output times Wo as epoch-tagged words [L][max_batch][H]
   const uint64_t* wtab; // device pointers of the weights
   const double* inv_freq; // [d/2]
   // activations
-  float* x;             // [L+1][max_batch][H]
+  float* x;             // [L+1][max_batch][H]: index l+1 holds x_l + moe_l (the expert half of x_{l+1})
+  float* xr;            // [L+1][max_batch][H]: x_l for l >= 1 as the kernel summed it (a record for the caller)
   float* qkv;           // [L][max_batch][qkv_rows]
   float* rlog;          // [L][max_batch][E]
   float* attn_part;     // [L][n_attn][attn_part_stride(group, d)]
   uint16_t* attn_out;   // [L][max_batch][nq*d]
-  float* wo_out;        // [L][max_batch][H] attention output times Wo
+  float* wo_out;        // [L][max_batch][H] attention output times Wo (the attention half of x_{l+1})
   uint16_t* h;          // [L][max_batch*topk][I]
   float* lm_part;       // [n_lm][max_batch][2] (value, index as float bits)
   int32_t* sel_out;     // [L][max_batch][topk] experts chosen per token

@@ -60,7 +60,8 @@ class ScheduleInfo(ctypes.Structure):
 
 class WsOffsets(ctypes.Structure):
     _fields_ = [("x", ctypes.c_int64), ("qkv", ctypes.c_int64), ("router", ctypes.c_int64),
-                ("attn_out", ctypes.c_int64), ("h", ctypes.c_int64), ("sel", ctypes.c_int64)]
+                ("attn_out", ctypes.c_int64), ("h", ctypes.c_int64), ("sel", ctypes.c_int64),
+                ("moe_half", ctypes.c_int64), ("attn_half", ctypes.c_int64)]
 
 
 _lib = None

@@ -194,6 +194,15 @@ class DeviceDecoder:
         v = self._ws_view(self.offsets.x, (s.n_layers + 1) * mb * s.hidden, torch.float32)
         return v.view(s.n_layers + 1, mb, s.hidden).cpu().numpy()
 
+    def residual_halves(self):
+        """(moe_half [L+1][max_batch][H], attn_half [L][max_batch][H]): x_l + moe_l in slot l+1 and
+        layer l's attention output times Wo; their sum is x_{l+1}."""
+        s = self.shape
+        mb = self.ctx.cfg.max_batch
+        m = self._ws_view(self.offsets.moe_half, (s.n_layers + 1) * mb * s.hidden, torch.float32)
+        a = self._ws_view(self.offsets.attn_half, s.n_layers * mb * s.hidden, torch.float32)
+        return (m.view(s.n_layers + 1, mb, s.hidden).cpu().numpy(), a.view(s.n_layers, mb, s.hidden).cpu().numpy())
+
     def kv_at(self, layer: int, b: int, pos: int):
         """(K, V) bf16 bits [n_kv][d] stored for logical position pos of sequence b."""
         ps = self.shape.page_size

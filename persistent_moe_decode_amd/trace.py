@@ -8,10 +8,10 @@ body, and when it had signalled.  This module joins them with the task table.
 Phase marks per op: PRE [inputs loaded, norm done, rows done]; ATTN [q
 rotated and new K/V written, copied pages landed, positions done, partial
 stored]; GATEUP [top-k selected (wave 0), routing tables built, norm done];
-OUT [h loaded, down rows done, Wo rows polled]; WO [attention output loaded,
-rows done]; LMHEAD [norm done, rows done, local argmax done].  Tasks that
-poll epoch-tagged inputs (ATTN, GATEUP, the Wo rows in OUT) record as
-"ready" the moment the tags matched.
+OUT [h loaded, wave 0's down rows done, all down rows done, residual rows stored]; WO [attention output loaded, rows done];
+LMHEAD [norm done, rows done, local argmax done].  Tasks that wait inside
+their body (ATTN, GATEUP, OUT, WO) record as "ready" the moment their inputs
+were there (for GATEUP: the epoch tags of the router logits matched).
 """
 from __future__ import annotations
 

@@ -186,8 +186,15 @@ def test_simulator_catches_a_shared_flag_word():
 def test_simulator_counts_the_in_body_wait():
     tasks, qoff, nctr = _tiny_table()
     outs = np.nonzero(tasks[:, F_OP] == OP_OUT)[0]
-    assert np.all(tasks[outs, F_LATE] >= 0)           # output tasks wait for the Wo rows inside the body
+    assert np.all(tasks[outs, F_LATE] < 0)            # the built table has no in-body counter wait
+    # an output task that waited inside its body for its layer's Wo rows: still deadlock free
+    wo = tasks[(tasks[:, F_OP] == OP_WO) & (tasks[:, F_LAYER] == tasks[outs[0], F_LAYER])]
     t = tasks.copy()
+    t[outs[0], F_LATE] = wo[0, F_SIGNAL]
+    t[outs[0], F_LATE_FAN] = len(wo)
+    code, done = mk.simulate_table(t, qoff, nctr)
+    assert code == 0 and done == len(t)
+    # the wrong fan-in on it is caught
     t[outs[0], F_LATE_FAN] += 1
     code, _ = mk.simulate_table(t, qoff, nctr)
     assert code == mk.CODES["MK_ERR_SCHEDULE"]
