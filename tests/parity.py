@@ -100,6 +100,17 @@ class Report:
         return s
 
 
+def kernel_src_hash() -> str:
+    """First 16 hex digits of the SHA-256 of the library's HIP/C++ sources (names the kernel a record is for)."""
+    import hashlib
+    csrc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "persistent_moe_decode_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("mk_kernel.hip", "mk_host.cpp", "mk_types.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def record(name: str, rep: Report, **extra) -> None:
     """Append the report's summary as one JSON line to $MK_PARITY_RECORDS/<name>.jsonl, when that is set."""
     d = os.environ.get("MK_PARITY_RECORDS")
@@ -108,7 +119,8 @@ def record(name: str, rep: Report, **extra) -> None:
     os.makedirs(d, exist_ok=True)
     rec = {k: v for k, v in asdict(rep).items() if k != "failures"}
     rec.update(name=name, ok=rep.ok(), n_failures=len(rep.failures), first_failures=rep.failures[:3],
-               summary=rep.summary(), time=time.strftime("%Y-%m-%d %H:%M:%S"), **extra)
+               summary=rep.summary(), time=time.strftime("%Y-%m-%d %H:%M:%S"), kernel_src=kernel_src_hash(),
+               **extra)
     rec = {k: (None if isinstance(v, float) and v == float("inf") else v) for k, v in rec.items()}
     with open(os.path.join(d, f"{name}.jsonl"), "a") as f:
         f.write(json.dumps(rec) + "\n")

@@ -72,9 +72,10 @@ def test_mid_free_running_64_steps():
     rep = parity.run(synth.workload("mid"), mode="free", log=_log)
     assert rep.steps == 64
     _check(rep, "mid_free_64")
-    # most steps keep the same routing end to end and are compared in full: 2 of 64 steps had a
-    # routing divergence (within the measured drift) when this bound was set; 4 more allow for
-    # the run-to-run spread of which steps meet a near-margin router decision
+    # most steps keep the same routing end to end and are compared in full.  Which steps meet a
+    # near-margin router decision depends on the fp32 summation order (the run is deterministic
+    # for one build): 2 of 64 diverged (within the measured drift) with x + attn summed first,
+    # 5 of 64 with x + moe summed first
     assert rep.cascade_steps <= 6, rep.summary()
 
 
