@@ -229,6 +229,24 @@ int mk_set_layer_inputs(mk_ctx* ctx, const float* d_x);
  * the next step. */
 int mk_set_trace(mk_ctx* ctx, uint64_t* d_records, int64_t capacity);
 
+/* How each step picks the next token (d_next_tokens, and the token fed to the
+ * next step of a multi-step launch).  temperature 0 (the default): the greedy
+ * argmax of the logits, ties to the lowest id.  temperature T > 0: a draw
+ * from softmax(logits / T) by the Gumbel-max rule, the argmax over i of
+ * logits_i / T + g_i (ties to the lowest id), with g_i = -log(-log(u_i)) and
+ * u_i = (top 53 bits of SplitMix64 output n + 1/2) / 2^53, where output n of
+ * the generator seeded with `seed` is its finalizer applied to
+ * seed + (n + 1) * 0x9E3779B97F4A7C15, and n = (p * max_batch + b) * vocab + i
+ * for batch slot b whose step input token sits at position p.  The draw
+ * depends only on (seed, p, b, i) and the logits, so it repeats exactly.
+ * The logits written to d_logits stay the unscaled ones.  Source: the pages
+ * call the engine's sampling options incomplete (ainews.surl.tw, the
+ * paragraph on limitations); this is the plainest sampling that needs no
+ * sort of the vocabulary.  Errors: MK_ERR_INVALID_ARG for a negative, NaN or
+ * infinite temperature, or one so small that 1/T overflows.  Host only;
+ * applies from the next step. */
+int mk_set_sampling(mk_ctx* ctx, double temperature, uint64_t seed);
+
 const char* mk_last_error_message(void);
 void mk_destroy(mk_ctx* ctx);
 

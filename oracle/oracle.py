@@ -27,7 +27,8 @@ kv head ``h // (n_q / n_kv)``; top-k by (value desc, index asc) and softmax over
 the selected logits; SwiGLU experts ``Wd (silu(Wg xn) * (Wu xn))``; the new
 token's K/V are written to slot ``seq_len`` before attention runs over
 ``0..seq_len`` inclusive; untied LM head after a final RMSNorm; greedy argmax
-with ties to the lowest id.
+with ties to the lowest id; sampling at temperature T by the Gumbel-max rule
+with SplitMix64 noise keyed by (seed, position, batch slot, token id).
 
 Parity unpinned: the composed multi-layer logits have no closed form; they
 are pinned only through the pinned ops and the whole-step invariants in
@@ -356,6 +357,47 @@ def prefill_as_decode(W: Weights, kv: PagedKV, prompt, page_table_row) -> StepOu
 
 # ----------------------------------------------------------------------------
 # speed-of-light model
+
+
+# ----------------------------------------------------------------------------
+# sampling (the pages call the engine's sampling options incomplete: the
+# ainews.surl.tw page, its paragraph on limitations; the reading here is
+# temperature sampling, softmax(logits / T), drawn by the Gumbel-max rule)
+
+_GOLDEN_GAMMA = 0x9E3779B97F4A7C15
+_M64 = (1 << 64) - 1
+
+
+def splitmix64_at(seed: int, n: np.ndarray) -> np.ndarray:
+    """Output n (0-based) of SplitMix64 seeded with `seed` (Steele, Lea and Flood, "Fast splittable
+    pseudorandom number generators", 2014): the state after n + 1 steps of adding the golden gamma
+    0x9E3779B97F4A7C15, through the finalizer z ^= z >> 30, z *= 0xBF58476D1CE4E5B9, z ^= z >> 27,
+    z *= 0x94D049BB133111EB, z ^= z >> 31 (all arithmetic mod 2^64)."""
+    n = np.asarray(n, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        z = np.uint64(seed & _M64) + (n + np.uint64(1)) * np.uint64(_GOLDEN_GAMMA)
+        z = (z ^ (z >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+        z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+    return z ^ (z >> np.uint64(31))
+
+
+def gumbel_noise(seed: int, pos: int, b: int, max_batch: int, vocab: int) -> np.ndarray:
+    """Gumbel(0, 1) noise for every vocabulary entry i of batch slot b whose step input token sits at
+    position `pos`: u = (top 53 bits of output n + 1/2) / 2^53 with n = (pos * max_batch + b) * vocab + i,
+    which lies in (0, 1), and g = -log(-log(u))."""
+    n = (np.uint64(pos) * np.uint64(max_batch) + np.uint64(b)) * np.uint64(vocab) + np.arange(vocab, dtype=np.uint64)
+    u = ((splitmix64_at(seed, n) >> np.uint64(11)).astype(np.float64) + 0.5) * 2.0 ** -53
+    return -np.log(-np.log(u))
+
+
+def sample_token(logits: np.ndarray, temperature: float, seed: int, pos: int, b: int, max_batch: int):
+    """The sampled next token and the perturbed scores: argmax_i (logits_i / T + g_i) (ties to the
+    lowest id), which draws i with probability softmax(logits / T)_i; T = 0 is the greedy argmax."""
+    z = np.asarray(logits, dtype=np.float64)
+    if temperature == 0:
+        return int(np.argmax(z)), z
+    v = z / temperature + gumbel_noise(seed, pos, b, max_batch, z.size)
+    return int(np.argmax(v)), v
 
 
 def sol_tokens_per_s(bandwidth_bytes_per_s: float, bytes_per_step: float, batch: int = 1) -> float:

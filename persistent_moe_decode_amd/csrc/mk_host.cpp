@@ -70,6 +70,8 @@ struct mk_ctx {
   uint16_t* vpool = nullptr;
   uint32_t epoch = 0;
   int64_t spin_us = 2000000;
+  double inv_temp = 0.0;  // sampling (0: greedy)
+  uint64_t seed = 0;
   const float* x_in = nullptr;
   uint64_t* trace = nullptr;
   int64_t trace_cap = 0;
@@ -621,6 +623,15 @@ extern "C" int mk_set_layer_inputs(mk_ctx* c, const float* d_x) {
   return MK_OK;
 }
 
+extern "C" int mk_set_sampling(mk_ctx* c, double temperature, uint64_t seed) {
+  if (!c) return fail(MK_ERR_INVALID_ARG, "null context");
+  if (!(temperature >= 0.0) || temperature == HUGE_VAL) return fail(MK_ERR_INVALID_ARG, "temperature must be finite and >= 0");
+  if (temperature > 0.0 && !(1.0 / temperature < HUGE_VAL)) return fail(MK_ERR_INVALID_ARG, "temperature too small");
+  c->inv_temp = temperature > 0.0 ? 1.0 / temperature : 0.0;
+  c->seed = seed;
+  return MK_OK;
+}
+
 extern "C" int mk_set_trace(mk_ctx* c, uint64_t* d_records, int64_t capacity) {
   if (!c) return fail(MK_ERR_INVALID_ARG, "null context");
   if (d_records && capacity < 1) return fail(MK_ERR_INVALID_ARG, "trace capacity must be positive");
@@ -804,6 +815,8 @@ extern "C" int mk_decode_steps(mk_ctx* c, int32_t n, int32_t steps, const int32_
   a.logits = d_logits;
   a.next_tok = d_next_tokens;
   a.spin_limit_ticks = (uint64_t)c->spin_us * 100;  // s_memrealtime runs at 100 MHz
+  a.inv_temp = c->inv_temp;
+  a.seed = c->seed;
   int r = mkk_launch_step(&a, c->ncu, c->lds_bytes, (hipStream_t)stream);
   if (r) return fail(MK_ERR_HIP, std::string("cooperative launch failed: ") + hipGetErrorString((hipError_t)r));
   c->epoch += (uint32_t)steps;

@@ -15,7 +15,8 @@
 //           gate and up projections and SwiGLU;
 //   OUT     rows of the selected experts' down projections, weighted expert
 //           sum and residual add (parallel block: x += attn + moe);
-//   LMHEAD  final RMSNorm, rows of the LM head, greedy argmax (last arriver).
+//   LMHEAD  final RMSNorm, rows of the LM head, greedy or sampled argmax
+//           (last arriver).
 // Weight rows stream from HBM with 128-bit loads; at batch 1 lanes accumulate
 // in fp32 with v_dot2_f32_bf16 and groups of lanes reduce through DPP, at
 // batch >= 2 rows that every token uses run as 16-row matrix-core tiles.
@@ -1904,7 +1905,7 @@ TASK void task_wo(const KArgs& a, const Task& t, const Lds& s, int qi, int npf) 
 }
 
 // ---------------------------------------------------------------------------
-// LMHEAD: rows [r0, r1) of the vocabulary, then the greedy argmax.
+// LMHEAD: rows [r0, r1) of the vocabulary, then the greedy or sampled argmax.
 
 struct JobLM {
   static constexpr bool kDense = true;
@@ -1922,6 +1923,31 @@ struct JobLM {
     lmv[(size_t)i * maxB + t] = v;
   }
 };
+
+// Sampling at temperature T by the Gumbel-max rule: the next token is
+// argmax_i (logit_i / T + g_i) with g_i ~ Gumbel(0, 1), which draws token i
+// with probability softmax(logits / T)_i.  The noise comes from SplitMix64
+// (Steele, Lea and Flood 2014) used as a counter-based generator: output n of
+// the generator seeded with `seed` is the finalizer applied to
+// seed + (n + 1) * 0x9E3779B97F4A7C15; token i of batch slot b whose step input
+// sits at position p takes n = (p * max_batch + b) * V + i, u = (top 53 bits +
+// 1/2) / 2^53 in (0, 1), and g = -log(-log(u)) in double.
+DEV uint64_t splitmix64_at(uint64_t seed, uint64_t n) {
+  uint64_t z = seed + (n + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// The score the argmax compares for logit x of token i, slot b: the logit
+// itself (greedy) or x / T + g_i, rounded to float.
+DEV float sample_score(const KArgs& a, float x, int b, int i) {
+  if (a.inv_temp == 0.0) return x;
+  const uint64_t p = (uint64_t)(a.seq_lens[b] + a.step);
+  const uint64_t n = (p * (uint64_t)a.max_batch + (uint64_t)b) * (uint64_t)a.V + (uint64_t)i;
+  const double u = ((double)(splitmix64_at(a.seed, n) >> 11) + 0.5) * 0x1.0p-53;
+  return (float)((double)x * a.inv_temp - log(-log(u)));
+}
 
 // Block-wide argmax (value desc, index asc); result valid in all threads.
 DEV void block_argmax(float& v, int& i, float* red) {
@@ -1979,6 +2005,7 @@ TASK void task_lmhead(const KArgs& a, const Task& t, const Lds& s, int qi) {
       for (int r = tid(); r < np; r += kThreads) {
         float x = j.lmv[(size_t)r * a.max_batch + b];
         if (x != x) x = kNegInf;
+        x = sample_score(a, x, b, j.r0 + r);
         if (better(x, j.r0 + r, v, i)) { v = x; i = j.r0 + r; }
       }
       block_argmax(v, i, s.red);

@@ -120,6 +120,8 @@ struct KArgs {
   float* logits;
   int32_t* next_tok;         // [nsteps][n] greedy tokens (step s > 0 reads step s - 1's), or NULL at one step
   uint64_t spin_limit_ticks; // s_memrealtime ticks (100 MHz)
+  double inv_temp;           // sampling: 1 / temperature, or 0 for the greedy argmax
+  uint64_t seed;             // sampling: generator seed
   int32_t nsteps;            // decode steps in this launch
   int32_t step;              // the step being run (set by the kernel: epoch + step, positions + step)
 };

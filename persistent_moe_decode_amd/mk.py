@@ -89,6 +89,7 @@ def lib():
         "mk_set_spin_limit_us": [P, I64],
         "mk_set_layer_inputs": [P, P],
         "mk_set_trace": [P, P, I64],
+        "mk_set_sampling": [P, ctypes.c_double, ctypes.c_uint64],
         "mk_get_schedule_info": [P, ctypes.POINTER(ScheduleInfo)],
         "mk_copy_schedule": [P, pi32, I64, pi32, I64],
         "mk_validate_schedule": [P, pi32],
@@ -235,6 +236,10 @@ class Context:
 
     def set_trace(self, ptr: int | None, capacity: int = 0):
         check(lib().mk_set_trace(self.h, ptr or None, capacity), "mk_set_trace")
+
+    def set_sampling(self, temperature: float, seed: int = 0):
+        """Temperature 0 (the default) is the greedy argmax; > 0 samples softmax(logits / T)."""
+        check(lib().mk_set_sampling(self.h, float(temperature), int(seed) & ((1 << 64) - 1)), "mk_set_sampling")
 
     def set_spin_limit_us(self, us: int):
         check(lib().mk_set_spin_limit_us(self.h, us), "mk_set_spin_limit_us")

@@ -377,3 +377,13 @@ def test_bind_scratch_rejects_a_workspace_beyond_the_static_one():
     with pytest.raises(mk.MkError) as e:  # nothing was bound
         c.decode_step(1, 0, 0, 0, 0, None, 0)
     assert e.value.code == mk.CODES["MK_ERR_STATE"]
+
+
+def test_sampling_arguments():
+    c = _ctx(synth.TINY)
+    for bad in (-1.0, float("nan"), float("inf"), 1e-320):
+        with pytest.raises(mk.MkError) as e:
+            c.set_sampling(bad, 1)
+        assert e.value.code == mk.CODES["MK_ERR_INVALID_ARG"], bad
+    c.set_sampling(0.0)
+    c.set_sampling(0.7, 2 ** 64 - 1)

@@ -13,6 +13,7 @@ import os
 import numpy as np
 import pytest
 import scipy.special
+import scipy.stats
 import torch
 
 import synth
@@ -473,3 +474,65 @@ def test_lm_logits_closed_form_through_the_final_gain():
     assert int(np.argmax(got)) == 5
     # the same input scaled by any positive factor normalizes to the same logits
     assert np.array_equal(O.lm_logits(W, np.array([0.5, -0.5, 0.5, -0.5])), got)
+
+
+# ----------------------------------------------------------------------------
+# sampling
+
+
+def test_sampler_generator_is_splitmix64():
+    """The sampler's generator reproduces SplitMix64's published reference outputs for seed 0
+    (the sequence Vigna distributes with splitmix64.c), and output n depends on n alone."""
+    got = [int(x) for x in O.splitmix64_at(0, np.arange(3))]
+    assert got == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+    assert int(O.splitmix64_at(0, np.array([2]))[0]) == got[2]
+
+
+def test_gumbel_noise_moments():
+    """Gumbel(0, 1): mean = Euler's constant, variance = pi^2 / 6.  Over 2^17 draws the sample
+    moments lie within 5 standard errors.  A flipped sign (mean -0.577), log(u) for -log(-log(u))
+    or a different scale all fail."""
+    g = np.concatenate([O.gumbel_noise(11, pos, 0, 1, 4096) for pos in range(32)])
+    n = g.size
+    var = math.pi ** 2 / 6
+    assert abs(g.mean() - np.euler_gamma) < 5 * math.sqrt(var / n)
+    # variance of the sample variance: (mu4 - sigma^4) / n, mu4 = 27/5 sigma^4 for the Gumbel
+    assert abs(g.var() - var) < 5 * math.sqrt((27 / 5 - 1) * var ** 2 / n)
+
+
+def test_sampling_draws_softmax_over_temperature():
+    """The Gumbel-max rule draws token i with probability softmax(z / T)_i: 40000 draws (one per
+    position) of 5 tokens at T = 0.7 match those probabilities within 5 standard errors each, and
+    a chi-square statistic stays under its 0.9999 quantile.  Dividing by T the wrong way (z * T),
+    taking the argmin or a noise other than Gumbel each shift the frequencies far outside."""
+    z = np.array([1.0, 0.2, -0.5, 1.4, 0.0])
+    T = 0.7
+    p = scipy.special.softmax(z / T)
+    N = 40000
+    counts = np.zeros(5)
+    for pos in range(N):
+        tok, _ = O.sample_token(z, T, 1234, pos, 0, 1)
+        counts[tok] += 1
+    f = counts / N
+    assert np.all(np.abs(f - p) < 5 * np.sqrt(p * (1 - p) / N)), (f, p)
+    chi2 = float(np.sum((counts - N * p) ** 2 / (N * p)))
+    assert chi2 < scipy.stats.chi2.ppf(0.9999, df=4)
+
+
+def test_sampling_special_cases():
+    """T = 0 is the greedy argmax; a tiny T gives the argmax whenever the gap dwarfs T times the
+    noise; the draw depends on the seed, the position and the batch slot, and repeats exactly."""
+    rng = np.random.default_rng(5)
+    z = rng.normal(size=1000)
+    assert O.sample_token(z, 0.0, 7, 3, 0, 1)[0] == int(np.argmax(z))
+    assert O.sample_token(z, 1e-9, 7, 3, 0, 1)[0] == int(np.argmax(z))
+    a = O.sample_token(z, 1.0, 7, 3, 0, 2)
+    assert a[0] == O.sample_token(z, 1.0, 7, 3, 0, 2)[0] and np.array_equal(a[1], O.sample_token(z, 1.0, 7, 3, 0, 2)[1])
+    others = [O.sample_token(z, 1.0, s, p, b, 2)[1] for s, p, b in ((8, 3, 0), (7, 4, 0), (7, 3, 1))]
+    for v in others:
+        assert not np.array_equal(v, a[1])
+    # slot b of max_batch 2 at position p is stream entry (2p + b) * V + i
+    g = O.gumbel_noise(7, 3, 1, 2, 1000)
+    n = np.arange(1000, dtype=np.uint64) + np.uint64((3 * 2 + 1) * 1000)
+    u = ((O.splitmix64_at(7, n) >> np.uint64(11)).astype(np.float64) + 0.5) / 2.0 ** 53
+    assert np.array_equal(g, -np.log(-np.log(u)))
