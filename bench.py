@@ -44,7 +44,8 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, if they match this kernel source."""
+    """HBM bytes per decode step (one step per dispatch in the counter runs) from the committed rocprofv3
+    counter record, if it was taken with this kernel source."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -52,15 +53,16 @@ def measured_traffic(workload: str):
         t = json.load(f)
     if t.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t.get("hbm_bytes_per_step")
 
 
 def write_traffic(fetch_csv: str, write_csv: str, workload: str, copy_bytes: int) -> dict:
-    """profiles/traffic_<workload>.json from two rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE, csv).
+    """profiles/traffic_<workload>.json from two rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE, csv),
+    each of bench.py with --steps-per-launch 1 (one decode step per mk_megakernel dispatch).
 
     Each run ends with one plain copy of copy_bytes (read copy_bytes, write
     copy_bytes): the largest __amd_rocclr_copyBuffer dispatch of a run scales
-    that counter's KiB to bytes; mk_megakernel dispatches give the per-launch values.
+    that counter's KiB to bytes; mk_megakernel dispatches give the per-step values.
     """
     import csv
 
@@ -92,8 +94,9 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str, copy_bytes: int
         "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk, "calib_copy_bytes": copy_bytes,
         "calib_fetch_kib": fcal, "calib_write_kib": wcal,
         "fetch_scale": round(fscale, 5), "write_scale": round(wscale, 5),
-        "hbm_fetch_bytes_per_launch": round(fb), "hbm_write_bytes_per_launch": round(wb),
-        "hbm_bytes_per_launch": round(fb + wb),
+        "steps_per_dispatch": 1,
+        "hbm_fetch_bytes_per_step": round(fb), "hbm_write_bytes_per_step": round(wb),
+        "hbm_bytes_per_step": round(fb + wb),
     }
     with open(os.path.join(ROOT, "profiles", f"traffic_{workload}.json"), "w") as f:
         json.dump(rec, f, indent=1)
@@ -215,7 +218,7 @@ def main():
     args = ap.parse_args()
     if args.write_traffic:
         rec = write_traffic(*args.write_traffic, args.workload, 1 << 30)
-        print(json.dumps({k: rec[k] for k in ("fetch_scale", "write_scale", "hbm_bytes_per_launch")}))
+        print(json.dumps({k: rec[k] for k in ("fetch_scale", "write_scale", "hbm_bytes_per_step")}))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one MI355X: the decode megakernel runs on a single GPU and has no "
@@ -281,6 +284,8 @@ def main():
     bytes_step = bytes_tot / args.steps
     gbs = bytes_step / (ms_step / 1e3) / 1e9
     traffic = measured_traffic(args.workload)
+    n_launch = -(-args.steps // spl)
+    launch_ms = ms / n_launch
     log(f"[bench] {ms_step:.3f} ms/step, {tok_s:.1f} tok/s, {bytes_step / 1e9:.4f} GB/step, {gbs:.0f} GB/s "
         f"({100 * gbs / PEAK_HBM_GBS:.1f}% of peak)")
 
@@ -351,8 +356,10 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(gbs / PEAK_HBM_GBS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": round(bytes_step),
+            "traffic": None if traffic is None else round(traffic * spl),
+            "algorithmic_bytes_per_launch": round(bytes_step * spl),
+            "launch_ms": round(launch_ms, 4),
+            "steps_per_launch": spl,
             "kernel": "mk_megakernel",
         },
         "cpu_baseline": cpu,

@@ -73,8 +73,13 @@ def run(configs, per_wg: int, reps: int = 3):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--quick", action="store_true")
+    ap.add_argument("--calib", action="store_true",
+                    help="one dispatch of each load form at 170 workgroups (counter calibration runs)")
     ap.add_argument("--per-wg", type=int, default=4 << 20)
     args = ap.parse_args()
+    if args.calib:
+        run([("reg", 170, 8), ("lds", 170, 2)], args.per_wg, reps=1)
+        return
     grids = [1, 8, 86, 170, 256] if not args.quick else [1, 170, 256]
     configs = [("reg", g, d) for d in (8, 16, 32, 48) for g in grids] + [("lds", g, c) for c in (1, 2) for g in grids]
     run(configs, args.per_wg)
