@@ -27,8 +27,9 @@
  *    mk_last_error_message() returns a thread-local description of the last
  *    failure on the calling thread.
  *  - "device pointer" = memory the caller allocated on the GPU (e.g. through
- *    PyTorch); the library never allocates or frees device memory and owns
- *    only its host-side state.
+ *    PyTorch); the library never allocates or frees device memory.  It owns
+ *    its host-side state and one static device array per GPU, used only by
+ *    mk_bind_scratch.
  *  - "stream" = a hipStream_t passed as void*; NULL means the default stream.
  *    Work is enqueued asynchronously on it.
  *  - Matrices are row-major [out][in] bfloat16 (raw 16-bit patterns).
@@ -132,7 +133,13 @@ int mk_build_schedule(mk_ctx* ctx, const mk_schedule_params* params, size_t* wor
  *  v_pool: device, [n_layers][num_pages][n_kv_heads][head_dim][page_size] bf16
  *    (dims-major inside a page, the layout the P*V matrix-core product reads).
  *  workspace: device, at least the size mk_build_schedule reported, 256-byte aligned.
- * The buffers must stay valid until the context is destroyed or bound again. */
+ * The buffers must stay valid until the context is destroyed or bound again.
+ * Errors: MK_ERR_STATE before mk_build_schedule; MK_ERR_INVALID_ARG for a
+ * wrong weight count, a null or misaligned pointer (weights and pools 16
+ * bytes) or a short workspace; MK_ERR_HIP if the upload fails.
+ * Source: BF16 weights of the 30B-total mixture-of-experts decoder and a paged
+ * KV cache (latestnews.news, paragraphs 1 and 3; ainews.surl.tw, paragraph 2);
+ * the V layout inside a page is this library's choice for the matrix cores. */
 int mk_bind(mk_ctx* ctx, const void* const* weights, int32_t n_weights, void* k_pool, void* v_pool,
             void* workspace, size_t workspace_bytes, void* stream);
 
@@ -171,26 +178,35 @@ size_t mk_scratch_capacity(void);
  *    sequence's row of the page table in the same step (pages are read before
  *    the new entries are written; shared prefix pages are fine).
  *  d_logits: device float[n][vocab], written.
- *  d_next_tokens: device int32[n] receiving the greedy argmax (lowest id on
- *    ties), or NULL.
+ *  d_next_tokens: device int32[n] receiving the next token (the greedy argmax,
+ *    lowest id on ties, or the draw mk_set_sampling asks for), or NULL.
  * Asynchronous.  One step per context may be in flight at a time; steps on
- * one stream are ordered.  Device-detected errors are sticky: read them with
- * mk_get_error. */
+ * one stream are ordered.  Device-detected errors (bad token, page or length;
+ * a dependency wait past the spin limit) are sticky: read them with
+ * mk_get_error.  Host-side errors: MK_ERR_STATE (not bound, or a device error
+ * not yet cleared by mk_reset), MK_ERR_INVALID_ARG (n outside [1, max_batch],
+ * a null buffer), MK_ERR_HIP (the launch failed).
+ * Source: one persistent kernel runs the whole decode forward pass of a
+ * ragged batch of 1 to 8 sequences over a paged KV cache (latestnews.news,
+ * paragraph 3; ainews.surl.tw, paragraphs 1, 2 and 4). */
 int mk_decode_step(mk_ctx* ctx, int32_t n, const int32_t* d_tokens, const int32_t* d_page_table,
                    const int32_t* d_seq_lens, float* d_logits, int32_t* d_next_tokens, void* stream);
 
-/* Enqueues `steps` greedy decode steps of the same ragged batch in ONE launch
- * of the persistent kernel: step s (0-based) feeds each sequence the greedy
- * token step s - 1 produced (step 0: d_tokens), writes K/V at position
+/* Enqueues `steps` decode steps of the same ragged batch in ONE launch
+ * of the persistent kernel: step s (0-based) feeds each sequence the token
+ * step s - 1 picked (greedy or sampled, mk_set_sampling; step 0: d_tokens), writes K/V at position
  * seq_lens[b] + s and attends over 0..seq_lens[b] + s.  No host round trip
  * and no kernel boundary between steps.
  *  d_next_tokens: device int32[steps][n], required when steps > 1: the
- *    greedy token of every step (lowest id on ties).
+ *    token every step picked.
  *  d_logits: device float[n][vocab]: the logits of the last step.
  *  The page table must hold every position up to seq_lens[b] + steps - 1;
  *  seq_lens is not modified (the caller advances it by `steps`).
- * The result equals `steps` calls of mk_decode_step that feed back the greedy
+ * The result equals `steps` calls of mk_decode_step that feed back the picked
  * token, bit for bit.  Not combinable with mk_set_layer_inputs.
+ * Errors: as mk_decode_step; MK_ERR_INVALID_ARG for steps outside
+ * [1, 2^20] or a missing d_next_tokens with steps > 1; MK_ERR_STATE with
+ * the layer-input hook set.
  * Source: the whole decode loop in one persistent kernel with no launch or
  * host synchronization between operations (aiweekly.co, paragraph 2;
  * ainews.surl.tw, paragraph 1); a step-after-step loop is the next step of
@@ -201,14 +217,25 @@ int mk_decode_steps(mk_ctx* ctx, int32_t n, int32_t steps, const int32_t* d_toke
 /* Synchronizes `stream`, reads the sticky device error word and clears it.
  * *code receives 0 or an MK_ERR_DEVICE_* code; *cu and *task (may be NULL)
  * the workgroup and task that raised it.  After a device error the context
- * needs mk_reset before the next step. */
+ * needs mk_reset before the next step.  Errors: MK_ERR_STATE when not bound,
+ * MK_ERR_HIP when the read fails.  Source: the dependency counters live in
+ * global memory (ainews.surl.tw, paragraph 2; aiweekly.co, paragraph 3); the
+ * pages say nothing of failures: a bounded wait and a sticky error word that
+ * makes every other wait give up (so the grid drains) are this library's
+ * reading of how such a kernel must fail. */
 int mk_get_error(mk_ctx* ctx, int32_t* code, int32_t* cu, int32_t* task, void* stream);
 
-/* Clears counters, tickets and the error word on `stream` with a fill kernel. */
+/* Clears counters, tickets, the error word and the epoch-tagged words on
+ * `stream` with a fill kernel, and restarts the epoch.  Errors: MK_ERR_STATE
+ * when not bound, MK_ERR_HIP when the fill cannot be launched.  Source: as
+ * mk_get_error (the counters of ainews.surl.tw, paragraph 2, are never reset
+ * between steps: each step waits for epoch times fan-in). */
 int mk_reset(mk_ctx* ctx, void* stream);
 
-/* Sets the bound of every dependency wait in microseconds (default 2e6).
- * Host only; applies from the next step. */
+/* Sets the bound of every dependency wait in microseconds (default 2e6);
+ * a wait past it raises MK_ERR_DEVICE_TIMEOUT and the grid drains.  Errors:
+ * MK_ERR_INVALID_ARG for a bound below 1.  Host only; applies from the next
+ * step.  Source: as mk_get_error. */
 int mk_set_spin_limit_us(mk_ctx* ctx, int64_t microseconds);
 
 /* Test hook for checking each layer in isolation: when d_x is not NULL,
@@ -217,7 +244,10 @@ int mk_set_spin_limit_us(mk_ctx* ctx, int64_t microseconds);
  * slot 0 unused) instead of the residual the previous layer wrote, so each
  * layer runs on inputs the caller chose (e.g. a reference implementation's).
  * Layer outputs are still written to the workspace (mk_get_ws_offsets).
- * NULL restores normal operation.  Host only; applies from the next step. */
+ * NULL restores normal operation.  Host only; applies from the next step.
+ * Errors: MK_ERR_INVALID_ARG for a pointer not 4-byte aligned.  A test hook
+ * with no counterpart in the pages: it lets each layer be compared with a
+ * reference on the reference's own inputs. */
 int mk_set_layer_inputs(mk_ctx* ctx, const float* d_x);
 
 /* Per-task timeline: when d_records is not NULL, every task q < capacity
@@ -226,7 +256,8 @@ int mk_set_layer_inputs(mk_ctx* ctx, const float* d_x);
  * were met, [2..5] phase marks inside the task body (0 where the body has
  * fewer phases), [6] it had signalled, [7] unused.  Tasks are numbered as
  * in mk_copy_schedule.  NULL turns tracing off.  Host only; applies from
- * the next step. */
+ * the next step.  Errors: MK_ERR_INVALID_ARG for capacity < 1 or a pointer
+ * not 8-byte aligned.  Instrumentation with no counterpart in the pages. */
 int mk_set_trace(mk_ctx* ctx, uint64_t* d_records, int64_t capacity);
 
 /* How each step picks the next token (d_next_tokens, and the token fed to the
@@ -247,10 +278,18 @@ int mk_set_trace(mk_ctx* ctx, uint64_t* d_records, int64_t capacity);
  * applies from the next step. */
 int mk_set_sampling(mk_ctx* ctx, double temperature, uint64_t seed);
 
+/* Thread-local text of the last failure on the calling thread. */
 const char* mk_last_error_message(void);
+/* Frees the context's host state (device buffers stay the caller's); NULL is a no-op. */
 void mk_destroy(mk_ctx* ctx);
 
-/* ---- host-only introspection (no GPU call; for tests and tooling) ---- */
+/* ---- host-only introspection (no GPU call; for tests and tooling) ----
+ * The task table they expose is the host-built schedule of ainews.surl.tw,
+ * paragraph 2, with 32-int32 descriptors (aiweekly.co, paragraph 2).  The
+ * calls that take a context return MK_ERR_STATE before mk_build_schedule
+ * (or when it is NULL); the others MK_ERR_INVALID_ARG for a null input, and
+ * all MK_ERR_INVALID_ARG for a short output buffer (mk_copy_schedule skips a
+ * NULL one). */
 
 typedef struct mk_schedule_info {
   int32_t num_cus;
@@ -296,7 +335,11 @@ int mk_attn_plan(const int32_t* seq_lens, int32_t n, int32_t n_kv, int32_t n_tas
                  int32_t* chunk, int32_t* plan);
 
 /* Offsets (bytes from the workspace base) of the per-layer activation
- * buffers, for debugging and layer-by-layer comparison:
+ * buffers, for debugging and layer-by-layer comparison.  The normalized input
+ * of a layer is not among them: it lives only in each unit's LDS.  The router
+ * logits (the router rows times it, in fp32) and the new K/V entries pin it
+ * down, and the top-k margin of a layer is the gap between its k-th and
+ * (k+1)-th router logit in the `router` buffer.
  *  x: float [n_layers+1][max_batch][hidden] residual entering each layer l >= 1 and the
  *     final norm (slot 0 unused), as the step summed it from layer l-1's outputs, also when
  *     mk_set_layer_inputs feeds the layers other inputs
