@@ -97,6 +97,15 @@ int mk_create(const mk_config* cfg, mk_ctx** out);
  *  prefetch_bytes: upper bound on the LDS region that receives weight tiles
  *    and K/V pages before a task's wait (0 = all LDS left over by the other
  *    regions; > 0 = at most this many bytes; < 0 = no such region).
+ *  pool_64ths: share of each layer's expert gate/up rows, in 64ths, that is
+ *    not assigned ahead but claimed at run time, 16 rows at a time, by
+ *    whichever unit is idle: the gate/up units once their own rows are done
+ *    and the attention units past their chunk (0 or < 0 = none, the default;
+ *    at most 63).  On the 30B shape at batch 1 and 8K, 8 to 24 64ths cost
+ *    about 11% per step: every claimer's final claim is one more device
+ *    round trip, and the attention units' own top-k and normalization before
+ *    their pool items delay their Wo rows.  Source: idle units take over
+ *    tail-end work from the other path (ainews.surl.tw, paragraph 2).
  *  ctx_hint: expected cached tokens per sequence (0 = 4096); used only to
  *    size attn_units when that is 0. */
 typedef struct mk_schedule_params {
@@ -104,6 +113,7 @@ typedef struct mk_schedule_params {
   int32_t attn_units;
   int32_t router_units;
   int32_t prefetch_bytes;
+  int32_t pool_64ths;
   int64_t ctx_hint;
 } mk_schedule_params;
 

@@ -44,7 +44,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
   size_t state = 0, n_state_u32 = 0;  // counter flags, tickets, error word (zeroed by mk_reset)
-  size_t ctr = 0, tickets = 0, err = 0, rll = 0;  // (u32 offsets in the state region)
+  size_t ctr = 0, tickets = 0, err = 0, rll = 0, claims = 0;  // (u32 offsets in the state region)
   size_t tasks = 0, queue_off = 0, wtab = 0, inv_freq = 0;
   size_t x = 0, xr = 0, qkv = 0, rlog = 0, attn_part = 0, attn_out = 0, wo_out = 0, h = 0, lm_part = 0, sel = 0;
   size_t total = 0;
@@ -58,6 +58,7 @@ struct mk_ctx {
   int ncu = 0, n_attn = 0, n_gu = 0, n_out = 0, n_lm = 0, n_ctr = 0, n_tickets = 0, n_slots = 0;
   int out_rows_max = 0, gu_rows_max = 0, lm_rows_max = 0, pre_rows_max = 0;
   int lds_b = 0, lds_c = 0, lds_p = 0, pf_bytes = 0, pf_wide = 0, tile_off = 0;
+  int gu_pool = 0, gu_items = 0, gu_parts = 0;  // the shared gate/up pool
   size_t lds_bytes = 0;
   std::vector<Task> tasks;
   std::vector<int32_t> qoff;
@@ -248,9 +249,10 @@ static WsLayout layout_workspace(const mk_ctx* c) {
   w.ctr = 0;
   w.tickets = (size_t)c->n_ctr * kCounterWords;
   w.err = w.tickets + c->n_tickets;
-  // epoch-tagged words (8-byte aligned): router logits
+  // epoch-tagged words (8-byte aligned): router logits; then the pool claim counters
   w.rll = align_up(w.err + E_WORDS, 2);
-  w.n_state_u32 = w.rll + 2 * L * B * (size_t)f.n_experts;
+  w.claims = w.rll + 2 * L * B * (size_t)f.n_experts;
+  w.n_state_u32 = w.claims + L;
   take(4 * w.n_state_u32);
   w.tasks = take(sizeof(Task) * c->tasks.size());
   w.queue_off = take(4 * (c->ncu + 1));
@@ -317,6 +319,21 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
   n_attn = std::min(n_attn, ncu - 2);  // at least one unit each for the QKV and the router rows
   if (n_attn < n_lead + 1) return fail(MK_ERR_UNSUPPORTED, "too few compute units for the attention split");
   const int n_gu = ncu - n_attn;
+
+  // The shared gate/up pool: the last pool/64 of a layer's virtual gate/up rows
+  // (one expert's gate and up row each) go out in items of kGuItem rows, claimed
+  // at run time by the gate/up tasks once their own rows are done and by a pool
+  // task on every non-lead attention unit right after its chunk.  Every claimer
+  // ends with one failed claim, so a step adds exactly items + claimers to the
+  // layer's claim counter whatever the order: the kernel subtracts
+  // (epoch - 1) * (items + claimers) to number this step's items.
+  const int pool = std::max(0, std::min(p.pool_64ths, 63));
+  const int64_t rows_max = (int64_t)std::min(E, B * f.top_k) * f.inter;
+  const int gu_items = pool > 0 ? (int)((rows_max * pool / 64 + kGuItem - 1) / kGuItem) : 0;
+  const int n_pool_tasks = gu_items > 0 ? n_attn - n_lead : 0;
+  c->gu_pool = gu_items > 0 ? pool : 0;
+  c->gu_items = gu_items;
+  c->gu_parts = n_gu + n_pool_tasks;
 
   c->tasks.clear();
   c->qoff.assign(ncu + 1, 0);
@@ -419,6 +436,14 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
         // to their segment's ticket instead
         t.signal = q < n_lead ? ctr_index(l, C_ATTN) : -1;
         c->tasks.push_back(t);
+        if (n_pool_tasks > 0 && q >= n_lead) {
+          // gate/up rows from the shared pool (needs the router logits; polls them itself)
+          Task g = make_task(OP_GUTAIL, l);
+          g.wait[0] = ctr_index(l, C_ROUTER);
+          g.fanin[0] = n_router_tasks[l];
+          g.signal = ctr_index(l, C_GATEUP);
+          c->tasks.push_back(g);
+        }
         wo_rows(q, &r0, &r1);
         if (r1 > r0) {
           Task w = make_task(OP_WO, l);
@@ -445,7 +470,7 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
         // update, x_l + moe_l; the next layer adds the Wo rows' half
         Task t = make_task(OP_OUT, l);
         t.wait[0] = ctr_index(l, C_GATEUP);
-        t.fanin[0] = n_gu;
+        t.fanin[0] = c->gu_parts;
         t.wait[1] = ctr_index(l, C_ROUTER);  // for the top-k, where no gate/up task left it in LDS
         t.fanin[1] = n_router_tasks[l];
         t.r0 = r0;
@@ -500,7 +525,7 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
                              (size_t)(group + 1) * f.head_dim * 2});  // attention: rotated q heads + the new k
   a_bytes = align_up(a_bytes, 256);
   const size_t b_bytes = kLdsB;
-  size_t c_gu = (size_t)std::min(c->gu_rows_max, kGuPass) * B * 2 * 4;
+  size_t c_gu = (size_t)std::max(std::min(c->gu_rows_max, kGuPass), c->gu_items > 0 ? kGuItem : 0) * B * 2 * 4;
   size_t c_out = (size_t)c->out_rows_max * B * f.top_k * 4;  // the experts' contributions to the task's rows
   size_t c_lm = (size_t)std::min(c->lm_rows_max, kLmPass) * B * 4;
   // attention: the waves' partial results, or (a segment's lead) the (max, sum) of all chunks plus one float4 per thread
@@ -780,6 +805,9 @@ extern "C" int mk_decode_steps(mk_ctx* c, int32_t n, int32_t steps, const int32_
   a.pf_bytes = c->pf_bytes;
   a.pf_wide = c->pf_wide;
   a.tile_off = c->tile_off;
+  a.gu_pool = c->gu_pool;
+  a.gu_items = c->gu_items;
+  a.gu_parts = c->gu_parts;
   uint8_t* w = c->wsp;
   a.tasks = (const Task*)(w + c->ws.tasks);
   a.queue_off = (const int32_t*)(w + c->ws.queue_off);
@@ -788,6 +816,7 @@ extern "C" int mk_decode_steps(mk_ctx* c, int32_t n, int32_t steps, const int32_
   a.tickets = st + c->ws.tickets;
   a.err = (int32_t*)(st + c->ws.err);
   a.rll = (uint64_t*)(st + c->ws.rll);
+  a.claims = st + c->ws.claims;
   a.wtab = (const uint64_t*)(w + c->ws.wtab);
   a.inv_freq = (const double*)(w + c->ws.inv_freq);
   a.x = (float*)(w + c->ws.x);

@@ -1673,19 +1673,11 @@ struct JobGateUp {
 // (once the router rows are done), which spares the routing a hop of its own.
 // have_xs: region A still holds this layer's normalized input, left there by
 // the PRE task that ran just before on this compute unit.
-// Returns whether region B holds this layer's top-k afterwards (false when the
-// router logits never arrived: abort or time-out).
-TASK bool task_gateup(const KArgs& a, const Task& t, const Lds& s, int qi, bool have_xs) {
-  const int l = t.layer;
-  if (!compute_topk(a, l, s.tk, s.C, qi, s.flags + 0, 0)) return false;
-  if (t.idx == 0) write_sel(a, l, s.tk);
-  mark(a, qi, 1);
-  uint16_t* xs = (uint16_t*)s.A;
-  if (!have_xs) norm_inputs(a, l, wptr(a, widx(l, WL_NORM)), xs, s.red8, qi, -1);
-  mark(a, qi, 2);
+// Virtual gate/up rows [va, vb) of layer l (row v: expert U[v / I], row
+// v % I of its gate and up matrices), in passes of at most kGuPass (bounds the
+// LDS of the gate/up results): SwiGLU of each token's pair into h.
+DEV void gateup_range(const KArgs& a, const Lds& s, int l, const uint16_t* xs, int64_t va, int64_t vb) {
   const TopK* tk = s.tk;
-  const int64_t R = (int64_t)tk->nU * a.I;
-  const int64_t va = R * t.idx / a.n_gu, vb = R * (t.idx + 1) / a.n_gu;
   JobGateUp j;
   j.tk = tk;
   j.wg = wptr(a, widx(l, WL_GATE));
@@ -1698,7 +1690,6 @@ TASK bool task_gateup(const KArgs& a, const Task& t, const Lds& s, int qi, bool 
   j.topk = a.topk;
   const int mt = tk->maxtok;
   uint16_t* hl = a.h + (size_t)l * a.max_batch * a.topk * a.I;
-  // virtual rows in passes of at most kGuPass (bounds the LDS of gate/up results)
   for (int64_t v0 = va; v0 < vb; v0 += kGuPass) {
     const int nvr = (int)((vb - v0) < kGuPass ? (vb - v0) : kGuPass);
     j.v0 = v0;
@@ -1717,6 +1708,70 @@ TASK bool task_gateup(const KArgs& a, const Task& t, const Lds& s, int qi, bool 
     }
     __syncthreads();
   }
+}
+
+// The split of layer l's R = nU * I virtual rows: [0, Rs) cut evenly over the
+// gate/up tasks, [Rs, R) the shared pool in items of kGuItem rows.
+DEV int64_t gateup_static_rows(const KArgs& a, int64_t R, int* n_items) {
+  int64_t items = a.gu_items ? (R * a.gu_pool / 64 + kGuItem - 1) / kGuItem : 0;
+  if (items > a.gu_items) items = a.gu_items;
+  if (items * kGuItem > R) items = R / kGuItem;
+  *n_items = (int)items;
+  return R - items * kGuItem;
+}
+
+// Claims items of layer l's shared pool until none is left.  The claim counter
+// is never reset: every claimer of a step ends with one failed claim, so each
+// step adds exactly gu_items + gu_parts, and this step's items are numbered
+// from (epoch - 1) times that (mod 2^32).  Items past this step's count (fewer
+// distinct experts than the most there can be) are claimed and skipped.
+DEV void gateup_pool(const KArgs& a, const Lds& s, int l, const uint16_t* xs, int64_t R) {
+  if (a.gu_items == 0) return;
+  int n_items;
+  const int64_t Rs = gateup_static_rows(a, R, &n_items);
+  const uint32_t base = (a.epoch - 1u) * (uint32_t)(a.gu_items + a.gu_parts);
+  for (;;) {
+    if (tid() == 0)
+      s.flags[12] = (int32_t)(__hip_atomic_fetch_add(a.claims + l, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - base);
+    __syncthreads();
+    const int k = s.flags[12];
+    __syncthreads();
+    if (k < 0 || k >= a.gu_items) break;
+    if (k < n_items) {
+      const int64_t v0 = Rs + (int64_t)k * kGuItem;
+      gateup_range(a, s, l, xs, v0, v0 + kGuItem);
+    }
+  }
+}
+
+// Returns whether region B holds this layer's top-k afterwards (false when the
+// router logits never arrived: abort or time-out).
+TASK bool task_gateup(const KArgs& a, const Task& t, const Lds& s, int qi, bool have_xs) {
+  const int l = t.layer;
+  if (!compute_topk(a, l, s.tk, s.C, qi, s.flags + 0, 0)) return false;
+  if (t.idx == 0) write_sel(a, l, s.tk);
+  mark(a, qi, 1);
+  uint16_t* xs = (uint16_t*)s.A;
+  if (!have_xs) norm_inputs(a, l, wptr(a, widx(l, WL_NORM)), xs, s.red8, qi, -1);
+  mark(a, qi, 2);
+  const int64_t R = (int64_t)s.tk->nU * a.I;
+  int n_items;
+  const int64_t Rs = gateup_static_rows(a, R, &n_items);
+  gateup_range(a, s, l, xs, Rs * t.idx / a.n_gu, Rs * (t.idx + 1) / a.n_gu);
+  mark(a, qi, 3);
+  gateup_pool(a, s, l, xs, R);
+  return true;
+}
+
+// An attention unit past its chunk: the layer's top-k and normalized input,
+// then items of the shared gate/up pool.  Returns as task_gateup.
+TASK bool task_gutail(const KArgs& a, const Task& t, const Lds& s, int qi) {
+  const int l = t.layer;
+  if (!compute_topk(a, l, s.tk, s.C, qi, s.flags + 0, 0)) return false;
+  uint16_t* xs = (uint16_t*)s.A;
+  norm_inputs(a, l, wptr(a, widx(l, WL_NORM)), xs, s.red8, qi, 1);
+  gateup_pool(a, s, l, xs, (int64_t)s.tk->nU * a.I);
+  mark(a, qi, 2);
   return true;
 }
 
@@ -2070,7 +2125,7 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a0
         ok = wait_counter_at(a, ctr_index(a.L, C_DONE), a.n_lm, q, s.flags + 1, a.epoch - 1);
       // attention, Wo and output tasks wait inside, once their loads are in flight; gate/up
       // tasks poll the tagged router logits inside
-      const bool own_wait = t.op == OP_ATTN || t.op == OP_OUT || t.op == OP_WO || t.op == OP_GATEUP;
+      const bool own_wait = t.op == OP_ATTN || t.op == OP_OUT || t.op == OP_WO || t.op == OP_GATEUP || t.op == OP_GUTAIL;
       if (ok && !own_wait) ok = wait_counter(a, t.wait[0], t.fanin[0], q, s.flags + 0);
       if (ok && !own_wait && t.wait[1] >= 0) ok = wait_counter(a, t.wait[1], t.fanin[1], q, s.flags + 1);
       if (a.trace && tid() == 0) t_ready = wall_clock64();
@@ -2082,6 +2137,7 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a0
           case OP_GATEUP: tk_layer = task_gateup(a, t, s, q, xs_layer == t.layer) ? t.layer : -1; break;
           case OP_OUT: wait_waves = task_out(a, t, s, q, tk_layer == t.layer, tk_layer); break;
           case OP_WO: task_wo(a, t, s, q, npf); break;
+          case OP_GUTAIL: tk_layer = task_gutail(a, t, s, q) ? t.layer : -1; break;
           case OP_LMHEAD: task_lmhead(a, t, s, q); break;
           default: break;
         }

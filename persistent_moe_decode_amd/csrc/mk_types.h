@@ -21,6 +21,7 @@ constexpr int kMaxExperts = 128;   // the top-k's expert pass covers lanes e and
 constexpr int kMaxGroup = 8;       // q heads per kv head
 constexpr int kTaskInts = 32;      // 128-byte descriptor
 constexpr int kGuPass = 256;       // gate/up virtual rows per pass of one task
+constexpr int kGuItem = 16;        // gate/up virtual rows per item of the shared pool
 constexpr int kLmPass = 512;       // LM head rows per pass of one task
 constexpr int kMfmaRedBytes = 16 * 1024; // region C bytes for the matrix-core path's partial tiles (batch >= 2)
 constexpr int kTraceWords = 8;     // per task: fetch, ready, 4 phase marks, done, spare
@@ -34,6 +35,7 @@ enum Op : int32_t {
   OP_OUT = 4,     // rows of the selected experts' down projection + residual update
   OP_LMHEAD = 5,  // final RMSNorm + LM head rows; last arriver takes the argmax
   OP_WO = 6,      // rows of Wo times the merged attention output (run by the attention units)
+  OP_GUTAIL = 7,  // an attention unit past its chunk takes gate/up rows from the layer's shared pool
 };
 
 // One task: 32 int32 (128 bytes, one cache line).
@@ -86,12 +88,16 @@ struct KArgs {
   int32_t pf_wide;                                 // bytes of the PRE / WO weight tile region, which starts tile_off
                                                    // bytes into region C and runs to the end of LDS
   int32_t tile_off;                                // (region C below it: the output task's expert contributions)
+  int32_t gu_pool;                                 // 64ths of a layer's gate/up virtual rows in the shared pool
+  int32_t gu_items;                                // pool items per layer at the largest expert count
+  int32_t gu_parts;                                // tasks per layer that claim from the pool
   const Task* tasks;
   const int32_t* queue_off;
   uint32_t* flags;      // counters: [(L + 1) * kCtrPerLayer][kCounterWords]
   uint32_t* tickets;    // attention tickets [L][max_batch][nkv], then 1 for the LM head
   int32_t* err;         // E_WORDS
   uint64_t* rll;        // router logits as epoch-tagged words [L][max_batch][E] (zeroed with the counters)
+  uint32_t* claims;     // per layer: items of the shared gate/up pool claimed so far (zeroed with the counters)
   const uint64_t* wtab; // device pointers of the weights
   const double* inv_freq; // [d/2]
   // activations

@@ -62,7 +62,7 @@ class DeviceDecoder:
     def __init__(self, w: synth.Workload, device: str = "cuda:0", num_cus: int = 0, ctx_hint: int | None = None,
                  max_batch: int | None = None, static_workspace: bool = False, **sched):
         """static_workspace: bind with the library's static workspace (no workspace tensor);
-        sched: further mk_schedule_params fields (attn_units, router_units, prefetch_bytes)."""
+        sched: further mk_schedule_params fields (attn_units, router_units, prefetch_bytes, pool_64ths)."""
         self.w = w
         self.shape = s = w.shape
         self.dev = torch.device(device)

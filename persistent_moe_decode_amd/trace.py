@@ -7,7 +7,8 @@ body, and when it had signalled.  This module joins them with the task table.
 
 Phase marks per op: PRE [inputs loaded, norm done, rows done]; ATTN [q
 rotated and new K/V written, copied pages landed, positions done, partial
-stored]; GATEUP [top-k selected (wave 0), routing tables built, norm done];
+stored]; GATEUP [top-k selected (wave 0), routing tables built, norm done, own rows done];
+GUTAIL [top-k selected (wave 0), norm done, pool items done];
 OUT [h loaded, wave 0's down rows done, all down rows done, residual rows stored]; WO [attention output loaded, rows done];
 LMHEAD [norm done, rows done, local argmax done].  Tasks that wait inside
 their body (ATTN, GATEUP, OUT, WO) record as "ready" the moment their inputs

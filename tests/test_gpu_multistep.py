@@ -21,13 +21,14 @@ def _kv_slots(dec, n, lens, steps):
     return np.stack(out)
 
 
-@pytest.mark.parametrize("batch,context", [(1, [2048]), (3, [900, 17, 1500])])
-def test_steps_in_one_launch_equal_single_launches(batch, context):
+@pytest.mark.parametrize("batch,context,pool", [(1, [2048], 0), (3, [900, 17, 1500], 0), (3, [900, 17, 1500], 16)])
+def test_steps_in_one_launch_equal_single_launches(batch, context, pool):
+    """pool: 64ths of the gate/up rows in the shared pool (its claim counters run across the steps)."""
     from persistent_moe_decode_amd.runtime import DeviceDecoder
     steps = 8
     w = synth.Workload(f"mid_ms{batch}", synth.MID, batch=batch, steps=steps + 1, context=context)
-    print(f"workload {w.name}: batch {batch}, {steps} steps", flush=True)
-    dec = DeviceDecoder(w)
+    print(f"workload {w.name}: batch {batch}, {steps} steps, pool {pool}", flush=True)
+    dec = DeviceDecoder(w, pool_64ths=pool)
     dev, n = dec.dev, batch
     lens0 = torch.tensor(context, dtype=torch.int32, device=dev)
     tok0 = torch.tensor([int(w.prompt(b)[context[b]]) for b in range(n)], dtype=torch.int32, device=dev)

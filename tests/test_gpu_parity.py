@@ -121,6 +121,16 @@ def test_mid_small_prefetch_region(pf_bytes):
     _check(parity.run(w, mode="isolated", log=_log, prefetch_bytes=pf_bytes))
 
 
+@pytest.mark.parametrize("pool", [16, 63])
+def test_mid_shared_gateup_pool(pool):
+    """Part of every layer's gate/up rows claimed at run time from a shared pool, by the gate/up units
+    after their own rows and by the non-lead attention units after their chunk (16/64 of the rows,
+    and all but one 64th): same parity bar, 3 steps in one process (the claim counters carry over)."""
+    from tests import parity
+    w = synth.Workload(f"mid_pool{pool}", synth.MID, batch=3, steps=3, context=[1500, 17, 600])
+    _check(parity.run(w, mode="isolated", log=_log, pool_64ths=pool))
+
+
 @pytest.mark.parametrize("attn_cus", [13, 40])
 def test_mid_attention_unit_counts(attn_cus):
     """Attention units forced to leads + 1 (one unit takes every Wo row and every chunk past a
