@@ -1859,20 +1859,43 @@ TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have
   mark(a, qi, 0);
   // expert down projections: the register rows, then the rest from HBM
   const int mt = tk->maxtok;
+  if (cpl == kDownC) {
+    // every chunk present: a row's kDownC LDS reads go out together, then the
+    // arithmetic (a guard per chunk would make each read wait for the last)
 #pragma unroll
-  for (int g = 0; g < kDownGroups; ++g) {
-    const int i = g * kGroupRows + ig;
-    const bool act = i < npre;
-    const int nx = act ? jd.nx(i) : 0;
-    for (int tt = 0; tt < mt; ++tt) {
-      const bool on = tt < nx;
-      const uint4* xr = jd.x(act ? i : 0, on ? tt : 0) + li;
-      float acc = 0.f;
+    for (int g = 0; g < kDownGroups; ++g) {
+      const int i = g * kGroupRows + ig;
+      const bool act = i < npre;
+      const int nx = act ? jd.nx(i) : 0;
+      for (int tt = 0; tt < mt; ++tt) {
+        const bool on = tt < nx;
+        const uint4* xr = jd.x(act ? i : 0, on ? tt : 0) + li;
+        uint4 xv[kDownC];
 #pragma unroll
-      for (int c = 0; c < kDownC; ++c)
-        if (c < cpl) acc = dot8(dp[g][c], xr[16 * c], acc);
-      acc = group_sum<16>(acc);
-      if (on && li == 0) jd.emit(i, tt, acc);
+        for (int c = 0; c < kDownC; ++c) xv[c] = xr[16 * c];
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < kDownC; ++c) acc = dot8(dp[g][c], xv[c], acc);
+        acc = group_sum<16>(acc);
+        if (on && li == 0) jd.emit(i, tt, acc);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < kDownGroups; ++g) {
+      const int i = g * kGroupRows + ig;
+      const bool act = i < npre;
+      const int nx = act ? jd.nx(i) : 0;
+      for (int tt = 0; tt < mt; ++tt) {
+        const bool on = tt < nx;
+        const uint4* xr = jd.x(act ? i : 0, on ? tt : 0) + li;
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < kDownC; ++c)
+          if (c < cpl) acc = dot8(dp[g][c], xr[16 * c], acc);
+        acc = group_sum<16>(acc);
+        if (on && li == 0) jd.emit(i, tt, acc);
+      }
     }
   }
   rowdots_range<false>(a.I, npre, nd, mt, jd);
