@@ -154,6 +154,7 @@ static Task make_task(int op, int layer) {
   t.wait[0] = t.wait[1] = -1;
   t.late_wait = -1;
   t.signal = -1;
+  t.report = -1;
   return t;
 }
 
@@ -172,9 +173,10 @@ static int simulate_raw(const Task* tasks, int nt, const int32_t* qoff, int ncu,
   std::vector<int64_t> ctr(n_ctr, 0), signals(n_ctr, 0);
   for (int i = 0; i < nt; ++i) {
     const Task& t = tasks[i];
-    if (t.signal >= n_ctr || t.wait[0] >= n_ctr || t.wait[1] >= n_ctr || t.late_wait >= n_ctr)
+    if (t.signal >= n_ctr || t.wait[0] >= n_ctr || t.wait[1] >= n_ctr || t.late_wait >= n_ctr || t.report >= n_ctr)
       return fail(MK_ERR_INVALID_ARG, "counter index out of range");
     if (t.signal >= 0) signals[t.signal]++;
+    if (t.report >= 0) signals[t.report]++;
   }
   // the signalling tasks of a counter hold slots 0 .. signals - 1, one each (slots spread the adds over sub-counters)
   std::vector<std::vector<char>> owned(n_ctr);
@@ -211,6 +213,7 @@ static int simulate_raw(const Task* tasks, int nt, const int32_t* qoff, int ncu,
         }
         if (!ready) break;
         if (t.signal >= 0) ctr[t.signal]++;
+        if (t.report >= 0) ctr[t.report]++;
         head[q]++;
         done++;
         progress = true;
@@ -433,8 +436,17 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
         t.idx = q;
         t.count = n_attn;
         // leads signal once their segment is merged; the other chunks report
-        // to their segment's ticket instead
+        // to their segment's ticket instead.  Which chunks feed which lead is
+        // decided at run time (the split follows the sequence lengths), so the
+        // simulator takes the superset: every lead waits, inside its body, for
+        // every other chunk task of the layer
         t.signal = q < n_lead ? ctr_index(l, C_ATTN) : -1;
+        if (q < n_lead) {
+          t.late_wait = ctr_index(l, C_CHUNK);
+          t.late_fanin = n_attn - n_lead;
+        } else {
+          t.report = ctr_index(l, C_CHUNK);
+        }
         c->tasks.push_back(t);
         if (n_pool_tasks > 0 && q >= n_lead) {
           // gate/up rows from the shared pool (needs the router logits; polls them itself)

@@ -47,15 +47,17 @@ struct Task {
   int32_t signal;     // counter this task adds one to when done, or -1
   int32_t r0, r1;     // row range (PRE, OUT, LMHEAD)
   int32_t idx, count; // index of this task among the op's tasks of the layer, and their number
-  int32_t late_wait;  // counter waited inside the body, once its first part is done (-1 = none)
-  int32_t late_fanin;
+  int32_t late_wait;  // host simulator only: a counter the task's body waits on after its first
+  int32_t late_fanin; // part (-1 = none); the kernel waits there by other means (a segment ticket)
   int32_t slot;       // this task's index among the tasks signalling its counter: 0 .. (signals) - 1
   int32_t tagged;     // 1: consumers read this task's output as epoch-tagged words (value | epoch << 32),
                       // so its signal is an edge for the host simulator only: on the device no counter
                       // add and no wait for the stores to complete
   int32_t next_layer, next_r0, next_r1;  // OUT: the PRE task that follows on this queue (rows; r1 = 0: none),
                                          // whose weight tile the OUT task copies into LDS while it waits
-  int32_t pad[14];
+  int32_t report;     // host simulator only: a counter this task feeds by other means (a non-lead
+                      // attention chunk reports to its segment's ticket), or -1
+  int32_t pad[13];
 };
 static_assert(sizeof(Task) == kTaskInts * 4, "task descriptor is 128 bytes");
 
@@ -64,7 +66,8 @@ static_assert(sizeof(Task) == kTaskInts * 4, "task descriptor is 128 bytes");
 // s % kSubCounters, and a wait is over when the words sum to epoch * fan-in
 // (no reset between steps).  Spreading the adds keeps any one line from
 // serializing many of them, and a waiter reads only kSubCounters lines.
-enum CtrSlot : int32_t { C_QKV = 0, C_ROUTER = 1, C_ATTN = 2, C_GATEUP = 3, C_XNEXT = 4, C_DONE = 5, C_WO = 6 };
+enum CtrSlot : int32_t { C_QKV = 0, C_ROUTER = 1, C_ATTN = 2, C_GATEUP = 3, C_XNEXT = 4, C_DONE = 5, C_WO = 6,
+                         C_CHUNK = 7 };  // C_CHUNK: simulation only (the leads' ticket waits)
 constexpr int kCtrPerLayer = 8;
 constexpr int kSubCounters = 16;
 constexpr int kSubStride = 32;                           // words between sub-counters (128 bytes)

@@ -387,3 +387,37 @@ def test_sampling_arguments():
         assert e.value.code == mk.CODES["MK_ERR_INVALID_ARG"], bad
     c.set_sampling(0.0)
     c.set_sampling(0.7, 2 ** 64 - 1)
+
+
+def test_simulator_models_the_leads_ticket_wait():
+    """Every segment lead waits inside its body for the other chunks of its layer (modelled as a
+    superset, the split being decided at run time); a table where a non-lead chunk sits behind a
+    task that needs the leads' merge must deadlock in the simulation."""
+    F_REPORT = 18
+    w = synth.workload("mid")
+    c = _ctx(w.shape, 1, w.max_pages_per_seq, w.num_pages)
+    c.build_schedule(64, 2048)
+    tasks, qoff = c.schedule()
+    nctr = c.info().n_counters
+    attn0 = tasks[(tasks[:, F_OP] == OP_ATTN) & (tasks[:, F_LAYER] == 0)]
+    leads = attn0[attn0[:, F_SIGNAL] >= 0]
+    others = attn0[attn0[:, F_SIGNAL] < 0]
+    assert len(leads) >= 1 and len(others) >= 1
+    assert np.all(leads[:, F_LATE] >= 0) and np.all(leads[:, F_LATE_FAN] == len(others))
+    assert np.all(others[:, F_REPORT] == leads[0, F_LATE])
+    assert mk.simulate_table(tasks, qoff, nctr) == (0, len(tasks))
+    # on a unit with Wo rows, put its layer-0 Wo task in front of its layer-0 chunk
+    t = tasks.copy()
+    for q in range(len(qoff) - 1):
+        qt = t[qoff[q]:qoff[q + 1]]
+        ia = np.nonzero((qt[:, F_OP] == OP_ATTN) & (qt[:, F_LAYER] == 0) & (qt[:, F_SIGNAL] < 0))[0]
+        iw = np.nonzero((qt[:, F_OP] == OP_WO) & (qt[:, F_LAYER] == 0))[0]
+        if len(ia) and len(iw):
+            a, b = int(ia[0]), int(iw[0])
+            qt[[a, b]] = qt[[b, a]]
+            t[qoff[q]:qoff[q + 1]] = qt
+            break
+    else:
+        pytest.fail("no unit with both a chunk and Wo rows")
+    code, done = mk.simulate_table(t, qoff, nctr)
+    assert code == mk.CODES["MK_ERR_SCHEDULE"] and done < len(t)
