@@ -210,6 +210,8 @@ def main():
                     help="decode steps per launch of the persistent kernel (greedy tokens fed on the device)")
     ap.add_argument("--attn-units", type=int, default=0, help="schedule: attention compute units (0 = default)")
     ap.add_argument("--router-units", type=int, default=0, help="schedule: router compute units (0 = default)")
+    ap.add_argument("--qkv-units", type=int, default=0, help="schedule: dedicated Wqkv compute units (0 = none)")
+    ap.add_argument("--pool-64ths", type=int, default=0, help="schedule: shared gate/up pool share (0 = none)")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="after the run, one plain device-to-device copy of this many bytes (counter calibration)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -236,7 +238,8 @@ def main():
     if total > w.steps:
         w.steps = total  # page capacity for every position the run writes
     t0 = time.time()
-    dec = DeviceDecoder(w, attn_units=args.attn_units, router_units=args.router_units)
+    dec = DeviceDecoder(w, attn_units=args.attn_units, router_units=args.router_units, qkv_units=args.qkv_units,
+                        pool_64ths=args.pool_64ths)
     dec.fill_synthetic_kv()
     log(f"[bench] setup {time.time() - t0:.1f}s, {dec.info.num_cus} CUs, n_attn {dec.info.n_attn}, "
         f"lds {dec.info.lds_bytes} B, workspace {dec.ws_bytes / 2**20:.1f} MiB")

@@ -106,6 +106,11 @@ int mk_create(const mk_config* cfg, mk_ctx** out);
  *    round trip, and the attention units' own top-k and normalization before
  *    their pool items delay their Wo rows.  Source: idle units take over
  *    tail-end work from the other path (ainews.surl.tw, paragraph 2).
+ *  qkv_units: stage-1 units that take the Wqkv rows and no gate/up rows
+ *    (0 = none: the Wqkv rows go to every stage-1 unit but the router's, each
+ *    of which then also takes gate/up rows).  With qkv_units > 0 the other
+ *    stage-1 units normalize and go straight to the router poll and their
+ *    gate/up rows.  Clamped to [1, stage-1 units - router units - 1].
  *  ctx_hint: expected cached tokens per sequence (0 = 4096); used only to
  *    size attn_units when that is 0. */
 typedef struct mk_schedule_params {
@@ -114,6 +119,7 @@ typedef struct mk_schedule_params {
   int32_t router_units;
   int32_t prefetch_bytes;
   int32_t pool_64ths;
+  int32_t qkv_units;
   int64_t ctx_hint;
 } mk_schedule_params;
 

@@ -321,7 +321,21 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
   n_attn = std::max(n_attn, n_lead + 1);
   n_attn = std::min(n_attn, ncu - 2);  // at least one unit each for the QKV and the router rows
   if (n_attn < n_lead + 1) return fail(MK_ERR_UNSUPPORTED, "too few compute units for the attention split");
-  const int n_gu = ncu - n_attn;
+  // Stage-1 units n_attn ..: the router's rows go to the last n_rcu of them.
+  // Without dedicated QKV units every other stage-1 unit takes Wqkv rows and
+  // then gate/up rows; with qkv_units = n_q > 0 the first n_q take only Wqkv
+  // rows and the rest (router units included) only gate/up rows, the ones
+  // without router rows running a PRE task that just normalizes (no rows, no
+  // signal), so their gate/up rows start as soon as the routing is in.
+  const int R1 = qkv_rows + E;
+  const int m1 = ncu - n_attn;
+  int n_rcu = (int)(((int64_t)m1 * E + R1 - 1) / R1);
+  if (p.router_units > 0) n_rcu = p.router_units;
+  n_rcu = std::min(m1 - 1, std::max(1, n_rcu));
+  const int n_q = p.qkv_units > 0 ? std::max(1, std::min(p.qkv_units, m1 - n_rcu - 1)) : 0;
+  const int n_qcu = n_q > 0 ? n_q : m1 - n_rcu;  // units with Wqkv rows
+  const int gu0 = n_attn + n_q;                  // first unit with gate/up rows
+  const int n_gu = ncu - gu0;
 
   // The shared gate/up pool: the last pool/64 of a layer's virtual gate/up rows
   // (one expert's gate and up row each) go out in items of kGuItem rows, claimed
@@ -346,23 +360,16 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
   c->n_ctr = (L + 1) * kCtrPerLayer;
   c->n_tickets = L * B * f.n_kv_heads + 1;  // attention (seq, kv head) merges, LM argmax
 
-  // Stage-1 rows over units n_attn ..: the router's rows go to the last n_rcu
-  // of them, Wqkv rows to the others, so no unit has two stage-1 tasks and the
-  // routing is ready as early as the QKV rows.
-  const int R1 = qkv_rows + E;
-  const int m1 = ncu - n_attn;
-  int n_rcu = (int)(((int64_t)m1 * E + R1 - 1) / R1);
-  if (p.router_units > 0) n_rcu = p.router_units;
-  n_rcu = std::min(m1 - 1, std::max(1, n_rcu));
-  const int n_qcu = m1 - n_rcu;
+  // Stage-1 rows: no unit has two stage-1 tasks, and the routing is ready as
+  // early as the QKV rows.
   auto pre_rows = [&](int q, int* r0, int* r1) {
     *r0 = *r1 = 0;
     if (q < n_attn) return;
     q -= n_attn;
     if (q < n_qcu) {
       split_rows(qkv_rows, n_qcu, q, r0, r1);
-    } else {
-      split_rows(E, n_rcu, q - n_qcu, r0, r1);
+    } else if (q >= m1 - n_rcu) {
+      split_rows(E, n_rcu, q - (m1 - n_rcu), r0, r1);
       *r0 += qkv_rows;
       *r1 += qkv_rows;
     }
@@ -412,7 +419,7 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
     for (int l = 0; l < L; ++l) {
       int r0, r1;
       pre_rows(q, &r0, &r1);
-      if (r1 > r0) {
+      if (r1 > r0 || (n_q > 0 && q >= gu0)) {
         const bool router = r0 >= qkv_rows;
         Task t = make_task(OP_PRE, l);
         if (l > 0) {
@@ -424,8 +431,10 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
         }
         t.r0 = r0;
         t.r1 = r1;
-        t.signal = ctr_index(l, router ? C_ROUTER : C_QKV);
-        t.tagged = router ? 1 : 0;  // gate/up and output tasks poll the tagged router logits
+        if (r1 > r0) {
+          t.signal = ctr_index(l, router ? C_ROUTER : C_QKV);
+          t.tagged = router ? 1 : 0;  // gate/up and output tasks poll the tagged router logits
+        }
         c->tasks.push_back(t);
       }
       // stage 2: attention units run their chunk, the others gate/up rows
@@ -466,11 +475,11 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
           w.signal = ctr_index(l, C_WO);
           c->tasks.push_back(w);
         }
-      } else {
+      } else if (q >= gu0) {
         Task t = make_task(OP_GATEUP, l);
         t.wait[0] = ctr_index(l, C_ROUTER);
         t.fanin[0] = n_router_tasks[l];
-        t.idx = q - n_attn;
+        t.idx = q - gu0;
         t.count = n_gu;
         t.signal = ctr_index(l, C_GATEUP);
         c->tasks.push_back(t);

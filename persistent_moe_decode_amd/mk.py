@@ -46,7 +46,8 @@ class MkConfig(ctypes.Structure):
 class ScheduleParams(ctypes.Structure):
     """mk_schedule_params: how the schedule is cut (all zero = defaults)."""
     _fields_ = [("num_cus", ctypes.c_int32), ("attn_units", ctypes.c_int32), ("router_units", ctypes.c_int32),
-                ("prefetch_bytes", ctypes.c_int32), ("pool_64ths", ctypes.c_int32), ("ctx_hint", ctypes.c_int64)]
+                ("prefetch_bytes", ctypes.c_int32), ("pool_64ths", ctypes.c_int32), ("qkv_units", ctypes.c_int32),
+                ("ctx_hint", ctypes.c_int64)]
 
 
 class ScheduleInfo(ctypes.Structure):
@@ -170,12 +171,12 @@ class Context:
             pass
 
     def build_schedule(self, num_cus: int = 0, ctx_hint: int = 0, attn_units: int = 0, router_units: int = 0,
-                       prefetch_bytes: int = 0, pool_64ths: int = 0) -> int:
+                       prefetch_bytes: int = 0, pool_64ths: int = 0, qkv_units: int = 0) -> int:
         """mk_build_schedule; returns the workspace size in bytes."""
         p = ScheduleParams()
         lib().mk_schedule_params_default(ctypes.byref(p))
-        p.num_cus, p.ctx_hint, p.attn_units, p.router_units, p.prefetch_bytes, p.pool_64ths = (
-            num_cus, ctx_hint, attn_units, router_units, prefetch_bytes, pool_64ths)
+        p.num_cus, p.ctx_hint, p.attn_units, p.router_units, p.prefetch_bytes, p.pool_64ths, p.qkv_units = (
+            num_cus, ctx_hint, attn_units, router_units, prefetch_bytes, pool_64ths, qkv_units)
         ws = ctypes.c_size_t()
         check(lib().mk_build_schedule(self.h, ctypes.byref(p), ctypes.byref(ws)), "mk_build_schedule")
         return ws.value

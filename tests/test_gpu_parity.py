@@ -131,6 +131,14 @@ def test_mid_shared_gateup_pool(pool):
     _check(parity.run(w, mode="isolated", log=_log, pool_64ths=pool))
 
 
+def test_mid_dedicated_qkv_units():
+    """60 stage-1 units take only the Wqkv rows; the others normalize in a PRE task with no rows and go
+    straight to the routing and their gate/up rows: same parity bar."""
+    from tests import parity
+    w = synth.Workload("mid_qkvu", synth.MID, batch=3, steps=3, context=[1500, 17, 600])
+    _check(parity.run(w, mode="isolated", log=_log, qkv_units=60))
+
+
 @pytest.mark.parametrize("attn_cus", [13, 40])
 def test_mid_attention_unit_counts(attn_cus):
     """Attention units forced to leads + 1 (one unit takes every Wo row and every chunk past a
