@@ -6,8 +6,10 @@
 // paragraph 2: tiles and attention splits assigned to compute units in
 // advance; aiweekly.co, paragraphs 2-3: fixed-size descriptors, a task waits
 // on one count) with its own layout: one queue per compute unit, per layer
-//   PRE (norm + Wqkv / router rows)  ->  ATTN or GATEUP  ->  OUT (Wo + down rows),
-// then LM head rows.  A counter is a set of sub-counters in separate lines;
+//   attention units:  ATTN (a chunk; leads merge)  ->  WO (Wo rows: the attention half)
+//   stage-1 units:    PRE (norm + Wqkv / router rows)  ->  GATEUP  ->  OUT (down rows: the expert half)
+// then LM head rows on every unit.  (Opt-in: pool tasks on the attention units
+// after their chunk; dedicated Wqkv units.)  A counter is a set of sub-counters in separate lines;
 // the task with slot s (its index among the counter's signallers) adds one to
 // sub-counter s mod 16, and a wait ends when they sum to epoch * fan-in, so
 // nothing is reset between steps.

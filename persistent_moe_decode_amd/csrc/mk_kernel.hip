@@ -13,8 +13,12 @@
 //           chunks once the others have reported (log-sum-exp combine);
 //   GATEUP  top-k of the router logits, then rows of the selected experts'
 //           gate and up projections and SwiGLU;
+//   WO      rows of Wo times the merged attention output: the attention half
+//           of the residual;
 //   OUT     rows of the selected experts' down projections, weighted expert
-//           sum and residual add (parallel block: x += attn + moe);
+//           sum added to the residual rows: the expert half (parallel block:
+//           the next layer's readers add the two halves, x + moe + attn);
+//   GUTAIL  (opt-in) gate/up rows claimed from the layer's shared pool;
 //   LMHEAD  final RMSNorm, rows of the LM head, greedy or sampled argmax
 //           (last arriver).
 // Weight rows stream from HBM with 128-bit loads; at batch 1 lanes accumulate
