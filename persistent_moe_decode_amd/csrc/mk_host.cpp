@@ -308,13 +308,25 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
   // Compute units 0 .. n_attn - 1 run the attention split and no stage-1
   // rows, so their K/V loads are in flight while the other units normalize
   // and project, and then the Wo rows; units n_attn .. ncu - 1 run the
-  // stage-1 rows, the selected experts' gate/up rows and the output rows.  n_attn follows the bytes attention streams per layer
-  // against the expert gate/up bytes (attention weighted 1.5x for its extra
-  // arithmetic); the split never changes results.
+  // stage-1 rows, the selected experts' gate/up rows and the output rows.
+  // A stage-1 unit streams weight rows about 2.25x as fast as an attention
+  // unit streams K/V pages, so a layer takes at least the longer of
+  //   the expert path:    (gate/up + down bytes) / (2.25 * (ncu - n_attn))
+  //   the attention path: QKV bytes / (2.25 * (ncu - n_attn)) + K/V bytes / n_attn
+  // (the attention of a layer waits for its QKV rows).  The first grows with
+  // n_attn; the second is least at n_attn / (ncu - n_attn) =
+  // sqrt(2.25 * K/V bytes / QKV bytes).  So n_attn is the smaller of the
+  // point where the expert path meets the attention chunks and that minimum:
+  // short contexts take the first, long single-sequence contexts the second.
+  // The split never changes results.
   const double hint = ctx_hint > 0 ? (double)ctx_hint : 4096.0;
-  const double attn_bytes = 1.5 * hint * B * f.n_kv_heads * f.head_dim * 4.0;
-  const double gu_bytes = (double)std::min(E, B * f.top_k) * 2.0 * f.inter * H * 2.0;
-  int n_attn = (int)std::lround(ncu * attn_bytes / (attn_bytes + gu_bytes));
+  const double kRate = 2.25;
+  const double kv_bytes = kRate * hint * B * f.n_kv_heads * f.head_dim * 4.0;
+  const double expert_bytes = (double)std::min(E, B * f.top_k) * 3.0 * f.inter * H * 2.0;
+  const double qkv_bytes = (double)qkv_rows * H * 2.0;
+  const double chain = std::sqrt(kv_bytes / qkv_bytes);
+  const double n_fit = std::min(ncu * kv_bytes / (kv_bytes + expert_bytes), ncu * chain / (1.0 + chain));
+  int n_attn = (int)std::lround(n_fit);
   if (p.attn_units > 0) n_attn = p.attn_units;
   // attention units 0 .. n_lead - 1 lead a (sequence, kv head) segment each:
   // first chunk and merge, no Wo rows; the others take the remaining chunks

@@ -331,6 +331,30 @@ def test_schedule_params_attn_units_and_clamping():
         assert c.validate() == c.info().n_tasks
 
 
+def test_default_split_follows_both_bounds():
+    """The default attention/stage-1 split on the 30B shape (256 units): at 8K and at batch 8 it sits where
+    the expert bytes meet the K/V bytes (gate/up + down at 2.25x the per-unit rate of K/V); at 256K it is
+    capped where the QKV-then-attention chain is shortest, n / (256 - n) = sqrt(2.25 K/V / QKV bytes).
+    Both bounds are written out here so a change of either formula shows."""
+    s = synth.MOE30B
+    qkv = (s.n_q_heads + 2 * s.n_kv_heads) * s.head_dim * s.hidden * 2.0
+    got = {}
+    for batch, hint in ((1, 8256), (8, 12780), (1, 262160)):
+        kv = 2.25 * hint * batch * s.n_kv_heads * s.head_dim * 4.0
+        ex = min(s.n_experts, batch * s.top_k) * 3.0 * s.inter * s.hidden * 2.0
+        balance = 256 * kv / (kv + ex)
+        r = np.sqrt(kv / qkv)
+        chain = 256 * r / (1 + r)
+        c = _ctx(s, batch, 4, 8)
+        c.build_schedule(256, hint)
+        got[(batch, hint)] = (c.info().n_attn, balance, chain)
+        assert c.info().n_attn == round(min(balance, chain))
+        assert c.validate() == c.info().n_tasks
+    assert got[(1, 8256)][0] == 86 and got[(1, 8256)][1] < got[(1, 8256)][2]
+    assert got[(8, 12780)][0] == 112 and got[(8, 12780)][1] < got[(8, 12780)][2]
+    assert got[(1, 262160)][0] == 226 and got[(1, 262160)][2] < got[(1, 262160)][1]
+
+
 def test_schedule_params_router_units():
     w, c = _mid_ctx()
     for nr in (1, 2, 7):
