@@ -90,8 +90,10 @@ int mk_create(const mk_config* cfg, mk_ctx** out);
  *    unit of the current device, which also sets the LDS capacity from the
  *    device; otherwise 160 KB is assumed and no GPU call is made).
  *  attn_units: compute units that run the attention split and the Wo rows
- *    (0 = from ctx_hint: attention's K/V bytes against the experts' gate/up
- *    bytes).  Clamped to [max_batch*n_kv_heads + 1, num_cus - 2].
+ *    (0 = from ctx_hint: the smaller of the split where attention's K/V
+ *    bytes meet the experts' gate/up/down bytes and the split where the QKV
+ *    rows plus the K/V reads take least time).  Clamped to
+ *    [max_batch*n_kv_heads + 1, num_cus - 2].
  *  router_units: stage-1 units that compute the router rows (0 = default).
  *    Clamped to [1, stage-1 units - 1].
  *  prefetch_bytes: upper bound on the LDS region that receives weight tiles
