@@ -294,18 +294,18 @@ DEV uint32_t counter_sum(const KArgs& a, int idx) {
 }
 
 // Wave 0 polls the counter (relaxed device-coherent loads of its
-// sub-counters, s_sleep between polls) until it reaches epoch * fanin; the
+// sub-counters, s_sleep between polls) until it sums to want (mod 2^32,
+// compared as a signed difference; a full wait is epoch * fanin); the
 // barrier hands the result to the other waves.  The wait is bounded: past
 // the spin limit the task raises MK_ERR_DEVICE_TIMEOUT and the grid drains.
 // The abort flag is read every 32 polls, not before the first one (that
 // would put a dependent round trip in front of every wait).  Returns false
 // when the grid is aborting or the wait timed out.
-DEV bool wait_counter_at(const KArgs& a, int idx, int fanin, int task, int32_t* slot, uint32_t epoch) {
+DEV bool wait_counter_until(const KArgs& a, int idx, uint32_t want, int task, int32_t* slot) {
   if (tid() < 64) {
     const int lane = tid();
     int ok = 1;
     if (idx >= 0) {
-      const uint32_t want = epoch * (uint32_t)fanin;
       const uint64_t t0 = wall_clock64();
       uint32_t it = 0;
       while ((int32_t)(counter_sum(a, idx) - want) < 0) {
@@ -328,8 +328,17 @@ DEV bool wait_counter_at(const KArgs& a, int idx, int fanin, int task, int32_t* 
   return *slot != 0;
 }
 
+DEV bool wait_counter_at(const KArgs& a, int idx, int fanin, int task, int32_t* slot, uint32_t epoch) {
+  return wait_counter_until(a, idx, epoch * (uint32_t)fanin, task, slot);
+}
+
 DEV bool wait_counter(const KArgs& a, int idx, int fanin, int task, int32_t* slot) {
   return wait_counter_at(a, idx, fanin, task, slot, a.epoch);
+}
+
+// Until need of this step's fanin signals of counter idx are in.
+DEV bool wait_counter_part(const KArgs& a, int idx, int fanin, int need, int task, int32_t* slot) {
+  return wait_counter_until(a, idx, (a.epoch - 1u) * (uint32_t)fanin + (uint32_t)need, task, slot);
 }
 
 // A workgroup barrier that orders LDS accesses only: each wave waits for its
@@ -1313,14 +1322,18 @@ DEV AttnMerge attn_merge_area(const Lds& s, int G, int d) {
   return r;
 }
 
-// This wave's pages of the chunk: its early blocks, already in registers
-// (waves 1..7: e0 = block wave - 1, e1 = block wave + 6, of [0, ne)), then
-// the LDS blocks [bl0, nblk) and HBM blocks [ne, bl0) congruent to the wave
-// mod 8, the HBM ones with the next page loaded while the current one is
-// processed.  Leaves (o, m, sum) per head in the merge area.
+// This wave's pages of the chunk: its early blocks, already in ring[0] and
+// ring[1] (waves 1..7: blocks wave - 1 and wave + 6, of [0, ne)), then the
+// LDS blocks [bl0, nblk) and HBM blocks [ne, bl0) congruent to the wave mod
+// 8.  The pages go through a ring of kAttnRing page registers: while page j
+// is processed, pages j + 1 .. j + kAttnDepth are being fetched (a long
+// chunk streams most of its pages from HBM this way).  Leaves (o, m, sum)
+// per head in the merge area.
+constexpr int kAttnDepth = 2, kAttnRing = kAttnDepth + 1;
+
 template <int D>
 DEV void attn_wave(const KArgs& a, const Lds& s, int qi, const uint16_t* q_s, int l, int b, int g, int t0, int t1,
-                   int ne, int bl0, int nl, const AttnPage<D>& e0, const AttnPage<D>& e1, const AttnMerge& mrg) {
+                   int ne, int bl0, int nl, AttnPage<D> (&ring)[kAttnRing], const AttnMerge& mrg) {
   const int lane = tid() & 63, wave = tid() >> 6, r = lane & 15, grp = lane >> 4;
   const int G = a.group;
   bf16x8_v qb[D / 32];
@@ -1335,9 +1348,8 @@ DEV void attn_wave(const KArgs& a, const Lds& s, int qi, const uint16_t* q_s, in
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) o[t] = float4_v{0.f, 0.f, 0.f, 0.f};
   // this wave's pages in order: its early blocks (registers), its LDS blocks,
-  // its HBM blocks; page j + 1 is fetched while page j is processed, and one
-  // call site processes them all (the code runs once per layer: fewer copies,
-  // fewer instruction fetches)
+  // its HBM blocks; one call site processes them all (the code runs once per
+  // layer: fewer copies, fewer instruction fetches)
   const int nblk = (t1 - t0 + 15) / 16;
   const int n_e = (wave >= 1 && wave - 1 < ne) + (wave >= 1 && wave + kWaves - 2 < ne);
   const int l0 = bl0 + (wave - bl0 % kWaves + kWaves) % kWaves;  // first LDS block of the wave
@@ -1345,22 +1357,28 @@ DEV void attn_wave(const KArgs& a, const Lds& s, int qi, const uint16_t* q_s, in
   const int h0 = ne + (wave - ne % kWaves + kWaves) % kWaves;    // first HBM block of the wave
   const int n_h = h0 < bl0 ? (bl0 - h0 + kWaves - 1) / kWaves : 0;
   const int total = n_e + n_l + n_h;
-  AttnPage<D> cur, nxt;
-  for (int j = -1; j < total; ++j) {
-    const int jn = j + 1;
-    if (jn < total) {
-      if (jn < n_e) {
-        nxt = jn == 0 ? e0 : e1;
-      } else if (jn < n_e + n_l) {
-        const int blk = l0 + kWaves * (jn - n_e);
-        attn_fetch_lds<D>(s, nxt, nl, blk - bl0, t0 + 16 * blk, t1);
-      } else {
-        const int blk = h0 + kWaves * (jn - n_e - n_l);
-        attn_fetch<D>(a, nxt, l, b, g, t0 + 16 * blk, t1, qi);
+  // pages [0, n_e) are in ring[0 .. n_e) already (n_e <= 2 <= kAttnDepth)
+  auto fetch = [&](int jn, AttnPage<D>& dst) {
+    if (jn < n_e + n_l) {
+      const int blk = l0 + kWaves * (jn - n_e);
+      attn_fetch_lds<D>(s, dst, nl, blk - bl0, t0 + 16 * blk, t1);
+    } else {
+      const int blk = h0 + kWaves * (jn - n_e - n_l);
+      attn_fetch<D>(a, dst, l, b, g, t0 + 16 * blk, t1, qi);
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < kAttnDepth; ++k)
+    if (k >= n_e && k < total) fetch(k, ring[k]);
+  for (int j0 = 0; j0 < total; j0 += kAttnRing) {
+#pragma unroll
+    for (int k = 0; k < kAttnRing; ++k) {
+      const int j = j0 + k;
+      if (j < total) {
+        if (j + kAttnDepth < total) fetch(j + kAttnDepth, ring[(k + kAttnDepth) % kAttnRing]);
+        attn_page<D>(ring[k], qb, scale, m, lsum, o);
       }
     }
-    if (j >= 0) attn_page<D>(cur, qb, scale, m, lsum, o);
-    cur = nxt;
   }
   // per-head totals over the 4 lane groups, then this wave's part of the merge area
   lsum = rows4_sum(lsum);
@@ -1508,9 +1526,9 @@ DEV void attn_task(const KArgs& a, const Task& t, const Lds& s, int qi) {
   const int ne = max(0, min(bl0 - (nl == 0 ? 1 : 0), 2 * (kWaves - 1)));
   attn_prefetch<D>(a, s, qi, l, b, g, t0, bl0, nl);
   const int wave = tid() >> 6;
-  AttnPage<D> e0, e1;
-  if (wave >= 1 && wave - 1 < ne) attn_fetch<D>(a, e0, l, b, g, t0 + 16 * (wave - 1), t1, qi);
-  if (wave >= 1 && wave + kWaves - 2 < ne) attn_fetch<D>(a, e1, l, b, g, t0 + 16 * (wave + kWaves - 2), t1, qi);
+  AttnPage<D> ring[kAttnRing];
+  if (wave >= 1 && wave - 1 < ne) attn_fetch<D>(a, ring[0], l, b, g, t0 + 16 * (wave - 1), t1, qi);
+  if (wave >= 1 && wave + kWaves - 2 < ne) attn_fetch<D>(a, ring[1], l, b, g, t0 + 16 * (wave + kWaves - 2), t1, qi);
   // the chunk holding position p writes the new token's K (rotated) and V, to
   // HBM and, when its block was copied, to the LDS copy as well
   const bool mine = t1 == p + 1;
@@ -1580,7 +1598,7 @@ DEV void attn_task(const KArgs& a, const Task& t, const Lds& s, int qi) {
 
   // positions of the chunk, 16 (one page) at a time, pages dealt to waves round robin
   const AttnMerge mrg = attn_merge_area(s, G, D);
-  attn_wave<D>(a, s, qi, q_s, l, b, g, t0, t1, ne, bl0, nl, e0, e1, mrg);
+  attn_wave<D>(a, s, qi, q_s, l, b, g, t0, t1, ne, bl0, nl, ring, mrg);
   mark(a, qi, 2);
   __syncthreads();
   // this chunk's partial: the waves' results merged, as [G][D] outputs, G maxima, G sums
@@ -1806,9 +1824,10 @@ struct JobDown {
 constexpr int kDownC = 6;
 constexpr int kDownGroups = 4;
 
-// Output tasks wait for their inputs themselves: the residual rows, the
-// top-k (from LDS, or computed once the router rows are done) and the first
-// down-projection rows are loaded before the gate/up results are waited for.
+// Output tasks wait for their inputs themselves: the residual rows and the
+// top-k (from LDS, or computed once the router rows are done) first; the
+// first down-projection rows once nine tenths of the gate/up tasks are in,
+// and the gate/up results after the last one.
 // have_tk: region B still holds this layer's top-k, left there by the gate/up
 // task that ran just before on this compute unit.  tk_layer: set to the layer
 // whose top-k region B holds when the task ends (-1: none).
@@ -1844,6 +1863,10 @@ TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have
   // waves 1..7 hold them (wave 0, whose thread 0 polls the flags, loads none)
   constexpr int kGroupRows = (kWaves - 1) * 4;
   const int npre = (a.I % 128 == 0 && cpl <= kDownC) ? min(nd, kDownGroups * kGroupRows) : 0;
+  // the down rows go out once nine tenths of the gate/up tasks are done: issued
+  // earlier, by the units that finish first, they take bandwidth from the last
+  // gate/up tasks, which every output task waits for
+  if (!wait_counter_part(a, t.wait[0], t.fanin[0], (t.fanin[0] * 9 + 9) / 10, qi, s.flags + 0)) return kWaves;
   const int lane = tid() & 63, wave = tid() >> 6, li = lane & 15;
   const int ig = wave >= 1 ? (wave - 1) * 4 + (lane >> 4) : kDownGroups * kGroupRows;  // row within a group
   uint4 dp[kDownGroups][kDownC];
