@@ -30,6 +30,14 @@ token's K/V are written to slot ``seq_len`` before attention runs over
 with ties to the lowest id; sampling at temperature T by the Gumbel-max rule
 with SplitMix64 noise keyed by (seed, position, batch slot, token id).
 
+FP8 weights (a model whose shape says ``weights="fp8"``): the pages list FP8
+weight streaming as a next step (aiweekly.co page, sixth paragraph) and fix no
+format.  The reading taken: the large streamed matrices (LM head, Wqkv, Wo,
+expert gate/up/down) are OCP E4M3 codes times one fp32 scale per output row;
+the weight value is decode(code) * scale, exactly, in float64, and every
+product then runs as with bfloat16 weights.  Router, norm gains and embedding
+stay bfloat16.
+
 Parity unpinned: the composed multi-layer logits have no closed form; they
 are pinned only through the pinned ops and the whole-step invariants in
 ``tests/test_oracle_pins.py``.  The ulp behaviour of exp/silu is covered only
@@ -50,6 +58,19 @@ import synth
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     """Exact value of bfloat16 bit patterns (uint16) as float64."""
     return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """Exact value of OCP E4M3 codes (uint8) as float64: sign bit 7, exponent bits 6..3 with bias
+    7, mantissa bits 2..0; exponent field 0 holds the subnormals m * 2^-9; 0x7F and 0xFF are NaN;
+    there are no infinities."""
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    mag = np.where((e == 0xF) & ((c & 7) == 7), np.nan, mag)
+    return sign * mag
 
 
 _BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
@@ -140,12 +161,18 @@ class Weights:
         self.used = 0
         self.cache: dict = {}
         self.source = source or (lambda kind, layer, expert: synth.weight_bits(shape, kind, layer, expert))
+        self.source_fp8 = lambda kind, layer, expert: synth.weight_fp8(shape, kind, layer, expert)
 
     def get(self, kind: int, layer: int = 0, expert: int | None = None) -> np.ndarray:
         key = (kind, layer, expert)
         w = self.cache.get(key)
         if w is None:
-            w = bf16_to_f64(self.source(kind, layer, expert))
+            if self.shape.quantized(kind):
+                # FP8 weights: each row's codes times the row's scale
+                codes, scales = self.source_fp8(kind, layer, expert)
+                w = e4m3_to_f64(codes) * scales.astype(np.float64).reshape(codes.shape[:-1] + (1,))
+            else:
+                w = bf16_to_f64(self.source(kind, layer, expert))
             if self.used + w.nbytes <= self.budget:
                 self.cache[key] = w
                 self.used += w.nbytes

@@ -22,7 +22,7 @@ import ctypes
 import math
 import os
 import subprocess
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 
 import numpy as np
 
@@ -83,6 +83,12 @@ def lib():
             f = getattr(L, name)
             f.restype = None
             f.argtypes = [u64, u64, u64, u64, ctypes.c_double, p]
+        L.synth_fp8_codes.restype = None
+        L.synth_fp8_codes.argtypes = [u64, u64, u64, u64, p]
+        L.synth_fp8_scales.restype = None
+        L.synth_fp8_scales.argtypes = [u64, u64, u64, u64, ctypes.c_double, ctypes.c_double, p]
+        L.synth_e4m3_rne.restype = ctypes.c_uint8
+        L.synth_e4m3_rne.argtypes = [ctypes.c_float]
         L.synth_uniform_u32.restype = None
         L.synth_uniform_u32.argtypes = [u64, u64, u64, u64, ctypes.c_uint32, p]
         L.synth_permutation.restype = None
@@ -187,6 +193,33 @@ def gain_bf16_np(seed: int, t: int, start: int, count: int, sigma: float) -> np.
     return _f32_to_bf16_np(np.float32(1.0) + s * normal_scale_np(sigma))
 
 
+def e4m3_rne_np(f: np.ndarray) -> np.ndarray:
+    """numpy mirror of the generator's E4M3 encoder (nearest code, ties to even, saturating)."""
+    f = np.asarray(f, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    sign = ((u >> np.uint64(24)) & np.uint64(0x80)).astype(np.uint8)
+    u = u & np.uint64(0x7FFFFFFF)
+    a = u.astype(np.uint32).view(np.float32)
+    sub = np.rint(a * np.float32(512.0)).astype(np.int64)
+    r = u + np.uint64(0x7FFFF) + ((u >> np.uint64(20)) & np.uint64(1))
+    e = (r >> np.uint64(23)).astype(np.int64) - 127
+    nrm = np.minimum(((e + 7) << 3) | ((r >> np.uint64(20)) & np.uint64(7)).astype(np.int64), 0x7E)
+    with np.errstate(invalid="ignore"):
+        code = np.where(~(a < np.float32(464.0)), 0x7E, np.where(a < np.float32(0.015625), sub, nrm))
+    return (code.astype(np.uint8) | sign).astype(np.uint8)
+
+
+def fp8_codes_np(seed: int, t: int, start: int, count: int) -> np.ndarray:
+    with np.errstate(over="ignore"):
+        s = _irwin_hall_np(words_np(seed, t, start, count)).astype(np.float32)
+    return e4m3_rne_np(s * normal_scale_np(32.0))
+
+
+def fp8_scales_np(seed: int, t: int, start: int, count: int) -> np.ndarray:
+    g = gain_bf16_np(seed, t, start, count, GAIN_SIGMA).astype(np.uint32) << np.uint32(16)
+    return np.float32(WEIGHT_SIGMA / 32.0) * g.view(np.float32)
+
+
 def uniform_u32_np(seed: int, t: int, start: int, count: int, n: int) -> np.ndarray:
     w = words_np(seed, t, start, count)
     hi = (w >> np.uint64(32))
@@ -222,6 +255,18 @@ class ModelShape:
     rope_theta: float = 1.0e4
     rms_eps: float = 1.0e-6
     page_size: int = 16
+    weights: str = "bf16"   # "bf16", or "fp8": the QUANT_KINDS matrices as E4M3 codes + fp32 row scales
+
+    def quantized(self, kind: int) -> bool:
+        return self.weights == "fp8" and kind in QUANT_KINDS
+
+    def weight_nbytes(self, kind: int) -> int:
+        """Bytes of one weight tensor as bound: bf16, or (quantized) codes then one fp32 scale per row."""
+        shp = self.weight_shape(kind)
+        n = int(np.prod(shp))
+        if self.quantized(kind):
+            return n + 4 * (n // shp[-1])
+        return 2 * n
 
     @property
     def qkv_rows(self) -> int:
@@ -243,14 +288,24 @@ class ModelShape:
         return self.n_layers * 2 * self.n_kv_heads * self.head_dim * 2
 
     def active_weight_bytes(self, distinct_experts_per_layer: float) -> float:
-        """Algorithmic weight bytes read by one decode step (one embedding row per token aside)."""
-        H, d = self.hidden, self.head_dim
-        per_layer = (H * self.qkv_rows + self.attn_dim * H + H * self.n_experts
-                     + distinct_experts_per_layer * 3 * H * self.inter + H)
-        return 2.0 * (self.n_layers * per_layer + self.vocab * H + H)
+        """Algorithmic weight bytes read by one decode step (one embedding row per token aside):
+        2 bytes per bf16 element; 1 per quantized element plus 4 per quantized row."""
+        H, I = self.hidden, self.inter
+        q = self.weights == "fp8"
+
+        def mat(rows: float, cols: int) -> float:
+            return rows * cols + 4.0 * rows if q else 2.0 * rows * cols
+
+        per_layer = (mat(self.qkv_rows, H) + mat(H, self.attn_dim) + 2.0 * H * self.n_experts
+                     + distinct_experts_per_layer * (2 * mat(I, H) + mat(H, I)) + 2.0 * H)
+        return self.n_layers * per_layer + mat(self.vocab, H) + 2.0 * H
 
 
 LAYER_KINDS = (K_ATTN_NORM, K_WQKV, K_WO, K_ROUTER, K_W_GATE, K_W_UP, K_W_DOWN)
+# matrices streamed as FP8 in an "fp8" model: every large weight stream; the router rows (which
+# decide the routing), the norm gains and the embedding rows stay bf16
+QUANT_KINDS = (K_LM_HEAD, K_WQKV, K_WO, K_W_GATE, K_W_UP, K_W_DOWN)
+FP8_SCALE_KIND = 64   # scale stream of kind k: tensor id tid(FP8_SCALE_KIND + k, index)
 GLOBAL_KINDS = (K_EMBED, K_LM_HEAD, K_FINAL_NORM)
 GAIN_KINDS = (K_ATTN_NORM, K_FINAL_NORM)
 
@@ -277,6 +332,39 @@ def weight_bits(shape: ModelShape, kind: int, layer: int = 0, expert: int | None
     else:
         a = normal_bf16(SEED_WEIGHTS, t, start, count, WEIGHT_SIGMA)
     return a.reshape(out_shape)
+
+
+def fp8_codes(seed: int, t: int, start: int, count: int, out: np.ndarray | None = None) -> np.ndarray:
+    """E4M3 codes (uint8) of elements ``start .. start+count-1`` of stream (seed, t)."""
+    if out is None:
+        out = np.empty(count, dtype=np.uint8)
+    lib().synth_fp8_codes(seed, t, start, count, _ptr(out))
+    return out
+
+
+def fp8_scales(seed: int, t: int, start: int, count: int) -> np.ndarray:
+    """fp32 row scales ``start .. start+count-1`` of stream (seed, t)."""
+    out = np.empty(count, dtype=np.float32)
+    lib().synth_fp8_scales(seed, t, start, count, WEIGHT_SIGMA, GAIN_SIGMA, _ptr(out))
+    return out
+
+
+def weight_fp8(shape: ModelShape, kind: int, layer: int = 0, expert: int | None = None):
+    """(codes uint8 [..][cols], scales float32 [rows]) of one quantized weight tensor (or one expert's
+    slice of it), generated from the recipe."""
+    assert shape.quantized(kind)
+    full = shape.weight_shape(kind)
+    index = layer if kind in LAYER_KINDS else 0
+    if expert is not None:
+        assert len(full) == 3
+        per = full[1] * full[2]
+        start, count, out_shape = expert * per, per, full[1:]
+    else:
+        start, count, out_shape = 0, int(np.prod(full)), full
+    cols = full[-1]
+    codes = fp8_codes(SEED_WEIGHTS, tid(kind, index), start, count).reshape(out_shape)
+    scales = fp8_scales(SEED_WEIGHTS, tid(FP8_SCALE_KIND + kind, index), start // cols, count // cols)
+    return codes, scales
 
 
 def kv_bits(shape: ModelShape, layer: int, which: str, seq: int, t0: int, t1: int) -> np.ndarray:
@@ -335,7 +423,13 @@ def ragged_lengths(batch: int, lo: int, hi: int) -> list:
 
 
 def workload(name: str) -> Workload:
-    """The five workloads: tiny, mid, moe30b_8k, moe30b_bs8_ragged, moe30b_256k."""
+    """The five workloads: tiny, mid, moe30b_8k, moe30b_bs8_ragged, moe30b_256k; a name ending in
+    ``_fp8`` is the same workload with the QUANT_KINDS matrices in FP8."""
+    if name.endswith("_fp8"):
+        w = workload(name[: -len("_fp8")])
+        w.name = name
+        w.shape = replace(w.shape, weights="fp8")
+        return w
     if name == "tiny":
         return Workload(name, TINY, batch=1, steps=16, context=[128], kv_mode="prefill", shuffle_pages=False)
     if name == "mid":

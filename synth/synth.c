@@ -22,6 +22,14 @@
  * Gains near one: v = bf16_rne( 1.0f + f32(s) * f32(sigma / SD) ).
  * Uniform integers in [0, n): Lemire multiply-shift on the high 32 bits.
  * Permutations: Fisher-Yates, swap partner for position i drawn from word(i).
+ *
+ * FP8 weights (8-bit floating point, OCP E4M3: 1 sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits, subnormals, no infinities, largest finite 448):
+ *     code = e4m3_rne( f32(s) * f32(32 / SD) )   (the same s; |value| < 111)
+ * the nearest code, ties to the even one.  Row scales:
+ *     scale = f32(sigma / 32) * f32(bf16_rne(1 + f32(s') * f32(0.02 / SD)))
+ * with s' from the scale stream of the tensor, so code * scale is a weight of
+ * about the same spread as the bf16 recipe's.
  */
 #include <math.h>
 #include <stdint.h>
@@ -111,5 +119,58 @@ void synth_permutation(uint64_t seed, uint64_t tid, uint32_t n, int32_t* out) {
     int32_t t = out[i];
     out[i] = out[j];
     out[j] = t;
+  }
+}
+
+/* The E4M3 code nearest to f, ties to the even code; |f| >= 464 saturates to
+ * the largest finite code (448).  Subnormal codes hold m * 2^-9, m = 1..7. */
+static inline uint8_t f32_to_e4m3_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  const uint8_t sign = (uint8_t)((u >> 24) & 0x80u);
+  u &= 0x7FFFFFFFu;
+  float a;
+  memcpy(&a, &u, 4);
+  uint8_t code;
+  if (!(a < 464.0f)) {
+    code = 0x7E;
+  } else if (a < 0.015625f) {
+    code = (uint8_t)nearbyintf(a * 512.0f); /* 0 .. 8; 8 is the smallest normal code */
+  } else {
+    u += 0x7FFFFu + ((u >> 20) & 1u); /* round the mantissa to 3 bits, ties to even */
+    const int e = (int)(u >> 23) - 127;
+    const uint32_t c = ((uint32_t)(e + 7) << 3) | ((u >> 20) & 7u);
+    code = (uint8_t)(c > 0x7Eu ? 0x7Eu : c);
+  }
+  return (uint8_t)(sign | code);
+}
+
+uint8_t synth_e4m3_rne(float f) { return f32_to_e4m3_rne(f); }
+
+/* out[j] = E4M3 code of the normal deviate at element start + j, spread 32. */
+void synth_fp8_codes(uint64_t seed, uint64_t tid, uint64_t start, uint64_t count, uint8_t* out) {
+  const uint64_t key = synth_key(seed, tid);
+  const float c = synth_normal_scale(32.0);
+  int64_t n = (int64_t)count;
+#pragma omp parallel for schedule(static) if (n > 262144)
+  for (int64_t j = 0; j < n; ++j) {
+    float s = (float)irwin_hall(word_at(key, start + (uint64_t)j));
+    out[j] = f32_to_e4m3_rne(s * c);
+  }
+}
+
+/* out[j] = row scale start + j: f32(sigma / 32) * (a gain near one, as bf16). */
+void synth_fp8_scales(uint64_t seed, uint64_t tid, uint64_t start, uint64_t count, double sigma,
+                      double gain_sigma, float* out) {
+  const uint64_t key = synth_key(seed, tid);
+  const float c = synth_normal_scale(gain_sigma);
+  const float base = (float)(sigma / 32.0);
+  for (uint64_t j = 0; j < count; ++j) {
+    float s = (float)irwin_hall(word_at(key, start + j));
+    uint16_t g = f32_to_bf16_rne(1.0f + s * c);
+    uint32_t gu = (uint32_t)g << 16;
+    float gf;
+    memcpy(&gf, &gu, 4);
+    out[j] = base * gf;
   }
 }

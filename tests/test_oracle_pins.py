@@ -536,3 +536,103 @@ def test_sampling_special_cases():
     n = np.arange(1000, dtype=np.uint64) + np.uint64((3 * 2 + 1) * 1000)
     u = ((O.splitmix64_at(7, n) >> np.uint64(11)).astype(np.float64) + 0.5) / 2.0 ** 53
     assert np.array_equal(g, -np.log(-np.log(u)))
+
+
+# ----------------------------------------------------------------------------
+# FP8 (E4M3) weights
+
+
+def test_e4m3_decode_matches_torch_for_every_code():
+    """The oracle's decoder, written from the format's definition, against torch's own
+    float8_e4m3fn conversion (an independent implementation) on all 256 codes."""
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.e4m3_to_f64(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_e4m3_decode_spec_values():
+    """Values fixed by the format: bias 7, 3 mantissa bits, subnormals m * 2^-9, largest 448."""
+    cases = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x30: 0.5, 0x38: 1.0,
+             0x39: 1.125, 0x40: 2.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+    for c, v in cases.items():
+        assert O.e4m3_to_f64(np.uint8(c)) == v, hex(c)
+    assert np.signbit(O.e4m3_to_f64(np.uint8(0x80))) and O.e4m3_to_f64(np.uint8(0x80)) == 0.0
+    finite = O.e4m3_to_f64(np.arange(256, dtype=np.uint8))
+    finite = finite[~np.isnan(finite)]
+    assert not np.any(np.isinf(finite)) and finite.max() == 448.0
+    # positive codes 0x00..0x7E are strictly increasing
+    pos = O.e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0)
+
+
+def _fp8(shape):
+    from dataclasses import replace
+    return replace(shape, weights="fp8")
+
+
+def test_fp8_weights_are_codes_times_row_scales():
+    """Weights.get of a quantized matrix = decode(code) * row scale, checked with torch's decoder in
+    float64 (the product of a 4-significant-bit value and an fp32 scale is exact there)."""
+    s = _fp8(synth.TINY)
+    W = O.Weights(s)
+    for kind, layer, expert in ((synth.K_WQKV, 1, None), (synth.K_W_DOWN, 0, 3), (synth.K_LM_HEAD, 0, None)):
+        codes, scales = synth.weight_fp8(s, kind, layer, expert)
+        dec = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64)
+        ref = (dec * torch.from_numpy(scales).to(torch.float64)[..., None]).numpy()
+        assert np.array_equal(W.get(kind, layer, expert), ref)
+    # one expert's slice is that expert's rows of the whole tensor
+    full = W.get(synth.K_W_GATE, 1)
+    assert np.array_equal(full[5], O.Weights(s).get(synth.K_W_GATE, 1, 5))
+    # router, gains and embedding stay bfloat16
+    assert np.array_equal(W.get(synth.K_ROUTER, 0), O.bf16_to_f64(synth.weight_bits(s, synth.K_ROUTER, 0)))
+    assert np.array_equal(W.get(synth.K_EMBED), O.bf16_to_f64(synth.weight_bits(s, synth.K_EMBED)))
+
+
+def test_fp8_step_is_the_bf16_step_on_the_dequantized_weights():
+    """The FP8 model changes nothing but the weight values: a step of it equals, bit for bit, a
+    step of the bf16-format model whose quantized matrices are replaced by their dequantized values
+    (computed here through torch's decoder)."""
+    sq = _fp8(synth.TINY)
+    Wq = O.Weights(sq)
+    Wb = O.Weights(synth.TINY)
+    for kind in synth.QUANT_KINDS:
+        layers = range(sq.n_layers) if kind in synth.LAYER_KINDS else [0]
+        for l in layers:
+            codes, scales = synth.weight_fp8(sq, kind, l)
+            dec = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64)
+            sc = torch.from_numpy(scales).to(torch.float64).reshape(codes.shape[:-1] + (1,))
+            Wb.cache[(kind, l, None)] = (dec * sc).numpy()
+            if kind in (synth.K_W_GATE, synth.K_W_UP, synth.K_W_DOWN):
+                for e in range(sq.n_experts):
+                    Wb.cache[(kind, l, e)] = Wb.cache[(kind, l, None)][e]
+    toks = [5, 77, 300]
+    outs = []
+    for W, s in ((Wq, sq), (Wb, synth.TINY)):
+        kv = O.PagedKV(s, 4)
+        pt = np.arange(4, dtype=np.int32)[None]
+        for t, tok in enumerate(toks):
+            out = O.decode_step(W, kv, [tok], pt, [t])
+        outs.append(out.logits)
+    assert np.array_equal(outs[0], outs[1])
+    # and it differs from the bf16 model's own step (the weights did change)
+    kv = O.PagedKV(synth.TINY, 4)
+    W0 = O.Weights(synth.TINY)
+    for t, tok in enumerate(toks):
+        out0 = O.decode_step(W0, kv, [tok], np.arange(4, dtype=np.int32)[None], [t])
+    assert not np.array_equal(out0.logits, outs[0])
+
+
+def test_fp8_step_bytes_30b_shape():
+    """Algorithmic bytes of the FP8 model: 1 byte per quantized weight plus 4 per quantized row."""
+    s = _fp8(synth.MOE30B)
+    H, I, E, V, L = s.hidden, s.inter, s.n_experts, s.vocab, s.n_layers
+    qkv, ad = s.qkv_rows, s.attn_dim
+    per_layer = (qkv * H + 4 * qkv) + (H * ad + 4 * H) + 2 * E * H + 8 * (2 * (I * H + 4 * I) + (H * I + 4 * H)) + 2 * H
+    want = L * per_layer + (V * H + 4 * V) + 2 * H
+    assert s.active_weight_bytes(8) == want
+    assert abs(want / synth.MOE30B.active_weight_bytes(8) - 0.5) < 0.01

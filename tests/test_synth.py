@@ -83,3 +83,58 @@ def test_workloads_page_tables():
         assert used.max() < w.num_pages
     r = synth.workload("moe30b_bs8_ragged")
     assert all(1024 <= c <= 32768 for c in r.context) and len(set(r.context)) > 1
+
+
+def test_fp8_codes_and_scales_c_equals_numpy():
+    for kind, idx, start, n in ((synth.K_WQKV, 0, 0, 70001), (synth.K_W_GATE, 5, 123457, 50000)):
+        t = synth.tid(kind, idx)
+        assert np.array_equal(synth.fp8_codes(0, t, start, n), synth.fp8_codes_np(0, t, start, n))
+        ts = synth.tid(synth.FP8_SCALE_KIND + kind, idx)
+        assert np.array_equal(synth.fp8_scales(0, ts, start, 999), synth.fp8_scales_np(0, ts, start, 999))
+
+
+def test_e4m3_encoder_picks_the_nearest_code_ties_to_even():
+    """Brute force over every finite code (decoded by torch): the encoder's code is nearest, and an
+    exact midpoint goes to the code with an even mantissa; beyond 464 it saturates to 448."""
+    import torch
+    codes = np.arange(0x7F, dtype=np.uint8)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    rng = np.random.default_rng(5)
+    mids = (vals[1:] + vals[:-1]) / 2
+    x = np.concatenate([rng.uniform(0, 470, 20000), rng.uniform(0, 0.03, 5000), mids,
+                        [0.0, 448.0, 463.99, 464.0, 1e4]]).astype(np.float32)
+    for sgn in (1.0, -1.0):
+        xs = (sgn * x).astype(np.float32)
+        got = synth.e4m3_rne_np(xs)
+        # the C encoder agrees with the mirror (on every midpoint and a sample of the rest)
+        pick = np.concatenate([np.arange(0, len(xs), 17), np.arange(25000, len(xs))])
+        assert np.array_equal(got[pick], np.array([synth.lib().synth_e4m3_rne(float(v)) for v in xs[pick]],
+                                                  dtype=np.uint8))
+        mag = np.abs(xs.astype(np.float64))
+        d = np.abs(mag[:, None] - vals[None, :])
+        best = d.min(1)
+        cand = d == best[:, None]
+        want = np.where(cand.sum(1) == 1, cand.argmax(1),
+                        np.where(cand & ((codes[None, :] & 1) == 0), codes[None, :], 255).min(1))
+        want = np.where(mag >= 464.0, 0x7E, want)
+        assert np.array_equal(got & 0x7F, want.astype(np.uint8))
+        assert np.all((got >> 7)[mag > 0] == (1 if sgn < 0 else 0))
+
+
+def test_fp8_weight_slices_and_workloads():
+    from dataclasses import replace
+    s = replace(synth.TINY, weights="fp8")
+    codes, scales = synth.weight_fp8(s, synth.K_W_DOWN, 1)
+    assert codes.shape == s.weight_shape(synth.K_W_DOWN) and codes.dtype == np.uint8
+    assert scales.shape == (s.n_experts * s.hidden,) and scales.dtype == np.float32
+    for e in (0, 5):
+        c, sc = synth.weight_fp8(s, synth.K_W_DOWN, 1, e)
+        assert np.array_equal(c, codes[e]) and np.array_equal(sc, scales[e * s.hidden:(e + 1) * s.hidden])
+    assert s.weight_nbytes(synth.K_W_DOWN) == codes.size + 4 * scales.size
+    assert s.weight_nbytes(synth.K_ROUTER) == 2 * s.n_experts * s.hidden
+    w = synth.workload("moe30b_8k_fp8")
+    assert w.shape.weights == "fp8" and w.context == [8192] and w.name == "moe30b_8k_fp8"
+    assert synth.workload("moe30b_8k").shape.weights == "bf16"
+    # codes never saturate and use both signs; scales sit near sigma / 32
+    assert (codes & 0x7F).max() < 0x7E and (codes >> 7).min() == 0 and (codes >> 7).max() == 1
+    assert np.all(np.abs(scales / (synth.WEIGHT_SIGMA / 32) - 1) < 0.2)
