@@ -32,7 +32,8 @@
  *    mk_bind_scratch.
  *  - "stream" = a hipStream_t passed as void*; NULL means the default stream.
  *    Work is enqueued asynchronously on it.
- *  - Matrices are row-major [out][in] bfloat16 (raw 16-bit patterns).
+ *  - Matrices are row-major [out][in] bfloat16 (raw 16-bit patterns), or, in
+ *    the FP8 weight format, E4M3 codes with per-row scales (mk_bind).
  */
 #ifndef MK_H
 #define MK_H
@@ -72,7 +73,16 @@ typedef struct mk_config {
   int32_t num_pages;          /* pages in each layer's K pool and V pool */
   float rms_eps;              /* RMSNorm epsilon (1e-6) */
   double rope_theta;          /* RoPE base (1e4) */
+  int32_t weight_format;      /* MK_WEIGHTS_BF16 (0) or MK_WEIGHTS_FP8_E4M3 (1), see mk_bind */
 } mk_config;
+
+/* Weight formats.  FP8_E4M3: the LM head, wqkv, wo, w_gate, w_up and w_down
+ * are OCP FP8 E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits, subnormals, no infinities) with one fp32 scale per row: the weight is
+ * code * scale.  The pages list FP8 weights as a next step (aiweekly.co,
+ * paragraph 6) and fix no format; per-row scales are this library's reading.
+ * Router, norm gains, embedding and the KV cache stay bfloat16. */
+enum { MK_WEIGHTS_BF16 = 0, MK_WEIGHTS_FP8_E4M3 = 1 };
 
 /* Creates a context for one model shape.  Host only, no GPU call.
  * cfg is copied.  *out receives the context (free with mk_destroy).
@@ -147,6 +157,10 @@ int mk_build_schedule(mk_ctx* ctx, const mk_schedule_params* params, size_t* wor
  *    wo [hidden][n_q*head_dim], router [n_experts][hidden],
  *    w_gate [n_experts][inter][hidden], w_up [n_experts][inter][hidden],
  *    w_down [n_experts][hidden][inter].
+ *    With weight_format MK_WEIGHTS_FP8_E4M3 each of lm_head, wqkv, wo,
+ *    w_gate, w_up and w_down is one buffer: the [rows][cols] E4M3 codes
+ *    (one byte each, same row order as above; an expert tensor's rows are
+ *    [n_experts * rows]) followed at byte rows*cols by rows fp32 row scales.
  *  k_pool: device, [n_layers][num_pages][n_kv_heads][page_size][head_dim] bf16.
  *  v_pool: device, [n_layers][num_pages][n_kv_heads][head_dim][page_size] bf16
  *    (dims-major inside a page, the layout the P*V matrix-core product reads).

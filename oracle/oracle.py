@@ -73,6 +73,15 @@ def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
     return sign * mag
 
 
+# the 256 values of the definition above, for decoding whole weight tensors by lookup
+_E4M3_VALUES = e4m3_to_f64(np.arange(256, dtype=np.uint8))
+
+
+def e4m3_lookup(codes: np.ndarray) -> np.ndarray:
+    """e4m3_to_f64 by a table of its 256 values (the same numbers, one gather per code)."""
+    return _E4M3_VALUES[np.asarray(codes, dtype=np.uint8)]
+
+
 _BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
 
 
@@ -170,7 +179,7 @@ class Weights:
             if self.shape.quantized(kind):
                 # FP8 weights: each row's codes times the row's scale
                 codes, scales = self.source_fp8(kind, layer, expert)
-                w = e4m3_to_f64(codes) * scales.astype(np.float64).reshape(codes.shape[:-1] + (1,))
+                w = e4m3_lookup(codes) * scales.astype(np.float64).reshape(codes.shape[:-1] + (1,))
             else:
                 w = bf16_to_f64(self.source(kind, layer, expert))
             if self.used + w.nbytes <= self.budget:

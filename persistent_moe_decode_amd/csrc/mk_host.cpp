@@ -29,6 +29,7 @@
 using namespace mk;
 
 extern "C" int mkk_launch_step(const KArgs* a, int grid, size_t lds_bytes, hipStream_t stream);
+extern "C" int mkk_launch_step_fp8(const KArgs* a, int grid, size_t lds_bytes, hipStream_t stream);
 extern "C" int mkk_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t stream);
 extern "C" size_t mkk_scratch_bytes();
 extern "C" int mkk_scratch(int* device, void** ptr);
@@ -97,6 +98,8 @@ static int check_config(const mk_config& c) {
   if (c.max_batch > kMaxBatch) return bad("max_batch > 8");
   if (!(c.rms_eps >= 0.f) || !(c.rope_theta > 0.0)) return fail(MK_ERR_INVALID_ARG, "bad rms_eps or rope_theta");
   if ((int64_t)c.max_pages_per_seq * c.page_size > (1 << 30)) return bad("context bound too large");
+  if (c.weight_format != MK_WEIGHTS_BF16 && c.weight_format != MK_WEIGHTS_FP8_E4M3)
+    return fail(MK_ERR_INVALID_ARG, "unknown weight_format");
   return MK_OK;
 }
 
@@ -881,7 +884,8 @@ extern "C" int mk_decode_steps(mk_ctx* c, int32_t n, int32_t steps, const int32_
   a.spin_limit_ticks = (uint64_t)c->spin_us * 100;  // s_memrealtime runs at 100 MHz
   a.inv_temp = c->inv_temp;
   a.seed = c->seed;
-  int r = mkk_launch_step(&a, c->ncu, c->lds_bytes, (hipStream_t)stream);
+  int r = c->cfg.weight_format == MK_WEIGHTS_FP8_E4M3 ? mkk_launch_step_fp8(&a, c->ncu, c->lds_bytes, (hipStream_t)stream)
+                                                      : mkk_launch_step(&a, c->ncu, c->lds_bytes, (hipStream_t)stream);
   if (r) return fail(MK_ERR_HIP, std::string("cooperative launch failed: ") + hipGetErrorString((hipError_t)r));
   c->epoch += (uint32_t)steps;
   return MK_OK;

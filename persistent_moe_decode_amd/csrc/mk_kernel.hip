@@ -24,6 +24,14 @@
 // Weight rows stream from HBM with 128-bit loads; at batch 1 lanes accumulate
 // in fp32 with v_dot2_f32_bf16 and groups of lanes reduce through DPP, at
 // batch >= 2 rows that every token uses run as 16-row matrix-core tiles.
+//
+// This file is compiled twice.  With MK_W8 = 0 it is the kernel for bf16
+// weights; with MK_W8 = 1 (mk_kernel_fp8.hip) the LM head, Wqkv, Wo and the
+// expert gate/up/down matrices are FP8 (OCP E4M3) codes with one fp32 scale
+// per row after each matrix's codes: the row loops convert the codes to bf16
+// in registers (exact: every E4M3 value is a bf16 value), accumulate as for
+// bf16 weights and multiply the row's sum by its scale.  Router, norm gains,
+// embedding and the KV cache stay bf16.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -36,6 +44,18 @@ using namespace mk;
 
 #define DEV __device__ __forceinline__
 #define TASK __device__ __forceinline__
+
+#ifndef MK_W8
+#define MK_W8 0
+#endif
+#if MK_W8
+#define MKK(name) name##_fp8
+#else
+#define MKK(name) name
+#endif
+// bytes per element of the streamed matrices (LM head, Wqkv, Wo, experts)
+constexpr bool kW8 = MK_W8 != 0;
+constexpr int kWB = kW8 ? 1 : 2;
 
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
 
@@ -130,6 +150,43 @@ DEV float dot8(const uint4& w, const uint4& x, float acc) {
   acc = dot2(w.z, x.z, acc);
   acc = dot2(w.w, x.w, acc);
   return acc;
+}
+
+#if MK_W8
+// Two E4M3 codes (bytes 0, 1, or with HI bytes 2, 3 of w) as a bf16 pair, exactly (scale 1).
+template <bool HI>
+DEV uint32_t fp8x2_bf16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+// 16 E4M3 codes (one 16-byte chunk) dotted with 16 bf16 inputs (xa: the first 8).
+DEV float dot16w(const uint4& w, const uint4& xa, const uint4& xb, float acc) {
+  acc = dot2(fp8x2_bf16<false>(w.x), xa.x, acc);
+  acc = dot2(fp8x2_bf16<true>(w.x), xa.y, acc);
+  acc = dot2(fp8x2_bf16<false>(w.y), xa.z, acc);
+  acc = dot2(fp8x2_bf16<true>(w.y), xa.w, acc);
+  acc = dot2(fp8x2_bf16<false>(w.z), xb.x, acc);
+  acc = dot2(fp8x2_bf16<true>(w.z), xb.y, acc);
+  acc = dot2(fp8x2_bf16<false>(w.w), xb.z, acc);
+  acc = dot2(fp8x2_bf16<true>(w.w), xb.w, acc);
+  return acc;
+}
+
+// The 8 bf16 values of codes 0..7 (lo) or 8..15 (hi) of a 16-byte chunk.
+DEV uint4 fp8x8_bf16(const uint4& w, bool hi) {
+  const uint32_t a = hi ? w.z : w.x, b = hi ? w.w : w.y;
+  return make_uint4(fp8x2_bf16<false>(a), fp8x2_bf16<true>(a), fp8x2_bf16<false>(b), fp8x2_bf16<true>(b));
+}
+#endif
+
+// One 16-byte weight chunk dotted with its inputs: 8 bf16 weights with x[0],
+// or (W8) 16 E4M3 codes with x[0], x[1].
+template <bool W8>
+DEV float dotw(const uint4& w, const uint4* x, float acc) {
+#if MK_W8
+  if constexpr (W8) return dot16w(w, x[0], x[1], acc);
+#endif
+  return dot8(w, x[0], acc);
 }
 
 // The thread's index, read through an empty volatile asm: the compiler then
@@ -412,6 +469,13 @@ DEV bool wait_ticket(const KArgs& a, uint32_t* ticket, uint32_t want, int task, 
 // inputs
 
 DEV const gu16* wptr(const KArgs& a, int i) { return (const gu16*)(uintptr_t)a.wtab[i]; }
+// a streamed matrix as bytes (bf16 elements, or FP8 codes followed by the rows' fp32 scales)
+typedef const AS_GLOBAL uint8_t gu8;
+DEV const gu8* wbytes(const KArgs& a, int i) { return (const gu8*)(uintptr_t)a.wtab[i]; }
+// row scales of an FP8 matrix of `rows` rows of `cols` codes
+DEV const AS_GLOBAL float* wscales(const KArgs& a, int i, size_t rows, int cols) {
+  return (const AS_GLOBAL float*)(wbytes(a, i) + rows * (size_t)cols);
+}
 
 // Trace mark k (0..3) of task qi: the clock when thread 0 passes this point.
 DEV void mark(const KArgs& a, int qi, int k) {
@@ -688,10 +752,18 @@ DEV void load_row(const Job& job, int i, int li, bool act, uint4 (&wv)[CPL]) {
   }
 }
 
-template <int LPR, int CPL, bool FromLds, class Job>
+// A row's sum times its FP8 scale (W8), or as it is (bf16 rows).
+template <bool W8, class Job>
+DEV float scaled(const Job& job, int i, float v) {
+  if constexpr (W8) return v * job.scale(i);
+  return v;
+}
+
+// W8: a 16-byte chunk holds 16 codes, so it meets two 16-byte input chunks.
+template <int LPR, int CPL, bool FromLds, bool W8, class Job>
 DEV void rowdots(int i0, int i1, int maxnx, const Job& job) {
   const int lane = tid() & 63, wave = tid() >> 6;
-  constexpr int RPW = 64 / LPR;
+  constexpr int RPW = 64 / LPR, XM = W8 ? 2 : 1;
   const int sub = lane / LPR, li = lane % LPR;
   for (int base = i0; base < i1; base += kWaves * RPW) {
     const int i = base + wave * RPW + sub;
@@ -702,38 +774,40 @@ DEV void rowdots(int i0, int i1, int maxnx, const Job& job) {
     const int nx = act ? job.nx(ic) : 0;
     for (int t = 0; t < maxnx; ++t) {
       const bool on = t < nx;
-      const uint4* xr = job.x(ic, on ? t : 0) + li;
+      const uint4* xr = job.x(ic, on ? t : 0) + XM * li;
       float acc = 0.f;
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) acc = dot8(wv[c], xr[LPR * c], acc);
+      for (int c = 0; c < CPL; ++c) acc = dotw<W8>(wv[c], xr + XM * LPR * c, acc);
       acc = group_sum<LPR>(acc);
-      if (on && li == 0) job.emit(i, t, acc);
+      if (on && li == 0) job.emit(i, t, scaled<W8>(job, i, acc));
     }
   }
 }
 
-// Any K that is a multiple of 128: 16 lanes per row, chunks of 8 per load batch.
-template <bool FromLds, class Job>
+// Any row of a multiple of 128 elements: 16 lanes per row (bf16) or 8 (W8),
+// one 16-byte chunk per lane per load.
+template <bool FromLds, bool W8, class Job>
 DEV void rowdots_generic(int K, int i0, int i1, int maxnx, const Job& job) {
+  constexpr int LPR = W8 ? 8 : 16, RPW = 64 / LPR, XM = W8 ? 2 : 1;
   const int lane = tid() & 63, wave = tid() >> 6;
-  const int sub = lane / 16, li = lane % 16;
-  const int cpl = K / 128;
-  for (int base = i0; base < i1; base += kWaves * 4) {
-    const int i = base + wave * 4 + sub;
+  const int sub = lane / LPR, li = lane % LPR;
+  const int cpl = K * (W8 ? 1 : 2) / (16 * LPR);
+  for (int base = i0; base < i1; base += kWaves * RPW) {
+    const int i = base + wave * RPW + sub;
     const bool act = i < i1;
     const int ic = act ? i : i0;
     const int nx = act ? job.nx(ic) : 0;
     for (int t = 0; t < maxnx; ++t) {
       const bool on = t < nx;
-      const uint4* xr = job.x(ic, on ? t : 0) + li;
+      const uint4* xr = job.x(ic, on ? t : 0) + XM * li;
       float acc = 0.f;
       for (int c = 0; c < cpl; ++c) {
         uint4 w[1];
-        load_row<FromLds, 1, 16>(job, ic, li + 16 * c, act, w);
-        acc = dot8(w[0], xr[16 * c], acc);
+        load_row<FromLds, 1, LPR>(job, ic, li + LPR * c, act, w);
+        acc = dotw<W8>(w[0], xr + XM * LPR * c, acc);
       }
-      acc = group_sum<16>(acc);
-      if (on && li == 0) job.emit(i, t, acc);
+      acc = group_sum<LPR>(acc);
+      if (on && li == 0) job.emit(i, t, scaled<W8>(job, i, acc));
     }
   }
 }
@@ -748,32 +822,48 @@ DEV void rowdots_generic(int K, int i0, int i1, int maxnx, const Job& job) {
 // stream from HBM, eight 16-byte loads per lane in flight per batch.  With
 // fewer tiles than waves the columns are split into kp parts whose partial
 // tiles are summed in LDS (red: kMfmaRedBytes of region C) in part order.
-constexpr int kMfmaBatch = 8;                   // 32-column blocks per load batch
+// W8: one 16-byte load holds columns 16 * (l / 16) .. + 15 of a 64-column
+// block, converted to bf16 and contracted as two products (the first and the
+// second 8 of those columns, with the inputs at the same columns): the sum
+// over the block is the same, only its order differs.
+constexpr int kMfmaBatch = 8;                   // 16-byte loads per lane per batch
 
-template <class Job>
+template <bool W8, class Job>
 DEV void rowdots_mfma(int K, int i0, int i1, int n, const Job& job, float* red) {
   typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  constexpr int CB = W8 ? 64 : 32;              // columns per 16-byte load of a 4-lane-group row
   const int lane = tid() & 63, wave = tid() >> 6;
   const int r = lane & 15, grp = lane >> 4;
   const int ntile = (i1 - i0 + 15) / 16;
   int kp = 1;
-  while (red && kp < 8 && ntile * kp < kWaves && (K / (2 * kp)) % (32 * kMfmaBatch) == 0) kp *= 2;
+  while (red && kp < 8 && ntile * kp < kWaves && (K / (2 * kp)) % (CB * kMfmaBatch) == 0) kp *= 2;
   const int kl = K / kp;                        // columns per part
   const int nitem = ntile * kp;
   const uint4* xb = job.x(i0, r < n ? r : 0);   // token r's input vector (LDS)
   for (int it = wave; it < nitem; it += kWaves) {
     const int tile = it / kp, part = it - tile * kp;
     const int row = i0 + tile * 16 + r;
-    const gu4* wr = job.row(row < i1 ? row : i0) + (size_t)part * (kl / 8) + grp;
-    const uint4* xr = xb + (size_t)part * (kl / 8) + grp;
+    const gu4* wr = job.row(row < i1 ? row : i0) + (size_t)part * (kl / (CB / 4)) + grp;
+    const uint4* xr = xb + (size_t)part * (kl / 8) + (W8 ? 2 : 1) * grp;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int kb = 0; kb < kl / 32; kb += kMfmaBatch) {
+    for (int kb = 0; kb < kl / CB; kb += kMfmaBatch) {
       uint4 wa[kMfmaBatch];
 #pragma unroll
       for (int u = 0; u < kMfmaBatch; ++u) wa[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(wr + 4 * (kb + u)));
 #pragma unroll
       for (int u = 0; u < kMfmaBatch; ++u) {
+#if MK_W8
+        if constexpr (W8) {
+          const uint4 xl = r < n ? xr[8 * (kb + u)] : make_uint4(0, 0, 0, 0);
+          const uint4 xh = r < n ? xr[8 * (kb + u) + 1] : make_uint4(0, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fp8x8_bf16(wa[u], false)),
+                                                        __builtin_bit_cast(bf16x8_t, xl), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fp8x8_bf16(wa[u], true)),
+                                                        __builtin_bit_cast(bf16x8_t, xh), acc, 0, 0, 0);
+          continue;
+        }
+#endif
         const uint4 xv = r < n ? xr[4 * (kb + u)] : make_uint4(0, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wa[u]),
                                                       __builtin_bit_cast(bf16x8_t, xv), acc, 0, 0, 0);
@@ -783,7 +873,7 @@ DEV void rowdots_mfma(int K, int i0, int i1, int n, const Job& job, float* red) 
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int rq = i0 + tile * 16 + 4 * grp + q;
-        if (rq < i1 && r < n) job.emit(rq, r, acc[q]);
+        if (rq < i1 && r < n) job.emit(rq, r, scaled<W8>(job, rq, acc[q]));
       }
     } else {
 #pragma unroll
@@ -797,53 +887,61 @@ DEV void rowdots_mfma(int K, int i0, int i1, int n, const Job& job, float* red) 
       const int rq = i0 + tile * 16 + rt;
       float v = 0.f;
       for (int part = 0; part < kp; ++part) v += red[(tile * kp + part) * 256 + rt * 16 + tok];
-      if (rq < i1 && tok < n) job.emit(rq, tok, v);
+      if (rq < i1 && tok < n) job.emit(rq, tok, scaled<W8>(job, rq, v));
     }
     __syncthreads();
   }
 }
 
-template <bool FromLds, class Job>
+// Rows [i0, i1) of a job with K-element rows; W8: the rows are FP8 codes.
+template <bool FromLds, bool W8, class Job>
 DEV void rowdots_range(int K, int i0, int i1, int maxnx, const Job& job) {
   const int nj = i1 - i0;
   if (nj <= 0 || maxnx <= 0) return;
   if constexpr (!FromLds && Job::kDense)
-    if (maxnx >= 2 && K % (32 * kMfmaBatch) == 0) return rowdots_mfma(K, i0, i1, maxnx, job, job.red);
-  const int ch = K / 8;  // 16-byte chunks per row
-  if (nj <= 8 && ch == 512) return rowdots<64, 8, FromLds>(i0, i1, maxnx, job);
-  if (nj <= 8 && ch == 256) return rowdots<64, 4, FromLds>(i0, i1, maxnx, job);
+    if (maxnx >= 2 && K % ((W8 ? 64 : 32) * kMfmaBatch) == 0) return rowdots_mfma<W8>(K, i0, i1, maxnx, job, job.red);
+  const int ch = K * (W8 ? 1 : 2) / 16;  // 16-byte chunks per row
+  if (nj <= 8 && ch == 512) return rowdots<64, 8, FromLds, W8>(i0, i1, maxnx, job);
+  if (nj <= 8 && ch == 256) return rowdots<64, 4, FromLds, W8>(i0, i1, maxnx, job);
   if (nj <= 16 || ch > 256) {
     switch (ch) {
-      case 64: return rowdots<32, 2, FromLds>(i0, i1, maxnx, job);
-      case 96: return rowdots<32, 3, FromLds>(i0, i1, maxnx, job);
-      case 128: return rowdots<32, 4, FromLds>(i0, i1, maxnx, job);
-      case 256: return rowdots<32, 8, FromLds>(i0, i1, maxnx, job);
-      case 512: return rowdots<32, 16, FromLds>(i0, i1, maxnx, job);
+      case 64: return rowdots<32, 2, FromLds, W8>(i0, i1, maxnx, job);
+      case 96: return rowdots<32, 3, FromLds, W8>(i0, i1, maxnx, job);
+      case 128: return rowdots<32, 4, FromLds, W8>(i0, i1, maxnx, job);
+      case 256: return rowdots<32, 8, FromLds, W8>(i0, i1, maxnx, job);
+      case 512: return rowdots<32, 16, FromLds, W8>(i0, i1, maxnx, job);
       default: break;
     }
   }
   switch (ch) {
-    case 16: return rowdots<16, 1, FromLds>(i0, i1, maxnx, job);
-    case 32: return rowdots<16, 2, FromLds>(i0, i1, maxnx, job);
-    case 64: return rowdots<16, 4, FromLds>(i0, i1, maxnx, job);
-    case 96: return rowdots<16, 6, FromLds>(i0, i1, maxnx, job);
-    case 128: return rowdots<16, 8, FromLds>(i0, i1, maxnx, job);
-    case 256: return rowdots<16, 16, FromLds>(i0, i1, maxnx, job);
-    default: return rowdots_generic<FromLds>(K, i0, i1, maxnx, job);
+    case 8:
+      if constexpr (W8) return rowdots<8, 1, FromLds, W8>(i0, i1, maxnx, job);
+      break;
+    case 16: return rowdots<16, 1, FromLds, W8>(i0, i1, maxnx, job);
+    case 32: return rowdots<16, 2, FromLds, W8>(i0, i1, maxnx, job);
+    case 48:
+      if constexpr (W8) return rowdots<16, 3, FromLds, W8>(i0, i1, maxnx, job);
+      break;
+    case 64: return rowdots<16, 4, FromLds, W8>(i0, i1, maxnx, job);
+    case 96: return rowdots<16, 6, FromLds, W8>(i0, i1, maxnx, job);
+    case 128: return rowdots<16, 8, FromLds, W8>(i0, i1, maxnx, job);
+    case 256: return rowdots<16, 16, FromLds, W8>(i0, i1, maxnx, job);
+    default: break;
   }
+  rowdots_generic<FromLds, W8>(K, i0, i1, maxnx, job);
 }
 
 // All rows of a job from HBM.
-template <class Job>
+template <bool W8, class Job>
 DEV void run_rowdots(int K, int njobs, int maxnx, const Job& job) {
-  rowdots_range<false>(K, 0, njobs, maxnx, job);
+  rowdots_range<false, W8>(K, 0, njobs, maxnx, job);
 }
 
 // Rows [0, npf) from the LDS tile, the rest from HBM.
-template <class Job>
+template <bool W8, class Job>
 DEV void run_rowdots_pf(int K, int njobs, int npf, int maxnx, const Job& job) {
-  rowdots_range<true>(K, 0, npf, maxnx, job);
-  rowdots_range<false>(K, npf, njobs, maxnx, job);
+  rowdots_range<true, W8>(K, 0, npf, maxnx, job);
+  rowdots_range<false, W8>(K, npf, njobs, maxnx, job);
 }
 
 // ---------------------------------------------------------------------------
@@ -1019,7 +1117,7 @@ DEV void write_sel(const KArgs& a, int layer, const TopK* tk) {
 // Each of waves 1..7 copies one contiguous run of 1 KB chunks: measured on
 // this part, that runs at about 2.5x the rate of dealing the chunks to the
 // waves round robin.
-DEV void prefetch_to_lds(const gu16* src, uint8_t* dst_lds, int nbytes) {
+DEV void prefetch_to_lds(const gu8* src, uint8_t* dst_lds, int nbytes) {
   const int lane = tid() & 63, wave = tid() >> 6;
   const AS_GLOBAL uint8_t* s8 = (const AS_GLOBAL uint8_t*)src;
   const int nchunk = (nbytes + 1023) >> 10;
@@ -1040,25 +1138,32 @@ DEV void prefetch_to_lds(const gu16* src, uint8_t* dst_lds, int nbytes) {
 // output task keeps only its expert contributions, below tile_off).  A PRE
 // task that follows an output task finds its tile already copied by it.
 // Returns the rows in LDS.
+// The first rows of a PRE task (Wqkv rows in the kernel's weight format,
+// router rows bf16): start and bytes per row.
+DEV const gu8* pre_rows_src(const KArgs& a, int layer, int r0, int* rowb) {
+  if (r0 < a.qkv_rows) {
+    *rowb = a.H * kWB;
+    return wbytes(a, widx(layer, WL_QKV)) + (size_t)r0 * *rowb;
+  }
+  *rowb = a.H * 2;
+  return wbytes(a, widx(layer, WL_ROUTER)) + (size_t)(r0 - a.qkv_rows) * *rowb;
+}
+
 DEV int task_prefetch(const KArgs& a, const Task& t, const Lds& s, int qi) {
-  const gu16* src;
-  int K, nrows;
+  const gu8* src;
+  int rowb, nrows = t.r1 - t.r0;
   if (t.op == OP_PRE) {
-    K = a.H;
-    nrows = t.r1 - t.r0;
-    src = t.r0 < a.qkv_rows ? wptr(a, widx(t.layer, WL_QKV)) + (size_t)t.r0 * K
-                            : wptr(a, widx(t.layer, WL_ROUTER)) + (size_t)(t.r0 - a.qkv_rows) * K;
+    src = pre_rows_src(a, t.layer, t.r0, &rowb);
   } else if (t.op == OP_WO) {
-    K = a.nq * a.d;
-    nrows = t.r1 - t.r0;
-    src = wptr(a, widx(t.layer, WL_O)) + (size_t)t.r0 * K;
+    rowb = a.nq * a.d * kWB;
+    src = wbytes(a, widx(t.layer, WL_O)) + (size_t)t.r0 * rowb;
   } else {
     return 0;
   }
   // (with several tokens the rows go to the matrix cores straight from HBM)
-  const int npf = a.n == 1 ? min(nrows, a.pf_wide / (K * 2)) : 0;
+  const int npf = a.n == 1 ? min(nrows, a.pf_wide / rowb) : 0;
   // flags[18] = layer + 1 of a PRE tile the preceding output task has already copied
-  if (npf > 0 && !(t.op == OP_PRE && s.flags[18] == t.layer + 1)) prefetch_to_lds(src, s.C + a.tile_off, npf * K * 2);
+  if (npf > 0 && !(t.op == OP_PRE && s.flags[18] == t.layer + 1)) prefetch_to_lds(src, s.C + a.tile_off, npf * rowb);
   return npf;
 }
 
@@ -1070,18 +1175,20 @@ DEV void prefetch_wait() {
 
 struct JobPre {
   static constexpr bool kDense = true;  // every row is dotted with every token
-  const gu16* W;
-  const AS_LDS uint16_t* pf;  // prefetched rows [0, npf)
-  float* red;                 // LDS for the matrix-core path's partial tiles (region C)
+  const gu8* W;                     // the matrix (bytes)
+  const AS_GLOBAL float* sc = nullptr;  // FP8 rows: the matrix's row scales
+  const AS_LDS uint8_t* pf;         // prefetched rows [0, npf)
+  float* red;                       // LDS for the matrix-core path's partial tiles (region C)
   int npf;
-  int r0, K;
+  int r0, K, rowb;                  // rowb: bytes per row (K * 2, or K for FP8 rows)
   const uint16_t* xs;
   float* out;  // [b][ld] + r0 already applied
   int ld;
   uint64_t* tag_out = nullptr;  // router rows: the same values as epoch-tagged words ([b][ld] + r0 applied)
   uint32_t epoch = 0;
-  DEV const gu4* row(int i) const { return (const gu4*)(W + (size_t)(r0 + i) * K); }
-  DEV const lu4* lrow(int i) const { return (const lu4*)(pf + i * K); }
+  DEV const gu4* row(int i) const { return (const gu4*)(W + (size_t)(r0 + i) * rowb); }
+  DEV const lu4* lrow(int i) const { return (const lu4*)(pf + (size_t)i * rowb); }
+  DEV float scale(int i) const { return sc[r0 + i]; }
   DEV int nx(int) const { return 1 << 30; }
   DEV const uint4* x(int, int t) const { return (const uint4*)(xs + (size_t)t * K); }
   DEV void emit(int i, int t, float v) const {
@@ -1099,23 +1206,28 @@ TASK void task_pre(const KArgs& a, const Task& t, const Lds& s, int qi, int npf)
   JobPre j;
   j.K = a.H;
   j.xs = xs;
-  j.pf = (const AS_LDS uint16_t*)(s.C + a.tile_off);
+  j.pf = (const AS_LDS uint8_t*)(s.C + a.tile_off);
   j.npf = npf;
   j.red = (float*)s.C;
   if (t.r0 < a.qkv_rows) {
-    j.W = wptr(a, widx(l, WL_QKV));
+    j.W = wbytes(a, widx(l, WL_QKV));
+    j.rowb = a.H * kWB;
+    if constexpr (kW8) j.sc = wscales(a, widx(l, WL_QKV), a.qkv_rows, a.H);
     j.r0 = t.r0;
     j.out = a.qkv + (size_t)l * a.max_batch * a.qkv_rows + t.r0;
     j.ld = a.qkv_rows;
   } else {
-    j.W = wptr(a, widx(l, WL_ROUTER));
+    j.W = wbytes(a, widx(l, WL_ROUTER));
+    j.rowb = a.H * 2;
     j.r0 = t.r0 - a.qkv_rows;
     j.out = a.rlog + (size_t)l * a.max_batch * a.E + j.r0;
     j.tag_out = a.rll + (size_t)l * a.max_batch * a.E + j.r0;
     j.epoch = a.epoch;
     j.ld = a.E;
   }
-  run_rowdots_pf(a.H, t.r1 - t.r0, npf, a.n, j);
+  // Wqkv rows in the kernel's weight format, router rows always bf16
+  if (t.r0 < a.qkv_rows) run_rowdots_pf<kW8>(a.H, t.r1 - t.r0, npf, a.n, j);
+  else run_rowdots_pf<false>(a.H, t.r1 - t.r0, npf, a.n, j);
   mark(a, qi, 2);
 }
 
@@ -1664,7 +1776,8 @@ struct JobGateUp {
   static constexpr bool kDense = false;  // rows see a varying token subset
   float* red = nullptr;
   const TopK* tk;
-  const gu16 *wg, *wu;
+  const gu8 *wg, *wu;                       // gate and up matrices (bytes)
+  const AS_GLOBAL float *sg = nullptr, *su = nullptr;  // FP8: their row scales
   const uint16_t* xs;
   float* gs;
   int64_t v0;
@@ -1677,7 +1790,12 @@ struct JobGateUp {
   DEV const gu4* row(int i) const {
     int r;
     const int u = urow(i, &r);
-    return (const gu4*)(((i & 1) ? wu : wg) + ((size_t)tk->U[u] * I + r) * H);
+    return (const gu4*)(((i & 1) ? wu : wg) + ((size_t)tk->U[u] * I + r) * H * kWB);
+  }
+  DEV float scale(int i) const {
+    int r;
+    const int u = urow(i, &r);
+    return ((i & 1) ? su : sg)[(size_t)tk->U[u] * I + r];
   }
   DEV int nx(int i) const {
     int r;
@@ -1702,8 +1820,12 @@ DEV void gateup_range(const KArgs& a, const Lds& s, int l, const uint16_t* xs, i
   const TopK* tk = s.tk;
   JobGateUp j;
   j.tk = tk;
-  j.wg = wptr(a, widx(l, WL_GATE));
-  j.wu = wptr(a, widx(l, WL_UP));
+  j.wg = wbytes(a, widx(l, WL_GATE));
+  j.wu = wbytes(a, widx(l, WL_UP));
+  if constexpr (kW8) {
+    j.sg = wscales(a, widx(l, WL_GATE), (size_t)a.E * a.I, a.H);
+    j.su = wscales(a, widx(l, WL_UP), (size_t)a.E * a.I, a.H);
+  }
   j.xs = xs;
   j.gs = (float*)s.C;
   j.H = a.H;
@@ -1715,7 +1837,7 @@ DEV void gateup_range(const KArgs& a, const Lds& s, int l, const uint16_t* xs, i
   for (int64_t v0 = va; v0 < vb; v0 += kGuPass) {
     const int nvr = (int)((vb - v0) < kGuPass ? (vb - v0) : kGuPass);
     j.v0 = v0;
-    run_rowdots(a.H, 2 * nvr, mt, j);
+    run_rowdots<kW8>(a.H, 2 * nvr, mt, j);
     __syncthreads();
     for (int e = tid(); e < nvr * mt; e += kThreads) {
       const int vi = e / mt, tt = e % mt;
@@ -1804,13 +1926,18 @@ struct JobDown {
   static constexpr bool kDense = false;  // rows see a varying token subset
   float* red = nullptr;
   const TopK* tk;
-  const gu16* W;
+  const gu8* W;                           // down matrices (bytes)
+  const AS_GLOBAL float* sc = nullptr;    // FP8: their row scales
   const uint16_t* hs;
   float* contrib;
   int r0, H, I, nU, maxBK;
   DEV const gu4* row(int i) const {
     const int rr = i / nU, u = i % nU;
-    return (const gu4*)(W + ((size_t)tk->U[u] * H + r0 + rr) * I);
+    return (const gu4*)(W + ((size_t)tk->U[u] * H + r0 + rr) * I * kWB);
+  }
+  DEV float scale(int i) const {
+    const int rr = i / nU, u = i % nU;
+    return sc[(size_t)tk->U[u] * H + r0 + rr];
   }
   DEV int nx(int i) const { return tk->ntok[i % nU]; }
   DEV const uint4* x(int i, int t) const { return (const uint4*)(hs + (size_t)tk->pair[i % nU][t] * I); }
@@ -1851,7 +1978,8 @@ TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have
   const TopK* tk = s.tk;
   JobDown jd;
   jd.tk = tk;
-  jd.W = wptr(a, widx(l, WL_DOWN));
+  jd.W = wbytes(a, widx(l, WL_DOWN));
+  if constexpr (kW8) jd.sc = wscales(a, widx(l, WL_DOWN), (size_t)a.E * a.H, a.I);
   jd.hs = xs;
   jd.contrib = contrib;
   jd.r0 = t.r0;
@@ -1859,10 +1987,11 @@ TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have
   jd.I = a.I;
   jd.nU = tk->nU;
   jd.maxBK = maxBK;
-  const int nd = nr * jd.nU, cpl = a.I / 128;
+  // 16-byte chunks per lane of a down row (16 lanes per row)
+  const int nd = nr * jd.nU, cpl = a.I * kWB / 256;
   // waves 1..7 hold them (wave 0, whose thread 0 polls the flags, loads none)
   constexpr int kGroupRows = (kWaves - 1) * 4;
-  const int npre = (a.I % 128 == 0 && cpl <= kDownC) ? min(nd, kDownGroups * kGroupRows) : 0;
+  const int npre = ((a.I * kWB) % 256 == 0 && cpl <= kDownC) ? min(nd, kDownGroups * kGroupRows) : 0;
   // the down rows go out once nine tenths of the gate/up tasks are done: issued
   // earlier, by the units that finish first, they take bandwidth from the last
   // gate/up tasks, which every output task waits for
@@ -1886,8 +2015,10 @@ TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have
   mark(a, qi, 0);
   // expert down projections: the register rows, then the rest from HBM
   const int mt = tk->maxtok;
-  if (cpl == kDownC) {
-    // every chunk present: a row's kDownC LDS reads go out together, then the
+  constexpr int XM = kW8 ? 2 : 1;                    // input chunks per weight chunk
+  constexpr int kDC = kW8 ? kDownC / 2 : kDownC;     // chunks per lane of a 768-element row
+  if (cpl == kDC) {
+    // every chunk present: a row's LDS reads go out together, then the
     // arithmetic (a guard per chunk would make each read wait for the last)
 #pragma unroll
     for (int g = 0; g < kDownGroups; ++g) {
@@ -1896,15 +2027,17 @@ TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have
       const int nx = act ? jd.nx(i) : 0;
       for (int tt = 0; tt < mt; ++tt) {
         const bool on = tt < nx;
-        const uint4* xr = jd.x(act ? i : 0, on ? tt : 0) + li;
-        uint4 xv[kDownC];
+        const uint4* xr = jd.x(act ? i : 0, on ? tt : 0) + XM * li;
+        uint4 xv[kDC * XM];
 #pragma unroll
-        for (int c = 0; c < kDownC; ++c) xv[c] = xr[16 * c];
+        for (int c = 0; c < kDC; ++c)
+#pragma unroll
+          for (int m = 0; m < XM; ++m) xv[XM * c + m] = xr[XM * 16 * c + m];
         float acc = 0.f;
 #pragma unroll
-        for (int c = 0; c < kDownC; ++c) acc = dot8(dp[g][c], xv[c], acc);
+        for (int c = 0; c < kDC; ++c) acc = dotw<kW8>(dp[g][c], xv + XM * c, acc);
         acc = group_sum<16>(acc);
-        if (on && li == 0) jd.emit(i, tt, acc);
+        if (on && li == 0) jd.emit(i, tt, scaled<kW8>(jd, i, acc));
       }
     }
   } else {
@@ -1915,17 +2048,17 @@ TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have
       const int nx = act ? jd.nx(i) : 0;
       for (int tt = 0; tt < mt; ++tt) {
         const bool on = tt < nx;
-        const uint4* xr = jd.x(act ? i : 0, on ? tt : 0) + li;
+        const uint4* xr = jd.x(act ? i : 0, on ? tt : 0) + XM * li;
         float acc = 0.f;
 #pragma unroll
         for (int c = 0; c < kDownC; ++c)
-          if (c < cpl) acc = dot8(dp[g][c], xr[16 * c], acc);
+          if (c < cpl) acc = dotw<kW8>(dp[g][c], xr + XM * 16 * c, acc);
         acc = group_sum<16>(acc);
-        if (on && li == 0) jd.emit(i, tt, acc);
+        if (on && li == 0) jd.emit(i, tt, scaled<kW8>(jd, i, acc));
       }
     }
   }
-  rowdots_range<false>(a.I, npre, nd, mt, jd);
+  rowdots_range<false, kW8>(a.I, npre, nd, mt, jd);
   mark(a, qi, 1);
   // batch 1, wave 0 alone storing the residual rows: meanwhile waves 1..7
   // copy the weight tile of the PRE task that follows on this unit into LDS
@@ -1933,10 +2066,10 @@ TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have
   // there instead of issuing it in front of its own wait
   const bool early = n == 1 && nr <= 64 && t.next_r1 > t.next_r0 && a.pf_wide > 0;
   if (early) {
-    const int npf = min(t.next_r1 - t.next_r0, a.pf_wide / (a.H * 2));
-    const gu16* src = t.next_r0 < a.qkv_rows ? wptr(a, widx(t.next_layer, WL_QKV)) + (size_t)t.next_r0 * a.H
-                                             : wptr(a, widx(t.next_layer, WL_ROUTER)) + (size_t)(t.next_r0 - a.qkv_rows) * a.H;
-    prefetch_to_lds(src, s.C + a.tile_off, npf * a.H * 2);
+    int rowb;
+    const gu8* src = pre_rows_src(a, t.next_layer, t.next_r0, &rowb);
+    const int npf = min(t.next_r1 - t.next_r0, a.pf_wide / rowb);
+    prefetch_to_lds(src, s.C + a.tile_off, npf * rowb);
     if (tid() == 0) s.flags[18] = t.next_layer + 1;
   }
   // the expert half of x_{l+1}: x_l + sum_j w_j y_j (the next layer adds the
@@ -1971,14 +2104,16 @@ constexpr int kWoC = 16;
 TASK void task_wo(const KArgs& a, const Task& t, const Lds& s, int qi, int npf) {
   const int l = t.layer, AD = a.nq * a.d, nr = t.r1 - t.r0, n = a.n;
   const int lane = tid() & 63, wave = tid() >> 6, li = lane & 31;
-  const int nreg = AD == 32 * kWoC * 8 && n == 1 ? min(nr - npf, (kWaves - 1) * 2) : 0;
+  constexpr int kWC = kW8 ? kWoC / 2 : kWoC;  // chunks per lane of a register row
+  const int rowb = AD * kWB;
+  const int nreg = rowb == 32 * kWC * 16 && n == 1 ? min(nr - npf, (kWaves - 1) * 2) : 0;
   const int ir = npf + (wave >= 1 ? (wave - 1) * 2 + (lane >> 5) : nreg);  // this lane's register row
   const bool act = ir < npf + nreg;
-  const gu16* W = wptr(a, widx(l, WL_O));
-  const gu4* wsrc = (const gu4*)(W + (size_t)(t.r0 + (act ? ir : 0)) * AD) + li;
-  uint4 wr[kWoC];
+  const gu8* W = wbytes(a, widx(l, WL_O));
+  const gu4* wsrc = (const gu4*)(W + (size_t)(t.r0 + (act ? ir : 0)) * rowb) + li;
+  uint4 wr[kWC];
 #pragma unroll
-  for (int c = 0; c < kWoC; ++c)
+  for (int c = 0; c < kWC; ++c)
     wr[c] = __builtin_bit_cast(uint4, act ? __builtin_nontemporal_load(wsrc + 32 * c) : u32x4_v{0, 0, 0, 0});
   if (!wait_counter(a, t.wait[0], t.fanin[0], qi, s.flags + 0)) return;
   if (a.trace && tid() == 0 && qi < a.trace_cap) a.trace[kTraceWords * (size_t)qi + 1] = wall_clock64();
@@ -1987,25 +2122,28 @@ TASK void task_wo(const KArgs& a, const Task& t, const Lds& s, int qi, int npf) 
   prefetch_wait();
   mark(a, qi, 0);
   JobPre j;
-  j.pf = (const AS_LDS uint16_t*)(s.C + a.tile_off);
+  j.pf = (const AS_LDS uint8_t*)(s.C + a.tile_off);
   j.npf = npf;
   j.red = (float*)s.C;
   j.W = W;
+  if constexpr (kW8) j.sc = wscales(a, widx(l, WL_O), a.H, AD);
   j.r0 = t.r0;
   j.K = AD;
+  j.rowb = rowb;
   j.xs = xs;
   j.out = a.wo_out + (size_t)l * a.max_batch * a.H + t.r0;
   j.ld = a.H;
-  rowdots_range<true>(AD, 0, npf, n, j);
+  rowdots_range<true, kW8>(AD, 0, npf, n, j);
+  constexpr int XM = kW8 ? 2 : 1;
   for (int b = 0; b < n; ++b) {
-    const uint4* xr = (const uint4*)(xs + (size_t)b * AD) + li;
+    const uint4* xr = (const uint4*)(xs + (size_t)b * AD) + XM * li;
     float acc = 0.f;
 #pragma unroll
-    for (int c = 0; c < kWoC; ++c) acc = dot8(wr[c], xr[32 * c], acc);
+    for (int c = 0; c < kWC; ++c) acc = dotw<kW8>(wr[c], xr + XM * 32 * c, acc);
     acc = group_sum<32>(acc);
-    if (act && li == 0) j.emit(ir, b, acc);
+    if (act && li == 0) j.emit(ir, b, scaled<kW8>(j, ir, acc));
   }
-  rowdots_range<false>(AD, npf + nreg, nr, n, j);
+  rowdots_range<false, kW8>(AD, npf + nreg, nr, n, j);
   mark(a, qi, 1);
 }
 
@@ -2015,12 +2153,14 @@ TASK void task_wo(const KArgs& a, const Task& t, const Lds& s, int qi, int npf) 
 struct JobLM {
   static constexpr bool kDense = true;
   float* red = nullptr;  // region C holds the logits for the argmax: no column split
-  const gu16* W;
+  const gu8* W;                           // the LM head (bytes)
+  const AS_GLOBAL float* sc = nullptr;    // FP8: its row scales
   int r0, K, V, maxB;
   const uint16_t* xs;
   float* lmv;
   float* logits;
-  DEV const gu4* row(int i) const { return (const gu4*)(W + (size_t)(r0 + i) * K); }
+  DEV const gu4* row(int i) const { return (const gu4*)(W + (size_t)(r0 + i) * K * kWB); }
+  DEV float scale(int i) const { return sc[r0 + i]; }
   DEV int nx(int) const { return 1 << 30; }
   DEV const uint4* x(int, int t) const { return (const uint4*)(xs + (size_t)t * K); }
   DEV void emit(int i, int t, float v) const {
@@ -2081,7 +2221,8 @@ TASK void task_lmhead(const KArgs& a, const Task& t, const Lds& s, int qi) {
   norm_inputs(a, L, wptr(a, W_FINAL_NORM), xs, s.red8, qi, -1, t.idx == 0 ? a.xr : nullptr);
   mark(a, qi, 0);
   JobLM j;
-  j.W = wptr(a, W_LM_HEAD);
+  j.W = wbytes(a, W_LM_HEAD);
+  if constexpr (kW8) j.sc = wscales(a, W_LM_HEAD, a.V, a.H);
   j.K = a.H;
   j.V = a.V;
   j.maxB = a.max_batch;
@@ -2100,7 +2241,7 @@ TASK void task_lmhead(const KArgs& a, const Task& t, const Lds& s, int qi) {
   for (int p0 = 0; p0 < nr; p0 += kLmPass) {
     const int np = min(kLmPass, nr - p0);
     j.r0 = t.r0 + p0;
-    run_rowdots(a.H, np, a.n, j);
+    run_rowdots<kW8>(a.H, np, a.n, j);
     __syncthreads();
 #pragma unroll
     for (int b = 0; b < kMaxBatch; ++b) {
@@ -2147,7 +2288,7 @@ TASK void task_lmhead(const KArgs& a, const Task& t, const Lds& s, int qi) {
 // tags) and positions seq_lens + s; its layer-0 tasks wait for step s - 1's
 // LM head (the greedy token).  Every queue ends with its LM head task, so a
 // queue starts step s + 1 only after its share of step s.
-extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a0) {
+extern "C" __global__ void __launch_bounds__(kThreads, 1) MKK(mk_megakernel)(KArgs a0) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
   KArgs a = a0;
   const Lds s = carve(lds_raw, a);
@@ -2208,6 +2349,8 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) mk_megakernel(KArgs a0
   }
 }
 
+#if !MK_W8
+// One copy of what follows (not per weight format): the fill kernel and the static workspace.
 __global__ void mk_fill_u32_kernel(uint32_t* p, uint32_t v, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + tid(); i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
@@ -2251,16 +2394,17 @@ extern "C" int mkk_scratch(int* device, void** ptr) {
   *ptr = addr[dev];
   return 0;
 }
+#endif  // !MK_W8
 
-extern "C" int mkk_launch_step(const KArgs* a, int grid, size_t lds_bytes, hipStream_t stream) {
+extern "C" int MKK(mkk_launch_step)(const KArgs* a, int grid, size_t lds_bytes, hipStream_t stream) {
   static size_t attr_bytes = 0;
   if (lds_bytes > attr_bytes) {
-    hipError_t e = hipFuncSetAttribute((const void*)mk_megakernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+    hipError_t e = hipFuncSetAttribute((const void*)MKK(mk_megakernel), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
     if (e != hipSuccess) return (int)e;
     attr_bytes = lds_bytes;
   }
   KArgs copy = *a;
   void* args[] = {&copy};
-  return (int)hipLaunchCooperativeKernel((const void*)mk_megakernel, dim3(grid), dim3(kThreads), args,
+  return (int)hipLaunchCooperativeKernel((const void*)MKK(mk_megakernel), dim3(grid), dim3(kThreads), args,
                                          (unsigned)lds_bytes, stream);
 }

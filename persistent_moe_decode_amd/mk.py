@@ -40,6 +40,7 @@ class MkConfig(ctypes.Structure):
         ("top_k", ctypes.c_int32), ("inter", ctypes.c_int32), ("vocab", ctypes.c_int32),
         ("page_size", ctypes.c_int32), ("max_batch", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
         ("num_pages", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_double),
+        ("weight_format", ctypes.c_int32),
     ]
 
 
@@ -144,10 +145,14 @@ def _i32p(arr):
     return arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
 
 
+WEIGHT_FORMATS = {"bf16": 0, "fp8": 1}   # MK_WEIGHTS_BF16, MK_WEIGHTS_FP8_E4M3
+
+
 def config_from_shape(shape, max_batch: int, max_pages_per_seq: int, num_pages: int) -> MkConfig:
     return MkConfig(shape.n_layers, shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
                     shape.n_experts, shape.top_k, shape.inter, shape.vocab, shape.page_size, max_batch,
-                    max_pages_per_seq, num_pages, shape.rms_eps, shape.rope_theta)
+                    max_pages_per_seq, num_pages, shape.rms_eps, shape.rope_theta,
+                    WEIGHT_FORMATS[getattr(shape, "weights", "bf16")])
 
 
 class Context:

@@ -20,23 +20,25 @@ POISON = 0x7FC0  # bfloat16 NaN: unwritten KV slots poison any stray read
 class _Stager:
     """Double-buffered pinned host staging for host-generated data."""
 
-    def __init__(self, elems: int = 1 << 25):
-        self.elems = elems
-        self.bufs = [torch.empty(elems, dtype=torch.int16, pin_memory=True) for _ in range(2)]
+    def __init__(self, nbytes: int = 1 << 26):
+        self.nbytes = nbytes
+        self.bufs = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
         self.events = [None, None]
         self.k = 0
 
-    def fill(self, dst_flat: torch.Tensor, gen) -> None:
-        """dst_flat (int16 view, on device) <- gen(start, count, host_ptr) chunk by chunk."""
-        n = dst_flat.numel()
-        for start in range(0, n, self.elems):
-            cnt = min(self.elems, n - start)
+    def fill(self, dst_flat: torch.Tensor, gen, esize: int = 2) -> None:
+        """dst_flat (uint8 view, on device) <- gen(start, count, host_ptr) in elements of esize bytes,
+        chunk by chunk."""
+        n = dst_flat.numel() // esize
+        per = self.nbytes // esize
+        for start in range(0, n, per):
+            cnt = min(per, n - start)
             k = self.k
             if self.events[k] is not None:
                 self.events[k].synchronize()
             buf = self.bufs[k]
             gen(start, cnt, buf.data_ptr())
-            dst_flat[start:start + cnt].copy_(buf[:cnt], non_blocking=True)
+            dst_flat[start * esize:(start + cnt) * esize].copy_(buf[:cnt * esize], non_blocking=True)
             ev = torch.cuda.Event()
             ev.record()
             self.events[k] = ev
@@ -54,6 +56,12 @@ def _kind_gen(kind: int, layer: int):
     if kind in synth.GAIN_KINDS:
         return lambda s, c, p: lib.synth_gain_bf16(synth.SEED_WEIGHTS, t, s, c, synth.GAIN_SIGMA, p)
     return lambda s, c, p: lib.synth_normal_bf16(synth.SEED_WEIGHTS, t, s, c, synth.WEIGHT_SIGMA, p)
+
+
+def _fp8_gen(kind: int, layer: int):
+    t = synth.tid(kind, layer if kind in synth.LAYER_KINDS else 0)
+    lib = synth.lib()
+    return lambda s, c, p: lib.synth_fp8_codes(synth.SEED_WEIGHTS, t, s, c, p)
 
 
 class DeviceDecoder:
@@ -84,8 +92,19 @@ class DeviceDecoder:
             order = list(synth.GLOBAL_KINDS) + [(k, l) for l in range(s.n_layers) for k in synth.LAYER_KINDS]
             for item in order:
                 kind, layer = (item, 0) if isinstance(item, int) else item
-                t = torch.empty(s.weight_shape(kind), dtype=torch.bfloat16, device=self.dev)
-                stager.fill(t.view(torch.int16).view(-1), _kind_gen(kind, layer))
+                if s.quantized(kind):
+                    # FP8: the E4M3 codes, then one fp32 scale per row, in one buffer
+                    shp = s.weight_shape(kind)
+                    ncode = int(np.prod(shp))
+                    t = torch.empty(s.weight_nbytes(kind), dtype=torch.uint8, device=self.dev)
+                    stager.fill(t[:ncode], _fp8_gen(kind, layer), esize=1)
+                    idx = layer if kind in synth.LAYER_KINDS else 0
+                    sc = synth.fp8_scales(synth.SEED_WEIGHTS, synth.tid(synth.FP8_SCALE_KIND + kind, idx), 0,
+                                          ncode // shp[-1])
+                    t[ncode:].copy_(torch.from_numpy(sc.view(np.uint8)))
+                else:
+                    t = torch.empty(s.weight_shape(kind), dtype=torch.bfloat16, device=self.dev)
+                    stager.fill(t.view(torch.uint8).view(-1), _kind_gen(kind, layer))
                 self.weights.append(t)
             stager.sync()
             self.stager = stager

@@ -555,6 +555,12 @@ def test_e4m3_decode_matches_torch_for_every_code():
     assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
 
 
+def test_e4m3_lookup_is_the_decoder():
+    codes = np.random.default_rng(3).integers(0, 256, size=(37, 129), dtype=np.uint8)
+    a, b = O.e4m3_lookup(codes), O.e4m3_to_f64(codes)
+    assert np.array_equal(np.isnan(a), np.isnan(b)) and np.array_equal(a[~np.isnan(a)], b[~np.isnan(b)])
+
+
 def test_e4m3_decode_spec_values():
     """Values fixed by the format: bias 7, 3 mantissa bits, subnormals m * 2^-9, largest 448."""
     cases = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x30: 0.5, 0x38: 1.0,
