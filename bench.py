@@ -343,8 +343,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic: seeded random-init weights N(0, 0.02), synthetic N(0, 1) KV, shuffled pages",
+        "dtype": "fp8-e4m3 weights, bf16 activations" if s.weights == "fp8" else "bf16",
+        "data": ("synthetic: seeded random-init weights " +
+                 ("as E4M3 codes (N(0, 32) rounded) times row scales near 0.02/32, " if s.weights == "fp8"
+                  else "N(0, 0.02), ") + "synthetic N(0, 1) KV, shuffled pages"),
         "config": {
             "workload": f"{w.name}: {s.n_layers} layers, hidden {s.hidden}, {s.n_q_heads}q/{s.n_kv_heads}kv x "
                         f"{s.head_dim}, {s.n_experts} experts top-{s.top_k} inter {s.inter}, vocab {s.vocab}; "
@@ -363,7 +365,7 @@ def main():
             "algorithmic_bytes_per_launch": round(bytes_step * spl),
             "launch_ms": round(launch_ms, 4),
             "steps_per_launch": spl,
-            "kernel": "mk_megakernel",
+            "kernel": "mk_megakernel_fp8" if s.weights == "fp8" else "mk_megakernel",
         },
         "cpu_baseline": cpu,
     }

@@ -353,6 +353,14 @@ def test_default_split_follows_both_bounds():
     assert got[(1, 8256)][0] == 86 and got[(1, 8256)][1] < got[(1, 8256)][2]
     assert got[(8, 12780)][0] == 112 and got[(8, 12780)][1] < got[(8, 12780)][2]
     assert got[(1, 262160)][0] == 226 and got[(1, 262160)][2] < got[(1, 262160)][1]
+    # FP8 weights at batch 1: streamed-matrix rows count 1.5 bytes per element (measured cost), so
+    # more units go to attention at 8K; at batch 8 the bf16 split
+    from dataclasses import replace
+    sq = replace(s, weights="fp8")
+    for batch, hint, want in ((1, 8256, 103), (8, 12780, 112), (1, 262160, 230)):
+        c = _ctx(sq, batch, 4, 8)
+        c.build_schedule(256, hint)
+        assert c.info().n_attn == want, (batch, hint, c.info().n_attn)
 
 
 def test_schedule_params_router_units():
