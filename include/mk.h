@@ -246,6 +246,27 @@ int mk_decode_step(mk_ctx* ctx, int32_t n, const int32_t* d_tokens, const int32_
 int mk_decode_steps(mk_ctx* ctx, int32_t n, int32_t steps, const int32_t* d_tokens, const int32_t* d_page_table,
                     const int32_t* d_seq_lens, float* d_logits, int32_t* d_next_tokens, void* stream);
 
+/* One step whose batch entries may belong to the same sequence: chunked
+ * prefill mixed with decode.  Arguments as mk_decode_step; each entry b is
+ * one token at position seq_lens[b] of the sequence its page-table row
+ * names.  Entries of one sequence give it the same row and distinct
+ * positions (a chunk of its prompt, say positions p .. p + k - 1 in k
+ * entries); entries of other sequences decode as usual in the same launch.
+ * Every entry's new K/V is written before any entry's attention reads the
+ * pages, and entry b attends over positions 0..seq_lens[b] of its row, so a
+ * chunk entry sees the earlier tokens of its chunk: the result equals running
+ * the entries one at a time, in order of position within each sequence, as
+ * single-token decode steps.  Every position below seq_lens[b] must hold K/V
+ * (written before, or by an entry of this step).  Logits and next tokens are
+ * written for every entry (a prefill chunk's last entry gives the first
+ * generated token).  This step reads no K/V page before its waits, so it is
+ * slower per token than mk_decode_step.  Errors: as mk_decode_step.
+ * Source: the pages list prefill running apart from decode, which it pauses,
+ * as a limit of the engine and mixed prefill and decode as what to watch next
+ * (ainews.surl.tw, paragraph 4; aiweekly.co, paragraph 6). */
+int mk_mixed_step(mk_ctx* ctx, int32_t n, const int32_t* d_tokens, const int32_t* d_page_table,
+                  const int32_t* d_seq_lens, float* d_logits, int32_t* d_next_tokens, void* stream);
+
 /* Synchronizes `stream`, reads the sticky device error word and clears it.
  * *code receives 0 or an MK_ERR_DEVICE_* code; *cu and *task (may be NULL)
  * the workgroup and task that raised it.  After a device error the context

@@ -462,9 +462,21 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
       }
       // stage 2: attention units run their chunk, the others gate/up rows
       if (q < n_attn) {
+        if (q < n_lead) {
+          // the new K/V of lead q's (sequence, kv head): written here in mixed steps (the kernel
+          // waits for the QKV rows only then), signalled in every step so the counter's targets hold
+          Task k = make_task(OP_KVW, l);
+          k.wait[0] = ctr_index(l, C_QKV);
+          k.fanin[0] = n_qkv_tasks[l];
+          k.idx = q;
+          k.signal = ctr_index(l, C_KVW);
+          c->tasks.push_back(k);
+        }
         Task t = make_task(OP_ATTN, l);
         t.wait[0] = ctr_index(l, C_QKV);
         t.fanin[0] = n_qkv_tasks[l];
+        t.wait[1] = ctr_index(l, C_KVW);  // waited in mixed steps only
+        t.fanin[1] = n_lead;
         t.idx = q;
         t.count = n_attn;
         // leads signal once their segment is merged; the other chunks report
@@ -805,9 +817,9 @@ extern "C" int mk_bind_scratch(mk_ctx* c, const void* const* weights, int32_t n_
   return bind_workspace(c, weights, n_weights, k_pool, v_pool, (uint8_t*)p, (hipStream_t)stream);
 }
 
-extern "C" int mk_decode_steps(mk_ctx* c, int32_t n, int32_t steps, const int32_t* d_tokens,
-                               const int32_t* d_page_table, const int32_t* d_seq_lens, float* d_logits,
-                               int32_t* d_next_tokens, void* stream) {
+static int launch_steps(mk_ctx* c, int32_t n, int32_t steps, const int32_t* d_tokens,
+                        const int32_t* d_page_table, const int32_t* d_seq_lens, float* d_logits,
+                        int32_t* d_next_tokens, void* stream, int32_t kv_sync) {
   if (!c) return fail(MK_ERR_INVALID_ARG, "null context");
   if (!c->bound) return fail(MK_ERR_STATE, "context not bound");
   if (scratch_lost(c)) return fail(MK_ERR_STATE, "the static workspace was bound to another context since");
@@ -880,6 +892,7 @@ extern "C" int mk_decode_steps(mk_ctx* c, int32_t n, int32_t steps, const int32_
   a.v_pool = c->vpool;
   a.n = n;
   a.nsteps = steps;
+  a.kv_sync = kv_sync;
   a.step = 0;
   a.epoch = c->epoch + 1;
   a.tokens = d_tokens;
@@ -897,9 +910,20 @@ extern "C" int mk_decode_steps(mk_ctx* c, int32_t n, int32_t steps, const int32_
   return MK_OK;
 }
 
+extern "C" int mk_decode_steps(mk_ctx* c, int32_t n, int32_t steps, const int32_t* d_tokens,
+                               const int32_t* d_page_table, const int32_t* d_seq_lens, float* d_logits,
+                               int32_t* d_next_tokens, void* stream) {
+  return launch_steps(c, n, steps, d_tokens, d_page_table, d_seq_lens, d_logits, d_next_tokens, stream, 0);
+}
+
 extern "C" int mk_decode_step(mk_ctx* c, int32_t n, const int32_t* d_tokens, const int32_t* d_page_table,
                               const int32_t* d_seq_lens, float* d_logits, int32_t* d_next_tokens, void* stream) {
-  return mk_decode_steps(c, n, 1, d_tokens, d_page_table, d_seq_lens, d_logits, d_next_tokens, stream);
+  return launch_steps(c, n, 1, d_tokens, d_page_table, d_seq_lens, d_logits, d_next_tokens, stream, 0);
+}
+
+extern "C" int mk_mixed_step(mk_ctx* c, int32_t n, const int32_t* d_tokens, const int32_t* d_page_table,
+                             const int32_t* d_seq_lens, float* d_logits, int32_t* d_next_tokens, void* stream) {
+  return launch_steps(c, n, 1, d_tokens, d_page_table, d_seq_lens, d_logits, d_next_tokens, stream, 1);
 }
 
 extern "C" int mk_get_error(mk_ctx* c, int32_t* code, int32_t* cu, int32_t* task, void* stream) {

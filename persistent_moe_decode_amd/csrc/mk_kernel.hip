@@ -1254,6 +1254,12 @@ typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
 typedef short short4_v __attribute__((ext_vector_type(4)));
 typedef float float4_v __attribute__((ext_vector_type(4)));
 
+// One rotated pair (i, i + d/2) of a head at angle (cos cf, sin sf), each half rounded to bf16.
+DEV void rope_pair(float x0, float x1, float cf, float sf, uint16_t& lo, uint16_t& hi) {
+  lo = f2bf(x0 * cf - x1 * sf);
+  hi = f2bf(x0 * sf + x1 * cf);
+}
+
 template <int D>
 struct AttnPage {
   uint4 k[D / 32];  // lane l: K[pos l%16][32c + 8*(l/16) .. +7]
@@ -1631,11 +1637,13 @@ DEV void attn_task(const KArgs& a, const Task& t, const Lds& s, int qi) {
   const int l = t.layer, G = a.group, ps = a.ps;
   const int b = plan[0], g = plan[1], t0 = plan[2], t1 = plan[3], first = plan[4], nch = plan[5], p = plan[7];
   const int nblk = (t1 - t0 + 15) / 16;
-  const int nl = attn_lds_pages<D>(a, nblk);
+  // a mixed step reads no page before every entry's new K/V is in (they may
+  // share a sequence): no LDS copies or early blocks then
+  const int nl = a.kv_sync ? 0 : attn_lds_pages<D>(a, nblk);
   const int bl0 = nblk - nl;
   // early blocks never include the last one (it receives the new token); wave
   // 0, whose thread 0 polls the flags, loads none
-  const int ne = max(0, min(bl0 - (nl == 0 ? 1 : 0), 2 * (kWaves - 1)));
+  const int ne = a.kv_sync ? 0 : max(0, min(bl0 - (nl == 0 ? 1 : 0), 2 * (kWaves - 1)));
   attn_prefetch<D>(a, s, qi, l, b, g, t0, bl0, nl);
   const int wave = tid() >> 6;
   AttnPage<D> ring[kAttnRing];
@@ -1647,11 +1655,12 @@ DEV void attn_task(const KArgs& a, const Task& t, const Lds& s, int qi) {
   const int page = mine ? a.page_table[(size_t)b * a.max_pages + p / ps] : 0;
   const bool pg_ok = page >= 0 && page < a.num_pages;
   if (mine && !pg_ok && tid() == 0) raise_error(a, MK_ERR_DEVICE_PAGE, qi, page);
-  const bool put = mine && pg_ok;
+  const bool put = mine && pg_ok && !a.kv_sync;  // (a mixed step's KVW tasks wrote it)
   const size_t koff = ((((size_t)l * a.num_pages + page) * a.nkv + g) * ps + p % ps) * D;
   constexpr int half = D / 2;
   const int nrot = (G + (put ? 1 : 0)) * half;  // pairs: q heads, then (put) the new k
   if (!wait_counter(a, t.wait[0], t.fanin[0], qi, s.flags + 0)) return;
+  if (a.kv_sync && !wait_counter(a, t.wait[1], t.fanin[1], qi, s.flags + 0)) return;
   if (a.trace && tid() == 0 && qi < a.trace_cap) a.trace[kTraceWords * (size_t)qi + 1] = wall_clock64();
   // q of the group's heads, the new k and v (all loads in flight before any use)
   const float* qkv = a.qkv + ((size_t)l * a.max_batch + b) * a.qkv_rows;
@@ -1675,8 +1684,8 @@ DEV void attn_task(const KArgs& a, const Task& t, const Lds& s, int qi) {
     const int e = tid() + k * kThreads;
     if (e < nrot) {
       const int hh = e / half, i = e % half;
-      const float cf = s.rot[i], sf = s.rot[64 + i];
-      const uint16_t lo = f2bf(x0[k] * cf - x1[k] * sf), hi = f2bf(x0[k] * sf + x1[k] * cf);
+      uint16_t lo, hi;
+      rope_pair(x0[k], x1[k], s.rot[i], s.rot[64 + i], lo, hi);
       q_s[hh * D + i] = lo;
       q_s[hh * D + i + half] = hi;
       if (hh == G) {
@@ -1761,6 +1770,44 @@ DEV void attn_task(const KArgs& a, const Task& t, const Lds& s, int qi) {
   uint16_t* out = a.attn_out + ((size_t)l * a.max_batch + b) * a.nq * D + (size_t)g * G * D;
   attn_combine(a, s, parts, nch, out);
   return;
+}
+
+// Mixed steps only: the new K (rotated) and V of lead t.idx's (sequence, kv
+// head), written through to memory before the task's signal, so that every
+// attention task of the layer, which waits for all of them, reads them from
+// the pages.  In other steps the task only signals.
+TASK void task_kvw(const KArgs& a, const Task& t, const Lds& s, int qi) {
+  if (!a.kv_sync) return;
+  if (!wait_counter(a, t.wait[0], t.fanin[0], qi, s.flags + 0)) return;
+  const int m = t.idx, b = m / a.nkv, g = m % a.nkv;
+  if (b >= a.n) return;
+  const int D = a.d, half = D / 2, ps = a.ps, l = t.layer;
+  const int p = a.seq_lens[b] + a.step;
+  if (p < 0 || p + 1 > a.max_pages * ps) {
+    if (tid() == 0) raise_error(a, MK_ERR_DEVICE_SEQ, qi, b);
+    return;
+  }
+  const int page = a.page_table[(size_t)b * a.max_pages + p / ps];
+  if (page < 0 || page >= a.num_pages) {
+    if (tid() == 0) raise_error(a, MK_ERR_DEVICE_PAGE, qi, page);
+    return;
+  }
+  const float* qkv = a.qkv + ((size_t)l * a.max_batch + b) * a.qkv_rows;
+  const float* kr = qkv + (size_t)a.nq * D + (size_t)g * D;
+  const float* vr = qkv + (size_t)(a.nq + a.nkv) * D + (size_t)g * D;
+  const size_t koff = ((((size_t)l * a.num_pages + page) * a.nkv + g) * ps + p % ps) * D;
+  const size_t voff = (((size_t)l * a.num_pages + page) * a.nkv + g) * (size_t)ps * D + p % ps;
+  const int i = tid();
+  if (i < half) {
+    // the rotation at position p as the attention tasks compute it (angle in double, cos / sin in float)
+    double sd, cd;
+    sincos((double)p * a.inv_freq[i], &sd, &cd);
+    uint16_t lo, hi;
+    rope_pair(ld_coh(kr + i), ld_coh(kr + i + half), (float)cd, (float)sd, lo, hi);
+    st_coh(a.k_pool + koff + i, lo);
+    st_coh(a.k_pool + koff + i + half, hi);
+  }
+  if (i < D) st_coh(a.v_pool + voff + (size_t)i * ps, f2bf(ld_coh(vr + i)));
 }
 
 TASK void task_attn(const KArgs& a, const Task& t, const Lds& s, int qi) {
@@ -2316,7 +2363,8 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) MKK(mk_megakernel)(KAr
         ok = wait_counter_at(a, ctr_index(a.L, C_DONE), a.n_lm, q, s.flags + 1, a.epoch - 1);
       // attention, Wo and output tasks wait inside, once their loads are in flight; gate/up
       // tasks poll the tagged router logits inside
-      const bool own_wait = t.op == OP_ATTN || t.op == OP_OUT || t.op == OP_WO || t.op == OP_GATEUP || t.op == OP_GUTAIL;
+      const bool own_wait = t.op == OP_ATTN || t.op == OP_OUT || t.op == OP_WO || t.op == OP_GATEUP ||
+                            t.op == OP_GUTAIL || t.op == OP_KVW;
       if (ok && !own_wait) ok = wait_counter(a, t.wait[0], t.fanin[0], q, s.flags + 0);
       if (ok && !own_wait && t.wait[1] >= 0) ok = wait_counter(a, t.wait[1], t.fanin[1], q, s.flags + 1);
       if (a.trace && tid() == 0) t_ready = wall_clock64();
@@ -2328,6 +2376,7 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) MKK(mk_megakernel)(KAr
           case OP_GATEUP: tk_layer = task_gateup(a, t, s, q, xs_layer == t.layer) ? t.layer : -1; break;
           case OP_OUT: wait_waves = task_out(a, t, s, q, tk_layer == t.layer, tk_layer); break;
           case OP_WO: task_wo(a, t, s, q, npf); break;
+          case OP_KVW: task_kvw(a, t, s, q); break;
           case OP_GUTAIL: tk_layer = task_gutail(a, t, s, q) ? t.layer : -1; break;
           case OP_LMHEAD: task_lmhead(a, t, s, q); break;
           default: break;

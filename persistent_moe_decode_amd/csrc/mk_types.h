@@ -36,6 +36,7 @@ enum Op : int32_t {
   OP_LMHEAD = 5,  // final RMSNorm + LM head rows; last arriver takes the argmax
   OP_WO = 6,      // rows of Wo times the merged attention output (run by the attention units)
   OP_GUTAIL = 7,  // an attention unit past its chunk takes gate/up rows from the layer's shared pool
+  OP_KVW = 8,     // a segment lead's unit: (mixed steps) the new K/V of its (sequence, kv head), then its signal
 };
 
 // One task: 32 int32 (128 bytes, one cache line).
@@ -67,8 +68,9 @@ static_assert(sizeof(Task) == kTaskInts * 4, "task descriptor is 128 bytes");
 // (no reset between steps).  Spreading the adds keeps any one line from
 // serializing many of them, and a waiter reads only kSubCounters lines.
 enum CtrSlot : int32_t { C_QKV = 0, C_ROUTER = 1, C_ATTN = 2, C_GATEUP = 3, C_XNEXT = 4, C_DONE = 5, C_WO = 6,
-                         C_CHUNK = 7 };  // C_CHUNK: simulation only (the leads' ticket waits)
-constexpr int kCtrPerLayer = 8;
+                         C_CHUNK = 7,   // simulation only (the leads' ticket waits)
+                         C_KVW = 8 };   // the step's new K/V written (every lead signals; mixed steps wait)
+constexpr int kCtrPerLayer = 9;
 constexpr int kSubCounters = 16;
 constexpr int kSubStride = 32;                           // words between sub-counters (128 bytes)
 constexpr int kCounterWords = kSubCounters * kSubStride;
@@ -132,6 +134,8 @@ struct KArgs {
   double inv_temp;           // sampling: 1 / temperature, or 0 for the greedy argmax
   uint64_t seed;             // sampling: generator seed
   int32_t nsteps;            // decode steps in this launch
+  int32_t kv_sync;           // mixed step: entries may share a sequence; attention reads pages only after
+                             // every entry's new K/V is written (the KVW tasks), and no page is read before
   int32_t step;              // the step being run (set by the kernel: epoch + step, positions + step)
 };
 

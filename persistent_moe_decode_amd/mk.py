@@ -24,7 +24,7 @@ ERRORS = {
 }
 CODES = {v: k for k, v in ERRORS.items()}
 TASK_INT32S = 32
-OPS = {1: "PRE", 2: "ATTN", 3: "GATEUP", 4: "OUT", 5: "LMHEAD", 6: "WO", 7: "GUTAIL"}
+OPS = {1: "PRE", 2: "ATTN", 3: "GATEUP", 4: "OUT", 5: "LMHEAD", 6: "WO", 7: "GUTAIL", 8: "KVW"}
 
 
 class MkError(RuntimeError):
@@ -86,6 +86,7 @@ def lib():
         "mk_bind_scratch": [P, ctypes.POINTER(P), I32, P, P, P],
         "mk_decode_step": [P, I32, P, P, P, P, P, P],
         "mk_decode_steps": [P, I32, I32, P, P, P, P, P, P],
+        "mk_mixed_step": [P, I32, P, P, P, P, P, P],
         "mk_get_error": [P, pi32, pi32, pi32, P],
         "mk_reset": [P, P],
         "mk_set_spin_limit_us": [P, I64],
@@ -222,6 +223,11 @@ class Context:
                     next_ptr: int | None, stream: int):
         check(lib().mk_decode_step(self.h, n, tokens_ptr, page_table_ptr, seq_lens_ptr, logits_ptr,
                                    next_ptr or None, stream), "mk_decode_step")
+
+    def mixed_step(self, n: int, tokens_ptr: int, page_table_ptr: int, seq_lens_ptr: int, logits_ptr: int,
+                   next_ptr: int | None, stream: int):
+        check(lib().mk_mixed_step(self.h, n, tokens_ptr, page_table_ptr, seq_lens_ptr, logits_ptr,
+                                  next_ptr or None, stream), "mk_mixed_step")
 
     def decode_steps(self, n: int, steps: int, tokens_ptr: int, page_table_ptr: int, seq_lens_ptr: int,
                      logits_ptr: int, next_ptr: int | None, stream: int):
