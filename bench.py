@@ -197,6 +197,83 @@ def cpu_baseline(w, budget_s: float = 25.0, budget_1t_s: float = 20.0):
     }
 
 
+def mixed_bench(args, w0, total):
+    """Mixed steps: sequence A (the workload's single sequence) decodes one token per step while
+    sequence B's prompt runs K tokens per step at positions K*i .. K*i + K - 1 (its own page-table
+    row).  Timed against plain single-entry decode steps of A at the same contexts."""
+    import numpy as np
+    import torch
+
+    import synth
+    from persistent_moe_decode_amd.runtime import DeviceDecoder
+
+    K = args.mixed
+    if w0.batch != 1 or not 1 <= K <= 7:
+        sys.exit("--mixed needs a batch-1 workload and 1 <= K <= 7")
+    w = synth.Workload(w0.name + f"_mixed{K}", w0.shape, batch=1 + K, steps=K * total + 16,
+                       context=[w0.context[0]] + [0] * K)
+    # the default split would size attention for 1 + K sequences of the mean context and reserve a
+    # lead unit per possible (entry, kv head): here one sequence holds nearly all K/V, so keep the
+    # batch-1 split's other attention units (--attn-units overrides)
+    ref = synth.workload(w0.name)
+    from persistent_moe_decode_amd import mk
+    c1 = mk.Context(mk.config_from_shape(ref.shape, 1, ref.max_pages_per_seq, ref.num_pages))
+    c1.build_schedule(0, ref.context[0] + ref.steps // 2)
+    n_other = c1.info().n_attn - ref.shape.n_kv_heads
+    attn = args.attn_units or (1 + K) * w.shape.n_kv_heads + n_other
+    log(f"[bench] mixed: {attn} attention units ({n_other} besides the {(1 + K) * w.shape.n_kv_heads} segment leads)")
+    dec = DeviceDecoder(w, attn_units=attn)
+    dec.fill_synthetic_kv()
+    dev, n = dec.dev, 1 + K
+    pt_np = dec.page_table_np.copy()
+    pt_np[2:] = pt_np[1]
+    pt = torch.from_numpy(np.ascontiguousarray(pt_np)).to(dev)
+    ctx = w0.context[0]
+    b_prompt = synth.uniform_u32(synth.SEED_PROMPT, synth.tid(synth.K_PROMPT, 1), 0, K * total,
+                                 w.shape.vocab).astype(np.int32)
+    toks = torch.zeros(total, n, dtype=torch.int32, device=dev)
+    lens = torch.zeros(total, n, dtype=torch.int32, device=dev)
+    for i in range(total):
+        toks[i, 0] = int(w0.prompt(0)[ctx])
+        toks[i, 1:] = torch.from_numpy(b_prompt[K * i:K * (i + 1)])
+        lens[i, 0] = ctx + i
+        lens[i, 1:] = torch.arange(K * i, K * (i + 1), dtype=torch.int32)
+    nxt = torch.zeros(n, dtype=torch.int32, device=dev)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize(dev)
+        dec.check_error()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.warmup, total):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize(dev)
+        dec.check_error()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_mixed = timed(lambda i: dec.ctx.mixed_step(n, toks[i].data_ptr(), pt.data_ptr(), lens[i].data_ptr(),
+                                                  dec.logits.data_ptr(), nxt.data_ptr(), dec.stream))
+    ms_decode = timed(lambda i: dec.ctx.decode_step(1, toks[i].data_ptr(), pt.data_ptr(), lens[i].data_ptr(),
+                                                    dec.logits.data_ptr(), nxt.data_ptr(), dec.stream))
+    log(f"[bench] mixed step ({K} prompt tokens + 1 decode): {ms_mixed:.3f} ms; plain decode step "
+        f"{ms_decode:.3f} ms")
+    dec.close()
+    s = w.shape
+    print(json.dumps({
+        "metric": "mixed step: one decode token plus K chunked-prefill tokens per persistent launch",
+        "value": round(n / (ms_mixed / 1e3), 2), "unit": "tok/s (decode + prefill)", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_mixed, 4), "higher_is_better": True,
+        "dtype": "fp8-e4m3 weights, bf16 activations" if s.weights == "fp8" else "bf16", "data": "synthetic",
+        "config": {"workload": f"{w0.name}: decode at {ctx}+ plus a prompt in chunks of {K}", "prefill_chunk": K,
+                   "decode_tok_s": round(1 / (ms_mixed / 1e3), 2),
+                   "prefill_tok_s": round(K / (ms_mixed / 1e3), 2),
+                   "plain_decode_ms_per_step": round(ms_decode, 4)},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -214,6 +291,10 @@ def main():
     ap.add_argument("--pool-64ths", type=int, default=0, help="schedule: shared gate/up pool share (0 = none)")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="after the run, one plain device-to-device copy of this many bytes (counter calibration)")
+    ap.add_argument("--mixed", type=int, default=0, metavar="K",
+                    help="time mixed steps instead (mk_mixed_step): the workload's batch-1 decode plus K "
+                         "prompt tokens of a second sequence per step (its prompt advancing K positions a "
+                         "step), against plain decode steps of the same context; prints its own JSON line")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_<workload>.json from two rocprofv3 counter runs made with "
                          "--copy-calib 1073741824, then exit (no GPU needed)")
@@ -235,6 +316,8 @@ def main():
 
     w = synth.workload(args.workload)
     total = args.warmup + args.steps
+    if args.mixed:
+        return mixed_bench(args, w, total)
     if total > w.steps:
         w.steps = total  # page capacity for every position the run writes
     t0 = time.time()
