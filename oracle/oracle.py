@@ -36,7 +36,8 @@ format.  The reading taken: the large streamed matrices (LM head, Wqkv, Wo,
 expert gate/up/down) are OCP E4M3 codes times one fp32 scale per output row;
 the weight value is decode(code) * scale, exactly, in float64, and every
 product then runs as with bfloat16 weights.  Router, norm gains and embedding
-stay bfloat16.
+stay bfloat16.  FP4 weights (``weights="fp4"``) are the same with OCP E2M1
+codes, two a byte (the even element in the low nibble).
 
 Parity unpinned: the composed multi-layer logits have no closed form; they
 are pinned only through the pinned ops and the whole-step invariants in
@@ -72,6 +73,29 @@ def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
     mag = np.where((e == 0xF) & ((c & 7) == 7), np.nan, mag)
     return sign * mag
 
+
+def e2m1_to_f64(codes: np.ndarray) -> np.ndarray:
+    """Exact value of OCP E2M1 codes (4-bit, in uint8) as float64: sign bit 3, exponent bits 2..1
+    with bias 1, mantissa bit 0; exponent field 0 holds the subnormal m * 0.5; no NaN, no infinity."""
+    c = np.asarray(codes).astype(np.int64) & 0xF
+    sign = np.where(c & 8, -1.0, 1.0)
+    e = (c >> 1) & 3
+    m = (c & 1).astype(np.float64)
+    mag = np.where(e == 0, m * 0.5, (1.0 + m / 2.0) * np.exp2((e - 1).astype(np.float64)))
+    return sign * mag
+
+
+def fp4_unpack_f64(packed: np.ndarray) -> np.ndarray:
+    """Values of packed E2M1 codes: byte j holds element 2j (low nibble) and 2j + 1 (high nibble);
+    the last axis doubles."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],))
+    out[..., 0::2] = _E2M1_VALUES[p & 0xF]
+    out[..., 1::2] = _E2M1_VALUES[p >> 4]
+    return out
+
+
+_E2M1_VALUES = e2m1_to_f64(np.arange(16, dtype=np.uint8))
 
 # the 256 values of the definition above, for decoding whole weight tensors by lookup
 _E4M3_VALUES = e4m3_to_f64(np.arange(256, dtype=np.uint8))
@@ -176,7 +200,11 @@ class Weights:
         key = (kind, layer, expert)
         w = self.cache.get(key)
         if w is None:
-            if self.shape.quantized(kind):
+            if self.shape.quantized(kind) and self.shape.weights == "fp4":
+                # FP4 weights: each row's codes (two a byte) times the row's scale
+                codes, scales = synth.weight_fp4(self.shape, kind, layer, expert)
+                w = fp4_unpack_f64(codes) * scales.astype(np.float64).reshape(codes.shape[:-1] + (1,))
+            elif self.shape.quantized(kind):
                 # FP8 weights: each row's codes times the row's scale
                 codes, scales = self.source_fp8(kind, layer, expert)
                 w = e4m3_lookup(codes) * scales.astype(np.float64).reshape(codes.shape[:-1] + (1,))

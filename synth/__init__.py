@@ -89,6 +89,12 @@ def lib():
         L.synth_fp8_scales.argtypes = [u64, u64, u64, u64, ctypes.c_double, ctypes.c_double, p]
         L.synth_e4m3_rne.restype = ctypes.c_uint8
         L.synth_e4m3_rne.argtypes = [ctypes.c_float]
+        L.synth_fp4_codes.restype = None
+        L.synth_fp4_codes.argtypes = [u64, u64, u64, u64, p]
+        L.synth_fp4_scales.restype = None
+        L.synth_fp4_scales.argtypes = [u64, u64, u64, u64, ctypes.c_double, ctypes.c_double, p]
+        L.synth_e2m1_rne.restype = ctypes.c_uint8
+        L.synth_e2m1_rne.argtypes = [ctypes.c_float]
         L.synth_uniform_u32.restype = None
         L.synth_uniform_u32.argtypes = [u64, u64, u64, u64, ctypes.c_uint32, p]
         L.synth_permutation.restype = None
@@ -220,6 +226,27 @@ def fp8_scales_np(seed: int, t: int, start: int, count: int) -> np.ndarray:
     return np.float32(WEIGHT_SIGMA / 32.0) * g.view(np.float32)
 
 
+def e2m1_rne_np(f: np.ndarray) -> np.ndarray:
+    """numpy mirror of the generator's E2M1 encoder (nearest code, ties to even, saturating at 6)."""
+    f = np.asarray(f, dtype=np.float32)
+    a = np.abs(f)
+    m = np.select([a <= 0.25, a < 0.75, a <= 1.25, a < 1.75, a <= 2.5, a < 3.5, a <= 5.0], [0, 1, 2, 3, 4, 5, 6], 7)
+    sign = np.where(np.signbit(f), 8, 0)
+    return (m | sign).astype(np.uint8)
+
+
+def fp4_codes_np(seed: int, t: int, start: int, count: int) -> np.ndarray:
+    with np.errstate(over="ignore"):
+        s = _irwin_hall_np(words_np(seed, t, start, count)).astype(np.float32)
+    c = e2m1_rne_np(s * normal_scale_np(1.5))
+    return (c[0::2] | (c[1::2] << 4)).astype(np.uint8)
+
+
+def fp4_scales_np(seed: int, t: int, start: int, count: int) -> np.ndarray:
+    g = gain_bf16_np(seed, t, start, count, GAIN_SIGMA).astype(np.uint32) << np.uint32(16)
+    return np.float32(WEIGHT_SIGMA / 1.5) * g.view(np.float32)
+
+
 def uniform_u32_np(seed: int, t: int, start: int, count: int, n: int) -> np.ndarray:
     w = words_np(seed, t, start, count)
     hi = (w >> np.uint64(32))
@@ -255,17 +282,17 @@ class ModelShape:
     rope_theta: float = 1.0e4
     rms_eps: float = 1.0e-6
     page_size: int = 16
-    weights: str = "bf16"   # "bf16", or "fp8": the QUANT_KINDS matrices as E4M3 codes + fp32 row scales
+    weights: str = "bf16"   # "bf16"; "fp8" / "fp4": the QUANT_KINDS matrices as E4M3 / E2M1 codes + fp32 row scales
 
     def quantized(self, kind: int) -> bool:
-        return self.weights == "fp8" and kind in QUANT_KINDS
+        return self.weights in ("fp8", "fp4") and kind in QUANT_KINDS
 
     def weight_nbytes(self, kind: int) -> int:
         """Bytes of one weight tensor as bound: bf16, or (quantized) codes then one fp32 scale per row."""
         shp = self.weight_shape(kind)
         n = int(np.prod(shp))
         if self.quantized(kind):
-            return n + 4 * (n // shp[-1])
+            return (n if self.weights == "fp8" else n // 2) + 4 * (n // shp[-1])
         return 2 * n
 
     @property
@@ -291,10 +318,10 @@ class ModelShape:
         """Algorithmic weight bytes read by one decode step (one embedding row per token aside):
         2 bytes per bf16 element; 1 per quantized element plus 4 per quantized row."""
         H, I = self.hidden, self.inter
-        q = self.weights == "fp8"
+        per_el = {"fp8": 1.0, "fp4": 0.5}.get(self.weights)
 
         def mat(rows: float, cols: int) -> float:
-            return rows * cols + 4.0 * rows if q else 2.0 * rows * cols
+            return per_el * rows * cols + 4.0 * rows if per_el else 2.0 * rows * cols
 
         per_layer = (mat(self.qkv_rows, H) + mat(H, self.attn_dim) + 2.0 * H * self.n_experts
                      + distinct_experts_per_layer * (2 * mat(I, H) + mat(H, I)) + 2.0 * H)
@@ -349,10 +376,43 @@ def fp8_scales(seed: int, t: int, start: int, count: int) -> np.ndarray:
     return out
 
 
+def fp4_codes(seed: int, t: int, start: int, count: int, out: np.ndarray | None = None) -> np.ndarray:
+    """Packed E2M1 codes (uint8, two a byte, the even element in the low nibble) of elements
+    ``start .. start+count-1`` of stream (seed, t); start and count even."""
+    assert start % 2 == 0 and count % 2 == 0
+    if out is None:
+        out = np.empty(count // 2, dtype=np.uint8)
+    lib().synth_fp4_codes(seed, t, start, count, _ptr(out))
+    return out
+
+
+def fp4_scales(seed: int, t: int, start: int, count: int) -> np.ndarray:
+    out = np.empty(count, dtype=np.float32)
+    lib().synth_fp4_scales(seed, t, start, count, WEIGHT_SIGMA, GAIN_SIGMA, _ptr(out))
+    return out
+
+
+def weight_fp4(shape: ModelShape, kind: int, layer: int = 0, expert: int | None = None):
+    """(packed codes uint8 [..][cols / 2], scales float32 [rows]) of one FP4 weight tensor (or one
+    expert's slice of it), generated from the recipe."""
+    assert shape.quantized(kind) and shape.weights == "fp4"
+    full = shape.weight_shape(kind)
+    index = layer if kind in LAYER_KINDS else 0
+    if expert is not None:
+        per = full[1] * full[2]
+        start, count, out_shape = expert * per, per, full[1:]
+    else:
+        start, count, out_shape = 0, int(np.prod(full)), full
+    cols = full[-1]
+    codes = fp4_codes(SEED_WEIGHTS, tid(kind, index), start, count).reshape(out_shape[:-1] + (cols // 2,))
+    scales = fp4_scales(SEED_WEIGHTS, tid(FP8_SCALE_KIND + kind, index), start // cols, count // cols)
+    return codes, scales
+
+
 def weight_fp8(shape: ModelShape, kind: int, layer: int = 0, expert: int | None = None):
     """(codes uint8 [..][cols], scales float32 [rows]) of one quantized weight tensor (or one expert's
     slice of it), generated from the recipe."""
-    assert shape.quantized(kind)
+    assert shape.quantized(kind) and shape.weights == "fp8"
     full = shape.weight_shape(kind)
     index = layer if kind in LAYER_KINDS else 0
     if expert is not None:
@@ -425,11 +485,12 @@ def ragged_lengths(batch: int, lo: int, hi: int) -> list:
 def workload(name: str) -> Workload:
     """The five workloads: tiny, mid, moe30b_8k, moe30b_bs8_ragged, moe30b_256k; a name ending in
     ``_fp8`` is the same workload with the QUANT_KINDS matrices in FP8."""
-    if name.endswith("_fp8"):
-        w = workload(name[: -len("_fp8")])
-        w.name = name
-        w.shape = replace(w.shape, weights="fp8")
-        return w
+    for fmt in ("fp8", "fp4"):
+        if name.endswith("_" + fmt):
+            w = workload(name[: -len(fmt) - 1])
+            w.name = name
+            w.shape = replace(w.shape, weights=fmt)
+            return w
     if name == "tiny":
         return Workload(name, TINY, batch=1, steps=16, context=[128], kv_mode="prefill", shuffle_pages=False)
     if name == "mid":

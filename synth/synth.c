@@ -30,6 +30,12 @@
  *     scale = f32(sigma / 32) * f32(bf16_rne(1 + f32(s') * f32(0.02 / SD)))
  * with s' from the scale stream of the tensor, so code * scale is a weight of
  * about the same spread as the bf16 recipe's.
+ *
+ * FP4 weights (OCP E2M1: 1 sign, 2 exponent bits with bias 1, 1 mantissa bit,
+ * magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), two codes a byte, element 2j in the
+ * low nibble of byte j:
+ *     code = e2m1_rne( f32(s) * f32(1.5 / SD) )   (|value| < 5.2: no saturation)
+ * and row scales f32(sigma / 1.5) * (the same gain near one).
  */
 #include <math.h>
 #include <stdint.h>
@@ -173,4 +179,44 @@ void synth_fp8_scales(uint64_t seed, uint64_t tid, uint64_t start, uint64_t coun
     memcpy(&gf, &gu, 4);
     out[j] = base * gf;
   }
+}
+
+/* The E2M1 code nearest to f, ties to the even code (mantissa bit 0); |f| > 6
+ * saturates to 6. */
+static inline uint8_t f32_to_e2m1_rne(float f) {
+  const uint8_t sign = f < 0.0f || (f == 0.0f && signbit(f)) ? 8 : 0;
+  const float a = fabsf(f);
+  uint8_t m;
+  if (a <= 0.25f) m = 0;          /* 0 (tie at 0.25 -> 0) */
+  else if (a < 0.75f) m = 1;      /* 0.5 */
+  else if (a <= 1.25f) m = 2;     /* 1 (ties at 0.75 and 1.25 -> 1) */
+  else if (a < 1.75f) m = 3;      /* 1.5 */
+  else if (a <= 2.5f) m = 4;      /* 2 (ties at 1.75 and 2.5 -> 2) */
+  else if (a < 3.5f) m = 5;       /* 3 */
+  else if (a <= 5.0f) m = 6;      /* 4 (ties at 3.5 and 5 -> 4) */
+  else m = 7;                     /* 6 */
+  return (uint8_t)(sign | m);
+}
+
+uint8_t synth_e2m1_rne(float f) { return f32_to_e2m1_rne(f); }
+
+/* Packed FP4 codes of elements start .. start + count - 1 (start, count even):
+ * out[j] holds elements start + 2j (low nibble) and start + 2j + 1 (high). */
+void synth_fp4_codes(uint64_t seed, uint64_t tid, uint64_t start, uint64_t count, uint8_t* out) {
+  const uint64_t key = synth_key(seed, tid);
+  const float c = synth_normal_scale(1.5);
+  int64_t n = (int64_t)(count / 2);
+#pragma omp parallel for schedule(static) if (n > 131072)
+  for (int64_t j = 0; j < n; ++j) {
+    const uint64_t e = start + 2 * (uint64_t)j;
+    const uint8_t lo = f32_to_e2m1_rne((float)irwin_hall(word_at(key, e)) * c);
+    const uint8_t hi = f32_to_e2m1_rne((float)irwin_hall(word_at(key, e + 1)) * c);
+    out[j] = (uint8_t)(lo | (hi << 4));
+  }
+}
+
+/* FP4 row scales: f32(sigma / 1.5) * (a gain near one, as bf16). */
+void synth_fp4_scales(uint64_t seed, uint64_t tid, uint64_t start, uint64_t count, double sigma,
+                      double gain_sigma, float* out) {
+  synth_fp8_scales(seed, tid, start, count, sigma * 32.0 / 1.5, gain_sigma, out);
 }

@@ -642,3 +642,57 @@ def test_fp8_step_bytes_30b_shape():
     want = L * per_layer + (V * H + 4 * V) + 2 * H
     assert s.active_weight_bytes(8) == want
     assert abs(want / synth.MOE30B.active_weight_bytes(8) - 0.5) < 0.01
+
+
+# ----------------------------------------------------------------------------
+# FP4 (E2M1) weights
+
+
+def test_e2m1_decode_table():
+    """The OCP E2M1 values (the format's whole table: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6)."""
+    want = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    got = O.e2m1_to_f64(np.arange(16, dtype=np.uint8))
+    assert list(got[:8]) == want and list(got[8:]) == [-v for v in want]
+    assert np.signbit(got[8]) and got[8] == 0.0
+    assert np.all(np.diff(got[:8]) > 0)
+
+
+def test_fp4_unpack_nibble_order():
+    """Byte j holds element 2j in its low nibble and 2j + 1 in its high nibble."""
+    packed = np.array([[0x21, 0xF7]], dtype=np.uint8)   # elements: 1, 2, 7, 15
+    assert O.fp4_unpack_f64(packed).tolist() == [[0.5, 1.0, 6.0, -6.0]]
+
+
+def test_fp4_step_is_the_bf16_step_on_the_dequantized_weights():
+    """As for FP8: a step of the FP4 model equals, bit for bit, the bf16-format step whose quantized
+    matrices hold the dequantized values (decoded here from the table by hand)."""
+    from dataclasses import replace
+    sq = replace(synth.TINY, weights="fp4")
+    table = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0])
+    Wq, Wb = O.Weights(sq), O.Weights(synth.TINY)
+    for kind in synth.QUANT_KINDS:
+        for l in (range(sq.n_layers) if kind in synth.LAYER_KINDS else [0]):
+            codes, scales = synth.weight_fp4(sq, kind, l)
+            vals = np.stack([table[codes & 15], table[codes >> 4]], axis=-1).reshape(codes.shape[:-1] + (-1,))
+            Wb.cache[(kind, l, None)] = vals * scales.astype(np.float64).reshape(codes.shape[:-1] + (1,))
+            if kind in (synth.K_W_GATE, synth.K_W_UP, synth.K_W_DOWN):
+                for e in range(sq.n_experts):
+                    Wb.cache[(kind, l, e)] = Wb.cache[(kind, l, None)][e]
+    outs = []
+    for W, s in ((Wq, sq), (Wb, synth.TINY)):
+        kv = O.PagedKV(s, 4)
+        for t, tok in enumerate([5, 77, 300]):
+            out = O.decode_step(W, kv, [tok], np.arange(4, dtype=np.int32)[None], [t])
+        outs.append(out.logits)
+    assert np.array_equal(outs[0], outs[1])
+    assert np.array_equal(Wq.get(synth.K_W_DOWN, 1, 3), Wq.get(synth.K_W_DOWN, 1)[3])
+
+
+def test_fp4_step_bytes_30b_shape():
+    from dataclasses import replace
+    s = replace(synth.MOE30B, weights="fp4")
+    H, I, E, V, L = s.hidden, s.inter, s.n_experts, s.vocab, s.n_layers
+    qkv, ad = s.qkv_rows, s.attn_dim
+    m = lambda r, c: r * c / 2 + 4 * r
+    want = L * (m(qkv, H) + m(H, ad) + 2 * E * H + 8 * (2 * m(I, H) + m(H, I)) + 2 * H) + m(V, H) + 2 * H
+    assert s.active_weight_bytes(8) == want

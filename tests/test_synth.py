@@ -138,3 +138,22 @@ def test_fp8_weight_slices_and_workloads():
     # codes never saturate and use both signs; scales sit near sigma / 32
     assert (codes & 0x7F).max() < 0x7E and (codes >> 7).min() == 0 and (codes >> 7).max() == 1
     assert np.all(np.abs(scales / (synth.WEIGHT_SIGMA / 32) - 1) < 0.2)
+
+
+def test_fp4_codes_c_equals_numpy_and_encoder_is_nearest():
+    for kind, idx, start, n in ((synth.K_WQKV, 0, 0, 70002), (synth.K_W_DOWN, 5, 123456, 50000)):
+        t = synth.tid(kind, idx)
+        assert np.array_equal(synth.fp4_codes(0, t, start, n), synth.fp4_codes_np(0, t, start, n))
+        ts = synth.tid(synth.FP8_SCALE_KIND + kind, idx)
+        assert np.array_equal(synth.fp4_scales(0, ts, start, 999), synth.fp4_scales_np(0, ts, start, 999))
+    vals = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    rng = np.random.default_rng(8)
+    x = np.concatenate([rng.uniform(-7, 7, 20000), (vals[1:] + vals[:-1]) / 2, -(vals[1:] + vals[:-1]) / 2]).astype(np.float32)
+    got = synth.e2m1_rne_np(x)
+    assert np.array_equal(got[::50], np.array([synth.lib().synth_e2m1_rne(float(v)) for v in x[::50]], dtype=np.uint8))
+    mag = np.abs(x.astype(np.float64))
+    d = np.abs(mag[:, None] - vals[None, :])
+    cand = d == d.min(1)[:, None]
+    want = np.where(cand.sum(1) == 1, cand.argmax(1), np.where(cand & (np.arange(8)[None, :] % 2 == 0), np.arange(8)[None, :], 99).min(1))
+    assert np.array_equal(got & 7, want.astype(np.uint8))
+    assert np.all((got >> 3)[x < 0] == 1) and np.all((got >> 3)[x > 0] == 0)
