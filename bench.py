@@ -28,6 +28,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+DTYPES = {"bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 activations", "fp4": "fp4-e2m1 weights, bf16 activations"}
+KERNELS = {"bf16": "mk_megakernel", "fp8": "mk_megakernel_fp8", "fp4": "mk_megakernel_fp4"}
 METRIC = "decode tok/s at bs=1 8K ctx; achieved HBM GB/s as % of MI355X peak"
 
 
@@ -37,7 +39,7 @@ def log(*a):
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("mk_kernel.hip", "mk_kernel_fp8.hip", "mk_host.cpp", "mk_types.h"):
+    for f in ("mk_kernel.hip", "mk_kernel_fp8.hip", "mk_kernel_fp4.hip", "mk_host.cpp", "mk_types.h"):
         with open(os.path.join(ROOT, "persistent_moe_decode_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -266,7 +268,7 @@ def mixed_bench(args, w0, total):
         "metric": "mixed step: one decode token plus K chunked-prefill tokens per persistent launch",
         "value": round(n / (ms_mixed / 1e3), 2), "unit": "tok/s (decode + prefill)", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_mixed, 4), "higher_is_better": True,
-        "dtype": "fp8-e4m3 weights, bf16 activations" if s.weights == "fp8" else "bf16", "data": "synthetic",
+        "dtype": DTYPES[s.weights], "data": "synthetic",
         "config": {"workload": f"{w0.name}: decode at {ctx}+ plus a prompt in chunks of {K}", "prefill_chunk": K,
                    "decode_tok_s": round(1 / (ms_mixed / 1e3), 2),
                    "prefill_tok_s": round(K / (ms_mixed / 1e3), 2),
@@ -426,10 +428,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3 weights, bf16 activations" if s.weights == "fp8" else "bf16",
+        "dtype": DTYPES[s.weights],
         "data": ("synthetic: seeded random-init weights " +
-                 ("as E4M3 codes (N(0, 32) rounded) times row scales near 0.02/32, " if s.weights == "fp8"
-                  else "N(0, 0.02), ") + "synthetic N(0, 1) KV, shuffled pages"),
+                 {"fp8": "as E4M3 codes (N(0, 32) rounded) times row scales near 0.02/32, ",
+                  "fp4": "as E2M1 codes (N(0, 1.5) rounded) times row scales near 0.02/1.5, "}.get(s.weights, "N(0, 0.02), ")) + "synthetic N(0, 1) KV, shuffled pages"),
         "config": {
             "workload": f"{w.name}: {s.n_layers} layers, hidden {s.hidden}, {s.n_q_heads}q/{s.n_kv_heads}kv x "
                         f"{s.head_dim}, {s.n_experts} experts top-{s.top_k} inter {s.inter}, vocab {s.vocab}; "
@@ -448,7 +450,7 @@ def main():
             "algorithmic_bytes_per_launch": round(bytes_step * spl),
             "launch_ms": round(launch_ms, 4),
             "steps_per_launch": spl,
-            "kernel": "mk_megakernel_fp8" if s.weights == "fp8" else "mk_megakernel",
+            "kernel": KERNELS[s.weights],
         },
         "cpu_baseline": cpu,
     }

@@ -73,7 +73,7 @@ typedef struct mk_config {
   int32_t num_pages;          /* pages in each layer's K pool and V pool */
   float rms_eps;              /* RMSNorm epsilon (1e-6) */
   double rope_theta;          /* RoPE base (1e4) */
-  int32_t weight_format;      /* MK_WEIGHTS_BF16 (0) or MK_WEIGHTS_FP8_E4M3 (1), see mk_bind */
+  int32_t weight_format;      /* MK_WEIGHTS_BF16 (0), MK_WEIGHTS_FP8_E4M3 (1) or MK_WEIGHTS_FP4_E2M1 (2), see mk_bind */
 } mk_config;
 
 /* Weight formats.  FP8_E4M3: the LM head, wqkv, wo, w_gate, w_up and w_down
@@ -81,8 +81,11 @@ typedef struct mk_config {
  * bits, subnormals, no infinities) with one fp32 scale per row: the weight is
  * code * scale.  The pages list FP8 weights as a next step (aiweekly.co,
  * paragraph 6) and fix no format; per-row scales are this library's reading.
+ * FP4_E2M1: the same matrices as OCP FP4 E2M1 codes (1 sign, 2 exponent bits
+ * with bias 1, 1 mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), two a
+ * byte (element 2j in the low nibble of byte j), with one fp32 scale per row.
  * Router, norm gains, embedding and the KV cache stay bfloat16. */
-enum { MK_WEIGHTS_BF16 = 0, MK_WEIGHTS_FP8_E4M3 = 1 };
+enum { MK_WEIGHTS_BF16 = 0, MK_WEIGHTS_FP8_E4M3 = 1, MK_WEIGHTS_FP4_E2M1 = 2 };
 
 /* Creates a context for one model shape.  Host only, no GPU call.
  * cfg is copied.  *out receives the context (free with mk_destroy).
@@ -161,6 +164,8 @@ int mk_build_schedule(mk_ctx* ctx, const mk_schedule_params* params, size_t* wor
  *    w_gate, w_up and w_down is one buffer: the [rows][cols] E4M3 codes
  *    (one byte each, same row order as above; an expert tensor's rows are
  *    [n_experts * rows]) followed at byte rows*cols by rows fp32 row scales.
+ *    With MK_WEIGHTS_FP4_E2M1 the same, with cols / 2 bytes of E2M1 codes per
+ *    row and the scales at byte rows*cols/2.
  *  k_pool: device, [n_layers][num_pages][n_kv_heads][page_size][head_dim] bf16.
  *  v_pool: device, [n_layers][num_pages][n_kv_heads][head_dim][page_size] bf16
  *    (dims-major inside a page, the layout the P*V matrix-core product reads).

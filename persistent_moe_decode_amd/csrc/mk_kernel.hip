@@ -25,13 +25,14 @@
 // in fp32 with v_dot2_f32_bf16 and groups of lanes reduce through DPP, at
 // batch >= 2 rows that every token uses run as 16-row matrix-core tiles.
 //
-// This file is compiled twice.  With MK_W8 = 0 it is the kernel for bf16
-// weights; with MK_W8 = 1 (mk_kernel_fp8.hip) the LM head, Wqkv, Wo and the
-// expert gate/up/down matrices are FP8 (OCP E4M3) codes with one fp32 scale
-// per row after each matrix's codes: the row loops convert the codes to bf16
-// in registers (exact: every E4M3 value is a bf16 value), accumulate as for
-// bf16 weights and multiply the row's sum by its scale.  Router, norm gains,
-// embedding and the KV cache stay bf16.
+// This file is compiled three times.  With MK_WFMT = 0 it is the kernel for
+// bf16 weights; with MK_WFMT = 1 (mk_kernel_fp8.hip) or 2 (mk_kernel_fp4.hip)
+// the LM head, Wqkv, Wo and the expert gate/up/down matrices are FP8 (OCP
+// E4M3) or FP4 (OCP E2M1, two codes a byte) codes with one fp32 scale per row
+// after each matrix's codes: the row loops convert the codes to bf16 in
+// registers (exact: every E4M3 and E2M1 value is a bf16 value), accumulate as
+// for bf16 weights and multiply the row's sum by its scale.  Router, norm
+// gains, embedding and the KV cache stay bf16.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -45,17 +46,24 @@ using namespace mk;
 #define DEV __device__ __forceinline__
 #define TASK __device__ __forceinline__
 
-#ifndef MK_W8
-#define MK_W8 0
+#ifndef MK_WFMT
+#define MK_WFMT 0  // weight format: 0 bf16, 1 FP8 E4M3, 2 FP4 E2M1
 #endif
-#if MK_W8
+#if MK_WFMT == 1
 #define MKK(name) name##_fp8
+#elif MK_WFMT == 2
+#define MKK(name) name##_fp4
 #else
 #define MKK(name) name
 #endif
-// bytes per element of the streamed matrices (LM head, Wqkv, Wo, experts)
-constexpr bool kW8 = MK_W8 != 0;
-constexpr int kWB = kW8 ? 1 : 2;
+// the streamed matrices (LM head, Wqkv, Wo, experts): quantized or not, bits per element
+constexpr bool kWQ = MK_WFMT != 0;
+constexpr int kWBits = MK_WFMT == 1 ? 8 : (MK_WFMT == 2 ? 4 : 16);
+// bits per element of a row: WQ (the kernel's quantized format) or bf16
+template <bool WQ>
+constexpr int row_bits() { return WQ ? kWBits : 16; }
+// bytes of a K-element streamed-matrix row in the kernel's format
+DEV constexpr int wrow_bytes(int K) { return K * kWBits / 8; }
 
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
 
@@ -152,42 +160,74 @@ DEV float dot8(const uint4& w, const uint4& x, float acc) {
   return acc;
 }
 
-#if MK_W8
+#if MK_WFMT == 1
 // Two E4M3 codes (bytes 0, 1, or with HI bytes 2, 3 of w) as a bf16 pair, exactly (scale 1).
 template <bool HI>
 DEV uint32_t fp8x2_bf16(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
-// 16 E4M3 codes (one 16-byte chunk) dotted with 16 bf16 inputs (xa: the first 8).
-DEV float dot16w(const uint4& w, const uint4& xa, const uint4& xb, float acc) {
-  acc = dot2(fp8x2_bf16<false>(w.x), xa.x, acc);
-  acc = dot2(fp8x2_bf16<true>(w.x), xa.y, acc);
-  acc = dot2(fp8x2_bf16<false>(w.y), xa.z, acc);
-  acc = dot2(fp8x2_bf16<true>(w.y), xa.w, acc);
-  acc = dot2(fp8x2_bf16<false>(w.z), xb.x, acc);
-  acc = dot2(fp8x2_bf16<true>(w.z), xb.y, acc);
-  acc = dot2(fp8x2_bf16<false>(w.w), xb.z, acc);
-  acc = dot2(fp8x2_bf16<true>(w.w), xb.w, acc);
+// 16 E4M3 codes (one 16-byte chunk) dotted with 16 bf16 inputs (x[0]: the first 8).
+DEV float dotq(const uint4& w, const uint4* x, float acc) {
+  acc = dot2(fp8x2_bf16<false>(w.x), x[0].x, acc);
+  acc = dot2(fp8x2_bf16<true>(w.x), x[0].y, acc);
+  acc = dot2(fp8x2_bf16<false>(w.y), x[0].z, acc);
+  acc = dot2(fp8x2_bf16<true>(w.y), x[0].w, acc);
+  acc = dot2(fp8x2_bf16<false>(w.z), x[1].x, acc);
+  acc = dot2(fp8x2_bf16<true>(w.z), x[1].y, acc);
+  acc = dot2(fp8x2_bf16<false>(w.w), x[1].z, acc);
+  acc = dot2(fp8x2_bf16<true>(w.w), x[1].w, acc);
   return acc;
 }
 
-// The 8 bf16 values of codes 0..7 (lo) or 8..15 (hi) of a 16-byte chunk.
-DEV uint4 fp8x8_bf16(const uint4& w, bool hi) {
-  const uint32_t a = hi ? w.z : w.x, b = hi ? w.w : w.y;
+// The 8 bf16 values of codes 8j .. 8j + 7 of a 16-byte chunk (j = 0, 1).
+DEV uint4 q8_bf16(const uint4& w, int j) {
+  const uint32_t a = j ? w.z : w.x, b = j ? w.w : w.y;
   return make_uint4(fp8x2_bf16<false>(a), fp8x2_bf16<true>(a), fp8x2_bf16<false>(b), fp8x2_bf16<true>(b));
 }
+#elif MK_WFMT == 2
+// The two E2M1 codes of byte B of w (low nibble first) as a bf16 pair, exactly (scale 1).
+template <int B>
+DEV uint32_t fp4x2_bf16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, B));
+}
+
+// The 8 bf16 values of the 8 E2M1 codes of one 32-bit word.
+DEV uint4 fp4x8_bf16(uint32_t w) {
+  return make_uint4(fp4x2_bf16<0>(w), fp4x2_bf16<1>(w), fp4x2_bf16<2>(w), fp4x2_bf16<3>(w));
+}
+
+// 32 E2M1 codes (one 16-byte chunk) dotted with 32 bf16 inputs (x[0..3], 8 each).
+DEV float dotq(const uint4& w, const uint4* x, float acc) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    acc = dot2(fp4x2_bf16<0>(ws[k]), x[k].x, acc);
+    acc = dot2(fp4x2_bf16<1>(ws[k]), x[k].y, acc);
+    acc = dot2(fp4x2_bf16<2>(ws[k]), x[k].z, acc);
+    acc = dot2(fp4x2_bf16<3>(ws[k]), x[k].w, acc);
+  }
+  return acc;
+}
+
+// The 8 bf16 values of codes 8j .. 8j + 7 of a 16-byte chunk (j = 0..3).
+DEV uint4 q8_bf16(const uint4& w, int j) { return fp4x8_bf16(j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w); }
 #endif
 
 // One 16-byte weight chunk dotted with its inputs: 8 bf16 weights with x[0],
-// or (W8) 16 E4M3 codes with x[0], x[1].
-template <bool W8>
+// or (WQ) the chunk's 16 / kWBits * 8 codes with x[0 .. 16 / kWBits - 1].
+template <bool WQ>
 DEV float dotw(const uint4& w, const uint4* x, float acc) {
-#if MK_W8
-  if constexpr (W8) return dot16w(w, x[0], x[1], acc);
+#if MK_WFMT != 0
+  if constexpr (WQ) return dotq(w, x, acc);
 #endif
   return dot8(w, x[0], acc);
 }
+
+// w, passed through an empty volatile asm: its conversion to bf16 inside a loop
+// over tokens then stays in that loop instead of being hoisted out of it as
+// XM times as many live registers.
+DEV void opaque(uint4& w) { asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w)); }
 
 // The thread's index, read through an empty volatile asm: the compiler then
 // cannot hoist per-lane arithmetic out of the persistent task loop, where it
@@ -472,9 +512,9 @@ DEV const gu16* wptr(const KArgs& a, int i) { return (const gu16*)(uintptr_t)a.w
 // a streamed matrix as bytes (bf16 elements, or FP8 codes followed by the rows' fp32 scales)
 typedef const AS_GLOBAL uint8_t gu8;
 DEV const gu8* wbytes(const KArgs& a, int i) { return (const gu8*)(uintptr_t)a.wtab[i]; }
-// row scales of an FP8 matrix of `rows` rows of `cols` codes
+// row scales of a quantized matrix of `rows` rows of `cols` codes
 DEV const AS_GLOBAL float* wscales(const KArgs& a, int i, size_t rows, int cols) {
-  return (const AS_GLOBAL float*)(wbytes(a, i) + rows * (size_t)cols);
+  return (const AS_GLOBAL float*)(wbytes(a, i) + rows * (size_t)wrow_bytes(cols));
 }
 
 // Trace mark k (0..3) of task qi: the clock when thread 0 passes this point.
@@ -752,18 +792,19 @@ DEV void load_row(const Job& job, int i, int li, bool act, uint4 (&wv)[CPL]) {
   }
 }
 
-// A row's sum times its FP8 scale (W8), or as it is (bf16 rows).
-template <bool W8, class Job>
+// A row's sum times its scale (WQ: quantized rows), or as it is (bf16 rows).
+template <bool WQ, class Job>
 DEV float scaled(const Job& job, int i, float v) {
-  if constexpr (W8) return v * job.scale(i);
+  if constexpr (WQ) return v * job.scale(i);
   return v;
 }
 
-// W8: a 16-byte chunk holds 16 codes, so it meets two 16-byte input chunks.
-template <int LPR, int CPL, bool FromLds, bool W8, class Job>
+// WQ: a 16-byte chunk holds 128 / kWBits codes, so it meets XM = 16 / kWBits
+// 16-byte input chunks.
+template <int LPR, int CPL, bool FromLds, bool WQ, class Job>
 DEV void rowdots(int i0, int i1, int maxnx, const Job& job) {
   const int lane = tid() & 63, wave = tid() >> 6;
-  constexpr int RPW = 64 / LPR, XM = W8 ? 2 : 1;
+  constexpr int RPW = 64 / LPR, XM = 16 / row_bits<WQ>();
   const int sub = lane / LPR, li = lane % LPR;
   for (int base = i0; base < i1; base += kWaves * RPW) {
     const int i = base + wave * RPW + sub;
@@ -777,21 +818,25 @@ DEV void rowdots(int i0, int i1, int maxnx, const Job& job) {
       const uint4* xr = job.x(ic, on ? t : 0) + XM * li;
       float acc = 0.f;
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) acc = dotw<W8>(wv[c], xr + XM * LPR * c, acc);
+      for (int c = 0; c < CPL; ++c) {
+        uint4 w = wv[c];
+        if constexpr (WQ) opaque(w);
+        acc = dotw<WQ>(w, xr + XM * LPR * c, acc);
+      }
       acc = group_sum<LPR>(acc);
-      if (on && li == 0) job.emit(i, t, scaled<W8>(job, i, acc));
+      if (on && li == 0) job.emit(i, t, scaled<WQ>(job, i, acc));
     }
   }
 }
 
-// Any row of a multiple of 128 elements: 16 lanes per row (bf16) or 8 (W8),
-// one 16-byte chunk per lane per load.
-template <bool FromLds, bool W8, class Job>
+// Any row of a multiple of 128 elements: 16 lanes per row (bf16), 8 (FP8) or
+// 4 (FP4), one 16-byte chunk per lane per load.
+template <bool FromLds, bool WQ, class Job>
 DEV void rowdots_generic(int K, int i0, int i1, int maxnx, const Job& job) {
-  constexpr int LPR = W8 ? 8 : 16, RPW = 64 / LPR, XM = W8 ? 2 : 1;
+  constexpr int LPR = row_bits<WQ>(), RPW = 64 / LPR, XM = 16 / row_bits<WQ>();  // 128 elements per lane-group chunk
   const int lane = tid() & 63, wave = tid() >> 6;
   const int sub = lane / LPR, li = lane % LPR;
-  const int cpl = K * (W8 ? 1 : 2) / (16 * LPR);
+  const int cpl = K * row_bits<WQ>() / (128 * LPR);
   for (int base = i0; base < i1; base += kWaves * RPW) {
     const int i = base + wave * RPW + sub;
     const bool act = i < i1;
@@ -804,10 +849,10 @@ DEV void rowdots_generic(int K, int i0, int i1, int maxnx, const Job& job) {
       for (int c = 0; c < cpl; ++c) {
         uint4 w[1];
         load_row<FromLds, 1, LPR>(job, ic, li + LPR * c, act, w);
-        acc = dotw<W8>(w[0], xr + XM * LPR * c, acc);
+        acc = dotw<WQ>(w[0], xr + XM * LPR * c, acc);
       }
       acc = group_sum<LPR>(acc);
-      if (on && li == 0) job.emit(i, t, scaled<W8>(job, i, acc));
+      if (on && li == 0) job.emit(i, t, scaled<WQ>(job, i, acc));
     }
   }
 }
@@ -822,17 +867,18 @@ DEV void rowdots_generic(int K, int i0, int i1, int maxnx, const Job& job) {
 // stream from HBM, eight 16-byte loads per lane in flight per batch.  With
 // fewer tiles than waves the columns are split into kp parts whose partial
 // tiles are summed in LDS (red: kMfmaRedBytes of region C) in part order.
-// W8: one 16-byte load holds columns 16 * (l / 16) .. + 15 of a 64-column
-// block, converted to bf16 and contracted as two products (the first and the
-// second 8 of those columns, with the inputs at the same columns): the sum
-// over the block is the same, only its order differs.
+// WQ: one 16-byte load holds XM * 8 consecutive columns of a block of
+// 32 * XM columns (XM = 16 / kWBits), converted to bf16 and contracted as XM
+// products, each with the inputs at the same 8 columns: the sum over the
+// block is the same, only its order differs.
 constexpr int kMfmaBatch = 8;                   // 16-byte loads per lane per batch
 
-template <bool W8, class Job>
+template <bool WQ, class Job>
 DEV void rowdots_mfma(int K, int i0, int i1, int n, const Job& job, float* red) {
   typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
-  constexpr int CB = W8 ? 64 : 32;              // columns per 16-byte load of a 4-lane-group row
+  constexpr int XM = 16 / row_bits<WQ>();       // products (8 columns each) per 16-byte load
+  constexpr int CB = 32 * XM;                   // columns per block (one load per lane)
   const int lane = tid() & 63, wave = tid() >> 6;
   const int r = lane & 15, grp = lane >> 4;
   const int ntile = (i1 - i0 + 15) / 16;
@@ -845,7 +891,7 @@ DEV void rowdots_mfma(int K, int i0, int i1, int n, const Job& job, float* red) 
     const int tile = it / kp, part = it - tile * kp;
     const int row = i0 + tile * 16 + r;
     const gu4* wr = job.row(row < i1 ? row : i0) + (size_t)part * (kl / (CB / 4)) + grp;
-    const uint4* xr = xb + (size_t)part * (kl / 8) + (W8 ? 2 : 1) * grp;
+    const uint4* xr = xb + (size_t)part * (kl / 8) + XM * grp;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     for (int kb = 0; kb < kl / CB; kb += kMfmaBatch) {
       uint4 wa[kMfmaBatch];
@@ -853,27 +899,23 @@ DEV void rowdots_mfma(int K, int i0, int i1, int n, const Job& job, float* red) 
       for (int u = 0; u < kMfmaBatch; ++u) wa[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(wr + 4 * (kb + u)));
 #pragma unroll
       for (int u = 0; u < kMfmaBatch; ++u) {
-#if MK_W8
-        if constexpr (W8) {
-          const uint4 xl = r < n ? xr[8 * (kb + u)] : make_uint4(0, 0, 0, 0);
-          const uint4 xh = r < n ? xr[8 * (kb + u) + 1] : make_uint4(0, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fp8x8_bf16(wa[u], false)),
-                                                        __builtin_bit_cast(bf16x8_t, xl), acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fp8x8_bf16(wa[u], true)),
-                                                        __builtin_bit_cast(bf16x8_t, xh), acc, 0, 0, 0);
-          continue;
-        }
+#pragma unroll
+        for (int j = 0; j < XM; ++j) {
+          const uint4 xv = r < n ? xr[4 * XM * (kb + u) + j] : make_uint4(0, 0, 0, 0);
+          uint4 av = wa[u];
+#if MK_WFMT != 0
+          if constexpr (WQ) av = q8_bf16(wa[u], j);
 #endif
-        const uint4 xv = r < n ? xr[4 * (kb + u)] : make_uint4(0, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wa[u]),
-                                                      __builtin_bit_cast(bf16x8_t, xv), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                        __builtin_bit_cast(bf16x8_t, xv), acc, 0, 0, 0);
+        }
       }
     }
     if (kp == 1) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int rq = i0 + tile * 16 + 4 * grp + q;
-        if (rq < i1 && r < n) job.emit(rq, r, scaled<W8>(job, rq, acc[q]));
+        if (rq < i1 && r < n) job.emit(rq, r, scaled<WQ>(job, rq, acc[q]));
       }
     } else {
 #pragma unroll
@@ -887,61 +929,69 @@ DEV void rowdots_mfma(int K, int i0, int i1, int n, const Job& job, float* red) 
       const int rq = i0 + tile * 16 + rt;
       float v = 0.f;
       for (int part = 0; part < kp; ++part) v += red[(tile * kp + part) * 256 + rt * 16 + tok];
-      if (rq < i1 && tok < n) job.emit(rq, tok, scaled<W8>(job, rq, v));
+      if (rq < i1 && tok < n) job.emit(rq, tok, scaled<WQ>(job, rq, v));
     }
     __syncthreads();
   }
 }
 
-// Rows [i0, i1) of a job with K-element rows; W8: the rows are FP8 codes.
-template <bool FromLds, bool W8, class Job>
+// Rows [i0, i1) of a job with K-element rows; WQ: the rows are in the
+// kernel's quantized format.
+template <bool FromLds, bool WQ, class Job>
 DEV void rowdots_range(int K, int i0, int i1, int maxnx, const Job& job) {
   const int nj = i1 - i0;
   if (nj <= 0 || maxnx <= 0) return;
   if constexpr (!FromLds && Job::kDense)
-    if (maxnx >= 2 && K % ((W8 ? 64 : 32) * kMfmaBatch) == 0) return rowdots_mfma<W8>(K, i0, i1, maxnx, job, job.red);
-  const int ch = K * (W8 ? 1 : 2) / 16;  // 16-byte chunks per row
-  if (nj <= 8 && ch == 512) return rowdots<64, 8, FromLds, W8>(i0, i1, maxnx, job);
-  if (nj <= 8 && ch == 256) return rowdots<64, 4, FromLds, W8>(i0, i1, maxnx, job);
+    if (maxnx >= 2 && K % (32 * (16 / row_bits<WQ>()) * kMfmaBatch) == 0)
+      return rowdots_mfma<WQ>(K, i0, i1, maxnx, job, job.red);
+  const int ch = K * row_bits<WQ>() / 128;  // 16-byte chunks per row
+  if (nj <= 8 && ch == 512) return rowdots<64, 8, FromLds, WQ>(i0, i1, maxnx, job);
+  if (nj <= 8 && ch == 256) return rowdots<64, 4, FromLds, WQ>(i0, i1, maxnx, job);
   if (nj <= 16 || ch > 256) {
     switch (ch) {
-      case 64: return rowdots<32, 2, FromLds, W8>(i0, i1, maxnx, job);
-      case 96: return rowdots<32, 3, FromLds, W8>(i0, i1, maxnx, job);
-      case 128: return rowdots<32, 4, FromLds, W8>(i0, i1, maxnx, job);
-      case 256: return rowdots<32, 8, FromLds, W8>(i0, i1, maxnx, job);
-      case 512: return rowdots<32, 16, FromLds, W8>(i0, i1, maxnx, job);
+      case 64: return rowdots<32, 2, FromLds, WQ>(i0, i1, maxnx, job);
+      case 96: return rowdots<32, 3, FromLds, WQ>(i0, i1, maxnx, job);
+      case 128: return rowdots<32, 4, FromLds, WQ>(i0, i1, maxnx, job);
+      case 256: return rowdots<32, 8, FromLds, WQ>(i0, i1, maxnx, job);
+      case 512: return rowdots<32, 16, FromLds, WQ>(i0, i1, maxnx, job);
       default: break;
     }
   }
   switch (ch) {
+    case 4:
+      if constexpr (WQ && kWBits == 4) return rowdots<4, 1, FromLds, WQ>(i0, i1, maxnx, job);
+      break;
     case 8:
-      if constexpr (W8) return rowdots<8, 1, FromLds, W8>(i0, i1, maxnx, job);
+      if constexpr (WQ) return rowdots<8, 1, FromLds, WQ>(i0, i1, maxnx, job);
       break;
-    case 16: return rowdots<16, 1, FromLds, W8>(i0, i1, maxnx, job);
-    case 32: return rowdots<16, 2, FromLds, W8>(i0, i1, maxnx, job);
+    case 16: return rowdots<16, 1, FromLds, WQ>(i0, i1, maxnx, job);
+    case 24:
+      if constexpr (WQ && kWBits == 4) return rowdots<8, 3, FromLds, WQ>(i0, i1, maxnx, job);
+      break;
+    case 32: return rowdots<16, 2, FromLds, WQ>(i0, i1, maxnx, job);
     case 48:
-      if constexpr (W8) return rowdots<16, 3, FromLds, W8>(i0, i1, maxnx, job);
+      if constexpr (WQ) return rowdots<16, 3, FromLds, WQ>(i0, i1, maxnx, job);
       break;
-    case 64: return rowdots<16, 4, FromLds, W8>(i0, i1, maxnx, job);
-    case 96: return rowdots<16, 6, FromLds, W8>(i0, i1, maxnx, job);
-    case 128: return rowdots<16, 8, FromLds, W8>(i0, i1, maxnx, job);
-    case 256: return rowdots<16, 16, FromLds, W8>(i0, i1, maxnx, job);
+    case 64: return rowdots<16, 4, FromLds, WQ>(i0, i1, maxnx, job);
+    case 96: return rowdots<16, 6, FromLds, WQ>(i0, i1, maxnx, job);
+    case 128: return rowdots<16, 8, FromLds, WQ>(i0, i1, maxnx, job);
+    case 256: return rowdots<16, 16, FromLds, WQ>(i0, i1, maxnx, job);
     default: break;
   }
-  rowdots_generic<FromLds, W8>(K, i0, i1, maxnx, job);
+  rowdots_generic<FromLds, WQ>(K, i0, i1, maxnx, job);
 }
 
 // All rows of a job from HBM.
-template <bool W8, class Job>
+template <bool WQ, class Job>
 DEV void run_rowdots(int K, int njobs, int maxnx, const Job& job) {
-  rowdots_range<false, W8>(K, 0, njobs, maxnx, job);
+  rowdots_range<false, WQ>(K, 0, njobs, maxnx, job);
 }
 
 // Rows [0, npf) from the LDS tile, the rest from HBM.
-template <bool W8, class Job>
+template <bool WQ, class Job>
 DEV void run_rowdots_pf(int K, int njobs, int npf, int maxnx, const Job& job) {
-  rowdots_range<true, W8>(K, 0, npf, maxnx, job);
-  rowdots_range<false, W8>(K, npf, njobs, maxnx, job);
+  rowdots_range<true, WQ>(K, 0, npf, maxnx, job);
+  rowdots_range<false, WQ>(K, npf, njobs, maxnx, job);
 }
 
 // ---------------------------------------------------------------------------
@@ -1142,7 +1192,7 @@ DEV void prefetch_to_lds(const gu8* src, uint8_t* dst_lds, int nbytes) {
 // router rows bf16): start and bytes per row.
 DEV const gu8* pre_rows_src(const KArgs& a, int layer, int r0, int* rowb) {
   if (r0 < a.qkv_rows) {
-    *rowb = a.H * kWB;
+    *rowb = wrow_bytes(a.H);
     return wbytes(a, widx(layer, WL_QKV)) + (size_t)r0 * *rowb;
   }
   *rowb = a.H * 2;
@@ -1155,7 +1205,7 @@ DEV int task_prefetch(const KArgs& a, const Task& t, const Lds& s, int qi) {
   if (t.op == OP_PRE) {
     src = pre_rows_src(a, t.layer, t.r0, &rowb);
   } else if (t.op == OP_WO) {
-    rowb = a.nq * a.d * kWB;
+    rowb = wrow_bytes(a.nq * a.d);
     src = wbytes(a, widx(t.layer, WL_O)) + (size_t)t.r0 * rowb;
   } else {
     return 0;
@@ -1211,8 +1261,8 @@ TASK void task_pre(const KArgs& a, const Task& t, const Lds& s, int qi, int npf)
   j.red = (float*)s.C;
   if (t.r0 < a.qkv_rows) {
     j.W = wbytes(a, widx(l, WL_QKV));
-    j.rowb = a.H * kWB;
-    if constexpr (kW8) j.sc = wscales(a, widx(l, WL_QKV), a.qkv_rows, a.H);
+    j.rowb = wrow_bytes(a.H);
+    if constexpr (kWQ) j.sc = wscales(a, widx(l, WL_QKV), a.qkv_rows, a.H);
     j.r0 = t.r0;
     j.out = a.qkv + (size_t)l * a.max_batch * a.qkv_rows + t.r0;
     j.ld = a.qkv_rows;
@@ -1226,7 +1276,7 @@ TASK void task_pre(const KArgs& a, const Task& t, const Lds& s, int qi, int npf)
     j.ld = a.E;
   }
   // Wqkv rows in the kernel's weight format, router rows always bf16
-  if (t.r0 < a.qkv_rows) run_rowdots_pf<kW8>(a.H, t.r1 - t.r0, npf, a.n, j);
+  if (t.r0 < a.qkv_rows) run_rowdots_pf<kWQ>(a.H, t.r1 - t.r0, npf, a.n, j);
   else run_rowdots_pf<false>(a.H, t.r1 - t.r0, npf, a.n, j);
   mark(a, qi, 2);
 }
@@ -1837,7 +1887,7 @@ struct JobGateUp {
   DEV const gu4* row(int i) const {
     int r;
     const int u = urow(i, &r);
-    return (const gu4*)(((i & 1) ? wu : wg) + ((size_t)tk->U[u] * I + r) * H * kWB);
+    return (const gu4*)(((i & 1) ? wu : wg) + ((size_t)tk->U[u] * I + r) * wrow_bytes(H));
   }
   DEV float scale(int i) const {
     int r;
@@ -1869,7 +1919,7 @@ DEV void gateup_range(const KArgs& a, const Lds& s, int l, const uint16_t* xs, i
   j.tk = tk;
   j.wg = wbytes(a, widx(l, WL_GATE));
   j.wu = wbytes(a, widx(l, WL_UP));
-  if constexpr (kW8) {
+  if constexpr (kWQ) {
     j.sg = wscales(a, widx(l, WL_GATE), (size_t)a.E * a.I, a.H);
     j.su = wscales(a, widx(l, WL_UP), (size_t)a.E * a.I, a.H);
   }
@@ -1884,7 +1934,7 @@ DEV void gateup_range(const KArgs& a, const Lds& s, int l, const uint16_t* xs, i
   for (int64_t v0 = va; v0 < vb; v0 += kGuPass) {
     const int nvr = (int)((vb - v0) < kGuPass ? (vb - v0) : kGuPass);
     j.v0 = v0;
-    run_rowdots<kW8>(a.H, 2 * nvr, mt, j);
+    run_rowdots<kWQ>(a.H, 2 * nvr, mt, j);
     __syncthreads();
     for (int e = tid(); e < nvr * mt; e += kThreads) {
       const int vi = e / mt, tt = e % mt;
@@ -1980,7 +2030,7 @@ struct JobDown {
   int r0, H, I, nU, maxBK;
   DEV const gu4* row(int i) const {
     const int rr = i / nU, u = i % nU;
-    return (const gu4*)(W + ((size_t)tk->U[u] * H + r0 + rr) * I * kWB);
+    return (const gu4*)(W + ((size_t)tk->U[u] * H + r0 + rr) * wrow_bytes(I));
   }
   DEV float scale(int i) const {
     const int rr = i / nU, u = i % nU;
@@ -2026,7 +2076,7 @@ TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have
   JobDown jd;
   jd.tk = tk;
   jd.W = wbytes(a, widx(l, WL_DOWN));
-  if constexpr (kW8) jd.sc = wscales(a, widx(l, WL_DOWN), (size_t)a.E * a.H, a.I);
+  if constexpr (kWQ) jd.sc = wscales(a, widx(l, WL_DOWN), (size_t)a.E * a.H, a.I);
   jd.hs = xs;
   jd.contrib = contrib;
   jd.r0 = t.r0;
@@ -2035,10 +2085,10 @@ TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have
   jd.nU = tk->nU;
   jd.maxBK = maxBK;
   // 16-byte chunks per lane of a down row (16 lanes per row)
-  const int nd = nr * jd.nU, cpl = a.I * kWB / 256;
+  const int nd = nr * jd.nU, cpl = wrow_bytes(a.I) / 256;
   // waves 1..7 hold them (wave 0, whose thread 0 polls the flags, loads none)
   constexpr int kGroupRows = (kWaves - 1) * 4;
-  const int npre = ((a.I * kWB) % 256 == 0 && cpl <= kDownC) ? min(nd, kDownGroups * kGroupRows) : 0;
+  const int npre = (wrow_bytes(a.I) % 256 == 0 && cpl <= kDownC) ? min(nd, kDownGroups * kGroupRows) : 0;
   // the down rows go out once nine tenths of the gate/up tasks are done: issued
   // earlier, by the units that finish first, they take bandwidth from the last
   // gate/up tasks, which every output task waits for
@@ -2062,8 +2112,8 @@ TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have
   mark(a, qi, 0);
   // expert down projections: the register rows, then the rest from HBM
   const int mt = tk->maxtok;
-  constexpr int XM = kW8 ? 2 : 1;                    // input chunks per weight chunk
-  constexpr int kDC = kW8 ? kDownC / 2 : kDownC;     // chunks per lane of a 768-element row
+  constexpr int XM = 16 / kWBits;                    // input chunks per weight chunk
+  constexpr int kDC = kDownC * kWBits / 16;          // chunks per lane of a 768-element row (bf16, FP8)
   if (cpl == kDC) {
     // every chunk present: a row's LDS reads go out together, then the
     // arithmetic (a guard per chunk would make each read wait for the last)
@@ -2082,9 +2132,9 @@ TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have
           for (int m = 0; m < XM; ++m) xv[XM * c + m] = xr[XM * 16 * c + m];
         float acc = 0.f;
 #pragma unroll
-        for (int c = 0; c < kDC; ++c) acc = dotw<kW8>(dp[g][c], xv + XM * c, acc);
+        for (int c = 0; c < kDC; ++c) acc = dotw<kWQ>(dp[g][c], xv + XM * c, acc);
         acc = group_sum<16>(acc);
-        if (on && li == 0) jd.emit(i, tt, scaled<kW8>(jd, i, acc));
+        if (on && li == 0) jd.emit(i, tt, scaled<kWQ>(jd, i, acc));
       }
     }
   } else {
@@ -2099,13 +2149,13 @@ TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have
         float acc = 0.f;
 #pragma unroll
         for (int c = 0; c < kDownC; ++c)
-          if (c < cpl) acc = dotw<kW8>(dp[g][c], xr + XM * 16 * c, acc);
+          if (c < cpl) acc = dotw<kWQ>(dp[g][c], xr + XM * 16 * c, acc);
         acc = group_sum<16>(acc);
-        if (on && li == 0) jd.emit(i, tt, scaled<kW8>(jd, i, acc));
+        if (on && li == 0) jd.emit(i, tt, scaled<kWQ>(jd, i, acc));
       }
     }
   }
-  rowdots_range<false, kW8>(a.I, npre, nd, mt, jd);
+  rowdots_range<false, kWQ>(a.I, npre, nd, mt, jd);
   mark(a, qi, 1);
   // batch 1, wave 0 alone storing the residual rows: meanwhile waves 1..7
   // copy the weight tile of the PRE task that follows on this unit into LDS
@@ -2151,8 +2201,8 @@ constexpr int kWoC = 16;
 TASK void task_wo(const KArgs& a, const Task& t, const Lds& s, int qi, int npf) {
   const int l = t.layer, AD = a.nq * a.d, nr = t.r1 - t.r0, n = a.n;
   const int lane = tid() & 63, wave = tid() >> 6, li = lane & 31;
-  constexpr int kWC = kW8 ? kWoC / 2 : kWoC;  // chunks per lane of a register row
-  const int rowb = AD * kWB;
+  constexpr int kWC = kWoC * kWBits / 16;  // chunks per lane of a register row
+  const int rowb = wrow_bytes(AD);
   const int nreg = rowb == 32 * kWC * 16 && n == 1 ? min(nr - npf, (kWaves - 1) * 2) : 0;
   const int ir = npf + (wave >= 1 ? (wave - 1) * 2 + (lane >> 5) : nreg);  // this lane's register row
   const bool act = ir < npf + nreg;
@@ -2173,24 +2223,24 @@ TASK void task_wo(const KArgs& a, const Task& t, const Lds& s, int qi, int npf) 
   j.npf = npf;
   j.red = (float*)s.C;
   j.W = W;
-  if constexpr (kW8) j.sc = wscales(a, widx(l, WL_O), a.H, AD);
+  if constexpr (kWQ) j.sc = wscales(a, widx(l, WL_O), a.H, AD);
   j.r0 = t.r0;
   j.K = AD;
   j.rowb = rowb;
   j.xs = xs;
   j.out = a.wo_out + (size_t)l * a.max_batch * a.H + t.r0;
   j.ld = a.H;
-  rowdots_range<true, kW8>(AD, 0, npf, n, j);
-  constexpr int XM = kW8 ? 2 : 1;
+  rowdots_range<true, kWQ>(AD, 0, npf, n, j);
+  constexpr int XM = 16 / kWBits;
   for (int b = 0; b < n; ++b) {
     const uint4* xr = (const uint4*)(xs + (size_t)b * AD) + XM * li;
     float acc = 0.f;
 #pragma unroll
-    for (int c = 0; c < kWC; ++c) acc = dotw<kW8>(wr[c], xr + XM * 32 * c, acc);
+    for (int c = 0; c < kWC; ++c) acc = dotw<kWQ>(wr[c], xr + XM * 32 * c, acc);
     acc = group_sum<32>(acc);
-    if (act && li == 0) j.emit(ir, b, scaled<kW8>(j, ir, acc));
+    if (act && li == 0) j.emit(ir, b, scaled<kWQ>(j, ir, acc));
   }
-  rowdots_range<false, kW8>(AD, npf + nreg, nr, n, j);
+  rowdots_range<false, kWQ>(AD, npf + nreg, nr, n, j);
   mark(a, qi, 1);
 }
 
@@ -2206,7 +2256,7 @@ struct JobLM {
   const uint16_t* xs;
   float* lmv;
   float* logits;
-  DEV const gu4* row(int i) const { return (const gu4*)(W + (size_t)(r0 + i) * K * kWB); }
+  DEV const gu4* row(int i) const { return (const gu4*)(W + (size_t)(r0 + i) * wrow_bytes(K)); }
   DEV float scale(int i) const { return sc[r0 + i]; }
   DEV int nx(int) const { return 1 << 30; }
   DEV const uint4* x(int, int t) const { return (const uint4*)(xs + (size_t)t * K); }
@@ -2269,7 +2319,7 @@ TASK void task_lmhead(const KArgs& a, const Task& t, const Lds& s, int qi) {
   mark(a, qi, 0);
   JobLM j;
   j.W = wbytes(a, W_LM_HEAD);
-  if constexpr (kW8) j.sc = wscales(a, W_LM_HEAD, a.V, a.H);
+  if constexpr (kWQ) j.sc = wscales(a, W_LM_HEAD, a.V, a.H);
   j.K = a.H;
   j.V = a.V;
   j.maxB = a.max_batch;
@@ -2288,7 +2338,7 @@ TASK void task_lmhead(const KArgs& a, const Task& t, const Lds& s, int qi) {
   for (int p0 = 0; p0 < nr; p0 += kLmPass) {
     const int np = min(kLmPass, nr - p0);
     j.r0 = t.r0 + p0;
-    run_rowdots<kW8>(a.H, np, a.n, j);
+    run_rowdots<kWQ>(a.H, np, a.n, j);
     __syncthreads();
 #pragma unroll
     for (int b = 0; b < kMaxBatch; ++b) {
@@ -2398,7 +2448,7 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) MKK(mk_megakernel)(KAr
   }
 }
 
-#if !MK_W8
+#if MK_WFMT == 0
 // One copy of what follows (not per weight format): the fill kernel and the static workspace.
 __global__ void mk_fill_u32_kernel(uint32_t* p, uint32_t v, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + tid(); i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
@@ -2443,7 +2493,7 @@ extern "C" int mkk_scratch(int* device, void** ptr) {
   *ptr = addr[dev];
   return 0;
 }
-#endif  // !MK_W8
+#endif  // MK_WFMT == 0
 
 extern "C" int MKK(mkk_launch_step)(const KArgs* a, int grid, size_t lds_bytes, hipStream_t stream) {
   static size_t attr_bytes = 0;

@@ -146,7 +146,7 @@ def _i32p(arr):
     return arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
 
 
-WEIGHT_FORMATS = {"bf16": 0, "fp8": 1}   # MK_WEIGHTS_BF16, MK_WEIGHTS_FP8_E4M3
+WEIGHT_FORMATS = {"bf16": 0, "fp8": 1, "fp4": 2}   # MK_WEIGHTS_BF16, _FP8_E4M3, _FP4_E2M1
 
 
 def config_from_shape(shape, max_batch: int, max_pages_per_seq: int, num_pages: int) -> MkConfig:

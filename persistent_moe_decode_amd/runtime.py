@@ -64,6 +64,13 @@ def _fp8_gen(kind: int, layer: int):
     return lambda s, c, p: lib.synth_fp8_codes(synth.SEED_WEIGHTS, t, s, c, p)
 
 
+def _fp4_gen(kind: int, layer: int):
+    """Packed E2M1 codes by byte: byte i holds elements 2i (low nibble) and 2i + 1."""
+    t = synth.tid(kind, layer if kind in synth.LAYER_KINDS else 0)
+    lib = synth.lib()
+    return lambda s, c, p: lib.synth_fp4_codes(synth.SEED_WEIGHTS, t, 2 * s, 2 * c, p)
+
+
 class DeviceDecoder:
     """All device state of one workload, bound to one mk context."""
 
@@ -93,14 +100,16 @@ class DeviceDecoder:
             for item in order:
                 kind, layer = (item, 0) if isinstance(item, int) else item
                 if s.quantized(kind):
-                    # FP8: the E4M3 codes, then one fp32 scale per row, in one buffer
+                    # FP8 / FP4: the E4M3 / packed E2M1 codes, then one fp32 scale per row, in one buffer
                     shp = s.weight_shape(kind)
-                    ncode = int(np.prod(shp))
+                    nel = int(np.prod(shp))
+                    fp4 = s.weights == "fp4"
+                    ncode = nel // 2 if fp4 else nel
                     t = torch.empty(s.weight_nbytes(kind), dtype=torch.uint8, device=self.dev)
-                    stager.fill(t[:ncode], _fp8_gen(kind, layer), esize=1)
+                    stager.fill(t[:ncode], (_fp4_gen if fp4 else _fp8_gen)(kind, layer), esize=1)
                     idx = layer if kind in synth.LAYER_KINDS else 0
-                    sc = synth.fp8_scales(synth.SEED_WEIGHTS, synth.tid(synth.FP8_SCALE_KIND + kind, idx), 0,
-                                          ncode // shp[-1])
+                    scales = synth.fp4_scales if fp4 else synth.fp8_scales
+                    sc = scales(synth.SEED_WEIGHTS, synth.tid(synth.FP8_SCALE_KIND + kind, idx), 0, nel // shp[-1])
                     t[ncode:].copy_(torch.from_numpy(sc.view(np.uint8)))
                 else:
                     t = torch.empty(s.weight_shape(kind), dtype=torch.bfloat16, device=self.dev)

@@ -105,7 +105,7 @@ def kernel_src_hash() -> str:
     import hashlib
     csrc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "persistent_moe_decode_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("mk_kernel.hip", "mk_kernel_fp8.hip", "mk_host.cpp", "mk_types.h"):
+    for f in ("mk_kernel.hip", "mk_kernel_fp8.hip", "mk_kernel_fp4.hip", "mk_host.cpp", "mk_types.h"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -361,6 +361,12 @@ def test_default_split_follows_both_bounds():
         c = _ctx(sq, batch, 4, 8)
         c.build_schedule(256, hint)
         assert c.info().n_attn == want, (batch, hint, c.info().n_attn)
+    # FP4 weights take the FP8 split (measured best at 8K, batch 1)
+    s4 = replace(s, weights="fp4")
+    for batch, hint, want in ((1, 8256, 103), (8, 12780, 112), (1, 262160, 230)):
+        c = _ctx(s4, batch, 4, 8)
+        c.build_schedule(256, hint)
+        assert c.info().n_attn == want, (batch, hint, c.info().n_attn)
 
 
 def test_schedule_params_router_units():
