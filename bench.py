@@ -431,7 +431,7 @@ def main():
         "dtype": DTYPES[s.weights],
         "data": ("synthetic: seeded random-init weights " +
                  {"fp8": "as E4M3 codes (N(0, 32) rounded) times row scales near 0.02/32, ",
-                  "fp4": "as E2M1 codes (N(0, 1.5) rounded) times row scales near 0.02/1.5, "}.get(s.weights, "N(0, 0.02), ")) + "synthetic N(0, 1) KV, shuffled pages"),
+                  "fp4": "as E2M1 codes (N(0, 1.5) rounded) times row scales near 0.02/1.5, "}.get(s.weights, "N(0, 0.02), ") + "synthetic N(0, 1) KV, shuffled pages"),
         "config": {
             "workload": f"{w.name}: {s.n_layers} layers, hidden {s.hidden}, {s.n_q_heads}q/{s.n_kv_heads}kv x "
                         f"{s.head_dim}, {s.n_experts} experts top-{s.top_k} inter {s.inter}, vocab {s.vocab}; "
