@@ -1827,8 +1827,10 @@ DEV void attn_task(const KArgs& a, const Task& t, const Lds& s, int qi) {
 // attention task of the layer, which waits for all of them, reads them from
 // the pages.  In other steps the task only signals.
 TASK void task_kvw(const KArgs& a, const Task& t, const Lds& s, int qi) {
+  if (a.kv_sync && !wait_counter(a, t.wait[0], t.fanin[0], qi, s.flags + 0)) return;
+  // the trace's ready time: after the wait, or at once in a plain decode step (nothing to write)
+  if (a.trace && tid() == 0 && qi < a.trace_cap) a.trace[kTraceWords * (size_t)qi + 1] = wall_clock64();
   if (!a.kv_sync) return;
-  if (!wait_counter(a, t.wait[0], t.fanin[0], qi, s.flags + 0)) return;
   const int m = t.idx, b = m / a.nkv, g = m % a.nkv;
   if (b >= a.n) return;
   const int D = a.d, half = D / 2, ps = a.ps, l = t.layer;

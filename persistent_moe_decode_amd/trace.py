@@ -10,9 +10,11 @@ rotated and new K/V written, copied pages landed, positions done, partial
 stored]; GATEUP [top-k selected (wave 0), routing tables built, norm done, own rows done];
 GUTAIL [top-k selected (wave 0), norm done, pool items done];
 OUT [h loaded, wave 0's down rows done, all down rows done, residual rows stored]; WO [attention output loaded, rows done];
-LMHEAD [norm done, rows done, local argmax done].  Tasks that wait inside
-their body (ATTN, GATEUP, OUT, WO) record as "ready" the moment their inputs
-were there (for GATEUP: the epoch tags of the router logits matched).
+LMHEAD [norm done, rows done, local argmax done]; KVW none.  Tasks that wait
+inside their body (ATTN, GATEUP, OUT, WO, KVW) record as "ready" the moment
+their inputs were there (for GATEUP: the epoch tags of the router logits
+matched); a KVW task in a plain decode step waits for nothing.  A task that gave
+up on its wait (abort or time-out) leaves its ready word zero.
 """
 from __future__ import annotations
 
@@ -26,9 +28,18 @@ TICK_US = 0.01  # s_memrealtime runs at 100 MHz
 WORDS = 8
 
 
+def _ready_filled(rec: np.ndarray) -> np.ndarray:
+    """Records as int64 [tasks][WORDS], a ready word never written (a task that gave up on its wait)
+    taken as its fetch time."""
+    rec = rec.astype(np.int64).reshape(-1, WORDS).copy()
+    unset = rec[:, 1] == 0
+    rec[unset, 1] = rec[unset, 0]
+    return rec
+
+
 def summarize(tasks: np.ndarray, qoff: np.ndarray, rec: np.ndarray) -> dict:
     """Per op kind: mean wait, busy time and phase durations (us); per layer span; overall span."""
-    rec = rec.astype(np.int64).reshape(-1, WORDS)
+    rec = _ready_filled(rec)
     t0 = rec[:, 0].min()
     start, ready, end = (rec[:, 0] - t0) * TICK_US, (rec[:, 1] - t0) * TICK_US, (rec[:, 6] - t0) * TICK_US
     ops = tasks[:, 0]
@@ -71,7 +82,7 @@ def summarize(tasks: np.ndarray, qoff: np.ndarray, rec: np.ndarray) -> dict:
 
 def perfetto(tasks: np.ndarray, qoff: np.ndarray, rec: np.ndarray) -> dict:
     """Chrome/Perfetto trace events: one track per compute unit, wait and busy slices."""
-    rec = rec.astype(np.int64).reshape(-1, WORDS)
+    rec = _ready_filled(rec)
     t0 = rec[:, 0].min()
     ev = []
     for cu in range(len(qoff) - 1):
