@@ -2043,12 +2043,13 @@ struct JobDown {
   DEV void emit(int i, int t, float v) const { contrib[(size_t)(i / nU) * maxBK + tk->pair[i % nU][t]] = v; }
 };
 
-// Down-projection rows held in registers across the gate/up wait: 16 lanes
-// per row, up to kDownC 16-byte chunks per lane (rows up to 128 * kDownC
-// elements), kDownGroups groups of 4 rows per wave (the 96 rows of a 12-row
-// task at 8 experts fit).
+// Down-projection rows held in registers across the gate/up wait: kDownL
+// lanes per row (16; 8 for FP4, whose 768-element rows are 24 chunks), up to
+// kDownC 16-byte chunks per lane, kDownGroups groups of 64 / kDownL rows per
+// wave (the 96 rows of a 12-row task at 8 experts fit).
 constexpr int kDownC = 6;
 constexpr int kDownGroups = 4;
+constexpr int kDownL = kWBits == 4 ? 8 : 16;
 
 // Output tasks wait for their inputs themselves: the residual rows and the
 // top-k (from LDS, or computed once the router rows are done) first; the
@@ -2086,17 +2087,17 @@ TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have
   jd.I = a.I;
   jd.nU = tk->nU;
   jd.maxBK = maxBK;
-  // 16-byte chunks per lane of a down row (16 lanes per row)
-  const int nd = nr * jd.nU, cpl = wrow_bytes(a.I) / 256;
+  // 16-byte chunks per lane of a down row (kDownL lanes per row)
+  const int nd = nr * jd.nU, cpl = wrow_bytes(a.I) / (16 * kDownL);
   // waves 1..7 hold them (wave 0, whose thread 0 polls the flags, loads none)
-  constexpr int kGroupRows = (kWaves - 1) * 4;
-  const int npre = (wrow_bytes(a.I) % 256 == 0 && cpl <= kDownC) ? min(nd, kDownGroups * kGroupRows) : 0;
+  constexpr int kGroupRows = (kWaves - 1) * (64 / kDownL);
+  const int npre = (wrow_bytes(a.I) % (16 * kDownL) == 0 && cpl <= kDownC) ? min(nd, kDownGroups * kGroupRows) : 0;
   // the down rows go out once nine tenths of the gate/up tasks are done: issued
   // earlier, by the units that finish first, they take bandwidth from the last
   // gate/up tasks, which every output task waits for
   if (!wait_counter_part(a, t.wait[0], t.fanin[0], (t.fanin[0] * 9 + 9) / 10, qi, s.flags + 0)) return kWaves;
-  const int lane = tid() & 63, wave = tid() >> 6, li = lane & 15;
-  const int ig = wave >= 1 ? (wave - 1) * 4 + (lane >> 4) : kDownGroups * kGroupRows;  // row within a group
+  const int lane = tid() & 63, wave = tid() >> 6, li = lane % kDownL;
+  const int ig = wave >= 1 ? (wave - 1) * (64 / kDownL) + lane / kDownL : kDownGroups * kGroupRows;  // row within a group
   uint4 dp[kDownGroups][kDownC];
 #pragma unroll
   for (int g = 0; g < kDownGroups; ++g) {
@@ -2105,7 +2106,7 @@ TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have
     const gu4* wr = jd.row(act ? i : 0) + li;
 #pragma unroll
     for (int c = 0; c < kDownC; ++c)
-      dp[g][c] = __builtin_bit_cast(uint4, act && c < cpl ? __builtin_nontemporal_load(wr + 16 * c) : u32x4_v{0, 0, 0, 0});
+      dp[g][c] = __builtin_bit_cast(uint4, act && c < cpl ? __builtin_nontemporal_load(wr + kDownL * c) : u32x4_v{0, 0, 0, 0});
   }
   if (!wait_counter(a, t.wait[0], t.fanin[0], qi, s.flags + 0)) return kWaves;
   if (a.trace && tid() == 0 && qi < a.trace_cap) a.trace[kTraceWords * (size_t)qi + 1] = wall_clock64();
@@ -2115,7 +2116,7 @@ TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have
   // expert down projections: the register rows, then the rest from HBM
   const int mt = tk->maxtok;
   constexpr int XM = 16 / kWBits;                    // input chunks per weight chunk
-  constexpr int kDC = kDownC * kWBits / 16;          // chunks per lane of a 768-element row (bf16, FP8)
+  constexpr int kDC = 768 * kWBits / (128 * kDownL);  // chunks per lane of a 768-element row
   if (cpl == kDC) {
     // every chunk present: a row's LDS reads go out together, then the
     // arithmetic (a guard per chunk would make each read wait for the last)
@@ -2131,11 +2132,11 @@ TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have
 #pragma unroll
         for (int c = 0; c < kDC; ++c)
 #pragma unroll
-          for (int m = 0; m < XM; ++m) xv[XM * c + m] = xr[XM * 16 * c + m];
+          for (int m = 0; m < XM; ++m) xv[XM * c + m] = xr[XM * kDownL * c + m];
         float acc = 0.f;
 #pragma unroll
         for (int c = 0; c < kDC; ++c) acc = dotw<kWQ>(dp[g][c], xv + XM * c, acc);
-        acc = group_sum<16>(acc);
+        acc = group_sum<kDownL>(acc);
         if (on && li == 0) jd.emit(i, tt, scaled<kWQ>(jd, i, acc));
       }
     }
@@ -2151,8 +2152,8 @@ TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have
         float acc = 0.f;
 #pragma unroll
         for (int c = 0; c < kDownC; ++c)
-          if (c < cpl) acc = dotw<kWQ>(dp[g][c], xr + XM * 16 * c, acc);
-        acc = group_sum<16>(acc);
+          if (c < cpl) acc = dotw<kWQ>(dp[g][c], xr + XM * kDownL * c, acc);
+        acc = group_sum<kDownL>(acc);
         if (on && li == 0) jd.emit(i, tt, scaled<kWQ>(jd, i, acc));
       }
     }

@@ -484,7 +484,7 @@ def ragged_lengths(batch: int, lo: int, hi: int) -> list:
 
 def workload(name: str) -> Workload:
     """The five workloads: tiny, mid, moe30b_8k, moe30b_bs8_ragged, moe30b_256k; a name ending in
-    ``_fp8`` is the same workload with the QUANT_KINDS matrices in FP8."""
+    ``_fp8`` (``_fp4``) is the same workload with the QUANT_KINDS matrices in FP8 (FP4)."""
     for fmt in ("fp8", "fp4"):
         if name.endswith("_" + fmt):
             w = workload(name[: -len(fmt) - 1])
