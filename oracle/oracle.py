@@ -39,6 +39,14 @@ product then runs as with bfloat16 weights.  Router, norm gains and embedding
 stay bfloat16.  FP4 weights (``weights="fp4"``) are the same with OCP E2M1
 codes, two a byte (the even element in the low nibble).
 
+Sequential block (a shape with ``block="sequential"``): the pages tailor the
+engine to one model and ask whether it generalizes to other MoE models
+(ainews.surl.tw page, fourth paragraph), naming none.  The reading taken: the
+common pre-norm decoder layer of such models, attention then MoE, each behind
+its own RMSNorm: x' = x + Wo attn(bf16(rmsnorm(x, g_attn))), then
+x <- x' + moe(bf16(rmsnorm(x', g_moe))), with the same shapes, rounding points
+and routing as the parallel block.
+
 Parity unpinned: the composed multi-layer logits have no closed form; they
 are pinned only through the pinned ops and the whole-step invariants in
 ``tests/test_oracle_pins.py``.  The ulp behaviour of exp/silu is covered only
@@ -303,8 +311,11 @@ def layer_forward(W: Weights, kv: PagedKV, l: int, x: np.ndarray, p: int, pt: np
     Parallel block from one normalized input: attention (QKV, rotary, the new
     K/V written at p, attention over 0..p, O projection) and the MoE path
     (router, top-k, softmax over the selected logits, SwiGLU experts, weighted
-    sum), then x <- (x + attn) + moe.  take_alt: take the other correct
-    routing at a near-tie of the k-th and (k+1)-th router logits (checked).
+    sum), then x <- (x + attn) + moe.  Sequential block (shape.block ==
+    "sequential"): attention as above, then the MoE path from its own norm of
+    the updated residual, x' = x + attn, xm = bf16(rmsnorm(x', g_moe)), and
+    x <- x' + moe(xm).  take_alt: take the other correct routing at a
+    near-tie of the k-th and (k+1)-th router logits (checked).
     """
     s = W.shape
     H, d, E, k = s.hidden, s.head_dim, s.n_experts, s.top_k
@@ -327,8 +338,13 @@ def layer_forward(W: Weights, kv: PagedKV, l: int, x: np.ndarray, p: int, pt: np
             o[h] = attention_head(q16[h], K, V)
     a16 = round_bf16(o.reshape(-1))
     attn = W.get(synth.K_WO, l) @ a16
-    # MoE path, from the same normalized input
-    r = (W.get(synth.K_ROUTER, l) @ xn).astype(np.float32)
+    # MoE path: from the same normalized input (parallel block), or from the norm of x + attn
+    # with the MoE path's own gain (sequential block)
+    if s.sequential:
+        xm = round_bf16(rmsnorm(x + attn, W.get(synth.K_MOE_NORM, l), s.rms_eps))
+    else:
+        xm = xn
+    r = (W.get(synth.K_ROUTER, l) @ xm).astype(np.float32)
     sel = topk_desc(r, k)
     alt = None
     if k < E:
@@ -343,14 +359,14 @@ def layer_forward(W: Weights, kv: PagedKV, l: int, x: np.ndarray, p: int, pt: np
     hs = []
     for j in range(k):
         e = int(sel[j])
-        gate = W.get(synth.K_W_GATE, l, e) @ xn
-        up = W.get(synth.K_W_UP, l, e) @ xn
+        gate = W.get(synth.K_W_GATE, l, e) @ xm
+        up = W.get(synth.K_W_UP, l, e) @ xm
         h16 = round_bf16(silu(gate) * up)
         hs.append(h16)
         moe = moe + wsel[j] * (W.get(synth.K_W_DOWN, l, e) @ h16)
     srt = np.sort(r.astype(np.float64))[::-1]
     margin = srt[k - 1] - srt[k] if k < E else np.inf
-    parts = {"xn": xn, "q16": q16, "k16": k16, "v16": v16, "a16": a16, "attn": attn, "moe": moe,
+    parts = {"xn": xn, "xm": xm, "q16": q16, "k16": k16, "v16": v16, "a16": a16, "attn": attn, "moe": moe,
              "h16": np.stack(hs), "w": wsel}
     return LayerOut((x + attn) + moe, r, sel, alt, margin, parts)
 

@@ -51,7 +51,7 @@ class _Stager:
 
 
 def _kind_gen(kind: int, layer: int):
-    t = synth.tid(kind, layer if kind in synth.LAYER_KINDS else 0)
+    t = synth.tid(kind, layer if kind in synth.PER_LAYER_KINDS else 0)
     lib = synth.lib()
     if kind in synth.GAIN_KINDS:
         return lambda s, c, p: lib.synth_gain_bf16(synth.SEED_WEIGHTS, t, s, c, synth.GAIN_SIGMA, p)
@@ -59,14 +59,14 @@ def _kind_gen(kind: int, layer: int):
 
 
 def _fp8_gen(kind: int, layer: int):
-    t = synth.tid(kind, layer if kind in synth.LAYER_KINDS else 0)
+    t = synth.tid(kind, layer if kind in synth.PER_LAYER_KINDS else 0)
     lib = synth.lib()
     return lambda s, c, p: lib.synth_fp8_codes(synth.SEED_WEIGHTS, t, s, c, p)
 
 
 def _fp4_gen(kind: int, layer: int):
     """Packed E2M1 codes by byte: byte i holds elements 2i (low nibble) and 2i + 1."""
-    t = synth.tid(kind, layer if kind in synth.LAYER_KINDS else 0)
+    t = synth.tid(kind, layer if kind in synth.PER_LAYER_KINDS else 0)
     lib = synth.lib()
     return lambda s, c, p: lib.synth_fp4_codes(synth.SEED_WEIGHTS, t, 2 * s, 2 * c, p)
 
@@ -96,9 +96,7 @@ class DeviceDecoder:
         with torch.cuda.device(self.dev):
             stager = _Stager()
             self.weights = []
-            order = list(synth.GLOBAL_KINDS) + [(k, l) for l in range(s.n_layers) for k in synth.LAYER_KINDS]
-            for item in order:
-                kind, layer = (item, 0) if isinstance(item, int) else item
+            for kind, layer in s.bind_order():
                 if s.quantized(kind):
                     # FP8 / FP4: the E4M3 / packed E2M1 codes, then one fp32 scale per row, in one buffer
                     shp = s.weight_shape(kind)
@@ -107,7 +105,7 @@ class DeviceDecoder:
                     ncode = nel // 2 if fp4 else nel
                     t = torch.empty(s.weight_nbytes(kind), dtype=torch.uint8, device=self.dev)
                     stager.fill(t[:ncode], (_fp4_gen if fp4 else _fp8_gen)(kind, layer), esize=1)
-                    idx = layer if kind in synth.LAYER_KINDS else 0
+                    idx = layer if kind in synth.PER_LAYER_KINDS else 0
                     scales = synth.fp4_scales if fp4 else synth.fp8_scales
                     sc = scales(synth.SEED_WEIGHTS, synth.tid(synth.FP8_SCALE_KIND + kind, idx), 0, nel // shp[-1])
                     t[ncode:].copy_(torch.from_numpy(sc.view(np.uint8)))

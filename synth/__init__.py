@@ -36,6 +36,7 @@ _M64 = (1 << 64) - 1
 # tensor kinds
 K_EMBED, K_LM_HEAD, K_FINAL_NORM = 1, 2, 3
 K_ATTN_NORM, K_WQKV, K_WO, K_ROUTER, K_W_GATE, K_W_UP, K_W_DOWN = 10, 11, 12, 13, 14, 15, 16
+K_MOE_NORM = 17   # sequential block only: the gain of the norm in front of the MoE path
 K_K_CACHE, K_V_CACHE = 20, 21
 K_PROMPT, K_PAGE_PERM, K_SEQ_LENS = 30, 31, 32
 
@@ -283,6 +284,24 @@ class ModelShape:
     rms_eps: float = 1.0e-6
     page_size: int = 16
     weights: str = "bf16"   # "bf16"; "fp8" / "fp4": the QUANT_KINDS matrices as E4M3 / E2M1 codes + fp32 row scales
+    block: str = "parallel"  # "parallel": attention and MoE from one normalized input; "sequential": the MoE
+                             # path normalizes (x + attention) with its own gain (K_MOE_NORM)
+
+    @property
+    def sequential(self) -> bool:
+        return self.block == "sequential"
+
+    def layer_kinds(self) -> tuple:
+        """Per-layer weight kinds: LAYER_KINDS, plus K_MOE_NORM in the sequential block."""
+        return LAYER_KINDS + ((K_MOE_NORM,) if self.sequential else ())
+
+    def bind_order(self) -> list:
+        """(kind, layer) of every weight tensor in the order the library binds them: the global
+        tensors, each layer's LAYER_KINDS, then (sequential block) every layer's K_MOE_NORM."""
+        order = [(k, 0) for k in GLOBAL_KINDS] + [(k, l) for l in range(self.n_layers) for k in LAYER_KINDS]
+        if self.sequential:
+            order += [(K_MOE_NORM, l) for l in range(self.n_layers)]
+        return order
 
     def quantized(self, kind: int) -> bool:
         return self.weights in ("fp8", "fp4") and kind in QUANT_KINDS
@@ -307,7 +326,7 @@ class ModelShape:
         H, E, I = self.hidden, self.n_experts, self.inter
         return {
             K_EMBED: (self.vocab, H), K_LM_HEAD: (self.vocab, H), K_FINAL_NORM: (H,),
-            K_ATTN_NORM: (H,), K_WQKV: (self.qkv_rows, H), K_WO: (H, self.attn_dim),
+            K_ATTN_NORM: (H,), K_MOE_NORM: (H,), K_WQKV: (self.qkv_rows, H), K_WO: (H, self.attn_dim),
             K_ROUTER: (E, H), K_W_GATE: (E, I, H), K_W_UP: (E, I, H), K_W_DOWN: (E, H, I),
         }[kind]
 
@@ -324,17 +343,18 @@ class ModelShape:
             return per_el * rows * cols + 4.0 * rows if per_el else 2.0 * rows * cols
 
         per_layer = (mat(self.qkv_rows, H) + mat(H, self.attn_dim) + 2.0 * H * self.n_experts
-                     + distinct_experts_per_layer * (2 * mat(I, H) + mat(H, I)) + 2.0 * H)
+                     + distinct_experts_per_layer * (2 * mat(I, H) + mat(H, I)) + 2.0 * H * (2 if self.sequential else 1))
         return self.n_layers * per_layer + mat(self.vocab, H) + 2.0 * H
 
 
 LAYER_KINDS = (K_ATTN_NORM, K_WQKV, K_WO, K_ROUTER, K_W_GATE, K_W_UP, K_W_DOWN)
+PER_LAYER_KINDS = LAYER_KINDS + (K_MOE_NORM,)   # kinds with one tensor per layer (tensor id indexed by layer)
 # matrices streamed as FP8 in an "fp8" model: every large weight stream; the router rows (which
 # decide the routing), the norm gains and the embedding rows stay bf16
 QUANT_KINDS = (K_LM_HEAD, K_WQKV, K_WO, K_W_GATE, K_W_UP, K_W_DOWN)
 FP8_SCALE_KIND = 64   # scale stream of kind k: tensor id tid(FP8_SCALE_KIND + k, index)
 GLOBAL_KINDS = (K_EMBED, K_LM_HEAD, K_FINAL_NORM)
-GAIN_KINDS = (K_ATTN_NORM, K_FINAL_NORM)
+GAIN_KINDS = (K_ATTN_NORM, K_FINAL_NORM, K_MOE_NORM)
 
 TINY = ModelShape(n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
                   n_experts=8, top_k=2, inter=128, vocab=1024)
@@ -347,7 +367,7 @@ MOE30B = ModelShape(n_layers=48, hidden=2048, n_q_heads=32, n_kv_heads=4, head_d
 def weight_bits(shape: ModelShape, kind: int, layer: int = 0, expert: int | None = None) -> np.ndarray:
     """bf16 bits of one weight tensor (or one expert's slice of it), generated from the recipe."""
     full = shape.weight_shape(kind)
-    t = tid(kind, layer if kind in LAYER_KINDS else 0)
+    t = tid(kind, layer if kind in PER_LAYER_KINDS else 0)
     if expert is not None:
         assert len(full) == 3
         per = full[1] * full[2]
@@ -397,7 +417,7 @@ def weight_fp4(shape: ModelShape, kind: int, layer: int = 0, expert: int | None 
     expert's slice of it), generated from the recipe."""
     assert shape.quantized(kind) and shape.weights == "fp4"
     full = shape.weight_shape(kind)
-    index = layer if kind in LAYER_KINDS else 0
+    index = layer if kind in PER_LAYER_KINDS else 0
     if expert is not None:
         per = full[1] * full[2]
         start, count, out_shape = expert * per, per, full[1:]
@@ -414,7 +434,7 @@ def weight_fp8(shape: ModelShape, kind: int, layer: int = 0, expert: int | None 
     slice of it), generated from the recipe."""
     assert shape.quantized(kind) and shape.weights == "fp8"
     full = shape.weight_shape(kind)
-    index = layer if kind in LAYER_KINDS else 0
+    index = layer if kind in PER_LAYER_KINDS else 0
     if expert is not None:
         assert len(full) == 3
         per = full[1] * full[2]
@@ -484,13 +504,19 @@ def ragged_lengths(batch: int, lo: int, hi: int) -> list:
 
 def workload(name: str) -> Workload:
     """The five workloads: tiny, mid, moe30b_8k, moe30b_bs8_ragged, moe30b_256k; a name ending in
-    ``_fp8`` (``_fp4``) is the same workload with the QUANT_KINDS matrices in FP8 (FP4)."""
+    ``_fp8`` (``_fp4``) is the same workload with the QUANT_KINDS matrices in FP8 (FP4), one ending
+    in ``_seq`` the same with the sequential block (suffixes combine: ``mid_seq_fp8``)."""
     for fmt in ("fp8", "fp4"):
         if name.endswith("_" + fmt):
             w = workload(name[: -len(fmt) - 1])
             w.name = name
             w.shape = replace(w.shape, weights=fmt)
             return w
+    if name.endswith("_seq"):
+        w = workload(name[:-4])
+        w.name = name
+        w.shape = replace(w.shape, block="sequential")
+        return w
     if name == "tiny":
         return Workload(name, TINY, batch=1, steps=16, context=[128], kv_mode="prefill", shuffle_pages=False)
     if name == "mid":

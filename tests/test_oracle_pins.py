@@ -10,6 +10,8 @@ import json
 import math
 import os
 
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import scipy.special
@@ -274,6 +276,85 @@ def test_zero_attention_and_expert_outputs_leave_residual_as_embedding():
     assert np.array_equal(out.trace["x_final"][0], e)
     want = W.get(synth.K_LM_HEAD) @ O.round_bf16(O.rmsnorm(e, W.get(synth.K_FINAL_NORM), s.rms_eps))
     assert np.array_equal(out.logits[0], want)
+
+
+def _seq_source(s, zero_kinds=(), moe_gain_factor=None, wo_factor=None):
+    """Sources for a sequential-block model: optionally zeroed kinds, the MoE norm gain as a multiple
+    of the attention norm gain (exact for powers of two), Wo scaled (a power of two: exact)."""
+    def src(kind, layer, expert):
+        if kind == synth.K_MOE_NORM and moe_gain_factor is not None:
+            g = O.bf16_to_f64(synth.weight_bits(s, synth.K_ATTN_NORM, layer)) * moe_gain_factor
+            return O.f64_to_bf16_bits(g)
+        a = synth.weight_bits(s, kind, layer, expert)
+        if kind in zero_kinds:
+            a = np.zeros_like(a)
+        if kind == synth.K_WO and wo_factor is not None:
+            a = O.f64_to_bf16_bits(O.bf16_to_f64(a) * wo_factor)
+        return a
+    return src
+
+
+def _step_pair(zero_kinds=(), moe_gain_factor=None, toks=(77, 5, 301)):
+    """The same three decode steps through the parallel and the sequential tiny model."""
+    outs = []
+    for block in ("parallel", "sequential"):
+        s = replace(synth.TINY, block=block)
+        W = O.Weights(s, source=_seq_source(s, zero_kinds, moe_gain_factor))
+        kv = O.PagedKV(s, 2)
+        pt = np.arange(2, dtype=np.int32)[None]
+        outs.append([O.decode_step(W, kv, [t], pt, [i], trace=True) for i, t in enumerate(toks)])
+    return outs
+
+
+def test_sequential_block_without_expert_outputs_equals_parallel():
+    """With every down matrix zero the MoE path adds nothing, so both blocks leave x + attn: a
+    sequential block that added the attention output twice, or lost it, would differ."""
+    par, seq = _step_pair(zero_kinds=(synth.K_W_DOWN,))
+    for a, b in zip(par, seq):
+        assert np.array_equal(a.logits, b.logits)
+        for key in a.trace["x_in"]:
+            assert np.array_equal(a.trace["x_in"][key], b.trace["x_in"][key])
+
+
+def test_sequential_block_without_attention_output_equals_parallel():
+    """With Wo zero and the MoE norm gain equal to the attention norm gain, x + attn = x and the MoE
+    path sees the parallel block's normalized input: the steps agree bit for bit."""
+    par, seq = _step_pair(zero_kinds=(synth.K_WO,), moe_gain_factor=1.0)
+    for a, b in zip(par, seq):
+        assert np.array_equal(a.logits, b.logits)
+        assert np.array_equal(a.sel, b.sel)
+
+
+def test_sequential_block_normalizes_with_the_moe_gain():
+    """Wo zero and the MoE gain twice the attention gain: the MoE input is exactly twice the
+    attention input (a power of two commutes with the bf16 rounding), so are the router logits."""
+    s = replace(synth.TINY, block="sequential")
+    W = O.Weights(s, source=_seq_source(s, zero_kinds=(synth.K_WO,), moe_gain_factor=2.0))
+    kv = O.PagedKV(s, 2)
+    out = O.decode_step(W, kv, [123], np.arange(2, dtype=np.int32)[None], [0], trace=True)
+    for l in range(s.n_layers):
+        xn, xm = out.trace["xn"][(l, 0)], out.trace["xm"][(l, 0)]
+        assert np.array_equal(xm, 2.0 * xn)
+        assert np.array_equal(out.router_logits[l, 0], (W.get(synth.K_ROUTER, l) @ (2.0 * xn)).astype(np.float32))
+
+
+def test_sequential_block_moe_input_follows_the_attention_output():
+    """Wo scaled by 2^20: in layer 0, x (an embedding row) + attn is attn to within ~2^-20
+    relative, and rmsnorm ignores scale, so the MoE input is the normalized attention output (a
+    block that fed the MoE path x alone, or the attention input, would not be).  Later layers'
+    x carries the earlier layers' scaled attention outputs, so the check is layer 0's."""
+    s = replace(synth.TINY, block="sequential")
+    W = O.Weights(s, source=_seq_source(s, wo_factor=2.0 ** 20))
+    kv = O.PagedKV(s, 2)
+    for pos, tok in enumerate((9, 400, 33)):
+        out = O.decode_step(W, kv, [tok], np.arange(2, dtype=np.int32)[None], [pos], trace=True)
+        l = 0
+        attn = out.trace["attn"][(l, 0)]
+        want = O.round_bf16(O.rmsnorm(attn, W.get(synth.K_MOE_NORM, l), s.rms_eps))
+        xm = out.trace["xm"][(l, 0)]
+        # equal but for the rare element whose bf16 rounding the 2^-20 remainder tips
+        assert np.mean(xm == want) > 0.97 and np.max(np.abs(xm - want)) <= 2.0 ** -7 * np.max(np.abs(want))
+        assert np.mean(xm == out.trace["xn"][(l, 0)]) < 0.5
 
 
 def test_identical_experts_reduce_to_one_dense_swiglu_ffn():
