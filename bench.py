@@ -39,7 +39,7 @@ def log(*a):
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("mk_kernel.hip", "mk_kernel_fp8.hip", "mk_kernel_fp4.hip", "mk_host.cpp", "mk_types.h"):
+    for f in ("mk_kernel.hip", "mk_kernel_fp8.hip", "mk_kernel_fp4.hip", "mk_kernel_seq.hip", "mk_host.cpp", "mk_types.h"):
         with open(os.path.join(ROOT, "persistent_moe_decode_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -74,7 +74,18 @@ typedef struct mk_config {
   float rms_eps;              /* RMSNorm epsilon (1e-6) */
   double rope_theta;          /* RoPE base (1e4) */
   int32_t weight_format;      /* MK_WEIGHTS_BF16 (0), MK_WEIGHTS_FP8_E4M3 (1) or MK_WEIGHTS_FP4_E2M1 (2), see mk_bind */
+  int32_t block_style;        /* MK_BLOCK_PARALLEL (0) or MK_BLOCK_SEQUENTIAL (1) */
 } mk_config;
+
+/* Layer forms.  PARALLEL: attention and the MoE path both read
+ * bf16(rmsnorm(x, attn_norm)) and the layer leaves x + attention + moe, the
+ * model the pages describe (latestnews.news, paragraph 1).  SEQUENTIAL: the
+ * MoE path reads bf16(rmsnorm(x + attention, moe_norm)) with a gain of its own
+ * and the layer leaves (x + attention) + moe: the pre-norm layer of other MoE
+ * models, to which the pages ask whether the engine generalizes
+ * (ainews.surl.tw, paragraph 4).  Its router rows wait for the layer's Wo
+ * rows, so a layer's attention and experts run one after the other. */
+enum { MK_BLOCK_PARALLEL = 0, MK_BLOCK_SEQUENTIAL = 1 };
 
 /* Weight formats.  FP8_E4M3: the LM head, wqkv, wo, w_gate, w_up and w_down
  * are OCP FP8 E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa
@@ -153,13 +164,15 @@ int mk_build_schedule(mk_ctx* ctx, const mk_schedule_params* params, size_t* wor
 
 /* Binds caller-owned device buffers and uploads the task table into the
  * workspace on `stream` (synchronizes that stream before returning).
- *  weights: host array of n_weights device pointers, n_weights = 3 + 7*n_layers,
+ *  weights: host array of n_weights device pointers, n_weights = 3 + 7*n_layers
+ *    (3 + 8*n_layers with MK_BLOCK_SEQUENTIAL),
  *    in this order: embed [vocab][hidden], lm_head [vocab][hidden],
  *    final_norm [hidden], then per layer: attn_norm [hidden],
  *    wqkv [(n_q+2*n_kv)*head_dim][hidden] (q rows, then k rows, then v rows),
  *    wo [hidden][n_q*head_dim], router [n_experts][hidden],
  *    w_gate [n_experts][inter][hidden], w_up [n_experts][inter][hidden],
- *    w_down [n_experts][hidden][inter].
+ *    w_down [n_experts][hidden][inter]; with MK_BLOCK_SEQUENTIAL then, after
+ *    every layer's seven, one moe_norm [hidden] per layer.
  *    With weight_format MK_WEIGHTS_FP8_E4M3 each of lm_head, wqkv, wo,
  *    w_gate, w_up and w_down is one buffer: the [rows][cols] E4M3 codes
  *    (one byte each, same row order as above; an expert tensor's rows are

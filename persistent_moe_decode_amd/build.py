@@ -7,7 +7,7 @@ import subprocess
 _HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(_HERE, "csrc")
 LIB = os.path.join(_HERE, "libmk.so")
-SOURCES = ["mk_host.cpp", "mk_kernel.hip", "mk_kernel_fp8.hip", "mk_kernel_fp4.hip"]
+SOURCES = ["mk_host.cpp", "mk_kernel.hip", "mk_kernel_fp8.hip", "mk_kernel_fp4.hip", "mk_kernel_seq.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -31,6 +31,7 @@ using namespace mk;
 extern "C" int mkk_launch_step(const KArgs* a, int grid, size_t lds_bytes, hipStream_t stream);
 extern "C" int mkk_launch_step_fp8(const KArgs* a, int grid, size_t lds_bytes, hipStream_t stream);
 extern "C" int mkk_launch_step_fp4(const KArgs* a, int grid, size_t lds_bytes, hipStream_t stream);
+extern "C" int mkk_launch_step_seq(const KArgs* a, int grid, size_t lds_bytes, hipStream_t stream);
 extern "C" int mkk_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t stream);
 extern "C" size_t mkk_scratch_bytes();
 extern "C" int mkk_scratch(int* device, void** ptr);
@@ -102,7 +103,17 @@ static int check_config(const mk_config& c) {
   if (c.weight_format != MK_WEIGHTS_BF16 && c.weight_format != MK_WEIGHTS_FP8_E4M3 &&
       c.weight_format != MK_WEIGHTS_FP4_E2M1)
     return fail(MK_ERR_INVALID_ARG, "unknown weight_format");
+  if (c.block_style != MK_BLOCK_PARALLEL && c.block_style != MK_BLOCK_SEQUENTIAL)
+    return fail(MK_ERR_INVALID_ARG, "unknown block_style");
+  if (c.block_style == MK_BLOCK_SEQUENTIAL && c.weight_format != MK_WEIGHTS_BF16)
+    return bad("the sequential block is built for bf16 weights only");
   return MK_OK;
+}
+
+// Weight pointers mk_bind takes: 3 global, 7 per layer, and with the
+// sequential block one more per layer (the MoE norm gains, after the rest).
+static int n_weights_of(const mk_config& f) {
+  return 3 + (f.block_style == MK_BLOCK_SEQUENTIAL ? 8 : 7) * f.n_layers;
 }
 
 extern "C" int mk_create(const mk_config* cfg, mk_ctx** out) {
@@ -266,7 +277,7 @@ static WsLayout layout_workspace(const mk_ctx* c) {
   take(4 * w.n_state_u32);
   w.tasks = take(sizeof(Task) * c->tasks.size());
   w.queue_off = take(4 * (c->ncu + 1));
-  w.wtab = take(8 * (3 + 7 * L));
+  w.wtab = take(8 * (size_t)n_weights_of(c->cfg));
   w.inv_freq = take(8 * (f.head_dim / 2));
   w.x = take(4 * (L + 1) * B * f.hidden);
   w.xr = take(4 * (L + 1) * B * f.hidden);
@@ -372,6 +383,9 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
   // ends with one failed claim, so a step adds exactly items + claimers to the
   // layer's claim counter whatever the order: the kernel subtracts
   // (epoch - 1) * (items + claimers) to number this step's items.
+  const bool seq = f.block_style == MK_BLOCK_SEQUENTIAL;
+  if (seq && (p.qkv_units > 0 || p.pool_64ths > 0))
+    return fail(MK_ERR_UNSUPPORTED, "qkv_units and pool_64ths are not supported with the sequential block");
   const int pool = std::max(0, std::min(p.pool_64ths, 63));
   const int64_t rows_max = (int64_t)std::min(E, B * f.top_k) * f.inter;
   const int gu_items = pool > 0 ? (int)((rows_max * pool / 64 + kGuItem - 1) / kGuItem) : 0;
@@ -462,6 +476,11 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
         if (r1 > r0) {
           t.signal = ctr_index(l, router ? C_ROUTER : C_QKV);
           t.tagged = router ? 1 : 0;  // gate/up and output tasks poll the tagged router logits
+        }
+        if (seq && router) {
+          // sequential block: the router reads the norm of x_l + this layer's Wo rows
+          t.wait[1] = ctr_index(l, C_WO);
+          t.fanin[1] = n_wo_tasks[l];
         }
         c->tasks.push_back(t);
       }
@@ -754,7 +773,8 @@ static int check_bind_args(const mk_ctx* c, const void* const* weights, int32_t 
   if (!c) return fail(MK_ERR_INVALID_ARG, "null context");
   if (!c->built) return fail(MK_ERR_STATE, "mk_build_schedule must run before binding");
   const mk_config& f = c->cfg;
-  if (!weights || n_weights != 3 + 7 * f.n_layers) return fail(MK_ERR_INVALID_ARG, "weights must hold 3 + 7*n_layers pointers");
+  if (!weights || n_weights != n_weights_of(f))
+    return fail(MK_ERR_INVALID_ARG, "weights must hold 3 + 7*n_layers pointers (3 + 8*n_layers for the sequential block)");
   for (int i = 0; i < n_weights; ++i)
     if (!weights[i]) return fail(MK_ERR_INVALID_ARG, "null weight pointer " + std::to_string(i));
   if (!k_pool || !v_pool) return fail(MK_ERR_INVALID_ARG, "null pool");
@@ -867,6 +887,7 @@ static int launch_steps(mk_ctx* c, int32_t n, int32_t steps, const int32_t* d_to
   a.pf_wide = c->pf_wide;
   a.tile_off = c->tile_off;
   a.gu_pool = c->gu_pool;
+  a.seq_block = c->cfg.block_style == MK_BLOCK_SEQUENTIAL ? 1 : 0;
   a.gu_items = c->gu_items;
   a.gu_parts = c->gu_parts;
   uint8_t* w = c->wsp;
@@ -911,6 +932,7 @@ static int launch_steps(mk_ctx* c, int32_t n, int32_t steps, const int32_t* d_to
   const hipStream_t hs = (hipStream_t)stream;
   int r = c->cfg.weight_format == MK_WEIGHTS_FP8_E4M3   ? mkk_launch_step_fp8(&a, c->ncu, c->lds_bytes, hs)
           : c->cfg.weight_format == MK_WEIGHTS_FP4_E2M1 ? mkk_launch_step_fp4(&a, c->ncu, c->lds_bytes, hs)
+          : c->cfg.block_style == MK_BLOCK_SEQUENTIAL   ? mkk_launch_step_seq(&a, c->ncu, c->lds_bytes, hs)
                                                         : mkk_launch_step(&a, c->ncu, c->lds_bytes, hs);
   if (r) return fail(MK_ERR_HIP, std::string("cooperative launch failed: ") + hipGetErrorString((hipError_t)r));
   c->epoch += (uint32_t)steps;

@@ -25,8 +25,9 @@
 // in fp32 with v_dot2_f32_bf16 and groups of lanes reduce through DPP, at
 // batch >= 2 rows that every token uses run as 16-row matrix-core tiles.
 //
-// This file is compiled three times.  With MK_WFMT = 0 it is the kernel for
-// bf16 weights; with MK_WFMT = 1 (mk_kernel_fp8.hip) or 2 (mk_kernel_fp4.hip)
+// This file is compiled four times.  With MK_WFMT = 0 it is the kernel for
+// bf16 weights (and with MK_SEQ = 1, mk_kernel_seq.hip, the same for the
+// sequential block); with MK_WFMT = 1 (mk_kernel_fp8.hip) or 2 (mk_kernel_fp4.hip)
 // the LM head, Wqkv, Wo and the expert gate/up/down matrices are FP8 (OCP
 // E4M3) or FP4 (OCP E2M1, two codes a byte) codes with one fp32 scale per row
 // after each matrix's codes: the row loops convert the codes to bf16 in
@@ -49,13 +50,23 @@ using namespace mk;
 #ifndef MK_WFMT
 #define MK_WFMT 0  // weight format: 0 bf16, 1 FP8 E4M3, 2 FP4 E2M1
 #endif
+#ifndef MK_SEQ
+#define MK_SEQ 0   // 1: the sequential block (attention, then the MoE path behind its own norm)
+#endif
+#if MK_SEQ && MK_WFMT != 0
+#error "the sequential block is built for bf16 weights only"
+#endif
 #if MK_WFMT == 1
 #define MKK(name) name##_fp8
 #elif MK_WFMT == 2
 #define MKK(name) name##_fp4
+#elif MK_SEQ
+#define MKK(name) name##_seq
 #else
 #define MKK(name) name
 #endif
+// a separate build, so the parallel block's kernel carries none of the sequential block's branches
+constexpr bool kSeq = MK_SEQ != 0;
 // the streamed matrices (LM head, Wqkv, Wo, experts): quantized or not, bits per element
 constexpr bool kWQ = MK_WFMT != 0;
 constexpr int kWBits = MK_WFMT == 1 ? 8 : (MK_WFMT == 2 ? 4 : 16);
@@ -509,6 +520,12 @@ DEV bool wait_ticket(const KArgs& a, uint32_t* ticket, uint32_t want, int task, 
 // inputs
 
 DEV const gu16* wptr(const KArgs& a, int i) { return (const gu16*)(uintptr_t)a.wtab[i]; }
+
+// The gain of the norm in front of layer l's MoE path: the attention norm's
+// (parallel block), or the MoE path's own (sequential block).
+DEV const gu16* moe_gain(const KArgs& a, int l) {
+  return wptr(a, kSeq ? widx_moe_norm(a.L, l) : widx(l, WL_NORM));
+}
 // a streamed matrix as bytes (bf16 elements, or FP8 codes followed by the rows' fp32 scales)
 typedef const AS_GLOBAL uint8_t gu8;
 DEV const gu8* wbytes(const KArgs& a, int i) { return (const gu8*)(uintptr_t)a.wtab[i]; }
@@ -546,10 +563,18 @@ DEV float resid(const KArgs& a, int layer, int b, int i) {
 // Residual entering `layer` (layer 0: the embedding row).
 // With the layer-input hook set, layers >= 1 (and the final norm) read the
 // residual the caller supplied instead of the one the previous layer wrote.
+// Sequential block: the residual the MoE path starts from, x_layer plus this
+// layer's Wo rows (x_layer itself whole in the x buffer).
 DEV float load_x(const KArgs& a, int layer, int b, int i, const gu16* emb) {
-  if (layer == 0) return bf2f(emb[i]);
-  if (a.x_in) return a.x_in[((size_t)layer * a.max_batch + b) * a.H + i];
-  return resid(a, layer, b, i);
+  if constexpr (!kSeq) {
+    if (layer == 0) return bf2f(emb[i]);
+    if (a.x_in) return a.x_in[((size_t)layer * a.max_batch + b) * a.H + i];
+    return resid(a, layer, b, i);
+  } else {
+    const size_t o = ((size_t)layer * a.max_batch + b) * a.H + i;
+    const float x = layer == 0 ? bf2f(emb[i]) : (a.x_in ? a.x_in[o] : ld_coh(a.x + o));
+    return x + ld_coh(a.wo_out + o);
+  }
 }
 
 DEV u32x4_v add4(u32x4_v u, u32x4_v v) {
@@ -638,50 +663,114 @@ DEV void norm_row4(const uint8_t* stage, bool emb, int H, int n, int c, float (&
 // mk >= 0: trace mark mk of the task once the inputs are in LDS.  rec (or
 // NULL): where to record the residual entering `layer` (>= 1) as summed here
 // from the previous layer's halves, also when the hook supplies the input.
+// side: kParallel, the residual entering `layer` as the sum of the previous
+// layer's halves (x + moe, and its Wo rows); kAlone (sequential block:
+// attention side and final norm), x_layer as the previous layer's output
+// tasks wrote it whole; kWithWo (sequential block: the MoE path), x_layer
+// plus this layer's Wo rows.  The layer-input hook, where set, supplies
+// x_layer for layers >= 1.
+enum NormSide : int { kParallel = 0, kAlone = 1, kWithWo = 2 };
+
 DEV void norm_inputs(const KArgs& a, int layer, const gu16* gain, uint16_t* xs, double* red8, int task, int mk,
-                     float* rec = nullptr) {
+                     float* rec = nullptr, int side = kParallel) {
   const int H = a.H, n = a.n, lane = tid() & 63, wave = tid() >> 6;
   uint8_t* stage = norm_stage(a, xs);
   uint16_t* gs = (uint16_t*)(stage + (size_t)a.max_batch * H * 4);
-  const bool emb = layer == 0;
+  const bool emb = layer == 0 && side != kWithWo;
   {
-    // the input rows (the two halves of x: one 16-byte load each per thread
-    // and row at hidden 2048) and the gain, all in flight before any is
-    // written to LDS
-    const uint32_t nx16 = emb ? 0u : (uint32_t)n * H / 4, ng16 = (uint32_t)H / 8;
-    const size_t o = (size_t)layer * a.max_batch * H;
-    const float* xh = a.x + o;                                  // x + moe of the previous layer
-    const float* wh = a.wo_out + o - (size_t)a.max_batch * H;   // its attention output times Wo
-    u32x4_v* st = (u32x4_v*)stage;
-    for (uint32_t q0 = 0; q0 < nx16 + ng16; q0 += 4 * kThreads) {
-      u32x4_v v[4], w[4];
+    if constexpr (!kSeq) {
+      // the input rows (the two halves of x: one 16-byte load each per thread
+      // and row at hidden 2048) and the gain, all in flight before any is
+      // written to LDS
+      const uint32_t nx16 = emb ? 0u : (uint32_t)n * H / 4, ng16 = (uint32_t)H / 8;
+      const size_t o = (size_t)layer * a.max_batch * H;
+      const float* xh = a.x + o;                                  // x + moe of the previous layer
+      const float* wh = a.wo_out + o - (size_t)a.max_batch * H;   // its attention output times Wo
+      u32x4_v* st = (u32x4_v*)stage;
+      for (uint32_t q0 = 0; q0 < nx16 + ng16; q0 += 4 * kThreads) {
+        u32x4_v v[4], w[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t q = q0 + k * kThreads + tid();
-        if (q < nx16 && a.x_in) {
-          v[k] = ((const gu4*)(a.x_in + o))[q];
-        } else if (q < nx16) {
-          v[k] = ld_coh16(xh, nx16 * 16, q * 16);
-          w[k] = ld_coh16(wh, nx16 * 16, q * 16);
-        } else if (q < nx16 + ng16) {
-          v[k] = ((const gu4*)gain)[q - nx16];
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t q = q0 + k * kThreads + tid();
+          if (q < nx16 && a.x_in) {
+            v[k] = ((const gu4*)(a.x_in + o))[q];
+          } else if (q < nx16) {
+            v[k] = ld_coh16(xh, nx16 * 16, q * 16);
+            w[k] = ld_coh16(wh, nx16 * 16, q * 16);
+          } else if (q < nx16 + ng16) {
+            v[k] = ((const gu4*)gain)[q - nx16];
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t q = q0 + k * kThreads + tid();
+          if (q < nx16) {
+            const u32x4_v x = a.x_in ? v[k] : add4(v[k], w[k]);
+            st[q] = x;
+            if (rec && !a.x_in) ((u32x4_v*)(rec + o))[q] = x;
+          } else if (q < nx16 + ng16) {
+            ((u32x4_v*)gs)[q - nx16] = v[k];
+          }
         }
       }
+      if (rec && a.x_in)
+        for (uint32_t q = tid(); q < nx16; q += kThreads)
+          ((u32x4_v*)(rec + o))[q] = add4(ld_coh16(xh, nx16 * 16, q * 16), ld_coh16(wh, nx16 * 16, q * 16));
+    } else {
+      // the input rows (x and, where added, the Wo rows: one 16-byte load each
+      // per thread and row at hidden 2048) and the gain, all in flight before
+      // any is written to LDS
+      const uint32_t nx16 = emb ? 0u : (uint32_t)n * H / 4, ng16 = (uint32_t)H / 8;
+      const size_t o = (size_t)layer * a.max_batch * H;
+      const float* xh = a.x + o;                                  // x as the previous layer's output tasks wrote it
+      const float* wh = side == kWithWo ? a.wo_out + o            // this layer's attention output times Wo
+                                        : a.wo_out + o - (size_t)a.max_batch * H;  // the previous layer's
+      // whether the Wo rows are added: the parallel block's halves (unless the
+      // hook supplies their sum), the sequential block's MoE side always
+      const bool add_w = side == kWithWo || (side == kParallel && !a.x_in);
+      const bool emb_w = layer == 0 && side == kWithWo;           // the embedding row plus layer 0's Wo rows
+      u32x4_v* st = (u32x4_v*)stage;
+      if (emb_w)
+        for (int b = 0; b < n; ++b) {
+          const gu16* er = token_row(a, b, task);
+          for (int c = tid(); 4 * c < H; c += kThreads) {
+            const uint2 e = *(const uint2*)(er + 4 * c);
+            const u32x4_v v = {__float_as_uint(bf2f(e.x & 0xffffu)), __float_as_uint(bf2f(e.x >> 16)),
+                               __float_as_uint(bf2f(e.y & 0xffffu)), __float_as_uint(bf2f(e.y >> 16))};
+            const uint32_t q = (uint32_t)(b * (H / 4) + c);
+            st[q] = add4(v, ld_coh16(wh, nx16 * 16, q * 16));
+          }
+        }
+      for (uint32_t q0 = emb_w ? nx16 : 0u; q0 < nx16 + ng16; q0 += 4 * kThreads) {
+        u32x4_v v[4], w[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t q = q0 + k * kThreads + tid();
-        if (q < nx16) {
-          const u32x4_v x = a.x_in ? v[k] : add4(v[k], w[k]);
-          st[q] = x;
-          if (rec && !a.x_in) ((u32x4_v*)(rec + o))[q] = x;
-        } else if (q < nx16 + ng16) {
-          ((u32x4_v*)gs)[q - nx16] = v[k];
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t q = q0 + k * kThreads + tid();
+          if (q < nx16) {
+            v[k] = a.x_in ? ((const gu4*)(a.x_in + o))[q] : ld_coh16(xh, nx16 * 16, q * 16);
+            if (add_w) w[k] = ld_coh16(wh, nx16 * 16, q * 16);
+          } else if (q < nx16 + ng16) {
+            v[k] = ((const gu4*)gain)[q - nx16];
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t q = q0 + k * kThreads + tid();
+          if (q < nx16) {
+            const u32x4_v x = add_w ? add4(v[k], w[k]) : v[k];
+            st[q] = x;
+            if (rec && !a.x_in) ((u32x4_v*)(rec + o))[q] = x;
+          } else if (q < nx16 + ng16) {
+            ((u32x4_v*)gs)[q - nx16] = v[k];
+          }
         }
       }
+      // the record of the residual as this kernel computed it (the hook's input aside)
+      if (rec && a.x_in)
+        for (uint32_t q = tid(); q < nx16; q += kThreads)
+          ((u32x4_v*)(rec + o))[q] = side == kParallel ? add4(ld_coh16(xh, nx16 * 16, q * 16), ld_coh16(wh, nx16 * 16, q * 16))
+                                                       : ld_coh16(xh, nx16 * 16, q * 16);
     }
-    if (rec && a.x_in)
-      for (uint32_t q = tid(); q < nx16; q += kThreads)
-        ((u32x4_v*)(rec + o))[q] = add4(ld_coh16(xh, nx16 * 16, q * 16), ld_coh16(wh, nx16 * 16, q * 16));
     if (emb)
       for (int b = 0; b < n; ++b)
         copy_to_lds<false>(stage + (size_t)b * H * 2, (const void*)(uintptr_t)token_row(a, b, task), H * 2);
@@ -1250,7 +1339,10 @@ struct JobPre {
 TASK void task_pre(const KArgs& a, const Task& t, const Lds& s, int qi, int npf) {
   const int l = t.layer;
   uint16_t* xs = (uint16_t*)s.A;
-  norm_inputs(a, l, wptr(a, widx(l, WL_NORM)), xs, s.red8, qi, 0);
+  // sequential block: the Wqkv rows read the attention side's norm, the router rows the MoE path's
+  const bool moe_side = kSeq && t.r0 >= a.qkv_rows;
+  norm_inputs(a, l, moe_side ? moe_gain(a, l) : wptr(a, widx(l, WL_NORM)), xs, s.red8, qi, 0, nullptr,
+              kSeq ? (moe_side ? kWithWo : kAlone) : kParallel);
   prefetch_wait();
   mark(a, qi, 1);
   JobPre j;
@@ -1995,7 +2087,7 @@ TASK bool task_gateup(const KArgs& a, const Task& t, const Lds& s, int qi, bool 
   if (t.idx == 0) write_sel(a, l, s.tk);
   mark(a, qi, 1);
   uint16_t* xs = (uint16_t*)s.A;
-  if (!have_xs) norm_inputs(a, l, wptr(a, widx(l, WL_NORM)), xs, s.red8, qi, -1);
+  if (!have_xs) norm_inputs(a, l, moe_gain(a, l), xs, s.red8, qi, -1, nullptr, kSeq ? kWithWo : kParallel);
   mark(a, qi, 2);
   const int64_t R = (int64_t)s.tk->nU * a.I;
   int n_items;
@@ -2012,7 +2104,7 @@ TASK bool task_gutail(const KArgs& a, const Task& t, const Lds& s, int qi) {
   const int l = t.layer;
   if (!compute_topk(a, l, s.tk, s.C, qi, s.flags + 0, 0)) return false;
   uint16_t* xs = (uint16_t*)s.A;
-  norm_inputs(a, l, wptr(a, widx(l, WL_NORM)), xs, s.red8, qi, 1);
+  norm_inputs(a, l, moe_gain(a, l), xs, s.red8, qi, 1, nullptr, kSeq ? kWithWo : kParallel);
   gateup_pool(a, s, l, xs, (int64_t)s.tk->nU * a.I);
   mark(a, qi, 2);
   return true;
@@ -2185,7 +2277,7 @@ TASK int task_out(const KArgs& a, const Task& t, const Lds& s, int qi, bool have
     const float xo = e == tid() ? x_first : load_x(a, l, b, t.r0 + rr, l == 0 ? token_row(a, b, qi) : nullptr);
     const size_t o = ((size_t)l * a.max_batch + b) * a.H + t.r0 + rr;
     st_coh(a.x + o + (size_t)a.max_batch * a.H, xo + moe);
-    if (l > 0) a.xr[o] = a.x_in ? resid(a, l, b, t.r0 + rr) : xo;
+    if (l > 0) a.xr[o] = kSeq ? ld_coh(a.x + o) : (a.x_in ? resid(a, l, b, t.r0 + rr) : xo);
   }
   mark(a, qi, 3);
   // waves whose stores the consumers read must see them complete before the signal
@@ -2318,7 +2410,8 @@ DEV void block_argmax(float& v, int& i, float* red) {
 TASK void task_lmhead(const KArgs& a, const Task& t, const Lds& s, int qi) {
   const int L = a.L, nr = t.r1 - t.r0;
   uint16_t* xs = (uint16_t*)s.A;
-  norm_inputs(a, L, wptr(a, W_FINAL_NORM), xs, s.red8, qi, -1, t.idx == 0 ? a.xr : nullptr);
+  norm_inputs(a, L, wptr(a, W_FINAL_NORM), xs, s.red8, qi, -1, t.idx == 0 ? a.xr : nullptr,
+              kSeq ? kAlone : kParallel);
   mark(a, qi, 0);
   JobLM j;
   j.W = wbytes(a, W_LM_HEAD);
@@ -2435,7 +2528,9 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) MKK(mk_megakernel)(KAr
           default: break;
         }
       }
-      xs_layer = ok && t.op == OP_PRE ? t.layer : (ok && t.op == OP_GATEUP ? xs_layer : -1);
+      // (sequential block: only a router task's norm is the one the gate/up task needs)
+      xs_layer = ok && t.op == OP_PRE && (!kSeq || t.r0 >= a.qkv_rows) ? t.layer
+                                                                            : (ok && t.op == OP_GATEUP ? xs_layer : -1);
       // region B holds a layer's top-k only after a top-k that succeeded (a failed one, on
       // abort or time-out, leaves whatever an earlier task or kernel left there)
       if (t.op == OP_LMHEAD) tk_layer = -1;
@@ -2451,7 +2546,7 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) MKK(mk_megakernel)(KAr
   }
 }
 
-#if MK_WFMT == 0
+#if MK_WFMT == 0 && !MK_SEQ
 // One copy of what follows (not per weight format): the fill kernel and the static workspace.
 __global__ void mk_fill_u32_kernel(uint32_t* p, uint32_t v, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + tid(); i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;

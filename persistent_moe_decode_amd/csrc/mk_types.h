@@ -137,12 +137,17 @@ struct KArgs {
   int32_t kv_sync;           // mixed step: entries may share a sequence; attention reads pages only after
                              // every entry's new K/V is written (the KVW tasks), and no page is read before
   int32_t step;              // the step being run (set by the kernel: epoch + step, positions + step)
+  int32_t seq_block;         // sequential block: attention-side norms read x_l alone, the MoE path's norm
+                             // reads x_l + this layer's Wo rows with its own gain, and the output tasks
+                             // write the whole next residual
 };
 
 // Weight table order.
 enum WIdx : int32_t { W_EMBED = 0, W_LM_HEAD = 1, W_FINAL_NORM = 2, W_LAYER0 = 3 };
 enum WLayer : int32_t { WL_NORM = 0, WL_QKV = 1, WL_O = 2, WL_ROUTER = 3, WL_GATE = 4, WL_UP = 5, WL_DOWN = 6, WL_COUNT = 7 };
 MK_HD int widx(int layer, int which) { return W_LAYER0 + layer * WL_COUNT + which; }
+// the sequential block's MoE norm gain of a layer, after every layer's WL_COUNT tensors
+MK_HD int widx_moe_norm(int n_layers, int layer) { return W_LAYER0 + n_layers * WL_COUNT + layer; }
 
 // Floats per attention partial (one split task): outputs [group][d], then the
 // running maxima [kMaxGroup] and sums [kMaxGroup]; a multiple of 4, so every

@@ -40,7 +40,7 @@ class MkConfig(ctypes.Structure):
         ("top_k", ctypes.c_int32), ("inter", ctypes.c_int32), ("vocab", ctypes.c_int32),
         ("page_size", ctypes.c_int32), ("max_batch", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
         ("num_pages", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_double),
-        ("weight_format", ctypes.c_int32),
+        ("weight_format", ctypes.c_int32), ("block_style", ctypes.c_int32),
     ]
 
 
@@ -147,13 +147,14 @@ def _i32p(arr):
 
 
 WEIGHT_FORMATS = {"bf16": 0, "fp8": 1, "fp4": 2}   # MK_WEIGHTS_BF16, _FP8_E4M3, _FP4_E2M1
+BLOCK_STYLES = {"parallel": 0, "sequential": 1}     # MK_BLOCK_PARALLEL, MK_BLOCK_SEQUENTIAL
 
 
 def config_from_shape(shape, max_batch: int, max_pages_per_seq: int, num_pages: int) -> MkConfig:
     return MkConfig(shape.n_layers, shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
                     shape.n_experts, shape.top_k, shape.inter, shape.vocab, shape.page_size, max_batch,
                     max_pages_per_seq, num_pages, shape.rms_eps, shape.rope_theta,
-                    WEIGHT_FORMATS[getattr(shape, "weights", "bf16")])
+                    WEIGHT_FORMATS[getattr(shape, "weights", "bf16")], BLOCK_STYLES[getattr(shape, "block", "parallel")])
 
 
 class Context:

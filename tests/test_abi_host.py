@@ -459,3 +459,61 @@ def test_simulator_models_the_leads_ticket_wait():
         pytest.fail("no unit with both a chunk and Wo rows")
     code, done = mk.simulate_table(t, qoff, nctr)
     assert code == mk.CODES["MK_ERR_SCHEDULE"] and done < len(t)
+
+
+# --------------------------------------------------------------------------- sequential block
+
+def test_create_rejects_an_unknown_block_style():
+    cfg = mk.config_from_shape(synth.TINY, 1, 8, 8)
+    cfg.block_style = 2
+    with pytest.raises(mk.MkError) as e:
+        mk.Context(cfg)
+    assert e.value.code == mk.CODES["MK_ERR_INVALID_ARG"]
+
+
+def test_sequential_block_schedule():
+    """Sequential block: every router task (a PRE task with router rows) waits for its own layer's Wo
+    rows; the Wqkv tasks keep the parallel block's waits; the table simulates to completion."""
+    from dataclasses import replace
+    s = replace(synth.MID, block="sequential")
+    c = _ctx(s, 2, 16, 64)
+    c.build_schedule(256, 2000)
+    tasks, qoff = c.schedule()
+    assert c.validate() == c.info().n_tasks
+    op, layer, w0, w1 = tasks[:, 0], tasks[:, 1], tasks[:, 2], tasks[:, 3]
+    r0 = tasks[:, 7]
+    pre = op == 1
+    router = pre & (r0 >= s.qkv_rows)
+    assert router.any() and (pre & ~router).any()
+    n_ctr_layer, c_wo = 9, 6
+    assert np.array_equal(w1[router], layer[router] * n_ctr_layer + c_wo)
+    # the parallel block's router tasks wait on the previous layer's Wo rows instead
+    p = _ctx(synth.MID, 2, 16, 64)
+    p.build_schedule(256, 2000)
+    pt, _ = p.schedule()
+    prouter = (pt[:, 0] == 1) & (pt[:, 7] >= s.qkv_rows) & (pt[:, 1] > 0)
+    assert np.array_equal(pt[prouter, 3], (pt[prouter, 1] - 1) * n_ctr_layer + c_wo)
+    # dedicated QKV units and the shared pool are not offered with the sequential block
+    for kw in ({"qkv_units": 20}, {"pool_64ths": 8}):
+        with pytest.raises(mk.MkError) as e:
+            c.build_schedule(256, 2000, **kw)
+        assert e.value.code == mk.CODES["MK_ERR_UNSUPPORTED"]
+
+
+def test_sequential_block_binds_eight_tensors_per_layer():
+    """3 + 8 * n_layers weight pointers (the MoE norm gains after every layer's seven); the count is
+    checked before any device call, so fake aligned pointers suffice to see it refused."""
+    from dataclasses import replace
+    s = replace(synth.TINY, block="sequential")
+    c = _ctx(s, 1, 8, 8)
+    c.build_schedule(256, 100)
+    fake = [0x1000 * (i + 1) for i in range(3 + 7 * s.n_layers)]
+    with pytest.raises(mk.MkError) as e:
+        c.bind(fake, 0x100000, 0x200000, 0, 0, 0)
+    assert e.value.code == mk.CODES["MK_ERR_INVALID_ARG"] and "3 + 7*n_layers" in str(e.value)
+    fake = [0x1000 * (i + 1) for i in range(3 + 8 * s.n_layers)]
+    with pytest.raises(mk.MkError) as e:   # now the count passes and the missing workspace is refused
+        c.bind(fake, 0x100000, 0x200000, 0, 0, 0)
+    assert "n_layers" not in str(e.value)
+    assert len(s.bind_order()) == 3 + 8 * s.n_layers
+    assert s.bind_order()[3 + 7 * s.n_layers:] == [(synth.K_MOE_NORM, l) for l in range(s.n_layers)]

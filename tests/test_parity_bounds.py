@@ -1,0 +1,34 @@
+"""The parity harness's reference for the sequential block's router, on the CPU."""
+from dataclasses import replace
+
+import numpy as np
+
+import synth
+from oracle import oracle as O
+from tests import parity
+
+
+def test_sequential_router_reference_equals_the_oracle_on_the_oracle_inputs():
+    """Fed the oracle's own x_l and Wo output, the reference is the oracle's router logits up to the
+    fp32 sum the kernel forms (a bf16 flip of the MoE input aside, which this step does not have)."""
+    s = replace(synth.TINY, block="sequential")
+    W = O.Weights(s)
+    kv = O.PagedKV(s, 2)
+    ref = O.decode_step(W, kv, [17], np.arange(2, dtype=np.int32)[None], [0], trace=True)
+    for l in range(s.n_layers):
+        r = parity.seq_router_reference(W, ref.trace["x_in"][(l, 0)], ref.trace["attn"][(l, 0)], l)
+        assert np.max(np.abs(r - ref.router_logits[l, 0])) <= 2e-4
+
+
+def test_sequential_router_reference_follows_the_kernel_wo_output():
+    """A Wo output off by one bf16-sized step in one element moves the reference's logits by that
+    element's weights, as it moves the kernel's."""
+    s = replace(synth.TINY, block="sequential")
+    W = O.Weights(s)
+    kv = O.PagedKV(s, 2)
+    ref = O.decode_step(W, kv, [17], np.arange(2, dtype=np.int32)[None], [0], trace=True)
+    x, wo = ref.trace["x_in"][(0, 0)], ref.trace["attn"][(0, 0)].copy()
+    r0 = parity.seq_router_reference(W, x, wo, 0)
+    wo[3] += 0.25 * np.max(np.abs(x + wo))
+    r1 = parity.seq_router_reference(W, x, wo, 0)
+    assert np.max(np.abs(r1 - r0)) > 1e-3
