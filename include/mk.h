@@ -130,13 +130,16 @@ int mk_create(const mk_config* cfg, mk_ctx** out);
  *    at most 63).  On the 30B shape at batch 1 and 8K, 8 to 24 64ths cost
  *    about 11% per step: every claimer's final claim is one more device
  *    round trip, and the attention units' own top-k and normalization before
- *    their pool items delay their Wo rows.  Source: idle units take over
- *    tail-end work from the other path (ainews.surl.tw, paragraph 2).
+ *    their pool items delay their Wo rows.  With MK_BLOCK_SEQUENTIAL the
+ *    attention units claim after their Wo rows (the router waits for them).
+ *    Source: idle units take over tail-end work from the other path
+ *    (ainews.surl.tw, paragraph 2).
  *  qkv_units: stage-1 units that take the Wqkv rows and no gate/up rows
  *    (0 = none: the Wqkv rows go to every stage-1 unit but the router's, each
  *    of which then also takes gate/up rows).  With qkv_units > 0 the other
  *    stage-1 units normalize and go straight to the router poll and their
  *    gate/up rows.  Clamped to [1, stage-1 units - router units - 1].
+ *    MK_ERR_UNSUPPORTED with MK_BLOCK_SEQUENTIAL.
  *  ctx_hint: expected cached tokens per sequence (0 = 4096); used only to
  *    size attn_units when that is 0. */
 typedef struct mk_schedule_params {

@@ -384,8 +384,8 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
   // layer's claim counter whatever the order: the kernel subtracts
   // (epoch - 1) * (items + claimers) to number this step's items.
   const bool seq = f.block_style == MK_BLOCK_SEQUENTIAL;
-  if (seq && (p.qkv_units > 0 || p.pool_64ths > 0))
-    return fail(MK_ERR_UNSUPPORTED, "qkv_units and pool_64ths are not supported with the sequential block");
+  if (seq && p.qkv_units > 0)
+    return fail(MK_ERR_UNSUPPORTED, "qkv_units is not supported with the sequential block");
   const int pool = std::max(0, std::min(p.pool_64ths, 63));
   const int64_t rows_max = (int64_t)std::min(E, B * f.top_k) * f.inter;
   const int gu_items = pool > 0 ? (int)((rows_max * pool / 64 + kGuItem - 1) / kGuItem) : 0;
@@ -516,14 +516,14 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
           t.report = ctr_index(l, C_CHUNK);
         }
         c->tasks.push_back(t);
-        if (n_pool_tasks > 0 && q >= n_lead) {
-          // gate/up rows from the shared pool (needs the router logits; polls them itself)
-          Task g = make_task(OP_GUTAIL, l);
-          g.wait[0] = ctr_index(l, C_ROUTER);
-          g.fanin[0] = n_router_tasks[l];
-          g.signal = ctr_index(l, C_GATEUP);
-          c->tasks.push_back(g);
-        }
+        // gate/up rows from the shared pool (needs the router logits; polls them itself): right
+        // after the chunk, or in the sequential block after the Wo rows, which its router waits for
+        Task g = make_task(OP_GUTAIL, l);
+        g.wait[0] = ctr_index(l, C_ROUTER);
+        g.fanin[0] = n_router_tasks[l];
+        g.signal = ctr_index(l, C_GATEUP);
+        const bool pool_task = n_pool_tasks > 0 && q >= n_lead;
+        if (pool_task && !seq) c->tasks.push_back(g);
         wo_rows(q, &r0, &r1);
         if (r1 > r0) {
           Task w = make_task(OP_WO, l);
@@ -534,6 +534,7 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
           w.signal = ctr_index(l, C_WO);
           c->tasks.push_back(w);
         }
+        if (pool_task && seq) c->tasks.push_back(g);
       } else if (q >= gu0) {
         Task t = make_task(OP_GATEUP, l);
         t.wait[0] = ctr_index(l, C_ROUTER);

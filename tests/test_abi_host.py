@@ -493,11 +493,20 @@ def test_sequential_block_schedule():
     pt, _ = p.schedule()
     prouter = (pt[:, 0] == 1) & (pt[:, 7] >= s.qkv_rows) & (pt[:, 1] > 0)
     assert np.array_equal(pt[prouter, 3], (pt[prouter, 1] - 1) * n_ctr_layer + c_wo)
-    # dedicated QKV units and the shared pool are not offered with the sequential block
-    for kw in ({"qkv_units": 20}, {"pool_64ths": 8}):
-        with pytest.raises(mk.MkError) as e:
-            c.build_schedule(256, 2000, **kw)
-        assert e.value.code == mk.CODES["MK_ERR_UNSUPPORTED"]
+    # dedicated QKV units are not offered with the sequential block
+    with pytest.raises(mk.MkError) as e:
+        c.build_schedule(256, 2000, qkv_units=20)
+    assert e.value.code == mk.CODES["MK_ERR_UNSUPPORTED"]
+    # the shared pool is: each attention unit's pool task follows its Wo task (the router waits for
+    # the Wo rows, the pool task for the router), and the table still drains
+    c.build_schedule(256, 2000, pool_64ths=16)
+    assert c.validate() == c.info().n_tasks
+    tasks, qoff = c.schedule()
+    for q in range(len(qoff) - 1):
+        ops = [int(o) for o in tasks[qoff[q]:qoff[q + 1], 0]]
+        for i, o in enumerate(ops):
+            if o == 7:   # GUTAIL
+                assert 6 in ops[:i] and ops[i - 1] == 6, (q, ops[:i + 1])
 
 
 def test_sequential_block_binds_eight_tensors_per_layer():
