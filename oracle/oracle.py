@@ -304,6 +304,48 @@ class LayerOut:
     parts: dict            # intermediates: xn, q16, k16, v16, a16, attn, moe, h16, w
 
 
+@dataclass
+class MoeOut:
+    r: np.ndarray          # [E] float32 values: router logits
+    sel: np.ndarray        # [k] experts in slot order
+    sel_alt: np.ndarray    # [k] the set with the k-th and (k+1)-th exchanged (or None when k == E)
+    margin: float          # r_(k) - r_(k+1)
+    w: np.ndarray          # [k] softmax of the selected logits
+    moe: np.ndarray        # [H] weighted sum of the experts' outputs
+    h16: np.ndarray        # [k][I] the experts' bf16 hidden vectors
+
+
+def moe_path(W: Weights, l: int, xm: np.ndarray, take_alt: bool = False) -> MoeOut:
+    """Layer l's MoE path from its normalized input xm: router, top-k by (value desc, index asc),
+    softmax over the selected logits, SwiGLU experts, weighted sum.  take_alt: take the other
+    correct routing at a near-tie of the k-th and (k+1)-th router logits (checked)."""
+    s = W.shape
+    H, E, k = s.hidden, s.n_experts, s.top_k
+    r = (W.get(synth.K_ROUTER, l) @ xm).astype(np.float32)
+    sel = topk_desc(r, k)
+    alt = None
+    if k < E:
+        ext = topk_desc(r, k + 1)
+        alt = np.concatenate([ext[: k - 1], ext[k:]])
+        if take_alt:
+            if not float(r[ext[k - 1]]) - float(r[ext[k]]) <= ROUTE_TIE:
+                raise ValueError(f"layer {l}: no routing near-tie to take the alternative of")
+            sel = alt
+    wsel = softmax(r[sel].astype(np.float64))
+    moe = np.zeros(H)
+    hs = []
+    for j in range(k):
+        e = int(sel[j])
+        gate = W.get(synth.K_W_GATE, l, e) @ xm
+        up = W.get(synth.K_W_UP, l, e) @ xm
+        h16 = round_bf16(silu(gate) * up)
+        hs.append(h16)
+        moe = moe + wsel[j] * (W.get(synth.K_W_DOWN, l, e) @ h16)
+    srt = np.sort(r.astype(np.float64))[::-1]
+    margin = srt[k - 1] - srt[k] if k < E else np.inf
+    return MoeOut(r, sel, alt, margin, wsel, moe, np.stack(hs))
+
+
 def layer_forward(W: Weights, kv: PagedKV, l: int, x: np.ndarray, p: int, pt: np.ndarray,
                   take_alt: bool = False) -> LayerOut:
     """One decoder layer for one sequence whose new token sits at position p.
@@ -344,31 +386,10 @@ def layer_forward(W: Weights, kv: PagedKV, l: int, x: np.ndarray, p: int, pt: np
         xm = round_bf16(rmsnorm(x + attn, W.get(synth.K_MOE_NORM, l), s.rms_eps))
     else:
         xm = xn
-    r = (W.get(synth.K_ROUTER, l) @ xm).astype(np.float32)
-    sel = topk_desc(r, k)
-    alt = None
-    if k < E:
-        ext = topk_desc(r, k + 1)
-        alt = np.concatenate([ext[: k - 1], ext[k:]])
-        if take_alt:
-            if not float(r[ext[k - 1]]) - float(r[ext[k]]) <= ROUTE_TIE:
-                raise ValueError(f"layer {l}: no routing near-tie to take the alternative of")
-            sel = alt
-    wsel = softmax(r[sel].astype(np.float64))
-    moe = np.zeros(H)
-    hs = []
-    for j in range(k):
-        e = int(sel[j])
-        gate = W.get(synth.K_W_GATE, l, e) @ xm
-        up = W.get(synth.K_W_UP, l, e) @ xm
-        h16 = round_bf16(silu(gate) * up)
-        hs.append(h16)
-        moe = moe + wsel[j] * (W.get(synth.K_W_DOWN, l, e) @ h16)
-    srt = np.sort(r.astype(np.float64))[::-1]
-    margin = srt[k - 1] - srt[k] if k < E else np.inf
-    parts = {"xn": xn, "xm": xm, "q16": q16, "k16": k16, "v16": v16, "a16": a16, "attn": attn, "moe": moe,
-             "h16": np.stack(hs), "w": wsel}
-    return LayerOut((x + attn) + moe, r, sel, alt, margin, parts)
+    m = moe_path(W, l, xm, take_alt)
+    parts = {"xn": xn, "xm": xm, "q16": q16, "k16": k16, "v16": v16, "a16": a16, "attn": attn, "moe": m.moe,
+             "h16": m.h16, "w": m.w}
+    return LayerOut((x + attn) + m.moe, m.r, m.sel, m.sel_alt, m.margin, parts)
 
 
 def lm_logits(W: Weights, x: np.ndarray) -> np.ndarray:

@@ -126,19 +126,19 @@ def record(name: str, rep: Report, **extra) -> None:
         f.write(json.dumps(rec) + "\n")
 
 
-def seq_router_reference(W, x_l: np.ndarray, wo_gpu: np.ndarray, l: int) -> np.ndarray:
-    """Sequential block, isolated mode: the router logits of layer l recomputed in float64 from the
-    kernel's own MoE input.  The router reads bf16(rmsnorm(x_l + Wo attn)); the kernel's Wo attn
+def seq_moe_input(W, x_l: np.ndarray, wo_gpu: np.ndarray, l: int):
+    """Sequential block, isolated mode: (x_l + Wo attn, bf16(rmsnorm(that, g_moe))) as the kernel
+    forms them, in float64.  The MoE path reads the norm of x_l + Wo attn; the kernel's Wo attn
     (fp32, after its own bf16 rounding of the attention output) is a few ulps from the oracle's, and
     an element of the normalized input near a bf16 rounding midpoint may then round the other way,
-    moving router logit e by |Wr[e][i]| times one bf16 ulp.  So the reference takes the kernel's
-    Wo rows (read back from the workspace) and the same x_l the kernel read (the injected fp32 input,
-    or layer 0's embedding row), adds them in fp32 as the kernel does, and normalizes in float64 (as
-    the kernel does): what is left to compare is the router rows' fp32 accumulation."""
+    moving router logit e by |Wr[e][i]| times one bf16 ulp (and the experts' inputs with it).  So
+    the reference takes the kernel's Wo rows (read back from the workspace) and the same x_l the
+    kernel read (the injected fp32 input, or layer 0's embedding row), adds them in fp32 as the
+    kernel does, and normalizes in float64 as the kernel does: the oracle's MoE path (moe_path) from
+    that input leaves the router rows' and the experts' fp32 sums to compare."""
     s = W.shape
     xp = (x_l.astype(np.float32) + wo_gpu.astype(np.float32)).astype(np.float64)
-    xm = O.round_bf16(O.rmsnorm(xp, W.get(synth.K_MOE_NORM, l), s.rms_eps))
-    return W.get(synth.K_ROUTER, l) @ xm
+    return xp, O.round_bf16(O.rmsnorm(xp, W.get(synth.K_MOE_NORM, l), s.rms_eps))
 
 
 def _topk(r: np.ndarray, k: int) -> list:
@@ -308,24 +308,41 @@ class Runner:
             for l in range(L):
                 rep.route_checked += 1
                 if s.sequential:
+                    # the MoE path from the kernel's own MoE input (seq_moe_input); the layer's
+                    # output is then x_l + Wo attn (the kernel's, fp32) plus that path's sum
                     x_l = ref.trace["x_in"][(l, b)] if l == 0 else host[l, b]
-                    r_ref = seq_router_reference(self.W, x_l, attn_half[l, b], l)
+                    xp, xm_g = seq_moe_input(self.W, x_l, attn_half[l, b], l)
+                    mo = O.moe_path(self.W, l, xm_g)
+                    r_ref, r_sel, r_alt, r_margin = mo.r, mo.sel, mo.sel_alt, mo.margin
                 else:
-                    r_ref = ref.router_logits[l, b]
+                    r_ref, r_sel, r_alt, r_margin = ref.router_logits[l, b], ref.sel[l, b], ref.sel_alt[l, b], ref.margin[l, b]
                 dr = float(np.max(np.abs(rl[l, b].astype(np.float64) - r_ref)))
                 rep.max_router = max(rep.max_router, dr)
                 if not dr <= ROUTER_TOL:
                     rep.failures.append(f"{tag} layer {l} seq {b}: router logits differ by {dr:.2e}")
-                a, e = sorted(sel[l, b].tolist()), sorted(ref.sel[l, b].tolist())
+                a, e = sorted(sel[l, b].tolist()), sorted(r_sel.tolist())
                 took_alt = False
                 if a != e:
-                    if ref.margin[l, b] <= MARGIN and a == sorted(ref.sel_alt[l, b].tolist()):
+                    if r_margin <= MARGIN and a == sorted(r_alt.tolist()):
                         rep.route_ties += 1
                         took_alt = True
                     else:
-                        rep.failures.append(f"{tag} layer {l} seq {b}: experts {a} vs {e} (margin {ref.margin[l, b]:.2e})")
+                        rep.failures.append(f"{tag} layer {l} seq {b}: experts {a} vs {e} (margin {r_margin:.2e})")
                 # the layer's output residual
-                xo = ref.trace["x_in"][(l + 1, b)] if l + 1 < L else ref.trace["x_final"][b]
+                if s.sequential:
+                    if took_alt:
+                        mo = O.moe_path(self.W, l, xm_g, take_alt=True)
+                    xo = xp + mo.moe
+                    took_alt = False
+                    # the kernel's Wo output, which that reference takes as given, against the
+                    # oracle's, within the residual check's budget (the parallel block's residual
+                    # check holds the same attention half to it)
+                    rw = float(np.max(np.abs(attn_half[l, b] - ref.trace["attn"][(l, b)])) / np.max(np.abs(xo)))
+                    rep.max_x = max(rep.max_x, rw)
+                    if not rw <= X_TOL:
+                        rep.failures.append(f"{tag} layer {l} seq {b}: Wo output rel err {rw:.2e}")
+                else:
+                    xo = ref.trace["x_in"][(l + 1, b)] if l + 1 < L else ref.trace["x_final"][b]
                 if not took_alt:
                     rx = float(np.max(np.abs(xs[l + 1, b] - xo)) / np.max(np.abs(xo)))
                     rep.max_x = max(rep.max_x, rx)

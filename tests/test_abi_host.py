@@ -493,20 +493,43 @@ def test_sequential_block_schedule():
     pt, _ = p.schedule()
     prouter = (pt[:, 0] == 1) & (pt[:, 7] >= s.qkv_rows) & (pt[:, 1] > 0)
     assert np.array_equal(pt[prouter, 3], (pt[prouter, 1] - 1) * n_ctr_layer + c_wo)
-    # dedicated QKV units are not offered with the sequential block
-    with pytest.raises(mk.MkError) as e:
-        c.build_schedule(256, 2000, qkv_units=20)
-    assert e.value.code == mk.CODES["MK_ERR_UNSUPPORTED"]
-    # the shared pool is: each attention unit's pool task follows its Wo task (the router waits for
-    # the Wo rows, the pool task for the router), and the table still drains
-    c.build_schedule(256, 2000, pool_64ths=16)
-    assert c.validate() == c.info().n_tasks
+    # dedicated QKV units and the shared pool are not offered with the sequential block
+    for kw in ({"qkv_units": 20}, {"pool_64ths": 8}):
+        with pytest.raises(mk.MkError) as e:
+            c.build_schedule(256, 2000, **kw)
+        assert e.value.code == mk.CODES["MK_ERR_UNSUPPORTED"]
+
+
+def test_sequential_block_schedule_puts_every_unit_in_every_phase():
+    """From batch 2, every unit, per layer: its Wqkv rows (if any), its attention chunk, its Wo rows
+    (non-leads), its router rows (if any: after its Wo rows), its gate/up rows, its output rows;
+    attn_units still limits the attention to the first units.  At batch 1 the parallel split."""
+    from dataclasses import replace
+    s = replace(synth.MID, block="sequential")
+    c1 = _ctx(s, 1, 16, 64)
+    c1.build_schedule(256, 2000)
+    assert c1.info().n_attn < 200 and c1.validate() == c1.info().n_tasks
+    c = _ctx(s, 2, 16, 64)
+    c.build_schedule(256, 2000)
+    assert c.info().n_attn == 256 and c.validate() == c.info().n_tasks
     tasks, qoff = c.schedule()
-    for q in range(len(qoff) - 1):
-        ops = [int(o) for o in tasks[qoff[q]:qoff[q + 1], 0]]
-        for i, o in enumerate(ops):
-            if o == 7:   # GUTAIL
-                assert 6 in ops[:i] and ops[i - 1] == 6, (q, ops[:i + 1])
+    PRE, ATTN, GATEUP, OUT, WO, KVW = 1, 2, 3, 4, 6, 8
+    for q in range(256):
+        t = tasks[qoff[q]:qoff[q + 1]]
+        lay0 = t[t[:, 1] == 0]
+        ops = [int(o) for o in lay0[:, 0]]
+        plain = [o for o in ops if o != KVW]
+        assert ATTN in plain and GATEUP in plain and OUT in plain, (q, ops)
+        assert plain.index(ATTN) < plain.index(GATEUP) < plain.index(OUT)
+        pres = lay0[lay0[:, 0] == PRE]
+        for r in pres:
+            i = plain.index(PRE) if r[7] < s.qkv_rows else len(plain) - 1 - plain[::-1].index(PRE)
+            if r[7] < s.qkv_rows:
+                assert i < plain.index(ATTN)
+            else:
+                assert WO in plain[:i] and i < plain.index(GATEUP), (q, plain)
+    c.build_schedule(256, 2000, attn_units=100)
+    assert c.info().n_attn == 100 and c.validate() == c.info().n_tasks
 
 
 def test_sequential_block_binds_eight_tensors_per_layer():

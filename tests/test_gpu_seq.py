@@ -70,10 +70,12 @@ def test_seq_30b_bs1_8k_isolated_2_steps():
     _check("moe30b_8k_seq_isolated_2", rep)
 
 
-@pytest.mark.parametrize("pool", [16])
-def test_seq_mid_isolated_with_the_shared_gate_up_pool(pool):
-    """The attention units, idle while the sequential block's MoE path runs, claim gate/up rows from
-    the shared pool after their Wo rows."""
+def test_seq_30b_bs8_ragged_isolated_1_step():
+    """Batch 8 at the 30B shape: the schedule where every unit takes part in every phase."""
+    import torch
     from tests import parity
-    rep = parity.run(synth.workload("mid_seq"), steps=8, mode="isolated", log=_log, pool_64ths=pool)
-    _check(f"mid_seq_isolated_8_pool{pool}", rep)
+    gc.collect()
+    torch.cuda.empty_cache()
+    rep = parity.run(synth.workload("moe30b_bs8_ragged_seq"), steps=1, mode="isolated", log=_log)
+    assert rep.route_checked == 8 * 48
+    _check("moe30b_bs8_ragged_seq_isolated_1", rep)

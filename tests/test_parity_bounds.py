@@ -1,4 +1,4 @@
-"""The parity harness's reference for the sequential block's router, on the CPU."""
+"""The parity harness's reference for the sequential block's MoE path, on the CPU."""
 from dataclasses import replace
 
 import numpy as np
@@ -16,8 +16,12 @@ def test_sequential_router_reference_equals_the_oracle_on_the_oracle_inputs():
     kv = O.PagedKV(s, 2)
     ref = O.decode_step(W, kv, [17], np.arange(2, dtype=np.int32)[None], [0], trace=True)
     for l in range(s.n_layers):
-        r = parity.seq_router_reference(W, ref.trace["x_in"][(l, 0)], ref.trace["attn"][(l, 0)], l)
-        assert np.max(np.abs(r - ref.router_logits[l, 0])) <= 2e-4
+        xp, xm = parity.seq_moe_input(W, ref.trace["x_in"][(l, 0)], ref.trace["attn"][(l, 0)], l)
+        mo = O.moe_path(W, l, xm)
+        assert np.max(np.abs(mo.r.astype(np.float64) - ref.router_logits[l, 0])) <= 2e-4
+        # and the layer output from it is the oracle's, but for the fp32 sum x + Wo attn
+        out = ref.trace["x_in"][(l + 1, 0)] if l + 1 < s.n_layers else ref.trace["x_final"][0]
+        assert np.max(np.abs(xp + mo.moe - out)) <= 1e-5 * np.max(np.abs(out))
 
 
 def test_sequential_router_reference_follows_the_kernel_wo_output():
@@ -28,7 +32,7 @@ def test_sequential_router_reference_follows_the_kernel_wo_output():
     kv = O.PagedKV(s, 2)
     ref = O.decode_step(W, kv, [17], np.arange(2, dtype=np.int32)[None], [0], trace=True)
     x, wo = ref.trace["x_in"][(0, 0)], ref.trace["attn"][(0, 0)].copy()
-    r0 = parity.seq_router_reference(W, x, wo, 0)
+    r0 = O.moe_path(W, 0, parity.seq_moe_input(W, x, wo, 0)[1]).r.astype(np.float64)
     wo[3] += 0.25 * np.max(np.abs(x + wo))
-    r1 = parity.seq_router_reference(W, x, wo, 0)
+    r1 = O.moe_path(W, 0, parity.seq_moe_input(W, x, wo, 0)[1]).r.astype(np.float64)
     assert np.max(np.abs(r1 - r0)) > 1e-3
