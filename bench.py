@@ -281,7 +281,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--workload", default="moe30b_8k")
+    ap.add_argument("--workload", default="moe30b_8k",
+                    help="tiny, mid, moe30b_8k, moe30b_bs8_ragged or moe30b_256k; suffixes _seq (the sequential "
+                         "block), _fp8 / _fp4 (quantized weights), e.g. moe30b_8k_fp4, moe30b_bs8_ragged_seq")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=25.0)
     ap.add_argument("--trace", default="", help="write a Perfetto timeline of one extra step to this path")
@@ -433,7 +435,8 @@ def main():
                  {"fp8": "as E4M3 codes (N(0, 32) rounded) times row scales near 0.02/32, ",
                   "fp4": "as E2M1 codes (N(0, 1.5) rounded) times row scales near 0.02/1.5, "}.get(s.weights, "N(0, 0.02), ") + "synthetic N(0, 1) KV, shuffled pages"),
         "config": {
-            "workload": f"{w.name}: {s.n_layers} layers, hidden {s.hidden}, {s.n_q_heads}q/{s.n_kv_heads}kv x "
+            "workload": f"{w.name}: {'sequential block, ' if s.sequential else ''}{s.n_layers} layers, hidden {s.hidden}, "
+                        f"{s.n_q_heads}q/{s.n_kv_heads}kv x "
                         f"{s.head_dim}, {s.n_experts} experts top-{s.top_k} inter {s.inter}, vocab {s.vocab}; "
                         f"batch {B}, context {w.context if B > 1 else w.context[0]}, page {s.page_size}",
             "batch": B,
@@ -450,7 +453,7 @@ def main():
             "algorithmic_bytes_per_launch": round(bytes_step * spl),
             "launch_ms": round(launch_ms, 4),
             "steps_per_launch": spl,
-            "kernel": KERNELS[s.weights],
+            "kernel": KERNELS[s.weights] + ("_seq" if s.sequential else ""),
         },
         "cpu_baseline": cpu,
     }
