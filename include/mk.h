@@ -2,7 +2,8 @@
  * mk.h -- C ABI of the persistent MoE decode megakernel for MI355X (gfx950).
  *
  * One call to mk_decode_step runs one BF16 autoregressive decode step of a
- * parallel-block mixture-of-experts decoder (RMSNorm, QKV projection, rotary
+ * parallel-block mixture-of-experts decoder, or of its sequential-block form
+ * (mk_config.block_style) (RMSNorm, QKV projection, rotary
  * embedding, paged split-KV attention, router top-k, expert gather with
  * gate/up/down projections, residuals, LM head) as a single persistent kernel:
  * one workgroup per compute unit works through a task table that the host
@@ -33,7 +34,8 @@
  *  - "stream" = a hipStream_t passed as void*; NULL means the default stream.
  *    Work is enqueued asynchronously on it.
  *  - Matrices are row-major [out][in] bfloat16 (raw 16-bit patterns), or, in
- *    the FP8 weight format, E4M3 codes with per-row scales (mk_bind).
+ *    the FP8 / FP4 weight formats, E4M3 / packed E2M1 codes with per-row
+ *    scales (mk_bind).
  */
 #ifndef MK_H
 #define MK_H
