@@ -549,3 +549,12 @@ def test_sequential_block_binds_eight_tensors_per_layer():
     assert "n_layers" not in str(e.value)
     assert len(s.bind_order()) == 3 + 8 * s.n_layers
     assert s.bind_order()[3 + 7 * s.n_layers:] == [(synth.K_MOE_NORM, l) for l in range(s.n_layers)]
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
+def test_sequential_block_is_built_for_bf16_weights_only(fmt):
+    from dataclasses import replace
+    s = replace(synth.TINY, block="sequential", weights=fmt)
+    with pytest.raises(mk.MkError) as e:
+        _ctx(s, 1, 8, 8)
+    assert e.value.code == mk.CODES["MK_ERR_UNSUPPORTED"]

@@ -79,3 +79,14 @@ def test_seq_30b_bs8_ragged_isolated_1_step():
     rep = parity.run(synth.workload("moe30b_bs8_ragged_seq"), steps=1, mode="isolated", log=_log)
     assert rep.route_checked == 8 * 48
     _check("moe30b_bs8_ragged_seq_isolated_1", rep)
+
+
+def test_seq_mid_free_running_no_teacher_forcing():
+    """Up to 64 steps, each side feeding its own greedy token until they first disagree: the
+    agreement length is recorded, and the disagreement must be admissible (a near-tie of the top-2
+    logits, or a routing divergence within the measured router drift)."""
+    from tests import parity
+    rep = parity.run(synth.workload("mid_seq"), mode="free", log=_log, teacher=False)
+    assert rep.agree_steps == 64 or rep.disagree_cause, rep.summary()
+    _check("mid_seq_free_no_teacher", rep)
+    _log(f"free-running agreement: {rep.agree_steps} of 64 steps ({rep.disagree_cause or 'no disagreement'})")
