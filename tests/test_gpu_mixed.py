@@ -94,13 +94,14 @@ def test_chunked_prefill_equals_token_at_a_time():
             assert g_next == int(ref.next_token[0])
 
 
-@pytest.mark.parametrize("shape_name", ["mid", "mid_fp8", "mid_fp4"])
+@pytest.mark.parametrize("shape_name", ["mid", "mid_fp8", "mid_fp4", "mid_seq"])
 def test_decode_and_prefill_chunk_in_one_step(shape_name):
     """One step: sequence A decodes at position 300 while sequence B's first 7 prompt tokens run as
     entries 1..7 (B's row, positions 0..6).  Against the oracle's step over the same entries in order."""
     from dataclasses import replace
     from persistent_moe_decode_amd.runtime import DeviceDecoder
-    s = synth.MID if shape_name == "mid" else replace(synth.MID, weights=shape_name.split("_")[1])
+    suffix = shape_name.split("_")[1] if "_" in shape_name else ""
+    s = replace(synth.MID, block="sequential") if suffix == "seq" else replace(synth.MID, weights=suffix or "bf16")
     w = synth.Workload("mixed_" + shape_name, s, batch=8, steps=2, context=[300] + [0] * 7)
     _log(f"workload {w.name}: A at 300, B positions 0..6")
     dec = DeviceDecoder(w)
