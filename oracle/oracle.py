@@ -39,6 +39,13 @@ product then runs as with bfloat16 weights.  Router, norm gains and embedding
 stay bfloat16.  FP4 weights (``weights="fp4"``) are the same with OCP E2M1
 codes, two a byte (the even element in the low nibble).
 
+Top-p sampling (top_p_nucleus, sample_token_top_p): the pages call the
+engine's sampling options incomplete (ainews.surl.tw page, fourth paragraph)
+and define none.  The reading taken: at temperature T the nucleus is every
+token whose scaled logit is at least the largest threshold keeping mass
+>= top_p of softmax(logits / T), tokens tied at the threshold included, and
+the draw is the Gumbel-max rule restricted to the nucleus.
+
 Sequential block (a shape with ``block="sequential"``): the pages tailor the
 engine to one model and ask whether it generalizes to other MoE models
 (ainews.surl.tw page, fourth paragraph), naming none.  The reading taken: the
@@ -499,6 +506,34 @@ def sample_token(logits: np.ndarray, temperature: float, seed: int, pos: int, b:
         return int(np.argmax(z)), z
     v = z / temperature + gumbel_noise(seed, pos, b, max_batch, z.size)
     return int(np.argmax(v)), v
+
+
+def top_p_nucleus(logits: np.ndarray, temperature: float, top_p: float) -> np.ndarray:
+    """Boolean mask of the nucleus: with q = softmax(logits / T), every token whose scaled logit is
+    at least the largest threshold tau (a scaled logit value) such that the tokens at or above tau
+    hold mass >= top_p.  Tokens tied at tau are all in (the nucleus is a set of values, not of
+    ids).  top_p >= 1: every token."""
+    z = np.asarray(logits, dtype=np.float64) / temperature
+    if top_p >= 1.0:
+        return np.ones(z.size, dtype=bool)
+    q = np.exp(z - np.max(z))
+    q = q / q.sum()
+    vals, inv = np.unique(-z, return_inverse=True)     # distinct scaled logits, largest first
+    mass = np.bincount(inv, weights=q)                 # probability of each distinct value
+    k = int(np.searchsorted(np.cumsum(mass), top_p))   # first value whose cumulative mass >= top_p
+    k = min(k, vals.size - 1)
+    return z >= -vals[k]
+
+
+def sample_token_top_p(logits: np.ndarray, temperature: float, top_p: float, seed: int, pos: int, b: int,
+                       max_batch: int):
+    """Top-p sampling by the Gumbel-max rule restricted to the nucleus: argmax over the nucleus of
+    logits_i / T + g_i (ties to the lowest id), which draws from softmax(logits / T) renormalized
+    over the nucleus.  Returns (token, nucleus mask)."""
+    nuc = top_p_nucleus(logits, temperature, top_p)
+    v = np.asarray(logits, dtype=np.float64) / temperature + gumbel_noise(seed, pos, b, max_batch, len(logits))
+    v = np.where(nuc, v, -np.inf)
+    return int(np.argmax(v)), nuc
 
 
 def sol_tokens_per_s(bandwidth_bytes_per_s: float, bytes_per_step: float, batch: int = 1) -> float:

@@ -777,3 +777,66 @@ def test_fp4_step_bytes_30b_shape():
     m = lambda r, c: r * c / 2 + 4 * r
     want = L * (m(qkv, H) + m(H, ad) + 2 * E * H + 8 * (2 * m(I, H) + m(H, I)) + 2 * H) + m(V, H) + 2 * H
     assert s.active_weight_bytes(8) == want
+
+
+# --------------------------------------------------------------------------- top-p sampling
+
+def _nucleus_brute(z_over_t: np.ndarray, p: float) -> set:
+    """The nucleus by its definition, by trying every threshold: the largest value t among the
+    scaled logits with mass(z >= t) >= p; the tokens at or above it."""
+    q = np.exp(z_over_t - z_over_t.max())
+    q = q / q.sum()
+    best = None
+    for t in sorted(set(z_over_t.tolist())):
+        if q[z_over_t >= t].sum() >= p:
+            best = t
+    return set(np.flatnonzero(z_over_t >= best).tolist())
+
+
+def test_top_p_nucleus_brute_force_on_small_vocabularies():
+    rng = np.random.default_rng(21)
+    for trial in range(300):
+        V = int(rng.integers(1, 12))
+        z = np.round(rng.standard_normal(V) * 2, 1)      # rounding makes ties common
+        T = float(rng.choice([0.5, 1.0, 2.0]))
+        p = float(rng.uniform(0.05, 0.999))
+        got = set(np.flatnonzero(O.top_p_nucleus(z, T, p)).tolist())
+        assert got == _nucleus_brute(z / T, p), (trial, z, T, p)
+
+
+def test_top_p_closed_cases():
+    z = np.array([3.0, 1.0, 1.0, -2.0])
+    # p = 1: everything; p tiny: the top value only; mass of the top value exactly p: just it
+    assert O.top_p_nucleus(z, 1.0, 1.0).all()
+    assert O.top_p_nucleus(z, 1.0, 1e-9).tolist() == [True, False, False, False]
+    q = np.exp(z - 3.0) / np.exp(z - 3.0).sum()
+    assert O.top_p_nucleus(z, 1.0, q[0]).tolist() == [True, False, False, False]
+    # just above the top mass: the tied pair comes in together
+    assert O.top_p_nucleus(z, 1.0, q[0] + 1e-12).tolist() == [True, True, True, False]
+
+
+def test_top_p_sampling_reduces_to_plain_and_greedy():
+    rng = np.random.default_rng(5)
+    logits = rng.standard_normal(1000) * 3
+    for pos in range(5):
+        tok1, _ = O.sample_token_top_p(logits, 0.8, 1.0, 0x5EED, pos, 0, 1)
+        tok0, _ = O.sample_token(logits, 0.8, 0x5EED, pos, 0, 1)
+        assert tok1 == tok0
+        tokg, nuc = O.sample_token_top_p(logits, 0.8, 1e-12, 0x5EED, pos, 0, 1)
+        assert tokg == int(np.argmax(logits)) and nuc.sum() == 1
+
+
+def test_top_p_draw_frequencies_follow_the_renormalized_distribution():
+    """Many draws (different positions) from a small vocabulary: frequencies within 5 sigma of
+    softmax(z / T) restricted to the nucleus and renormalized."""
+    z = np.array([2.0, 1.5, 1.0, 0.0, -1.0, -3.0])
+    T, p, n = 1.0, 0.8, 20000
+    nuc = O.top_p_nucleus(z, T, p)
+    q = np.where(nuc, np.exp(z / T), 0.0)
+    q = q / q.sum()
+    counts = np.zeros(z.size)
+    for pos in range(n):
+        counts[O.sample_token_top_p(z, T, p, 7, pos, 0, 1)[0]] += 1
+    sigma = np.sqrt(n * q * (1 - q)) + 1e-9
+    assert np.all(np.abs(counts - n * q) <= 5 * sigma + 1e-9), (counts, n * q)
+    assert np.all(counts[~nuc] == 0)
