@@ -354,6 +354,20 @@ int mk_set_trace(mk_ctx* ctx, uint64_t* d_records, int64_t capacity);
  * applies from the next step. */
 int mk_set_sampling(mk_ctx* ctx, double temperature, uint64_t seed);
 
+/* Top-p (nucleus) sampling on top of mk_set_sampling's temperature draw:
+ * with temperature T > 0 and top_p < 1, the draw is the same Gumbel-max rule
+ * restricted to the nucleus, every token whose logit / T is at least the
+ * largest threshold that keeps probability mass >= top_p of softmax(logits / T)
+ * (tokens tied at the threshold included).  The masses are summed as 32-bit
+ * fixed-point integers, so the threshold does not depend on summation order;
+ * it can differ from an exact-arithmetic one only where the mass of the tokens
+ * at a threshold is within that rounding of top_p.  top_p = 1 (the default)
+ * switches it off; it has no effect at temperature 0.
+ * Errors: MK_ERR_INVALID_ARG for a null context or top_p outside (0, 1].
+ * Source: the pages call the engine's sampling options incomplete
+ * (ainews.surl.tw, paragraph 4); the nucleus rule is this library's reading. */
+int mk_set_top_p(mk_ctx* ctx, float top_p);
+
 /* Thread-local text of the last failure on the calling thread. */
 const char* mk_last_error_message(void);
 /* Frees the context's host state (device buffers stay the caller's); NULL is a no-op. */

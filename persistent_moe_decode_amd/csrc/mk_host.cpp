@@ -77,6 +77,7 @@ struct mk_ctx {
   uint32_t epoch = 0;
   int64_t spin_us = 2000000;
   double inv_temp = 0.0;  // sampling (0: greedy)
+  float top_p = 1.0f;     // sampling: nucleus mass (1: off)
   uint64_t seed = 0;
   const float* x_in = nullptr;
   uint64_t* trace = nullptr;
@@ -629,7 +630,8 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
   size_t c_attn = std::max((size_t)kWaves * (group * f.head_dim + 2 * kMaxGroup) * 4,
                            align_up((size_t)n_attn * kMaxGroup * 2 * 4, 16) + (size_t)kThreads * 16);
   const size_t c_mfma = B >= 2 ? (size_t)kMfmaRedBytes : 0;  // partial tiles of split dense rows
-  size_t c_bytes = align_up(std::max({c_gu, c_out, c_lm, c_attn, c_mfma, (size_t)kTopKScratch}), 256);
+  const size_t c_topp = (size_t)(kTopPBins + kWaves) * 8;  // the top-p histogram and block sums of the last LM-head unit
+  size_t c_bytes = align_up(std::max({c_gu, c_out, c_lm, c_attn, c_mfma, c_topp, (size_t)kTopKScratch}), 256);
   c->lds_b = (int)a_bytes;
   c->lds_c = (int)(a_bytes + b_bytes);
   c->lds_p = (int)(a_bytes + b_bytes + c_bytes);
@@ -751,6 +753,13 @@ extern "C" int mk_set_sampling(mk_ctx* c, double temperature, uint64_t seed) {
   if (temperature > 0.0 && !(1.0 / temperature < HUGE_VAL)) return fail(MK_ERR_INVALID_ARG, "temperature too small");
   c->inv_temp = temperature > 0.0 ? 1.0 / temperature : 0.0;
   c->seed = seed;
+  return MK_OK;
+}
+
+extern "C" int mk_set_top_p(mk_ctx* c, float top_p) {
+  if (!c) return fail(MK_ERR_INVALID_ARG, "null context");
+  if (!(top_p > 0.0f && top_p <= 1.0f)) return fail(MK_ERR_INVALID_ARG, "top_p must be in (0, 1]");
+  c->top_p = top_p;
   return MK_OK;
 }
 
@@ -946,6 +955,7 @@ static int launch_steps(mk_ctx* c, int32_t n, int32_t steps, const int32_t* d_to
   a.spin_limit_ticks = (uint64_t)c->spin_us * 100;  // s_memrealtime runs at 100 MHz
   a.inv_temp = c->inv_temp;
   a.seed = c->seed;
+  a.top_p = c->top_p;
   const hipStream_t hs = (hipStream_t)stream;
   int r = c->cfg.weight_format == MK_WEIGHTS_FP8_E4M3   ? mkk_launch_step_fp8(&a, c->ncu, c->lds_bytes, hs)
           : c->cfg.weight_format == MK_WEIGHTS_FP4_E2M1 ? mkk_launch_step_fp4(&a, c->ncu, c->lds_bytes, hs)

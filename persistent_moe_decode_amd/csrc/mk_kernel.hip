@@ -2351,12 +2351,14 @@ struct JobLM {
   const uint16_t* xs;
   float* lmv;
   float* logits;
+  bool coh;  // top-p: the last LM-head unit reads every unit's logits, so they go out device-coherent
   DEV const gu4* row(int i) const { return (const gu4*)(W + (size_t)(r0 + i) * wrow_bytes(K)); }
   DEV float scale(int i) const { return sc[r0 + i]; }
   DEV int nx(int) const { return 1 << 30; }
   DEV const uint4* x(int, int t) const { return (const uint4*)(xs + (size_t)t * K); }
   DEV void emit(int i, int t, float v) const {
-    logits[(size_t)t * V + r0 + i] = v;
+    if (coh) st_coh(logits + (size_t)t * V + r0 + i, v);
+    else logits[(size_t)t * V + r0 + i] = v;
     lmv[(size_t)i * maxB + t] = v;
   }
 };
@@ -2384,6 +2386,100 @@ DEV float sample_score(const KArgs& a, float x, int b, int i) {
   const uint64_t n = (p * (uint64_t)a.max_batch + (uint64_t)b) * (uint64_t)a.V + (uint64_t)i;
   const double u = ((double)(splitmix64_at(a.seed, n) >> 11) + 0.5) * 0x1.0p-53;
   return (float)((double)x * a.inv_temp - log(-log(u)));
+}
+
+// Top-p sampling for slot b, by the last LM-head unit once every unit's logits
+// are stored: the nucleus is every token whose scaled logit s = x / T is at
+// least the largest threshold keeping mass >= top_p of softmax(s), tokens tied
+// at it included; the draw is the Gumbel-max argmax within it.  No sort: the
+// masses exp(s - max) as 32-bit fixed point (integer sums, so no order
+// dependence) go into a histogram over the ordered bits of s, 11 bits a pass
+// from the top (three passes), which pins the threshold's key; one more pass
+// takes the argmax of the scores of the tokens at or above it.  hist: LDS,
+// kTopPBins 64-bit words.  Returns the token, in every thread.
+DEV void block_argmax(float& v, int& i, float* red);
+
+DEV float scaled_logit(const KArgs& a, const float* lg, int i) {
+  const float x = ld_coh(lg + i);
+  return x != x ? kNegInf : (float)((double)x * a.inv_temp);
+}
+
+DEV uint64_t block_sum_u64(uint64_t v, uint64_t* scratch) {
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  __syncthreads();
+  if ((tid() & 63) == 0) scratch[tid() >> 6] = v;
+  __syncthreads();
+  uint64_t t = 0;
+  for (int w = 0; w < kWaves; ++w) t += scratch[w];
+  __syncthreads();
+  return t;
+}
+
+DEV int top_p_draw(const KArgs& a, int b, uint64_t* hist, float* red) {
+  const int V = a.V;
+  const float* lg = a.logits + (size_t)b * V;
+  uint64_t* scratch = hist + kTopPBins;           // kWaves words for the block sums
+  // the largest scaled logit
+  float smax = kNegInf;
+  int imax = 0;
+  for (int i = tid(); i < V; i += kThreads) {
+    const float sv = scaled_logit(a, lg, i);
+    if (better(sv, i, smax, imax)) { smax = sv; imax = i; }
+  }
+  block_argmax(smax, imax, red);
+  // three radix passes: 11, 11 and 10 bits of the key, each among the tokens whose
+  // higher bits equal the threshold's so far; `above` is the mass of the tokens
+  // whose key lies above every bucket of this pass
+  uint32_t prefix = 0;
+  uint64_t above = 0, need = 0;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int nb = pass == 2 ? 1024 : 2048;
+    for (int k = tid(); k < nb; k += kThreads) hist[k] = 0;
+    __syncthreads();
+    uint64_t mine = 0;
+    for (int i = tid(); i < V; i += kThreads) {
+      const float sv = scaled_logit(a, lg, i);
+      const uint32_t key = topk_key(sv);
+      if (pass > 0 && (key >> (shift + (pass == 1 ? 11 : 10))) != prefix) continue;
+      const uint64_t m = (uint64_t)(__expf(sv - smax) * 4294967296.0f);
+      atomicAdd((unsigned long long*)(hist + ((key >> shift) & (uint32_t)(nb - 1))), (unsigned long long)m);
+      mine += m;
+    }
+    if (pass == 0) {
+      const uint64_t z = block_sum_u64(mine, scratch);
+      need = (uint64_t)ceil((double)a.top_p * (double)z);
+    }
+    __syncthreads();
+    if (tid() == 0) {
+      // the highest bucket at which the mass from the top reaches `need`
+      uint64_t acc = above;
+      int k = nb - 1;
+      for (; k > 0; --k) {
+        if (acc + hist[k] >= need) break;
+        acc += hist[k];
+      }
+      scratch[0] = (uint64_t)k;
+      scratch[1] = acc;
+    }
+    __syncthreads();
+    prefix = (prefix << (pass == 2 ? 10 : 11)) | (uint32_t)scratch[0];
+    above = scratch[1];
+    __syncthreads();
+  }
+  // prefix is now the threshold's whole key: the draw among the tokens at or above it
+  float v = kNegInf;
+  int pick = 0x7fffffff;
+  for (int i = tid(); i < V; i += kThreads) {
+    const float sv = scaled_logit(a, lg, i);
+    if (topk_key(sv) < prefix) continue;
+    float x = ld_coh(lg + i);
+    if (x != x) x = kNegInf;
+    const float sc = sample_score(a, x, b, i);
+    if (better(sc, i, v, pick)) { v = sc; pick = i; }
+  }
+  block_argmax(v, pick, red);
+  return pick;
 }
 
 // Block-wide argmax (value desc, index asc); result valid in all threads.
@@ -2422,6 +2518,8 @@ TASK void task_lmhead(const KArgs& a, const Task& t, const Lds& s, int qi) {
   j.xs = xs;
   j.lmv = (float*)s.C;
   j.logits = a.logits;
+  const bool top_p = a.inv_temp != 0.0 && a.top_p < 1.0f;
+  j.coh = top_p;
   // rows in passes of at most kLmPass (bounds the LDS copy of the logits); thread 0
   // keeps the running best of each sequence
   float best_v[kMaxBatch];
@@ -2464,12 +2562,16 @@ TASK void task_lmhead(const KArgs& a, const Task& t, const Lds& s, int qi) {
     for (int b = 0; b < a.n; ++b) {
       float v = kNegInf;
       int i = 0x7fffffff;
-      for (int k = tid(); k < a.n_lm; k += kThreads) {
-        const float x = ld_coh(a.lm_part + ((size_t)k * a.max_batch + b) * 2);
-        const int xi = (int)ld_coh((const uint32_t*)a.lm_part + ((size_t)k * a.max_batch + b) * 2 + 1);
-        if (better(x, xi, v, i)) { v = x; i = xi; }
+      if (top_p) {
+        i = top_p_draw(a, b, (uint64_t*)s.C, s.red);
+      } else {
+        for (int k = tid(); k < a.n_lm; k += kThreads) {
+          const float x = ld_coh(a.lm_part + ((size_t)k * a.max_batch + b) * 2);
+          const int xi = (int)ld_coh((const uint32_t*)a.lm_part + ((size_t)k * a.max_batch + b) * 2 + 1);
+          if (better(x, xi, v, i)) { v = x; i = xi; }
+        }
+        block_argmax(v, i, s.red);
       }
-      block_argmax(v, i, s.red);
       if (tid() == 0 && a.next_tok) st_coh((uint32_t*)a.next_tok + (size_t)a.step * a.n + b, (uint32_t)i);
     }
   }

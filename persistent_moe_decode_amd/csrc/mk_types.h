@@ -24,6 +24,7 @@ constexpr int kGuPass = 256;       // gate/up virtual rows per pass of one task
 constexpr int kGuItem = 16;        // gate/up virtual rows per item of the shared pool
 constexpr int kLmPass = 512;       // LM head rows per pass of one task
 constexpr int kMfmaRedBytes = 16 * 1024; // region C bytes for the matrix-core path's partial tiles (batch >= 2)
+constexpr int kTopPBins = 2048;  // top-p threshold search: buckets per radix pass (11 bits)
 constexpr int kTraceWords = 8;     // per task: fetch, ready, 4 phase marks, done, spare
 constexpr int kLdsB = 8192;        // LDS region B: top-k state, flags, reductions, router logits
 constexpr int kTopKScratch = 4 * kMaxExperts + kMaxBatch * kMaxExperts + kWaves * 4 * kMaxTopK * 4;  // region C bytes the top-k borrows
@@ -133,6 +134,7 @@ struct KArgs {
   uint64_t spin_limit_ticks; // s_memrealtime ticks (100 MHz)
   double inv_temp;           // sampling: 1 / temperature, or 0 for the greedy argmax
   uint64_t seed;             // sampling: generator seed
+  float top_p;               // sampling: nucleus mass (1: every token)
   int32_t nsteps;            // decode steps in this launch
   int32_t kv_sync;           // mixed step: entries may share a sequence; attention reads pages only after
                              // every entry's new K/V is written (the KVW tasks), and no page is read before

@@ -93,6 +93,7 @@ def lib():
         "mk_set_layer_inputs": [P, P],
         "mk_set_trace": [P, P, I64],
         "mk_set_sampling": [P, ctypes.c_double, ctypes.c_uint64],
+        "mk_set_top_p": [P, ctypes.c_float],
         "mk_get_schedule_info": [P, ctypes.POINTER(ScheduleInfo)],
         "mk_copy_schedule": [P, pi32, I64, pi32, I64],
         "mk_validate_schedule": [P, pi32],
@@ -253,6 +254,10 @@ class Context:
     def set_sampling(self, temperature: float, seed: int = 0):
         """Temperature 0 (the default) is the greedy argmax; > 0 samples softmax(logits / T)."""
         check(lib().mk_set_sampling(self.h, float(temperature), int(seed) & ((1 << 64) - 1)), "mk_set_sampling")
+
+    def set_top_p(self, top_p: float):
+        """Nucleus mass for sampling at temperature > 0 (1, the default: every token)."""
+        check(lib().mk_set_top_p(self.h, float(top_p)), "mk_set_top_p")
 
     def set_spin_limit_us(self, us: int):
         check(lib().mk_set_spin_limit_us(self.h, us), "mk_set_spin_limit_us")

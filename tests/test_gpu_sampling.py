@@ -143,3 +143,41 @@ def test_zero_temperature_is_the_greedy_argmax():
         assert tok == [int(np.argmax(got[b])) for b in range(2)]
     finally:
         dec.close()
+
+
+@pytest.mark.parametrize("top_p", [0.9, 0.5])
+def test_top_p_draw_follows_the_nucleus_of_the_device_logits(top_p):
+    """mk_set_top_p: each step's device token is the Gumbel-max argmax within the nucleus that the
+    oracle's definition gives for the device's own logits; only where the mass at the threshold is
+    within the fixed-point rounding of top_p may the device take the neighbouring nucleus."""
+    from oracle import oracle as O
+    from persistent_moe_decode_amd.runtime import DeviceDecoder
+    w = synth.Workload("mid_top_p", synth.MID, batch=3, steps=6, context=[900, 17, 1500])
+    n = w.batch
+    dec = DeviceDecoder(w)
+    dec.fill_synthetic_kv()
+    dec.ctx.set_sampling(T, SEED)
+    dec.ctx.set_top_p(top_p)
+    mb = dec.ctx.cfg.max_batch
+    toks = [int(w.prompt(b)[w.context[b]]) for b in range(n)]
+    exact = near = 0
+    try:
+        for step in range(w.steps):
+            lens = [c + step for c in w.context]
+            got, dev_tok = _device_step(dec, toks, lens, n)
+            for b in range(n):
+                lg = got[b].astype(np.float32).astype(np.float64)
+                want, nuc = O.sample_token_top_p(lg, T, top_p, SEED, lens[b], b, mb)
+                if dev_tok[b] == want:
+                    exact += 1
+                    continue
+                # the neighbouring nuclei: the threshold one distinct value lower or higher
+                lo, _ = O.sample_token_top_p(lg, T, min(1.0, top_p * (1 + 1e-6)), SEED, lens[b], b, mb)
+                hi, _ = O.sample_token_top_p(lg, T, top_p * (1 - 1e-6), SEED, lens[b], b, mb)
+                assert dev_tok[b] in (lo, hi), (step, b, dev_tok[b], want, int(nuc.sum()))
+                near += 1
+            toks = dev_tok
+    finally:
+        dec.close()
+    print(f"top-p {top_p}: {exact} draws equal, {near} at a threshold near-tie", flush=True)
+    assert exact >= 3 * w.steps - 1
