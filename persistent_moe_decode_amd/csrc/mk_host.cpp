@@ -630,7 +630,9 @@ extern "C" int mk_build_schedule(mk_ctx* c, const mk_schedule_params* params, si
   size_t c_attn = std::max((size_t)kWaves * (group * f.head_dim + 2 * kMaxGroup) * 4,
                            align_up((size_t)n_attn * kMaxGroup * 2 * 4, 16) + (size_t)kThreads * 16);
   const size_t c_mfma = B >= 2 ? (size_t)kMfmaRedBytes : 0;  // partial tiles of split dense rows
-  const size_t c_topp = (size_t)(kTopPBins + kWaves) * 8;  // the top-p histogram and block sums of the last LM-head unit
+  // the top-p histogram and block sums of the last LM-head unit (whole KiB, so the region that
+  // follows keeps the KiB alignment the prefetch region is cut in)
+  const size_t c_topp = align_up((size_t)(kTopPBins + kWaves) * 8, 1024);
   size_t c_bytes = align_up(std::max({c_gu, c_out, c_lm, c_attn, c_mfma, c_topp, (size_t)kTopKScratch}), 256);
   c->lds_b = (int)a_bytes;
   c->lds_c = (int)(a_bytes + b_bytes);
