@@ -21,14 +21,19 @@ def _kv_slots(dec, n, lens, steps):
     return np.stack(out)
 
 
-@pytest.mark.parametrize("batch,context,pool", [(1, [2048], 0), (3, [900, 17, 1500], 0), (3, [900, 17, 1500], 16)])
-def test_steps_in_one_launch_equal_single_launches(batch, context, pool):
-    """pool: 64ths of the gate/up rows in the shared pool (its claim counters run across the steps)."""
+@pytest.mark.parametrize("batch,context,pool,top_p", [(1, [2048], 0, None), (3, [900, 17, 1500], 0, None),
+                                                     (3, [900, 17, 1500], 16, None), (3, [900, 17, 1500], 0, 0.9)])
+def test_steps_in_one_launch_equal_single_launches(batch, context, pool, top_p):
+    """pool: 64ths of the gate/up rows in the shared pool (its claim counters run across the steps);
+    top_p: nucleus sampling at temperature 0.8 (each step's draw feeds the next step on the device)."""
     from persistent_moe_decode_amd.runtime import DeviceDecoder
     steps = 8
     w = synth.Workload(f"mid_ms{batch}", synth.MID, batch=batch, steps=steps + 1, context=context)
     print(f"workload {w.name}: batch {batch}, {steps} steps, pool {pool}", flush=True)
     dec = DeviceDecoder(w, pool_64ths=pool)
+    if top_p is not None:
+        dec.ctx.set_sampling(0.8, 0x5EED)
+        dec.ctx.set_top_p(top_p)
     dev, n = dec.dev, batch
     lens0 = torch.tensor(context, dtype=torch.int32, device=dev)
     tok0 = torch.tensor([int(w.prompt(b)[context[b]]) for b in range(n)], dtype=torch.int32, device=dev)
